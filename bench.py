@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed single-pair-single block on one MI355X.
+
+One step = the whole hot path on one batch: build the partition from host
+lengths (offset scan, row splits), then every block of the workload
+(projections, broadcast fused into the transition, column mean, output
+projection). Inputs are resident in HBM before timing starts. Prints one
+JSON line; progress goes to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import pair_inputs as pin  # noqa: E402
+
+HEADLINE = "high_variation_x4"
+METRIC = "pair cells/sec per block (1 GPU) + HBM GB/s & MFMA util vs peak"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector/MFMA
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def dev(t: pin.Tensor, torch):
+    if t.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(t.data).view(np.int16)).view(
+            torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(t.data)).cuda()
+
+
+class PackedRunner:
+    """Preallocated buffers and one-step function for a workload."""
+
+    def __init__(self, x: pin.Inputs, torch, nt):
+        self.torch, self.nt, self.x = torch, nt, x
+        self.lengths = torch.from_numpy(x.lengths.astype(np.int32)).pin_memory()
+        T, cells, _, nbytes = nt.nt_partition_sizes(x.lengths)
+        self.T, self.cells = T, cells
+        self.part_buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        self.p = nt.nt_make_partition(self.lengths, buffer=self.part_buf)
+        tdt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+        self.s0 = dev(x.s, torch)
+        self.s = [torch.empty_like(self.s0), torch.empty_like(self.s0)]
+        self.z = torch.empty((cells, x.c_z), dtype=tdt, device="cuda")
+        self.ws = torch.empty(max(nt.nt_block_workspace_bytes(self.p, x.c_s, x.c_z, x.hidden, tdt),
+                                  1), dtype=torch.uint8, device="cuda")
+        self.w = [{k: dev(v, torch) for k, v in wk.items()} for wk in x.weights]
+
+    def step(self):
+        nt = self.nt
+        p = nt.nt_make_partition(self.lengths, buffer=self.part_buf)
+        s_in = self.s0
+        for k, w in enumerate(self.w):
+            s_out = self.s[k % 2]
+            nt.nt_pair_block(p, s_in, w, s_out=s_out, z_out=self.z, workspace=self.ws)
+            s_in = s_out
+        return s_in, self.z
+
+
+def time_steps(fn, steps: int, warmup: int, torch) -> float:
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def time_kernel(fn, reps: int, torch) -> float:
+    """Average duration (s) of fn's launches, from HIP events on the current
+    stream (the stream the library launches on)."""
+    fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        fn()
+    end.record()
+    end.synchronize()
+    return start.elapsed_time(end) / 1e3 / reps
+
+
+def kernel_rooflines(r: PackedRunner, reps: int):
+    """Per-kernel durations on block 0's data: the fused broadcast+transition
+    (the kernel the block launches), the standalone broadcast and the column
+    mean, each against its roofline."""
+    torch, nt, x = r.torch, r.nt, r.x
+    w = r.w[0]
+    # a and b as the block's projections produce them (harness inputs only)
+    s32 = r.s0.float()
+    a = (s32 @ w["Wa"].float().t().contiguous()).to(r.s0.dtype).contiguous()
+    b = (s32 @ w["Wb"].float().t().contiguous()).to(r.s0.dtype).contiguous()
+    es = 2 if x.dtype == "bf16" else 4
+    T, cells, cz, hd = r.T, r.cells, x.c_z, x.hidden
+    m = torch.empty((T, cz), dtype=torch.float32, device="cuda")
+    zt = torch.empty_like(r.z)
+    out = {}
+
+    t = time_kernel(lambda: nt.nt_pair_broadcast_transition(r.p, a, b, w["W1"], w["W2"],
+                                                            z_out=r.z), reps, torch)
+    flops = 4.0 * cz * hd * cells
+    nbytes = cells * cz * es + 2 * T * cz * es + 2 * hd * cz * es
+    peak_f = PEAK_BF16_TFLOPS if x.dtype == "bf16" else PEAK_F32_TFLOPS
+    t_f, t_b = flops / (peak_f * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_f >= t_b:
+        out["transition"] = {"kernel": "k_transition_mfma (fused broadcast prologue)",
+                             "bound": "mfma", "ms": t * 1e3, "achieved": flops / t / 1e12,
+                             "peak": peak_f, "unit": "TFLOP/s", "flop_per_launch": flops,
+                             "bytes_per_launch": nbytes}
+    else:
+        out["transition"] = {"kernel": "k_transition_mfma (fused broadcast prologue)",
+                             "bound": "hbm", "ms": t * 1e3, "achieved": nbytes / t / 1e9,
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "flop_per_launch": flops,
+                             "bytes_per_launch": nbytes}
+    t = time_kernel(lambda: nt.nt_pair_broadcast(r.p, a, b, z=zt), reps, torch)
+    nbytes = cells * cz * es + 2 * T * cz * es
+    out["broadcast"] = {"kernel": "k_broadcast", "bound": "hbm", "ms": t * 1e3,
+                        "achieved": nbytes / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "bytes_per_launch": nbytes}
+    t = time_kernel(lambda: nt.nt_pair_reduce(r.p, zt, m=m), reps, torch)
+    nbytes = cells * cz * es + T * cz * 4
+    out["reduce"] = {"kernel": "k_reduce_pow2", "bound": "hbm", "ms": t * 1e3,
+                     "achieved": nbytes / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "bytes_per_launch": nbytes}
+    for v in out.values():
+        v["frac"] = v["achieved"] / v["peak"]
+    return out
+
+
+def traffic_for(kernel_key: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    entry = data.get(kernel_key)
+    if not entry:
+        return None
+    src = os.path.join(ROOT, "padding_free_pair_amd", "csrc", entry["source"])
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if digest != entry.get("source_sha256"):
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def padded_baseline(x: pin.Inputs, steps: int, warmup: int, torch):
+    """The same blocks over the B x N_max^2 envelope with PyTorch-native ops
+    (zero-padded singles, validity mask, mean over valid columns): the
+    comparator of the packed path, not part of it."""
+    L = x.lengths.astype(np.int64)
+    B, nmax = len(L), int(L.max())
+    tdt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+    s = dev(x.s, torch)
+    S0 = torch.zeros((B, nmax, x.c_s), dtype=tdt, device="cuda")
+    eta = np.concatenate([[0], np.cumsum(L)])
+    for i in range(B):
+        S0[i, :L[i]] = s[eta[i]:eta[i + 1]]
+    valid = torch.zeros((B, nmax), dtype=torch.bool, device="cuda")
+    for i in range(B):
+        valid[i, :L[i]] = True
+    colmask = valid[:, None, :, None].to(torch.float32)
+    cnt = torch.from_numpy(L.astype(np.float32)).cuda()[:, None, None]
+    W = [{k: dev(v, torch).t().contiguous() for k, v in wk.items()} for wk in x.weights]
+
+    def step():
+        S = S0
+        P = None
+        for w in W:
+            U = (S.reshape(-1, x.c_s) @ w["Wa"]).reshape(B, nmax, x.c_z)
+            V = (S.reshape(-1, x.c_s) @ w["Wb"]).reshape(B, nmax, x.c_z)
+            P = (U[:, :, None, :] + V[:, None, :, :]).reshape(-1, x.c_z)
+            H = torch.relu(P @ w["W1"])
+            P = P + H @ w["W2"]
+            M = (P.reshape(B, nmax, nmax, x.c_z).float() * colmask).sum(dim=2) / cnt
+            S = S + (M.reshape(-1, x.c_z) @ w["Wo"].float()).to(tdt).reshape(B, nmax, x.c_s)
+        return S, P
+
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    t = time_steps(step, steps, warmup, torch)
+    peak = torch.cuda.max_memory_allocated() - base
+    return t, peak
+
+
+def cpu_baseline(x: pin.Inputs, target_cells: int = 120_000):
+    """The float64 oracle on this host, on the workload's first samples up to
+    about target_cells pair cells, all of the workload's blocks."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = None
+    L = x.lengths.astype(np.int64)
+    take, cells = 0, 0
+    while take < len(L) and cells < target_cells:
+        cells += int(L[take]) ** 2
+        take += 1
+    T = int(L[:take].sum())
+    s = x.s.f64[:T]
+    ws = [{k: v.f64 for k, v in wk.items()} for wk in x.weights]
+    t0 = time.perf_counter()
+    oracle.chain(L[:take].tolist(), s, ws)
+    dt = time.perf_counter() - t0
+    return {"value": cells * len(ws) / dt, "unit": "pair cells/s per block",
+            "cores": threads if threads else len(os.sched_getaffinity(0)),
+            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"first {take} of {len(L)} samples ({cells} of "
+                      f"{int((L * L).sum())} cells), all {len(ws)} blocks, float64 numpy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--quick", action="store_true",
+                    help="timed steps and kernel timings only (for profiler runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the packed block is sample-local and is not sharded here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import padding_free_pair_amd as nt
+    nt._native.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    w = pin.workload(args.workload)
+    x = pin.workload_inputs(w.index)
+    log(f"workload {w.name}: B={w.B} cells={int((x.lengths.astype(np.int64) ** 2).sum())} "
+        f"blocks={w.blocks}")
+    r = PackedRunner(x, torch, nt)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base_mem = torch.cuda.memory_allocated()
+    t_step = time_steps(r.step, args.steps, args.warmup, torch)
+    packed_peak = torch.cuda.max_memory_allocated() - base_mem + sum(
+        t.numel() * t.element_size() for t in (r.z, r.ws, r.part_buf, r.s[0], r.s[1], r.s0))
+    value = r.cells * w.blocks / t_step
+    log(f"step {t_step * 1e3:.3f} ms -> {value:.4g} cells/s per block")
+
+    kern = kernel_rooflines(r, args.kernel_reps)
+    for k, v in kern.items():
+        log(f"kernel {k}: {v['ms'] * 1e3:.1f} us, {v['achieved']:.1f} {v['unit']} "
+            f"({100 * v['frac']:.1f}% of peak)")
+    dom = kern["transition"]
+    roofline = {"bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
+                "unit": dom["unit"], "frac": dom["frac"],
+                "traffic": traffic_for(f"transition_fused:{w.name}"),
+                "kernel": dom["kernel"], "avg_launch_ms": dom["ms"]}
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "pair cells/s per block", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": t_step * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded lengths, N(0,1) singles, "
+                                  "N(0,1/fan_in) weights)",
+        "config": {"workload": w.name, "B": w.B, "lengths": x.lengths.tolist(), "c_s": w.c_s,
+                   "c_z": w.c_z, "hidden": w.hidden, "blocks": w.blocks, "cells": r.cells,
+                   "T": r.T, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels": kern,
+    }
+
+    if not args.quick:
+        env = int(x.lengths.max()) ** 2 * len(x.lengths)
+        log("padded envelope baseline")
+        t_pad, pad_peak = padded_baseline(x, max(3, args.steps // 4), 2, torch)
+        result["padded"] = {"ms_per_step": t_pad * 1e3, "speedup": t_pad / t_step,
+                            "envelope_cells": env, "rho_pair": r.cells / env,
+                            "peak_bytes_padded": pad_peak, "peak_bytes_packed": packed_peak,
+                            "memory_efficiency": pad_peak / max(packed_peak, 1),
+                            "impl": "PyTorch ops over B x N_max^2 (bf16 matmul, masked mean)"}
+        regimes = {}
+        for other in pin.WORKLOADS[1:]:
+            if other.name == w.name:
+                continue
+            log(f"regime {other.name}")
+            xo = pin.workload_inputs(other.index)
+            ro = PackedRunner(xo, torch, nt)
+            to = time_steps(ro.step, args.steps, args.warmup, torch)
+            ko = kernel_rooflines(ro, args.kernel_reps)
+            regimes[other.name] = {
+                "value": ro.cells * other.blocks / to, "ms_per_step": to * 1e3,
+                "cells": ro.cells, "blocks": other.blocks,
+                "kernels": {k: {"ms": v["ms"], "achieved": v["achieved"], "unit": v["unit"],
+                                "frac": v["frac"]} for k, v in ko.items()}}
+            del ro
+            torch.cuda.empty_cache()
+        result["regimes"] = regimes
+    if not args.no_cpu_baseline and not args.quick:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

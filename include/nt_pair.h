@@ -1,0 +1,213 @@
+/*
+ * nt_pair.h - packed single-pair-single block on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the single-pair-single block of the DanLing NestedTensor
+ * paper (arXiv 2609.30379, Section 3, Equation 1), run on packed
+ * multi-ragged storage instead of a B x N_max^2 envelope:
+ *
+ *   a = s Wa^T,  b = s Wb^T                    (single projections)
+ *   z[o_i + r N_i + c] = a[eta_i + r] + b[eta_i + c]        (broadcast)
+ *   z~ = z + relu(z W1^T) W2^T                  (residual cell transition)
+ *   m[eta_i + r] = (1/N_i) sum_c z~[o_i + r N_i + c]        (column mean)
+ *   s~ = s + m Wo^T                             (output projection, residual)
+ *
+ * eta_i = sum_{k<i} N_k are the single offsets and o_i = sum_{k<i} N_k^2 the
+ * pair offsets (Section 3.1, Equation 2); the packed row of pair cell (r, c)
+ * of sample i is Equation 3's o_i + r N_i + c; the column sum is Equation 4.
+ *
+ * Conventions for every call:
+ *  - Memory: every array argument is device memory owned by the caller and
+ *    must stay alive until the work enqueued on `stream` has finished. The
+ *    library allocates no device memory and keeps no state except a
+ *    thread-local error message.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *    stream). Every device call is asynchronous on it.
+ *  - Layout: row-major, contiguous, feature dimension innermost. Singles are
+ *    [T, c_s], pair states [cells, c_z]. Weights are [out, in] (the layout of
+ *    the paper's V W^T, Section 3.3), without bias:
+ *       Wa, Wb: [c_z, c_s]  W1: [hidden, c_z]  W2: [c_z, hidden]  Wo: [c_s, c_z]
+ *  - Element type: NT_BF16 (storage bf16, accumulation fp32, results rounded
+ *    to nearest-even) or NT_F32 (fp32 throughout). The column mean m is always
+ *    fp32.
+ *  - Widths c_s, c_z and hidden must be positive multiples of 8, with
+ *    c_z <= 512 and c_s, hidden <= 16384.
+ *  - Alignment: every array pointer must be 16-byte aligned.
+ *  - Errors: arguments are checked on the host before anything is enqueued;
+ *    a validation failure enqueues nothing and leaves outputs untouched.
+ *    NT_ERR_HIP means the runtime rejected a launch; stages of the same call
+ *    before it may already be enqueued. nt_last_error() describes the
+ *    failure. Faults inside kernels surface at the caller's next
+ *    synchronisation, as with any HIP launch. No call aborts or throws.
+ */
+#ifndef NT_PAIR_H
+#define NT_PAIR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nt_status {
+  NT_OK = 0,
+  NT_ERR_NULL = 1,      /* a required pointer is NULL */
+  NT_ERR_INVALID = 2,   /* bad length, width, partition, or overlapping buffers */
+  NT_ERR_OVERFLOW = 3,  /* a size does not fit the index types */
+  NT_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
+  NT_ERR_WORKSPACE = 5, /* buffer or workspace smaller than required */
+  NT_ERR_DTYPE = 6,     /* unknown element type */
+  NT_ERR_HIP = 7        /* the HIP runtime rejected a launch */
+} nt_status;
+
+typedef enum nt_dtype { NT_F32 = 0, NT_BF16 = 1 } nt_dtype;
+
+/*
+ * A square pair partition (Section 3.1 "Structural metadata"; Figure 2;
+ * Appendix A "Structural invariants"). Host scalars are canonical; the
+ * arrays are device mirrors inside the caller's partition buffer. Filled by
+ * nt_make_partition; read-only for callers.
+ *
+ *   single_offsets [B+1]  eta_i (first-level row splits), eta_B = T
+ *   pair_offsets   [B+1]  o_i, o_B = cells; zero-length samples repeat offsets
+ *   row_splits     [T+1]  second-level splits: pair row r of sample i starts
+ *                         at o_i + r N_i; row_splits[T] = cells
+ *   row_sample     [T]    sample index of each pair row
+ *   item_offsets   [B+1]  execution index of the column-mean schedule: sample
+ *                         i owns work items [item_offsets[i], item_offsets[i+1])
+ */
+typedef struct nt_partition {
+  uint32_t magic;       /* set by nt_make_partition */
+  int32_t B;            /* samples */
+  int32_t n_max;        /* max_i N_i (0 if every sample is empty) */
+  int32_t reserved;
+  int64_t T;            /* sum_i N_i */
+  int64_t cells;        /* sum_i N_i^2 */
+  int64_t n_items;      /* item_offsets[B] */
+  const int32_t* lengths;
+  const int64_t* single_offsets;
+  const int64_t* pair_offsets;
+  const int64_t* row_splits;
+  const int32_t* row_sample;
+  const int64_t* item_offsets;
+} nt_partition;
+
+/* The five weights of one block; see the layout convention above. */
+typedef struct nt_block_weights {
+  const void* Wa;
+  const void* Wb;
+  const void* W1;
+  const void* W2;
+  const void* Wo;
+} nt_block_weights;
+
+/*
+ * Host only. Validates lengths and reports the partition's sizes and the
+ * device buffer nt_make_partition needs. lengths: host int32 [B], N_i >= 0
+ * (NULL allowed only when B == 0). Any output pointer may be NULL.
+ * Errors: NT_ERR_INVALID (B < 0 or a negative length), NT_ERR_NULL,
+ * NT_ERR_OVERFLOW (sum N_i^2 exceeds int64, or T exceeds INT32_MAX).
+ */
+nt_status nt_partition_sizes(const int32_t* lengths, int32_t B, int64_t* T, int64_t* cells,
+                             int32_t* n_max, size_t* buffer_bytes);
+
+/*
+ * Builds the partition of Section 3.1 / Figure 2 for square pairs: the
+ * lengths are copied from host memory into `buffer` on `stream` (pageable
+ * memory is read before the call returns; page-locked memory is read
+ * asynchronously and must stay unchanged until the stream passes this
+ * call), then an
+ * exclusive scan on the device produces eta, o and the item offsets, and a
+ * second kernel fills row_splits and row_sample. `out` receives the host
+ * scalars and pointers into `buffer` immediately; the device arrays are
+ * valid once the stream reaches this point. The partition stays valid while
+ * `buffer` lives. buffer: device, at least nt_partition_sizes' buffer_bytes,
+ * 256-byte aligned. Errors: as nt_partition_sizes, plus NT_ERR_WORKSPACE,
+ * NT_ERR_ALIGN, NT_ERR_HIP.
+ */
+nt_status nt_make_partition(const int32_t* lengths, int32_t B, void* buffer, size_t buffer_bytes,
+                            void* stream, nt_partition* out);
+
+/*
+ * Test hook: materialises the decode of every packed cell t into its
+ * (sample, row, col) with t = o_sample + row * N_sample + col (Equation 3
+ * inverted). sample, row, col: device int32 [cells]. The hot kernels decode
+ * on the fly and never build these maps.
+ */
+nt_status nt_decode_cells(const nt_partition* p, int32_t* sample, int32_t* row, int32_t* col,
+                          void* stream);
+
+/*
+ * Broadcast (Equation 1, first line; Section 3.2 "Creating axes through
+ * broadcasting"): z[o_i + r N_i + c, :] = a[eta_i + r, :] + b[eta_i + c, :].
+ * a, b: [T, c_z]; z: [cells, c_z], all of `dtype`. The sum is formed in fp32
+ * and rounded once to the storage type. z must not overlap a or b.
+ */
+nt_status nt_pair_broadcast(const nt_partition* p, const void* a, const void* b, void* z,
+                            int32_t c_z, nt_dtype dtype, void* stream);
+
+/*
+ * Residual pair transition (Equation 1, second line, with a two-layer ReLU
+ * MLP as the feature update; Section 3.3 "Dense work across valid
+ * positions": it runs over the sum N_i^2 packed cells only):
+ *   z_out = z_in + relu(z_in W1^T) W2^T, cell by cell.
+ * z_in, z_out: [cells, c_z]; W1: [hidden, c_z]; W2: [c_z, hidden]. In bf16
+ * the hidden activations are rounded to bf16 before the second product and
+ * both products accumulate in fp32. z_out may equal z_in (in place); other
+ * overlaps are rejected.
+ */
+nt_status nt_pair_transition(const nt_partition* p, const void* z_in, void* z_out, const void* W1,
+                             const void* W2, int32_t c_z, int32_t hidden, nt_dtype dtype,
+                             void* stream);
+
+/*
+ * Broadcast fused into the transition (Equation 1's first two lines in one
+ * kernel): z_out[o_i + r N_i + c] = z + relu(z W1^T) W2^T with
+ * z = a[eta_i + r] + b[eta_i + c] formed on chip (rounded to the storage
+ * type exactly as nt_pair_broadcast rounds it) and never written to memory.
+ * a, b: [T, c_z]; z_out: [cells, c_z]; W1, W2 as for nt_pair_transition.
+ * This is the kernel nt_pair_block runs for these two stages. z_out must not
+ * overlap a, b or the weights.
+ */
+nt_status nt_pair_broadcast_transition(const nt_partition* p, const void* a, const void* b,
+                                       void* z_out, const void* W1, const void* W2, int32_t c_z,
+                                       int32_t hidden, nt_dtype dtype, void* stream);
+
+/*
+ * Column mean (Equation 1, third line; Equation 4 divided by N_i):
+ *   m[eta_i + r, :] = (1/N_i) sum_{c < N_i} z[o_i + r N_i + c, :].
+ * z: [cells, c_z] of `dtype`; m: fp32 [T, c_z]. Deterministic: every row is
+ * summed by one workgroup in a fixed order, no atomics.
+ */
+nt_status nt_pair_reduce(const nt_partition* p, const void* z, float* m, int32_t c_z,
+                         nt_dtype dtype, void* stream);
+
+/*
+ * Workspace bytes nt_pair_block needs for this partition and widths.
+ */
+nt_status nt_block_workspace_bytes(const nt_partition* p, int32_t c_s, int32_t c_z,
+                                   int32_t hidden, nt_dtype dtype, size_t* bytes);
+
+/*
+ * One whole block (Equation 1; Figure 3's three lines): projections, the
+ * broadcast fused into the transition's prologue, the column mean and the
+ * output projection with its residual. Returns both outputs, as the paper's
+ * block does: s_out [T, c_s] and z_out [cells, c_z]. s_out may equal s_in.
+ * workspace: device, at least nt_block_workspace_bytes, 256-byte aligned;
+ * it holds a, b and m between the stages.
+ */
+nt_status nt_pair_block(const nt_partition* p, const void* s_in, void* s_out, void* z_out,
+                        const nt_block_weights* w, int32_t c_s, int32_t c_z, int32_t hidden,
+                        nt_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Thread-local description of the last failure in this thread ("" if none). */
+const char* nt_last_error(void);
+
+/* Library ABI version: 1. */
+int32_t nt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NT_PAIR_H */

@@ -1,0 +1,260 @@
+"""Packed single-pair-single block on MI355X: Python binding of libntpair.so.
+
+The functions below carry the C entry points' names and only marshal
+arguments: PyTorch supplies device memory and the current HIP stream, and
+every step of the computation runs in the library's gfx950 kernels. There is
+no fallback path; calls fail if the library is not built or rejects its
+arguments (NtError carries the status and the library's message).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import _native
+from ._native import (NT_BF16, NT_F32, NativeLibraryMissing, NtBlockWeights,  # noqa: F401
+                      NtPartition)
+
+__all__ = ["NtError", "Partition", "nt_partition_sizes", "nt_make_partition", "nt_decode_cells",
+           "nt_pair_broadcast", "nt_pair_transition", "nt_pair_broadcast_transition",
+           "nt_pair_reduce",
+           "nt_block_workspace_bytes", "nt_pair_block", "nt_last_error", "nt_version",
+           "NT_F32", "NT_BF16"]
+
+
+class NtError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_native.STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+def _check(status: int) -> None:
+    if status != _native.NT_OK:
+        raise NtError(status, _native.lib().nt_last_error().decode())
+
+
+def nt_last_error() -> str:
+    return _native.lib().nt_last_error().decode()
+
+
+def nt_version() -> int:
+    return int(_native.lib().nt_version())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return NT_BF16
+    if t.dtype == torch.float32:
+        return NT_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream, device) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _lengths_array(lengths) -> np.ndarray:
+    arr = np.ascontiguousarray(np.asarray(lengths, dtype=np.int64))
+    if arr.ndim != 1:
+        raise ValueError("lengths must be one-dimensional")
+    if arr.size and (arr.min() < np.iinfo(np.int32).min or arr.max() > np.iinfo(np.int32).max):
+        raise OverflowError("lengths must fit int32")
+    return arr.astype(np.int32)
+
+
+def nt_partition_sizes(lengths: Sequence[int]) -> Tuple[int, int, int, int]:
+    """(T, cells, n_max, buffer_bytes) of a length vector; host only."""
+    arr = _lengths_array(lengths)
+    T, cells, n_max, nbytes = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32(), \
+        ctypes.c_size_t()
+    ptr = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if arr.size else None
+    _check(_native.lib().nt_partition_sizes(ptr, arr.size, ctypes.byref(T), ctypes.byref(cells),
+                                            ctypes.byref(n_max), ctypes.byref(nbytes)))
+    return T.value, cells.value, n_max.value, nbytes.value
+
+
+class Partition:
+    """A built partition: the C struct plus the device buffer it points into."""
+
+    def __init__(self, struct: NtPartition, buffer, lengths: np.ndarray):
+        self.struct = struct
+        self.buffer = buffer
+        self.lengths = lengths
+
+    B = property(lambda self: self.struct.B)
+    T = property(lambda self: self.struct.T)
+    cells = property(lambda self: self.struct.cells)
+    n_max = property(lambda self: self.struct.n_max)
+    n_items = property(lambda self: self.struct.n_items)
+    device = property(lambda self: self.buffer.device)
+
+    def _view(self, addr: int, count: int, dtype):
+        torch = _torch()
+        off = addr - self.buffer.data_ptr()
+        size = torch.tensor([], dtype=dtype).element_size()
+        return self.buffer[off:off + count * size].view(dtype)
+
+    def arrays(self) -> dict:
+        """Device views of the partition arrays (Figure 2's offsets and splits)."""
+        torch = _torch()
+        s, B, T = self.struct, self.B, self.T
+        return {
+            "lengths": self._view(s.lengths, B, torch.int32),
+            "single_offsets": self._view(s.single_offsets, B + 1, torch.int64),
+            "pair_offsets": self._view(s.pair_offsets, B + 1, torch.int64),
+            "item_offsets": self._view(s.item_offsets, B + 1, torch.int64),
+            "row_splits": self._view(s.row_splits, T + 1, torch.int64),
+            "row_sample": self._view(s.row_sample, T, torch.int32),
+        }
+
+
+def nt_make_partition(lengths, device=None, stream=None, buffer=None) -> Partition:
+    """Build a square pair partition on the device (nt_make_partition).
+
+    lengths: a sequence / numpy array (copied to pageable int32 memory), or a
+    CPU int32 torch tensor, passed as is (if it is pinned, the copy to the
+    device is asynchronous and the tensor must not change until the stream
+    has passed the call). buffer: optional preallocated uint8 device tensor.
+    """
+    torch = _torch()
+    host = None
+    if isinstance(lengths, torch.Tensor):
+        if lengths.device.type != "cpu" or lengths.dtype != torch.int32 or \
+                not lengths.is_contiguous():
+            raise ValueError("tensor lengths must be a contiguous CPU int32 tensor")
+        host = lengths
+        arr = lengths.numpy()
+    else:
+        arr = _lengths_array(lengths)
+    _, _, _, nbytes = nt_partition_sizes(arr)
+    dev = torch.device(device) if device is not None else torch.device("cuda",
+                                                                        torch.cuda.current_device())
+    if buffer is None or buffer.numel() < nbytes:
+        buffer = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    st = NtPartition()
+    ptr = ctypes.cast(host.data_ptr(), ctypes.POINTER(ctypes.c_int32)) if host is not None \
+        else arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    if arr.size == 0:
+        ptr = None
+    _check(_native.lib().nt_make_partition(ptr, arr.size, buffer.data_ptr(), buffer.numel(),
+                                           _stream(stream, dev), ctypes.byref(st)))
+    return Partition(st, buffer, arr if host is None else host)
+
+
+def nt_decode_cells(p: Partition, stream=None):
+    """(sample, row, col) int32 of every packed cell (test hook)."""
+    torch = _torch()
+    out = [torch.empty(p.cells, dtype=torch.int32, device=p.device) for _ in range(3)]
+    _check(_native.lib().nt_decode_cells(ctypes.byref(p.struct), *[_ptr(t) for t in out],
+                                         _stream(stream, p.device)))
+    return tuple(out)
+
+
+def nt_pair_broadcast(p: Partition, a, b, z=None, stream=None):
+    """z[o_i + r N_i + c] = a[eta_i + r] + b[eta_i + c]."""
+    torch = _torch()
+    c_z = a.shape[-1]
+    if z is None:
+        z = torch.empty((p.cells, c_z), dtype=a.dtype, device=a.device)
+    if a.dtype != b.dtype or z.dtype != a.dtype:
+        raise TypeError("a, b and z must share a dtype")
+    _check(_native.lib().nt_pair_broadcast(ctypes.byref(p.struct), _ptr(a), _ptr(b), _ptr(z),
+                                           c_z, _dtype_code(a), _stream(stream, a.device)))
+    return z
+
+
+def nt_pair_transition(p: Partition, z_in, W1, W2, z_out=None, stream=None):
+    """z_out = z_in + relu(z_in W1^T) W2^T; pass z_out=z_in to work in place."""
+    torch = _torch()
+    c_z, hidden = z_in.shape[-1], W1.shape[0]
+    if z_out is None:
+        z_out = torch.empty_like(z_in)
+    if not (z_in.dtype == W1.dtype == W2.dtype == z_out.dtype):
+        raise TypeError("z and weights must share a dtype")
+    _check(_native.lib().nt_pair_transition(ctypes.byref(p.struct), _ptr(z_in), _ptr(z_out),
+                                            _ptr(W1), _ptr(W2), c_z, hidden,
+                                            _dtype_code(z_in), _stream(stream, z_in.device)))
+    return z_out
+
+
+def nt_pair_broadcast_transition(p: Partition, a, b, W1, W2, z_out=None, stream=None):
+    """z_out = z + relu(z W1^T) W2^T with z = a[row] + b[col] formed on chip."""
+    torch = _torch()
+    c_z, hidden = a.shape[-1], W1.shape[0]
+    if z_out is None:
+        z_out = torch.empty((p.cells, c_z), dtype=a.dtype, device=a.device)
+    if not (a.dtype == b.dtype == W1.dtype == W2.dtype == z_out.dtype):
+        raise TypeError("a, b, weights and z_out must share a dtype")
+    _check(_native.lib().nt_pair_broadcast_transition(
+        ctypes.byref(p.struct), _ptr(a), _ptr(b), _ptr(z_out), _ptr(W1), _ptr(W2), c_z, hidden,
+        _dtype_code(a), _stream(stream, a.device)))
+    return z_out
+
+
+def nt_pair_reduce(p: Partition, z, m=None, stream=None):
+    """m[eta_i + r] = mean over columns c of z[o_i + r N_i + c] (fp32)."""
+    torch = _torch()
+    c_z = z.shape[-1]
+    if m is None:
+        m = torch.empty((p.T, c_z), dtype=torch.float32, device=z.device)
+    _check(_native.lib().nt_pair_reduce(ctypes.byref(p.struct), _ptr(z), _ptr(m), c_z,
+                                        _dtype_code(z), _stream(stream, z.device)))
+    return m
+
+
+def nt_block_workspace_bytes(p: Partition, c_s: int, c_z: int, hidden: int, dtype) -> int:
+    n = ctypes.c_size_t()
+    code = dtype if isinstance(dtype, int) else (NT_BF16 if "bfloat16" in str(dtype) else NT_F32)
+    _check(_native.lib().nt_block_workspace_bytes(ctypes.byref(p.struct), c_s, c_z, hidden, code,
+                                                  ctypes.byref(n)))
+    return n.value
+
+
+def nt_pair_block(p: Partition, s_in, weights, s_out=None, z_out=None, workspace=None,
+                  stream=None):
+    """One single-pair-single block; returns (s_out, z_out).
+
+    weights: dict (or sequence in this order) of Wa, Wb [c_z, c_s], W1
+    [hidden, c_z], W2 [c_z, hidden], Wo [c_s, c_z], all in s_in's dtype.
+    """
+    torch = _torch()
+    if isinstance(weights, dict):
+        weights = [weights[k] for k in ("Wa", "Wb", "W1", "W2", "Wo")]
+    Wa, Wb, W1, W2, Wo = weights
+    c_s, c_z, hidden = s_in.shape[-1], Wa.shape[0], W1.shape[0]
+    for w in weights:
+        if w.dtype != s_in.dtype:
+            raise TypeError("weights must share s_in's dtype")
+    if s_out is None:
+        s_out = torch.empty_like(s_in)
+    if z_out is None:
+        z_out = torch.empty((p.cells, c_z), dtype=s_in.dtype, device=s_in.device)
+    need = nt_block_workspace_bytes(p, c_s, c_z, hidden, _dtype_code(s_in))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=s_in.device)
+    wst = NtBlockWeights(*[_ptr(w) for w in weights])
+    _check(_native.lib().nt_pair_block(ctypes.byref(p.struct), _ptr(s_in), _ptr(s_out),
+                                       _ptr(z_out), ctypes.byref(wst), c_s, c_z, hidden,
+                                       _dtype_code(s_in), _ptr(workspace),
+                                       workspace.numel(), _stream(stream, s_in.device)))
+    return s_out, z_out

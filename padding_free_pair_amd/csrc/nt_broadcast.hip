@@ -1,0 +1,76 @@
+// Pair broadcast (DanLing NestedTensor, Equation 1 first line; Section 3.2
+// "Creating axes through broadcasting"):
+//   z[o_i + r N_i + c, :] = a[eta_i + r, :] + b[eta_i + c, :].
+// HBM-write bound: each cell writes c_z elements, a and b are L2 resident.
+#include "nt_device.hpp"
+#include "nt_internal.hpp"
+
+namespace nt {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kSteps = 8;  // cells each thread visits
+
+// Thread (f, cl) owns 16-byte feature vector f of every CL-th cell of the
+// workgroup's chunk of CL * kSteps consecutive cells. The cell decode is done
+// once per thread and then advanced by CL cells at a time.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_broadcast(
+    const T* __restrict__ a, const T* __restrict__ b, T* __restrict__ z,
+    const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
+    const int32_t* __restrict__ lengths, int B, int64_t cells, int c_z, int G, int CL) {
+  constexpr int VEC = Vec16<T>::N;
+  const int tid = threadIdx.x;
+  const int f = tid % G;
+  const int cl = tid / G;
+  if (cl >= CL) return;
+  int64_t t = (int64_t)blockIdx.x * CL * kSteps + cl;
+  if (t >= cells) return;
+  Cell x = decode_cell(pair_offsets, single_offsets, lengths, B, t);
+  const int64_t fo = (int64_t)f * VEC;
+#pragma unroll
+  for (int k = 0; k < kSteps; ++k) {
+    const Vec16<T> va = load16(a + (x.eta + x.r) * c_z + fo);
+    const Vec16<T> vb = load16(b + (x.eta + x.c) * c_z + fo);
+    Vec16<T> out;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) out.set(e, va.get(e) + vb.get(e));
+    store16(z + t * c_z + fo, out);
+    t += CL;
+    if (k + 1 == kSteps || t >= cells) break;
+    x.c += CL;
+    if (x.c >= x.n) {
+      if (x.n > CL) {  // at most one wrap into the next row
+        x.c -= x.n;
+        x.r += 1;
+        if (x.r >= x.n) x = decode_cell(pair_offsets, single_offsets, lengths, B, t);
+      } else {
+        x = decode_cell(pair_offsets, single_offsets, lengths, B, t);
+      }
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_t(const nt_partition& p, const void* a, const void* b, void* z, int c_z,
+                    hipStream_t stream) {
+  const int G = c_z / Vec16<T>::N;  // <= 256 for c_z <= kMaxCz
+  const int CL = kThreads / G;
+  const int64_t per_block = (int64_t)CL * kSteps;
+  const int64_t blocks = (p.cells + per_block - 1) / per_block;
+  hipLaunchKernelGGL(k_broadcast<T>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                     static_cast<const T*>(a), static_cast<const T*>(b), static_cast<T*>(z),
+                     p.pair_offsets, p.single_offsets, p.lengths, p.B, p.cells, c_z, G, CL);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_broadcast(const nt_partition& p, const void* a, const void* b, void* z, int c_z,
+                            nt_dtype dtype, hipStream_t stream) {
+  if (p.cells == 0) return hipSuccess;
+  if (dtype == NT_BF16) return launch_t<bf16>(p, a, b, z, c_z, stream);
+  return launch_t<float>(p, a, b, z, c_z, stream);
+}
+
+}  // namespace nt

@@ -1,0 +1,81 @@
+// Internal definitions shared by the gfx950 kernels and the host API.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nt_pair.h"
+
+namespace nt {
+
+constexpr uint32_t kPartitionMagic = 0x4E545031u;  // "NTP1"
+
+// Widths the library accepts (all multiples of 8).
+constexpr int kMaxCz = 512;
+constexpr int kMaxCs = 16384;
+constexpr int kMaxHidden = 16384;
+
+// ---------------------------------------------------------------------------
+// Column-mean schedule. Rows of one sample all have N_i cells. A row of at
+// least kLongRow cells is one work item, reduced by a whole workgroup; shorter
+// rows are grouped, rows_per_item(N) at a time, and each wave of the
+// workgroup reduces whole rows. Items never cross samples, so the item of a
+// workgroup is found by a search over per-sample item offsets.
+constexpr int64_t kLongRow = 256;
+constexpr int64_t kItemCells = 512;
+
+__host__ __device__ inline int64_t rows_per_item(int64_t n) {
+  if (n >= kLongRow) return 1;
+  int64_t k = kItemCells / (4 * n);
+  return 4 * (k < 1 ? 1 : k);
+}
+
+__host__ __device__ inline int64_t items_of(int64_t n) {
+  if (n <= 0) return 0;
+  const int64_t r = rows_per_item(n);
+  return (n + r - 1) / r;
+}
+
+// Byte layout of the partition buffer: each array starts 256-byte aligned.
+struct PartitionLayout {
+  size_t lengths, single_offsets, pair_offsets, item_offsets, row_splits, row_sample, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline PartitionLayout partition_layout(int64_t B, int64_t T) {
+  PartitionLayout L;
+  size_t off = 0;
+  L.lengths = off;        off = align256(off + sizeof(int32_t) * (B > 0 ? B : 1));
+  L.single_offsets = off; off = align256(off + sizeof(int64_t) * (B + 1));
+  L.pair_offsets = off;   off = align256(off + sizeof(int64_t) * (B + 1));
+  L.item_offsets = off;   off = align256(off + sizeof(int64_t) * (B + 1));
+  L.row_splits = off;     off = align256(off + sizeof(int64_t) * (T + 1));
+  L.row_sample = off;     off = align256(off + sizeof(int32_t) * (T > 0 ? T : 1));
+  L.total = off;
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (defined in the .hip sources). Each returns the launch's
+// hipError_t; arguments are validated by the host API beforehand.
+hipError_t launch_partition(const nt_partition& p, int64_t* single_offsets, int64_t* pair_offsets,
+                            int64_t* item_offsets, int64_t* row_splits, int32_t* row_sample,
+                            hipStream_t stream);
+hipError_t launch_decode(const nt_partition& p, int32_t* sample, int32_t* row, int32_t* col,
+                         hipStream_t stream);
+hipError_t launch_broadcast(const nt_partition& p, const void* a, const void* b, void* z, int c_z,
+                            nt_dtype dtype, hipStream_t stream);
+// z_in == nullptr selects the fused form: z is formed from a and b in the prologue.
+bool transition_has_mfma(int c_z, int hidden, nt_dtype dtype);
+hipError_t launch_transition(const nt_partition& p, const void* z_in, const void* a, const void* b,
+                             void* z_out, const void* W1, const void* W2, int c_z, int hidden,
+                             nt_dtype dtype, hipStream_t stream);
+hipError_t launch_reduce(const nt_partition& p, const void* z, float* m, int c_z, nt_dtype dtype,
+                         hipStream_t stream);
+// C[M, N] = (R ? R : 0) + A[M, K] W[N, K]^T. A is `a_dtype` (NT_F32 or the
+// block dtype), W, R and C are `dtype`.
+hipError_t launch_linear(const void* A, nt_dtype a_dtype, const void* W, const void* R, void* C,
+                         nt_dtype dtype, int64_t M, int N, int K, hipStream_t stream);
+
+}  // namespace nt

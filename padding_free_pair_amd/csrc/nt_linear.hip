@@ -1,0 +1,122 @@
+// Projections on packed single rows (DanLing NestedTensor, Section 3.3 "Dense
+// work across valid positions": V' = V W^T, here without bias):
+//   C[M, N] = R[M, N] + A[M, K] W[N, K]^T      (R optional).
+// These are the block's small GEMMs (a, b and the output projection), a few
+// hundred MFLOP each; one wave computes a 32 x 32 tile straight from L2.
+#include "nt_device.hpp"
+#include "nt_internal.hpp"
+
+namespace nt {
+namespace {
+
+// A, W: storage types; C, R: output type. BF16MMA: A and W are bf16 and K is a
+// multiple of 32 (v_mfma_f32_16x16x32_bf16); otherwise v_mfma_f32_16x16x4_f32
+// on fp32 values (bf16 inputs are widened exactly).
+template <typename TA, typename TW, typename TO, bool BF16MMA>
+__global__ __launch_bounds__(64) void k_linear(const TA* __restrict__ A, const TW* __restrict__ W,
+                                               const TO* R, TO* C, int64_t M, int N, int K) {
+  const int lane = threadIdx.x;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int64_t m0 = (int64_t)blockIdx.x * 32;
+  const int n0 = blockIdx.y * 32;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const TA* arow[2];
+  const TW* wrow[2];
+  bool aok[2], wok[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t row = m0 + 16 * i + l16;
+    aok[i] = row < M;
+    arow[i] = A + (aok[i] ? row : 0) * K;
+    const int col = n0 + 16 * i + l16;
+    wok[i] = col < N;
+    wrow[i] = W + (int64_t)(wok[i] ? col : 0) * K;
+  }
+
+  if constexpr (BF16MMA) {
+    for (int k0 = 0; k0 < K; k0 += 32) {
+      bf16x8 af[2], wf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = aok[i] ? *reinterpret_cast<const bf16x8*>(arow[i] + k0 + 8 * g) : bf16x8{};
+        wf[i] = wok[i] ? *reinterpret_cast<const bf16x8*>(wrow[i] + k0 + 8 * g) : bf16x8{};
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], wf[j], acc[i][j], 0, 0, 0);
+    }
+  } else {
+    // 16 k per step: lane group g holds k0 + 4g .. 4g+3 of its row, and the
+    // four sub-steps s pair A[., k0 + 4g + s] with W[., k0 + 4g + s].
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      const int kk = k0 + 4 * g;
+      const bool kin = kk < K;  // K is a multiple of 8, so groups are whole
+      float av[2][4], wv[2][4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          av[i][s] = (aok[i] && kin) ? to_f32(arow[i][kk + s]) : 0.f;
+          wv[i][s] = (wok[i] && kin) ? to_f32(wrow[i][kk + s]) : 0.f;
+        }
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][s], wv[j][s], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // result lane layout: rows 4g + e, column l16 of each 16x16 block
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + 16 * j + l16;
+      if (col >= N) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = m0 + 16 * i + 4 * g + e;
+        if (row >= M) continue;
+        float v = acc[i][j][e];
+        if (R) v += to_f32(R[row * N + col]);
+        C[row * N + col] = from_f32<TO>(v);
+      }
+    }
+}
+
+template <typename TA, typename TW, bool BF16MMA>
+hipError_t launch_t(const void* A, const void* W, const void* R, void* C, int64_t M, int N, int K,
+                    hipStream_t stream) {
+  const dim3 grid((unsigned)((M + 31) / 32), (unsigned)((N + 31) / 32));
+  hipLaunchKernelGGL((k_linear<TA, TW, TW, BF16MMA>), grid, dim3(64), 0, stream,
+                     static_cast<const TA*>(A), static_cast<const TW*>(W),
+                     static_cast<const TW*>(R), static_cast<TW*>(C), M, N, K);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_linear(const void* A, nt_dtype a_dtype, const void* W, const void* R, void* C,
+                         nt_dtype dtype, int64_t M, int N, int K, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  if (dtype == NT_BF16) {
+    if (a_dtype == NT_BF16) {
+      if (K % 32 == 0) return launch_t<bf16, bf16, true>(A, W, R, C, M, N, K, stream);
+      return launch_t<bf16, bf16, false>(A, W, R, C, M, N, K, stream);
+    }
+    return launch_t<float, bf16, false>(A, W, R, C, M, N, K, stream);
+  }
+  return launch_t<float, float, false>(A, W, R, C, M, N, K, stream);
+}
+
+}  // namespace nt

@@ -1,0 +1,181 @@
+// Column mean over packed pair rows (DanLing NestedTensor, Equation 4 and the
+// square mean of Equation 1's third line):
+//   m[eta_i + r, :] = (1 / N_i) * sum_{c < N_i} z[o_i + r N_i + c, :].
+// HBM-read bound. Deterministic: each row is summed by one wave or one
+// workgroup in a fixed order (no atomics).
+#include "nt_device.hpp"
+#include "nt_internal.hpp"
+
+namespace nt {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kUnroll = 4;
+
+template <typename T>
+__device__ __forceinline__ void accumulate(float (&acc)[Vec16<T>::N], const T* p) {
+  const Vec16<T> v = load16(p);
+#pragma unroll
+  for (int e = 0; e < Vec16<T>::N; ++e) acc[e] += v.get(e);
+}
+
+// Sum of the 16-byte vectors at cells c0, c0 + step, ... < n of one pair row.
+template <typename T>
+__device__ __forceinline__ void row_partial(float (&acc)[Vec16<T>::N], const T* row_base,
+                                            int64_t c0, int64_t n, int64_t step, int c_z) {
+  constexpr int VEC = Vec16<T>::N;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  int64_t c = c0;
+  for (; c + (kUnroll - 1) * step < n; c += kUnroll * step) {
+    Vec16<T> v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = load16(row_base + (c + u * step) * c_z);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] += v[u].get(e);
+  }
+  for (; c < n; c += step) accumulate<T>(acc, row_base + c * c_z);
+}
+
+// G = c_z / VEC feature vectors per cell, a power of two <= 64: lane (f, cl)
+// of a wave holds vector f of every (64/G)-th cell; a butterfly over the
+// cell-lane bits sums the lanes that share f.
+template <typename T, int G>
+__global__ __launch_bounds__(kThreads) void k_reduce_pow2(
+    const T* __restrict__ z, float* __restrict__ m, const int64_t* __restrict__ item_offsets,
+    const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
+    const int32_t* __restrict__ lengths, int B, int c_z) {
+  constexpr int VEC = Vec16<T>::N;
+  constexpr int CLW = 64 / G;
+  __shared__ float part[kWaves][G * VEC];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int f = lane % G, cl = lane / G;
+  const int64_t item = blockIdx.x;
+  const int i = find_segment(item_offsets, 0, B, item);
+  const int64_t n = lengths[i];
+  const int64_t eta = single_offsets[i];
+  const int64_t o = pair_offsets[i];
+  const int64_t j = item - item_offsets[i];
+  const float nf = (float)n;
+  float acc[VEC];
+  if (n >= kLongRow) {
+    // one row, every wave takes a share of its cells
+    const int64_t r = j;
+    const T* base = z + (o + r * n) * c_z + f * VEC;
+    row_partial<T>(acc, base, wave * CLW + cl, n, kWaves * CLW, c_z);
+#pragma unroll
+    for (int off = G; off < 64; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
+    if (cl == 0) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) part[wave][f * VEC + e] = acc[e];
+    }
+    __syncthreads();
+    if (wave == 0 && cl == 0) {
+      Vec16<float> out[VEC / 4];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        float s = part[0][f * VEC + e];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) s += part[w][f * VEC + e];
+        out[e / 4].set(e % 4, s / nf);
+      }
+      float* dst = m + (eta + r) * c_z + f * VEC;
+#pragma unroll
+      for (int q = 0; q < VEC / 4; ++q) store16(dst + 4 * q, out[q]);
+    }
+  } else {
+    // a group of whole rows; each wave reduces its own rows
+    const int64_t R = rows_per_item(n);
+    const int64_t r0 = j * R;
+    const int64_t r1 = r0 + R < n ? r0 + R : n;
+    for (int64_t r = r0 + wave; r < r1; r += kWaves) {
+      const T* base = z + (o + r * n) * c_z + f * VEC;
+      row_partial<T>(acc, base, cl, n, CLW, c_z);
+#pragma unroll
+      for (int off = G; off < 64; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
+      if (cl == 0) {
+        float* dst = m + (eta + r) * c_z + f * VEC;
+#pragma unroll
+        for (int q = 0; q < VEC / 4; ++q) {
+          Vec16<float> out;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out.set(e, acc[4 * q + e] / nf);
+          store16(dst + 4 * q, out);
+        }
+      }
+    }
+  }
+}
+
+// Any width: one thread per (pair row, 16-byte feature vector), summing the
+// row's cells in order.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_reduce_generic(
+    const T* __restrict__ z, float* __restrict__ m, const int64_t* __restrict__ row_splits,
+    const int32_t* __restrict__ row_sample, const int32_t* __restrict__ lengths, int64_t T_rows,
+    int c_z, int G) {
+  constexpr int VEC = Vec16<T>::N;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= T_rows * G) return;
+  const int64_t g = idx / G;
+  const int f = (int)(idx - g * G);
+  const int64_t n = lengths[row_sample[g]];
+  float acc[VEC];
+  row_partial<T>(acc, z + row_splits[g] * c_z + f * VEC, 0, n, 1, c_z);
+  float* dst = m + g * c_z + f * VEC;
+#pragma unroll
+  for (int q = 0; q < VEC / 4; ++q) {
+    Vec16<float> out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out.set(e, acc[4 * q + e] / (float)n);
+    store16(dst + 4 * q, out);
+  }
+}
+
+template <typename T, int G>
+hipError_t launch_pow2(const nt_partition& p, const void* z, float* m, int c_z,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL((k_reduce_pow2<T, G>), dim3((unsigned)p.n_items), dim3(kThreads), 0, stream,
+                     static_cast<const T*>(z), m, p.item_offsets, p.pair_offsets,
+                     p.single_offsets, p.lengths, p.B, c_z);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_t(const nt_partition& p, const void* z, float* m, int c_z, hipStream_t stream) {
+  const int G = c_z / Vec16<T>::N;
+  switch (G) {
+    case 1: return launch_pow2<T, 1>(p, z, m, c_z, stream);
+    case 2: return launch_pow2<T, 2>(p, z, m, c_z, stream);
+    case 4: return launch_pow2<T, 4>(p, z, m, c_z, stream);
+    case 8: return launch_pow2<T, 8>(p, z, m, c_z, stream);
+    case 16: return launch_pow2<T, 16>(p, z, m, c_z, stream);
+    case 32: return launch_pow2<T, 32>(p, z, m, c_z, stream);
+    case 64: return launch_pow2<T, 64>(p, z, m, c_z, stream);
+    default: break;
+  }
+  const int64_t total = p.T * G;
+  hipLaunchKernelGGL(k_reduce_generic<T>, dim3((unsigned)((total + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, stream, static_cast<const T*>(z), m, p.row_splits,
+                     p.row_sample, p.lengths, p.T, c_z, G);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const nt_partition& p, const void* z, float* m, int c_z, nt_dtype dtype,
+                         hipStream_t stream) {
+  if (p.T == 0) return hipSuccess;
+  if (dtype == NT_BF16) return launch_t<bf16>(p, z, m, c_z, stream);
+  return launch_t<float>(p, z, m, c_z, stream);
+}
+
+}  // namespace nt

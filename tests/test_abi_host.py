@@ -1,0 +1,177 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load and export every function include/nt_pair.h declares,
+size partitions like the oracle, and reject invalid arguments with the right
+status before anything is enqueued. No call here reaches a HIP launch: each
+argument set is invalid by construction.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from padding_free_pair_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nt_pair.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_native.LIB_PATH):
+        from padding_free_pair_amd import build
+        build.build(verbose=False)
+    return _native.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return set(re.findall(r"^\s*(?:nt_status|const char\s*\*|int32_t)\s+(nt_\w+)\s*\(", text,
+                          flags=re.M))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == set(_native.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _native.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = declared_functions() - exported
+    assert not missing, missing
+    for name in declared_functions():
+        assert hasattr(lib, name)
+    assert lib.nt_version() == 1
+
+
+def test_struct_layout_matches_header(lib):
+    # int32 x4, int64 x3, six pointers
+    assert ctypes.sizeof(_native.NtPartition) == 16 + 24 + 6 * 8
+    assert _native.NtPartition.lengths.offset == 40
+    assert ctypes.sizeof(_native.NtBlockWeights) == 5 * 8
+
+
+def _sizes(lib, lengths):
+    arr = np.ascontiguousarray(lengths, dtype=np.int32)
+    T, cells, nmax, nb = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32(), ctypes.c_size_t()
+    ptr = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if arr.size else None
+    st = lib.nt_partition_sizes(ptr, arr.size, ctypes.byref(T), ctypes.byref(cells),
+                                ctypes.byref(nmax), ctypes.byref(nb))
+    return st, T.value, cells.value, nmax.value, nb.value
+
+
+@pytest.mark.parametrize("lengths", [[2, 3], [7, 12, 5, 16], [0], [], [0, 0, 9, 0],
+                                     [1024, 768, 384, 96], list(range(300))])
+def test_partition_sizes_match_oracle(lib, lengths):
+    st, T, cells, nmax, nb = _sizes(lib, lengths)
+    p = oracle.partition(lengths)
+    assert st == 0
+    assert (T, cells, nmax) == (p["T"], p["cells"], p["n_max"])
+    assert nb >= 8 * (len(lengths) + 1) * 3 + 8 * (T + 1) + 4 * T
+
+
+def test_partition_sizes_errors(lib):
+    assert _sizes(lib, [3, -1])[0] == _native.NT_ERR_INVALID
+    assert "negative" in lib.nt_last_error().decode()
+    # sum of squares beyond the cell limit
+    assert _sizes(lib, [2 ** 31 - 1])[0] == _native.NT_ERR_OVERFLOW
+    # T beyond int32
+    assert _sizes(lib, [2 ** 30] * 3)[0] == _native.NT_ERR_OVERFLOW
+    assert lib.nt_partition_sizes(None, 2, None, None, None, None) == _native.NT_ERR_NULL
+    assert lib.nt_partition_sizes(None, -1, None, None, None, None) == _native.NT_ERR_INVALID
+    assert lib.nt_partition_sizes(None, 0, None, None, None, None) == _native.NT_OK
+
+
+def test_make_partition_rejects_before_launch(lib):
+    arr = np.array([2, 3], dtype=np.int32)
+    ptr = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    out = _native.NtPartition()
+    need = _sizes(lib, [2, 3])[4]
+    assert lib.nt_make_partition(ptr, 2, None, need, None, ctypes.byref(out)) == _native.NT_ERR_NULL
+    assert lib.nt_make_partition(ptr, 2, 0x10000 + 64, need, None,
+                                 ctypes.byref(out)) == _native.NT_ERR_ALIGN
+    assert lib.nt_make_partition(ptr, 2, 0x10000, need - 1, None,
+                                 ctypes.byref(out)) == _native.NT_ERR_WORKSPACE
+    assert lib.nt_make_partition(ptr, 2, 0x10000, need, None, None) == _native.NT_ERR_NULL
+    bad = np.array([2, -3], dtype=np.int32)
+    assert lib.nt_make_partition(bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 2, 0x10000,
+                                 need, None, ctypes.byref(out)) == _native.NT_ERR_INVALID
+    assert out.magic == 0  # untouched on failure
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation
+
+
+def fake_partition(B=2, T=5, cells=13):
+    p = _native.NtPartition()
+    p.magic = 0x4E545031
+    p.B, p.T, p.cells, p.n_items, p.n_max = B, T, cells, 2, 3
+    for k, name in enumerate(("lengths", "single_offsets", "pair_offsets", "row_splits",
+                              "row_sample", "item_offsets")):
+        setattr(p, name, FAKE + 0x1000 * k)
+    return p
+
+
+def test_stage_calls_validate(lib):
+    p = fake_partition()
+    P = ctypes.byref(p)
+    a, b, z = FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000
+    E = _native
+    # unbuilt partition
+    raw = _native.NtPartition()
+    assert lib.nt_pair_broadcast(ctypes.byref(raw), a, b, z, 16, 1, None) == E.NT_ERR_INVALID
+    assert lib.nt_pair_broadcast(None, a, b, z, 16, 1, None) == E.NT_ERR_NULL
+    # widths
+    for cz in (0, 12, -8, 520):
+        assert lib.nt_pair_broadcast(P, a, b, z, cz, 1, None) == E.NT_ERR_INVALID
+    assert lib.nt_pair_broadcast(P, a, b, z, 16, 7, None) == E.NT_ERR_DTYPE
+    assert lib.nt_pair_broadcast(P, None, b, z, 16, 1, None) == E.NT_ERR_NULL
+    assert lib.nt_pair_broadcast(P, a + 8, b, z, 16, 1, None) == E.NT_ERR_ALIGN
+    # z overlapping b
+    assert lib.nt_pair_broadcast(P, a, b, b + 16, 16, 1, None) == E.NT_ERR_INVALID
+    # transition
+    W1, W2 = FAKE + 0x400000, FAKE + 0x500000
+    assert lib.nt_pair_transition(P, z, z, W1, W2, 16, 12, 1, None) == E.NT_ERR_INVALID
+    assert lib.nt_pair_transition(P, z, z + 32, W1, W2, 16, 32, 1, None) == E.NT_ERR_INVALID
+    assert lib.nt_pair_transition(P, z, W1 + 16, W1, W2, 16, 32, 1, None) == E.NT_ERR_INVALID
+    assert lib.nt_pair_transition(P, z, z, None, W2, 16, 32, 1, None) == E.NT_ERR_NULL
+    # reduce
+    assert lib.nt_pair_reduce(P, z, None, 16, 1, None) == E.NT_ERR_NULL
+    assert lib.nt_pair_reduce(P, z, z + 16, 16, 1, None) == E.NT_ERR_INVALID
+    assert lib.nt_pair_reduce(P, z, a + 4, 16, 1, None) == E.NT_ERR_ALIGN
+    # decode
+    assert lib.nt_decode_cells(P, None, a, b, None) == E.NT_ERR_NULL
+
+
+def test_block_validates(lib):
+    p = fake_partition()
+    P = ctypes.byref(p)
+    s, so, z = FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000
+    w = _native.NtBlockWeights(FAKE + 0x400000, FAKE + 0x410000, FAKE + 0x420000,
+                               FAKE + 0x430000, FAKE + 0x440000)
+    ws = FAKE + 0x800000
+    need = ctypes.c_size_t()
+    assert lib.nt_block_workspace_bytes(P, 16, 16, 32, 1, ctypes.byref(need)) == 0
+    assert need.value >= 2 * 5 * 16 * 2 + 5 * 16 * 4
+    E = _native
+    W = ctypes.byref(w)
+    assert lib.nt_pair_block(P, s, so, z, W, 16, 16, 32, 1, ws, need.value - 1,
+                             None) == E.NT_ERR_WORKSPACE
+    assert lib.nt_pair_block(P, s, so, z, W, 16, 16, 32, 1, None, need.value,
+                             None) == E.NT_ERR_NULL
+    assert lib.nt_pair_block(P, s, so, z, None, 16, 16, 32, 1, ws, need.value,
+                             None) == E.NT_ERR_NULL
+    assert lib.nt_pair_block(P, s, s + 16, z, W, 16, 16, 32, 1, ws, need.value,
+                             None) == E.NT_ERR_INVALID
+    assert lib.nt_pair_block(P, s, so, ws, W, 16, 16, 32, 1, ws, need.value,
+                             None) == E.NT_ERR_INVALID
+    assert lib.nt_pair_block(P, s, so, z, W, 20, 16, 32, 1, ws, need.value,
+                             None) == E.NT_ERR_INVALID
+    w.W1 = None
+    assert lib.nt_pair_block(P, s, so, z, W, 16, 16, 32, 1, ws, need.value,
+                             None) == E.NT_ERR_NULL

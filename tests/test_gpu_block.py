@@ -1,0 +1,132 @@
+"""GPU parity of the whole block (nt_pair_block) and of the four-block chain
+against the float64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import pair_inputs as pin
+from gpu_util import announce, bits, expected_bits, f64, to_dev, weights_to_dev
+from helpers import TOL, scaled_max_err
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def nt():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import padding_free_pair_amd as nt
+    nt._native.lib()
+    return nt
+
+
+def _w64(w):
+    return {k: v.f64 for k, v in w.items()}
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_block_small_workloads_full(nt, idx):
+    x = pin.workload_inputs(idx)
+    L = x.lengths.tolist()
+    announce(f"block workload {x.name}")
+    p = nt.nt_make_partition(L)
+    s_out, z_out = nt.nt_pair_block(p, to_dev(x.s, torch), weights_to_dev(x.weights[0], torch))
+    torch.cuda.synchronize()
+    ref_s, ref_z = oracle.block(L, x.s.f64, _w64(x.weights[0]))
+    tol = TOL[x.dtype]
+    assert scaled_max_err(f64(z_out, torch), ref_z) <= tol
+    assert scaled_max_err(f64(s_out, torch), ref_s) <= tol
+
+
+@pytest.mark.parametrize("lengths,c_s,c_z,hidden,dtype", [
+    ([3, 0, 9, 1], 32, 128, 512, "bf16"),
+    ([0], 16, 64, 128, "bf16"),
+    ([5, 70], 48, 24, 40, "bf16"),
+    ([6, 2], 24, 16, 8, "f32"),
+    ([300], 64, 64, 128, "bf16"),
+])
+def test_block_edge_shapes(nt, lengths, c_s, c_z, hidden, dtype):
+    announce(f"block edge {dtype} {lengths} c_s={c_s} c_z={c_z} h={hidden}")
+    x = pin.make_inputs(lengths, c_s, c_z, hidden, dtype, seed=21)
+    p = nt.nt_make_partition(lengths)
+    s_out, z_out = nt.nt_pair_block(p, to_dev(x.s, torch), weights_to_dev(x.weights[0], torch))
+    torch.cuda.synchronize()
+    ref_s, ref_z = oracle.block(lengths, x.s.f64, _w64(x.weights[0]))
+    assert scaled_max_err(f64(z_out, torch), ref_z) <= TOL[dtype]
+    assert scaled_max_err(f64(s_out, torch), ref_s) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("c_z,hidden", [(128, 512), (64, 128), (16, 32)])
+def test_block_exact(nt, dtype, c_z, hidden):
+    lengths = [2, 4, 8, 16, 1]
+    announce(f"block exact {dtype} c_z={c_z}")
+    x = pin.exact_inputs(lengths, 32, c_z, hidden, dtype, seed=5)
+    p = nt.nt_make_partition(lengths)
+    sd = to_dev(x.s, torch)
+    s_out, z_out = nt.nt_pair_block(p, sd, weights_to_dev(x.weights[0], torch))
+    # in place on the singles gives the same bits
+    s_copy = sd.clone()
+    nt.nt_pair_block(p, s_copy, weights_to_dev(x.weights[0], torch), s_out=s_copy)
+    torch.cuda.synchronize()
+    ref_s, ref_z = oracle.block(lengths, x.s.f64, _w64(x.weights[0]))
+    np.testing.assert_array_equal(bits(z_out, torch), expected_bits(ref_z, dtype, oracle))
+    np.testing.assert_array_equal(bits(s_out, torch), expected_bits(ref_s, dtype, oracle))
+    np.testing.assert_array_equal(bits(s_copy, torch), bits(s_out, torch))
+
+
+def test_block_fused_matches_stages(nt):
+    # exact inputs: the fused broadcast prologue equals broadcast + transition
+    lengths = [4, 8, 16]
+    announce("block fused vs staged")
+    x = pin.exact_inputs(lengths, 32, 128, 512, "bf16", seed=8)
+    w = _w64(x.weights[0])
+    a = pin.store(oracle.project(x.s.f64, w["Wa"]), "bf16")
+    b = pin.store(oracle.project(x.s.f64, w["Wb"]), "bf16")
+    p = nt.nt_make_partition(lengths)
+    wd = weights_to_dev(x.weights[0], torch)
+    _, z_block = nt.nt_pair_block(p, to_dev(x.s, torch), wd)
+    z = nt.nt_pair_broadcast(p, to_dev(a, torch), to_dev(b, torch))
+    z_stage = nt.nt_pair_transition(p, z, wd["W1"], wd["W2"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(z_block, torch), bits(z_stage, torch))
+
+
+def _sampled_block_check(lengths, s_in64, w64, s_out, z_out, rng, n_cells=6000, n_rows=48):
+    o = oracle.partition(lengths)["pair_offsets"]
+    cells = int(o[-1])
+    ids = np.unique(np.concatenate([rng.integers(0, cells, n_cells), o[:-1], o[1:] - 1]))
+    got_z = f64(z_out[torch.from_numpy(ids).cuda()], torch)
+    ref_z = oracle.block_cells(lengths, s_in64, w64, ids)
+    T = sum(lengths)
+    eta = np.concatenate([[0], np.cumsum(lengths)])
+    rows = np.unique(np.concatenate([rng.integers(0, T, n_rows), eta[:-1], eta[1:] - 1]))
+    _, ref_s = oracle.block_rows(lengths, s_in64, w64, rows)
+    got_s = f64(s_out[torch.from_numpy(rows).cuda()], torch)
+    return scaled_max_err(got_z, ref_z), scaled_max_err(got_s, ref_s)
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4])
+def test_chain_full_size_per_block(nt, idx):
+    """Each block of the four-block chain at full size, launched as the
+    benchmark launches it, against the oracle on that block's GPU inputs."""
+    x = pin.workload_inputs(idx)
+    L = x.lengths.tolist()
+    p = nt.nt_make_partition(L)
+    rng = np.random.default_rng(idx)
+    s = to_dev(x.s, torch)
+    z_out = torch.empty((p.cells, x.c_z), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(nt.nt_block_workspace_bytes(p, x.c_s, x.c_z, x.hidden, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    for k, wk in enumerate(x.weights):
+        announce(f"chain {x.name} block {k}")
+        s_in64 = f64(s, torch)
+        s_next = torch.empty_like(s)
+        nt.nt_pair_block(p, s, weights_to_dev(wk, torch), s_out=s_next, z_out=z_out,
+                         workspace=ws)
+        torch.cuda.synchronize()
+        ez, es = _sampled_block_check(L, s_in64, _w64(wk), s_next, z_out, rng)
+        assert ez <= TOL["bf16"], (k, ez)
+        assert es <= TOL["bf16"], (k, es)
+        s = s_next

@@ -1,0 +1,183 @@
+"""GPU parity of the three pair stages (broadcast, transition, column mean)
+against the float64 oracle, on the same seeded inputs."""
+import numpy as np
+import pytest
+
+import oracle
+import pair_inputs as pin
+from gpu_util import announce, bits, expected_bits, f64, to_dev
+from helpers import TOL, scaled_max_err
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+TINY = [7, 12, 5, 16]                                  # 474 cells: ragged tail of every tile
+ONE_BLOCK = pin.workload_inputs(1, blocks=0).lengths.tolist()
+HIGH_VAR = pin.workload_inputs(3, blocks=0).lengths.tolist()
+LONG = [1024, 768, 384, 96]
+EDGE = [0, 3, 0, 1, 17, 0]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def nt():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import padding_free_pair_amd as nt
+    nt._native.lib()
+    return nt
+
+
+def _guarded(n_rows, width, dtype, pad=64, fill=-7.0):
+    """A tensor with sentinel rows around it; returns (full, view)."""
+    full = torch.full((n_rows + 2 * pad, width), fill, dtype=dtype, device="cuda")
+    return full, full[pad:pad + n_rows]
+
+
+def _check_guard(full, pad, n_rows, fill=-7.0):
+    f = full.float().cpu()
+    assert (f[:pad] == fill).all() and (f[pad + n_rows:] == fill).all(), "write outside output"
+
+
+TD = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+# ------------------------------------------------------------------ broadcast
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("lengths,c_z", [(TINY, 8), (TINY, 24), (ONE_BLOCK, 64), (EDGE, 128),
+                                         (HIGH_VAR, 128), ([300], 512), ([1] * 70, 16)])
+def test_broadcast_bit_exact(nt, lengths, c_z, dtype):
+    announce(f"broadcast {dtype} c_z={c_z} B={len(lengths)}")
+    T = sum(lengths)
+    a = pin.random_rows(T, c_z, dtype, seed=1)
+    b = pin.random_rows(T, c_z, dtype, seed=2, scale=3.0)
+    p = nt.nt_make_partition(lengths)
+    full, z = _guarded(p.cells, c_z, TD[dtype])
+    nt.nt_pair_broadcast(p, to_dev(a, torch), to_dev(b, torch), z)
+    torch.cuda.synchronize()
+    _check_guard(full, 64, p.cells)
+    want = expected_bits(oracle.broadcast(lengths, a.f64, b.f64), dtype, oracle)
+    np.testing.assert_array_equal(bits(z, torch), want)
+
+
+def test_broadcast_full_size_sampled(nt):
+    lengths, c_z = LONG, 128
+    announce("broadcast full size, long square lengths")
+    T = sum(lengths)
+    a = pin.random_rows(T, c_z, "bf16", seed=3)
+    b = pin.random_rows(T, c_z, "bf16", seed=4)
+    p = nt.nt_make_partition(lengths)
+    z = nt.nt_pair_broadcast(p, to_dev(a, torch), to_dev(b, torch))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    o = oracle.partition(lengths)["pair_offsets"]
+    ids = np.unique(np.concatenate([rng.integers(0, p.cells, 20000), o[:-1], o[1:] - 1,
+                                    o[:-1] + lengths]))
+    got = bits(z[torch.from_numpy(ids).cuda()], torch)
+    want = oracle.bf16_bits(oracle.broadcast_cells(lengths, a.f64, b.f64, ids))
+    np.testing.assert_array_equal(got, want)
+
+
+# ----------------------------------------------------------------- transition
+def _mlp(c_z, hidden, dtype, seed):
+    W1 = pin.random_rows(hidden, c_z, dtype, seed=seed, scale=1.0 / np.sqrt(c_z))
+    W2 = pin.random_rows(c_z, hidden, dtype, seed=seed + 1, scale=1.0 / np.sqrt(hidden))
+    return W1, W2
+
+
+@pytest.mark.parametrize("lengths,c_z,hidden,dtype", [
+    (TINY, 128, 512, "bf16"),        # MFMA path, ragged tail
+    ([40, 3], 128, 512, "bf16"),
+    (ONE_BLOCK, 64, 128, "bf16"),    # MFMA path, one-block widths
+    (EDGE, 64, 96, "bf16"),
+    (TINY, 48, 40, "bf16"),          # generic path
+    (TINY, 8, 16, "f32"),            # tiny fp32 widths
+    ([20, 9], 32, 64, "f32"),
+    ([11], 128, 512, "f32"),
+])
+def test_transition_parity(nt, lengths, c_z, hidden, dtype):
+    announce(f"transition {dtype} c_z={c_z} hidden={hidden} B={len(lengths)}")
+    cells = int(np.sum(np.square(lengths)))
+    z = pin.random_pair_rows(lengths, c_z, dtype, seed=5)
+    W1, W2 = _mlp(c_z, hidden, dtype, seed=6)
+    p = nt.nt_make_partition(lengths)
+    zd = to_dev(z, torch)
+    full, out = _guarded(cells, c_z, TD[dtype])
+    nt.nt_pair_transition(p, zd, to_dev(W1, torch), to_dev(W2, torch), z_out=out)
+    # in place gives the same bits
+    nt.nt_pair_transition(p, zd, to_dev(W1, torch), to_dev(W2, torch), z_out=zd)
+    torch.cuda.synchronize()
+    _check_guard(full, 64, cells)
+    np.testing.assert_array_equal(bits(out, torch), bits(zd, torch))
+    ref = oracle.transition(z.f64, W1.f64, W2.f64)
+    err = scaled_max_err(f64(out, torch), ref)
+    assert err <= TOL[dtype], err
+
+
+def test_transition_full_size_sampled(nt):
+    lengths, c_z, hidden = LONG, 128, 512
+    announce("transition full size, long square lengths")
+    z = pin.random_pair_rows(lengths, c_z, "bf16", seed=7)
+    W1, W2 = _mlp(c_z, hidden, "bf16", seed=8)
+    p = nt.nt_make_partition(lengths)
+    out = nt.nt_pair_transition(p, to_dev(z, torch), to_dev(W1, torch), to_dev(W2, torch))
+    torch.cuda.synchronize()
+    ids = np.unique(np.concatenate([np.random.default_rng(1).integers(0, p.cells, 30000),
+                                    np.arange(256), np.arange(p.cells - 300, p.cells)]))
+    got = f64(out[torch.from_numpy(ids).cuda()], torch)
+    ref = oracle.transition(z.f64[ids], W1.f64, W2.f64)
+    assert scaled_max_err(got, ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("c_z,hidden", [(128, 512), (64, 128), (16, 24)])
+def test_transition_exact(nt, dtype, c_z, hidden):
+    lengths = [2, 4, 8, 16, 1]
+    announce(f"transition exact {dtype} c_z={c_z}")
+    x = pin.exact_inputs(lengths, 16, c_z, hidden, dtype, seed=3)
+    w = {k: v.f64 for k, v in x.weights[0].items()}
+    z64 = oracle.broadcast(lengths, oracle.project(x.s.f64, w["Wa"]),
+                           oracle.project(x.s.f64, w["Wb"]))
+    zt = pin.store(z64, dtype)   # integers: exact in both dtypes
+    p = nt.nt_make_partition(lengths)
+    out = nt.nt_pair_transition(p, to_dev(zt, torch), to_dev(x.weights[0]["W1"], torch),
+                                to_dev(x.weights[0]["W2"], torch))
+    torch.cuda.synchronize()
+    want = expected_bits(oracle.transition(z64, w["W1"], w["W2"]), dtype, oracle)
+    np.testing.assert_array_equal(bits(out, torch), want)
+
+
+# ----------------------------------------------------------------- column mean
+@pytest.mark.parametrize("lengths,c_z,dtype", [
+    (LONG, 128, "bf16"), (HIGH_VAR, 128, "bf16"), (ONE_BLOCK, 64, "bf16"), (TINY, 8, "f32"),
+    (TINY, 24, "bf16"), (TINY, 24, "f32"), ([300, 5], 512, "bf16"), ([300, 5], 512, "f32"),
+    (EDGE, 128, "bf16"), ([255, 256, 257, 1], 64, "f32"), ([1], 8, "bf16"),
+])
+def test_reduce_parity(nt, lengths, c_z, dtype):
+    announce(f"reduce {dtype} c_z={c_z} B={len(lengths)}")
+    z = pin.random_pair_rows(lengths, c_z, dtype, seed=9)
+    p = nt.nt_make_partition(lengths)
+    full, m = _guarded(p.T, c_z, torch.float32)
+    zd = to_dev(z, torch)
+    nt.nt_pair_reduce(p, zd, m=m)
+    m2 = nt.nt_pair_reduce(p, zd)
+    torch.cuda.synchronize()
+    _check_guard(full, 64, p.T)
+    np.testing.assert_array_equal(bits(m, torch), bits(m2, torch))  # deterministic
+    ref = oracle.reduce_mean(lengths, z.f64)
+    # inputs are exact in the storage type; only fp32 accumulation remains
+    assert scaled_max_err(f64(m, torch), ref) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("c_z", [128, 24])
+def test_reduce_exact(nt, dtype, c_z):
+    lengths = [2, 4, 8, 16, 1, 256, 512]
+    announce(f"reduce exact {dtype} c_z={c_z}")
+    rng = np.random.default_rng(11)
+    cells = int(np.sum(np.square(lengths)))
+    z = pin.store(rng.integers(-40, 41, (cells, c_z)).astype(np.float64), dtype)
+    p = nt.nt_make_partition(lengths)
+    m = nt.nt_pair_reduce(p, to_dev(z, torch))
+    torch.cuda.synchronize()
+    want = oracle.reduce_mean(lengths, z.f64).astype(np.float32).view(np.uint32)
+    np.testing.assert_array_equal(bits(m, torch), want)

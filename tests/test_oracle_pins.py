@@ -275,6 +275,10 @@ def test_sampled_forms_match_full_block():
     cells = np.array([0, 5, 80, 81, 276, len(zo) - 1])
     np.testing.assert_allclose(oracle.block_cells(lengths, x.s.f64, w, cells), zo[cells],
                                rtol=1e-13, atol=1e-13)
+    a = oracle.project(x.s.f64, w["Wa"])
+    b = oracle.project(x.s.f64, w["Wb"])
+    np.testing.assert_array_equal(oracle.broadcast_cells(lengths, a, b, cells),
+                                  oracle.broadcast(lengths, a, b)[cells])
     rows = np.array([0, 8, 9, 22, 27])
     m_full = oracle.reduce_mean(lengths, zo)
     m_r, s_r = oracle.block_rows(lengths, x.s.f64, w, rows)
