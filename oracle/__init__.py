@@ -45,5 +45,5 @@ unpinned.
 from .pair_block import (  # noqa: F401
     partition, decode_cells, broadcast, transition, reduce_mean, project,
     block, chain, block_padded_masked, block_gather, block_bruteforce,
-    round_bf16, bf16_bits, block_cells, block_rows, dense_block,
+    round_bf16, bf16_bits, block_cells, block_rows, dense_block, broadcast_cells,
 )

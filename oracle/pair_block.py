@@ -259,6 +259,14 @@ def block_bruteforce(lengths, s, w):
 
 
 # ---------------------------------------------- sampled evaluation (large)
+def broadcast_cells(lengths, a, b, cell_ids):
+    """broadcast() at selected packed cells only: a[eta_i + r] + b[eta_i + c]."""
+    p = partition(lengths)
+    sample, row, col = _decode_some(p, lengths, np.asarray(cell_ids, dtype=np.int64))
+    eta = p["single_offsets"][sample]
+    return np.asarray(a, dtype=np.float64)[eta + row] + np.asarray(b, dtype=np.float64)[eta + col]
+
+
 def block_cells(lengths, s, w, cell_ids):
     """z_out of one block at selected packed cells only (the transition is
     cell-local, so each cell needs just its row and column singles)."""
