@@ -163,9 +163,11 @@ nt_status nt_pair_transition(const nt_partition* p, const void* z_in, void* z_ou
 /*
  * Broadcast fused into the transition (Equation 1's first two lines in one
  * kernel): z_out[o_i + r N_i + c] = z + relu(z W1^T) W2^T with
- * z = a[eta_i + r] + b[eta_i + c] formed on chip (rounded to the storage
- * type exactly as nt_pair_broadcast rounds it) and never written to memory.
- * a, b: [T, c_z]; z_out: [cells, c_z]; W1, W2 as for nt_pair_transition.
+ * z = a[eta_i + r] + b[eta_i + c] formed on chip and never written to
+ * memory. a, b: fp32 [T, c_z] whatever `dtype` is (the projections' fp32
+ * results); z_out: [cells, c_z] of `dtype`; W1, W2 as for
+ * nt_pair_transition. With NT_BF16 the MLP reads z rounded to bf16 while the
+ * residual adds z in fp32, so the pair state is rounded once, on output.
  * This is the kernel nt_pair_block runs for these two stages. z_out must not
  * overlap a, b or the weights.
  */
@@ -193,8 +195,8 @@ nt_status nt_block_workspace_bytes(const nt_partition* p, int32_t c_s, int32_t c
  * broadcast fused into the transition's prologue, the column mean and the
  * output projection with its residual. Returns both outputs, as the paper's
  * block does: s_out [T, c_s] and z_out [cells, c_z]. s_out may equal s_in.
- * workspace: device, at least nt_block_workspace_bytes, 256-byte aligned;
- * it holds a, b and m between the stages.
+ * workspace: device, at least nt_block_workspace_bytes, 16-byte aligned;
+ * it holds a, b (fp32, unrounded projections) and m (fp32) between stages.
  */
 nt_status nt_pair_block(const nt_partition* p, const void* s_in, void* s_out, void* z_out,
                         const nt_block_weights* w, int32_t c_s, int32_t c_z, int32_t hidden,

@@ -198,16 +198,21 @@ def nt_pair_transition(p: Partition, z_in, W1, W2, z_out=None, stream=None):
 
 
 def nt_pair_broadcast_transition(p: Partition, a, b, W1, W2, z_out=None, stream=None):
-    """z_out = z + relu(z W1^T) W2^T with z = a[row] + b[col] formed on chip."""
+    """z_out = z + relu(z W1^T) W2^T with z = a[row] + b[col] formed on chip.
+
+    a, b: float32 [T, c_z]; W1, W2 and z_out share the storage dtype.
+    """
     torch = _torch()
     c_z, hidden = a.shape[-1], W1.shape[0]
+    if a.dtype != torch.float32 or b.dtype != torch.float32:
+        raise TypeError("a and b must be float32")
     if z_out is None:
-        z_out = torch.empty((p.cells, c_z), dtype=a.dtype, device=a.device)
-    if not (a.dtype == b.dtype == W1.dtype == W2.dtype == z_out.dtype):
-        raise TypeError("a, b, weights and z_out must share a dtype")
+        z_out = torch.empty((p.cells, c_z), dtype=W1.dtype, device=a.device)
+    if not (W1.dtype == W2.dtype == z_out.dtype):
+        raise TypeError("weights and z_out must share a dtype")
     _check(_native.lib().nt_pair_broadcast_transition(
         ctypes.byref(p.struct), _ptr(a), _ptr(b), _ptr(z_out), _ptr(W1), _ptr(W2), c_z, hidden,
-        _dtype_code(a), _stream(stream, a.device)))
+        _dtype_code(W1), _stream(stream, a.device)))
     return z_out
 
 

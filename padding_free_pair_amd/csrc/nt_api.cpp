@@ -91,9 +91,10 @@ struct BlockWorkspace {
   uint64_t a, b, m, total;
 };
 
-BlockWorkspace block_workspace(int64_t T, int c_z, nt_dtype d) {
+// a and b are kept in fp32 (the projections' accumulators, unrounded), m too.
+BlockWorkspace block_workspace(int64_t T, int c_z, nt_dtype) {
   BlockWorkspace w;
-  const uint64_t ab = nt::align256((size_t)T * c_z * esize(d));
+  const uint64_t ab = nt::align256((size_t)T * c_z * sizeof(float));
   w.a = 0;
   w.b = ab;
   w.m = 2 * ab;
@@ -241,7 +242,7 @@ nt_status nt_pair_broadcast_transition(const nt_partition* p, const void* a, con
   NT_TRY(check_dtype(dtype));
   NT_TRY(check_width("c_z", c_z, nt::kMaxCz));
   NT_TRY(check_width("hidden", hidden, nt::kMaxHidden));
-  const uint64_t single = (uint64_t)p->T * c_z * esize(dtype);
+  const uint64_t single = (uint64_t)p->T * c_z * sizeof(float);
   const uint64_t pair = (uint64_t)p->cells * c_z * esize(dtype);
   const uint64_t wbytes = (uint64_t)hidden * c_z * esize(dtype);
   NT_TRY(check_array("a", a, single));
@@ -331,15 +332,18 @@ nt_status nt_pair_block(const nt_partition* p, const void* s_in, void* s_out, vo
   void* a = base + ws.a;
   void* b = base + ws.b;
   float* m = reinterpret_cast<float*>(base + ws.m);
-  NT_TRY(hip_status(nt::launch_linear(s_in, dtype, w->Wa, nullptr, a, dtype, p->T, c_z, c_s, s),
+  NT_TRY(hip_status(nt::launch_linear(s_in, dtype, w->Wa, dtype, nullptr, a, NT_F32, p->T, c_z,
+                                      c_s, s),
                     "projection a"));
-  NT_TRY(hip_status(nt::launch_linear(s_in, dtype, w->Wb, nullptr, b, dtype, p->T, c_z, c_s, s),
+  NT_TRY(hip_status(nt::launch_linear(s_in, dtype, w->Wb, dtype, nullptr, b, NT_F32, p->T, c_z,
+                                      c_s, s),
                     "projection b"));
   NT_TRY(hip_status(nt::launch_transition(*p, nullptr, a, b, z_out, w->W1, w->W2, c_z, hidden,
                                           dtype, s),
                     "fused broadcast + transition"));
   NT_TRY(hip_status(nt::launch_reduce(*p, z_out, m, c_z, dtype, s), "column mean"));
-  return hip_status(nt::launch_linear(m, NT_F32, w->Wo, s_in, s_out, dtype, p->T, c_s, c_z, s),
+  return hip_status(nt::launch_linear(m, NT_F32, w->Wo, dtype, s_in, s_out, dtype, p->T, c_s,
+                                      c_z, s),
                     "output projection");
 }
 

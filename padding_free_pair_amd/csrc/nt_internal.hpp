@@ -66,16 +66,19 @@ hipError_t launch_decode(const nt_partition& p, int32_t* sample, int32_t* row, i
                          hipStream_t stream);
 hipError_t launch_broadcast(const nt_partition& p, const void* a, const void* b, void* z, int c_z,
                             nt_dtype dtype, hipStream_t stream);
-// z_in == nullptr selects the fused form: z is formed from a and b in the prologue.
+// z_in == nullptr selects the fused form: z is formed from fp32 a and b in
+// the prologue (a, b are fp32 [T, c_z] whatever the storage dtype).
 bool transition_has_mfma(int c_z, int hidden, nt_dtype dtype);
 hipError_t launch_transition(const nt_partition& p, const void* z_in, const void* a, const void* b,
                              void* z_out, const void* W1, const void* W2, int c_z, int hidden,
                              nt_dtype dtype, hipStream_t stream);
 hipError_t launch_reduce(const nt_partition& p, const void* z, float* m, int c_z, nt_dtype dtype,
                          hipStream_t stream);
-// C[M, N] = (R ? R : 0) + A[M, K] W[N, K]^T. A is `a_dtype` (NT_F32 or the
-// block dtype), W, R and C are `dtype`.
-hipError_t launch_linear(const void* A, nt_dtype a_dtype, const void* W, const void* R, void* C,
-                         nt_dtype dtype, int64_t M, int N, int K, hipStream_t stream);
+// C[M, N] = (R ? R : 0) + A[M, K] W[N, K]^T with fp32 accumulation. R has
+// C's type. Supported (A, W, C) types: (bf16, bf16, f32), (f32, bf16, bf16),
+// (f32, f32, f32).
+hipError_t launch_linear(const void* A, nt_dtype a_dtype, const void* W, nt_dtype w_dtype,
+                         const void* R, void* C, nt_dtype c_dtype, int64_t M, int N, int K,
+                         hipStream_t stream);
 
 }  // namespace nt

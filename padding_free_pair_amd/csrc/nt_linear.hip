@@ -94,29 +94,31 @@ __global__ __launch_bounds__(64) void k_linear(const TA* __restrict__ A, const T
     }
 }
 
-template <typename TA, typename TW, bool BF16MMA>
+template <typename TA, typename TW, typename TO, bool BF16MMA>
 hipError_t launch_t(const void* A, const void* W, const void* R, void* C, int64_t M, int N, int K,
                     hipStream_t stream) {
   const dim3 grid((unsigned)((M + 31) / 32), (unsigned)((N + 31) / 32));
-  hipLaunchKernelGGL((k_linear<TA, TW, TW, BF16MMA>), grid, dim3(64), 0, stream,
+  hipLaunchKernelGGL((k_linear<TA, TW, TO, BF16MMA>), grid, dim3(64), 0, stream,
                      static_cast<const TA*>(A), static_cast<const TW*>(W),
-                     static_cast<const TW*>(R), static_cast<TW*>(C), M, N, K);
+                     static_cast<const TO*>(R), static_cast<TO*>(C), M, N, K);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_linear(const void* A, nt_dtype a_dtype, const void* W, const void* R, void* C,
-                         nt_dtype dtype, int64_t M, int N, int K, hipStream_t stream) {
+hipError_t launch_linear(const void* A, nt_dtype a_dtype, const void* W, nt_dtype w_dtype,
+                         const void* R, void* C, nt_dtype c_dtype, int64_t M, int N, int K,
+                         hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  if (dtype == NT_BF16) {
-    if (a_dtype == NT_BF16) {
-      if (K % 32 == 0) return launch_t<bf16, bf16, true>(A, W, R, C, M, N, K, stream);
-      return launch_t<bf16, bf16, false>(A, W, R, C, M, N, K, stream);
-    }
-    return launch_t<float, bf16, false>(A, W, R, C, M, N, K, stream);
+  if (a_dtype == NT_BF16 && w_dtype == NT_BF16 && c_dtype == NT_F32) {
+    if (K % 32 == 0) return launch_t<bf16, bf16, float, true>(A, W, R, C, M, N, K, stream);
+    return launch_t<bf16, bf16, float, false>(A, W, R, C, M, N, K, stream);
   }
-  return launch_t<float, float, false>(A, W, R, C, M, N, K, stream);
+  if (a_dtype == NT_F32 && w_dtype == NT_BF16 && c_dtype == NT_BF16)
+    return launch_t<float, bf16, bf16, false>(A, W, R, C, M, N, K, stream);
+  if (a_dtype == NT_F32 && w_dtype == NT_F32 && c_dtype == NT_F32)
+    return launch_t<float, float, float, false>(A, W, R, C, M, N, K, stream);
+  return hipErrorInvalidValue;  // combination not used by the block
 }
 
 }  // namespace nt

@@ -12,8 +12,10 @@
 // (lane = cell, 4 consecutive rows per lane group) the operand layout of the
 // second product after a lane-local relu + bf16 pack, so H never leaves the
 // registers. z stays in registers from prologue to epilogue; the residual is
-// added in fp32 and rounded once. With a and b given instead of z, the
-// broadcast a[row] + b[col] is formed in the prologue (fused form).
+// added in fp32 and rounded once. With fp32 a and b given instead of z, the
+// broadcast a[row] + b[col] is formed in the prologue (fused form): the MLP
+// reads it rounded to bf16 and the epilogue re-forms it in fp32 for the
+// residual, so the pair state is rounded once, on output.
 //
 // Generic path (any width, fp32 or bf16): plain fp32 arithmetic through LDS.
 #include "nt_device.hpp"
@@ -48,7 +50,7 @@ __device__ __forceinline__ int w2_row(int fb, int q) {
 
 template <int CZ, bool FUSED>
 __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_mfma(
-    const bf16* __restrict__ z_in, const bf16* __restrict__ a, const bf16* __restrict__ b,
+    const bf16* __restrict__ z_in, const float* __restrict__ a, const float* __restrict__ b,
     const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
     const int32_t* __restrict__ lengths, int B, const bf16* __restrict__ W1,
     const bf16* __restrict__ W2, bf16* z_out, int64_t cells, int hidden) {
@@ -69,20 +71,27 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_mfma(
 
   // ---- prologue: this lane's z slices, cell 16 cb + l16, features 32 kb + 8 g ..
   bf16x8 zb[kCellBlocks][KB];
+  int32_t arow[kCellBlocks], brow[kCellBlocks];  // fused form: single rows of the cell
 #pragma unroll
   for (int cb = 0; cb < kCellBlocks; ++cb) {
     const int64_t cell = cell0 + cb * 16 + l16;
+    arow[cb] = brow[cb] = 0;
     if (cell < cells) {
       if constexpr (FUSED) {
         const Cell x = decode_cell(pair_offsets, single_offsets, lengths, B, cell);
-        const bf16* ar = a + (x.eta + x.r) * CZ + 8 * g;
-        const bf16* br = b + (x.eta + x.c) * CZ + 8 * g;
+        arow[cb] = (int32_t)(x.eta + x.r);
+        brow[cb] = (int32_t)(x.eta + x.c);
+        const float* ar = a + (int64_t)arow[cb] * CZ + 8 * g;
+        const float* br = b + (int64_t)brow[cb] * CZ + 8 * g;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(ar + 32 * kb);
-          const bf16x8 vb = *reinterpret_cast<const bf16x8*>(br + 32 * kb);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) zb[cb][kb][e] = (bf16)((float)va[e] + (float)vb[e]);
+          for (int h = 0; h < 2; ++h) {
+            const f32x4 va = *reinterpret_cast<const f32x4*>(ar + 32 * kb + 4 * h);
+            const f32x4 vb = *reinterpret_cast<const f32x4*>(br + 32 * kb + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zb[cb][kb][4 * h + e] = (bf16)(va[e] + vb[e]);
+          }
         }
       } else {
         const bf16* zr = z_in + cell * CZ + 8 * g;
@@ -181,9 +190,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_mfma(
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       bf16x8 o;
+      if constexpr (FUSED) {
+        const float* ar = a + (int64_t)arow[cb] * CZ + 8 * g + 32 * kb;
+        const float* br = b + (int64_t)brow[cb] * CZ + 8 * g + 32 * kb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        o[e] = (bf16)((float)zb[cb][kb][e] + y[cb][2 * kb + (e >> 2)][e & 3]);
+        for (int h = 0; h < 2; ++h) {
+          const f32x4 va = *reinterpret_cast<const f32x4*>(ar + 4 * h);
+          const f32x4 vb = *reinterpret_cast<const f32x4*>(br + 4 * h);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[4 * h + e] = (bf16)((va[e] + vb[e]) + y[cb][2 * kb + h][e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          o[e] = (bf16)((float)zb[cb][kb][e] + y[cb][2 * kb + (e >> 2)][e & 3]);
+      }
       *reinterpret_cast<bf16x8*>(dst + 32 * kb) = o;
     }
   }
@@ -198,10 +219,11 @@ constexpr int kGenMaxAcc = kMaxCz / 16;  // features per thread at most
 // Thread (cell = tid / 16, lane16 = tid % 16) accumulates features
 // lane16 + 16 k of its cell. Per hidden chunk, the 16 x 32 activations are
 // formed in LDS (rounded to the storage type, as the bf16 fast path does),
-// then folded into the accumulators.
+// then folded into the accumulators. In the fused form z = a + b is kept in
+// fp32 for the residual and rounded to T where the MLP reads it.
 template <typename T, bool FUSED>
 __global__ __launch_bounds__(kGenThreads) void k_transition_generic(
-    const T* __restrict__ z_in, const T* __restrict__ a, const T* __restrict__ b,
+    const T* __restrict__ z_in, const float* __restrict__ a, const float* __restrict__ b,
     const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
     const int32_t* __restrict__ lengths, int B, const T* __restrict__ W1,
     const T* __restrict__ W2, T* z_out, int64_t cells, int c_z, int hidden) {
@@ -218,8 +240,7 @@ __global__ __launch_bounds__(kGenThreads) void k_transition_generic(
     if (t < cells) {
       if constexpr (FUSED) {
         const Cell x = decode_cell(pair_offsets, single_offsets, lengths, B, t);
-        v = to_f32(from_f32<T>(to_f32(a[(x.eta + x.r) * c_z + f]) +
-                               to_f32(b[(x.eta + x.c) * c_z + f])));
+        v = a[(x.eta + x.r) * c_z + f] + b[(x.eta + x.c) * c_z + f];
       } else {
         v = to_f32(z_in[t * c_z + f]);
       }
@@ -242,7 +263,7 @@ __global__ __launch_bounds__(kGenThreads) void k_transition_generic(
       if (hid < hidden) {
         const float* zr = zs + cl * c_z;
         const T* wr = W1 + (int64_t)hid * c_z;
-        for (int k = 0; k < c_z; ++k) v = fmaf(zr[k], to_f32(wr[k]), v);
+        for (int k = 0; k < c_z; ++k) v = fmaf(to_f32(from_f32<T>(zr[k])), to_f32(wr[k]), v);
         v = to_f32(from_f32<T>(fmaxf(v, 0.f)));
       }
       hs[p] = v;
@@ -287,8 +308,8 @@ hipError_t launch_mfma(const nt_partition& p, const void* z_in, const void* a, c
                        static_cast<bf16*>(z_out), p.cells, hidden);
   } else {
     hipLaunchKernelGGL((k_transition_mfma<CZ, true>), dim3((unsigned)blocks), dim3(kWaves * 64),
-                       0, stream, nullptr, static_cast<const bf16*>(a),
-                       static_cast<const bf16*>(b), p.pair_offsets, p.single_offsets, p.lengths,
+                       0, stream, nullptr, static_cast<const float*>(a),
+                       static_cast<const float*>(b), p.pair_offsets, p.single_offsets, p.lengths,
                        p.B, static_cast<const bf16*>(W1), static_cast<const bf16*>(W2),
                        static_cast<bf16*>(z_out), p.cells, hidden);
   }
@@ -309,8 +330,8 @@ hipError_t launch_generic(const nt_partition& p, const void* z_in, const void* a
                        static_cast<T*>(z_out), p.cells, c_z, hidden);
   } else {
     hipLaunchKernelGGL((k_transition_generic<T, true>), dim3((unsigned)blocks), dim3(kGenThreads),
-                       shmem, stream, nullptr, static_cast<const T*>(a),
-                       static_cast<const T*>(b), p.pair_offsets, p.single_offsets, p.lengths,
+                       shmem, stream, nullptr, static_cast<const float*>(a),
+                       static_cast<const float*>(b), p.pair_offsets, p.single_offsets, p.lengths,
                        p.B, static_cast<const T*>(W1), static_cast<const T*>(W2),
                        static_cast<T*>(z_out), p.cells, c_z, hidden);
   }

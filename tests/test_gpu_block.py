@@ -35,8 +35,10 @@ def test_block_small_workloads_full(nt, idx):
     torch.cuda.synchronize()
     ref_s, ref_z = oracle.block(L, x.s.f64, _w64(x.weights[0]))
     tol = TOL[x.dtype]
-    assert scaled_max_err(f64(z_out, torch), ref_z) <= tol
-    assert scaled_max_err(f64(s_out, torch), ref_s) <= tol
+    ez = scaled_max_err(f64(z_out, torch), ref_z)
+    es = scaled_max_err(f64(s_out, torch), ref_s)
+    announce(f"errors z={ez:.3e} s={es:.3e} (tol {tol})")
+    assert ez <= tol and es <= tol
 
 
 @pytest.mark.parametrize("lengths,c_s,c_z,hidden,dtype", [
@@ -127,6 +129,7 @@ def test_chain_full_size_per_block(nt, idx):
                          workspace=ws)
         torch.cuda.synchronize()
         ez, es = _sampled_block_check(L, s_in64, _w64(wk), s_next, z_out, rng)
+        announce(f"errors z={ez:.3e} s={es:.3e}")
         assert ez <= TOL["bf16"], (k, ez)
         assert es <= TOL["bf16"], (k, es)
         s = s_next

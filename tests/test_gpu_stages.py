@@ -181,3 +181,44 @@ def test_reduce_exact(nt, dtype, c_z):
     torch.cuda.synchronize()
     want = oracle.reduce_mean(lengths, z.f64).astype(np.float32).view(np.uint32)
     np.testing.assert_array_equal(bits(m, torch), want)
+
+
+# ------------------------------------------------- fused broadcast + transition
+@pytest.mark.parametrize("lengths,c_z,hidden,dtype", [
+    (TINY, 128, 512, "bf16"), (ONE_BLOCK, 64, 128, "bf16"), (EDGE, 48, 40, "bf16"),
+    (TINY, 8, 16, "f32"), ([9, 30], 32, 64, "f32"),
+])
+def test_broadcast_transition_parity(nt, lengths, c_z, hidden, dtype):
+    announce(f"broadcast+transition {dtype} c_z={c_z} hidden={hidden} B={len(lengths)}")
+    T = sum(lengths)
+    a = pin.random_rows(T, c_z, "f32", seed=12)
+    b = pin.random_rows(T, c_z, "f32", seed=13)
+    W1, W2 = _mlp(c_z, hidden, dtype, seed=14)
+    p = nt.nt_make_partition(lengths)
+    full, out = _guarded(p.cells, c_z, TD[dtype])
+    nt.nt_pair_broadcast_transition(p, to_dev(a, torch), to_dev(b, torch), to_dev(W1, torch),
+                                    to_dev(W2, torch), z_out=out)
+    torch.cuda.synchronize()
+    _check_guard(full, 64, p.cells)
+    ref = oracle.transition(oracle.broadcast(lengths, a.f64, b.f64), W1.f64, W2.f64)
+    assert scaled_max_err(f64(out, torch), ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("c_z,hidden", [(128, 512), (64, 128), (16, 24)])
+def test_broadcast_transition_exact(nt, dtype, c_z, hidden):
+    lengths = [2, 4, 8, 16, 1]
+    announce(f"broadcast+transition exact {dtype} c_z={c_z}")
+    x = pin.exact_inputs(lengths, 16, c_z, hidden, dtype, seed=4)
+    w = {k: v.f64 for k, v in x.weights[0].items()}
+    a64 = oracle.project(x.s.f64, w["Wa"])
+    b64 = oracle.project(x.s.f64, w["Wb"])
+    p = nt.nt_make_partition(lengths)
+    out = nt.nt_pair_broadcast_transition(p, to_dev(pin.store(a64, "f32"), torch),
+                                          to_dev(pin.store(b64, "f32"), torch),
+                                          to_dev(x.weights[0]["W1"], torch),
+                                          to_dev(x.weights[0]["W2"], torch))
+    torch.cuda.synchronize()
+    want = expected_bits(oracle.transition(oracle.broadcast(lengths, a64, b64), w["W1"], w["W2"]),
+                         dtype, oracle)
+    np.testing.assert_array_equal(bits(out, torch), want)
