@@ -243,6 +243,8 @@ def main():
     ap.add_argument("--quick", action="store_true",
                     help="timed steps and kernel timings only (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -259,6 +261,19 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+
+    if args.copy_reference:
+        # a plain copy kernel of known size: 1 GiB read + 1 GiB written per launch
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t = time_kernel(lambda: dst.copy_(src), 5, torch)
+        print(json.dumps({"copy_bytes_each_way": n * 4, "ms": t * 1e3,
+                          "GB/s (read+write)": 2 * n * 4 / t / 1e9}))
+        return
 
     w = pin.workload(args.workload)
     x = pin.workload_inputs(w.index)

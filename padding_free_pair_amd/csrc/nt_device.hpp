@@ -10,6 +10,7 @@ namespace nt {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // bf16 -> fp32 is exact; fp32 -> bf16 rounds to nearest-even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }

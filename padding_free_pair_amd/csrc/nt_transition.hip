@@ -210,6 +210,243 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_mfma(
   }
 }
 
+// ------------------------------------------------- persistent MFMA path
+// Throughput path for c_z in {64, 128} when W1 fits in LDS
+// (hidden * c_z * 2 bytes <= 128 KiB). v_mfma_f32_32x32x16_bf16 keeps the
+// matrix cores busy from a single wave per SIMD, which the 16x16 shape does
+// not. Organisation:
+//  * one workgroup (four waves) per CU, looping over 256-cell tiles; each
+//    wave owns 64 cells as two 32-cell MFMA column blocks;
+//  * W1 is loaded into LDS once per workgroup and stays resident;
+//  * W2 streams through a three-slot LDS ring, one 32-hidden chunk per step;
+//    its global loads are issued two steps before the ring slot is written;
+//  * each wave prefetches the next step's W2 fragments into registers, and
+//    the two GEMMs are skewed by one chunk: step j issues GEMM2 of chunk j - 1
+//    and GEMM1 of chunk j, one MFMA of each in turn.
+// Lane layouts of a 32x32x16 MFMA: operand lane l holds row / column l % 32
+// and k-group l / 32 (8 consecutive k); result element j of lane group
+// h = l / 32 is row 8 (j / 4) + 4 h + (j % 4) of column l % 32.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Result row rho of GEMM1 -> hidden unit within its 32-unit chunk, chosen so
+// that lane group h holds units 16 s + 8 h + (0..7) in elements 8 s .. 8 s + 7:
+// exactly the k-group of the second product's operand for its k-step s.
+__device__ __forceinline__ int p32_row(int rho) {
+  return 16 * (rho >> 4) + 8 * ((rho >> 2) & 1) + 4 * ((rho >> 3) & 1) + (rho & 3);
+}
+// GEMM2 feature block fb uses the same pattern over features 32 fb .. 32 fb + 31,
+// so result element j of lane group h is feature 16 (2 fb + j / 8) + 8 h + j % 8:
+// the feature the lane's z operand slice (k-step 2 fb + j / 8, slot j % 8) holds.
+
+template <int CZ, int HID, bool FUSED>
+__global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
+    const bf16* __restrict__ z_in, const float* __restrict__ a, const float* __restrict__ b,
+    const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
+    const int32_t* __restrict__ lengths, int B, const bf16* __restrict__ W1,
+    const bf16* __restrict__ W2, bf16* z_out, int64_t cells, int64_t ntiles) {
+  constexpr int KT = CZ / 16;        // GEMM1 k-steps
+  constexpr int FB = CZ / 32;        // GEMM2 feature blocks
+  constexpr int NCH = HID / kChunk;  // hidden chunks
+  constexpr int CB = kCellsPerWave / 32;
+  constexpr int THREADS = kWaves * 64;
+  constexpr int W1_PIECES = NCH * KT * 64;
+  constexpr int W2_PIECES = FB * 2 * 64;
+  constexpr int W2_PER_THREAD = W2_PIECES / THREADS;
+  constexpr int W1_PER_THREAD = W1_PIECES / THREADS;
+  constexpr int W1_BATCH = W1_PER_THREAD < 8 ? W1_PER_THREAD : 8;
+  static_assert(W2_PIECES % THREADS == 0 && W1_PIECES % THREADS == 0, "staging split");
+  static_assert(W1_PER_THREAD % W1_BATCH == 0, "W1 load batches");
+  static_assert(NCH >= 2 && CZ % 32 == 0, "shape");
+  // GEMM1 and GEMM2 each issue CB * KT MFMAs per step (CB * FB * 2 == CB * KT)
+  static_assert(FB * 2 == KT, "the two products interleave one to one");
+
+  __shared__ bf16x8 w1s[W1_PIECES];
+  __shared__ bf16x8 w2s[3][W2_PIECES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+
+  auto w1_src = [&](int p) -> const bf16* {
+    const int c = p / (KT * 64), t = (p >> 6) % KT, L = p & 63;
+    const int hid = c * kChunk + p32_row(L & 31);
+    return W1 + (int64_t)hid * CZ + 16 * t + 8 * (L >> 5);
+  };
+  auto w2_src = [&](int c, int p) -> const bf16* {
+    const int fb = p >> 7, s = (p >> 6) & 1, L = p & 63;
+    return W2 + (int64_t)(32 * fb + p32_row(L & 31)) * HID + c * kChunk + 16 * s + 8 * (L >> 5);
+  };
+
+  // resident W1 in fragment order (chunk, k-step, lane), batches of loads in flight
+  for (int k0 = 0; k0 < W1_PER_THREAD; k0 += W1_BATCH) {
+    bf16x8 tmp[W1_BATCH];
+#pragma unroll
+    for (int k = 0; k < W1_BATCH; ++k)
+      tmp[k] = *reinterpret_cast<const bf16x8*>(w1_src(tid + (k0 + k) * THREADS));
+#pragma unroll
+    for (int k = 0; k < W1_BATCH; ++k) w1s[tid + (k0 + k) * THREADS] = tmp[k];
+  }
+  // W2 stream. Stream position p carries chunk p % NCH. In the step that
+  // prefetches position P from ring slot rd into registers, the workgroup also
+  // issues the global loads of position P + 3 (into s_next) and stores
+  // position P + 2, loaded one step earlier (s_cur), into slot wr; so every
+  // load has two steps of MFMA work to arrive in.
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int k = 0; k < W2_PER_THREAD; ++k)
+      w2s[q][tid + k * THREADS] = *reinterpret_cast<const bf16x8*>(w2_src(q, tid + k * THREADS));
+  bf16x8 s_cur[W2_PER_THREAD];
+#pragma unroll
+  for (int k = 0; k < W2_PER_THREAD; ++k)
+    s_cur[k] = *reinterpret_cast<const bf16x8*>(w2_src(2 % NCH, tid + k * THREADS));
+  __syncthreads();
+  int rd = 0, wr = 2, ld = 3 % NCH;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t tile0 = tile * kTileCells;
+    const int64_t cell0 = tile0 + wave * kCellsPerWave;
+
+    // ---- prologue. The accumulator starts at z (fp32), so the epilogue only
+    // rounds and stores: y[cb][fb] element j is feature 16 (2 fb + j / 8) +
+    // 8 h + j % 8, the feature of operand slice zb[cb][2 fb + j / 8] slot j % 8.
+    bf16x8 zb[CB][KT];
+    f32x16 y[CB][FB];
+    int i0 = 0;
+    if constexpr (FUSED) i0 = find_segment(pair_offsets, 0, B, tile0);  // tile-uniform
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int64_t cell = cell0 + 32 * cb + l32;
+      if (cell < cells) {
+        if constexpr (FUSED) {
+          int i = i0;
+          while (pair_offsets[i + 1] <= cell) ++i;  // ends: pair_offsets[B] = cells > cell
+          const int64_t n = lengths[i], eta = single_offsets[i];
+          const int64_t local = cell - pair_offsets[i];
+          int64_t r, c;
+          if (n <= 65535) {
+            const uint32_t q32 = (uint32_t)local / (uint32_t)n;
+            r = q32;
+            c = (uint32_t)local - q32 * (uint32_t)n;
+          } else {
+            r = local / n;
+            c = local - r * n;
+          }
+          const float* ar = a + (eta + r) * CZ + 8 * h;
+          const float* br = b + (eta + c) * CZ + 8 * h;
+#pragma unroll
+          for (int t = 0; t < KT; ++t)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const f32x4 va = *reinterpret_cast<const f32x4*>(ar + 16 * t + 4 * u);
+              const f32x4 vb = *reinterpret_cast<const f32x4*>(br + 16 * t + 4 * u);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float zf = va[e] + vb[e];
+                zb[cb][t][4 * u + e] = (bf16)zf;
+                y[cb][t >> 1][8 * (t & 1) + 4 * u + e] = zf;
+              }
+            }
+        } else {
+          const bf16* zr = z_in + cell * CZ + 8 * h;
+#pragma unroll
+          for (int t = 0; t < KT; ++t) {
+            zb[cb][t] = *reinterpret_cast<const bf16x8*>(zr + 16 * t);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[cb][t >> 1][8 * (t & 1) + e] = (float)zb[cb][t][e];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            zb[cb][t][e] = (bf16)0.f;
+            y[cb][t >> 1][8 * (t & 1) + e] = 0.f;
+          }
+      }
+    }
+
+    bf16x8 w2f[FB][2];
+    bf16x8 hf[CB][2];
+
+    for (int j = 0; j <= NCH; ++j) {
+      const bool w2_step = j < NCH;  // steps 0..NCH-1 move the W2 stream
+      bf16x8 w1f[KT], w2n[FB][2];
+      bf16x8 s_next[W2_PER_THREAD];
+      if (j < NCH) {
+#pragma unroll
+        for (int t = 0; t < KT; ++t) w1f[t] = w1s[(j * KT + t) * 64 + lane];
+      }
+      if (w2_step) {
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) w2n[fb][s] = w2s[rd][(fb * 2 + s) * 64 + lane];
+#pragma unroll
+        for (int k = 0; k < W2_PER_THREAD; ++k)
+          s_next[k] = *reinterpret_cast<const bf16x8*>(w2_src(ld, tid + k * THREADS));
+      }
+
+      // GEMM2 of chunk j - 1 and GEMM1 of chunk j, one MFMA of each in turn
+      // (GEMM2 first: its operands are already in registers while W1's
+      // fragments arrive from LDS).
+      f32x16 hacc[CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) hacc[cb] = f32x16{};
+#pragma unroll
+      for (int k = 0; k < CB * KT; ++k) {
+        if (j > 0) {
+          const int s = k / (CB * FB), fb = (k / CB) % FB, cb = k % CB;
+          y[cb][fb] = mfma32(w2f[fb][s], hf[cb][s], y[cb][fb]);
+        }
+        if (j < NCH) {
+          const int t = k / CB, cb = k % CB;
+          hacc[cb] = mfma32(w1f[t], zb[cb][t], hacc[cb]);
+        }
+      }
+      if (j < NCH) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) hf[cb][s][e] = (bf16)fmaxf(hacc[cb][8 * s + e], 0.f);
+      }
+      if (w2_step) {
+#pragma unroll
+        for (int k = 0; k < W2_PER_THREAD; ++k) w2s[wr][tid + k * THREADS] = s_cur[k];
+        __syncthreads();
+        rd = rd == 2 ? 0 : rd + 1;
+        wr = wr == 2 ? 0 : wr + 1;
+        ld = ld + 1 == NCH ? 0 : ld + 1;
+#pragma unroll
+        for (int k = 0; k < W2_PER_THREAD; ++k) s_cur[k] = s_next[k];
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) w2f[fb][s] = w2n[fb][s];
+      }
+    }
+
+    // ---- epilogue: one rounding of z + Y, 16-byte stores
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int64_t cell = cell0 + 32 * cb + l32;
+      if (cell >= cells) continue;
+      bf16* dst = z_out + cell * CZ + 8 * h;
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        bf16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (bf16)y[cb][t >> 1][8 * (t & 1) + e];
+        *reinterpret_cast<bf16x8*>(dst + 16 * t) = o;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- generic path
 constexpr int kGenCells = 16;
 constexpr int kGenThreads = 256;
@@ -316,6 +553,42 @@ hipError_t launch_mfma(const nt_partition& p, const void* z_in, const void* a, c
   return hipGetLastError();
 }
 
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int CZ, int HID>
+hipError_t launch_persistent(const nt_partition& p, const void* z_in, const void* a,
+                             const void* b, void* z_out, const void* W1, const void* W2,
+                             hipStream_t stream) {
+  const int64_t ntiles = (p.cells + kTileCells - 1) / kTileCells;
+  const int64_t grid = ntiles < device_cus() ? ntiles : device_cus();
+  if (z_in) {
+    hipLaunchKernelGGL((k_transition_p32<CZ, HID, false>), dim3((unsigned)grid),
+                       dim3(kWaves * 64), 0, stream, static_cast<const bf16*>(z_in), nullptr,
+                       nullptr, p.pair_offsets, p.single_offsets, p.lengths, p.B,
+                       static_cast<const bf16*>(W1), static_cast<const bf16*>(W2),
+                       static_cast<bf16*>(z_out), p.cells, ntiles);
+  } else {
+    hipLaunchKernelGGL((k_transition_p32<CZ, HID, true>), dim3((unsigned)grid),
+                       dim3(kWaves * 64), 0, stream, nullptr, static_cast<const float*>(a),
+                       static_cast<const float*>(b), p.pair_offsets, p.single_offsets,
+                       p.lengths, p.B, static_cast<const bf16*>(W1),
+                       static_cast<const bf16*>(W2), static_cast<bf16*>(z_out), p.cells, ntiles);
+  }
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_generic(const nt_partition& p, const void* z_in, const void* a, const void* b,
                           void* z_out, const void* W1, const void* W2, int c_z, int hidden,
@@ -349,6 +622,10 @@ hipError_t launch_transition(const nt_partition& p, const void* z_in, const void
                              nt_dtype dtype, hipStream_t stream) {
   if (p.cells == 0) return hipSuccess;
   if (transition_has_mfma(c_z, hidden, dtype)) {
+    if (c_z == 128 && hidden == 512)
+      return launch_persistent<128, 512>(p, z_in, a, b, z_out, W1, W2, stream);
+    if (c_z == 64 && hidden == 128)
+      return launch_persistent<64, 128>(p, z_in, a, b, z_out, W1, W2, stream);
     if (c_z == 128) return launch_mfma<128>(p, z_in, a, b, z_out, W1, W2, hidden, stream);
     return launch_mfma<64>(p, z_in, a, b, z_out, W1, W2, hidden, stream);
   }
