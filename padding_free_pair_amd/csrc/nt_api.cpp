@@ -332,12 +332,8 @@ nt_status nt_pair_block(const nt_partition* p, const void* s_in, void* s_out, vo
   void* a = base + ws.a;
   void* b = base + ws.b;
   float* m = reinterpret_cast<float*>(base + ws.m);
-  NT_TRY(hip_status(nt::launch_linear(s_in, dtype, w->Wa, dtype, nullptr, a, NT_F32, p->T, c_z,
-                                      c_s, s),
-                    "projection a"));
-  NT_TRY(hip_status(nt::launch_linear(s_in, dtype, w->Wb, dtype, nullptr, b, NT_F32, p->T, c_z,
-                                      c_s, s),
-                    "projection b"));
+  NT_TRY(hip_status(nt::launch_linear2(s_in, dtype, w->Wa, w->Wb, a, b, p->T, c_z, c_s, s),
+                    "projections a, b"));
   NT_TRY(hip_status(nt::launch_transition(*p, nullptr, a, b, z_out, w->W1, w->W2, c_z, hidden,
                                           dtype, s),
                     "fused broadcast + transition"));

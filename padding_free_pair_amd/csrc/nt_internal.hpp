@@ -80,5 +80,9 @@ hipError_t launch_reduce(const nt_partition& p, const void* z, float* m, int c_z
 hipError_t launch_linear(const void* A, nt_dtype a_dtype, const void* W, nt_dtype w_dtype,
                          const void* R, void* C, nt_dtype c_dtype, int64_t M, int N, int K,
                          hipStream_t stream);
+// Two projections of one left operand in one launch: C0 = A W0^T, C1 = A W1^T
+// (fp32 results; A and the weights are `a_dtype`).
+hipError_t launch_linear2(const void* A, nt_dtype a_dtype, const void* W0, const void* W1,
+                          void* C0, void* C1, int64_t M, int N, int K, hipStream_t stream);
 
 }  // namespace nt
