@@ -240,11 +240,42 @@ __device__ __forceinline__ int p32_row(int rho) {
 // so result element j of lane group h is feature 16 (2 fb + j / 8) + 8 h + j % 8:
 // the feature the lane's z operand slice (k-step 2 fb + j / 8, slot j % 8) holds.
 
+// relu by the sign bit: a non-negative float has a non-negative integer image,
+// a negative one a negative image, so an integer max with 0 is max(x, +0).
+__device__ __forceinline__ float relu_bits(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
+// Samples whose partition arrays the fused persistent kernel keeps in LDS.
+constexpr int kLdsSamples = 384;
+
+// Sample, row and column of packed cell `cell` (Equation 3 inverted), with the
+// sample searched from `i0` upwards; po/eta/n are the pair offsets, single
+// offsets and lengths, in LDS or in global memory.
+template <typename OFF, typename IDX>
+__device__ __forceinline__ void decode_from(const OFF* po, const IDX* eta, const int32_t* n,
+                                            int i0, int64_t cell, int64_t& row, int64_t& col) {
+  int i = i0;
+  while (po[i + 1] <= cell) ++i;  // ends: po[B] = cells > cell
+  const int64_t len = n[i], local = cell - (int64_t)po[i];
+  int64_t r, c;
+  if (len <= 65535) {  // local < len^2 < 2^32
+    const uint32_t q32 = (uint32_t)local / (uint32_t)len;
+    r = q32;
+    c = (uint32_t)local - q32 * (uint32_t)len;
+  } else {
+    r = local / len;
+    c = local - r * len;
+  }
+  row = (int64_t)eta[i] + r;
+  col = (int64_t)eta[i] + c;
+}
+
 template <int CZ, int HID, bool FUSED>
 __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
     const bf16* __restrict__ z_in, const float* __restrict__ a, const float* __restrict__ b,
     const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
-    const int32_t* __restrict__ lengths, int B, const bf16* __restrict__ W1,
+    const int32_t* __restrict__ lengths, int B, bool lds_part, const bf16* __restrict__ W1,
     const bf16* __restrict__ W2, bf16* z_out, int64_t cells, int64_t ntiles) {
   constexpr int KT = CZ / 16;        // GEMM1 k-steps
   constexpr int FB = CZ / 32;        // GEMM2 feature blocks
@@ -264,6 +295,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
 
   __shared__ bf16x8 w1s[W1_PIECES];
   __shared__ bf16x8 w2s[3][W2_PIECES];
+  __shared__ int64_t po_s[FUSED ? kLdsSamples + 1 : 1];
+  __shared__ int32_t eta_s[FUSED ? kLdsSamples : 1];
+  __shared__ int32_t n_s[FUSED ? kLdsSamples : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -279,6 +313,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
     return W2 + (int64_t)(32 * fb + p32_row(L & 31)) * HID + c * kChunk + 16 * s + 8 * (L >> 5);
   };
 
+  if constexpr (FUSED) {
+    if (lds_part) {  // B <= kLdsSamples and every single offset fits in 32 bits
+      for (int i = tid; i <= B; i += THREADS) {
+        po_s[i] = pair_offsets[i];
+        if (i < B) {
+          eta_s[i] = (int32_t)single_offsets[i];
+          n_s[i] = lengths[i];
+        }
+      }
+    }
+  }
   // resident W1 in fragment order (chunk, k-step, lane), batches of loads in flight
   for (int k0 = 0; k0 < W1_PER_THREAD; k0 += W1_BATCH) {
     bf16x8 tmp[W1_BATCH];
@@ -289,7 +334,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
     for (int k = 0; k < W1_BATCH; ++k) w1s[tid + (k0 + k) * THREADS] = tmp[k];
   }
   // W2 stream. Stream position p carries chunk p % NCH. In the step that
-  // prefetches position P from ring slot rd into registers, the workgroup also
+  // reads position P from ring slot rd into registers, the workgroup also
   // issues the global loads of position P + 3 (into s_next) and stores
   // position P + 2, loaded one step earlier (s_cur), into slot wr; so every
   // load has two steps of MFMA work to arrive in.
@@ -303,6 +348,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
   for (int k = 0; k < W2_PER_THREAD; ++k)
     s_cur[k] = *reinterpret_cast<const bf16x8*>(w2_src(2 % NCH, tid + k * THREADS));
   __syncthreads();
+
+  // Fragments are read from LDS one step before the MFMAs that use them:
+  // w1f holds W1 of the chunk the next GEMM1 multiplies, w2f the W2 of the
+  // chunk the next GEMM2 multiplies.
+  bf16x8 w1f[KT], w2f[FB][2];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) w1f[t] = w1s[t * 64 + lane];
   int rd = 0, wr = 2, ld = 3 % NCH;
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int64_t tile0 = tile * kTileCells;
@@ -313,120 +365,126 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
     // 8 h + j % 8, the feature of operand slice zb[cb][2 fb + j / 8] slot j % 8.
     bf16x8 zb[CB][KT];
     f32x16 y[CB][FB];
-    int i0 = 0;
-    if constexpr (FUSED) i0 = find_segment(pair_offsets, 0, B, tile0);  // tile-uniform
+    if constexpr (FUSED) {
+      int64_t row[CB], col[CB];
+      if (lds_part) {
+        const int i0 = find_segment(po_s, 0, B, tile0);  // tile-uniform
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int64_t cell = cell0 + 32 * cb + l32;
-      if (cell < cells) {
-        if constexpr (FUSED) {
-          int i = i0;
-          while (pair_offsets[i + 1] <= cell) ++i;  // ends: pair_offsets[B] = cells > cell
-          const int64_t n = lengths[i], eta = single_offsets[i];
-          const int64_t local = cell - pair_offsets[i];
-          int64_t r, c;
-          if (n <= 65535) {
-            const uint32_t q32 = (uint32_t)local / (uint32_t)n;
-            r = q32;
-            c = (uint32_t)local - q32 * (uint32_t)n;
-          } else {
-            r = local / n;
-            c = local - r * n;
-          }
-          const float* ar = a + (eta + r) * CZ + 8 * h;
-          const float* br = b + (eta + c) * CZ + 8 * h;
-#pragma unroll
-          for (int t = 0; t < KT; ++t)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const f32x4 va = *reinterpret_cast<const f32x4*>(ar + 16 * t + 4 * u);
-              const f32x4 vb = *reinterpret_cast<const f32x4*>(br + 16 * t + 4 * u);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float zf = va[e] + vb[e];
-                zb[cb][t][4 * u + e] = (bf16)zf;
-                y[cb][t >> 1][8 * (t & 1) + 4 * u + e] = zf;
-              }
-            }
-        } else {
-          const bf16* zr = z_in + cell * CZ + 8 * h;
-#pragma unroll
-          for (int t = 0; t < KT; ++t) {
-            zb[cb][t] = *reinterpret_cast<const bf16x8*>(zr + 16 * t);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[cb][t >> 1][8 * (t & 1) + e] = (float)zb[cb][t][e];
-          }
+        for (int cb = 0; cb < CB; ++cb) {
+          const int64_t cell = cell0 + 32 * cb + l32;
+          decode_from(po_s, eta_s, n_s, i0, cell < cells ? cell : cells - 1, row[cb], col[cb]);
         }
       } else {
+        const int i0 = find_segment(pair_offsets, 0, B, tile0);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const int64_t cell = cell0 + 32 * cb + l32;
+          decode_from(pair_offsets, single_offsets, lengths, i0, cell < cells ? cell : cells - 1,
+                      row[cb], col[cb]);
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        // a cell past the end repeats the last cell's inputs; it is not stored
+        const float* ar = a + row[cb] * CZ + 8 * h;
+        const float* br = b + col[cb] * CZ + 8 * h;
+        // all of the cell's gathers in flight before the first use
+        f32x4 va[KT][2], vb[KT][2];
 #pragma unroll
         for (int t = 0; t < KT; ++t)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            zb[cb][t][e] = (bf16)0.f;
-            y[cb][t >> 1][8 * (t & 1) + e] = 0.f;
+          for (int u = 0; u < 2; ++u) {
+            va[t][u] = *reinterpret_cast<const f32x4*>(ar + 16 * t + 4 * u);
+            vb[t][u] = *reinterpret_cast<const f32x4*>(br + 16 * t + 4 * u);
           }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float zf = va[t][u][e] + vb[t][u][e];
+              zb[cb][t][4 * u + e] = (bf16)zf;
+              y[cb][t >> 1][8 * (t & 1) + 4 * u + e] = zf;
+            }
+      }
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int64_t cell = cell0 + 32 * cb + l32;
+        const bf16* zr = z_in + (cell < cells ? cell : cells - 1) * CZ + 8 * h;
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+          zb[cb][t] = *reinterpret_cast<const bf16x8*>(zr + 16 * t);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[cb][t >> 1][8 * (t & 1) + e] = (float)zb[cb][t][e];
+        }
       }
     }
 
-    bf16x8 w2f[FB][2];
+    // Step j runs GEMM1 of chunk j into hacc[j & 1] while the relu of chunk
+    // j - 1 (hacc[(j - 1) & 1]) is packed into hf a few values at a time, then
+    // GEMM2 of chunk j - 1. Each fragment register is refilled from LDS for
+    // the next step right after the two MFMAs that read it, so the reads have
+    // the rest of the step to arrive. sched_barrier keeps this order.
+    f32x16 hacc[2][CB];
     bf16x8 hf[CB][2];
-
-    for (int j = 0; j <= NCH; ++j) {
-      const bool w2_step = j < NCH;  // steps 0..NCH-1 move the W2 stream
-      bf16x8 w1f[KT], w2n[FB][2];
-      bf16x8 s_next[W2_PER_THREAD];
-      if (j < NCH) {
 #pragma unroll
-        for (int t = 0; t < KT; ++t) w1f[t] = w1s[(j * KT + t) * 64 + lane];
+    for (int j = 0; j <= NCH; ++j) {
+      const int jn = j + 1 < NCH ? j + 1 : 0;  // W1 chunk of the next step
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        if (j < NCH) {
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            hacc[j & 1][cb] = mfma32(w1f[t], zb[cb][t], t == 0 ? f32x16{} : hacc[j & 1][cb]);
+          w1f[t] = w1s[(jn * KT + t) * 64 + lane];
+        }
+        if (j > 0) {  // relu of chunk j - 1: piece t of CB * 2 * 8 values
+          constexpr int PER = CB * 2 * 8 / KT;
+#pragma unroll
+          for (int q = 0; q < PER; ++q) {
+            const int v = t * PER + q, cb = v / 16, s = (v / 8) % 2, e = v % 8;
+            hf[cb][s][e] = (bf16)relu_bits(hacc[(j - 1) & 1][cb][8 * s + e]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (w2_step) {
+      if (j > 0) {
+#pragma unroll
+        for (int k = 0; k < 2 * FB; ++k) {
+          const int s = k / FB, fb = k % FB;
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) y[cb][fb] = mfma32(w2f[fb][s], hf[cb][s], y[cb][fb]);
+          if (j < NCH) w2f[fb][s] = w2s[rd][(fb * 2 + s) * 64 + lane];
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-          for (int s = 0; s < 2; ++s) w2n[fb][s] = w2s[rd][(fb * 2 + s) * 64 + lane];
+          for (int s = 0; s < 2; ++s) w2f[fb][s] = w2s[rd][(fb * 2 + s) * 64 + lane];
+      }
+      if (j < NCH) {
+        // W2 stream: global loads of position + 3, ring store of position + 2
+        bf16x8 s_next[W2_PER_THREAD];
 #pragma unroll
         for (int k = 0; k < W2_PER_THREAD; ++k)
           s_next[k] = *reinterpret_cast<const bf16x8*>(w2_src(ld, tid + k * THREADS));
-      }
-
-      // GEMM2 of chunk j - 1 and GEMM1 of chunk j, one MFMA of each in turn
-      // (GEMM2 first: its operands are already in registers while W1's
-      // fragments arrive from LDS).
-      f32x16 hacc[CB];
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) hacc[cb] = f32x16{};
-#pragma unroll
-      for (int k = 0; k < CB * KT; ++k) {
-        if (j > 0) {
-          const int s = k / (CB * FB), fb = (k / CB) % FB, cb = k % CB;
-          y[cb][fb] = mfma32(w2f[fb][s], hf[cb][s], y[cb][fb]);
-        }
-        if (j < NCH) {
-          const int t = k / CB, cb = k % CB;
-          hacc[cb] = mfma32(w1f[t], zb[cb][t], hacc[cb]);
-        }
-      }
-      if (j < NCH) {
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) hf[cb][s][e] = (bf16)fmaxf(hacc[cb][8 * s + e], 0.f);
-      }
-      if (w2_step) {
 #pragma unroll
         for (int k = 0; k < W2_PER_THREAD; ++k) w2s[wr][tid + k * THREADS] = s_cur[k];
+        // The reads of slot rd must stay above the barrier: the next step
+        // overwrites that slot. Plain loads may otherwise sink past the fence.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
         rd = rd == 2 ? 0 : rd + 1;
         wr = wr == 2 ? 0 : wr + 1;
         ld = ld + 1 == NCH ? 0 : ld + 1;
 #pragma unroll
         for (int k = 0; k < W2_PER_THREAD; ++k) s_cur[k] = s_next[k];
-#pragma unroll
-        for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-          for (int s = 0; s < 2; ++s) w2f[fb][s] = w2n[fb][s];
       }
     }
 
@@ -573,17 +631,18 @@ hipError_t launch_persistent(const nt_partition& p, const void* z_in, const void
                              hipStream_t stream) {
   const int64_t ntiles = (p.cells + kTileCells - 1) / kTileCells;
   const int64_t grid = ntiles < device_cus() ? ntiles : device_cus();
+  const bool lds_part = p.B <= kLdsSamples && p.T <= INT32_MAX;
   if (z_in) {
     hipLaunchKernelGGL((k_transition_p32<CZ, HID, false>), dim3((unsigned)grid),
                        dim3(kWaves * 64), 0, stream, static_cast<const bf16*>(z_in), nullptr,
-                       nullptr, p.pair_offsets, p.single_offsets, p.lengths, p.B,
+                       nullptr, p.pair_offsets, p.single_offsets, p.lengths, p.B, false,
                        static_cast<const bf16*>(W1), static_cast<const bf16*>(W2),
                        static_cast<bf16*>(z_out), p.cells, ntiles);
   } else {
     hipLaunchKernelGGL((k_transition_p32<CZ, HID, true>), dim3((unsigned)grid),
                        dim3(kWaves * 64), 0, stream, nullptr, static_cast<const float*>(a),
                        static_cast<const float*>(b), p.pair_offsets, p.single_offsets,
-                       p.lengths, p.B, static_cast<const bf16*>(W1),
+                       p.lengths, p.B, lds_part, static_cast<const bf16*>(W1),
                        static_cast<const bf16*>(W2), static_cast<bf16*>(z_out), p.cells, ntiles);
   }
   return hipGetLastError();
