@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
     const bf16* __restrict__ z_in, const float* __restrict__ a, const float* __restrict__ b,
     const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
     const int32_t* __restrict__ lengths, int B, bool lds_part, const bf16* __restrict__ W1,
-    const bf16* __restrict__ W2, bf16* z_out, int64_t cells, int64_t ntiles) {
+    const bf16* __restrict__ W2, bf16* z_out, int64_t cells, int64_t ntiles, int64_t T) {
   constexpr int KT = CZ / 16;        // GEMM1 k-steps
   constexpr int FB = CZ / 32;        // GEMM2 feature blocks
   constexpr int NCH = HID / kChunk;  // hidden chunks
@@ -292,9 +292,24 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
   static_assert(NCH >= 2 && CZ % 32 == 0, "shape");
   // GEMM1 and GEMM2 each issue CB * KT MFMAs per step (CB * FB * 2 == CB * KT)
   static_assert(FB * 2 == KT, "the two products interleave one to one");
+  // Between tiles the W2 ring is empty and each wave stages rows through its
+  // quarter of it: RB bytes of 32 rows per round, rows SR bytes apart (the
+  // 16-byte pad spreads a column of 16-byte reads over all banks). A 16-byte
+  // per-lane access covers LPR lanes per row and CPI rows, 1 KiB per wave.
+  constexpr int STAGE = 3 * W2_PIECES * 16 / kWaves;
+  constexpr int RB = CZ == 128 ? 128 : 64;
+  constexpr int SR = RB + 16;
+  constexpr int LPR = RB / 16;
+  constexpr int CPI = 64 / LPR;
+  constexpr int IPR = 32 / CPI;
+  constexpr int AROW = CZ * 4;       // bytes of one fp32 row of a or b
+  constexpr int NBR = AROW / RB;     // rounds per fp32 row
+  constexpr int NZR = 2 * CZ / RB;   // rounds per bf16 row
+  static_assert(32 * SR + (FUSED ? 2 * AROW : 0) <= STAGE, "staging fits in the ring");
+  static_assert(RB % 64 == 0 && IPR * CPI == 32, "staging geometry");
 
   __shared__ bf16x8 w1s[W1_PIECES];
-  __shared__ bf16x8 w2s[3][W2_PIECES];
+  __shared__ bf16x8 ring[3 * W2_PIECES];
   __shared__ int64_t po_s[FUSED ? kLdsSamples + 1 : 1];
   __shared__ int32_t eta_s[FUSED ? kLdsSamples : 1];
   __shared__ int32_t n_s[FUSED ? kLdsSamples : 1];
@@ -302,6 +317,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
+  const int prow = lane / LPR, pseg = 16 * (lane % LPR);  // coalesced-access coordinates
+  unsigned char* const stage = reinterpret_cast<unsigned char*>(ring) + wave * STAGE;
 
   auto w1_src = [&](int p) -> const bf16* {
     const int c = p / (KT * 64), t = (p >> 6) % KT, L = p & 63;
@@ -312,6 +329,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
     const int fb = p >> 7, s = (p >> 6) & 1, L = p & 63;
     return W2 + (int64_t)(32 * fb + p32_row(L & 31)) * HID + c * kChunk + 16 * s + 8 * (L >> 5);
   };
+  auto slot = [&](int s) -> bf16x8* { return ring + s * W2_PIECES; };
 
   if constexpr (FUSED) {
     if (lds_part) {  // B <= kLdsSamples and every single offset fits in 32 bits
@@ -333,20 +351,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
 #pragma unroll
     for (int k = 0; k < W1_BATCH; ++k) w1s[tid + (k0 + k) * THREADS] = tmp[k];
   }
-  // W2 stream. Stream position p carries chunk p % NCH. In the step that
-  // reads position P from ring slot rd into registers, the workgroup also
-  // issues the global loads of position P + 3 (into s_next) and stores
-  // position P + 2, loaded one step earlier (s_cur), into slot wr; so every
-  // load has two steps of MFMA work to arrive in.
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int k = 0; k < W2_PER_THREAD; ++k)
-      w2s[q][tid + k * THREADS] = *reinterpret_cast<const bf16x8*>(w2_src(q, tid + k * THREADS));
-  bf16x8 s_cur[W2_PER_THREAD];
-#pragma unroll
-  for (int k = 0; k < W2_PER_THREAD; ++k)
-    s_cur[k] = *reinterpret_cast<const bf16x8*>(w2_src(2 % NCH, tid + k * THREADS));
   __syncthreads();
 
   // Fragments are read from LDS one step before the MFMAs that use them:
@@ -355,10 +359,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
   bf16x8 w1f[KT], w2f[FB][2];
 #pragma unroll
   for (int t = 0; t < KT; ++t) w1f[t] = w1s[t * 64 + lane];
-  int rd = 0, wr = 2, ld = 3 % NCH;
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int64_t tile0 = tile * kTileCells;
     const int64_t cell0 = tile0 + wave * kCellsPerWave;
+
+    // W2 chunks 0..2 of this tile, in flight while the prologue runs. The
+    // stream restarts every tile (position j carries chunk j) so the ring is
+    // free for staging between tiles.
+    bf16x8 s0[W2_PER_THREAD], s1[W2_PER_THREAD], s_cur[W2_PER_THREAD];
+#pragma unroll
+    for (int k = 0; k < W2_PER_THREAD; ++k) {
+      s0[k] = *reinterpret_cast<const bf16x8*>(w2_src(0, tid + k * THREADS));
+      s1[k] = *reinterpret_cast<const bf16x8*>(w2_src(1, tid + k * THREADS));
+      s_cur[k] = *reinterpret_cast<const bf16x8*>(w2_src(2 % NCH, tid + k * THREADS));
+    }
 
     // ---- prologue. The accumulator starts at z (fp32), so the epilogue only
     // rounds and stores: y[cb][fb] element j is feature 16 (2 fb + j / 8) +
@@ -366,68 +380,156 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
     bf16x8 zb[CB][KT];
     f32x16 y[CB][FB];
     if constexpr (FUSED) {
-      int64_t row[CB], col[CB];
-      if (lds_part) {
-        const int i0 = find_segment(po_s, 0, B, tile0);  // tile-uniform
+      int row32[CB], col32[CB];
+      {
+        int64_t row[CB], col[CB];
+        if (lds_part) {
+          const int i0 = find_segment(po_s, 0, B, tile0);  // tile-uniform
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const int64_t cell = cell0 + 32 * cb + l32;
-          decode_from(po_s, eta_s, n_s, i0, cell < cells ? cell : cells - 1, row[cb], col[cb]);
+          for (int cb = 0; cb < CB; ++cb) {
+            const int64_t cell = cell0 + 32 * cb + l32;
+            decode_from(po_s, eta_s, n_s, i0, cell < cells ? cell : cells - 1, row[cb], col[cb]);
+          }
+        } else {
+          const int i0 = find_segment(pair_offsets, 0, B, tile0);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            const int64_t cell = cell0 + 32 * cb + l32;
+            decode_from(pair_offsets, single_offsets, lengths, i0,
+                        cell < cells ? cell : cells - 1, row[cb], col[cb]);
+          }
         }
-      } else {
-        const int i0 = find_segment(pair_offsets, 0, B, tile0);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const int64_t cell = cell0 + 32 * cb + l32;
-          decode_from(pair_offsets, single_offsets, lengths, i0, cell < cells ? cell : cells - 1,
-                      row[cb], col[cb]);
+        for (int cb = 0; cb < CB; ++cb) {  // T < 2^31 on this path
+          row32[cb] = (int)row[cb];
+          col32[cb] = (int)col[cb];
         }
       }
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         // a cell past the end repeats the last cell's inputs; it is not stored
-        const float* ar = a + row[cb] * CZ + 8 * h;
-        const float* br = b + col[cb] * CZ + 8 * h;
-        // all of the cell's gathers in flight before the first use
-        f32x4 va[KT][2], vb[KT][2];
+        const int row_first = __builtin_amdgcn_readfirstlane(
+            __builtin_amdgcn_readlane(row32[cb], 0));
+        const int row_last = __builtin_amdgcn_readfirstlane(
+            __builtin_amdgcn_readlane(row32[cb], 31));
+        if (row_last - row_first <= 1) {
+          // The cell block spans at most two rows of a (N >= 32 always does):
+          // both a rows and the 32 b rows go through LDS, loaded with
+          // coalesced 16-byte accesses and read back in the operand layout.
+          unsigned char* const sb = stage;
+          unsigned char* const sa = stage + 32 * SR;
+          f32x4 braw[NBR][IPR], araw;
+          int src[IPR];
 #pragma unroll
-        for (int t = 0; t < KT; ++t)
+          for (int k = 0; k < IPR; ++k) src[k] = __shfl(col32[cb], k * CPI + prow);
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            va[t][u] = *reinterpret_cast<const f32x4*>(ar + 16 * t + 4 * u);
-            vb[t][u] = *reinterpret_cast<const f32x4*>(br + 16 * t + 4 * u);
+          for (int q = 0; q < NBR; ++q)
+#pragma unroll
+            for (int k = 0; k < IPR; ++k)
+              braw[q][k] = *reinterpret_cast<const f32x4*>(
+                  b + (int64_t)src[k] * CZ + (q * RB + pseg) / 4);
+          constexpr int ALANES = 2 * AROW / 16;
+          if (lane < ALANES) {
+            int64_t ar = row_first + lane / (AROW / 16);
+            ar = ar < T ? ar : T - 1;
+            araw = *reinterpret_cast<const f32x4*>(a + ar * CZ + 4 * (lane % (AROW / 16)));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (lane < ALANES) *reinterpret_cast<f32x4*>(sa + 16 * lane) = araw;
+          const unsigned char* const my_a = sa + (row32[cb] - row_first) * AROW + 32 * h;
+#pragma unroll
+          for (int q = 0; q < NBR; ++q) {
+#pragma unroll
+            for (int k = 0; k < IPR; ++k)
+              *reinterpret_cast<f32x4*>(sb + (k * CPI + prow) * SR + pseg) = braw[q][k];
+#pragma unroll
+            for (int mm = 0; mm < RB / 64; ++mm) {
+              const int m = q * (RB / 64) + mm;
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const f32x4 vb =
+                    *reinterpret_cast<const f32x4*>(sb + l32 * SR + 64 * mm + 32 * h + 16 * u);
+                const f32x4 va = *reinterpret_cast<const f32x4*>(my_a + 64 * m + 16 * u);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float zf = va[e] + vb[e];
+                  zb[cb][m][4 * u + e] = (bf16)zf;
+                  y[cb][m >> 1][8 * (m & 1) + 4 * u + e] = zf;
+                }
+              }
+            }
+          }
+        } else {
+          // many short rows: direct gathers, all in flight before the first use
+          const float* ar = a + (int64_t)row32[cb] * CZ + 8 * h;
+          const float* br = b + (int64_t)col32[cb] * CZ + 8 * h;
+          f32x4 va[KT][2], vb[KT][2];
+#pragma unroll
+          for (int t = 0; t < KT; ++t)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              va[t][u] = *reinterpret_cast<const f32x4*>(ar + 16 * t + 4 * u);
+              vb[t][u] = *reinterpret_cast<const f32x4*>(br + 16 * t + 4 * u);
+            }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int t = 0; t < KT; ++t)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float zf = va[t][u][e] + vb[t][u][e];
+                zb[cb][t][4 * u + e] = (bf16)zf;
+                y[cb][t >> 1][8 * (t & 1) + 4 * u + e] = zf;
+              }
+        }
+      }
+    } else {
+      // z rows of a cell block are contiguous: coalesced loads through LDS
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        bf16x8 zraw[NZR][IPR];
+#pragma unroll
+        for (int r = 0; r < NZR; ++r)
+#pragma unroll
+          for (int k = 0; k < IPR; ++k) {
+            int64_t c = cell0 + 32 * cb + k * CPI + prow;
+            c = c < cells ? c : cells - 1;
+            zraw[r][k] = *reinterpret_cast<const bf16x8*>(z_in + c * CZ + (r * RB + pseg) / 2);
           }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < KT; ++t)
+        for (int r = 0; r < NZR; ++r) {
 #pragma unroll
-          for (int u = 0; u < 2; ++u)
+          for (int k = 0; k < IPR; ++k)
+            *reinterpret_cast<bf16x8*>(stage + (k * CPI + prow) * SR + pseg) = zraw[r][k];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float zf = va[t][u][e] + vb[t][u][e];
-              zb[cb][t][4 * u + e] = (bf16)zf;
-              y[cb][t >> 1][8 * (t & 1) + 4 * u + e] = zf;
-            }
-      }
-    } else {
+          for (int tt = 0; tt < RB / 32; ++tt) {
+            const int t = r * (RB / 32) + tt;
+            zb[cb][t] = *reinterpret_cast<const bf16x8*>(stage + l32 * SR + 32 * tt + 16 * h);
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int64_t cell = cell0 + 32 * cb + l32;
-        const bf16* zr = z_in + (cell < cells ? cell : cells - 1) * CZ + 8 * h;
-#pragma unroll
-        for (int t = 0; t < KT; ++t) {
-          zb[cb][t] = *reinterpret_cast<const bf16x8*>(zr + 16 * t);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) y[cb][t >> 1][8 * (t & 1) + e] = (float)zb[cb][t][e];
+            for (int e = 0; e < 8; ++e) y[cb][t >> 1][8 * (t & 1) + e] = (float)zb[cb][t][e];
+          }
         }
       }
     }
+
+    // Chunks 0 and 1 into their ring slots once every wave is done staging.
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < W2_PER_THREAD; ++k) {
+      slot(0)[tid + k * THREADS] = s0[k];
+      slot(1)[tid + k * THREADS] = s1[k];
+    }
+    __syncthreads();
 
     // Step j runs GEMM1 of chunk j into hacc[j & 1] while the relu of chunk
     // j - 1 (hacc[(j - 1) & 1]) is packed into hf a few values at a time, then
     // GEMM2 of chunk j - 1. Each fragment register is refilled from LDS for
     // the next step right after the two MFMAs that read it, so the reads have
-    // the rest of the step to arrive. sched_barrier keeps this order.
+    // the rest of the step to arrive. sched_barrier keeps this order. Ring
+    // slot j % 3 holds chunk j; step j stores chunk j + 2 (loaded one step
+    // earlier) and issues the loads of chunk j + 3.
     f32x16 hacc[2][CB];
     bf16x8 hf[CB][2];
 #pragma unroll
@@ -457,49 +559,62 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
           const int s = k / FB, fb = k % FB;
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) y[cb][fb] = mfma32(w2f[fb][s], hf[cb][s], y[cb][fb]);
-          if (j < NCH) w2f[fb][s] = w2s[rd][(fb * 2 + s) * 64 + lane];
+          if (j < NCH) w2f[fb][s] = slot(j % 3)[(fb * 2 + s) * 64 + lane];
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-          for (int s = 0; s < 2; ++s) w2f[fb][s] = w2s[rd][(fb * 2 + s) * 64 + lane];
+          for (int s = 0; s < 2; ++s) w2f[fb][s] = slot(0)[(fb * 2 + s) * 64 + lane];
       }
       if (j < NCH) {
-        // W2 stream: global loads of position + 3, ring store of position + 2
         bf16x8 s_next[W2_PER_THREAD];
+        if (j + 3 < NCH) {
 #pragma unroll
-        for (int k = 0; k < W2_PER_THREAD; ++k)
-          s_next[k] = *reinterpret_cast<const bf16x8*>(w2_src(ld, tid + k * THREADS));
+          for (int k = 0; k < W2_PER_THREAD; ++k)
+            s_next[k] = *reinterpret_cast<const bf16x8*>(w2_src(j + 3, tid + k * THREADS));
+        }
+        if (j + 2 < NCH) {
 #pragma unroll
-        for (int k = 0; k < W2_PER_THREAD; ++k) w2s[wr][tid + k * THREADS] = s_cur[k];
-        // The reads of slot rd must stay above the barrier: the next step
-        // overwrites that slot. Plain loads may otherwise sink past the fence.
+          for (int k = 0; k < W2_PER_THREAD; ++k) slot((j + 2) % 3)[tid + k * THREADS] = s_cur[k];
+        }
+        // The reads of slot j % 3 must stay above the barrier: the next step
+        // overwrites that slot (or, after the last step, the staging does).
+        // Plain loads may otherwise sink past the fence.
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        rd = rd == 2 ? 0 : rd + 1;
-        wr = wr == 2 ? 0 : wr + 1;
-        ld = ld + 1 == NCH ? 0 : ld + 1;
+        if (j + 3 < NCH) {
 #pragma unroll
-        for (int k = 0; k < W2_PER_THREAD; ++k) s_cur[k] = s_next[k];
+          for (int k = 0; k < W2_PER_THREAD; ++k) s_cur[k] = s_next[k];
+        }
       }
     }
 
-    // ---- epilogue: one rounding of z + Y, 16-byte stores
+    // ---- epilogue: one rounding of z + Y, staged through LDS so that each
+    // store writes whole 16-byte-aligned runs of consecutive cells' rows.
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const int64_t cell = cell0 + 32 * cb + l32;
-      if (cell >= cells) continue;
-      bf16* dst = z_out + cell * CZ + 8 * h;
 #pragma unroll
-      for (int t = 0; t < KT; ++t) {
-        bf16x8 o;
+      for (int r = 0; r < NZR; ++r) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (bf16)y[cb][t >> 1][8 * (t & 1) + e];
-        *reinterpret_cast<bf16x8*>(dst + 16 * t) = o;
+        for (int tt = 0; tt < RB / 32; ++tt) {
+          const int t = r * (RB / 32) + tt;
+          bf16x8 o;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = (bf16)y[cb][t >> 1][8 * (t & 1) + e];
+          *reinterpret_cast<bf16x8*>(stage + l32 * SR + 32 * tt + 16 * h) = o;
+        }
+#pragma unroll
+        for (int k = 0; k < IPR; ++k) {
+          const int c_in = k * CPI + prow;
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(stage + c_in * SR + pseg);
+          const int64_t cell = cell0 + 32 * cb + c_in;
+          if (cell < cells)
+            *reinterpret_cast<bf16x8*>(z_out + cell * CZ + (r * RB + pseg) / 2) = v;
+        }
       }
     }
   }
@@ -637,13 +752,14 @@ hipError_t launch_persistent(const nt_partition& p, const void* z_in, const void
                        dim3(kWaves * 64), 0, stream, static_cast<const bf16*>(z_in), nullptr,
                        nullptr, p.pair_offsets, p.single_offsets, p.lengths, p.B, false,
                        static_cast<const bf16*>(W1), static_cast<const bf16*>(W2),
-                       static_cast<bf16*>(z_out), p.cells, ntiles);
+                       static_cast<bf16*>(z_out), p.cells, ntiles, p.T);
   } else {
     hipLaunchKernelGGL((k_transition_p32<CZ, HID, true>), dim3((unsigned)grid),
                        dim3(kWaves * 64), 0, stream, nullptr, static_cast<const float*>(a),
                        static_cast<const float*>(b), p.pair_offsets, p.single_offsets,
                        p.lengths, p.B, lds_part, static_cast<const bf16*>(W1),
-                       static_cast<const bf16*>(W2), static_cast<bf16*>(z_out), p.cells, ntiles);
+                       static_cast<const bf16*>(W2), static_cast<bf16*>(z_out), p.cells, ntiles,
+                       p.T);
   }
   return hipGetLastError();
 }
@@ -681,9 +797,11 @@ hipError_t launch_transition(const nt_partition& p, const void* z_in, const void
                              nt_dtype dtype, hipStream_t stream) {
   if (p.cells == 0) return hipSuccess;
   if (transition_has_mfma(c_z, hidden, dtype)) {
-    if (c_z == 128 && hidden == 512)
+    // the persistent kernel keeps single indices in 32 bits
+    const bool small_t = p.T <= INT32_MAX;
+    if (small_t && c_z == 128 && hidden == 512)
       return launch_persistent<128, 512>(p, z_in, a, b, z_out, W1, W2, stream);
-    if (c_z == 64 && hidden == 128)
+    if (small_t && c_z == 64 && hidden == 128)
       return launch_persistent<64, 128>(p, z_in, a, b, z_out, W1, W2, stream);
     if (c_z == 128) return launch_mfma<128>(p, z_in, a, b, z_out, W1, W2, hidden, stream);
     return launch_mfma<64>(p, z_in, a, b, z_out, W1, W2, hidden, stream);
