@@ -405,83 +405,104 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
           col32[cb] = (int)col[cb];
         }
       }
+      // The gathers of both cell blocks are issued together: the 32 b rows of
+      // each in coalesced 16-byte accesses, and the two a rows its cells
+      // start in (a cell past the end repeats the last cell's inputs; it is
+      // not stored).
+      constexpr int ALANES = 2 * AROW / 16;
+      f32x4 braw[CB][NBR][IPR], araw[CB];
+      int row_first[CB];
+      bool two_rows[CB];
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        // a cell past the end repeats the last cell's inputs; it is not stored
-        const int row_first = __builtin_amdgcn_readfirstlane(
-            __builtin_amdgcn_readlane(row32[cb], 0));
-        const int row_last = __builtin_amdgcn_readfirstlane(
-            __builtin_amdgcn_readlane(row32[cb], 31));
-        if (row_last - row_first <= 1) {
-          // The cell block spans at most two rows of a (N >= 32 always does):
-          // both a rows and the 32 b rows go through LDS, loaded with
-          // coalesced 16-byte accesses and read back in the operand layout.
-          unsigned char* const sb = stage;
-          unsigned char* const sa = stage + 32 * SR;
-          f32x4 braw[NBR][IPR], araw;
+        row_first[cb] =
+            __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(row32[cb], 0));
+        const int row_last =
+            __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(row32[cb], 31));
+        two_rows[cb] = row_last - row_first[cb] <= 1;  // every block does when N >= 32
+        int src[IPR];
+#pragma unroll
+        for (int k = 0; k < IPR; ++k) src[k] = __shfl(col32[cb], k * CPI + prow);
+#pragma unroll
+        for (int q = 0; q < NBR; ++q)
+#pragma unroll
+          for (int k = 0; k < IPR; ++k)
+            braw[cb][q][k] = *reinterpret_cast<const f32x4*>(
+                b + (int64_t)src[k] * CZ + (q * RB + pseg) / 4);
+        const int al = lane % ALANES;  // lanes past ALANES repeat lower ones
+        int64_t ar = row_first[cb] + al / (AROW / 16);
+        ar = ar < T ? ar : T - 1;
+        araw[cb] = *reinterpret_cast<const f32x4*>(a + ar * CZ + 4 * (al % (AROW / 16)));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Per block: its b rows go through LDS round by round and are read back
+      // in the operand layout; the a terms come from the two staged a rows,
+      // or, for a block of many short rows, from a second pass of per-cell a
+      // rows through the same registers and LDS (fp32 addition commutes, so
+      // the order of the two terms does not change z).
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        unsigned char* const sb = stage;
+        unsigned char* const sa = stage + 32 * SR;
+        if (lane < ALANES) *reinterpret_cast<f32x4*>(sa + 16 * lane) = araw[cb];
+        const int dr = row32[cb] - row_first[cb];
+        const unsigned char* const my_a = sa + (dr == 1 ? AROW : 0) + 32 * h;
+#pragma unroll
+        for (int q = 0; q < NBR; ++q) {
+#pragma unroll
+          for (int k = 0; k < IPR; ++k)
+            *reinterpret_cast<f32x4*>(sb + (k * CPI + prow) * SR + pseg) = braw[cb][q][k];
+#pragma unroll
+          for (int mm = 0; mm < RB / 64; ++mm) {
+            const int m = q * (RB / 64) + mm;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const f32x4 vb =
+                  *reinterpret_cast<const f32x4*>(sb + l32 * SR + 64 * mm + 32 * h + 16 * u);
+              // read unconditionally (inside the staging area) and select
+              const f32x4 vs = *reinterpret_cast<const f32x4*>(my_a + 64 * m + 16 * u);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float zf = (two_rows[cb] ? vs[e] : 0.f) + vb[e];
+                zb[cb][m][4 * u + e] = (bf16)zf;
+                y[cb][m >> 1][8 * (m & 1) + 4 * u + e] = zf;
+              }
+            }
+          }
+        }
+        if (!two_rows[cb]) {
           int src[IPR];
 #pragma unroll
-          for (int k = 0; k < IPR; ++k) src[k] = __shfl(col32[cb], k * CPI + prow);
+          for (int k = 0; k < IPR; ++k) src[k] = __shfl(row32[cb], k * CPI + prow);
 #pragma unroll
           for (int q = 0; q < NBR; ++q)
 #pragma unroll
             for (int k = 0; k < IPR; ++k)
-              braw[q][k] = *reinterpret_cast<const f32x4*>(
-                  b + (int64_t)src[k] * CZ + (q * RB + pseg) / 4);
-          constexpr int ALANES = 2 * AROW / 16;
-          if (lane < ALANES) {
-            int64_t ar = row_first + lane / (AROW / 16);
-            ar = ar < T ? ar : T - 1;
-            araw = *reinterpret_cast<const f32x4*>(a + ar * CZ + 4 * (lane % (AROW / 16)));
-          }
+              braw[cb][q][k] = *reinterpret_cast<const f32x4*>(
+                  a + (int64_t)src[k] * CZ + (q * RB + pseg) / 4);
           __builtin_amdgcn_sched_barrier(0);
-          if (lane < ALANES) *reinterpret_cast<f32x4*>(sa + 16 * lane) = araw;
-          const unsigned char* const my_a = sa + (row32[cb] - row_first) * AROW + 32 * h;
 #pragma unroll
           for (int q = 0; q < NBR; ++q) {
 #pragma unroll
             for (int k = 0; k < IPR; ++k)
-              *reinterpret_cast<f32x4*>(sb + (k * CPI + prow) * SR + pseg) = braw[q][k];
+              *reinterpret_cast<f32x4*>(sb + (k * CPI + prow) * SR + pseg) = braw[cb][q][k];
 #pragma unroll
             for (int mm = 0; mm < RB / 64; ++mm) {
               const int m = q * (RB / 64) + mm;
 #pragma unroll
               for (int u = 0; u < 2; ++u) {
-                const f32x4 vb =
+                const f32x4 va =
                     *reinterpret_cast<const f32x4*>(sb + l32 * SR + 64 * mm + 32 * h + 16 * u);
-                const f32x4 va = *reinterpret_cast<const f32x4*>(my_a + 64 * m + 16 * u);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                  const float zf = va[e] + vb[e];
+                  const int j = 8 * (m & 1) + 4 * u + e;
+                  const float zf = y[cb][m >> 1][j] + va[e];
                   zb[cb][m][4 * u + e] = (bf16)zf;
-                  y[cb][m >> 1][8 * (m & 1) + 4 * u + e] = zf;
+                  y[cb][m >> 1][j] = zf;
                 }
               }
             }
           }
-        } else {
-          // many short rows: direct gathers, all in flight before the first use
-          const float* ar = a + (int64_t)row32[cb] * CZ + 8 * h;
-          const float* br = b + (int64_t)col32[cb] * CZ + 8 * h;
-          f32x4 va[KT][2], vb[KT][2];
-#pragma unroll
-          for (int t = 0; t < KT; ++t)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              va[t][u] = *reinterpret_cast<const f32x4*>(ar + 16 * t + 4 * u);
-              vb[t][u] = *reinterpret_cast<const f32x4*>(br + 16 * t + 4 * u);
-            }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int t = 0; t < KT; ++t)
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float zf = va[t][u][e] + vb[t][u][e];
-                zb[cb][t][4 * u + e] = (bf16)zf;
-                y[cb][t >> 1][8 * (t & 1) + 4 * u + e] = zf;
-              }
         }
       }
     } else {
@@ -607,13 +628,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
           for (int e = 0; e < 8; ++e) o[e] = (bf16)y[cb][t >> 1][8 * (t & 1) + e];
           *reinterpret_cast<bf16x8*>(stage + l32 * SR + 32 * tt + 16 * h) = o;
         }
+        bf16x8 v[IPR];
 #pragma unroll
-        for (int k = 0; k < IPR; ++k) {
-          const int c_in = k * CPI + prow;
-          const bf16x8 v = *reinterpret_cast<const bf16x8*>(stage + c_in * SR + pseg);
-          const int64_t cell = cell0 + 32 * cb + c_in;
-          if (cell < cells)
-            *reinterpret_cast<bf16x8*>(z_out + cell * CZ + (r * RB + pseg) / 2) = v;
+        for (int k = 0; k < IPR; ++k)
+          v[k] = *reinterpret_cast<const bf16x8*>(stage + (k * CPI + prow) * SR + pseg);
+        const int64_t blk0 = cell0 + 32 * cb;
+        if (blk0 + 32 <= cells) {  // every cell of the block is valid: no per-lane guards
+#pragma unroll
+          for (int k = 0; k < IPR; ++k)
+            *reinterpret_cast<bf16x8*>(z_out + (blk0 + k * CPI + prow) * CZ + (r * RB + pseg) / 2) =
+                v[k];
+        } else {
+#pragma unroll
+          for (int k = 0; k < IPR; ++k) {
+            const int64_t cell = blk0 + k * CPI + prow;
+            if (cell < cells)
+              *reinterpret_cast<bf16x8*>(z_out + cell * CZ + (r * RB + pseg) / 2) = v[k];
+          }
         }
       }
     }
