@@ -112,13 +112,14 @@ nt_status nt_partition_sizes(const int32_t* lengths, int32_t B, int64_t* T, int6
                              int32_t* n_max, size_t* buffer_bytes);
 
 /*
- * Builds the partition of Section 3.1 / Figure 2 for square pairs: the
- * lengths are copied from host memory into `buffer` on `stream` (pageable
- * memory is read before the call returns; page-locked memory is read
- * asynchronously and must stay unchanged until the stream passes this
- * call), then an
- * exclusive scan on the device produces eta, o and the item offsets, and a
- * second kernel fills row_splits and row_sample. `out` receives the host
+ * Builds the partition of Section 3.1 / Figure 2 for square pairs on the
+ * device: the exclusive scans giving eta, o and the item offsets, then
+ * row_splits and row_sample. The host lengths reach the device as kernel
+ * arguments when B <= 256 (one launch; the lengths are read before the call
+ * returns); larger batches copy them into `buffer` on `stream` first
+ * (pageable memory is read before the call returns; page-locked memory is
+ * read asynchronously and must stay unchanged until the stream passes this
+ * call) and use two launches. `out` receives the host
  * scalars and pointers into `buffer` immediately; the device arrays are
  * valid once the stream reaches this point. The partition stays valid while
  * `buffer` lives. buffer: device, at least nt_partition_sizes' buffer_bytes,

@@ -173,13 +173,17 @@ nt_status nt_make_partition(const int32_t* lengths, int32_t B, void* buffer, siz
   p.row_sample = d_rows;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (B > 0) {
+  if (B <= nt::kArgSamples) {
+    NT_TRY(hip_status(nt::launch_partition_small(lengths, p, d_lengths, d_eta, d_o, d_items,
+                                                 d_splits, d_rows, s),
+                      "partition kernel"));
+  } else {
     const hipError_t e =
         hipMemcpyAsync(d_lengths, lengths, sizeof(int32_t) * B, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_status(e, "copying lengths");
+    NT_TRY(hip_status(nt::launch_partition(p, d_eta, d_o, d_items, d_splits, d_rows, s),
+                      "partition kernels"));
   }
-  NT_TRY(hip_status(nt::launch_partition(p, d_eta, d_o, d_items, d_splits, d_rows, s),
-                    "partition kernels"));
   *out = p;
   return ok();
 }

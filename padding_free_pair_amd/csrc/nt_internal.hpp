@@ -62,6 +62,13 @@ inline PartitionLayout partition_layout(int64_t B, int64_t T) {
 hipError_t launch_partition(const nt_partition& p, int64_t* single_offsets, int64_t* pair_offsets,
                             int64_t* item_offsets, int64_t* row_splits, int32_t* row_sample,
                             hipStream_t stream);
+// Batches of at most kArgSamples samples: one launch, lengths passed by value
+// from host memory (read before the call returns).
+constexpr int kArgSamples = 256;
+hipError_t launch_partition_small(const int32_t* lengths_host, const nt_partition& p,
+                                  int32_t* lengths, int64_t* single_offsets, int64_t* pair_offsets,
+                                  int64_t* item_offsets, int64_t* row_splits, int32_t* row_sample,
+                                  hipStream_t stream);
 hipError_t launch_decode(const nt_partition& p, int32_t* sample, int32_t* row, int32_t* col,
                          hipStream_t stream);
 hipError_t launch_broadcast(const nt_partition& p, const void* a, const void* b, void* z, int c_z,

@@ -69,6 +69,62 @@ __global__ __launch_bounds__(256) void k_row_splits(
   row_sample[g] = i;
 }
 
+// Small batches in one launch: the lengths travel by value in the kernel
+// arguments (no host-to-device copy), every workgroup rescans them in LDS
+// (at most kArgSamples entries), workgroup 0 writes the per-sample arrays and
+// each workgroup fills 256 entries of the row splits.
+struct LengthsArg {
+  int32_t n[kArgSamples];
+};
+
+__global__ __launch_bounds__(kArgSamples) void k_partition_small(
+    LengthsArg len, int B, int64_t T, int32_t* __restrict__ lengths, int64_t* __restrict__ eta,
+    int64_t* __restrict__ o, int64_t* __restrict__ items, int64_t* __restrict__ row_splits,
+    int32_t* __restrict__ row_sample) {
+  __shared__ int64_t buf[2][3][kArgSamples];
+  __shared__ int64_t s_eta[kArgSamples + 1], s_o[kArgSamples + 1];
+  const int tid = threadIdx.x;
+  const int64_t n = tid < B ? (int64_t)len.n[tid] : 0;
+  const int64_t v[3] = {n, n * n, items_of(n)};
+  int cur = 0;
+  for (int q = 0; q < 3; ++q) buf[cur][q][tid] = v[q];
+  __syncthreads();
+  for (int off = 1; off < kArgSamples; off <<= 1) {
+    for (int q = 0; q < 3; ++q) {
+      int64_t x = buf[cur][q][tid];
+      if (tid >= off) x += buf[cur][q][tid - off];
+      buf[cur ^ 1][q][tid] = x;
+    }
+    cur ^= 1;
+    __syncthreads();
+  }
+  // exclusive offsets; entry B closes each array
+  s_eta[tid + 1] = buf[cur][0][tid];
+  s_o[tid + 1] = buf[cur][1][tid];
+  if (tid == 0) s_eta[0] = s_o[0] = 0;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    if (tid < B) {
+      lengths[tid] = (int32_t)n;
+      eta[tid] = s_eta[tid];
+      o[tid] = s_o[tid];
+      items[tid] = tid == 0 ? 0 : buf[cur][2][tid - 1];
+    }
+    if (tid == 0) {  // entry B closes each array (B may equal kArgSamples)
+      eta[B] = s_eta[B];
+      o[B] = s_o[B];
+      items[B] = B == 0 ? 0 : buf[cur][2][B - 1];
+    }
+  }
+  const int64_t g = (int64_t)blockIdx.x * kArgSamples + tid;
+  if (g == 0) row_splits[T] = s_o[B];
+  if (g < T) {
+    const int i = find_segment(s_eta, 0, B, g);
+    row_splits[g] = s_o[i] + (g - s_eta[i]) * (int64_t)len.n[i];
+    row_sample[g] = i;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_decode(
     const int64_t* __restrict__ o, const int64_t* __restrict__ eta,
     const int32_t* __restrict__ lengths, int B, int64_t cells, int32_t* __restrict__ sample,
@@ -93,6 +149,19 @@ hipError_t launch_partition(const nt_partition& p, int64_t* single_offsets, int6
   const int64_t blocks = p.T > 0 ? (p.T + 255) / 256 : 1;
   hipLaunchKernelGGL(k_row_splits, dim3((unsigned)blocks), dim3(256), 0, stream, p.lengths,
                      single_offsets, pair_offsets, p.B, p.T, row_splits, row_sample);
+  return hipGetLastError();
+}
+
+hipError_t launch_partition_small(const int32_t* lengths_host, const nt_partition& p,
+                                  int32_t* lengths, int64_t* single_offsets, int64_t* pair_offsets,
+                                  int64_t* item_offsets, int64_t* row_splits, int32_t* row_sample,
+                                  hipStream_t stream) {
+  LengthsArg arg;
+  for (int i = 0; i < kArgSamples; ++i) arg.n[i] = i < p.B ? lengths_host[i] : 0;
+  const int64_t blocks = p.T > 0 ? (p.T + kArgSamples - 1) / kArgSamples : 1;
+  hipLaunchKernelGGL(k_partition_small, dim3((unsigned)blocks), dim3(kArgSamples), 0, stream, arg,
+                     p.B, p.T, lengths, single_offsets, pair_offsets, item_offsets, row_splits,
+                     row_sample);
   return hipGetLastError();
 }
 

@@ -24,7 +24,9 @@ def _cases():
     ragged = rng.integers(0, 40, 1000)
     ragged[rng.choice(1000, 200, replace=False)] = 0
     cases = [[2, 3], [3, 2], [1], [0], [], [0, 0, 5, 0], [1] * 300, [16] * 4,
-             [255, 256, 257, 0, 1], ragged.tolist()]
+             [255, 256, 257, 0, 1], ragged.tolist(),
+             # the one-launch path takes at most 256 samples
+             [3] * 255, [3] * 256, [3] * 257, [0] * 256, list(range(256))]
     cases += [pin.workload_inputs(i, blocks=0).lengths.tolist() for i in range(5)]
     return cases
 
