@@ -75,6 +75,8 @@ typedef enum nt_dtype { NT_F32 = 0, NT_BF16 = 1 } nt_dtype;
  *   row_sample     [T]    sample index of each pair row
  *   item_offsets   [B+1]  execution index of the column-mean schedule: sample
  *                         i owns work items [item_offsets[i], item_offsets[i+1])
+ *   tile_sample    [ceil(cells / 256)]  execution index of the pair kernels:
+ *                         the sample holding cell 256 k (the non-empty one)
  */
 typedef struct nt_partition {
   uint32_t magic;       /* set by nt_make_partition */
@@ -90,6 +92,7 @@ typedef struct nt_partition {
   const int64_t* row_splits;
   const int32_t* row_sample;
   const int64_t* item_offsets;
+  const int32_t* tile_sample;
 } nt_partition;
 
 /* The five weights of one block; see the layout convention above. */

@@ -125,6 +125,7 @@ class Partition:
             "item_offsets": self._view(s.item_offsets, B + 1, torch.int64),
             "row_splits": self._view(s.row_splits, T + 1, torch.int64),
             "row_sample": self._view(s.row_sample, T, torch.int32),
+            "tile_sample": self._view(s.tile_sample, (self.cells + 255) // 256, torch.int32),
         }
 
 

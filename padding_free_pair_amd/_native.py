@@ -26,6 +26,7 @@ class NtPartition(ctypes.Structure):
         ("lengths", ctypes.c_void_p), ("single_offsets", ctypes.c_void_p),
         ("pair_offsets", ctypes.c_void_p), ("row_splits", ctypes.c_void_p),
         ("row_sample", ctypes.c_void_p), ("item_offsets", ctypes.c_void_p),
+        ("tile_sample", ctypes.c_void_p),
     ]
 
 

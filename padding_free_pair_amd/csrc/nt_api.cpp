@@ -70,7 +70,8 @@ nt_status check_partition(const nt_partition* p) {
   if (p->B < 0 || p->T < 0 || p->cells < 0 || p->cells > kMaxCells || p->T > INT32_MAX)
     return fail(NT_ERR_INVALID, "partition sizes are corrupt");
   if (!p->single_offsets || !p->pair_offsets || !p->row_splits || !p->item_offsets ||
-      (p->B > 0 && !p->lengths) || (p->T > 0 && !p->row_sample))
+      (p->B > 0 && !p->lengths) || (p->T > 0 && !p->row_sample) ||
+      (p->cells > 0 && !p->tile_sample))
     return fail(NT_ERR_NULL, "partition arrays are NULL");
   return NT_OK;
 }
@@ -130,7 +131,7 @@ nt_status nt_partition_sizes(const int32_t* lengths, int32_t B, int64_t* T_out, 
   if (T_out) *T_out = T;
   if (cells_out) *cells_out = cells;
   if (n_max_out) *n_max_out = n_max;
-  if (bytes_out) *bytes_out = nt::partition_layout(B, T).total;
+  if (bytes_out) *bytes_out = nt::partition_layout(B, T, cells).total;
   return ok();
 }
 
@@ -149,7 +150,7 @@ nt_status nt_make_partition(const int32_t* lengths, int32_t B, void* buffer, siz
   int64_t items = 0;
   for (int32_t i = 0; i < B; ++i) items += nt::items_of(lengths[i]);
 
-  const nt::PartitionLayout L = nt::partition_layout(B, T);
+  const nt::PartitionLayout L = nt::partition_layout(B, T, cells);
   char* base = static_cast<char*>(buffer);
   nt_partition p;
   std::memset(&p, 0, sizeof(p));
@@ -165,23 +166,25 @@ nt_status nt_make_partition(const int32_t* lengths, int32_t B, void* buffer, siz
   int64_t* d_items = reinterpret_cast<int64_t*>(base + L.item_offsets);
   int64_t* d_splits = reinterpret_cast<int64_t*>(base + L.row_splits);
   int32_t* d_rows = reinterpret_cast<int32_t*>(base + L.row_sample);
+  int32_t* d_tiles = reinterpret_cast<int32_t*>(base + L.tile_sample);
   p.lengths = d_lengths;
   p.single_offsets = d_eta;
   p.pair_offsets = d_o;
   p.item_offsets = d_items;
   p.row_splits = d_splits;
   p.row_sample = d_rows;
+  p.tile_sample = d_tiles;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B <= nt::kArgSamples) {
     NT_TRY(hip_status(nt::launch_partition_small(lengths, p, d_lengths, d_eta, d_o, d_items,
-                                                 d_splits, d_rows, s),
+                                                 d_splits, d_rows, d_tiles, s),
                       "partition kernel"));
   } else {
     const hipError_t e =
         hipMemcpyAsync(d_lengths, lengths, sizeof(int32_t) * B, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_status(e, "copying lengths");
-    NT_TRY(hip_status(nt::launch_partition(p, d_eta, d_o, d_items, d_splits, d_rows, s),
+    NT_TRY(hip_status(nt::launch_partition(p, d_eta, d_o, d_items, d_splits, d_rows, d_tiles, s),
                       "partition kernels"));
   }
   *out = p;

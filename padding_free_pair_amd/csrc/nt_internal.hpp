@@ -36,14 +36,21 @@ __host__ __device__ inline int64_t items_of(int64_t n) {
   return (n + r - 1) / r;
 }
 
+// Cells per entry of the tile_sample execution index.
+constexpr int64_t kSampleIndexSpan = 256;
+inline int64_t sample_index_entries(int64_t cells) {
+  return (cells + kSampleIndexSpan - 1) / kSampleIndexSpan;
+}
+
 // Byte layout of the partition buffer: each array starts 256-byte aligned.
 struct PartitionLayout {
-  size_t lengths, single_offsets, pair_offsets, item_offsets, row_splits, row_sample, total;
+  size_t lengths, single_offsets, pair_offsets, item_offsets, row_splits, row_sample, tile_sample,
+      total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline PartitionLayout partition_layout(int64_t B, int64_t T) {
+inline PartitionLayout partition_layout(int64_t B, int64_t T, int64_t cells) {
   PartitionLayout L;
   size_t off = 0;
   L.lengths = off;        off = align256(off + sizeof(int32_t) * (B > 0 ? B : 1));
@@ -52,6 +59,8 @@ inline PartitionLayout partition_layout(int64_t B, int64_t T) {
   L.item_offsets = off;   off = align256(off + sizeof(int64_t) * (B + 1));
   L.row_splits = off;     off = align256(off + sizeof(int64_t) * (T + 1));
   L.row_sample = off;     off = align256(off + sizeof(int32_t) * (T > 0 ? T : 1));
+  const int64_t K = sample_index_entries(cells);
+  L.tile_sample = off;    off = align256(off + sizeof(int32_t) * (K > 0 ? K : 1));
   L.total = off;
   return L;
 }
@@ -61,14 +70,14 @@ inline PartitionLayout partition_layout(int64_t B, int64_t T) {
 // hipError_t; arguments are validated by the host API beforehand.
 hipError_t launch_partition(const nt_partition& p, int64_t* single_offsets, int64_t* pair_offsets,
                             int64_t* item_offsets, int64_t* row_splits, int32_t* row_sample,
-                            hipStream_t stream);
+                            int32_t* tile_sample, hipStream_t stream);
 // Batches of at most kArgSamples samples: one launch, lengths passed by value
 // from host memory (read before the call returns).
 constexpr int kArgSamples = 256;
 hipError_t launch_partition_small(const int32_t* lengths_host, const nt_partition& p,
                                   int32_t* lengths, int64_t* single_offsets, int64_t* pair_offsets,
                                   int64_t* item_offsets, int64_t* row_splits, int32_t* row_sample,
-                                  hipStream_t stream);
+                                  int32_t* tile_sample, hipStream_t stream);
 hipError_t launch_decode(const nt_partition& p, int32_t* sample, int32_t* row, int32_t* col,
                          hipStream_t stream);
 hipError_t launch_broadcast(const nt_partition& p, const void* a, const void* b, void* z, int c_z,

@@ -55,13 +55,16 @@ __global__ __launch_bounds__(kScanThreads) void k_offsets_scan(
 }
 
 // Second-level row splits: pair row g = eta_i + r starts at o_i + r * N_i
-// (Equation 3 at column 0); row_splits[T] closes with the cell total.
+// (Equation 3 at column 0); row_splits[T] closes with the cell total. The
+// same threads fill the tile index: entry k holds the sample of cell 256 k.
 __global__ __launch_bounds__(256) void k_row_splits(
     const int32_t* __restrict__ lengths, const int64_t* __restrict__ eta,
-    const int64_t* __restrict__ o, int B, int64_t T, int64_t* __restrict__ row_splits,
-    int32_t* __restrict__ row_sample) {
+    const int64_t* __restrict__ o, int B, int64_t T, int64_t K,
+    int64_t* __restrict__ row_splits, int32_t* __restrict__ row_sample,
+    int32_t* __restrict__ tile_sample) {
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (g == 0) row_splits[T] = o[B];
+  if (g < K) tile_sample[g] = find_segment(o, 0, B, g * kSampleIndexSpan);
   if (g >= T) return;
   const int i = find_segment(eta, 0, B, g);
   const int64_t r = g - eta[i];
@@ -78,9 +81,10 @@ struct LengthsArg {
 };
 
 __global__ __launch_bounds__(kArgSamples) void k_partition_small(
-    LengthsArg len, int B, int64_t T, int32_t* __restrict__ lengths, int64_t* __restrict__ eta,
-    int64_t* __restrict__ o, int64_t* __restrict__ items, int64_t* __restrict__ row_splits,
-    int32_t* __restrict__ row_sample) {
+    LengthsArg len, int B, int64_t T, int64_t K, int32_t* __restrict__ lengths,
+    int64_t* __restrict__ eta, int64_t* __restrict__ o, int64_t* __restrict__ items,
+    int64_t* __restrict__ row_splits, int32_t* __restrict__ row_sample,
+    int32_t* __restrict__ tile_sample) {
   __shared__ int64_t buf[2][3][kArgSamples];
   __shared__ int64_t s_eta[kArgSamples + 1], s_o[kArgSamples + 1];
   const int tid = threadIdx.x;
@@ -118,6 +122,7 @@ __global__ __launch_bounds__(kArgSamples) void k_partition_small(
   }
   const int64_t g = (int64_t)blockIdx.x * kArgSamples + tid;
   if (g == 0) row_splits[T] = s_o[B];
+  if (g < K) tile_sample[g] = find_segment(s_o, 0, B, g * kSampleIndexSpan);
   if (g < T) {
     const int i = find_segment(s_eta, 0, B, g);
     row_splits[g] = s_o[i] + (g - s_eta[i]) * (int64_t)len.n[i];
@@ -141,27 +146,32 @@ __global__ __launch_bounds__(256) void k_decode(
 
 hipError_t launch_partition(const nt_partition& p, int64_t* single_offsets, int64_t* pair_offsets,
                             int64_t* item_offsets, int64_t* row_splits, int32_t* row_sample,
-                            hipStream_t stream) {
+                            int32_t* tile_sample, hipStream_t stream) {
   hipLaunchKernelGGL(k_offsets_scan, dim3(1), dim3(kScanThreads), 0, stream, p.lengths, p.B,
                      single_offsets, pair_offsets, item_offsets);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t blocks = p.T > 0 ? (p.T + 255) / 256 : 1;
+  const int64_t K = sample_index_entries(p.cells);
+  const int64_t n = p.T > K ? p.T : K;
+  const int64_t blocks = n > 0 ? (n + 255) / 256 : 1;
   hipLaunchKernelGGL(k_row_splits, dim3((unsigned)blocks), dim3(256), 0, stream, p.lengths,
-                     single_offsets, pair_offsets, p.B, p.T, row_splits, row_sample);
+                     single_offsets, pair_offsets, p.B, p.T, K, row_splits, row_sample,
+                     tile_sample);
   return hipGetLastError();
 }
 
 hipError_t launch_partition_small(const int32_t* lengths_host, const nt_partition& p,
                                   int32_t* lengths, int64_t* single_offsets, int64_t* pair_offsets,
                                   int64_t* item_offsets, int64_t* row_splits, int32_t* row_sample,
-                                  hipStream_t stream) {
+                                  int32_t* tile_sample, hipStream_t stream) {
   LengthsArg arg;
   for (int i = 0; i < kArgSamples; ++i) arg.n[i] = i < p.B ? lengths_host[i] : 0;
-  const int64_t blocks = p.T > 0 ? (p.T + kArgSamples - 1) / kArgSamples : 1;
+  const int64_t K = sample_index_entries(p.cells);
+  const int64_t n = p.T > K ? p.T : K;
+  const int64_t blocks = n > 0 ? (n + kArgSamples - 1) / kArgSamples : 1;
   hipLaunchKernelGGL(k_partition_small, dim3((unsigned)blocks), dim3(kArgSamples), 0, stream, arg,
-                     p.B, p.T, lengths, single_offsets, pair_offsets, item_offsets, row_splits,
-                     row_sample);
+                     p.B, p.T, K, lengths, single_offsets, pair_offsets, item_offsets, row_splits,
+                     row_sample, tile_sample);
   return hipGetLastError();
 }
 

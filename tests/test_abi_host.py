@@ -50,8 +50,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_struct_layout_matches_header(lib):
-    # int32 x4, int64 x3, six pointers
-    assert ctypes.sizeof(_native.NtPartition) == 16 + 24 + 6 * 8
+    # int32 x4, int64 x3, seven pointers
+    assert ctypes.sizeof(_native.NtPartition) == 16 + 24 + 7 * 8
     assert _native.NtPartition.lengths.offset == 40
     assert ctypes.sizeof(_native.NtBlockWeights) == 5 * 8
 
@@ -112,7 +112,7 @@ def fake_partition(B=2, T=5, cells=13):
     p.magic = 0x4E545031
     p.B, p.T, p.cells, p.n_items, p.n_max = B, T, cells, 2, 3
     for k, name in enumerate(("lengths", "single_offsets", "pair_offsets", "row_splits",
-                              "row_sample", "item_offsets")):
+                              "row_sample", "item_offsets", "tile_sample")):
         setattr(p, name, FAKE + 0x1000 * k)
     return p
 

@@ -42,6 +42,10 @@ def test_partition_bit_exact(nt, lengths):
     assert arr["lengths"].tolist() == list(lengths)
     for k in ("single_offsets", "pair_offsets", "row_splits", "row_sample"):
         np.testing.assert_array_equal(arr[k], ref[k], err_msg=k)
+    # tile index: the sample holding every 256th cell (Eq. 3's o_i <= t < o_{i+1})
+    o = ref["pair_offsets"]
+    want = [int(np.searchsorted(o, t, side="right") - 1) for t in range(0, p.cells, 256)]
+    np.testing.assert_array_equal(arr["tile_sample"], np.array(want, dtype=np.int32))
     # the column-mean schedule covers every row exactly once
     items = arr["item_offsets"]
     assert items[0] == 0 and items[-1] == p.n_items
