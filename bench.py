@@ -87,7 +87,8 @@ def time_steps(fn, steps: int, warmup: int, torch) -> float:
 def time_kernel(fn, reps: int, torch) -> float:
     """Average duration (s) of fn's launches, from HIP events on the current
     stream (the stream the library launches on)."""
-    fn()
+    for _ in range(5):
+        fn()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -97,6 +98,16 @@ def time_kernel(fn, reps: int, torch) -> float:
     end.record()
     end.synchronize()
     return start.elapsed_time(end) / 1e3 / reps
+
+
+def transition_kernel_label(c_z: int, hidden: int, dtype: str) -> str:
+    """The kernel the library launches for the fused broadcast + transition."""
+    if dtype == "bf16" and c_z == 128 and hidden == 512 and \
+            os.environ.get("NT_TRANSITION_KERNEL") != "p32":
+        return "k_transition_pf (fused broadcast, next tile's b rows prefetched)"
+    if dtype == "bf16" and (c_z, hidden) in ((128, 512), (64, 128)):
+        return "k_transition_p32 (fused broadcast prologue)"
+    return "fused broadcast + transition"
 
 
 def kernel_rooflines(r: PackedRunner, reps: int):
@@ -122,13 +133,14 @@ def kernel_rooflines(r: PackedRunner, reps: int):
     nbytes = cells * cz * es + 2 * T * cz * 4 + 2 * hd * cz * es
     peak_f = PEAK_BF16_TFLOPS if x.dtype == "bf16" else PEAK_F32_TFLOPS
     t_f, t_b = flops / (peak_f * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)
+    label = transition_kernel_label(cz, hd, x.dtype)
     if t_f >= t_b:
-        out["transition"] = {"kernel": "k_transition_p32 (fused broadcast prologue)",
+        out["transition"] = {"kernel": label,
                              "bound": "mfma", "ms": t * 1e3, "achieved": flops / t / 1e12,
                              "peak": peak_f, "unit": "TFLOP/s", "flop_per_launch": flops,
                              "bytes_per_launch": nbytes}
     else:
-        out["transition"] = {"kernel": "k_transition_p32 (fused broadcast prologue)",
+        out["transition"] = {"kernel": label,
                              "bound": "hbm", "ms": t * 1e3, "achieved": nbytes / t / 1e9,
                              "peak": PEAK_HBM_GBS, "unit": "GB/s", "flop_per_launch": flops,
                              "bytes_per_launch": nbytes}
@@ -241,7 +253,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--kernel-reps", type=int, default=100)
     ap.add_argument("--quick", action="store_true",
                     help="timed steps and kernel timings only (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -30,6 +30,8 @@ COMMON = [
     f"-I{INCLUDE}", f"-I{CSRC}",
     # keep the compiler from forming packed fp32 ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # "#pragma unroll" loops are meant to unroll fully, however long the body
+    "-mllvm", "-pragma-unroll-threshold=1000000",
 ]
 
 

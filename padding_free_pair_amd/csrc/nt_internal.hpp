@@ -85,6 +85,11 @@ hipError_t launch_broadcast(const nt_partition& p, const void* a, const void* b,
 // z_in == nullptr selects the fused form: z is formed from fp32 a and b in
 // the prologue (a, b are fp32 [T, c_z] whatever the storage dtype).
 bool transition_has_mfma(int c_z, int hidden, nt_dtype dtype);
+// Fused broadcast + transition for c_z = 128, hidden = 512 with the next
+// tile's inputs prefetched into LDS; needs the tile_sample index and T < 2^31.
+hipError_t launch_transition_prefetch(const nt_partition& p, const void* a, const void* b,
+                                      void* z_out, const void* W1, const void* W2, int cus,
+                                      hipStream_t stream);
 hipError_t launch_transition(const nt_partition& p, const void* z_in, const void* a, const void* b,
                              void* z_out, const void* W1, const void* W2, int c_z, int hidden,
                              nt_dtype dtype, hipStream_t stream);

@@ -204,6 +204,63 @@ def test_broadcast_transition_parity(nt, lengths, c_z, hidden, dtype):
     assert scaled_max_err(f64(out, torch), ref) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("kernel", ["default", "p32"])
+def test_broadcast_transition_kernels_agree(nt, kernel, monkeypatch):
+    """The fused c_z = 128, hidden = 512 form has two kernels (the prefetching
+    one by default, the persistent one on request); both match the oracle on a
+    multi-tile ragged batch whose tiles mix short and long rows."""
+    if kernel == "p32":
+        monkeypatch.setenv("NT_TRANSITION_KERNEL", "p32")
+    lengths = [3, 40, 1, 17, 64, 5, 33, 2, 29, 8]
+    announce(f"broadcast+transition kernel={kernel} B={len(lengths)}")
+    T = sum(lengths)
+    a = pin.random_rows(T, 128, "f32", seed=21)
+    b = pin.random_rows(T, 128, "f32", seed=22)
+    W1, W2 = _mlp(128, 512, "bf16", seed=23)
+    p = nt.nt_make_partition(lengths)
+    full, out = _guarded(p.cells, 128, TD["bf16"])
+    nt.nt_pair_broadcast_transition(p, to_dev(a, torch), to_dev(b, torch), to_dev(W1, torch),
+                                    to_dev(W2, torch), z_out=out)
+    torch.cuda.synchronize()
+    _check_guard(full, 64, p.cells)
+    ref = oracle.transition(oracle.broadcast(lengths, a.f64, b.f64), W1.f64, W2.f64)
+    assert scaled_max_err(f64(out, torch), ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("kernel", ["default", "p32"])
+@pytest.mark.parametrize("idx", [3, 4])
+def test_broadcast_transition_full_size_sampled(nt, kernel, idx, monkeypatch):
+    """Both fused kernels at a full workload size, where every workgroup runs
+    several tiles (and the prefetching kernel prefetches across tiles),
+    checked on sampled cells: tile starts and ends, sample boundaries and
+    random cells."""
+    if kernel == "p32":
+        monkeypatch.setenv("NT_TRANSITION_KERNEL", "p32")
+    x = pin.workload_inputs(idx)
+    lengths = x.lengths.tolist()
+    announce(f"broadcast+transition full size {x.name} kernel={kernel}")
+    T = sum(lengths)
+    a = pin.random_rows(T, 128, "f32", seed=31)
+    b = pin.random_rows(T, 128, "f32", seed=32)
+    W1, W2 = _mlp(128, 512, "bf16", seed=33)
+    p = nt.nt_make_partition(lengths)
+    full, out = _guarded(p.cells, 128, TD["bf16"])
+    nt.nt_pair_broadcast_transition(p, to_dev(a, torch), to_dev(b, torch), to_dev(W1, torch),
+                                    to_dev(W2, torch), z_out=out)
+    torch.cuda.synchronize()
+    _check_guard(full, 64, p.cells)
+    o = np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64) ** 2)])
+    tiles = np.arange(0, p.cells, 256)
+    ids = np.unique(np.concatenate([np.random.default_rng(idx).integers(0, p.cells, 20000),
+                                    tiles, np.minimum(tiles + 255, p.cells - 1),
+                                    o[:-1], o[1:] - 1, np.arange(p.cells - 300, p.cells)]))
+    ids = ids[(ids >= 0) & (ids < p.cells)]
+    got = f64(out[torch.from_numpy(ids).cuda()], torch)
+    z = oracle.broadcast_cells(lengths, a.f64, b.f64, ids)
+    ref = oracle.transition(z, W1.f64, W2.f64)
+    assert scaled_max_err(got, ref) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("c_z,hidden", [(128, 512), (64, 128), (16, 24)])
 def test_broadcast_transition_exact(nt, dtype, c_z, hidden):
