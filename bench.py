@@ -73,6 +73,57 @@ class PackedRunner:
         return s_in, self.z
 
 
+class PerSampleRunner:
+    """The matched-granularity control (DanLing NestedTensor, Section 4
+    "Separating interface cost from execution strategy" and Appendix C.8,
+    Table 7): the same kernels, issued once per sample instead of once per
+    batch. Each sample gets its own one-sample partition and works on its
+    contiguous slices of the packed singles and pair state."""
+
+    def __init__(self, x: pin.Inputs, torch, nt, packed: PackedRunner):
+        self.torch, self.nt, self.x, self.r = torch, nt, x, packed
+        L = [int(n) for n in x.lengths]
+        self.L = L
+        self.eta = np.concatenate([[0], np.cumsum(L)]).astype(np.int64)
+        self.o = np.concatenate([[0], np.cumsum(np.square(np.asarray(L, dtype=np.int64)))])
+        self.lengths = [torch.tensor([n], dtype=torch.int32).pin_memory() for n in L]
+        self.bufs = [torch.empty(max(nt.nt_partition_sizes([n])[3], 256), dtype=torch.uint8,
+                                 device="cuda") for n in L]
+        tdt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+        ws = max(nt.nt_block_workspace_bytes(nt.nt_make_partition([n]), x.c_s, x.c_z, x.hidden,
+                                             tdt) for n in L)
+        self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
+
+    def step(self):
+        nt, r = self.nt, self.r
+        parts = [nt.nt_make_partition(self.lengths[i], buffer=self.bufs[i])
+                 for i in range(len(self.L))]
+        s_in = r.s0
+        for k, w in enumerate(r.w):
+            s_out = r.s[k % 2]
+            for i, p in enumerate(parts):
+                if self.L[i] == 0:
+                    continue
+                e0, e1 = int(self.eta[i]), int(self.eta[i + 1])
+                o0, o1 = int(self.o[i]), int(self.o[i + 1])
+                nt.nt_pair_block(p, s_in[e0:e1], w, s_out=s_out[e0:e1], z_out=r.z[o0:o1],
+                                 workspace=self.ws)
+            s_in = s_out
+        return s_in, r.z
+
+
+def granularity(x: pin.Inputs, r: PackedRunner, t_seg: float, args, torch, nt) -> dict:
+    """Per-sample launches against the segmented launch on the same kernels:
+    the granularity gain is per-sample time over segmented time."""
+    ps = PerSampleRunner(x, torch, nt, r)
+    t_ps = time_steps(ps.step, max(3, args.steps // 2), 2, torch)
+    log(f"per-sample launches {t_ps * 1e3:.3f} ms vs segmented {t_seg * 1e3:.3f} ms "
+        f"-> {t_ps / t_seg:.2f}x")
+    return {"segmented_ms_per_step": t_seg * 1e3, "per_sample_ms_per_step": t_ps * 1e3,
+            "gain": t_ps / t_seg, "launches_per_step_per_sample": len(x.weights) * 4 + 1,
+            "samples": len(x.lengths)}
+
+
 def time_steps(fn, steps: int, warmup: int, torch) -> float:
     for _ in range(warmup):
         fn()
@@ -335,6 +386,7 @@ def main():
                             "peak_bytes_padded": pad_peak, "peak_bytes_packed": packed_peak,
                             "memory_efficiency": pad_peak / max(packed_peak, 1),
                             "impl": "PyTorch ops over B x N_max^2 (bf16 matmul, masked mean)"}
+        result["granularity"] = granularity(x, r, t_step, args, torch, nt)
         regimes = {}
         for other in pin.WORKLOADS[1:]:
             if other.name == w.name:
@@ -349,6 +401,8 @@ def main():
                 "cells": ro.cells, "blocks": other.blocks,
                 "kernels": {k: {"ms": v["ms"], "achieved": v["achieved"], "unit": v["unit"],
                                 "frac": v["frac"]} for k, v in ko.items()}}
+            if other.blocks > 1:
+                regimes[other.name]["granularity"] = granularity(xo, ro, to, args, torch, nt)
             del ro
             torch.cuda.empty_cache()
         result["regimes"] = regimes
