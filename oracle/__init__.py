@@ -30,11 +30,14 @@ NestedTensor paper (arXiv 2609.30379):
   reference-semantics contract: a sample-local packed result, read logically,
   equals the dense per-sample computation.
 
-The transition here is z + relu(z W1^T) W2^T (a two-layer ReLU MLP without
-normalisation, the transition of the measured workloads); the paper's own
-pre-normalised SwiGLU transition is a different function and is not
-implemented. Weights are stored [out, in] as in the paper's V' = V W^T + b
-(Section 3.3), without biases.
+The block's transition is z + relu(z W1^T) W2^T (a two-layer ReLU MLP without
+normalisation, the transition of the measured workloads). The paper's own
+pre-normalised SwiGLU transition (Eq. 1 with h o LN; Appendix A.1, expansion
+four) is here too, as transition_swiglu: LN over the c_z features with affine
+gamma, beta and eps = 1e-5 (PyTorch's LayerNorm defaults), then
+(silu(x Wg^T) * (x Wu^T)) Wd^T without biases - the plainest reading, as the
+pages give SwiGLU's structure but not its formula. Weights are stored
+[out, in] as in the paper's V' = V W^T + b (Section 3.3), without biases.
 
 Pins (tests/test_oracle_pins.py) tie every function here to something
 outside itself: the Figure 2 worked example, a hand-computed block, closed
@@ -46,4 +49,5 @@ from .pair_block import (  # noqa: F401
     partition, decode_cells, broadcast, transition, reduce_mean, project,
     block, chain, block_padded_masked, block_gather, block_bruteforce,
     round_bf16, bf16_bits, block_cells, block_rows, dense_block, broadcast_cells,
+    layer_norm, transition_swiglu,
 )

@@ -108,6 +108,34 @@ def transition(z, W1, W2):
     return out
 
 
+def layer_norm(z, gamma, beta, eps):
+    """LN over the pair features of every cell (the LN_{C_p} of Eq. 1's second
+    line): (z - mean) / sqrt(var + eps) * gamma + beta, with the mean and the
+    biased variance taken over the c_z features of the cell."""
+    z = np.asarray(z, dtype=np.float64)
+    mu = z.mean(axis=-1, keepdims=True)
+    var = np.square(z - mu).mean(axis=-1, keepdims=True)
+    return (z - mu) / np.sqrt(var + eps) * np.asarray(gamma, dtype=np.float64) \
+        + np.asarray(beta, dtype=np.float64)
+
+
+def transition_swiglu(z, gamma, beta, Wg, Wu, Wd, eps=1e-5):
+    """The paper's measured transition (Eq. 1's second line; Appendix A.1: a
+    residual, pre-normalised SwiGLU update of expansion four): with x = LN(z),
+    z + (silu(x Wg^T) * (x Wu^T)) Wd^T, silu(g) = g / (1 + exp(-g)).
+    Wg, Wu are [hidden, c_z] and Wd is [c_z, hidden] ([out, in])."""
+    z = np.asarray(z, dtype=np.float64)
+    Wg, Wu, Wd = (np.asarray(w, dtype=np.float64) for w in (Wg, Wu, Wd))
+    out = np.empty_like(z)
+    for s in range(0, z.shape[0], _CHUNK_ROWS):
+        zc = z[s:s + _CHUNK_ROWS]
+        x = layer_norm(zc, gamma, beta, eps)
+        g = x @ Wg.T
+        u = x @ Wu.T
+        out[s:s + _CHUNK_ROWS] = zc + (g / (1.0 + np.exp(-g)) * u) @ Wd.T
+    return out
+
+
 def reduce_mean(lengths, zt):
     """Column mean of Eq. 1's third line: Eq. 4's grouped sum over the column
     index b, then division by N_i. Returns [T, C] with the singles' partition."""

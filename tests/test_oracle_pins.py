@@ -324,3 +324,78 @@ def test_round_bf16_matches_torch_on_fp32_values():
     x32 = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
     ref = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert (oracle.bf16_bits(x32.astype(np.float64)) == ref).all()
+
+
+# ------------------------------------------- pre-normalised SwiGLU transition
+def test_layer_norm_hand_computed():
+    # row [2, 2, 2, 6]: mean 3, biased variance (1 + 1 + 1 + 9) / 4 = 3
+    z = np.array([[1.0, 3.0], [2.0, 2.0]])
+    got = oracle.layer_norm(z, [1.0, 1.0], [0.0, 0.0], 0.0)
+    assert np.allclose(got[0], [-1.0, 1.0], rtol=0, atol=1e-15)
+    got = oracle.layer_norm([[2.0, 2.0, 2.0, 6.0]], [2.0, 1.0, 1.0, 1.0], [0.0, 0.0, 0.0, 5.0], 0.0)
+    r3 = np.sqrt(3.0)
+    assert np.allclose(got[0], [-2 / r3, -1 / r3, -1 / r3, 3 / r3 + 5.0], rtol=0, atol=1e-14)
+    # eps enters under the square root: var 3 + eps 1 -> divide by 2
+    got = oracle.layer_norm([[2.0, 2.0, 2.0, 6.0]], np.ones(4), np.zeros(4), 1.0)
+    assert np.allclose(got[0], [-0.5, -0.5, -0.5, 1.5], rtol=0, atol=1e-15)
+
+
+def test_layer_norm_invariances():
+    rng = np.random.default_rng(40)
+    z = rng.standard_normal((30, 16))
+    g, b = np.ones(16), np.zeros(16)
+    x = oracle.layer_norm(z, g, b, 0.0)
+    assert np.allclose(x.mean(axis=1), 0.0, atol=1e-13)
+    assert np.allclose(np.square(x).mean(axis=1), 1.0, atol=1e-12)
+    shift = rng.standard_normal((30, 1)) * 10
+    assert np.allclose(oracle.layer_norm(z + shift, g, b, 0.0), x, atol=1e-12)
+    scale = rng.uniform(0.1, 10.0, (30, 1))
+    assert np.allclose(oracle.layer_norm(z * scale, g, b, 0.0), x, atol=1e-12)
+
+
+def test_layer_norm_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(41)
+    z = rng.standard_normal((50, 24)) * 3 + 1
+    g, b = rng.standard_normal(24), rng.standard_normal(24)
+    want = torch.nn.functional.layer_norm(torch.from_numpy(z), (24,), torch.from_numpy(g),
+                                          torch.from_numpy(b), eps=1e-5).numpy()
+    assert np.allclose(oracle.layer_norm(z, g, b, 1e-5), want, rtol=1e-12, atol=1e-12)
+
+
+def test_swiglu_zero_weights_is_identity():
+    rng = np.random.default_rng(42)
+    z = rng.standard_normal((20, 8))
+    g, b = rng.standard_normal(8), rng.standard_normal(8)
+    Wg, Wu, Wd = (rng.standard_normal(s) for s in ((16, 8), (16, 8), (8, 16)))
+    for args in ((np.zeros_like(Wg), Wu, Wd), (Wg, np.zeros_like(Wu), Wd),
+                 (Wg, Wu, np.zeros_like(Wd))):
+        assert (oracle.transition_swiglu(z, g, b, *args) == z).all()
+
+
+def test_swiglu_hand_computed():
+    # z = [1, 3], eps = 0 -> x = [-1, 1]; g = -0.5 + 1.5 = 1; u = -2 + 1 = -1;
+    # silu(1) = 1 / (1 + e^-1); update = silu(1) * u * [1, -2]
+    s1 = 1.0 / (1.0 + np.exp(-1.0))
+    got = oracle.transition_swiglu([[1.0, 3.0]], [1.0, 1.0], [0.0, 0.0], [[0.5, 1.5]],
+                                   [[2.0, 1.0]], [[1.0], [-2.0]], eps=0.0)
+    assert np.allclose(got[0], [1.0 - s1, 3.0 + 2.0 * s1], rtol=0, atol=1e-14)
+    # gate and value are not interchangeable: swapping Wg and Wu changes the result
+    swapped = oracle.transition_swiglu([[1.0, 3.0]], [1.0, 1.0], [0.0, 0.0], [[2.0, 1.0]],
+                                       [[0.5, 1.5]], [[1.0], [-2.0]], eps=0.0)
+    sm1 = -1.0 / (1.0 + np.exp(1.0))          # silu(-1)
+    assert np.allclose(swapped[0], [1.0 + sm1 * 1.0, 3.0 - 2.0 * sm1], rtol=0, atol=1e-14)
+
+
+def test_swiglu_matches_torch():
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    rng = np.random.default_rng(43)
+    z = rng.standard_normal((64, 16))
+    g, b = rng.standard_normal(16), rng.standard_normal(16)
+    Wg, Wu = rng.standard_normal((48, 16)) / 4, rng.standard_normal((48, 16)) / 4
+    Wd = rng.standard_normal((16, 48)) / 7
+    t = lambda a: torch.from_numpy(np.asarray(a))
+    x = F.layer_norm(t(z), (16,), t(g), t(b), eps=1e-5)
+    want = (t(z) + F.linear(F.silu(F.linear(x, t(Wg))) * F.linear(x, t(Wu)), t(Wd))).numpy()
+    assert np.allclose(oracle.transition_swiglu(z, g, b, Wg, Wu, Wd), want, rtol=1e-12, atol=1e-12)
