@@ -210,6 +210,29 @@ def kernel_rooflines(r: PackedRunner, reps: int):
     return out
 
 
+def swiglu_roofline(r: PackedRunner, reps: int) -> dict:
+    """The paper's pre-normalised SwiGLU transition (expansion four) on the
+    workload's pair state: 6 c_z h flop per cell (gate, value and down
+    products), against the bf16 MFMA peak."""
+    torch, nt, x = r.torch, r.nt, r.x
+    cz, hd = x.c_z, x.hidden
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    gamma = 1.0 + 0.2 * torch.randn(cz, device="cuda", generator=g)
+    beta = 0.1 * torch.randn(cz, device="cuda", generator=g)
+    Wg = (torch.randn(hd, cz, device="cuda", generator=g) / cz ** 0.5).to(torch.bfloat16)
+    Wu = (torch.randn(hd, cz, device="cuda", generator=g) / cz ** 0.5).to(torch.bfloat16)
+    Wd = (torch.randn(cz, hd, device="cuda", generator=g) / hd ** 0.5).to(torch.bfloat16)
+    out = torch.empty_like(r.z)
+    t = time_kernel(lambda: nt.nt_pair_transition_swiglu(r.p, r.z, gamma, beta, Wg, Wu, Wd,
+                                                         z_out=out), reps, torch)
+    flops = 6.0 * cz * hd * r.cells
+    return {"kernel": "k_transition_swiglu (LN + SwiGLU, expansion four)", "bound": "mfma",
+            "ms": t * 1e3, "achieved": flops / t / 1e12, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "flop_per_launch": flops,
+            "frac": flops / t / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def traffic_for(kernel_key: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source; otherwise None."""
@@ -357,6 +380,11 @@ def main():
     kern = kernel_rooflines(r, args.kernel_reps)
     for k, v in kern.items():
         log(f"kernel {k}: {v['ms'] * 1e3:.1f} us, {v['achieved']:.1f} {v['unit']} "
+            f"({100 * v['frac']:.1f}% of peak)")
+    if x.dtype == "bf16" and x.c_z in (64, 128) and x.hidden % 32 == 0:
+        kern["swiglu_transition"] = swiglu_roofline(r, args.kernel_reps)
+        v = kern["swiglu_transition"]
+        log(f"kernel swiglu_transition: {v['ms'] * 1e3:.1f} us, {v['achieved']:.1f} TFLOP/s "
             f"({100 * v['frac']:.1f}% of peak)")
     dom = kern["transition"]
     roofline = {"bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],

@@ -180,6 +180,29 @@ nt_status nt_pair_broadcast_transition(const nt_partition* p, const void* a, con
                                        int32_t hidden, nt_dtype dtype, void* stream);
 
 /*
+ * The paper's own transition: a residual, pre-normalised SwiGLU update
+ * (Equation 1, second line, P~ = P + h(LN(P)); Appendix A.1, "transition
+ * expansion four"), cell by cell over the packed cells:
+ *   x = (z - mean) / sqrt(var + ln_eps) * ln_gamma + ln_beta,
+ *       mean and biased var over the c_z features of the cell;
+ *   z_out = z_in + (silu(x W_gate^T) * (x W_up^T)) W_down^T,
+ *       silu(g) = g / (1 + exp(-g)).
+ * z_in, z_out: [cells, c_z] bf16; ln_gamma, ln_beta: fp32 [c_z];
+ * W_gate, W_up: bf16 [hidden, c_z]; W_down: bf16 [c_z, hidden]. Statistics
+ * and products accumulate in fp32; x and the gated activations are rounded
+ * to bf16 before the products that read them; the residual adds z in fp32
+ * and rounds once.
+ * Supported: dtype NT_BF16 (else NT_ERR_DTYPE), c_z 64 or 128 and hidden a
+ * positive multiple of 32 (else NT_ERR_INVALID), ln_eps finite and >= 0.
+ * z_out may equal z_in (in place); other overlaps are rejected.
+ */
+nt_status nt_pair_transition_swiglu(const nt_partition* p, const void* z_in, void* z_out,
+                                    const float* ln_gamma, const float* ln_beta,
+                                    const void* W_gate, const void* W_up, const void* W_down,
+                                    int32_t c_z, int32_t hidden, float ln_eps, nt_dtype dtype,
+                                    void* stream);
+
+/*
  * Column mean (Equation 1, third line; Equation 4 divided by N_i):
  *   m[eta_i + r, :] = (1/N_i) sum_{c < N_i} z[o_i + r N_i + c, :].
  * z: [cells, c_z] of `dtype`; m: fp32 [T, c_z]. Deterministic: every row is

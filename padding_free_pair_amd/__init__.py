@@ -19,7 +19,7 @@ from ._native import (NT_BF16, NT_F32, NativeLibraryMissing, NtBlockWeights,  # 
 
 __all__ = ["NtError", "Partition", "nt_partition_sizes", "nt_make_partition", "nt_decode_cells",
            "nt_pair_broadcast", "nt_pair_transition", "nt_pair_broadcast_transition",
-           "nt_pair_reduce",
+           "nt_pair_transition_swiglu", "nt_pair_reduce",
            "nt_block_workspace_bytes", "nt_pair_block", "nt_last_error", "nt_version",
            "NT_F32", "NT_BF16"]
 
@@ -214,6 +214,28 @@ def nt_pair_broadcast_transition(p: Partition, a, b, W1, W2, z_out=None, stream=
     _check(_native.lib().nt_pair_broadcast_transition(
         ctypes.byref(p.struct), _ptr(a), _ptr(b), _ptr(z_out), _ptr(W1), _ptr(W2), c_z, hidden,
         _dtype_code(W1), _stream(stream, a.device)))
+    return z_out
+
+
+def nt_pair_transition_swiglu(p: Partition, z_in, ln_gamma, ln_beta, W_gate, W_up, W_down,
+                              z_out=None, ln_eps: float = 1e-5, stream=None):
+    """z_out = z_in + (silu(x W_gate^T) * (x W_up^T)) W_down^T, x = LN(z_in).
+
+    z_in, W_*: bf16; ln_gamma, ln_beta: float32 [c_z]; pass z_out=z_in to
+    work in place.
+    """
+    torch = _torch()
+    c_z, hidden = z_in.shape[-1], W_gate.shape[0]
+    if z_out is None:
+        z_out = torch.empty_like(z_in)
+    if ln_gamma.dtype != torch.float32 or ln_beta.dtype != torch.float32:
+        raise TypeError("ln_gamma and ln_beta must be float32")
+    if not (z_in.dtype == W_gate.dtype == W_up.dtype == W_down.dtype == z_out.dtype):
+        raise TypeError("z and weights must share a dtype")
+    _check(_native.lib().nt_pair_transition_swiglu(
+        ctypes.byref(p.struct), _ptr(z_in), _ptr(z_out), _ptr(ln_gamma), _ptr(ln_beta),
+        _ptr(W_gate), _ptr(W_up), _ptr(W_down), c_z, hidden, ln_eps, _dtype_code(z_in),
+        _stream(stream, z_in.device)))
     return z_out
 
 

@@ -14,7 +14,8 @@ NT_F32, NT_BF16 = 0, 1
 
 # Every symbol the header declares, for the export check.
 EXPORTS = ("nt_partition_sizes", "nt_make_partition", "nt_decode_cells", "nt_pair_broadcast",
-           "nt_pair_transition", "nt_pair_broadcast_transition", "nt_pair_reduce",
+           "nt_pair_transition", "nt_pair_broadcast_transition", "nt_pair_transition_swiglu",
+           "nt_pair_reduce",
            "nt_block_workspace_bytes", "nt_pair_block", "nt_last_error", "nt_version")
 
 
@@ -62,6 +63,8 @@ def lib() -> ctypes.CDLL:
         "nt_pair_broadcast": [part, vp, vp, vp, i32, ctypes.c_int, vp],
         "nt_pair_transition": [part, vp, vp, vp, vp, i32, i32, ctypes.c_int, vp],
         "nt_pair_broadcast_transition": [part, vp, vp, vp, vp, vp, i32, i32, ctypes.c_int, vp],
+        "nt_pair_transition_swiglu": [part, vp, vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float,
+                                      ctypes.c_int, vp],
         "nt_pair_reduce": [part, vp, vp, i32, ctypes.c_int, vp],
         "nt_block_workspace_bytes": [part, i32, i32, i32, ctypes.c_int, P(sz)],
         "nt_pair_block": [part, vp, vp, vp, P(NtBlockWeights), i32, i32, i32, ctypes.c_int, vp,

@@ -242,6 +242,42 @@ nt_status nt_pair_transition(const nt_partition* p, const void* z_in, void* z_ou
                     "transition kernel");
 }
 
+nt_status nt_pair_transition_swiglu(const nt_partition* p, const void* z_in, void* z_out,
+                                    const float* ln_gamma, const float* ln_beta,
+                                    const void* W_gate, const void* W_up, const void* W_down,
+                                    int32_t c_z, int32_t hidden, float ln_eps, nt_dtype dtype,
+                                    void* stream) {
+  NT_TRY(check_partition(p));
+  NT_TRY(check_dtype(dtype));
+  if (dtype != NT_BF16) return fail(NT_ERR_DTYPE, "the SwiGLU transition runs in bf16 only");
+  if (!nt::transition_swiglu_supported(c_z, hidden, dtype))
+    return fail(NT_ERR_INVALID, "SwiGLU transition needs c_z 64 or 128 and hidden a positive "
+                                "multiple of 32 (got c_z %d, hidden %d)", (int)c_z, (int)hidden);
+  if (!(ln_eps >= 0.f) || ln_eps > 3.0e38f)
+    return fail(NT_ERR_INVALID, "ln_eps must be finite and >= 0");
+  const uint64_t pair = (uint64_t)p->cells * c_z * esize(dtype);
+  const uint64_t wbytes = (uint64_t)hidden * c_z * esize(dtype);
+  const uint64_t lnbytes = (uint64_t)c_z * sizeof(float);
+  NT_TRY(check_array("z_in", z_in, pair));
+  NT_TRY(check_array("z_out", z_out, pair));
+  NT_TRY(check_array("ln_gamma", ln_gamma, lnbytes));
+  NT_TRY(check_array("ln_beta", ln_beta, lnbytes));
+  NT_TRY(check_array("W_gate", W_gate, wbytes));
+  NT_TRY(check_array("W_up", W_up, wbytes));
+  NT_TRY(check_array("W_down", W_down, wbytes));
+  if (z_in != z_out && overlaps(z_in, pair, z_out, pair))
+    return fail(NT_ERR_INVALID, "z_out partially overlaps z_in");
+  if (overlaps(z_out, pair, W_gate, wbytes) || overlaps(z_out, pair, W_up, wbytes) ||
+      overlaps(z_out, pair, W_down, wbytes) || overlaps(z_out, pair, ln_gamma, lnbytes) ||
+      overlaps(z_out, pair, ln_beta, lnbytes))
+    return fail(NT_ERR_INVALID, "z_out overlaps a parameter");
+  if (p->cells == 0) return ok();
+  return hip_status(nt::launch_transition_swiglu(*p, z_in, z_out, ln_gamma, ln_beta, W_gate, W_up,
+                                                 W_down, c_z, hidden, ln_eps,
+                                                 static_cast<hipStream_t>(stream)),
+                    "SwiGLU transition kernel");
+}
+
 nt_status nt_pair_broadcast_transition(const nt_partition* p, const void* a, const void* b,
                                        void* z_out, const void* W1, const void* W2, int32_t c_z,
                                        int32_t hidden, nt_dtype dtype, void* stream) {

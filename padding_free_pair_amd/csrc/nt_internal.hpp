@@ -85,6 +85,12 @@ hipError_t launch_broadcast(const nt_partition& p, const void* a, const void* b,
 // z_in == nullptr selects the fused form: z is formed from fp32 a and b in
 // the prologue (a, b are fp32 [T, c_z] whatever the storage dtype).
 bool transition_has_mfma(int c_z, int hidden, nt_dtype dtype);
+// Pre-normalised SwiGLU transition (bf16, c_z in {64, 128}, hidden % 32 == 0).
+bool transition_swiglu_supported(int c_z, int hidden, nt_dtype dtype);
+hipError_t launch_transition_swiglu(const nt_partition& p, const void* z_in, void* z_out,
+                                    const float* gamma, const float* beta, const void* Wg,
+                                    const void* Wu, const void* Wd, int c_z, int hidden,
+                                    float eps, hipStream_t stream);
 // Fused broadcast + transition for c_z = 128, hidden = 512 with the next
 // tile's inputs prefetched into LDS; needs the tile_sample index and T < 2^31.
 hipError_t launch_transition_prefetch(const nt_partition& p, const void* a, const void* b,

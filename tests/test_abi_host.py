@@ -146,6 +146,19 @@ def test_stage_calls_validate(lib):
     assert lib.nt_pair_reduce(P, z, a + 4, 16, 1, None) == E.NT_ERR_ALIGN
     # decode
     assert lib.nt_decode_cells(P, None, a, b, None) == E.NT_ERR_NULL
+    # SwiGLU transition: bf16 only, c_z 64 or 128, hidden a multiple of 32
+    g, bt, Wg, Wu, Wd = (FAKE + 0x600000 + 0x10000 * k for k in range(5))
+    sw = lib.nt_pair_transition_swiglu
+    assert sw(P, z, z, g, bt, Wg, Wu, Wd, 128, 512, 1e-5, 0, None) == E.NT_ERR_DTYPE
+    assert sw(P, z, z, g, bt, Wg, Wu, Wd, 96, 512, 1e-5, 1, None) == E.NT_ERR_INVALID
+    assert sw(P, z, z, g, bt, Wg, Wu, Wd, 128, 48, 1e-5, 1, None) == E.NT_ERR_INVALID
+    assert sw(P, z, z, g, bt, Wg, Wu, Wd, 128, 512, -1.0, 1, None) == E.NT_ERR_INVALID
+    assert sw(P, z, z, g, bt, Wg, Wu, Wd, 128, 512, float("nan"), 1, None) == E.NT_ERR_INVALID
+    assert sw(P, z, z, None, bt, Wg, Wu, Wd, 128, 512, 1e-5, 1, None) == E.NT_ERR_NULL
+    assert sw(P, z, z, g, bt, Wg, None, Wd, 128, 512, 1e-5, 1, None) == E.NT_ERR_NULL
+    assert sw(P, z, z + 64, g, bt, Wg, Wu, Wd, 128, 512, 1e-5, 1, None) == E.NT_ERR_INVALID
+    assert sw(P, z, Wd, g, bt, Wg, Wu, Wd, 128, 512, 1e-5, 1, None) == E.NT_ERR_INVALID
+    assert sw(P, z, z, g + 4, bt, Wg, Wu, Wd, 128, 512, 1e-5, 1, None) == E.NT_ERR_ALIGN
 
 
 def test_block_validates(lib):

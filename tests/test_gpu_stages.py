@@ -279,3 +279,77 @@ def test_broadcast_transition_exact(nt, dtype, c_z, hidden):
     want = expected_bits(oracle.transition(oracle.broadcast(lengths, a64, b64), w["W1"], w["W2"]),
                          dtype, oracle)
     np.testing.assert_array_equal(bits(out, torch), want)
+
+
+# ------------------------------------------- pre-normalised SwiGLU transition
+def _swiglu_params(c_z, hidden, seed):
+    """LN affine (fp32, gamma near 1) and gate / value / down weights (bf16)."""
+    rng = np.random.default_rng(seed)
+    gamma = (1.0 + 0.2 * rng.standard_normal(c_z)).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(c_z)).astype(np.float32)
+    Wg = pin.random_rows(hidden, c_z, "bf16", seed=seed + 1, scale=1.0 / np.sqrt(c_z))
+    Wu = pin.random_rows(hidden, c_z, "bf16", seed=seed + 2, scale=1.0 / np.sqrt(c_z))
+    Wd = pin.random_rows(c_z, hidden, "bf16", seed=seed + 3, scale=1.0 / np.sqrt(hidden))
+    return gamma, beta, Wg, Wu, Wd
+
+
+def _swiglu_dev(params):
+    gamma, beta, Wg, Wu, Wd = params
+    return (torch.from_numpy(gamma).cuda(), torch.from_numpy(beta).cuda(),
+            to_dev(Wg, torch), to_dev(Wu, torch), to_dev(Wd, torch))
+
+
+def _swiglu_ref(z64, params, eps=1e-5):
+    gamma, beta, Wg, Wu, Wd = params
+    return oracle.transition_swiglu(z64, gamma.astype(np.float64), beta.astype(np.float64),
+                                    Wg.f64, Wu.f64, Wd.f64, eps)
+
+
+@pytest.mark.parametrize("lengths,c_z,hidden", [
+    (TINY, 128, 512),        # ragged tail of a single tile
+    ([40, 3, 29], 128, 512),  # several tiles
+    (ONE_BLOCK, 64, 128),
+    (EDGE, 64, 96),           # zero-length samples, hidden not a power of two
+    ([33, 18], 128, 96),
+])
+def test_swiglu_transition_parity(nt, lengths, c_z, hidden):
+    announce(f"swiglu transition c_z={c_z} hidden={hidden} B={len(lengths)}")
+    z = pin.random_pair_rows(lengths, c_z, "bf16", seed=51)
+    params = _swiglu_params(c_z, hidden, seed=52)
+    p = nt.nt_make_partition(lengths)
+    full, out = _guarded(p.cells, c_z, torch.bfloat16)
+    nt.nt_pair_transition_swiglu(p, to_dev(z, torch), *_swiglu_dev(params), z_out=out)
+    torch.cuda.synchronize()
+    _check_guard(full, 64, p.cells)
+    err = scaled_max_err(f64(out, torch), _swiglu_ref(z.f64, params))
+    announce(f"error {err:.3e}")
+    assert err <= TOL["bf16"], err
+
+
+def test_swiglu_transition_in_place_and_eps(nt):
+    lengths, c_z, hidden = [21, 9, 30], 128, 512
+    announce("swiglu transition in place, eps 1e-3")
+    z = pin.random_pair_rows(lengths, c_z, "bf16", seed=53)
+    params = _swiglu_params(c_z, hidden, seed=54)
+    p = nt.nt_make_partition(lengths)
+    zd = to_dev(z, torch)
+    out = nt.nt_pair_transition_swiglu(p, zd, *_swiglu_dev(params), z_out=zd, ln_eps=1e-3)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == zd.data_ptr()
+    assert scaled_max_err(f64(zd, torch), _swiglu_ref(z.f64, params, 1e-3)) <= TOL["bf16"]
+
+
+def test_swiglu_transition_full_size_sampled(nt):
+    x = pin.workload_inputs(3)
+    lengths = x.lengths.tolist()
+    announce(f"swiglu transition full size {x.name}")
+    z = pin.random_pair_rows(lengths, 128, "bf16", seed=55)
+    params = _swiglu_params(128, 512, seed=56)
+    p = nt.nt_make_partition(lengths)
+    out = nt.nt_pair_transition_swiglu(p, to_dev(z, torch), *_swiglu_dev(params))
+    torch.cuda.synchronize()
+    o = np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64) ** 2)])
+    ids = np.unique(np.concatenate([np.random.default_rng(3).integers(0, p.cells, 20000),
+                                    o[:-1], o[1:] - 1, np.arange(p.cells - 300, p.cells)]))
+    got = f64(out[torch.from_numpy(ids).cuda()], torch)
+    assert scaled_max_err(got, _swiglu_ref(z.f64[ids], params)) <= TOL["bf16"]
