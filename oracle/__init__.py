@@ -50,4 +50,5 @@ from .pair_block import (  # noqa: F401
     block, chain, block_padded_masked, block_gather, block_bruteforce,
     round_bf16, bf16_bits, block_cells, block_rows, dense_block, broadcast_cells,
     layer_norm, transition_swiglu,
+    partition_rect, decode_cells_rect, broadcast_rect, reduce_mean_rect, block_rect,
 )

@@ -67,6 +67,99 @@ def decode_cells(lengths):
     return sample, row, col
 
 
+# ------------------------------------------------------ rectangular pairs
+# Section 3.1 packs rectangular pairs (N_i, M_i, C) as (sum N_i M_i, C); the
+# row axis follows one single partition (N_i, offsets eta), the column axis a
+# second one (M_i, offsets mu). Appendix A.1's rectangular variant builds the
+# pair from distinct row and column inputs and divides its column mean by M_i
+# (Eq. 4 groups the M_i cells of a row). With M = N every function below is
+# the square one.
+def partition_rect(rows, cols):
+    """Offsets and row splits of a rectangular pair partition: eta over the
+    row lengths N_i, mu over the column lengths M_i, o over N_i M_i (Eq. 2),
+    and pair row r of sample i starting at o_i + r M_i (Eq. 3)."""
+    N = [int(n) for n in rows]
+    M = [int(m) for m in cols]
+    if len(N) != len(M):
+        raise ValueError("row and column length vectors differ in size")
+    eta, mu, o = [0], [0], [0]
+    for n, m in zip(N, M):
+        eta.append(eta[-1] + n)
+        mu.append(mu[-1] + m)
+        o.append(o[-1] + n * m)
+    row_splits, row_sample = [], []
+    for i, (n, m) in enumerate(zip(N, M)):
+        for r in range(n):
+            row_splits.append(o[i] + r * m)
+            row_sample.append(i)
+    row_splits.append(o[-1])
+    return {
+        "B": len(N), "T": eta[-1], "T_cols": mu[-1], "cells": o[-1],
+        "single_offsets": np.array(eta, dtype=np.int64),
+        "col_offsets": np.array(mu, dtype=np.int64),
+        "pair_offsets": np.array(o, dtype=np.int64),
+        "row_splits": np.array(row_splits, dtype=np.int64),
+        "row_sample": np.array(row_sample, dtype=np.int32),
+    }
+
+
+def decode_cells_rect(rows, cols):
+    """(sample, row, col) of every packed cell: cell o_i + a M_i + b belongs to
+    sample i, row a < N_i, column b < M_i."""
+    p = partition_rect(rows, cols)
+    sample = np.full(p["cells"], -1, dtype=np.int64)
+    row = np.full(p["cells"], -1, dtype=np.int64)
+    col = np.full(p["cells"], -1, dtype=np.int64)
+    for i, (n, m) in enumerate(zip(rows, cols)):
+        n, m = int(n), int(m)
+        if n * m == 0:
+            continue
+        a = np.repeat(np.arange(n), m)
+        b = np.tile(np.arange(m), n)
+        ell = p["pair_offsets"][i] + a * m + b
+        sample[ell], row[ell], col[ell] = i, a, b
+    return sample, row, col
+
+
+def broadcast_rect(rows, cols, a, b):
+    """z[o_i + r M_i + c] = a[eta_i + r] + b[mu_i + c]: a [sum N_i, C] are the
+    row singles' projections, b [sum M_i, C] the column singles'."""
+    p = partition_rect(rows, cols)
+    sample, row, col = decode_cells_rect(rows, cols)
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return a[p["single_offsets"][sample] + row] + b[p["col_offsets"][sample] + col]
+
+
+def reduce_mean_rect(rows, cols, zt):
+    """Eq. 4's column sum over the M_i cells of each pair row, divided by M_i.
+    Returns [sum N_i, C] in the row singles' partition; a row of a sample with
+    M_i = 0 has no cells and no mean (NaN)."""
+    zt = np.asarray(zt, dtype=np.float64)
+    out = []
+    o = 0
+    for n, m in zip((int(x) for x in rows), (int(x) for x in cols)):
+        if n == 0:
+            continue
+        if m == 0:
+            out.append(np.full((n, zt.shape[1]), np.nan))
+            continue
+        out.append(zt[o:o + n * m].reshape(n, m, zt.shape[1]).sum(axis=1) / m)
+        o += n * m
+    return np.concatenate(out) if out else np.zeros((0, zt.shape[1]))
+
+
+def block_rect(rows, cols, s_rows, s_cols, w):
+    """The rectangular single-pair-single block (Appendix A.1's rectangular
+    variant): pair rows from s_rows [sum N_i, c_s], columns from s_cols
+    [sum M_i, c_s]; returns (s_rows + m Wo^T, z~)."""
+    a = project(s_rows, w["Wa"])
+    b = project(s_cols, w["Wb"])
+    zt = transition(broadcast_rect(rows, cols, a, b), w["W1"], w["W2"])
+    m = reduce_mean_rect(rows, cols, zt)
+    return np.asarray(s_rows, dtype=np.float64) + project(m, w["Wo"]), zt
+
+
 # ------------------------------------------------------------------ stages
 def project(x, W):
     """Dense projection on packed rows: x W^T (Section 3.3, no bias)."""

@@ -399,3 +399,91 @@ def test_swiglu_matches_torch():
     x = F.layer_norm(t(z), (16,), t(g), t(b), eps=1e-5)
     want = (t(z) + F.linear(F.silu(F.linear(x, t(Wg))) * F.linear(x, t(Wu)), t(Wd))).numpy()
     assert np.allclose(oracle.transition_swiglu(z, g, b, Wg, Wu, Wd), want, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------ rectangular pairs
+def test_rect_partition_hand_computed():
+    # N = [2, 0, 3], M = [4, 5, 1]: sample 0 is 2 x 4 (cells 0..7, rows at 0, 4),
+    # sample 1 has no rows (and no cells, although M_1 = 5), sample 2 is 3 x 1
+    # (cells 8, 9, 10, one per row).
+    p = oracle.partition_rect([2, 0, 3], [4, 5, 1])
+    assert p["T"] == 5 and p["T_cols"] == 10 and p["cells"] == 11
+    assert p["single_offsets"].tolist() == [0, 2, 2, 5]
+    assert p["col_offsets"].tolist() == [0, 4, 9, 10]
+    assert p["pair_offsets"].tolist() == [0, 8, 8, 11]
+    assert p["row_splits"].tolist() == [0, 4, 8, 9, 10, 11]
+    assert p["row_sample"].tolist() == [0, 0, 2, 2, 2]
+    sample, row, col = oracle.decode_cells_rect([2, 0, 3], [4, 5, 1])
+    assert sample.tolist() == [0] * 8 + [2] * 3
+    assert row.tolist() == [0, 0, 0, 0, 1, 1, 1, 1, 0, 1, 2]
+    assert col.tolist() == [0, 1, 2, 3, 0, 1, 2, 3, 0, 0, 0]
+
+
+@pytest.mark.parametrize("lengths", [[7, 12, 5, 16], [0, 3, 0, 1, 17, 0], [9]])
+def test_rect_with_equal_axes_is_square(lengths):
+    rng = np.random.default_rng(60)
+    p, q = oracle.partition_rect(lengths, lengths), oracle.partition(lengths)
+    for k in ("single_offsets", "pair_offsets", "row_splits", "row_sample"):
+        assert (p[k] == q[k]).all(), k
+    assert (p["col_offsets"] == q["single_offsets"]).all()
+    for u, v in zip(oracle.decode_cells_rect(lengths, lengths), oracle.decode_cells(lengths)):
+        assert (u == v).all()
+    T = sum(lengths)
+    a, b = rng.standard_normal((T, 6)), rng.standard_normal((T, 6))
+    z = oracle.broadcast_rect(lengths, lengths, a, b)
+    assert (z == oracle.broadcast(lengths, a, b)).all()
+    assert (oracle.reduce_mean_rect(lengths, lengths, z) == oracle.reduce_mean(lengths, z)).all()
+
+
+def test_rect_broadcast_bruteforce():
+    rows, cols = [3, 1, 0, 2], [2, 4, 3, 5]
+    rng = np.random.default_rng(61)
+    a = rng.standard_normal((sum(rows), 3))
+    b = rng.standard_normal((sum(cols), 3))
+    z = oracle.broadcast_rect(rows, cols, a, b)
+    t = eta = mu = 0
+    for n, m in zip(rows, cols):
+        for r in range(n):
+            for c in range(m):
+                for f in range(3):
+                    assert z[t, f] == a[eta + r, f] + b[mu + c, f]
+                t += 1
+        eta, mu = eta + n, mu + m
+    assert t == z.shape[0]
+
+
+def test_rect_reduce_closed_form_without_transition():
+    # no transition: mean_c (a[eta + r] + b[mu + c]) = a[eta + r] + mean(b of the sample)
+    rows, cols = [4, 2, 3], [3, 7, 1]
+    rng = np.random.default_rng(62)
+    a = rng.standard_normal((sum(rows), 5))
+    b = rng.standard_normal((sum(cols), 5))
+    m = oracle.reduce_mean_rect(rows, cols, oracle.broadcast_rect(rows, cols, a, b))
+    eta = np.concatenate([[0], np.cumsum(rows)])
+    mu = np.concatenate([[0], np.cumsum(cols)])
+    want = np.concatenate([a[eta[i]:eta[i + 1]] + b[mu[i]:mu[i + 1]].mean(axis=0)
+                           for i in range(3)])
+    assert np.allclose(m, want, rtol=0, atol=1e-14)
+
+
+def test_rect_block_equals_dense_per_sample():
+    rows, cols = [5, 0, 3, 8], [2, 6, 9, 1]
+    rng = np.random.default_rng(63)
+    c_s, c_z, h = 6, 4, 8
+    w = {"Wa": rng.standard_normal((c_z, c_s)), "Wb": rng.standard_normal((c_z, c_s)),
+         "W1": rng.standard_normal((h, c_z)), "W2": rng.standard_normal((c_z, h)),
+         "Wo": rng.standard_normal((c_s, c_z))}
+    s_rows = rng.standard_normal((sum(rows), c_s))
+    s_cols = rng.standard_normal((sum(cols), c_s))
+    s_new, zt = oracle.block_rect(rows, cols, s_rows, s_cols, w)
+    eta = np.concatenate([[0], np.cumsum(rows)])
+    mu = np.concatenate([[0], np.cumsum(cols)])
+    o = np.concatenate([[0], np.cumsum(np.multiply(rows, cols))])
+    for i in range(len(rows)):
+        X, Y = s_rows[eta[i]:eta[i + 1]], s_cols[mu[i]:mu[i + 1]]
+        P = (X @ w["Wa"].T)[:, None, :] + (Y @ w["Wb"].T)[None, :, :]   # [N, M, c_z]
+        Pt = P + np.maximum(P @ w["W1"].T, 0.0) @ w["W2"].T
+        assert np.allclose(zt[o[i]:o[i + 1]], Pt.reshape(-1, c_z), rtol=1e-12, atol=1e-12)
+        if rows[i] and cols[i]:
+            want = X + Pt.mean(axis=1) @ w["Wo"].T
+            assert np.allclose(s_new[eta[i]:eta[i + 1]], want, rtol=1e-12, atol=1e-12)
