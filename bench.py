@@ -112,6 +112,45 @@ class PerSampleRunner:
         return s_in, r.z
 
 
+def rectangular(x: pin.Inputs, args, torch, nt) -> dict:
+    """The rectangular variant (Appendix A.1) on the workload's shapes: pair
+    rows from the workload's singles (lengths N_i), pair columns from a second
+    set of singles whose lengths are the same lengths in reverse order (M_i),
+    the same four blocks; cells/s per block of the N_i x M_i pair state."""
+    rows = [int(n) for n in x.lengths]
+    cols = rows[::-1]
+    tdt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    s_rows = dev(x.s, torch)
+    s_cols = torch.randn(sum(cols), x.c_s, device="cuda", generator=g).to(tdt)
+    lengths_r = torch.tensor(rows, dtype=torch.int32).pin_memory()
+    lengths_c = torch.tensor(cols, dtype=torch.int32).pin_memory()
+    _, _, cells, nbytes = nt.nt_partition_sizes_rect(rows, cols)
+    buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    p = nt.nt_make_partition_rect(rows, cols, buffer=buf)
+    ws = torch.empty(max(nt.nt_block_workspace_bytes(p, x.c_s, x.c_z, x.hidden, tdt), 1),
+                     dtype=torch.uint8, device="cuda")
+    z = torch.empty((cells, x.c_z), dtype=tdt, device="cuda")
+    outs = [torch.empty_like(s_rows), torch.empty_like(s_rows)]
+    weights = [{k: dev(v, torch) for k, v in wk.items()} for wk in x.weights]
+
+    def step():
+        q = nt.nt_make_partition_rect(rows, cols, buffer=buf)
+        s_in = s_rows
+        for k, w in enumerate(weights):
+            s_out = outs[k % 2]
+            nt.nt_pair_block_rect(q, s_in, s_cols, w, s_out=s_out, z_out=z, workspace=ws)
+            s_in = s_out
+
+    t = time_steps(step, args.steps, args.warmup, torch)
+    log(f"rectangular (M = reversed N): {cells} cells, {t * 1e3:.3f} ms/step -> "
+        f"{cells * len(weights) / t:.4g} cells/s per block")
+    return {"rows": rows, "cols": cols, "cells": cells, "blocks": len(weights),
+            "ms_per_step": t * 1e3, "value": cells * len(weights) / t,
+            "unit": "pair cells/s per block"}
+
+
 def granularity(x: pin.Inputs, r: PackedRunner, t_seg: float, args, torch, nt) -> dict:
     """Per-sample launches against the segmented launch on the same kernels:
     the granularity gain is per-sample time over segmented time."""
@@ -415,6 +454,7 @@ def main():
                             "memory_efficiency": pad_peak / max(packed_peak, 1),
                             "impl": "PyTorch ops over B x N_max^2 (bf16 matmul, masked mean)"}
         result["granularity"] = granularity(x, r, t_step, args, torch, nt)
+        result["rectangular"] = rectangular(x, args, torch, nt)
         regimes = {}
         for other in pin.WORKLOADS[1:]:
             if other.name == w.name:

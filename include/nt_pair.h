@@ -63,15 +63,20 @@ typedef enum nt_status {
 typedef enum nt_dtype { NT_F32 = 0, NT_BF16 = 1 } nt_dtype;
 
 /*
- * A square pair partition (Section 3.1 "Structural metadata"; Figure 2;
- * Appendix A "Structural invariants"). Host scalars are canonical; the
- * arrays are device mirrors inside the caller's partition buffer. Filled by
- * nt_make_partition; read-only for callers.
+ * A pair partition (Section 3.1 "Structural metadata"; Figure 2; Appendix A
+ * "Structural invariants"): square, N_i x N_i (nt_make_partition), or
+ * rectangular, N_i x M_i (nt_make_partition_rect; Section 3.1 packs
+ * (N_i, M_i, C) pairs as (sum N_i M_i, C)). Host scalars are canonical; the
+ * arrays are device mirrors inside the caller's partition buffer. Read-only
+ * for callers. N_i counts pair rows (lengths), M_i pair columns
+ * (col_lengths); a square partition has M_i = N_i and its column arrays
+ * point at the row arrays.
  *
- *   single_offsets [B+1]  eta_i (first-level row splits), eta_B = T
- *   pair_offsets   [B+1]  o_i, o_B = cells; zero-length samples repeat offsets
+ *   single_offsets [B+1]  eta_i over N_i (the row singles), eta_B = T
+ *   col_offsets    [B+1]  mu_i over M_i (the column singles), mu_B = T_cols
+ *   pair_offsets   [B+1]  o_i over N_i M_i, o_B = cells; empty samples repeat
  *   row_splits     [T+1]  second-level splits: pair row r of sample i starts
- *                         at o_i + r N_i; row_splits[T] = cells
+ *                         at o_i + r M_i; row_splits[T] = cells
  *   row_sample     [T]    sample index of each pair row
  *   item_offsets   [B+1]  execution index of the column-mean schedule: sample
  *                         i owns work items [item_offsets[i], item_offsets[i+1])
@@ -84,7 +89,7 @@ typedef struct nt_partition {
   int32_t n_max;        /* max_i N_i (0 if every sample is empty) */
   int32_t reserved;
   int64_t T;            /* sum_i N_i */
-  int64_t cells;        /* sum_i N_i^2 */
+  int64_t cells;        /* sum_i N_i M_i (sum_i N_i^2 when square) */
   int64_t n_items;      /* item_offsets[B] */
   const int32_t* lengths;
   const int64_t* single_offsets;
@@ -93,6 +98,9 @@ typedef struct nt_partition {
   const int32_t* row_sample;
   const int64_t* item_offsets;
   const int32_t* tile_sample;
+  int64_t T_cols;                /* sum_i M_i (== T when square) */
+  const int32_t* col_lengths;    /* [B] M_i (== lengths when square) */
+  const int64_t* col_offsets;    /* [B+1] mu_i (== single_offsets when square) */
 } nt_partition;
 
 /* The five weights of one block; see the layout convention above. */
@@ -133,6 +141,28 @@ nt_status nt_make_partition(const int32_t* lengths, int32_t B, void* buffer, siz
                             void* stream, nt_partition* out);
 
 /*
+ * Rectangular pairs (Section 3.1: (N_i, M_i, C) packs as (sum N_i M_i, C);
+ * Appendix A.1's rectangular variant). Host only, like nt_partition_sizes:
+ * rows, cols: host int32 [B], N_i, M_i >= 0. T = sum N_i, T_cols = sum M_i,
+ * cells = sum N_i M_i. Errors as nt_partition_sizes (T_cols is bounded like
+ * T).
+ */
+nt_status nt_partition_sizes_rect(const int32_t* rows, const int32_t* cols, int32_t B, int64_t* T,
+                                  int64_t* T_cols, int64_t* cells, size_t* buffer_bytes);
+
+/*
+ * Builds a rectangular partition on the device, as nt_make_partition does a
+ * square one: eta over N_i, mu over M_i, o over N_i M_i, the column-mean
+ * item offsets, row_splits[eta_i + r] = o_i + r M_i, row_sample and the tile
+ * index. Every stage entry point accepts the result: the broadcast reads row
+ * singles a [T, c_z] and column singles b [T_cols, c_z], the column mean
+ * divides each row's sum by M_i (a row with M_i = 0 has no cells and its mean
+ * is 0/0, NaN). Host memory and buffer rules as nt_make_partition.
+ */
+nt_status nt_make_partition_rect(const int32_t* rows, const int32_t* cols, int32_t B, void* buffer,
+                                 size_t buffer_bytes, void* stream, nt_partition* out);
+
+/*
  * Test hook: materialises the decode of every packed cell t into its
  * (sample, row, col) with t = o_sample + row * N_sample + col (Equation 3
  * inverted). sample, row, col: device int32 [cells]. The hot kernels decode
@@ -143,9 +173,10 @@ nt_status nt_decode_cells(const nt_partition* p, int32_t* sample, int32_t* row, 
 
 /*
  * Broadcast (Equation 1, first line; Section 3.2 "Creating axes through
- * broadcasting"): z[o_i + r N_i + c, :] = a[eta_i + r, :] + b[eta_i + c, :].
- * a, b: [T, c_z]; z: [cells, c_z], all of `dtype`. The sum is formed in fp32
- * and rounded once to the storage type. z must not overlap a or b.
+ * broadcasting"): z[o_i + r M_i + c, :] = a[eta_i + r, :] + b[mu_i + c, :]
+ * (M_i = N_i and mu = eta for square pairs). a: [T, c_z]; b: [T_cols, c_z];
+ * z: [cells, c_z], all of `dtype`. The sum is formed in fp32 and rounded once
+ * to the storage type. z must not overlap a or b.
  */
 nt_status nt_pair_broadcast(const nt_partition* p, const void* a, const void* b, void* z,
                             int32_t c_z, nt_dtype dtype, void* stream);
@@ -166,9 +197,9 @@ nt_status nt_pair_transition(const nt_partition* p, const void* z_in, void* z_ou
 
 /*
  * Broadcast fused into the transition (Equation 1's first two lines in one
- * kernel): z_out[o_i + r N_i + c] = z + relu(z W1^T) W2^T with
- * z = a[eta_i + r] + b[eta_i + c] formed on chip and never written to
- * memory. a, b: fp32 [T, c_z] whatever `dtype` is (the projections' fp32
+ * kernel): z_out[o_i + r M_i + c] = z + relu(z W1^T) W2^T with
+ * z = a[eta_i + r] + b[mu_i + c] formed on chip and never written to
+ * memory. a: fp32 [T, c_z], b: fp32 [T_cols, c_z] whatever `dtype` is (the projections' fp32
  * results); z_out: [cells, c_z] of `dtype`; W1, W2 as for
  * nt_pair_transition. With NT_BF16 the MLP reads z rounded to bf16 while the
  * residual adds z in fp32, so the pair state is rounded once, on output.
@@ -203,8 +234,9 @@ nt_status nt_pair_transition_swiglu(const nt_partition* p, const void* z_in, voi
                                     void* stream);
 
 /*
- * Column mean (Equation 1, third line; Equation 4 divided by N_i):
- *   m[eta_i + r, :] = (1/N_i) sum_{c < N_i} z[o_i + r N_i + c, :].
+ * Column mean (Equation 1, third line; Equation 4 divided by M_i, which is
+ * N_i for square pairs):
+ *   m[eta_i + r, :] = (1/M_i) sum_{c < M_i} z[o_i + r M_i + c, :].
  * z: [cells, c_z] of `dtype`; m: fp32 [T, c_z]. Deterministic: every row is
  * summed by one workgroup in a fixed order, no atomics.
  */
@@ -228,6 +260,20 @@ nt_status nt_block_workspace_bytes(const nt_partition* p, int32_t c_s, int32_t c
 nt_status nt_pair_block(const nt_partition* p, const void* s_in, void* s_out, void* z_out,
                         const nt_block_weights* w, int32_t c_s, int32_t c_z, int32_t hidden,
                         nt_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The rectangular block (Appendix A.1's rectangular variant of Equation 1):
+ * pair rows are built from s_rows [T, c_s], pair columns from s_cols
+ * [T_cols, c_s]: a = s_rows Wa^T, b = s_cols Wb^T, z~ = transition(a[row] +
+ * b[col]), m = column mean (divided by M_i), s_out = s_rows + m Wo^T. The
+ * partition comes from nt_make_partition_rect (a square one works too, with
+ * s_cols = s_rows giving nt_pair_block). s_out may equal s_rows, not s_cols.
+ * Workspace as nt_pair_block (nt_block_workspace_bytes accounts for T_cols).
+ */
+nt_status nt_pair_block_rect(const nt_partition* p, const void* s_rows, const void* s_cols,
+                             void* s_out, void* z_out, const nt_block_weights* w, int32_t c_s,
+                             int32_t c_z, int32_t hidden, nt_dtype dtype, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* Thread-local description of the last failure in this thread ("" if none). */
 const char* nt_last_error(void);

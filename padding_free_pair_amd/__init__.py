@@ -17,7 +17,9 @@ from . import _native
 from ._native import (NT_BF16, NT_F32, NativeLibraryMissing, NtBlockWeights,  # noqa: F401
                       NtPartition)
 
-__all__ = ["NtError", "Partition", "nt_partition_sizes", "nt_make_partition", "nt_decode_cells",
+__all__ = ["NtError", "Partition", "nt_partition_sizes", "nt_make_partition",
+           "nt_partition_sizes_rect", "nt_make_partition_rect", "nt_pair_block_rect",
+           "nt_decode_cells",
            "nt_pair_broadcast", "nt_pair_transition", "nt_pair_broadcast_transition",
            "nt_pair_transition_swiglu", "nt_pair_reduce",
            "nt_block_workspace_bytes", "nt_pair_block", "nt_last_error", "nt_version",
@@ -103,6 +105,8 @@ class Partition:
 
     B = property(lambda self: self.struct.B)
     T = property(lambda self: self.struct.T)
+    T_cols = property(lambda self: self.struct.T_cols)
+    rectangular = property(lambda self: self.struct.col_offsets != self.struct.single_offsets)
     cells = property(lambda self: self.struct.cells)
     n_max = property(lambda self: self.struct.n_max)
     n_items = property(lambda self: self.struct.n_items)
@@ -126,6 +130,8 @@ class Partition:
             "row_splits": self._view(s.row_splits, T + 1, torch.int64),
             "row_sample": self._view(s.row_sample, T, torch.int32),
             "tile_sample": self._view(s.tile_sample, (self.cells + 255) // 256, torch.int32),
+            "col_lengths": self._view(s.col_lengths, B, torch.int32),
+            "col_offsets": self._view(s.col_offsets, B + 1, torch.int64),
         }
 
 
@@ -160,6 +166,38 @@ def nt_make_partition(lengths, device=None, stream=None, buffer=None) -> Partiti
     _check(_native.lib().nt_make_partition(ptr, arr.size, buffer.data_ptr(), buffer.numel(),
                                            _stream(stream, dev), ctypes.byref(st)))
     return Partition(st, buffer, arr if host is None else host)
+
+
+def nt_partition_sizes_rect(rows: Sequence[int], cols: Sequence[int]) -> Tuple[int, int, int, int]:
+    """(T, T_cols, cells, buffer_bytes) of a rectangular partition; host only."""
+    r, c = _lengths_array(rows), _lengths_array(cols)
+    if r.size != c.size:
+        raise ValueError("rows and cols must have one entry per sample")
+    T, Tc, cells, nbytes = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    rp = r.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if r.size else None
+    cp = c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if c.size else None
+    _check(_native.lib().nt_partition_sizes_rect(rp, cp, r.size, ctypes.byref(T), ctypes.byref(Tc),
+                                                 ctypes.byref(cells), ctypes.byref(nbytes)))
+    return T.value, Tc.value, cells.value, nbytes.value
+
+
+def nt_make_partition_rect(rows, cols, device=None, stream=None, buffer=None) -> Partition:
+    """Build a rectangular (N_i x M_i) pair partition on the device."""
+    torch = _torch()
+    r, c = _lengths_array(rows), _lengths_array(cols)
+    _, _, _, nbytes = nt_partition_sizes_rect(r, c)
+    dev = torch.device(device) if device is not None else torch.device("cuda",
+                                                                        torch.cuda.current_device())
+    if buffer is None or buffer.numel() < nbytes:
+        buffer = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    st = NtPartition()
+    rp = r.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if r.size else None
+    cp = c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if c.size else None
+    _check(_native.lib().nt_make_partition_rect(rp, cp, r.size, buffer.data_ptr(), buffer.numel(),
+                                                _stream(stream, dev), ctypes.byref(st)))
+    part = Partition(st, buffer, r)
+    part.col_lengths_host = c
+    return part
 
 
 def nt_decode_cells(p: Partition, stream=None):
@@ -285,4 +323,33 @@ def nt_pair_block(p: Partition, s_in, weights, s_out=None, z_out=None, workspace
                                        _ptr(z_out), ctypes.byref(wst), c_s, c_z, hidden,
                                        _dtype_code(s_in), _ptr(workspace),
                                        workspace.numel(), _stream(stream, s_in.device)))
+    return s_out, z_out
+
+
+def nt_pair_block_rect(p: Partition, s_rows, s_cols, weights, s_out=None, z_out=None,
+                       workspace=None, stream=None):
+    """The rectangular block: pair rows from s_rows [T, c_s], columns from
+    s_cols [T_cols, c_s]; returns (s_out, z_out)."""
+    torch = _torch()
+    if isinstance(weights, dict):
+        weights = [weights[k] for k in ("Wa", "Wb", "W1", "W2", "Wo")]
+    Wa, Wb, W1, W2, Wo = weights
+    c_s, c_z, hidden = s_rows.shape[-1], Wa.shape[0], W1.shape[0]
+    for w in weights:
+        if w.dtype != s_rows.dtype:
+            raise TypeError("weights must share s_rows' dtype")
+    if s_cols.dtype != s_rows.dtype:
+        raise TypeError("s_rows and s_cols must share a dtype")
+    if s_out is None:
+        s_out = torch.empty_like(s_rows)
+    if z_out is None:
+        z_out = torch.empty((p.cells, c_z), dtype=s_rows.dtype, device=s_rows.device)
+    need = nt_block_workspace_bytes(p, c_s, c_z, hidden, _dtype_code(s_rows))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=s_rows.device)
+    wst = NtBlockWeights(*[_ptr(w) for w in weights])
+    _check(_native.lib().nt_pair_block_rect(ctypes.byref(p.struct), _ptr(s_rows), _ptr(s_cols),
+                                            _ptr(s_out), _ptr(z_out), ctypes.byref(wst), c_s, c_z,
+                                            hidden, _dtype_code(s_rows), _ptr(workspace),
+                                            workspace.numel(), _stream(stream, s_rows.device)))
     return s_out, z_out

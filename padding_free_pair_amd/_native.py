@@ -13,10 +13,12 @@ STATUS_NAMES = {0: "NT_OK", 1: "NT_ERR_NULL", 2: "NT_ERR_INVALID", 3: "NT_ERR_OV
 NT_F32, NT_BF16 = 0, 1
 
 # Every symbol the header declares, for the export check.
-EXPORTS = ("nt_partition_sizes", "nt_make_partition", "nt_decode_cells", "nt_pair_broadcast",
+EXPORTS = ("nt_partition_sizes", "nt_make_partition", "nt_partition_sizes_rect",
+           "nt_make_partition_rect", "nt_decode_cells", "nt_pair_broadcast",
            "nt_pair_transition", "nt_pair_broadcast_transition", "nt_pair_transition_swiglu",
            "nt_pair_reduce",
-           "nt_block_workspace_bytes", "nt_pair_block", "nt_last_error", "nt_version")
+           "nt_block_workspace_bytes", "nt_pair_block", "nt_pair_block_rect", "nt_last_error",
+           "nt_version")
 
 
 class NtPartition(ctypes.Structure):
@@ -27,7 +29,8 @@ class NtPartition(ctypes.Structure):
         ("lengths", ctypes.c_void_p), ("single_offsets", ctypes.c_void_p),
         ("pair_offsets", ctypes.c_void_p), ("row_splits", ctypes.c_void_p),
         ("row_sample", ctypes.c_void_p), ("item_offsets", ctypes.c_void_p),
-        ("tile_sample", ctypes.c_void_p),
+        ("tile_sample", ctypes.c_void_p), ("T_cols", ctypes.c_int64),
+        ("col_lengths", ctypes.c_void_p), ("col_offsets", ctypes.c_void_p),
     ]
 
 
@@ -59,6 +62,8 @@ def lib() -> ctypes.CDLL:
     sig = {
         "nt_partition_sizes": [P(i32), i32, P(i64), P(i64), P(i32), P(sz)],
         "nt_make_partition": [P(i32), i32, vp, sz, vp, part],
+        "nt_partition_sizes_rect": [P(i32), P(i32), i32, P(i64), P(i64), P(i64), P(sz)],
+        "nt_make_partition_rect": [P(i32), P(i32), i32, vp, sz, vp, part],
         "nt_decode_cells": [part, vp, vp, vp, vp],
         "nt_pair_broadcast": [part, vp, vp, vp, i32, ctypes.c_int, vp],
         "nt_pair_transition": [part, vp, vp, vp, vp, i32, i32, ctypes.c_int, vp],
@@ -69,6 +74,8 @@ def lib() -> ctypes.CDLL:
         "nt_block_workspace_bytes": [part, i32, i32, i32, ctypes.c_int, P(sz)],
         "nt_pair_block": [part, vp, vp, vp, P(NtBlockWeights), i32, i32, i32, ctypes.c_int, vp,
                           sz, vp],
+        "nt_pair_block_rect": [part, vp, vp, vp, vp, P(NtBlockWeights), i32, i32, i32,
+                               ctypes.c_int, vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)

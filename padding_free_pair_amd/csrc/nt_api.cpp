@@ -69,9 +69,11 @@ nt_status check_partition(const nt_partition* p) {
     return fail(NT_ERR_INVALID, "partition was not built by nt_make_partition");
   if (p->B < 0 || p->T < 0 || p->cells < 0 || p->cells > kMaxCells || p->T > INT32_MAX)
     return fail(NT_ERR_INVALID, "partition sizes are corrupt");
+  if (p->T_cols < 0 || p->T_cols > INT32_MAX)
+    return fail(NT_ERR_INVALID, "partition sizes are corrupt");
   if (!p->single_offsets || !p->pair_offsets || !p->row_splits || !p->item_offsets ||
-      (p->B > 0 && !p->lengths) || (p->T > 0 && !p->row_sample) ||
-      (p->cells > 0 && !p->tile_sample))
+      !p->col_offsets || (p->B > 0 && (!p->lengths || !p->col_lengths)) ||
+      (p->T > 0 && !p->row_sample) || (p->cells > 0 && !p->tile_sample))
     return fail(NT_ERR_NULL, "partition arrays are NULL");
   return NT_OK;
 }
@@ -92,15 +94,183 @@ struct BlockWorkspace {
   uint64_t a, b, m, total;
 };
 
-// a and b are kept in fp32 (the projections' accumulators, unrounded), m too.
-BlockWorkspace block_workspace(int64_t T, int c_z, nt_dtype) {
+// a and b are kept in fp32 (the projections' accumulators, unrounded), m too;
+// b has one row per column single (T_cols, which is T for square pairs).
+BlockWorkspace block_workspace(int64_t T, int64_t T_cols, int c_z, nt_dtype) {
   BlockWorkspace w;
-  const uint64_t ab = nt::align256((size_t)T * c_z * sizeof(float));
+  const uint64_t a = nt::align256((size_t)T * c_z * sizeof(float));
+  const uint64_t b = nt::align256((size_t)T_cols * c_z * sizeof(float));
   w.a = 0;
-  w.b = ab;
-  w.m = 2 * ab;
-  w.total = 2 * ab + nt::align256((size_t)T * c_z * sizeof(float));
+  w.b = a;
+  w.m = a + b;
+  w.total = a + b + a;
   return w;
+}
+
+// Totals of a partition with N_i = rows[i] pair rows of M_i = cols[i] cells
+// (cols == rows for square pairs). Any output may be NULL.
+nt_status partition_totals(const int32_t* rows, const int32_t* cols, int32_t B, int64_t* T_out,
+                           int64_t* T_cols_out, int64_t* cells_out, int32_t* n_max_out) {
+  if (B < 0) return fail(NT_ERR_INVALID, "B = %d is negative", (int)B);
+  if (B > 0 && !rows) return fail(NT_ERR_NULL, "lengths is NULL");
+  int64_t T = 0, T_cols = 0, cells = 0;
+  int32_t n_max = 0;
+  for (int32_t i = 0; i < B; ++i) {
+    const int64_t n = rows[i], m = cols[i];
+    if (n < 0) return fail(NT_ERR_INVALID, "length %d of sample %d is negative", (int)n, (int)i);
+    if (m < 0)
+      return fail(NT_ERR_INVALID, "column length %d of sample %d is negative", (int)m, (int)i);
+    T += n;
+    T_cols += m;
+    if (T > INT32_MAX || T_cols > INT32_MAX)
+      return fail(NT_ERR_OVERFLOW, "sum of lengths exceeds INT32_MAX");
+    if (m > 0 && n > (kMaxCells - cells) / m)
+      return fail(NT_ERR_OVERFLOW, "sum of pair cells exceeds %lld cells", (long long)kMaxCells);
+    cells += n * m;
+    if (n > n_max) n_max = (int32_t)n;
+  }
+  if (T_out) *T_out = T;
+  if (T_cols_out) *T_cols_out = T_cols;
+  if (cells_out) *cells_out = cells;
+  if (n_max_out) *n_max_out = n_max;
+  return ok();
+}
+
+nt_status make_partition(const int32_t* rows, const int32_t* cols, int32_t B, bool rect,
+                         void* buffer, size_t buffer_bytes, void* stream, nt_partition* out) {
+  if (!out) return fail(NT_ERR_NULL, "out is NULL");
+  int64_t T = 0, T_cols = 0, cells = 0;
+  int32_t n_max = 0;
+  NT_TRY(partition_totals(rows, cols, B, &T, &T_cols, &cells, &n_max));
+  const nt::PartitionLayout L = nt::partition_layout(B, T, cells, rect);
+  if (!buffer) return fail(NT_ERR_NULL, "buffer is NULL");
+  if (reinterpret_cast<uintptr_t>(buffer) % 256 != 0)
+    return fail(NT_ERR_ALIGN, "partition buffer is not 256-byte aligned");
+  if (buffer_bytes < L.total)
+    return fail(NT_ERR_WORKSPACE, "partition buffer has %zu bytes, needs %zu", buffer_bytes,
+                L.total);
+  int64_t items = 0;
+  for (int32_t i = 0; i < B; ++i) items += nt::items_of(rows[i], cols[i]);
+
+  char* base = static_cast<char*>(buffer);
+  nt_partition p;
+  std::memset(&p, 0, sizeof(p));
+  p.magic = nt::kPartitionMagic;
+  p.B = B;
+  p.n_max = n_max;
+  p.T = T;
+  p.T_cols = T_cols;
+  p.cells = cells;
+  p.n_items = items;
+  int32_t* d_lengths = reinterpret_cast<int32_t*>(base + L.lengths);
+  int32_t* d_cols = reinterpret_cast<int32_t*>(base + L.col_lengths);
+  int64_t* d_eta = reinterpret_cast<int64_t*>(base + L.single_offsets);
+  int64_t* d_mu = reinterpret_cast<int64_t*>(base + L.col_offsets);
+  int64_t* d_o = reinterpret_cast<int64_t*>(base + L.pair_offsets);
+  int64_t* d_items = reinterpret_cast<int64_t*>(base + L.item_offsets);
+  int64_t* d_splits = reinterpret_cast<int64_t*>(base + L.row_splits);
+  int32_t* d_rows = reinterpret_cast<int32_t*>(base + L.row_sample);
+  int32_t* d_tiles = reinterpret_cast<int32_t*>(base + L.tile_sample);
+  p.lengths = d_lengths;
+  p.col_lengths = d_cols;
+  p.single_offsets = d_eta;
+  p.col_offsets = d_mu;
+  p.pair_offsets = d_o;
+  p.item_offsets = d_items;
+  p.row_splits = d_splits;
+  p.row_sample = d_rows;
+  p.tile_sample = d_tiles;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (B <= nt::kArgSamples) {
+    NT_TRY(hip_status(nt::launch_partition_small(rows, cols, p, d_lengths, d_cols, d_eta, d_mu,
+                                                 d_o, d_items, d_splits, d_rows, d_tiles, s),
+                      "partition kernel"));
+  } else {
+    hipError_t e =
+        hipMemcpyAsync(d_lengths, rows, sizeof(int32_t) * B, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess && rect)
+      e = hipMemcpyAsync(d_cols, cols, sizeof(int32_t) * B, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_status(e, "copying lengths");
+    NT_TRY(hip_status(nt::launch_partition(p, d_eta, d_mu, d_o, d_items, d_splits, d_rows,
+                                           d_tiles, s),
+                      "partition kernels"));
+  }
+  *out = p;
+  return ok();
+}
+
+// One block; s_cols is s_rows for square partitions.
+nt_status pair_block(const nt_partition* p, const void* s_rows, const void* s_cols, void* s_out,
+                     void* z_out, const nt_block_weights* w, int32_t c_s, int32_t c_z,
+                     int32_t hidden, nt_dtype dtype, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  NT_TRY(check_partition(p));
+  NT_TRY(check_dtype(dtype));
+  NT_TRY(check_width("c_s", c_s, nt::kMaxCs));
+  NT_TRY(check_width("c_z", c_z, nt::kMaxCz));
+  NT_TRY(check_width("hidden", hidden, nt::kMaxHidden));
+  if (!w) return fail(NT_ERR_NULL, "weights is NULL");
+  const size_t es = esize(dtype);
+  const uint64_t sbytes = (uint64_t)p->T * c_s * es;
+  const uint64_t cbytes = (uint64_t)p->T_cols * c_s * es;
+  const uint64_t pair = (uint64_t)p->cells * c_z * es;
+  const uint64_t proj = (uint64_t)c_z * c_s * es;
+  const uint64_t mlp = (uint64_t)c_z * hidden * es;
+  NT_TRY(check_array("s_rows", s_rows, sbytes));
+  NT_TRY(check_array("s_cols", s_cols, cbytes));
+  NT_TRY(check_array("s_out", s_out, sbytes));
+  NT_TRY(check_array("z_out", z_out, pair));
+  NT_TRY(check_array("Wa", w->Wa, proj));
+  NT_TRY(check_array("Wb", w->Wb, proj));
+  NT_TRY(check_array("W1", w->W1, mlp));
+  NT_TRY(check_array("W2", w->W2, mlp));
+  NT_TRY(check_array("Wo", w->Wo, proj));
+  const BlockWorkspace ws = block_workspace(p->T, p->T_cols, c_z, dtype);
+  if (ws.total > 0) {
+    NT_TRY(check_array("workspace", workspace, ws.total));
+    if (workspace_bytes < ws.total)
+      return fail(NT_ERR_WORKSPACE, "workspace has %zu bytes, needs %llu", workspace_bytes,
+                  (unsigned long long)ws.total);
+  }
+  if (s_rows != s_out && overlaps(s_rows, sbytes, s_out, sbytes))
+    return fail(NT_ERR_INVALID, "s_out partially overlaps s_in");
+  if (s_cols != s_rows && overlaps(s_out, sbytes, s_cols, cbytes))
+    return fail(NT_ERR_INVALID, "s_out overlaps s_cols");
+  const void* ins[] = {s_rows, w->Wa, w->Wb, w->W1, w->W2, w->Wo, workspace, s_cols};
+  const uint64_t insz[] = {sbytes, proj, proj, mlp, mlp, proj, ws.total, cbytes};
+  for (int k = 0; k < 8; ++k) {
+    if (overlaps(z_out, pair, ins[k], insz[k]) ||
+        (k > 0 && k < 7 && overlaps(s_out, sbytes, ins[k], insz[k])))
+      return fail(NT_ERR_INVALID, "an output overlaps an input or the workspace");
+  }
+  if (overlaps(z_out, pair, s_out, sbytes))
+    return fail(NT_ERR_INVALID, "z_out overlaps s_out");
+  if (p->T == 0) return ok();
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
+  void* a = base + ws.a;
+  void* b = base + ws.b;
+  float* m = reinterpret_cast<float*>(base + ws.m);
+  if (s_cols == s_rows && p->T_cols == p->T) {
+    NT_TRY(hip_status(nt::launch_linear2(s_rows, dtype, w->Wa, w->Wb, a, b, p->T, c_z, c_s, s),
+                      "projections a, b"));
+  } else {
+    NT_TRY(hip_status(nt::launch_linear(s_rows, dtype, w->Wa, dtype, nullptr, a, NT_F32, p->T,
+                                        c_z, c_s, s),
+                      "projection a"));
+    NT_TRY(hip_status(nt::launch_linear(s_cols, dtype, w->Wb, dtype, nullptr, b, NT_F32,
+                                        p->T_cols, c_z, c_s, s),
+                      "projection b"));
+  }
+  NT_TRY(hip_status(nt::launch_transition(*p, nullptr, a, b, z_out, w->W1, w->W2, c_z, hidden,
+                                          dtype, s),
+                    "fused broadcast + transition"));
+  NT_TRY(hip_status(nt::launch_reduce(*p, z_out, m, c_z, dtype, s), "column mean"));
+  return hip_status(nt::launch_linear(m, NT_F32, w->Wo, dtype, s_rows, s_out, dtype, p->T, c_s,
+                                      c_z, s),
+                    "output projection");
 }
 
 }  // namespace
@@ -113,21 +283,9 @@ int32_t nt_version(void) { return 1; }
 
 nt_status nt_partition_sizes(const int32_t* lengths, int32_t B, int64_t* T_out, int64_t* cells_out,
                              int32_t* n_max_out, size_t* bytes_out) {
-  if (B < 0) return fail(NT_ERR_INVALID, "B = %d is negative", (int)B);
-  if (B > 0 && !lengths) return fail(NT_ERR_NULL, "lengths is NULL");
   int64_t T = 0, cells = 0;
   int32_t n_max = 0;
-  for (int32_t i = 0; i < B; ++i) {
-    const int64_t n = lengths[i];
-    if (n < 0) return fail(NT_ERR_INVALID, "length %d of sample %d is negative", (int)n, (int)i);
-    T += n;
-    if (T > INT32_MAX) return fail(NT_ERR_OVERFLOW, "sum of lengths exceeds INT32_MAX");
-    if (n * n > kMaxCells - cells)
-      return fail(NT_ERR_OVERFLOW, "sum of squared lengths exceeds %lld cells",
-                  (long long)kMaxCells);
-    cells += n * n;
-    if (n > n_max) n_max = (int32_t)n;
-  }
+  NT_TRY(partition_totals(lengths, lengths, B, &T, nullptr, &cells, &n_max));
   if (T_out) *T_out = T;
   if (cells_out) *cells_out = cells;
   if (n_max_out) *n_max_out = n_max;
@@ -135,60 +293,27 @@ nt_status nt_partition_sizes(const int32_t* lengths, int32_t B, int64_t* T_out, 
   return ok();
 }
 
+nt_status nt_partition_sizes_rect(const int32_t* rows, const int32_t* cols, int32_t B,
+                                  int64_t* T_out, int64_t* T_cols_out, int64_t* cells_out,
+                                  size_t* bytes_out) {
+  int64_t T = 0, T_cols = 0, cells = 0;
+  NT_TRY(partition_totals(rows, cols, B, &T, &T_cols, &cells, nullptr));
+  if (T_out) *T_out = T;
+  if (T_cols_out) *T_cols_out = T_cols;
+  if (cells_out) *cells_out = cells;
+  if (bytes_out) *bytes_out = nt::partition_layout(B, T, cells, true).total;
+  return ok();
+}
+
 nt_status nt_make_partition(const int32_t* lengths, int32_t B, void* buffer, size_t buffer_bytes,
                             void* stream, nt_partition* out) {
-  if (!out) return fail(NT_ERR_NULL, "out is NULL");
-  int64_t T = 0, cells = 0;
-  int32_t n_max = 0;
-  size_t need = 0;
-  NT_TRY(nt_partition_sizes(lengths, B, &T, &cells, &n_max, &need));
-  if (!buffer) return fail(NT_ERR_NULL, "buffer is NULL");
-  if (reinterpret_cast<uintptr_t>(buffer) % 256 != 0)
-    return fail(NT_ERR_ALIGN, "partition buffer is not 256-byte aligned");
-  if (buffer_bytes < need)
-    return fail(NT_ERR_WORKSPACE, "partition buffer has %zu bytes, needs %zu", buffer_bytes, need);
-  int64_t items = 0;
-  for (int32_t i = 0; i < B; ++i) items += nt::items_of(lengths[i]);
+  return make_partition(lengths, lengths, B, false, buffer, buffer_bytes, stream, out);
+}
 
-  const nt::PartitionLayout L = nt::partition_layout(B, T, cells);
-  char* base = static_cast<char*>(buffer);
-  nt_partition p;
-  std::memset(&p, 0, sizeof(p));
-  p.magic = nt::kPartitionMagic;
-  p.B = B;
-  p.n_max = n_max;
-  p.T = T;
-  p.cells = cells;
-  p.n_items = items;
-  int32_t* d_lengths = reinterpret_cast<int32_t*>(base + L.lengths);
-  int64_t* d_eta = reinterpret_cast<int64_t*>(base + L.single_offsets);
-  int64_t* d_o = reinterpret_cast<int64_t*>(base + L.pair_offsets);
-  int64_t* d_items = reinterpret_cast<int64_t*>(base + L.item_offsets);
-  int64_t* d_splits = reinterpret_cast<int64_t*>(base + L.row_splits);
-  int32_t* d_rows = reinterpret_cast<int32_t*>(base + L.row_sample);
-  int32_t* d_tiles = reinterpret_cast<int32_t*>(base + L.tile_sample);
-  p.lengths = d_lengths;
-  p.single_offsets = d_eta;
-  p.pair_offsets = d_o;
-  p.item_offsets = d_items;
-  p.row_splits = d_splits;
-  p.row_sample = d_rows;
-  p.tile_sample = d_tiles;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (B <= nt::kArgSamples) {
-    NT_TRY(hip_status(nt::launch_partition_small(lengths, p, d_lengths, d_eta, d_o, d_items,
-                                                 d_splits, d_rows, d_tiles, s),
-                      "partition kernel"));
-  } else {
-    const hipError_t e =
-        hipMemcpyAsync(d_lengths, lengths, sizeof(int32_t) * B, hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return hip_status(e, "copying lengths");
-    NT_TRY(hip_status(nt::launch_partition(p, d_eta, d_o, d_items, d_splits, d_rows, d_tiles, s),
-                      "partition kernels"));
-  }
-  *out = p;
-  return ok();
+nt_status nt_make_partition_rect(const int32_t* rows, const int32_t* cols, int32_t B, void* buffer,
+                                 size_t buffer_bytes, void* stream, nt_partition* out) {
+  if (B > 0 && !cols) return fail(NT_ERR_NULL, "cols is NULL");
+  return make_partition(rows, cols, B, true, buffer, buffer_bytes, stream, out);
 }
 
 nt_status nt_decode_cells(const nt_partition* p, int32_t* sample, int32_t* row, int32_t* col,
@@ -208,11 +333,12 @@ nt_status nt_pair_broadcast(const nt_partition* p, const void* a, const void* b,
   NT_TRY(check_dtype(dtype));
   NT_TRY(check_width("c_z", c_z, nt::kMaxCz));
   const uint64_t single = (uint64_t)p->T * c_z * esize(dtype);
+  const uint64_t bsingle = (uint64_t)p->T_cols * c_z * esize(dtype);
   const uint64_t pair = (uint64_t)p->cells * c_z * esize(dtype);
   NT_TRY(check_array("a", a, single));
-  NT_TRY(check_array("b", b, single));
+  NT_TRY(check_array("b", b, bsingle));
   NT_TRY(check_array("z", z, pair));
-  if (overlaps(z, pair, a, single) || overlaps(z, pair, b, single))
+  if (overlaps(z, pair, a, single) || overlaps(z, pair, b, bsingle))
     return fail(NT_ERR_INVALID, "z overlaps a or b");
   return hip_status(
       nt::launch_broadcast(*p, a, b, z, c_z, dtype, static_cast<hipStream_t>(stream)),
@@ -286,14 +412,15 @@ nt_status nt_pair_broadcast_transition(const nt_partition* p, const void* a, con
   NT_TRY(check_width("c_z", c_z, nt::kMaxCz));
   NT_TRY(check_width("hidden", hidden, nt::kMaxHidden));
   const uint64_t single = (uint64_t)p->T * c_z * sizeof(float);
+  const uint64_t bsingle = (uint64_t)p->T_cols * c_z * sizeof(float);
   const uint64_t pair = (uint64_t)p->cells * c_z * esize(dtype);
   const uint64_t wbytes = (uint64_t)hidden * c_z * esize(dtype);
   NT_TRY(check_array("a", a, single));
-  NT_TRY(check_array("b", b, single));
+  NT_TRY(check_array("b", b, bsingle));
   NT_TRY(check_array("z_out", z_out, pair));
   NT_TRY(check_array("W1", W1, wbytes));
   NT_TRY(check_array("W2", W2, wbytes));
-  if (overlaps(z_out, pair, a, single) || overlaps(z_out, pair, b, single) ||
+  if (overlaps(z_out, pair, a, single) || overlaps(z_out, pair, b, bsingle) ||
       overlaps(z_out, pair, W1, wbytes) || overlaps(z_out, pair, W2, wbytes))
     return fail(NT_ERR_INVALID, "z_out overlaps an input");
   if (p->cells == 0) return ok();
@@ -324,7 +451,7 @@ nt_status nt_block_workspace_bytes(const nt_partition* p, int32_t c_s, int32_t c
   NT_TRY(check_width("c_z", c_z, nt::kMaxCz));
   NT_TRY(check_width("hidden", hidden, nt::kMaxHidden));
   if (!bytes) return fail(NT_ERR_NULL, "bytes is NULL");
-  *bytes = block_workspace(p->T, c_z, dtype).total;
+  *bytes = block_workspace(p->T, p->T_cols, c_z, dtype).total;
   return ok();
 }
 
@@ -332,58 +459,18 @@ nt_status nt_pair_block(const nt_partition* p, const void* s_in, void* s_out, vo
                         const nt_block_weights* w, int32_t c_s, int32_t c_z, int32_t hidden,
                         nt_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
   NT_TRY(check_partition(p));
-  NT_TRY(check_dtype(dtype));
-  NT_TRY(check_width("c_s", c_s, nt::kMaxCs));
-  NT_TRY(check_width("c_z", c_z, nt::kMaxCz));
-  NT_TRY(check_width("hidden", hidden, nt::kMaxHidden));
-  if (!w) return fail(NT_ERR_NULL, "weights is NULL");
-  const size_t es = esize(dtype);
-  const uint64_t sbytes = (uint64_t)p->T * c_s * es;
-  const uint64_t pair = (uint64_t)p->cells * c_z * es;
-  const uint64_t proj = (uint64_t)c_z * c_s * es;
-  const uint64_t mlp = (uint64_t)c_z * hidden * es;
-  NT_TRY(check_array("s_in", s_in, sbytes));
-  NT_TRY(check_array("s_out", s_out, sbytes));
-  NT_TRY(check_array("z_out", z_out, pair));
-  NT_TRY(check_array("Wa", w->Wa, proj));
-  NT_TRY(check_array("Wb", w->Wb, proj));
-  NT_TRY(check_array("W1", w->W1, mlp));
-  NT_TRY(check_array("W2", w->W2, mlp));
-  NT_TRY(check_array("Wo", w->Wo, proj));
-  const BlockWorkspace ws = block_workspace(p->T, c_z, dtype);
-  if (ws.total > 0) {
-    NT_TRY(check_array("workspace", workspace, ws.total));
-    if (workspace_bytes < ws.total)
-      return fail(NT_ERR_WORKSPACE, "workspace has %zu bytes, needs %llu", workspace_bytes,
-                  (unsigned long long)ws.total);
-  }
-  if (s_in != s_out && overlaps(s_in, sbytes, s_out, sbytes))
-    return fail(NT_ERR_INVALID, "s_out partially overlaps s_in");
-  const void* ins[] = {s_in, w->Wa, w->Wb, w->W1, w->W2, w->Wo, workspace};
-  const uint64_t insz[] = {sbytes, proj, proj, mlp, mlp, proj, ws.total};
-  for (int k = 0; k < 7; ++k) {
-    if (overlaps(z_out, pair, ins[k], insz[k]) ||
-        (k > 0 && overlaps(s_out, sbytes, ins[k], insz[k])))
-      return fail(NT_ERR_INVALID, "an output overlaps an input or the workspace");
-  }
-  if (overlaps(z_out, pair, s_out, sbytes))
-    return fail(NT_ERR_INVALID, "z_out overlaps s_out");
-  if (p->T == 0) return ok();
+  if (p->col_offsets != p->single_offsets)
+    return fail(NT_ERR_INVALID, "rectangular partition: use nt_pair_block_rect");
+  return pair_block(p, s_in, s_in, s_out, z_out, w, c_s, c_z, hidden, dtype, workspace,
+                    workspace_bytes, stream);
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* base = static_cast<char*>(workspace);
-  void* a = base + ws.a;
-  void* b = base + ws.b;
-  float* m = reinterpret_cast<float*>(base + ws.m);
-  NT_TRY(hip_status(nt::launch_linear2(s_in, dtype, w->Wa, w->Wb, a, b, p->T, c_z, c_s, s),
-                    "projections a, b"));
-  NT_TRY(hip_status(nt::launch_transition(*p, nullptr, a, b, z_out, w->W1, w->W2, c_z, hidden,
-                                          dtype, s),
-                    "fused broadcast + transition"));
-  NT_TRY(hip_status(nt::launch_reduce(*p, z_out, m, c_z, dtype, s), "column mean"));
-  return hip_status(nt::launch_linear(m, NT_F32, w->Wo, dtype, s_in, s_out, dtype, p->T, c_s,
-                                      c_z, s),
-                    "output projection");
+nt_status nt_pair_block_rect(const nt_partition* p, const void* s_rows, const void* s_cols,
+                             void* s_out, void* z_out, const nt_block_weights* w, int32_t c_s,
+                             int32_t c_z, int32_t hidden, nt_dtype dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return pair_block(p, s_rows, s_cols, s_out, z_out, w, c_s, c_z, hidden, dtype, workspace,
+                    workspace_bytes, stream);
 }
 
 }  // extern "C"

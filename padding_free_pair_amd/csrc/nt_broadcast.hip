@@ -1,6 +1,7 @@
 // Pair broadcast (DanLing NestedTensor, Equation 1 first line; Section 3.2
 // "Creating axes through broadcasting"):
-//   z[o_i + r N_i + c, :] = a[eta_i + r, :] + b[eta_i + c, :].
+//   z[o_i + r M_i + c, :] = a[eta_i + r, :] + b[mu_i + c, :]
+// (M_i = N_i and mu = eta for square pairs).
 // HBM-write bound: each cell writes c_z elements, a and b are L2 resident.
 #include "nt_device.hpp"
 #include "nt_internal.hpp"
@@ -18,7 +19,8 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void k_broadcast(
     const T* __restrict__ a, const T* __restrict__ b, T* __restrict__ z,
     const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
-    const int32_t* __restrict__ lengths, int B, int64_t cells, int c_z, int G, int CL) {
+    const int64_t* __restrict__ col_offsets, const int32_t* __restrict__ col_lengths, int B,
+    int64_t cells, int c_z, int G, int CL) {
   constexpr int VEC = Vec16<T>::N;
   const int tid = threadIdx.x;
   const int f = tid % G;
@@ -26,12 +28,13 @@ __global__ __launch_bounds__(kThreads) void k_broadcast(
   if (cl >= CL) return;
   int64_t t = (int64_t)blockIdx.x * CL * kSteps + cl;
   if (t >= cells) return;
-  Cell x = decode_cell(pair_offsets, single_offsets, lengths, B, t);
+  Cell x = decode_cell(pair_offsets, single_offsets, col_offsets, col_lengths, B, t);
+  int64_t end = pair_offsets[x.i + 1];  // first cell past the sample
   const int64_t fo = (int64_t)f * VEC;
 #pragma unroll
   for (int k = 0; k < kSteps; ++k) {
     const Vec16<T> va = load16(a + (x.eta + x.r) * c_z + fo);
-    const Vec16<T> vb = load16(b + (x.eta + x.c) * c_z + fo);
+    const Vec16<T> vb = load16(b + (x.mu + x.c) * c_z + fo);
     Vec16<T> out;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) out.set(e, va.get(e) + vb.get(e));
@@ -39,13 +42,13 @@ __global__ __launch_bounds__(kThreads) void k_broadcast(
     t += CL;
     if (k + 1 == kSteps || t >= cells) break;
     x.c += CL;
-    if (x.c >= x.n) {
-      if (x.n > CL) {  // at most one wrap into the next row
-        x.c -= x.n;
+    if (x.c >= x.m) {
+      if (x.m > CL && t < end) {  // at most one wrap into the next row
+        x.c -= x.m;
         x.r += 1;
-        if (x.r >= x.n) x = decode_cell(pair_offsets, single_offsets, lengths, B, t);
       } else {
-        x = decode_cell(pair_offsets, single_offsets, lengths, B, t);
+        x = decode_cell(pair_offsets, single_offsets, col_offsets, col_lengths, B, t);
+        end = pair_offsets[x.i + 1];
       }
     }
   }
@@ -60,7 +63,8 @@ hipError_t launch_t(const nt_partition& p, const void* a, const void* b, void* z
   const int64_t blocks = (p.cells + per_block - 1) / per_block;
   hipLaunchKernelGGL(k_broadcast<T>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                      static_cast<const T*>(a), static_cast<const T*>(b), static_cast<T*>(z),
-                     p.pair_offsets, p.single_offsets, p.lengths, p.B, p.cells, c_z, G, CL);
+                     p.pair_offsets, p.single_offsets, p.col_offsets, p.col_lengths, p.B, p.cells,
+                     c_z, G, CL);
   return hipGetLastError();
 }
 

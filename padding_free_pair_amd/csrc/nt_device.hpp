@@ -58,33 +58,36 @@ __device__ __forceinline__ int find_segment(const int64_t* __restrict__ off, int
   return lo;
 }
 
-// Decoded pair cell: sample i, pair row r, pair column c, plus the single
-// offset eta_i and length N_i of its sample.
+// Decoded pair cell: sample i, pair row r, pair column c, the row singles'
+// offset eta_i, the column singles' offset mu_i, and M_i, the cells per pair
+// row (N_i for square pairs, whose mu is eta).
 struct Cell {
   int i;
-  int64_t r, c, eta, n;
+  int64_t r, c, eta, mu, m;
 };
 
 // Packed cell t -> (sample, row, col): the sample is found from the pair
-// offsets, then t - o_i = r * N_i + c (Equation 3, row-major within the
-// sample's N_i x N_i block).
+// offsets, then t - o_i = r * M_i + c (Equation 3, row-major within the
+// sample's N_i x M_i block).
 __device__ __forceinline__ Cell decode_cell(const int64_t* __restrict__ pair_offsets,
                                             const int64_t* __restrict__ single_offsets,
-                                            const int32_t* __restrict__ lengths, int B,
+                                            const int64_t* __restrict__ col_offsets,
+                                            const int32_t* __restrict__ col_lengths, int B,
                                             int64_t t) {
   Cell x;
   x.i = find_segment(pair_offsets, 0, B, t);
-  x.n = lengths[x.i];
+  x.m = col_lengths[x.i];
   x.eta = single_offsets[x.i];
+  x.mu = col_offsets[x.i];
   const int64_t local = t - pair_offsets[x.i];
-  if (x.n <= 65535) {  // local < N^2 < 2^32: 32-bit division suffices
-    const uint32_t l32 = (uint32_t)local, n32 = (uint32_t)x.n;
-    const uint32_t q = l32 / n32;
+  if (x.m <= 65535 && local <= 0xffffffffLL) {  // 32-bit division suffices
+    const uint32_t l32 = (uint32_t)local, m32 = (uint32_t)x.m;
+    const uint32_t q = l32 / m32;
     x.r = q;
-    x.c = l32 - q * n32;
+    x.c = l32 - q * m32;
   } else {
-    x.r = local / x.n;
-    x.c = local - x.r * x.n;
+    x.r = local / x.m;
+    x.c = local - x.r * x.m;
   }
   return x;
 }

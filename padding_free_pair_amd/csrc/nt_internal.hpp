@@ -24,15 +24,19 @@ constexpr int kMaxHidden = 16384;
 constexpr int64_t kLongRow = 256;
 constexpr int64_t kItemCells = 512;
 
-__host__ __device__ inline int64_t rows_per_item(int64_t n) {
-  if (n >= kLongRow) return 1;
-  int64_t k = kItemCells / (4 * n);
+// m: cells per pair row (M_i; N_i for square pairs). Rows without cells
+// (M_i = 0) are grouped 64 to an item; their mean is 0/0.
+__host__ __device__ inline int64_t rows_per_item(int64_t m) {
+  if (m >= kLongRow) return 1;
+  if (m <= 0) return 64;
+  int64_t k = kItemCells / (4 * m);
   return 4 * (k < 1 ? 1 : k);
 }
 
-__host__ __device__ inline int64_t items_of(int64_t n) {
+// Work items of a sample with n pair rows of m cells each.
+__host__ __device__ inline int64_t items_of(int64_t n, int64_t m) {
   if (n <= 0) return 0;
-  const int64_t r = rows_per_item(n);
+  const int64_t r = rows_per_item(m);
   return (n + r - 1) / r;
 }
 
@@ -45,12 +49,13 @@ inline int64_t sample_index_entries(int64_t cells) {
 // Byte layout of the partition buffer: each array starts 256-byte aligned.
 struct PartitionLayout {
   size_t lengths, single_offsets, pair_offsets, item_offsets, row_splits, row_sample, tile_sample,
-      total;
+      col_lengths, col_offsets, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline PartitionLayout partition_layout(int64_t B, int64_t T, int64_t cells) {
+// Square partitions alias the column arrays to the row arrays (rect false).
+inline PartitionLayout partition_layout(int64_t B, int64_t T, int64_t cells, bool rect = false) {
   PartitionLayout L;
   size_t off = 0;
   L.lengths = off;        off = align256(off + sizeof(int32_t) * (B > 0 ? B : 1));
@@ -61,6 +66,13 @@ inline PartitionLayout partition_layout(int64_t B, int64_t T, int64_t cells) {
   L.row_sample = off;     off = align256(off + sizeof(int32_t) * (T > 0 ? T : 1));
   const int64_t K = sample_index_entries(cells);
   L.tile_sample = off;    off = align256(off + sizeof(int32_t) * (K > 0 ? K : 1));
+  if (rect) {
+    L.col_lengths = off;  off = align256(off + sizeof(int32_t) * (B > 0 ? B : 1));
+    L.col_offsets = off;  off = align256(off + sizeof(int64_t) * (B + 1));
+  } else {
+    L.col_lengths = L.lengths;
+    L.col_offsets = L.single_offsets;
+  }
   L.total = off;
   return L;
 }
@@ -68,16 +80,20 @@ inline PartitionLayout partition_layout(int64_t B, int64_t T, int64_t cells) {
 // ---------------------------------------------------------------------------
 // Kernel launchers (defined in the .hip sources). Each returns the launch's
 // hipError_t; arguments are validated by the host API beforehand.
-hipError_t launch_partition(const nt_partition& p, int64_t* single_offsets, int64_t* pair_offsets,
-                            int64_t* item_offsets, int64_t* row_splits, int32_t* row_sample,
-                            int32_t* tile_sample, hipStream_t stream);
+// p.lengths and p.col_lengths (device) hold N and M; mu is written only
+// when it is a separate array (rectangular partitions).
+hipError_t launch_partition(const nt_partition& p, int64_t* single_offsets, int64_t* col_offsets,
+                            int64_t* pair_offsets, int64_t* item_offsets, int64_t* row_splits,
+                            int32_t* row_sample, int32_t* tile_sample, hipStream_t stream);
 // Batches of at most kArgSamples samples: one launch, lengths passed by value
 // from host memory (read before the call returns).
 constexpr int kArgSamples = 256;
-hipError_t launch_partition_small(const int32_t* lengths_host, const nt_partition& p,
-                                  int32_t* lengths, int64_t* single_offsets, int64_t* pair_offsets,
-                                  int64_t* item_offsets, int64_t* row_splits, int32_t* row_sample,
-                                  int32_t* tile_sample, hipStream_t stream);
+hipError_t launch_partition_small(const int32_t* lengths_host, const int32_t* cols_host,
+                                  const nt_partition& p, int32_t* lengths, int32_t* col_lengths,
+                                  int64_t* single_offsets, int64_t* col_offsets,
+                                  int64_t* pair_offsets, int64_t* item_offsets,
+                                  int64_t* row_splits, int32_t* row_sample, int32_t* tile_sample,
+                                  hipStream_t stream);
 hipError_t launch_decode(const nt_partition& p, int32_t* sample, int32_t* row, int32_t* col,
                          hipStream_t stream);
 hipError_t launch_broadcast(const nt_partition& p, const void* a, const void* b, void* z, int c_z,

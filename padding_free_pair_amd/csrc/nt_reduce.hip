@@ -1,6 +1,6 @@
 // Column mean over packed pair rows (DanLing NestedTensor, Equation 4 and the
-// square mean of Equation 1's third line):
-//   m[eta_i + r, :] = (1 / N_i) * sum_{c < N_i} z[o_i + r N_i + c, :].
+// mean of Equation 1's third line), M_i cells per row (N_i for square pairs):
+//   m[eta_i + r, :] = (1 / M_i) * sum_{c < M_i} z[o_i + r M_i + c, :].
 // HBM-read bound. Deterministic: each row is summed by one wave or one
 // workgroup in a fixed order (no atomics).
 #include "nt_device.hpp"
@@ -47,7 +47,8 @@ template <typename T, int G>
 __global__ __launch_bounds__(kThreads) void k_reduce_pow2(
     const T* __restrict__ z, float* __restrict__ m, const int64_t* __restrict__ item_offsets,
     const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
-    const int32_t* __restrict__ lengths, int B, int c_z) {
+    const int32_t* __restrict__ lengths, const int32_t* __restrict__ col_lengths, int B,
+    int c_z) {
   constexpr int VEC = Vec16<T>::N;
   constexpr int CLW = 64 / G;
   __shared__ float part[kWaves][G * VEC];
@@ -56,7 +57,8 @@ __global__ __launch_bounds__(kThreads) void k_reduce_pow2(
   const int f = lane % G, cl = lane / G;
   const int64_t item = blockIdx.x;
   const int i = find_segment(item_offsets, 0, B, item);
-  const int64_t n = lengths[i];
+  const int64_t rows = lengths[i];   // N_i
+  const int64_t n = col_lengths[i];  // M_i, cells per row and the divisor
   const int64_t eta = single_offsets[i];
   const int64_t o = pair_offsets[i];
   const int64_t j = item - item_offsets[i];
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_pow2(
     // a group of whole rows; each wave reduces its own rows
     const int64_t R = rows_per_item(n);
     const int64_t r0 = j * R;
-    const int64_t r1 = r0 + R < n ? r0 + R : n;
+    const int64_t r1 = r0 + R < rows ? r0 + R : rows;
     for (int64_t r = r0 + wave; r < r1; r += kWaves) {
       const T* base = z + (o + r * n) * c_z + f * VEC;
       row_partial<T>(acc, base, cl, n, CLW, c_z);
@@ -120,14 +122,14 @@ __global__ __launch_bounds__(kThreads) void k_reduce_pow2(
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_reduce_generic(
     const T* __restrict__ z, float* __restrict__ m, const int64_t* __restrict__ row_splits,
-    const int32_t* __restrict__ row_sample, const int32_t* __restrict__ lengths, int64_t T_rows,
+    const int32_t* __restrict__ row_sample, const int32_t* __restrict__ col_lengths, int64_t T_rows,
     int c_z, int G) {
   constexpr int VEC = Vec16<T>::N;
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= T_rows * G) return;
   const int64_t g = idx / G;
   const int f = (int)(idx - g * G);
-  const int64_t n = lengths[row_sample[g]];
+  const int64_t n = col_lengths[row_sample[g]];
   float acc[VEC];
   row_partial<T>(acc, z + row_splits[g] * c_z + f * VEC, 0, n, 1, c_z);
   float* dst = m + g * c_z + f * VEC;
@@ -145,7 +147,7 @@ hipError_t launch_pow2(const nt_partition& p, const void* z, float* m, int c_z,
                        hipStream_t stream) {
   hipLaunchKernelGGL((k_reduce_pow2<T, G>), dim3((unsigned)p.n_items), dim3(kThreads), 0, stream,
                      static_cast<const T*>(z), m, p.item_offsets, p.pair_offsets,
-                     p.single_offsets, p.lengths, p.B, c_z);
+                     p.single_offsets, p.lengths, p.col_lengths, p.B, c_z);
   return hipGetLastError();
 }
 
@@ -165,7 +167,7 @@ hipError_t launch_t(const nt_partition& p, const void* z, float* m, int c_z, hip
   const int64_t total = p.T * G;
   hipLaunchKernelGGL(k_reduce_generic<T>, dim3((unsigned)((total + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, stream, static_cast<const T*>(z), m, p.row_splits,
-                     p.row_sample, p.lengths, p.T, c_z, G);
+                     p.row_sample, p.col_lengths, p.T, c_z, G);
   return hipGetLastError();
 }
 

@@ -55,7 +55,8 @@ template <int CZ, bool FUSED>
 __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_mfma(
     const bf16* __restrict__ z_in, const float* __restrict__ a, const float* __restrict__ b,
     const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
-    const int32_t* __restrict__ lengths, int B, const bf16* __restrict__ W1,
+    const int64_t* __restrict__ col_offsets, const int32_t* __restrict__ col_lengths, int B,
+    const bf16* __restrict__ W1,
     const bf16* __restrict__ W2, bf16* z_out, int64_t cells, int hidden) {
   constexpr int KB = CZ / 32;             // k-blocks of GEMM1 (K = c_z)
   constexpr int FB = CZ / 16;             // feature blocks of GEMM2's result
@@ -81,9 +82,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_mfma(
     arow[cb] = brow[cb] = 0;
     if (cell < cells) {
       if constexpr (FUSED) {
-        const Cell x = decode_cell(pair_offsets, single_offsets, lengths, B, cell);
+        const Cell x = decode_cell(pair_offsets, single_offsets, col_offsets, col_lengths, B, cell);
         arow[cb] = (int32_t)(x.eta + x.r);
-        brow[cb] = (int32_t)(x.eta + x.c);
+        brow[cb] = (int32_t)(x.mu + x.c);
         const float* ar = a + (int64_t)arow[cb] * CZ + 8 * g;
         const float* br = b + (int64_t)brow[cb] * CZ + 8 * g;
 #pragma unroll
@@ -253,16 +254,18 @@ __device__ __forceinline__ float relu_bits(float x) {
 constexpr int kLdsSamples = 384;
 
 // Sample, row and column of packed cell `cell` (Equation 3 inverted), with the
-// sample searched from `i0` upwards; po/eta/n are the pair offsets, single
-// offsets and lengths, in LDS or in global memory.
-template <typename OFF, typename IDX>
-__device__ __forceinline__ void decode_from(const OFF* po, const IDX* eta, const int32_t* n,
-                                            int i0, int64_t cell, int64_t& row, int64_t& col) {
+// sample searched from `i0` upwards; po/eta/mu/m are the pair offsets, the
+// row and column single offsets and the cells per pair row (M_i), in LDS or
+// in global memory.
+template <typename OFF, typename IDX, typename CIDX>
+__device__ __forceinline__ void decode_from(const OFF* po, const IDX* eta, const CIDX* mu,
+                                            const int32_t* m, int i0, int64_t cell, int64_t& row,
+                                            int64_t& col) {
   int i = i0;
   while (po[i + 1] <= cell) ++i;  // ends: po[B] = cells > cell
-  const int64_t len = n[i], local = cell - (int64_t)po[i];
+  const int64_t len = m[i], local = cell - (int64_t)po[i];
   int64_t r, c;
-  if (len <= 65535) {  // local < len^2 < 2^32
+  if (len <= 65535 && local <= 0xffffffffLL) {
     const uint32_t q32 = (uint32_t)local / (uint32_t)len;
     r = q32;
     c = (uint32_t)local - q32 * (uint32_t)len;
@@ -271,14 +274,15 @@ __device__ __forceinline__ void decode_from(const OFF* po, const IDX* eta, const
     c = local - r * len;
   }
   row = (int64_t)eta[i] + r;
-  col = (int64_t)eta[i] + c;
+  col = (int64_t)mu[i] + c;
 }
 
 template <int CZ, int HID, bool FUSED>
 __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
     const bf16* __restrict__ z_in, const float* __restrict__ a, const float* __restrict__ b,
     const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
-    const int32_t* __restrict__ lengths, int B, bool lds_part, const bf16* __restrict__ W1,
+    const int64_t* __restrict__ col_offsets, const int32_t* __restrict__ col_lengths, int B,
+    bool lds_part, const bf16* __restrict__ W1,
     const bf16* __restrict__ W2, bf16* z_out, int64_t cells, int64_t ntiles, int64_t T) {
   constexpr int KT = CZ / 16;        // GEMM1 k-steps
   constexpr int FB = CZ / 32;        // GEMM2 feature blocks
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
         po_s[i] = pair_offsets[i];
         if (i < B) {
           eta_s[i] = (int32_t)single_offsets[i];
-          n_s[i] = lengths[i];
+          n_s[i] = col_lengths[i];
         }
       }
     }
@@ -391,14 +395,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_transition_p32(
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) {
             const int64_t cell = cell0 + 32 * cb + l32;
-            decode_from(po_s, eta_s, n_s, i0, cell < cells ? cell : cells - 1, row[cb], col[cb]);
+            decode_from(po_s, eta_s, eta_s, n_s, i0, cell < cells ? cell : cells - 1, row[cb],
+                        col[cb]);
           }
         } else {
           const int i0 = find_segment(pair_offsets, 0, B, tile0);
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) {
             const int64_t cell = cell0 + 32 * cb + l32;
-            decode_from(pair_offsets, single_offsets, lengths, i0,
+            decode_from(pair_offsets, single_offsets, col_offsets, col_lengths, i0,
                         cell < cells ? cell : cells - 1, row[cb], col[cb]);
           }
         }
@@ -669,7 +674,8 @@ template <typename T, bool FUSED>
 __global__ __launch_bounds__(kGenThreads) void k_transition_generic(
     const T* __restrict__ z_in, const float* __restrict__ a, const float* __restrict__ b,
     const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
-    const int32_t* __restrict__ lengths, int B, const T* __restrict__ W1,
+    const int64_t* __restrict__ col_offsets, const int32_t* __restrict__ col_lengths, int B,
+    const T* __restrict__ W1,
     const T* __restrict__ W2, T* z_out, int64_t cells, int c_z, int hidden) {
   extern __shared__ float smem[];
   float* zs = smem;                       // [kGenCells][c_z]
@@ -683,8 +689,8 @@ __global__ __launch_bounds__(kGenThreads) void k_transition_generic(
     float v = 0.f;
     if (t < cells) {
       if constexpr (FUSED) {
-        const Cell x = decode_cell(pair_offsets, single_offsets, lengths, B, t);
-        v = a[(x.eta + x.r) * c_z + f] + b[(x.eta + x.c) * c_z + f];
+        const Cell x = decode_cell(pair_offsets, single_offsets, col_offsets, col_lengths, B, t);
+        v = a[(x.eta + x.r) * c_z + f] + b[(x.mu + x.c) * c_z + f];
       } else {
         v = to_f32(z_in[t * c_z + f]);
       }
@@ -747,13 +753,14 @@ hipError_t launch_mfma(const nt_partition& p, const void* z_in, const void* a, c
   if (z_in) {
     hipLaunchKernelGGL((k_transition_mfma<CZ, false>), dim3((unsigned)blocks), dim3(kWaves * 64),
                        0, stream, static_cast<const bf16*>(z_in), nullptr, nullptr,
-                       p.pair_offsets, p.single_offsets, p.lengths, p.B,
+                       p.pair_offsets, p.single_offsets, p.col_offsets, p.col_lengths, p.B,
                        static_cast<const bf16*>(W1), static_cast<const bf16*>(W2),
                        static_cast<bf16*>(z_out), p.cells, hidden);
   } else {
     hipLaunchKernelGGL((k_transition_mfma<CZ, true>), dim3((unsigned)blocks), dim3(kWaves * 64),
                        0, stream, nullptr, static_cast<const float*>(a),
-                       static_cast<const float*>(b), p.pair_offsets, p.single_offsets, p.lengths,
+                       static_cast<const float*>(b), p.pair_offsets, p.single_offsets,
+                       p.col_offsets, p.col_lengths,
                        p.B, static_cast<const bf16*>(W1), static_cast<const bf16*>(W2),
                        static_cast<bf16*>(z_out), p.cells, hidden);
   }
@@ -780,18 +787,21 @@ hipError_t launch_persistent(const nt_partition& p, const void* z_in, const void
                              hipStream_t stream) {
   const int64_t ntiles = (p.cells + kTileCells - 1) / kTileCells;
   const int64_t grid = ntiles < device_cus() ? ntiles : device_cus();
-  const bool lds_part = p.B <= kLdsSamples && p.T <= INT32_MAX;
+  // the LDS copy of the partition holds square partitions (mu = eta, M = N)
+  const bool lds_part = p.B <= kLdsSamples && p.T <= INT32_MAX &&
+                        p.col_offsets == p.single_offsets;
   if (z_in) {
     hipLaunchKernelGGL((k_transition_p32<CZ, HID, false>), dim3((unsigned)grid),
                        dim3(kWaves * 64), 0, stream, static_cast<const bf16*>(z_in), nullptr,
-                       nullptr, p.pair_offsets, p.single_offsets, p.lengths, p.B, false,
+                       nullptr, p.pair_offsets, p.single_offsets, p.col_offsets, p.col_lengths,
+                       p.B, false,
                        static_cast<const bf16*>(W1), static_cast<const bf16*>(W2),
                        static_cast<bf16*>(z_out), p.cells, ntiles, p.T);
   } else {
     hipLaunchKernelGGL((k_transition_p32<CZ, HID, true>), dim3((unsigned)grid),
                        dim3(kWaves * 64), 0, stream, nullptr, static_cast<const float*>(a),
                        static_cast<const float*>(b), p.pair_offsets, p.single_offsets,
-                       p.lengths, p.B, lds_part, static_cast<const bf16*>(W1),
+                       p.col_offsets, p.col_lengths, p.B, lds_part, static_cast<const bf16*>(W1),
                        static_cast<const bf16*>(W2), static_cast<bf16*>(z_out), p.cells, ntiles,
                        p.T);
   }
@@ -807,13 +817,14 @@ hipError_t launch_generic(const nt_partition& p, const void* z_in, const void* a
   if (z_in) {
     hipLaunchKernelGGL((k_transition_generic<T, false>), dim3((unsigned)blocks),
                        dim3(kGenThreads), shmem, stream, static_cast<const T*>(z_in), nullptr,
-                       nullptr, p.pair_offsets, p.single_offsets, p.lengths, p.B,
+                       nullptr, p.pair_offsets, p.single_offsets, p.col_offsets, p.col_lengths, p.B,
                        static_cast<const T*>(W1), static_cast<const T*>(W2),
                        static_cast<T*>(z_out), p.cells, c_z, hidden);
   } else {
     hipLaunchKernelGGL((k_transition_generic<T, true>), dim3((unsigned)blocks), dim3(kGenThreads),
                        shmem, stream, nullptr, static_cast<const float*>(a),
-                       static_cast<const float*>(b), p.pair_offsets, p.single_offsets, p.lengths,
+                       static_cast<const float*>(b), p.pair_offsets, p.single_offsets,
+                       p.col_offsets, p.col_lengths,
                        p.B, static_cast<const T*>(W1), static_cast<const T*>(W2),
                        static_cast<T*>(z_out), p.cells, c_z, hidden);
   }
@@ -832,13 +843,13 @@ hipError_t launch_transition(const nt_partition& p, const void* z_in, const void
   if (p.cells == 0) return hipSuccess;
   if (transition_has_mfma(c_z, hidden, dtype)) {
     // the persistent kernel keeps single indices in 32 bits
-    const bool small_t = p.T <= INT32_MAX;
+    const bool small_t = p.T <= INT32_MAX && p.T_cols <= INT32_MAX;
     // NT_TRANSITION_KERNEL=p32 selects the persistent kernel for the fused
     // form as well (read on every call, for comparisons and tests)
     const char* choice = getenv("NT_TRANSITION_KERNEL");
     const bool use_pf = !(choice && strcmp(choice, "p32") == 0);
     // the prefetching kernel addresses a through a 32-bit buffer range
-    const bool pf_fits = p.T <= (int64_t)(INT32_MAX / (128 * 4));
+    const bool pf_fits = (p.T > p.T_cols ? p.T : p.T_cols) <= (int64_t)(INT32_MAX / (128 * 4));
     if (use_pf && pf_fits && !z_in && c_z == 128 && hidden == 512 && p.tile_sample)
       return launch_transition_prefetch(p, a, b, z_out, W1, W2, device_cus(), stream);
     if (small_t && c_z == 128 && hidden == 512)

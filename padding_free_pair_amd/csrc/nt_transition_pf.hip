@@ -80,15 +80,17 @@ __device__ __forceinline__ int pf_block(int x) {
 }
 
 // Sample, row and column of packed cell `cell` (Equation 3 inverted),
-// searching upwards from sample i0 <= the cell's sample.
-template <typename OFF, typename IDX>
-__device__ __forceinline__ void pf_decode(const OFF* po, const IDX* eta, const int32_t* n, int i0,
-                                          int64_t cell, int& row, int& col) {
+// searching upwards from sample i0 <= the cell's sample; eta and mu are the
+// row and column single offsets, m the cells per pair row (M_i).
+template <typename OFF, typename IDX, typename CIDX>
+__device__ __forceinline__ void pf_decode(const OFF* po, const IDX* eta, const CIDX* mu,
+                                          const int32_t* m, int i0, int64_t cell, int& row,
+                                          int& col) {
   int i = i0;
   while (po[i + 1] <= cell) ++i;
-  const int64_t len = n[i], local = cell - (int64_t)po[i];
+  const int64_t len = m[i], local = cell - (int64_t)po[i];
   int64_t r, c;
-  if (len <= 65535) {
+  if (len <= 65535 && local <= 0xffffffffLL) {
     const uint32_t q = (uint32_t)local / (uint32_t)len;
     r = q;
     c = (uint32_t)local - q * (uint32_t)len;
@@ -97,14 +99,15 @@ __device__ __forceinline__ void pf_decode(const OFF* po, const IDX* eta, const i
     c = local - r * len;
   }
   row = (int)((int64_t)eta[i] + r);
-  col = (int)((int64_t)eta[i] + c);
+  col = (int)((int64_t)mu[i] + c);
 }
 
 template <int HID>
 __global__ __launch_bounds__(kPfWaves * 64, 1) void k_transition_pf(
     const float* __restrict__ a, const float* __restrict__ b,
     const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
-    const int32_t* __restrict__ lengths, const int32_t* __restrict__ tile_sample, int B,
+    const int64_t* __restrict__ col_offsets, const int32_t* __restrict__ col_lengths,
+    const int32_t* __restrict__ tile_sample, int B,
     bool lds_part, const bf16* __restrict__ W1, const bf16* __restrict__ W2,
     bf16* __restrict__ z_out, int64_t cells, int64_t ntiles, int64_t T) {
   constexpr int CZ = 128;
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_transition_pf(
       po_s[i] = pair_offsets[i];
       if (i < B) {
         eta_s[i] = (int32_t)single_offsets[i];
-        n_s[i] = lengths[i];
+        n_s[i] = col_lengths[i];
       }
     }
   }
@@ -218,9 +221,9 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void k_transition_pf(
     cell = cell < cells ? cell : cells - 1;  // a cell past the end repeats the last one
     const int i0 = tile_sample[tile];
     if (lds_part)
-      pf_decode(po_s, eta_s, n_s, i0, cell, row, col);
+      pf_decode(po_s, eta_s, eta_s, n_s, i0, cell, row, col);
     else
-      pf_decode(pair_offsets, single_offsets, lengths, i0, cell, row, col);
+      pf_decode(pair_offsets, single_offsets, col_offsets, col_lengths, i0, cell, row, col);
   };
   // DMA block x: lanes 0..31 fetch the b row of cell x, lanes 32..63 that of
   // cell x + 32. Issued from inline assembly so that the compiler does not
@@ -491,10 +494,11 @@ hipError_t launch_transition_prefetch(const nt_partition& p, const void* a, cons
                                       hipStream_t stream) {
   const int64_t ntiles = (p.cells + kPfTileCells - 1) / kPfTileCells;
   const int64_t grid = ntiles < cus ? ntiles : cus;
-  const bool lds_part = p.B <= kPfSamples;
+  // the LDS copy of the partition holds square partitions (mu = eta, M = N)
+  const bool lds_part = p.B <= kPfSamples && p.col_offsets == p.single_offsets;
   hipLaunchKernelGGL((k_transition_pf<512>), dim3((unsigned)grid), dim3(kPfWaves * 64), 0, stream,
                      static_cast<const float*>(a), static_cast<const float*>(b), p.pair_offsets,
-                     p.single_offsets, p.lengths, p.tile_sample, p.B, lds_part,
+                     p.single_offsets, p.col_offsets, p.col_lengths, p.tile_sample, p.B, lds_part,
                      static_cast<const bf16*>(W1), static_cast<const bf16*>(W2),
                      static_cast<bf16*>(z_out), p.cells, ntiles, p.T);
   return hipGetLastError();

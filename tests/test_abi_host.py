@@ -50,8 +50,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_struct_layout_matches_header(lib):
-    # int32 x4, int64 x3, seven pointers
-    assert ctypes.sizeof(_native.NtPartition) == 16 + 24 + 7 * 8
+    # int32 x4, int64 x3, seven pointers, then T_cols and two more pointers
+    assert ctypes.sizeof(_native.NtPartition) == 16 + 24 + 7 * 8 + 8 + 2 * 8
     assert _native.NtPartition.lengths.offset == 40
     assert ctypes.sizeof(_native.NtBlockWeights) == 5 * 8
 
@@ -114,6 +114,7 @@ def fake_partition(B=2, T=5, cells=13):
     for k, name in enumerate(("lengths", "single_offsets", "pair_offsets", "row_splits",
                               "row_sample", "item_offsets", "tile_sample")):
         setattr(p, name, FAKE + 0x1000 * k)
+    p.T_cols, p.col_lengths, p.col_offsets = T, p.lengths, p.single_offsets
     return p
 
 
@@ -188,3 +189,48 @@ def test_block_validates(lib):
     w.W1 = None
     assert lib.nt_pair_block(P, s, so, z, W, 16, 16, 32, 1, ws, need.value,
                              None) == E.NT_ERR_NULL
+
+
+def _sizes_rect(lib, rows, cols):
+    r = np.ascontiguousarray(rows, dtype=np.int32)
+    c = np.ascontiguousarray(cols, dtype=np.int32)
+    T, Tc, cells, nb = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    rp = r.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if r.size else None
+    cp = c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if c.size else None
+    st = lib.nt_partition_sizes_rect(rp, cp, r.size, ctypes.byref(T), ctypes.byref(Tc),
+                                     ctypes.byref(cells), ctypes.byref(nb))
+    return st, T.value, Tc.value, cells.value, nb.value
+
+
+@pytest.mark.parametrize("rows,cols", [([2, 0, 3], [4, 5, 1]), ([7, 12], [7, 12]), ([], []),
+                                       ([0, 9], [3, 0])])
+def test_rect_partition_sizes_match_oracle(lib, rows, cols):
+    st, T, Tc, cells, nb = _sizes_rect(lib, rows, cols)
+    assert st == _native.NT_OK
+    ref = oracle.partition_rect(rows, cols)
+    assert (T, Tc, cells) == (ref["T"], ref["T_cols"], ref["cells"])
+    assert nb >= 256
+
+
+def test_rect_partition_sizes_errors(lib):
+    assert _sizes_rect(lib, [3, 2], [1, -1])[0] == _native.NT_ERR_INVALID
+    assert _sizes_rect(lib, [2 ** 30, 2 ** 30], [1, 1])[0] == _native.NT_ERR_OVERFLOW  # T > 2^31 - 1
+    assert _sizes_rect(lib, [2 ** 29, 2 ** 29], [1, 1])[0] == _native.NT_OK
+    assert _sizes_rect(lib, [1], [2 ** 31 - 1])[0] == _native.NT_OK
+    assert _sizes_rect(lib, [2 ** 31 - 1], [2 ** 31 - 1])[0] == _native.NT_ERR_OVERFLOW
+    out = _native.NtPartition()
+    r = np.array([2, 3], dtype=np.int32)
+    rp = r.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert lib.nt_make_partition_rect(rp, None, 2, 0x10000, 1 << 20, None,
+                                      ctypes.byref(out)) == _native.NT_ERR_NULL
+
+
+def test_square_block_rejects_rect_partition(lib):
+    p = fake_partition()
+    p.col_offsets = FAKE + 0x9000  # a rectangular partition's own column offsets
+    P = ctypes.byref(p)
+    w = _native.NtBlockWeights(*[FAKE + 0x100000 * (k + 1) for k in range(5)])
+    s, z, ws = FAKE + 0x800000, FAKE + 0x900000, FAKE + 0xA00000
+    assert lib.nt_pair_block(P, s, s, z, ctypes.byref(w), 16, 16, 32, 1, ws, 1 << 20,
+                             None) == _native.NT_ERR_INVALID
+    assert "nt_pair_block_rect" in lib.nt_last_error().decode()
