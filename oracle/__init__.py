@@ -30,6 +30,10 @@ NestedTensor paper (arXiv 2609.30379):
   reference-semantics contract: a sample-local packed result, read logically,
   equals the dense per-sample computation.
 
+backward.py holds the gradients: Equation 5's sample-weighted squared loss
+(Appendix A.1) over the returned singles and pair state, and the chain rule
+through every step of the block, in reverse.
+
 The block's transition is z + relu(z W1^T) W2^T (a two-layer ReLU MLP without
 normalisation, the transition of the measured workloads). The paper's own
 pre-normalised SwiGLU transition (Eq. 1 with h o LN; Appendix A.1, expansion
@@ -51,4 +55,8 @@ from .pair_block import (  # noqa: F401
     round_bf16, bf16_bits, block_cells, block_rows, dense_block, broadcast_cells,
     layer_norm, transition_swiglu,
     partition_rect, decode_cells_rect, broadcast_rect, reduce_mean_rect, block_rect,
+)
+from .backward import (  # noqa: F401
+    loss_weights, loss_eq5, reduce_mean_backward, broadcast_backward, transition_backward,
+    block_backward, chain_loss, chain_backward,
 )

@@ -1,0 +1,192 @@
+"""Plain float64 gradients of the packed single-pair-single block and the
+sample-weighted squared loss it is trained with.
+
+TEST INFRASTRUCTURE (see the package docstring): callers are tests/, the
+smoke check and the CPU-baseline leg of the benchmark only.
+
+Source: the DanLing NestedTensor paper (arXiv 2609.30379).
+
+* Appendix A.1, Equation 5 - the objective over the returned singles X~ and
+  pair state P~: L = sum_i alpha_i |X~_i|_F^2 / (S C sum_i N_i)
+  + sum_i beta_i |P~_i|_F^2 / (S C_p sum_i N_i M_i), with
+  alpha_i = 1 + i / B and beta_i = 1.5 - i / (2 B) for i = 0 .. B - 1, S = 1
+  for the leading layouts, M_i = N_i for square pairs. The squared sums
+  accumulate in at least fp32 (here fp64).
+* Section 4 (experimental setup) - the measured step is forward, loss and
+  backward; Section 3.4 - gradients must reach the projections, the pair
+  update and the reduction of Equation 1 through the packed storage.
+
+The backward pass is the chain rule applied to the forward of pair_block,
+step by step in reverse order, written from the forward's definitions:
+
+  forward                          adjoint (g_x = dL/dx)
+  a = s Wa^T, b = s Wb^T           g_s += g_a Wa + g_b Wb; dWa = g_a^T s; dWb = g_b^T s
+  z[o_i + r N_i + c] = a[r] + b[c] g_a[r] = sum_c g_z[..];   g_b[c] = sum_r g_z[..]
+  P = relu(z W1^T)                 G = g_z' ; g_P = G W2 ; dW2 = G^T P
+  z' = z + P W2^T                  g_H = g_P * [z W1^T > 0]; dW1 = g_H^T z
+                                   g_z = G + g_H W1
+  m[r] = (1/M_i) sum_c z'[..]      G[o_i + r M_i + c] += g_m[r] / M_i
+  s~ = s + m Wo^T                  g_m = g_s~ Wo; dWo = g_s~^T m; g_s = g_s~ + ...
+
+Pins (tests/test_oracle_pins.py): central finite differences of the whole
+loss through a two-block chain, a hand-evaluated Equation 5, adjoint
+(dot-product) identities of the broadcast and the mean, and the
+reduction of the transition's gradient to the closed form of a linear map
+when every hidden unit is active.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .pair_block import _CHUNK_ROWS, block, broadcast, project, reduce_mean, transition
+
+
+# ------------------------------------------------------------------ Eq. 5
+def loss_weights(B):
+    """alpha_i = 1 + i / B and beta_i = 1.5 - i / (2 B), i = 0 .. B - 1."""
+    i = np.arange(B, dtype=np.float64)
+    return 1.0 + i / B, 1.5 - i / (2.0 * B)
+
+
+def loss_eq5(rows, cols, x, pz, S=1):
+    """Equation 5 over the singles x [sum N_i, C] and the pair state
+    pz [sum N_i M_i, C_p]. Returns (L, g_x, g_pz) with the exact gradients
+    g_x = 2 alpha_i x / (S C sum N) and g_pz = 2 beta_i pz / (S C_p sum N M)."""
+    x = np.asarray(x, dtype=np.float64)
+    pz = np.asarray(pz, dtype=np.float64)
+    N = [int(n) for n in rows]
+    M = [int(m) for m in cols]
+    B = len(N)
+    alpha, beta = loss_weights(B)
+    C, Cp = x.shape[1], pz.shape[1]
+    d1 = S * C * sum(N)
+    d2 = S * Cp * sum(n * m for n, m in zip(N, M))
+    L = 0.0
+    g_x = np.zeros_like(x)
+    g_pz = np.zeros_like(pz)
+    r0 = c0 = 0
+    for i in range(B):
+        xi = x[r0:r0 + N[i]]
+        pi = pz[c0:c0 + N[i] * M[i]]
+        if d1:
+            L += alpha[i] * float(np.sum(xi * xi)) / d1
+            g_x[r0:r0 + N[i]] = 2.0 * alpha[i] * xi / d1
+        if d2:
+            L += beta[i] * float(np.sum(pi * pi)) / d2
+            g_pz[c0:c0 + N[i] * M[i]] = 2.0 * beta[i] * pi / d2
+        r0 += N[i]
+        c0 += N[i] * M[i]
+    return L, g_x, g_pz
+
+
+# ------------------------------------------------------------- adjoints
+def reduce_mean_backward(rows, cols, g_m):
+    """Adjoint of the column mean (Eq. 4 divided by M_i): every cell of pair
+    row r of sample i receives g_m[eta_i + r] / M_i."""
+    g_m = np.asarray(g_m, dtype=np.float64)
+    out = []
+    r0 = 0
+    for n, m in zip((int(v) for v in rows), (int(v) for v in cols)):
+        blk = g_m[r0:r0 + n]
+        if m:
+            out.append(np.repeat(blk / m, m, axis=0))
+        r0 += n
+    if not out:
+        return np.zeros((0, g_m.shape[1]))
+    return np.concatenate(out, axis=0)
+
+
+def broadcast_backward(rows, cols, g_z):
+    """Adjoint of z[o_i + r M_i + c] = a[eta_i + r] + b[mu_i + c]: g_a sums a
+    sample's pair rows over their columns, g_b its pair columns over rows."""
+    g_z = np.asarray(g_z, dtype=np.float64)
+    C = g_z.shape[1]
+    N = [int(n) for n in rows]
+    M = [int(m) for m in cols]
+    g_a = np.zeros((sum(N), C))
+    g_b = np.zeros((sum(M), C))
+    r0 = c0 = o = 0
+    for n, m in zip(N, M):
+        blk = g_z[o:o + n * m].reshape(n, m, C)
+        g_a[r0:r0 + n] = blk.sum(axis=1)
+        g_b[c0:c0 + m] = blk.sum(axis=0)
+        r0 += n
+        c0 += m
+        o += n * m
+    return g_a, g_b
+
+
+def transition_backward(z, W1, W2, G):
+    """Gradients of z' = z + relu(z W1^T) W2^T for an incoming G = dL/dz'.
+    Returns (g_z, dW1, dW2). The derivative of relu at 0 is taken as 0."""
+    z = np.asarray(z, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    W1 = np.asarray(W1, dtype=np.float64)
+    W2 = np.asarray(W2, dtype=np.float64)
+    g_z = np.empty_like(z)
+    dW1 = np.zeros_like(W1)
+    dW2 = np.zeros_like(W2)
+    for s in range(0, z.shape[0], _CHUNK_ROWS):
+        zc, Gc = z[s:s + _CHUNK_ROWS], G[s:s + _CHUNK_ROWS]
+        pre = zc @ W1.T
+        P = np.maximum(pre, 0.0)
+        g_H = (Gc @ W2) * (pre > 0.0)
+        dW2 += Gc.T @ P
+        dW1 += g_H.T @ zc
+        g_z[s:s + _CHUNK_ROWS] = Gc + g_H @ W1
+    return g_z, dW1, dW2
+
+
+# ------------------------------------------------------------- the block
+def block_backward(lengths, s, w, g_s_out, g_z_out=None):
+    """Gradients of one square block (pair_block.block) for incoming g_s_out
+    = dL/ds~ and, optionally, g_z_out = dL/dz' (the returned pair state).
+    Returns a dict with "s" (dL/ds) and "Wa", "Wb", "W1", "W2", "Wo"."""
+    s = np.asarray(s, dtype=np.float64)
+    g_s_out = np.asarray(g_s_out, dtype=np.float64)
+    W = {k: np.asarray(v, dtype=np.float64) for k, v in w.items()}
+    # forward, keeping what the adjoints read
+    a = project(s, W["Wa"])
+    b = project(s, W["Wb"])
+    z = broadcast(lengths, a, b)
+    zt = transition(z, W["W1"], W["W2"])
+    m = reduce_mean(lengths, zt)
+    # s~ = s + m Wo^T
+    g_m = g_s_out @ W["Wo"]
+    dWo = g_s_out.T @ m
+    G = reduce_mean_backward(lengths, lengths, g_m)
+    if g_z_out is not None:
+        G = G + np.asarray(g_z_out, dtype=np.float64)
+    g_z, dW1, dW2 = transition_backward(z, W["W1"], W["W2"], G)
+    g_a, g_b = broadcast_backward(lengths, lengths, g_z)
+    g_s = g_s_out + g_a @ W["Wa"] + g_b @ W["Wb"]
+    return {"s": g_s, "Wa": g_a.T @ s, "Wb": g_b.T @ s, "W1": dW1, "W2": dW2, "Wo": dWo}
+
+
+def chain_loss(lengths, s, ws, S=1):
+    """Equation 5 of a chain of blocks: the loss reads the last block's singles
+    and pair state. Returns the scalar loss."""
+    z = None
+    x = np.asarray(s, dtype=np.float64)
+    for w in ws:
+        x, z = block(lengths, x, w)
+    L, _, _ = loss_eq5(lengths, lengths, x, z, S)
+    return L
+
+
+def chain_backward(lengths, s, ws, S=1):
+    """Loss and gradients of a chain of square blocks under Equation 5.
+    Returns (L, g_s, [per-block weight gradients])."""
+    xs = [np.asarray(s, dtype=np.float64)]
+    z = None
+    for w in ws:
+        x, z = block(lengths, xs[-1], w)
+        xs.append(x)
+    L, g_x, g_z = loss_eq5(lengths, lengths, xs[-1], z, S)
+    grads = [None] * len(ws)
+    g = g_x
+    for k in range(len(ws) - 1, -1, -1):
+        r = block_backward(lengths, xs[k], ws[k], g, g_z if k == len(ws) - 1 else None)
+        g = r.pop("s")
+        grads[k] = r
+    return L, g, grads
