@@ -275,6 +275,118 @@ nt_status nt_pair_block_rect(const nt_partition* p, const void* s_rows, const vo
                              int32_t c_z, int32_t hidden, nt_dtype dtype, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Backward pass and loss (Section 4: the measured step is forward, loss and
+ * backward; Section 3.4: gradients reach the projections, the pair update
+ * and the reduction of Equation 1 through the packed storage). Gradients
+ * are fp32 whatever the storage type. With NT_BF16 the transition's products
+ * read their operands rounded to bf16 (G, the hidden gradient g_H, the
+ * hidden activations H) and accumulate in fp32, as the forward does.
+ * ------------------------------------------------------------------------ */
+
+/* The weight gradients of one block (fp32, [out, in] like the weights). */
+typedef struct nt_block_grads {
+  float* Wa;
+  float* Wb;
+  float* W1;
+  float* W2;
+  float* Wo;
+} nt_block_grads;
+
+/*
+ * Workspace bytes nt_pair_loss_eq5 needs: one fp64 per single row.
+ */
+nt_status nt_loss_workspace_bytes(const nt_partition* p, size_t* bytes);
+
+/*
+ * The sample-weighted squared loss of Appendix A.1, Equation 5, over a
+ * block's returned singles x [T, c_s] and pair state pz [cells, c_z]:
+ *   L = sum_i alpha_i |x_i|^2 / (S c_s sum_i N_i)
+ *     + sum_i beta_i |pz_i|^2 / (S c_z sum_i N_i M_i),
+ *   alpha_i = 1 + i / B, beta_i = 1.5 - i / (2 B), i = 0 .. B - 1,
+ * with S = 1 for the leading layouts (S >= 1 is accepted for others). The
+ * squares accumulate in fp32 per row and the rows' terms in fp64 into
+ * *loss (device, one double). g_x [T, c_s] and g_pz [cells, c_z] (fp32,
+ * either may be NULL) receive 2 alpha_i x / (S c_s sum N) and
+ * 2 beta_i pz / (S c_z sum N M). Deterministic. workspace: device, at least
+ * nt_loss_workspace_bytes, 16-byte aligned.
+ */
+nt_status nt_pair_loss_eq5(const nt_partition* p, const void* x, int32_t c_s, const void* pz,
+                           int32_t c_z, int32_t S, nt_dtype dtype, double* loss, float* g_x,
+                           float* g_pz, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Adjoint of the column mean (Equation 4 divided by M_i): every cell of pair
+ * row r of sample i receives g_m[eta_i + r] / M_i, added to g_z_in when it
+ * is not NULL:  G[o_i + r M_i + c] = g_z_in[...] + g_m[eta_i + r] / M_i.
+ * g_m: fp32 [T, c_z]; g_z_in, G: fp32 [cells, c_z]; G may equal g_z_in.
+ */
+nt_status nt_pair_reduce_backward(const nt_partition* p, const float* g_m, const float* g_z_in,
+                                  float* G, int32_t c_z, void* stream);
+
+/*
+ * Adjoint of the broadcast (Equation 1, first line): the row singles'
+ * gradient sums each pair row over its columns and the column singles'
+ * gradient sums each pair column over its rows:
+ *   g_a[eta_i + r] = sum_c g_z[o_i + r M_i + c],
+ *   g_b[mu_i + c]  = sum_r g_z[o_i + r M_i + c].
+ * g_z: fp32 [cells, c_z]; g_a: fp32 [T, c_z]; g_b: fp32 [T_cols, c_z].
+ * Deterministic (fixed summation order, no atomics).
+ */
+nt_status nt_pair_broadcast_backward(const nt_partition* p, const float* g_z, float* g_a,
+                                     float* g_b, int32_t c_z, void* stream);
+
+/*
+ * Workspace bytes nt_pair_transition_backward needs.
+ */
+nt_status nt_transition_backward_workspace_bytes(const nt_partition* p, int32_t c_z,
+                                                 int32_t hidden, nt_dtype dtype, size_t* bytes);
+
+/*
+ * Gradient of the residual transition z' = z + relu(z W1^T) W2^T for an
+ * incoming G = dL/dz' (fp32 [cells, c_z]):
+ *   pre = z W1^T, g_H = (G W2) * [pre > 0]   (relu'(0) = 0),
+ *   g_z = G + g_H W1,  dW1 = g_H^T z,  dW2 = G^T relu(pre).
+ * z: [cells, c_z] of `dtype` (the transition's input); W1: [hidden, c_z];
+ * W2: [c_z, hidden]; g_z: fp32 [cells, c_z], may equal G; dW1: fp32
+ * [hidden, c_z] and dW2: fp32 [c_z, hidden] are overwritten. The weight
+ * gradients are contractions over all cells, summed in fixed order.
+ * workspace: device, at least nt_transition_backward_workspace_bytes,
+ * 16-byte aligned (it holds H and g_H per cell).
+ */
+nt_status nt_pair_transition_backward(const nt_partition* p, const void* z, const float* G,
+                                      const void* W1, const void* W2, float* g_z, float* dW1,
+                                      float* dW2, int32_t c_z, int32_t hidden, nt_dtype dtype,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes nt_pair_block_backward needs.
+ */
+nt_status nt_block_backward_workspace_bytes(const nt_partition* p, int32_t c_s, int32_t c_z,
+                                            int32_t hidden, nt_dtype dtype, size_t* bytes);
+
+/*
+ * Backward of one square block (nt_pair_block) by the chain rule, step by
+ * step in reverse: for incoming g_s_out = dL/ds~ (fp32 [T, c_s]) and,
+ * optionally, g_z_out = dL/dz~ (fp32 [cells, c_z], NULL when the loss does
+ * not read the pair state):
+ *   g_m = g_s_out Wo,             dWo = g_s_out^T m,
+ *   G = g_z_out + g_m[row] / N_i  (the mean's adjoint),
+ *   g_z, dW1, dW2 = transition backward at z = a[row] + b[col],
+ *   g_a, g_b = row and column sums of g_z,
+ *   g_s_in = g_s_out + g_a Wa + g_b Wb,  dWa = g_a^T s,  dWb = g_b^T s.
+ * s_in: the block's input singles [T, c_s]; z_out: its returned pair state
+ * [cells, c_z] (m is recomputed from it); weights as for nt_pair_block.
+ * g_s_in: fp32 [T, c_s], may equal g_s_out; grads: fp32 outputs,
+ * overwritten. a, b and z are recomputed from s_in. workspace: device, at
+ * least nt_block_backward_workspace_bytes, 16-byte aligned.
+ */
+nt_status nt_pair_block_backward(const nt_partition* p, const void* s_in, const void* z_out,
+                                 const nt_block_weights* w, const float* g_s_out,
+                                 const float* g_z_out, float* g_s_in, const nt_block_grads* grads,
+                                 int32_t c_s, int32_t c_z, int32_t hidden, nt_dtype dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Thread-local description of the last failure in this thread ("" if none). */
 const char* nt_last_error(void);
 

@@ -353,3 +353,134 @@ def nt_pair_block_rect(p: Partition, s_rows, s_cols, weights, s_out=None, z_out=
                                             hidden, _dtype_code(s_rows), _ptr(workspace),
                                             workspace.numel(), _stream(stream, s_rows.device)))
     return s_out, z_out
+
+
+# ------------------------------------------------------------------ backward
+_WEIGHT_NAMES = ("Wa", "Wb", "W1", "W2", "Wo")
+
+
+def _code(dtype) -> int:
+    return dtype if isinstance(dtype, int) else (NT_BF16 if "bfloat16" in str(dtype) else NT_F32)
+
+
+def nt_loss_workspace_bytes(p: Partition) -> int:
+    n = ctypes.c_size_t()
+    _check(_native.lib().nt_loss_workspace_bytes(ctypes.byref(p.struct), ctypes.byref(n)))
+    return n.value
+
+
+def nt_pair_loss_eq5(p: Partition, x, pz, S: int = 1, grads: bool = True, workspace=None,
+                     stream=None):
+    """Equation 5 over singles x [T, c_s] and pair state pz [cells, c_z].
+    Returns (loss, g_x, g_pz): loss a float64 device tensor of one element,
+    the gradients fp32 (None when grads is False)."""
+    torch = _torch()
+    dev = x.device
+    if pz.dtype != x.dtype:
+        raise TypeError("x and pz must share a dtype")
+    loss = torch.empty(2, dtype=torch.float64, device=dev)  # 16 bytes, aligned
+    g_x = torch.empty(x.shape, dtype=torch.float32, device=dev) if grads else None
+    g_pz = torch.empty(pz.shape, dtype=torch.float32, device=dev) if grads else None
+    if workspace is None:
+        workspace = torch.empty(nt_loss_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    _check(_native.lib().nt_pair_loss_eq5(ctypes.byref(p.struct), _ptr(x), x.shape[-1], _ptr(pz),
+                                          pz.shape[-1], S, _dtype_code(x), _ptr(loss), _ptr(g_x),
+                                          _ptr(g_pz), _ptr(workspace), workspace.numel(),
+                                          _stream(stream, dev)))
+    return loss[:1], g_x, g_pz
+
+
+def nt_pair_reduce_backward(p: Partition, g_m, g_z_in=None, G=None, stream=None):
+    """G = g_z_in (or 0) + g_m[row] / M_i on every cell (fp32)."""
+    torch = _torch()
+    c_z = g_m.shape[-1]
+    if G is None:
+        G = torch.empty((p.cells, c_z), dtype=torch.float32, device=g_m.device)
+    _check(_native.lib().nt_pair_reduce_backward(ctypes.byref(p.struct), _ptr(g_m), _ptr(g_z_in),
+                                                 _ptr(G), c_z, _stream(stream, g_m.device)))
+    return G
+
+
+def nt_pair_broadcast_backward(p: Partition, g_z, g_a=None, g_b=None, stream=None):
+    """Row sums g_a [T, c_z] and column sums g_b [T_cols, c_z] of g_z (fp32)."""
+    torch = _torch()
+    c_z = g_z.shape[-1]
+    if g_a is None:
+        g_a = torch.empty((p.T, c_z), dtype=torch.float32, device=g_z.device)
+    if g_b is None:
+        g_b = torch.empty((p.T_cols, c_z), dtype=torch.float32, device=g_z.device)
+    _check(_native.lib().nt_pair_broadcast_backward(ctypes.byref(p.struct), _ptr(g_z), _ptr(g_a),
+                                                    _ptr(g_b), c_z, _stream(stream, g_z.device)))
+    return g_a, g_b
+
+
+def nt_transition_backward_workspace_bytes(p: Partition, c_z: int, hidden: int, dtype) -> int:
+    n = ctypes.c_size_t()
+    _check(_native.lib().nt_transition_backward_workspace_bytes(
+        ctypes.byref(p.struct), c_z, hidden, _code(dtype), ctypes.byref(n)))
+    return n.value
+
+
+def nt_pair_transition_backward(p: Partition, z, G, W1, W2, g_z=None, dW1=None, dW2=None,
+                                workspace=None, stream=None):
+    """Gradient of z + relu(z W1^T) W2^T for G = dL/dz' (fp32). Returns
+    (g_z, dW1, dW2), all fp32; g_z may be G (in place)."""
+    torch = _torch()
+    dev = z.device
+    c_z, hidden = z.shape[-1], W1.shape[0]
+    f32 = torch.float32
+    if g_z is None:
+        g_z = torch.empty((p.cells, c_z), dtype=f32, device=dev)
+    if dW1 is None:
+        dW1 = torch.empty((hidden, c_z), dtype=f32, device=dev)
+    if dW2 is None:
+        dW2 = torch.empty((c_z, hidden), dtype=f32, device=dev)
+    if workspace is None:
+        need = nt_transition_backward_workspace_bytes(p, c_z, hidden, _dtype_code(z))
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(_native.lib().nt_pair_transition_backward(
+        ctypes.byref(p.struct), _ptr(z), _ptr(G), _ptr(W1), _ptr(W2), _ptr(g_z), _ptr(dW1),
+        _ptr(dW2), c_z, hidden, _dtype_code(z), _ptr(workspace), workspace.numel(),
+        _stream(stream, dev)))
+    return g_z, dW1, dW2
+
+
+def nt_block_backward_workspace_bytes(p: Partition, c_s: int, c_z: int, hidden: int,
+                                      dtype) -> int:
+    n = ctypes.c_size_t()
+    _check(_native.lib().nt_block_backward_workspace_bytes(ctypes.byref(p.struct), c_s, c_z,
+                                                           hidden, _code(dtype),
+                                                           ctypes.byref(n)))
+    return n.value
+
+
+def nt_pair_block_backward(p: Partition, s_in, z_out, weights, g_s_out, g_z_out=None,
+                           g_s_in=None, grads=None, workspace=None, stream=None):
+    """Backward of nt_pair_block: s_in and z_out are the block's input singles
+    and returned pair state, g_s_out (and optionally g_z_out) the incoming
+    fp32 gradients. Returns (g_s_in, grads) with grads a dict of fp32 weight
+    gradients keyed like the weights."""
+    torch = _torch()
+    dev = s_in.device
+    if isinstance(weights, dict):
+        weights = [weights[k] for k in _WEIGHT_NAMES]
+    Wa, Wb, W1, W2, Wo = weights
+    c_s, c_z, hidden = s_in.shape[-1], Wa.shape[0], W1.shape[0]
+    for w in weights:
+        if w.dtype != s_in.dtype:
+            raise TypeError("weights must share s_in's dtype")
+    if g_s_in is None:
+        g_s_in = torch.empty((p.T, c_s), dtype=torch.float32, device=dev)
+    if grads is None:
+        grads = {k: torch.empty(w.shape, dtype=torch.float32, device=dev)
+                 for k, w in zip(_WEIGHT_NAMES, weights)}
+    if workspace is None:
+        need = nt_block_backward_workspace_bytes(p, c_s, c_z, hidden, _dtype_code(s_in))
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    wst = NtBlockWeights(*[_ptr(w) for w in weights])
+    gst = _native.NtBlockGrads(*[_ptr(grads[k]) for k in _WEIGHT_NAMES])
+    _check(_native.lib().nt_pair_block_backward(
+        ctypes.byref(p.struct), _ptr(s_in), _ptr(z_out), ctypes.byref(wst), _ptr(g_s_out),
+        _ptr(g_z_out), _ptr(g_s_in), ctypes.byref(gst), c_s, c_z, hidden, _dtype_code(s_in),
+        _ptr(workspace), workspace.numel(), _stream(stream, dev)))
+    return g_s_in, grads

@@ -17,8 +17,11 @@ EXPORTS = ("nt_partition_sizes", "nt_make_partition", "nt_partition_sizes_rect",
            "nt_make_partition_rect", "nt_decode_cells", "nt_pair_broadcast",
            "nt_pair_transition", "nt_pair_broadcast_transition", "nt_pair_transition_swiglu",
            "nt_pair_reduce",
-           "nt_block_workspace_bytes", "nt_pair_block", "nt_pair_block_rect", "nt_last_error",
-           "nt_version")
+           "nt_block_workspace_bytes", "nt_pair_block", "nt_pair_block_rect",
+           "nt_loss_workspace_bytes", "nt_pair_loss_eq5", "nt_pair_reduce_backward",
+           "nt_pair_broadcast_backward", "nt_transition_backward_workspace_bytes",
+           "nt_pair_transition_backward", "nt_block_backward_workspace_bytes",
+           "nt_pair_block_backward", "nt_last_error", "nt_version")
 
 
 class NtPartition(ctypes.Structure):
@@ -35,6 +38,11 @@ class NtPartition(ctypes.Structure):
 
 
 class NtBlockWeights(ctypes.Structure):
+    _fields_ = [("Wa", ctypes.c_void_p), ("Wb", ctypes.c_void_p), ("W1", ctypes.c_void_p),
+                ("W2", ctypes.c_void_p), ("Wo", ctypes.c_void_p)]
+
+
+class NtBlockGrads(ctypes.Structure):
     _fields_ = [("Wa", ctypes.c_void_p), ("Wb", ctypes.c_void_p), ("W1", ctypes.c_void_p),
                 ("W2", ctypes.c_void_p), ("Wo", ctypes.c_void_p)]
 
@@ -76,6 +84,16 @@ def lib() -> ctypes.CDLL:
                           sz, vp],
         "nt_pair_block_rect": [part, vp, vp, vp, vp, P(NtBlockWeights), i32, i32, i32,
                                ctypes.c_int, vp, sz, vp],
+        "nt_loss_workspace_bytes": [part, P(sz)],
+        "nt_pair_loss_eq5": [part, vp, i32, vp, i32, i32, ctypes.c_int, vp, vp, vp, vp, sz, vp],
+        "nt_pair_reduce_backward": [part, vp, vp, vp, i32, vp],
+        "nt_pair_broadcast_backward": [part, vp, vp, vp, i32, vp],
+        "nt_transition_backward_workspace_bytes": [part, i32, i32, ctypes.c_int, P(sz)],
+        "nt_pair_transition_backward": [part, vp, vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_int,
+                                        vp, sz, vp],
+        "nt_block_backward_workspace_bytes": [part, i32, i32, i32, ctypes.c_int, P(sz)],
+        "nt_pair_block_backward": [part, vp, vp, P(NtBlockWeights), vp, vp, vp, P(NtBlockGrads),
+                                   i32, i32, i32, ctypes.c_int, vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)

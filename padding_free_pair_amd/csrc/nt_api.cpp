@@ -273,6 +273,128 @@ nt_status pair_block(const nt_partition* p, const void* s_rows, const void* s_co
                     "output projection");
 }
 
+// ---------------------------------------------------------------------------
+// Backward helpers.
+
+// One array of a call: outputs must not overlap anything else of the call.
+struct Arr {
+  const char* name;
+  const void* ptr;
+  uint64_t bytes;
+  bool out;
+};
+
+// Every output is disjoint from every other array, except the pairs listed
+// in `same` (index pairs that may be the identical pointer, e.g. in-place).
+nt_status check_disjoint(const Arr* a, int n, const int (*same)[2] = nullptr, int nsame = 0) {
+  for (int i = 0; i < n; ++i)
+    for (int j = i + 1; j < n; ++j) {
+      if (!a[i].out && !a[j].out) continue;
+      bool allowed = false;
+      for (int k = 0; k < nsame; ++k)
+        if (((same[k][0] == i && same[k][1] == j) || (same[k][0] == j && same[k][1] == i)) &&
+            a[i].ptr == a[j].ptr)
+          allowed = true;
+      if (!allowed && overlaps(a[i].ptr, a[i].bytes, a[j].ptr, a[j].bytes))
+        return fail(NT_ERR_INVALID, "%s overlaps %s", a[i].name, a[j].name);
+    }
+  return NT_OK;
+}
+
+nt_status check_workspace(const void* ws, size_t have, uint64_t need) {
+  if (need == 0) return NT_OK;
+  NT_TRY(check_array("workspace", ws, need));
+  if (have < need)
+    return fail(NT_ERR_WORKSPACE, "workspace has %zu bytes, needs %llu", have,
+                (unsigned long long)need);
+  return NT_OK;
+}
+
+// Transition backward workspace: H and g_H per cell (storage type), G in the
+// storage type (dW2 reads it after g_z may have overwritten G), the
+// transposed weights, and the split partials of the weight gradients (both
+// are hidden x c_z contractions over the cells).
+struct TransBwdWs {
+  uint64_t H, GH, Gb, W1T, W2T, part, total;
+  int splits;
+};
+
+TransBwdWs transition_backward_ws(int64_t cells, int c_z, int hidden, nt_dtype dtype) {
+  TransBwdWs w;
+  const uint64_t es = esize(dtype);
+  const uint64_t hb = nt::align256((size_t)cells * hidden * es);
+  uint64_t off = 0;
+  w.H = off;    off += hb;
+  w.GH = off;   off += hb;
+  w.Gb = off;   off += nt::align256((size_t)cells * c_z * es);
+  w.W1T = off;  off += nt::align256((size_t)hidden * c_z * es);
+  w.W2T = off;  off += nt::align256((size_t)hidden * c_z * es);
+  w.splits = nt::gemm_tn_splits(cells, hidden, c_z);
+  w.part = off; off += nt::align256((size_t)w.splits * hidden * c_z * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+nt_status transition_backward(const nt_partition* p, const void* z, const float* G,
+                              const void* W1, const void* W2, float* g_z, float* dW1, float* dW2,
+                              int c_z, int hidden, nt_dtype dtype, char* ws, hipStream_t s) {
+  const TransBwdWs w = transition_backward_ws(p->cells, c_z, hidden, dtype);
+  void* H = ws + w.H;
+  void* GH = ws + w.GH;
+  void* Gb = ws + w.Gb;
+  float* part = reinterpret_cast<float*>(ws + w.part);
+  NT_TRY(hip_status(nt::launch_transition_backward_generic(*p, z, G, W1, W2, g_z, H, GH, Gb, c_z,
+                                                           hidden, dtype, s),
+                    "transition backward"));
+  // dW1 = g_H^T z ; dW2 = G^T H with G as stored in Gb
+  NT_TRY(hip_status(nt::launch_gemm_tn(GH, dtype, z, dtype, dW1, part, p->cells, hidden, c_z,
+                                       w.splits, s),
+                    "dW1 contraction"));
+  return hip_status(nt::launch_gemm_tn(Gb, dtype, H, dtype, dW2, part, p->cells, c_z, hidden,
+                                       w.splits, s),
+                    "dW2 contraction");
+}
+
+// Block backward workspace (square partitions): a, b (fp32), z (storage
+// type), m, g_m, G (fp32; G becomes g_z in place), g_a, g_b (fp32), the
+// transposed projection weights, the projections' split partials, then the
+// transition backward's own workspace.
+struct BlockBwdWs {
+  uint64_t a, b, z, m, g_m, G, g_a, g_b, WoT, WaT, WbT, ppart, trans, total;
+  int psplits;
+};
+
+BlockBwdWs block_backward_ws(const nt_partition* p, int c_s, int c_z, int hidden,
+                             nt_dtype dtype) {
+  BlockBwdWs w;
+  const uint64_t es = esize(dtype);
+  const uint64_t single = nt::align256((size_t)p->T * c_z * sizeof(float));
+  const uint64_t proj = nt::align256((size_t)c_s * c_z * es);
+  uint64_t off = 0;
+  w.a = off;     off += single;
+  w.b = off;     off += single;
+  w.z = off;     off += nt::align256((size_t)p->cells * c_z * es);
+  w.m = off;     off += single;
+  w.g_m = off;   off += single;
+  w.G = off;     off += nt::align256((size_t)p->cells * c_z * sizeof(float));
+  w.g_a = off;   off += single;
+  w.g_b = off;   off += single;
+  w.WoT = off;   off += proj;
+  w.WaT = off;   off += proj;
+  w.WbT = off;   off += proj;
+  w.psplits = nt::gemm_tn_splits(p->T, c_z, c_s);
+  w.ppart = off; off += nt::align256((size_t)w.psplits * c_s * c_z * sizeof(float));
+  w.trans = off; off += transition_backward_ws(p->cells, c_z, hidden, dtype).total;
+  w.total = off;
+  return w;
+}
+
+nt_status check_widths(int32_t c_s, int32_t c_z, int32_t hidden) {
+  NT_TRY(check_width("c_s", c_s, nt::kMaxCs));
+  NT_TRY(check_width("c_z", c_z, nt::kMaxCz));
+  return check_width("hidden", hidden, nt::kMaxHidden);
+}
+
 }  // namespace
 
 extern "C" {
@@ -471,6 +593,227 @@ nt_status nt_pair_block_rect(const nt_partition* p, const void* s_rows, const vo
                              size_t workspace_bytes, void* stream) {
   return pair_block(p, s_rows, s_cols, s_out, z_out, w, c_s, c_z, hidden, dtype, workspace,
                     workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Backward pass and loss.
+
+nt_status nt_loss_workspace_bytes(const nt_partition* p, size_t* bytes) {
+  NT_TRY(check_partition(p));
+  if (!bytes) return fail(NT_ERR_NULL, "bytes is NULL");
+  *bytes = nt::align256((size_t)(p->T > 0 ? p->T : 1) * sizeof(double));
+  return ok();
+}
+
+nt_status nt_pair_loss_eq5(const nt_partition* p, const void* x, int32_t c_s, const void* pz,
+                           int32_t c_z, int32_t S, nt_dtype dtype, double* loss, float* g_x,
+                           float* g_pz, void* workspace, size_t workspace_bytes, void* stream) {
+  NT_TRY(check_partition(p));
+  NT_TRY(check_dtype(dtype));
+  NT_TRY(check_width("c_s", c_s, nt::kMaxCs));
+  NT_TRY(check_width("c_z", c_z, nt::kMaxCz));
+  if (S < 1) return fail(NT_ERR_INVALID, "S = %d must be at least 1", (int)S);
+  const uint64_t es = esize(dtype);
+  const uint64_t xb = (uint64_t)p->T * c_s * es, pb = (uint64_t)p->cells * c_z * es;
+  const uint64_t gxb = (uint64_t)p->T * c_s * 4, gpb = (uint64_t)p->cells * c_z * 4;
+  const uint64_t need = nt::align256((size_t)(p->T > 0 ? p->T : 1) * sizeof(double));
+  NT_TRY(check_array("x", x, xb));
+  NT_TRY(check_array("pz", pz, pb));
+  NT_TRY(check_array("loss", loss, sizeof(double)));
+  if (g_x) NT_TRY(check_array("g_x", g_x, gxb));
+  if (g_pz) NT_TRY(check_array("g_pz", g_pz, gpb));
+  NT_TRY(check_workspace(workspace, workspace_bytes, need));
+  const Arr arrs[] = {{"x", x, xb, false},           {"pz", pz, pb, false},
+                      {"loss", loss, sizeof(double), true}, {"g_x", g_x, g_x ? gxb : 0, true},
+                      {"g_pz", g_pz, g_pz ? gpb : 0, true}, {"workspace", workspace, need, true}};
+  NT_TRY(check_disjoint(arrs, 6));
+  return hip_status(nt::launch_loss_eq5(*p, x, c_s, pz, c_z, S, dtype,
+                                        static_cast<double*>(workspace), loss, g_x, g_pz,
+                                        static_cast<hipStream_t>(stream)),
+                    "loss kernels");
+}
+
+nt_status nt_pair_reduce_backward(const nt_partition* p, const float* g_m, const float* g_z_in,
+                                  float* G, int32_t c_z, void* stream) {
+  NT_TRY(check_partition(p));
+  NT_TRY(check_width("c_z", c_z, nt::kMaxCz));
+  const uint64_t mb = (uint64_t)p->T * c_z * 4, gb = (uint64_t)p->cells * c_z * 4;
+  NT_TRY(check_array("g_m", g_m, mb));
+  if (g_z_in) NT_TRY(check_array("g_z_in", g_z_in, gb));
+  NT_TRY(check_array("G", G, gb));
+  const Arr arrs[] = {{"g_m", g_m, mb, false}, {"g_z_in", g_z_in, g_z_in ? gb : 0, false},
+                      {"G", G, gb, true}};
+  const int same[][2] = {{1, 2}};
+  NT_TRY(check_disjoint(arrs, 3, same, 1));
+  return hip_status(
+      nt::launch_mean_backward(*p, g_m, g_z_in, G, c_z, static_cast<hipStream_t>(stream)),
+      "mean backward kernel");
+}
+
+nt_status nt_pair_broadcast_backward(const nt_partition* p, const float* g_z, float* g_a,
+                                     float* g_b, int32_t c_z, void* stream) {
+  NT_TRY(check_partition(p));
+  NT_TRY(check_width("c_z", c_z, nt::kMaxCz));
+  const uint64_t zb = (uint64_t)p->cells * c_z * 4;
+  const uint64_t ab = (uint64_t)p->T * c_z * 4, bb = (uint64_t)p->T_cols * c_z * 4;
+  NT_TRY(check_array("g_z", g_z, zb));
+  NT_TRY(check_array("g_a", g_a, ab));
+  NT_TRY(check_array("g_b", g_b, bb));
+  const Arr arrs[] = {{"g_z", g_z, zb, false}, {"g_a", g_a, ab, true}, {"g_b", g_b, bb, true}};
+  NT_TRY(check_disjoint(arrs, 3));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  NT_TRY(hip_status(nt::launch_reduce(*p, g_z, g_a, c_z, NT_F32, s, false), "row sums"));
+  return hip_status(nt::launch_col_sums(*p, g_z, g_b, c_z, s), "column sums");
+}
+
+nt_status nt_transition_backward_workspace_bytes(const nt_partition* p, int32_t c_z,
+                                                 int32_t hidden, nt_dtype dtype, size_t* bytes) {
+  NT_TRY(check_partition(p));
+  NT_TRY(check_dtype(dtype));
+  NT_TRY(check_width("c_z", c_z, nt::kMaxCz));
+  NT_TRY(check_width("hidden", hidden, nt::kMaxHidden));
+  if (!bytes) return fail(NT_ERR_NULL, "bytes is NULL");
+  *bytes = transition_backward_ws(p->cells, c_z, hidden, dtype).total;
+  return ok();
+}
+
+nt_status nt_pair_transition_backward(const nt_partition* p, const void* z, const float* G,
+                                      const void* W1, const void* W2, float* g_z, float* dW1,
+                                      float* dW2, int32_t c_z, int32_t hidden, nt_dtype dtype,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  NT_TRY(check_partition(p));
+  NT_TRY(check_dtype(dtype));
+  NT_TRY(check_width("c_z", c_z, nt::kMaxCz));
+  NT_TRY(check_width("hidden", hidden, nt::kMaxHidden));
+  const uint64_t es = esize(dtype);
+  const uint64_t zb = (uint64_t)p->cells * c_z * es, fb = (uint64_t)p->cells * c_z * 4;
+  const uint64_t wb = (uint64_t)hidden * c_z * es, db = (uint64_t)hidden * c_z * 4;
+  const uint64_t need = transition_backward_ws(p->cells, c_z, hidden, dtype).total;
+  NT_TRY(check_array("z", z, zb));
+  NT_TRY(check_array("G", G, fb));
+  NT_TRY(check_array("W1", W1, wb));
+  NT_TRY(check_array("W2", W2, wb));
+  NT_TRY(check_array("g_z", g_z, fb));
+  NT_TRY(check_array("dW1", dW1, db));
+  NT_TRY(check_array("dW2", dW2, db));
+  NT_TRY(check_workspace(workspace, workspace_bytes, need));
+  const Arr arrs[] = {{"z", z, zb, false},     {"G", G, fb, false},
+                      {"W1", W1, wb, false},   {"W2", W2, wb, false},
+                      {"g_z", g_z, fb, true},  {"dW1", dW1, db, true},
+                      {"dW2", dW2, db, true},  {"workspace", workspace, need, true}};
+  const int same[][2] = {{1, 4}};
+  NT_TRY(check_disjoint(arrs, 8, same, 1));
+  return transition_backward(p, z, G, W1, W2, g_z, dW1, dW2, c_z, hidden, dtype,
+                             static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+nt_status nt_block_backward_workspace_bytes(const nt_partition* p, int32_t c_s, int32_t c_z,
+                                            int32_t hidden, nt_dtype dtype, size_t* bytes) {
+  NT_TRY(check_partition(p));
+  NT_TRY(check_dtype(dtype));
+  NT_TRY(check_widths(c_s, c_z, hidden));
+  if (!bytes) return fail(NT_ERR_NULL, "bytes is NULL");
+  *bytes = block_backward_ws(p, c_s, c_z, hidden, dtype).total;
+  return ok();
+}
+
+nt_status nt_pair_block_backward(const nt_partition* p, const void* s_in, const void* z_out,
+                                 const nt_block_weights* w, const float* g_s_out,
+                                 const float* g_z_out, float* g_s_in, const nt_block_grads* grads,
+                                 int32_t c_s, int32_t c_z, int32_t hidden, nt_dtype dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  NT_TRY(check_partition(p));
+  if (p->col_offsets != p->single_offsets)
+    return fail(NT_ERR_INVALID, "the block backward takes square partitions");
+  NT_TRY(check_dtype(dtype));
+  NT_TRY(check_widths(c_s, c_z, hidden));
+  if (!w) return fail(NT_ERR_NULL, "weights is NULL");
+  if (!grads) return fail(NT_ERR_NULL, "grads is NULL");
+  const uint64_t es = esize(dtype);
+  const uint64_t sb = (uint64_t)p->T * c_s * es, zb = (uint64_t)p->cells * c_z * es;
+  const uint64_t gsb = (uint64_t)p->T * c_s * 4, gzb = (uint64_t)p->cells * c_z * 4;
+  const uint64_t proj = (uint64_t)c_z * c_s * es, mlp = (uint64_t)c_z * hidden * es;
+  const uint64_t dproj = (uint64_t)c_z * c_s * 4, dmlp = (uint64_t)c_z * hidden * 4;
+  const BlockBwdWs L = block_backward_ws(p, c_s, c_z, hidden, dtype);
+  NT_TRY(check_array("s_in", s_in, sb));
+  NT_TRY(check_array("z_out", z_out, zb));
+  NT_TRY(check_array("Wa", w->Wa, proj));
+  NT_TRY(check_array("Wb", w->Wb, proj));
+  NT_TRY(check_array("W1", w->W1, mlp));
+  NT_TRY(check_array("W2", w->W2, mlp));
+  NT_TRY(check_array("Wo", w->Wo, proj));
+  NT_TRY(check_array("g_s_out", g_s_out, gsb));
+  if (g_z_out) NT_TRY(check_array("g_z_out", g_z_out, gzb));
+  NT_TRY(check_array("g_s_in", g_s_in, gsb));
+  NT_TRY(check_array("dWa", grads->Wa, dproj));
+  NT_TRY(check_array("dWb", grads->Wb, dproj));
+  NT_TRY(check_array("dW1", grads->W1, dmlp));
+  NT_TRY(check_array("dW2", grads->W2, dmlp));
+  NT_TRY(check_array("dWo", grads->Wo, dproj));
+  NT_TRY(check_workspace(workspace, workspace_bytes, L.total));
+  const Arr arrs[] = {
+      {"s_in", s_in, sb, false},          {"z_out", z_out, zb, false},
+      {"Wa", w->Wa, proj, false},         {"Wb", w->Wb, proj, false},
+      {"W1", w->W1, mlp, false},          {"W2", w->W2, mlp, false},
+      {"Wo", w->Wo, proj, false},         {"g_s_out", g_s_out, gsb, false},
+      {"g_z_out", g_z_out, g_z_out ? gzb : 0, false},
+      {"g_s_in", g_s_in, gsb, true},      {"dWa", grads->Wa, dproj, true},
+      {"dWb", grads->Wb, dproj, true},    {"dW1", grads->W1, dmlp, true},
+      {"dW2", grads->W2, dmlp, true},     {"dWo", grads->Wo, dproj, true},
+      {"workspace", workspace, L.total, true}};
+  const int same[][2] = {{7, 9}};
+  NT_TRY(check_disjoint(arrs, 16, same, 1));
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
+  float* a = reinterpret_cast<float*>(base + L.a);
+  float* b = reinterpret_cast<float*>(base + L.b);
+  void* z = base + L.z;
+  float* m = reinterpret_cast<float*>(base + L.m);
+  float* g_m = reinterpret_cast<float*>(base + L.g_m);
+  float* G = reinterpret_cast<float*>(base + L.G);
+  float* g_a = reinterpret_cast<float*>(base + L.g_a);
+  float* g_b = reinterpret_cast<float*>(base + L.g_b);
+  void* WoT = base + L.WoT;
+  void* WaT = base + L.WaT;
+  void* WbT = base + L.WbT;
+  float* ppart = reinterpret_cast<float*>(base + L.ppart);
+  const int64_t T = p->T;
+
+  // recompute the forward's a, b, z and m
+  NT_TRY(hip_status(nt::launch_linear2(s_in, dtype, w->Wa, w->Wb, a, b, T, c_z, c_s, s),
+                    "projections a, b"));
+  NT_TRY(hip_status(nt::launch_broadcast(*p, a, b, z, c_z, dtype, s, true), "broadcast"));
+  NT_TRY(hip_status(nt::launch_reduce(*p, z_out, m, c_z, dtype, s), "column mean"));
+  NT_TRY(hip_status(nt::launch_transpose(w->Wo, WoT, c_s, c_z, dtype, s), "transpose Wo"));
+  NT_TRY(hip_status(nt::launch_transpose(w->Wa, WaT, c_z, c_s, dtype, s), "transpose Wa"));
+  NT_TRY(hip_status(nt::launch_transpose(w->Wb, WbT, c_z, c_s, dtype, s), "transpose Wb"));
+  // s~ = s + m Wo^T
+  NT_TRY(hip_status(nt::launch_linear(g_s_out, NT_F32, WoT, dtype, nullptr, g_m, NT_F32, T, c_z,
+                                      c_s, s),
+                    "g_m = g_s Wo"));
+  NT_TRY(hip_status(nt::launch_gemm_tn(g_s_out, NT_F32, m, NT_F32, grads->Wo, ppart, T, c_s, c_z,
+                                       L.psplits, s),
+                    "dWo"));
+  // mean, transition, broadcast
+  NT_TRY(hip_status(nt::launch_mean_backward(*p, g_m, g_z_out, G, c_z, s), "mean backward"));
+  NT_TRY(transition_backward(p, z, G, w->W1, w->W2, G, grads->W1, grads->W2, c_z, hidden, dtype,
+                             base + L.trans, s));
+  NT_TRY(hip_status(nt::launch_reduce(*p, G, g_a, c_z, NT_F32, s, false), "row sums"));
+  NT_TRY(hip_status(nt::launch_col_sums(*p, G, g_b, c_z, s), "column sums"));
+  // a = s Wa^T, b = s Wb^T
+  NT_TRY(hip_status(nt::launch_linear(g_a, NT_F32, WaT, dtype, g_s_out, g_s_in, NT_F32, T, c_s,
+                                      c_z, s),
+                    "g_s += g_a Wa"));
+  NT_TRY(hip_status(nt::launch_linear(g_b, NT_F32, WbT, dtype, g_s_in, g_s_in, NT_F32, T, c_s,
+                                      c_z, s),
+                    "g_s += g_b Wb"));
+  NT_TRY(hip_status(nt::launch_gemm_tn(g_a, NT_F32, s_in, dtype, grads->Wa, ppart, T, c_z, c_s,
+                                       L.psplits, s),
+                    "dWa"));
+  return hip_status(nt::launch_gemm_tn(g_b, NT_F32, s_in, dtype, grads->Wb, ppart, T, c_z, c_s,
+                                       L.psplits, s),
+                    "dWb");
 }
 
 }  // extern "C"

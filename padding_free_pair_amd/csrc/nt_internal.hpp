@@ -96,8 +96,9 @@ hipError_t launch_partition_small(const int32_t* lengths_host, const int32_t* co
                                   hipStream_t stream);
 hipError_t launch_decode(const nt_partition& p, int32_t* sample, int32_t* row, int32_t* col,
                          hipStream_t stream);
+// f32_inputs: a and b are fp32 whatever dtype is (the projections' results).
 hipError_t launch_broadcast(const nt_partition& p, const void* a, const void* b, void* z, int c_z,
-                            nt_dtype dtype, hipStream_t stream);
+                            nt_dtype dtype, hipStream_t stream, bool f32_inputs = false);
 // z_in == nullptr selects the fused form: z is formed from fp32 a and b in
 // the prologue (a, b are fp32 [T, c_z] whatever the storage dtype).
 bool transition_has_mfma(int c_z, int hidden, nt_dtype dtype);
@@ -115,11 +116,13 @@ hipError_t launch_transition_prefetch(const nt_partition& p, const void* a, cons
 hipError_t launch_transition(const nt_partition& p, const void* z_in, const void* a, const void* b,
                              void* z_out, const void* W1, const void* W2, int c_z, int hidden,
                              nt_dtype dtype, hipStream_t stream);
+// mean == false: row sums instead of means (the broadcast's row adjoint).
 hipError_t launch_reduce(const nt_partition& p, const void* z, float* m, int c_z, nt_dtype dtype,
-                         hipStream_t stream);
+                         hipStream_t stream, bool mean = true);
 // C[M, N] = (R ? R : 0) + A[M, K] W[N, K]^T with fp32 accumulation. R has
 // C's type. Supported (A, W, C) types: (bf16, bf16, f32), (f32, bf16, bf16),
-// (f32, f32, f32).
+// (f32, bf16, f32), (f32, f32, f32). R may equal C (each element is read and
+// written by one thread).
 hipError_t launch_linear(const void* A, nt_dtype a_dtype, const void* W, nt_dtype w_dtype,
                          const void* R, void* C, nt_dtype c_dtype, int64_t M, int N, int K,
                          hipStream_t stream);
@@ -127,5 +130,30 @@ hipError_t launch_linear(const void* A, nt_dtype a_dtype, const void* W, nt_dtyp
 // (fp32 results; A and the weights are `a_dtype`).
 hipError_t launch_linear2(const void* A, nt_dtype a_dtype, const void* W0, const void* W1,
                           void* C0, void* C1, int64_t M, int N, int K, hipStream_t stream);
+
+// ---- backward (nt_backward.hip, nt_transition_bwd.hip)
+// G = g_in (or 0) + g_m[row] / M_i on every cell; G may equal g_in.
+hipError_t launch_mean_backward(const nt_partition& p, const float* g_m, const float* g_in,
+                                float* G, int c_z, hipStream_t stream);
+// g_b[mu_i + c] = sum_r g_z[o_i + r M_i + c] (fp32).
+hipError_t launch_col_sums(const nt_partition& p, const float* g_z, float* g_b, int c_z,
+                           hipStream_t stream);
+// Equation 5: partial [max(T, 1)] fp64 scratch, loss one fp64; g_x, g_pz may be null.
+hipError_t launch_loss_eq5(const nt_partition& p, const void* x, int c_s, const void* pz, int c_z,
+                           int S, nt_dtype dtype, double* partial, double* loss, float* g_x,
+                           float* g_pz, hipStream_t stream);
+hipError_t launch_transpose(const void* src, void* dst, int R, int C, nt_dtype dtype,
+                            hipStream_t stream);
+// C[M, N] = sum_k A[k, M] B[k, N]; partial holds splits * M * N floats.
+int gemm_tn_splits(int64_t K, int M, int N);
+hipError_t launch_gemm_tn(const void* A, nt_dtype a_dtype, const void* B, nt_dtype b_dtype,
+                          float* C, float* partial, int64_t K, int M, int N, int splits,
+                          hipStream_t stream);
+// Transition gradient without weight gradients: g_z, and H, GH and Gb (G in
+// the storage type) for them. g_z may equal G.
+hipError_t launch_transition_backward_generic(const nt_partition& p, const void* z,
+                                              const float* G, const void* W1, const void* W2,
+                                              float* g_z, void* H, void* GH, void* Gb, int c_z,
+                                              int hidden, nt_dtype dtype, hipStream_t stream);
 
 }  // namespace nt

@@ -250,6 +250,8 @@ hipError_t launch_linear(const void* A, nt_dtype a_dtype, const void* W, nt_dtyp
   }
   if (a_dtype == NT_F32 && w_dtype == NT_BF16 && c_dtype == NT_BF16)
     return launch_t<float, bf16, bf16, false>(A, W, R, C, M, N, K, stream);
+  if (a_dtype == NT_F32 && w_dtype == NT_BF16 && c_dtype == NT_F32)
+    return launch_t<float, bf16, float, false>(A, W, R, C, M, N, K, stream);
   if (a_dtype == NT_F32 && w_dtype == NT_F32 && c_dtype == NT_F32)
     return launch_t<float, float, float, false>(A, W, R, C, M, N, K, stream);
   return hipErrorInvalidValue;  // combination not used by the block

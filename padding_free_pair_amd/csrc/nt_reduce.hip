@@ -1,6 +1,8 @@
 // Column mean over packed pair rows (DanLing NestedTensor, Equation 4 and the
 // mean of Equation 1's third line), M_i cells per row (N_i for square pairs):
 //   m[eta_i + r, :] = (1 / M_i) * sum_{c < M_i} z[o_i + r M_i + c, :].
+// With `mean` false the sum is returned undivided: the row operand's
+// gradient of the broadcast (Equation 1's first line differentiated).
 // HBM-read bound. Deterministic: each row is summed by one wave or one
 // workgroup in a fixed order (no atomics).
 #include "nt_device.hpp"
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_pow2(
     const T* __restrict__ z, float* __restrict__ m, const int64_t* __restrict__ item_offsets,
     const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
     const int32_t* __restrict__ lengths, const int32_t* __restrict__ col_lengths, int B,
-    int c_z) {
+    int c_z, bool mean) {
   constexpr int VEC = Vec16<T>::N;
   constexpr int CLW = 64 / G;
   __shared__ float part[kWaves][G * VEC];
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_pow2(
   const int64_t eta = single_offsets[i];
   const int64_t o = pair_offsets[i];
   const int64_t j = item - item_offsets[i];
-  const float nf = (float)n;
+  const float nf = mean ? (float)n : 1.f;  // dividing by 1 is exact
   float acc[VEC];
   if (n >= kLongRow) {
     // one row, every wave takes a share of its cells
@@ -123,13 +125,14 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void k_reduce_generic(
     const T* __restrict__ z, float* __restrict__ m, const int64_t* __restrict__ row_splits,
     const int32_t* __restrict__ row_sample, const int32_t* __restrict__ col_lengths, int64_t T_rows,
-    int c_z, int G) {
+    int c_z, int G, bool mean) {
   constexpr int VEC = Vec16<T>::N;
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= T_rows * G) return;
   const int64_t g = idx / G;
   const int f = (int)(idx - g * G);
   const int64_t n = col_lengths[row_sample[g]];
+  const float nf = mean ? (float)n : 1.f;
   float acc[VEC];
   row_partial<T>(acc, z + row_splits[g] * c_z + f * VEC, 0, n, 1, c_z);
   float* dst = m + g * c_z + f * VEC;
@@ -137,47 +140,48 @@ __global__ __launch_bounds__(kThreads) void k_reduce_generic(
   for (int q = 0; q < VEC / 4; ++q) {
     Vec16<float> out;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out.set(e, acc[4 * q + e] / (float)n);
+    for (int e = 0; e < 4; ++e) out.set(e, acc[4 * q + e] / nf);
     store16(dst + 4 * q, out);
   }
 }
 
 template <typename T, int G>
-hipError_t launch_pow2(const nt_partition& p, const void* z, float* m, int c_z,
+hipError_t launch_pow2(const nt_partition& p, const void* z, float* m, int c_z, bool mean,
                        hipStream_t stream) {
   hipLaunchKernelGGL((k_reduce_pow2<T, G>), dim3((unsigned)p.n_items), dim3(kThreads), 0, stream,
                      static_cast<const T*>(z), m, p.item_offsets, p.pair_offsets,
-                     p.single_offsets, p.lengths, p.col_lengths, p.B, c_z);
+                     p.single_offsets, p.lengths, p.col_lengths, p.B, c_z, mean);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_t(const nt_partition& p, const void* z, float* m, int c_z, hipStream_t stream) {
+hipError_t launch_t(const nt_partition& p, const void* z, float* m, int c_z, bool mean,
+                    hipStream_t stream) {
   const int G = c_z / Vec16<T>::N;
   switch (G) {
-    case 1: return launch_pow2<T, 1>(p, z, m, c_z, stream);
-    case 2: return launch_pow2<T, 2>(p, z, m, c_z, stream);
-    case 4: return launch_pow2<T, 4>(p, z, m, c_z, stream);
-    case 8: return launch_pow2<T, 8>(p, z, m, c_z, stream);
-    case 16: return launch_pow2<T, 16>(p, z, m, c_z, stream);
-    case 32: return launch_pow2<T, 32>(p, z, m, c_z, stream);
-    case 64: return launch_pow2<T, 64>(p, z, m, c_z, stream);
+    case 1: return launch_pow2<T, 1>(p, z, m, c_z, mean, stream);
+    case 2: return launch_pow2<T, 2>(p, z, m, c_z, mean, stream);
+    case 4: return launch_pow2<T, 4>(p, z, m, c_z, mean, stream);
+    case 8: return launch_pow2<T, 8>(p, z, m, c_z, mean, stream);
+    case 16: return launch_pow2<T, 16>(p, z, m, c_z, mean, stream);
+    case 32: return launch_pow2<T, 32>(p, z, m, c_z, mean, stream);
+    case 64: return launch_pow2<T, 64>(p, z, m, c_z, mean, stream);
     default: break;
   }
   const int64_t total = p.T * G;
   hipLaunchKernelGGL(k_reduce_generic<T>, dim3((unsigned)((total + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, stream, static_cast<const T*>(z), m, p.row_splits,
-                     p.row_sample, p.col_lengths, p.T, c_z, G);
+                     p.row_sample, p.col_lengths, p.T, c_z, G, mean);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_reduce(const nt_partition& p, const void* z, float* m, int c_z, nt_dtype dtype,
-                         hipStream_t stream) {
+                         hipStream_t stream, bool mean) {
   if (p.T == 0) return hipSuccess;
-  if (dtype == NT_BF16) return launch_t<bf16>(p, z, m, c_z, stream);
-  return launch_t<float>(p, z, m, c_z, stream);
+  if (dtype == NT_BF16) return launch_t<bf16>(p, z, m, c_z, mean, stream);
+  return launch_t<float>(p, z, m, c_z, mean, stream);
 }
 
 }  // namespace nt

@@ -234,3 +234,68 @@ def test_square_block_rejects_rect_partition(lib):
     assert lib.nt_pair_block(P, s, s, z, ctypes.byref(w), 16, 16, 32, 1, ws, 1 << 20,
                              None) == _native.NT_ERR_INVALID
     assert "nt_pair_block_rect" in lib.nt_last_error().decode()
+
+
+def test_backward_calls_validate(lib):
+    p = fake_partition()
+    P = ctypes.byref(p)
+    E = _native
+    x, pz, loss, gx, gp, ws = (FAKE + 0x100000 * (k + 1) for k in range(6))
+    need = ctypes.c_size_t()
+    assert lib.nt_loss_workspace_bytes(P, ctypes.byref(need)) == 0
+    assert need.value >= 5 * 8
+    lw = need.value
+    assert lib.nt_pair_loss_eq5(P, x, 16, pz, 16, 0, 1, loss, gx, gp, ws, lw, None) == \
+        E.NT_ERR_INVALID                                                   # S < 1
+    assert lib.nt_pair_loss_eq5(P, x, 16, pz, 16, 1, 1, None, gx, gp, ws, lw, None) == \
+        E.NT_ERR_NULL
+    assert lib.nt_pair_loss_eq5(P, x, 16, pz, 16, 1, 1, loss, gx, gp, ws, lw - 1, None) == \
+        E.NT_ERR_WORKSPACE
+    assert lib.nt_pair_loss_eq5(P, x, 16, pz, 16, 1, 1, loss, x + 16, gp, ws, lw, None) == \
+        E.NT_ERR_INVALID                                                   # g_x overlaps x
+    assert lib.nt_pair_loss_eq5(P, x, 12, pz, 16, 1, 1, loss, gx, gp, ws, lw, None) == \
+        E.NT_ERR_INVALID
+    # mean and broadcast adjoints
+    gm, G, ga, gb = (FAKE + 0x1000000 + 0x100000 * k for k in range(4))
+    assert lib.nt_pair_reduce_backward(P, gm, None, gm + 16, 16, None) == E.NT_ERR_INVALID
+    assert lib.nt_pair_reduce_backward(P, gm, None, None, 16, None) == E.NT_ERR_NULL
+    assert lib.nt_pair_reduce_backward(P, gm, G + 16, G, 16, None) == E.NT_ERR_INVALID
+    assert lib.nt_pair_broadcast_backward(P, G, G + 64, gb, 16, None) == E.NT_ERR_INVALID
+    assert lib.nt_pair_broadcast_backward(P, G, ga, ga + 16, 16, None) == E.NT_ERR_INVALID
+    assert lib.nt_pair_broadcast_backward(P, G, ga + 4, gb, 16, None) == E.NT_ERR_ALIGN
+    # transition backward
+    z, W1, W2, gz, d1, d2 = (FAKE + 0x2000000 + 0x100000 * k for k in range(6))
+    tw = FAKE + 0x3000000
+    assert lib.nt_transition_backward_workspace_bytes(P, 16, 32, 1, ctypes.byref(need)) == 0
+    assert need.value >= 2 * 13 * 32 * 2
+    tb = lib.nt_pair_transition_backward
+    assert tb(P, z, G, W1, W2, gz, d1, d2, 16, 32, 1, tw, need.value - 1, None) == \
+        E.NT_ERR_WORKSPACE
+    assert tb(P, z, G, W1, W2, gz, None, d2, 16, 32, 1, tw, need.value, None) == E.NT_ERR_NULL
+    assert tb(P, z, G, W1, W2, W1 + 16, d1, d2, 16, 32, 1, tw, need.value, None) == \
+        E.NT_ERR_INVALID                                                   # g_z overlaps W1
+    assert tb(P, z, G, W1, W2, G + 16, d1, d2, 16, 32, 1, tw, need.value, None) == \
+        E.NT_ERR_INVALID                                                   # partial overlap
+    assert tb(P, z, G, W1, W2, gz, d1, d2, 16, 36, 1, tw, need.value, None) == E.NT_ERR_INVALID
+    assert tb(P, z, G, W1, W2, gz, d1, d2, 16, 32, 5, tw, need.value, None) == E.NT_ERR_DTYPE
+    # block backward
+    w = _native.NtBlockWeights(*(FAKE + 0x4000000 + 0x10000 * k for k in range(5)))
+    g = _native.NtBlockGrads(*(FAKE + 0x5000000 + 0x10000 * k for k in range(5)))
+    s, zo, gso, gsi = (FAKE + 0x6000000 + 0x100000 * k for k in range(4))
+    bw = FAKE + 0x7000000
+    assert lib.nt_block_backward_workspace_bytes(P, 16, 16, 32, 1, ctypes.byref(need)) == 0
+    bb = lib.nt_pair_block_backward
+    W, Gr = ctypes.byref(w), ctypes.byref(g)
+    assert bb(P, s, zo, W, gso, None, gsi, Gr, 16, 16, 32, 1, bw, need.value - 1, None) == \
+        E.NT_ERR_WORKSPACE
+    assert bb(P, s, zo, W, gso, None, gsi, None, 16, 16, 32, 1, bw, need.value, None) == \
+        E.NT_ERR_NULL
+    assert bb(P, s, zo, W, gso, None, s, Gr, 16, 16, 32, 1, bw, need.value, None) == \
+        E.NT_ERR_INVALID                                                   # g_s_in overlaps s_in
+    rect = fake_partition()
+    rect.col_offsets = FAKE + 0x9000
+    assert bb(ctypes.byref(rect), s, zo, W, gso, None, gsi, Gr, 16, 16, 32, 1, bw, need.value,
+              None) == E.NT_ERR_INVALID
+    g.W1 = None
+    assert bb(P, s, zo, W, gso, None, gsi, Gr, 16, 16, 32, 1, bw, need.value, None) == \
+        E.NT_ERR_NULL
