@@ -317,6 +317,7 @@ nt_status check_workspace(const void* ws, size_t have, uint64_t need) {
 struct TransBwdWs {
   uint64_t H, GH, Gb, W1T, W2T, part, total;
   int splits;
+  bool mfma;  // the weight gradients run on the matrix cores
 };
 
 TransBwdWs transition_backward_ws(int64_t cells, int c_z, int hidden, nt_dtype dtype) {
@@ -329,7 +330,8 @@ TransBwdWs transition_backward_ws(int64_t cells, int c_z, int hidden, nt_dtype d
   w.Gb = off;   off += nt::align256((size_t)cells * c_z * es);
   w.W1T = off;  off += nt::align256((size_t)hidden * c_z * es);
   w.W2T = off;  off += nt::align256((size_t)hidden * c_z * es);
-  w.splits = nt::gemm_tn_splits(cells, hidden, c_z);
+  w.mfma = dtype == NT_BF16 && nt::wgrad_supported(hidden, c_z);
+  w.splits = w.mfma ? nt::wgrad_splits(cells, hidden, c_z) : nt::gemm_tn_splits(cells, hidden, c_z);
   w.part = off; off += nt::align256((size_t)w.splits * hidden * c_z * sizeof(float));
   w.total = off;
   return w;
@@ -343,10 +345,26 @@ nt_status transition_backward(const nt_partition* p, const void* z, const float*
   void* GH = ws + w.GH;
   void* Gb = ws + w.Gb;
   float* part = reinterpret_cast<float*>(ws + w.part);
-  NT_TRY(hip_status(nt::launch_transition_backward_generic(*p, z, G, W1, W2, g_z, H, GH, Gb, c_z,
-                                                           hidden, dtype, s),
-                    "transition backward"));
+  if (nt::transition_backward_has_mfma(c_z, hidden, dtype)) {
+    void* W1T = ws + w.W1T;
+    void* W2T = ws + w.W2T;
+    NT_TRY(hip_status(nt::launch_transpose(W2, W2T, c_z, hidden, dtype, s), "transpose W2"));
+    NT_TRY(hip_status(nt::launch_transpose(W1, W1T, hidden, c_z, dtype, s), "transpose W1"));
+    NT_TRY(hip_status(nt::launch_transition_backward_mfma(*p, z, G, W1, W2T, W1T, g_z, H, GH, Gb,
+                                                          nt::device_cu_count(), s),
+                      "transition backward"));
+  } else {
+    NT_TRY(hip_status(nt::launch_transition_backward_generic(*p, z, G, W1, W2, g_z, H, GH, Gb,
+                                                             c_z, hidden, dtype, s),
+                      "transition backward"));
+  }
   // dW1 = g_H^T z ; dW2 = G^T H with G as stored in Gb
+  if (w.mfma) {
+    NT_TRY(hip_status(nt::launch_wgrad(GH, z, dW1, part, p->cells, hidden, c_z, w.splits, s),
+                      "dW1 contraction"));
+    return hip_status(nt::launch_wgrad(Gb, H, dW2, part, p->cells, c_z, hidden, w.splits, s),
+                      "dW2 contraction");
+  }
   NT_TRY(hip_status(nt::launch_gemm_tn(GH, dtype, z, dtype, dW1, part, p->cells, hidden, c_z,
                                        w.splits, s),
                     "dW1 contraction"));

@@ -350,6 +350,13 @@ hipError_t launch_transpose(const void* src, void* dst, int R, int C, nt_dtype d
   return hipGetLastError();
 }
 
+hipError_t launch_sum_splits(const float* part, float* C, int S, int64_t MN, hipStream_t s) {
+  int64_t g = (MN + kThreads - 1) / kThreads;
+  g = g > 4096 ? 4096 : (g < 1 ? 1 : g);
+  hipLaunchKernelGGL(k_sum_splits, dim3((unsigned)g), dim3(kThreads), 0, s, part, C, S, MN);
+  return hipGetLastError();
+}
+
 int gemm_tn_splits(int64_t K, int M, int N) {
   const int64_t tiles = (int64_t)((M + 31) / 32) * ((N + 31) / 32);
   int64_t S = (1024 + tiles - 1) / tiles;         // about 1024 workgroups

@@ -149,6 +149,23 @@ int gemm_tn_splits(int64_t K, int M, int N);
 hipError_t launch_gemm_tn(const void* A, nt_dtype a_dtype, const void* B, nt_dtype b_dtype,
                           float* C, float* partial, int64_t K, int M, int N, int splits,
                           hipStream_t stream);
+// C = sum of S partials [S][MN] in slice order (S = 0: C = 0).
+hipError_t launch_sum_splits(const float* part, float* C, int S, int64_t MN, hipStream_t stream);
+// Matrix-core form of launch_gemm_tn for bf16 A, B with M, N multiples of
+// 128; part holds wgrad_splits(K, M, N) * M * N floats.
+bool wgrad_supported(int M, int N);
+int wgrad_splits(int64_t K, int M, int N);
+hipError_t launch_wgrad(const void* A, const void* B, float* C, float* part, int64_t K, int M,
+                        int N, int splits, hipStream_t stream);
+// Compute units of the current device (cached per device).
+int device_cu_count();
+// Matrix-core transition gradient (bf16, c_z = 128, hidden = 512): W2T =
+// W2^T [hidden, c_z] and W1T = W1^T [c_z, hidden] are prepared by the caller.
+bool transition_backward_has_mfma(int c_z, int hidden, nt_dtype dtype);
+hipError_t launch_transition_backward_mfma(const nt_partition& p, const void* z, const float* G,
+                                           const void* W1, const void* W2T, const void* W1T,
+                                           float* g_z, void* H, void* GH, void* Gb, int cus,
+                                           hipStream_t stream);
 // Transition gradient without weight gradients: g_z, and H, GH and Gb (G in
 // the storage type) for them. g_z may equal G.
 hipError_t launch_transition_backward_generic(const nt_partition& p, const void* z,

@@ -833,6 +833,8 @@ hipError_t launch_generic(const nt_partition& p, const void* z_in, const void* a
 
 }  // namespace
 
+int device_cu_count() { return device_cus(); }
+
 bool transition_has_mfma(int c_z, int hidden, nt_dtype dtype) {
   return dtype == NT_BF16 && (c_z == 64 || c_z == 128) && hidden % kChunk == 0;
 }

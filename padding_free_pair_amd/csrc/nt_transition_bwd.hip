@@ -1,0 +1,232 @@
+// Gradient of the residual pair transition on the matrix cores (DanLing
+// NestedTensor, Equation 1's second line differentiated; Section 4 measures
+// forward, loss and backward). For an incoming G = dL/dz' per cell:
+//   pre = z W1^T,  H = relu(pre),  g_H = (G W2) * [pre > 0],
+//   g_z = G + g_H W1,
+// and H, g_H and bf16(G) are written for the weight gradients
+// dW1 = g_H^T z and dW2 = G^T H, contractions over all cells done by
+// k_wgrad in nt_wgrad.hip.
+//
+// Persistent kernel, bf16, c_z = 128, hidden a multiple of 32. A workgroup
+// of four waves takes 256 cells at a time (64 per wave, two 32-cell blocks).
+// Per 32-unit hidden chunk j, three products run on v_mfma_f32_32x32x16_bf16
+// with the cells as the N dimension:
+//   pre^T (32 x cells) = W1[j]   . z^T        (k = features)
+//   gh^T  (32 x cells) = W2T[j]  . bf16(G)^T  (k = features)
+//   g_z^T (c_z x cells) += W1T[:, j] . g_H^T  (k = the chunk's units)
+// The chunk's 24 KiB of weight fragments are double-buffered through LDS:
+// the loads of chunk j + 1 are issued at the start of chunk j and written
+// after its products. Result rows of the first two products are permuted
+// (bits 2 and 3 of the row swapped) so that lane group h holds units
+// 16 s + 8 h + 0..7 in elements 8 s .. 8 s + 7: the mask, the bf16 pack of
+// g_H and the third product's operand are lane-local, and the third
+// product's rows (features) use the same permutation, so its accumulator
+// matches the lane's slice of G and g_z (features 16 t + 8 h + 0..7).
+#include "nt_device.hpp"
+#include "nt_internal.hpp"
+
+namespace nt {
+namespace {
+
+constexpr int kBwWaves = 4;
+constexpr int kBwThreads = kBwWaves * 64;
+constexpr int kBwTileCells = kBwWaves * 64;
+
+__device__ __forceinline__ f32x16 bw_mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Result row rho of a 32x32 product <-> unit (or feature) within its block of
+// 32: bits 2 and 3 swapped (an involution).
+__device__ __forceinline__ int bw_p32(int rho) {
+  return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
+}
+
+template <int CZ, int HID>
+__global__ __launch_bounds__(kBwThreads, 1) void k_transition_bwd(
+    const bf16* __restrict__ z, const float* G, const bf16* __restrict__ W1,
+    const bf16* __restrict__ W2T, const bf16* __restrict__ W1T, float* g_z,
+    bf16* __restrict__ H, bf16* __restrict__ GH, bf16* __restrict__ Gb, int64_t cells,
+    int64_t ntiles) {
+  constexpr int KT = CZ / 16;    // k-steps of the first two products
+  constexpr int FB = CZ / 32;    // feature blocks of the third
+  constexpr int NCH = HID / 32;  // hidden chunks
+  constexpr int CB = 2;          // 32-cell blocks per wave
+  // one chunk's fragments: W1 (KT x 64 lanes), W2T (KT x 64), W1T (FB x 2 x 64)
+  constexpr int F1 = KT * 64, F2 = KT * 64, F3 = FB * 2 * 64;
+  constexpr int FRAGS = F1 + F2 + F3;                 // 16-byte pieces
+  constexpr int PER = FRAGS / kBwThreads;             // pieces per thread
+  static_assert(FRAGS % kBwThreads == 0, "chunk staging splits evenly");
+  static_assert(FB * 2 == KT, "shape");
+
+  __shared__ bf16x8 wbuf[2][FRAGS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+
+  // Piece p of a chunk (natural, coalesced global order) and its fragment
+  // slot. W1 / W2T chunk: 32 rows x CZ features, 16-byte piece q of row r
+  // goes to fragment t = q / 2, lane 32 (q % 2) + p32(r). W1T chunk: CZ rows
+  // x 32 units, piece q (0..3) of row f to fragment (2 (f / 32) + q / 2),
+  // lane 32 (q % 2) + p32(f % 32).
+  auto piece_src = [&](int j, int p) -> const bf16* {
+    if (p < F1 + F2) {
+      const int pp = p < F1 ? p : p - F1;
+      const int r = pp / (CZ / 8), q = pp % (CZ / 8);
+      const bf16* M = p < F1 ? W1 : W2T;
+      return M + (int64_t)(32 * j + r) * CZ + 8 * q;
+    }
+    const int pp = p - F1 - F2;
+    const int f = pp / 4, q = pp % 4;
+    return W1T + (int64_t)f * HID + 32 * j + 8 * q;
+  };
+  auto piece_slot = [&](int p) -> int {
+    if (p < F1 + F2) {
+      const int base = p < F1 ? 0 : F1;
+      const int pp = p - base;
+      const int r = pp / (CZ / 8), q = pp % (CZ / 8);
+      return base + 64 * (q / 2) + 32 * (q % 2) + bw_p32(r);
+    }
+    const int pp = p - F1 - F2;
+    const int f = pp / 4, q = pp % 4;
+    return F1 + F2 + 64 * (2 * (f / 32) + q / 2) + 32 * (q % 2) + bw_p32(f % 32);
+  };
+
+  bf16x8 stage[PER];
+  auto load_chunk = [&](int j) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+      stage[k] = *reinterpret_cast<const bf16x8*>(piece_src(j, tid + k * kBwThreads));
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) wbuf[buf][piece_slot(tid + k * kBwThreads)] = stage[k];
+  };
+
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t cell0 = tile * kBwTileCells + wave * 64;
+    // z and G of this wave's cells: lane (l32, h) of block cb holds features
+    // 16 t + 8 h + 0..7 of cell cell0 + 32 cb + l32
+    bf16x8 zb[CB][KT], gb[CB][KT];
+    f32x16 y[CB][FB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      int64_t c = cell0 + 32 * cb + l32;
+      c = c < cells ? c : cells - 1;
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        zb[cb][t] = *reinterpret_cast<const bf16x8*>(z + c * CZ + 16 * t + 8 * h);
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(G + c * CZ + 16 * t + 8 * h);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(G + c * CZ + 16 * t + 8 * h + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y[cb][t >> 1][8 * (t & 1) + e] = g0[e];
+          y[cb][t >> 1][8 * (t & 1) + 4 + e] = g1[e];
+          gb[cb][t][e] = (bf16)g0[e];
+          gb[cb][t][4 + e] = (bf16)g1[e];
+        }
+      }
+    }
+
+    for (int j = 0; j < NCH; ++j) {
+      const int buf = j & 1;
+      load_chunk(j + 1 < NCH ? j + 1 : 0);  // the next chunk (or the next tile's first)
+      const bf16x8* wb = wbuf[buf];
+      f32x16 pre[CB], gh[CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        pre[cb] = f32x16{};
+        gh[cb] = f32x16{};
+      }
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        const bf16x8 a1 = wb[64 * t + lane];
+        const bf16x8 a2 = wb[F1 + 64 * t + lane];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          pre[cb] = bw_mfma(a1, zb[cb][t], pre[cb]);
+          gh[cb] = bw_mfma(a2, gb[cb][t], gh[cb]);
+        }
+      }
+      // mask, pack, and the per-cell rows of H and g_H for the weight gradients
+      bf16x8 hf[CB][2];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int64_t c = cell0 + 32 * cb + l32;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          bf16x8 hv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pv = pre[cb][8 * s + e];
+            hv[e] = (bf16)(pv > 0.f ? pv : 0.f);
+            hf[cb][s][e] = (bf16)(pv > 0.f ? gh[cb][8 * s + e] : 0.f);
+          }
+          if (c < cells) {
+            const int64_t o = c * HID + 32 * j + 16 * s + 8 * h;
+            *reinterpret_cast<bf16x8*>(H + o) = hv;
+            *reinterpret_cast<bf16x8*>(GH + o) = hf[cb][s];
+          }
+        }
+      }
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8 a3 = wb[F1 + F2 + 64 * (2 * fb + s) + lane];
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) y[cb][fb] = bw_mfma(a3, hf[cb][s], y[cb][fb]);
+        }
+      // the other buffer was last read in chunk j - 1, before the previous barrier
+      store_chunk(buf ^ 1);
+      __syncthreads();
+    }
+
+    // g_z (fp32) and bf16(G) of this wave's cells
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int64_t c = cell0 + 32 * cb + l32;
+      if (c >= cells) continue;
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        f32x4 o0, o1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o0[e] = y[cb][t >> 1][8 * (t & 1) + e];
+          o1[e] = y[cb][t >> 1][8 * (t & 1) + 4 + e];
+        }
+        *reinterpret_cast<f32x4*>(g_z + c * CZ + 16 * t + 8 * h) = o0;
+        *reinterpret_cast<f32x4*>(g_z + c * CZ + 16 * t + 8 * h + 4) = o1;
+        *reinterpret_cast<bf16x8*>(Gb + c * CZ + 16 * t + 8 * h) = gb[cb][t];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool transition_backward_has_mfma(int c_z, int hidden, nt_dtype dtype) {
+  return dtype == NT_BF16 && c_z == 128 && hidden == 512;
+}
+
+hipError_t launch_transition_backward_mfma(const nt_partition& p, const void* z, const float* G,
+                                           const void* W1, const void* W2T, const void* W1T,
+                                           float* g_z, void* H, void* GH, void* Gb, int cus,
+                                           hipStream_t stream) {
+  if (p.cells == 0) return hipSuccess;
+  const int64_t ntiles = (p.cells + kBwTileCells - 1) / kBwTileCells;
+  const int64_t grid = ntiles < cus ? ntiles : cus;
+  hipLaunchKernelGGL((k_transition_bwd<128, 512>), dim3((unsigned)grid), dim3(kBwThreads), 0,
+                     stream, static_cast<const bf16*>(z), G, static_cast<const bf16*>(W1),
+                     static_cast<const bf16*>(W2T), static_cast<const bf16*>(W1T), g_z,
+                     static_cast<bf16*>(H), static_cast<bf16*>(GH), static_cast<bf16*>(Gb),
+                     p.cells, ntiles);
+  return hipGetLastError();
+}
+
+}  // namespace nt
