@@ -4,8 +4,9 @@
 One step = the whole hot path on one batch: build the partition from host
 lengths (offset scan, row splits), then every block of the workload
 (projections, broadcast fused into the transition, column mean, output
-projection). Inputs are resident in HBM before timing starts. Prints one
-JSON line; progress goes to stderr.
+projection). Inputs are resident in HBM before timing starts. The line also
+carries the training step (forward, Equation 5 loss, backward) as "train".
+Prints one JSON line; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -110,6 +111,72 @@ class PerSampleRunner:
                                  workspace=self.ws)
             s_in = s_out
         return s_in, r.z
+
+
+class TrainRunner:
+    """Forward, Equation 5 loss and backward of the workload's blocks (the
+    step the pages time: DanLing NestedTensor, Section 4 and Appendix A.1):
+    every block keeps its input singles and returned pair state, the loss
+    reads the last block's outputs, and the blocks' gradients run in reverse
+    order. Buffers are preallocated; the partition is rebuilt each step."""
+
+    def __init__(self, x: pin.Inputs, torch, nt, packed: PackedRunner):
+        self.torch, self.nt, self.x, self.r = torch, nt, x, packed
+        tdt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+        nb = len(x.weights)
+        self.s = [packed.s0] + [torch.empty_like(packed.s0) for _ in range(nb)]
+        self.z = [torch.empty((packed.cells, x.c_z), dtype=tdt, device="cuda")
+                  for _ in range(nb)]
+        self.g = [torch.empty((packed.T, x.c_s), dtype=torch.float32, device="cuda")
+                  for _ in range(2)]
+        self.grads = [{k: torch.empty(v.shape, dtype=torch.float32, device="cuda")
+                       for k, v in w.items()} for w in packed.w]
+        self.bws = torch.empty(max(nt.nt_block_backward_workspace_bytes(
+            packed.p, x.c_s, x.c_z, x.hidden, tdt), 1), dtype=torch.uint8, device="cuda")
+        self.lws = torch.empty(nt.nt_loss_workspace_bytes(packed.p), dtype=torch.uint8,
+                               device="cuda")
+
+    def step(self):
+        nt, r = self.nt, self.r
+        p = nt.nt_make_partition(r.lengths, buffer=r.part_buf)
+        for k, w in enumerate(r.w):
+            nt.nt_pair_block(p, self.s[k], w, s_out=self.s[k + 1], z_out=self.z[k],
+                             workspace=r.ws)
+        loss, g, g_pz = nt.nt_pair_loss_eq5(p, self.s[-1], self.z[-1], workspace=self.lws)
+        for k in range(len(r.w) - 1, -1, -1):
+            out = self.g[k % 2]
+            nt.nt_pair_block_backward(p, self.s[k], self.z[k], r.w[k], g,
+                                      g_pz if k == len(r.w) - 1 else None, g_s_in=out,
+                                      grads=self.grads[k], workspace=self.bws)
+            g = out
+        return loss, g
+
+
+def backward_rooflines(r: PackedRunner, reps: int) -> dict:
+    """The transition's gradient on block 0's pair state (matrix-core act
+    kernel plus the two weight-gradient contractions, one call), against
+    the bf16 MFMA peak: five products of 2 c_z h flop per cell."""
+    torch, nt, x = r.torch, r.nt, r.x
+    if x.dtype != "bf16":
+        return {}
+    w = r.w[0]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    G = torch.randn((r.cells, x.c_z), device="cuda", generator=g) / 64
+    g_z = torch.empty_like(G)
+    dW1 = torch.empty((x.hidden, x.c_z), device="cuda")
+    dW2 = torch.empty((x.c_z, x.hidden), device="cuda")
+    ws = torch.empty(nt.nt_transition_backward_workspace_bytes(r.p, x.c_z, x.hidden,
+                                                               torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    t = time_kernel(lambda: nt.nt_pair_transition_backward(r.p, r.z, G, w["W1"], w["W2"],
+                                                           g_z=g_z, dW1=dW1, dW2=dW2,
+                                                           workspace=ws), reps, torch)
+    flops = 10.0 * x.c_z * x.hidden * r.cells
+    return {"kernel": "k_transition_bwd + k_wgrad x2 (transition gradient, one call)",
+            "bound": "mfma", "ms": t * 1e3, "achieved": flops / t / 1e12,
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "flop_per_launch": flops,
+            "frac": flops / t / 1e12 / PEAK_BF16_TFLOPS}
 
 
 def rectangular(x: pin.Inputs, args, torch, nt) -> dict:
@@ -425,6 +492,19 @@ def main():
         v = kern["swiglu_transition"]
         log(f"kernel swiglu_transition: {v['ms'] * 1e3:.1f} us, {v['achieved']:.1f} TFLOP/s "
             f"({100 * v['frac']:.1f}% of peak)")
+    if x.dtype == "bf16":
+        kern["transition_backward"] = backward_rooflines(r, max(10, args.kernel_reps // 5))
+        v = kern["transition_backward"]
+        log(f"kernel transition_backward: {v['ms'] * 1e3:.1f} us, {v['achieved']:.1f} TFLOP/s "
+            f"({100 * v['frac']:.1f}% of peak)")
+    tr = TrainRunner(x, torch, nt, r)
+    t_train = time_steps(tr.step, args.steps, args.warmup, torch)
+    train = {"value": r.cells * w.blocks / t_train, "unit": "pair cells/s per block",
+             "ms_per_step": t_train * 1e3, "forward_ms": t_step * 1e3,
+             "step": "forward of every block, Equation 5 loss, backward of every block"}
+    log(f"train step {t_train * 1e3:.3f} ms -> {train['value']:.4g} cells/s per block")
+    del tr
+    torch.cuda.empty_cache()
     dom = kern["transition"]
     roofline = {"bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
                 "unit": dom["unit"], "frac": dom["frac"],
@@ -442,6 +522,7 @@ def main():
                    "T": r.T, "parallelism": "single GPU"},
         "roofline": roofline,
         "kernels": kern,
+        "train": train,
     }
 
     if not args.quick:
