@@ -318,12 +318,14 @@ struct TransBwdWs {
   uint64_t H, GH, Gb, W1T, W2T, part, total;
   int splits;
   bool mfma;  // the weight gradients run on the matrix cores
+  bool rc;    // ... recomputing H and g_H from z and bf16(G) (no H, GH buffers)
 };
 
 TransBwdWs transition_backward_ws(int64_t cells, int c_z, int hidden, nt_dtype dtype) {
   TransBwdWs w;
   const uint64_t es = esize(dtype);
-  const uint64_t hb = nt::align256((size_t)cells * hidden * es);
+  w.rc = nt::wgrad_rc_supported(c_z, hidden, dtype);
+  const uint64_t hb = w.rc ? 0 : nt::align256((size_t)cells * hidden * es);
   uint64_t off = 0;
   w.H = off;    off += hb;
   w.GH = off;   off += hb;
@@ -331,18 +333,27 @@ TransBwdWs transition_backward_ws(int64_t cells, int c_z, int hidden, nt_dtype d
   w.W1T = off;  off += nt::align256((size_t)hidden * c_z * es);
   w.W2T = off;  off += nt::align256((size_t)hidden * c_z * es);
   w.mfma = dtype == NT_BF16 && nt::wgrad_supported(hidden, c_z);
-  w.splits = w.mfma ? nt::wgrad_splits(cells, hidden, c_z) : nt::gemm_tn_splits(cells, hidden, c_z);
-  w.part = off; off += nt::align256((size_t)w.splits * hidden * c_z * sizeof(float));
+  if (w.rc) {
+    w.splits = nt::wgrad_rc_slices(cells);
+    w.part = off; off += nt::align256((size_t)2 * w.splits * hidden * c_z * sizeof(float));
+  } else {
+    w.splits = w.mfma ? nt::wgrad_splits(cells, hidden, c_z)
+                      : nt::gemm_tn_splits(cells, hidden, c_z);
+    w.part = off; off += nt::align256((size_t)w.splits * hidden * c_z * sizeof(float));
+  }
   w.total = off;
   return w;
 }
 
+// G given, or (g_m non-null) formed from the mean's adjoint g_m / M_i (+ g_in)
+// by the matrix-core kernel; the generic path forms it first, into g_z.
 nt_status transition_backward(const nt_partition* p, const void* z, const float* G,
                               const void* W1, const void* W2, float* g_z, float* dW1, float* dW2,
-                              int c_z, int hidden, nt_dtype dtype, char* ws, hipStream_t s) {
+                              int c_z, int hidden, nt_dtype dtype, char* ws, hipStream_t s,
+                              const float* g_m = nullptr, const float* g_in = nullptr) {
   const TransBwdWs w = transition_backward_ws(p->cells, c_z, hidden, dtype);
-  void* H = ws + w.H;
-  void* GH = ws + w.GH;
+  void* H = w.rc ? nullptr : ws + w.H;
+  void* GH = w.rc ? nullptr : ws + w.GH;
   void* Gb = ws + w.Gb;
   float* part = reinterpret_cast<float*>(ws + w.part);
   if (nt::transition_backward_has_mfma(c_z, hidden, dtype)) {
@@ -350,10 +361,18 @@ nt_status transition_backward(const nt_partition* p, const void* z, const float*
     void* W2T = ws + w.W2T;
     NT_TRY(hip_status(nt::launch_transpose(W2, W2T, c_z, hidden, dtype, s), "transpose W2"));
     NT_TRY(hip_status(nt::launch_transpose(W1, W1T, hidden, c_z, dtype, s), "transpose W1"));
-    NT_TRY(hip_status(nt::launch_transition_backward_mfma(*p, z, G, W1, W2T, W1T, g_z, H, GH, Gb,
-                                                          nt::device_cu_count(), s),
+    NT_TRY(hip_status(nt::launch_transition_backward_mfma(*p, z, G, g_m, g_in, W1, W2T, W1T, g_z,
+                                                          H, GH, Gb, nt::device_cu_count(), s),
                       "transition backward"));
+    if (w.rc)
+      return hip_status(nt::launch_wgrad_rc(z, Gb, W1, W2T, dW1, dW2, part, p->cells, w.splits,
+                                            s),
+                        "weight gradients");
   } else {
+    if (g_m) {
+      NT_TRY(hip_status(nt::launch_mean_backward(*p, g_m, g_in, g_z, c_z, s), "mean backward"));
+      G = g_z;
+    }
     NT_TRY(hip_status(nt::launch_transition_backward_generic(*p, z, G, W1, W2, g_z, H, GH, Gb,
                                                              c_z, hidden, dtype, s),
                       "transition backward"));
@@ -813,10 +832,9 @@ nt_status nt_pair_block_backward(const nt_partition* p, const void* s_in, const 
   NT_TRY(hip_status(nt::launch_gemm_tn(g_s_out, NT_F32, m, NT_F32, grads->Wo, ppart, T, c_s, c_z,
                                        L.psplits, s),
                     "dWo"));
-  // mean, transition, broadcast
-  NT_TRY(hip_status(nt::launch_mean_backward(*p, g_m, g_z_out, G, c_z, s), "mean backward"));
-  NT_TRY(transition_backward(p, z, G, w->W1, w->W2, G, grads->W1, grads->W2, c_z, hidden, dtype,
-                             base + L.trans, s));
+  // mean (formed inside the transition's gradient), transition, broadcast
+  NT_TRY(transition_backward(p, z, nullptr, w->W1, w->W2, G, grads->W1, grads->W2, c_z, hidden,
+                             dtype, base + L.trans, s, g_m, g_z_out));
   NT_TRY(hip_status(nt::launch_reduce(*p, G, g_a, c_z, NT_F32, s, false), "row sums"));
   NT_TRY(hip_status(nt::launch_col_sums(*p, G, g_b, c_z, s), "column sums"));
   // a = s Wa^T, b = s Wb^T

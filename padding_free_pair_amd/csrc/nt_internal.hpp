@@ -157,14 +157,25 @@ bool wgrad_supported(int M, int N);
 int wgrad_splits(int64_t K, int M, int N);
 hipError_t launch_wgrad(const void* A, const void* B, float* C, float* part, int64_t K, int M,
                         int N, int splits, hipStream_t stream);
+// Weight gradients recomputed from z and bf16(G) (bf16, c_z 128, hidden 512):
+// part holds 2 * wgrad_rc_slices(cells) * c_z * hidden floats.
+bool wgrad_rc_supported(int c_z, int hidden, nt_dtype dtype);
+int wgrad_rc_slices(int64_t cells);
+hipError_t launch_wgrad_rc(const void* z, const void* Gb, const void* W1, const void* W2T,
+                           float* dW1, float* dW2, float* part, int64_t cells, int slices,
+                           hipStream_t stream);
 // Compute units of the current device (cached per device).
 int device_cu_count();
 // Matrix-core transition gradient (bf16, c_z = 128, hidden = 512): W2T =
 // W2^T [hidden, c_z] and W1T = W1^T [c_z, hidden] are prepared by the caller.
+// H and GH may be null (then they are not written). With g_m non-null, G is
+// not read: it is formed per cell as g_m[row] / M_i (+ g_in[cell] when
+// g_in is non-null), exactly as launch_mean_backward forms it.
 bool transition_backward_has_mfma(int c_z, int hidden, nt_dtype dtype);
 hipError_t launch_transition_backward_mfma(const nt_partition& p, const void* z, const float* G,
-                                           const void* W1, const void* W2T, const void* W1T,
-                                           float* g_z, void* H, void* GH, void* Gb, int cus,
+                                           const float* g_m, const float* g_in, const void* W1,
+                                           const void* W2T, const void* W1T, float* g_z,
+                                           void* H, void* GH, void* Gb, int cus,
                                            hipStream_t stream);
 // Transition gradient without weight gradients: g_z, and H, GH and Gb (G in
 // the storage type) for them. g_z may equal G.

@@ -3,9 +3,9 @@
 // forward, loss and backward). For an incoming G = dL/dz' per cell:
 //   pre = z W1^T,  H = relu(pre),  g_H = (G W2) * [pre > 0],
 //   g_z = G + g_H W1,
-// and H, g_H and bf16(G) are written for the weight gradients
-// dW1 = g_H^T z and dW2 = G^T H, contractions over all cells done by
-// k_wgrad in nt_wgrad.hip.
+// and bf16(G) (plus, on request, H and g_H) is written for the weight
+// gradients dW1 = g_H^T z and dW2 = G^T H, contractions over all cells in
+// nt_wgrad.hip (k_wgrad_rc recomputes H and g_H from z and bf16(G)).
 //
 // Persistent kernel, bf16, c_z = 128, hidden a multiple of 32. A workgroup
 // of four waves takes 256 cells at a time (64 per wave, two 32-cell blocks).
@@ -42,9 +42,24 @@ __device__ __forceinline__ int bw_p32(int rho) {
   return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
 }
 
-template <int CZ, int HID>
+// Where G comes from: read from memory, or formed from the column mean's
+// adjoint, G[cell] = g_m[row] / M_i (+ g_in[cell]), with the cell decoded on
+// the fly (Eq. 3 inverted from the tile's first sample).
+struct MeanAdjoint {
+  const float* g_m;             // [T, c_z]
+  const float* g_in;            // [cells, c_z] or null
+  const int64_t* pair_offsets;
+  const int64_t* single_offsets;
+  const int32_t* col_lengths;   // M_i, the divisor
+  const int32_t* tile_sample;   // sample of cell 256 k
+};
+
+// WRITE_H: also store H and g_H per cell (for contractions that read them);
+// without it the weight gradients are recomputed from z and bf16(G).
+// FROM_MEAN: G is formed from `ma` instead of read.
+template <int CZ, int HID, bool WRITE_H, bool FROM_MEAN>
 __global__ __launch_bounds__(kBwThreads, 1) void k_transition_bwd(
-    const bf16* __restrict__ z, const float* G, const bf16* __restrict__ W1,
+    const bf16* __restrict__ z, const float* G, MeanAdjoint ma, const bf16* __restrict__ W1,
     const bf16* __restrict__ W2T, const bf16* __restrict__ W1T, float* g_z,
     bf16* __restrict__ H, bf16* __restrict__ GH, bf16* __restrict__ Gb, int64_t cells,
     int64_t ntiles) {
@@ -118,11 +133,42 @@ __global__ __launch_bounds__(kBwThreads, 1) void k_transition_bwd(
     for (int cb = 0; cb < CB; ++cb) {
       int64_t c = cell0 + 32 * cb + l32;
       c = c < cells ? c : cells - 1;
+      const float* grow = nullptr;  // g_m row of the cell (FROM_MEAN)
+      float mf = 0.f;  // M_i as a float (the divisor)
+      if constexpr (FROM_MEAN) {
+        int i = ma.tile_sample[tile];  // tiles are 256 cells, the index's span
+        while (ma.pair_offsets[i + 1] <= c) ++i;
+        const int64_t m = ma.col_lengths[i];
+        grow = ma.g_m + (ma.single_offsets[i] + (c - ma.pair_offsets[i]) / m) * CZ;
+        mf = (float)m;
+      }
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
         zb[cb][t] = *reinterpret_cast<const bf16x8*>(z + c * CZ + 16 * t + 8 * h);
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(G + c * CZ + 16 * t + 8 * h);
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(G + c * CZ + 16 * t + 8 * h + 4);
+        f32x4 g0, g1;
+        if constexpr (FROM_MEAN) {
+          // as the mean's adjoint kernel: g_m / M_i, then + g_in
+          const f32x4 m0 = *reinterpret_cast<const f32x4*>(grow + 16 * t + 8 * h);
+          const f32x4 m1 = *reinterpret_cast<const f32x4*>(grow + 16 * t + 8 * h + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            g0[e] = m0[e] / mf;
+            g1[e] = m1[e] / mf;
+          }
+          if (ma.g_in) {
+            const f32x4 i0 = *reinterpret_cast<const f32x4*>(ma.g_in + c * CZ + 16 * t + 8 * h);
+            const f32x4 i1 =
+                *reinterpret_cast<const f32x4*>(ma.g_in + c * CZ + 16 * t + 8 * h + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              g0[e] = g0[e] + i0[e];
+              g1[e] = g1[e] + i1[e];
+            }
+          }
+        } else {
+          g0 = *reinterpret_cast<const f32x4*>(G + c * CZ + 16 * t + 8 * h);
+          g1 = *reinterpret_cast<const f32x4*>(G + c * CZ + 16 * t + 8 * h + 4);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           y[cb][t >> 1][8 * (t & 1) + e] = g0[e];
@@ -167,7 +213,7 @@ __global__ __launch_bounds__(kBwThreads, 1) void k_transition_bwd(
             hv[e] = (bf16)(pv > 0.f ? pv : 0.f);
             hf[cb][s][e] = (bf16)(pv > 0.f ? gh[cb][8 * s + e] : 0.f);
           }
-          if (c < cells) {
+          if (WRITE_H && c < cells) {
             const int64_t o = c * HID + 32 * j + 16 * s + 8 * h;
             *reinterpret_cast<bf16x8*>(H + o) = hv;
             *reinterpret_cast<bf16x8*>(GH + o) = hf[cb][s];
@@ -215,17 +261,36 @@ bool transition_backward_has_mfma(int c_z, int hidden, nt_dtype dtype) {
 }
 
 hipError_t launch_transition_backward_mfma(const nt_partition& p, const void* z, const float* G,
-                                           const void* W1, const void* W2T, const void* W1T,
-                                           float* g_z, void* H, void* GH, void* Gb, int cus,
+                                           const float* g_m, const float* g_in, const void* W1,
+                                           const void* W2T, const void* W1T, float* g_z,
+                                           void* H, void* GH, void* Gb, int cus,
                                            hipStream_t stream) {
   if (p.cells == 0) return hipSuccess;
+  static_assert(kBwTileCells == kSampleIndexSpan, "tiles use the partition's sample index");
   const int64_t ntiles = (p.cells + kBwTileCells - 1) / kBwTileCells;
   const int64_t grid = ntiles < cus ? ntiles : cus;
-  hipLaunchKernelGGL((k_transition_bwd<128, 512>), dim3((unsigned)grid), dim3(kBwThreads), 0,
-                     stream, static_cast<const bf16*>(z), G, static_cast<const bf16*>(W1),
-                     static_cast<const bf16*>(W2T), static_cast<const bf16*>(W1T), g_z,
-                     static_cast<bf16*>(H), static_cast<bf16*>(GH), static_cast<bf16*>(Gb),
-                     p.cells, ntiles);
+  const MeanAdjoint ma{g_m, g_in, p.pair_offsets, p.single_offsets, p.col_lengths,
+                       p.tile_sample};
+  const bf16* zz = static_cast<const bf16*>(z);
+  const bf16* w1 = static_cast<const bf16*>(W1);
+  const bf16* w2t = static_cast<const bf16*>(W2T);
+  const bf16* w1t = static_cast<const bf16*>(W1T);
+  bf16* hh = static_cast<bf16*>(H);
+  bf16* gh = static_cast<bf16*>(GH);
+  bf16* gb = static_cast<bf16*>(Gb);
+  const dim3 gd((unsigned)grid), bd(kBwThreads);
+  if (H && g_m)
+    hipLaunchKernelGGL((k_transition_bwd<128, 512, true, true>), gd, bd, 0, stream, zz, G, ma,
+                       w1, w2t, w1t, g_z, hh, gh, gb, p.cells, ntiles);
+  else if (H)
+    hipLaunchKernelGGL((k_transition_bwd<128, 512, true, false>), gd, bd, 0, stream, zz, G, ma,
+                       w1, w2t, w1t, g_z, hh, gh, gb, p.cells, ntiles);
+  else if (g_m)
+    hipLaunchKernelGGL((k_transition_bwd<128, 512, false, true>), gd, bd, 0, stream, zz, G, ma,
+                       w1, w2t, w1t, g_z, hh, gh, gb, p.cells, ntiles);
+  else
+    hipLaunchKernelGGL((k_transition_bwd<128, 512, false, false>), gd, bd, 0, stream, zz, G, ma,
+                       w1, w2t, w1t, g_z, hh, gh, gb, p.cells, ntiles);
   return hipGetLastError();
 }
 

@@ -110,7 +110,215 @@ __global__ __launch_bounds__(kWgThreads) void k_wgrad(const bf16* __restrict__ A
       }
 }
 
+// ---------------------------------------------------------------------------
+// The transition's weight gradients recomputed from z and bf16(G), without
+// materialising H or g_H: for hidden chunk j (32 units),
+//   pre^T = z W1[j]^T, gh^T = bf16(G) W2T[j]^T     (cells x units, k = features)
+//   g_H = gh * [pre > 0], H = relu(pre)            (lane-local)
+//   dW1[j] += g_H^T z,  dW2[:, j] += bf16(G)^T H    (k = cells)
+// Workgroup (slice, group): four waves own chunks 4 group .. 4 group + 3 and
+// walk the same 64-cell blocks of the slice. In the first two products the
+// lane holds a unit and 16 cells, so the packed g_H and H are already the
+// MFMA operands of the contractions over cells (k-step s takes result
+// elements 8 s .. 8 s + 7, cells 16 s + 8 (e / 4) + 4 h + e % 4); the other
+// operand, z or bf16(G) with a feature per lane, is read from an LDS copy in
+// [feature][cell] layout as two 8-byte runs per fragment. Each block is
+// staged in LDS twice (row-major for the first two products, transposed for
+// the contractions); the next block's rows are loaded into registers while
+// the current block's products run and are written after them. Each wave
+// writes its chunk's partial dW1 rows and dW2 columns for the slice; the
+// slices are added in order afterwards.
+constexpr int kRcCells = 64;              // cells per block (two 32-cell halves)
+constexpr int kRcPitch = kRcCells + 4;   // [feature][cell] pitch in elements (136 bytes)
+constexpr int kRcRow = 128 + 8;          // [cell][feature] pitch in elements (272 bytes)
+
+template <int CZ, int HID>
+__global__ __launch_bounds__(256, 1) void k_wgrad_rc(
+    const bf16* __restrict__ z, const bf16* __restrict__ Gb, const bf16* __restrict__ W1,
+    const bf16* __restrict__ W2T, float* __restrict__ part1, float* __restrict__ part2,
+    int64_t cells, int64_t slice_cells) {
+  constexpr int KT = CZ / 16, FB = CZ / 32, GROUPS = HID / 128;
+  static_assert(CZ == 128, "row staging assumes 128 features");
+  // [buffer][operand: 0 z, 1 G]
+  __shared__ bf16 tr[2][2][CZ * kRcPitch];
+  __shared__ bf16 rm[2][2][kRcCells * kRcRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int group = blockIdx.x % GROUPS;
+  const int64_t slice = blockIdx.x / GROUPS;
+  const int j = 4 * group + wave;
+  const int64_t cb0 = slice * slice_cells;
+  const int64_t cb1 = cb0 + slice_cells < cells ? cb0 + slice_cells : cells;
+
+  // chunk j's weights as the B operand: unit 32 j + l32, features 16 t + 8 h ..
+  bf16x8 wf1[KT], wf2[KT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    wf1[t] = *reinterpret_cast<const bf16x8*>(W1 + (int64_t)(32 * j + l32) * CZ + 16 * t + 8 * h);
+    wf2[t] = *reinterpret_cast<const bf16x8*>(W2T + (int64_t)(32 * j + l32) * CZ + 16 * t + 8 * h);
+  }
+  f32x16 acc1[FB], acc2[FB];
+#pragma unroll
+  for (int f = 0; f < FB; ++f) {
+    acc1[f] = f32x16{};
+    acc2[f] = f32x16{};
+  }
+
+  // staging: thread -> operand (tid < 128: z, else G), cells 2 cp and 2 cp + 1,
+  // 16-byte pieces sp0 .. sp0 + 3 of each; the transposed copy is written a
+  // 4-byte word (two adjacent cells of one feature) at a time
+  const int op = tid >> 7, st = tid & 127, cp = st >> 2, sp0 = 4 * (st & 3);
+  const bf16* ssrc = op == 0 ? z : Gb;
+  bf16x8 nxt[2][4];  // [cell of the pair][piece]
+  auto load_rows = [&](int64_t c0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t c = c0 + 2 * cp + u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        nxt[u][q] = c < cb1 ? *reinterpret_cast<const bf16x8*>(ssrc + c * CZ + 8 * (sp0 + q))
+                            : bf16x8{};
+    }
+  };
+  auto write_rows = [&](int buf) {
+    bf16* T = tr[buf][op];
+    bf16* R = rm[buf][op];
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int f0 = 8 * (sp0 + q);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        *reinterpret_cast<bf16x8*>(R + (2 * cp + u) * kRcRow + f0) = nxt[u][q];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16x2 w;
+        w[0] = nxt[0][q][e];
+        w[1] = nxt[1][q][e];
+        *reinterpret_cast<bf16x2*>(T + (f0 + e) * kRcPitch + 2 * cp) = w;
+      }
+    }
+  };
+
+  int buf = 0;
+  if (cb0 < cb1) {
+    load_rows(cb0);
+    write_rows(0);
+  }
+  __syncthreads();
+  for (int64_t c0 = cb0; c0 < cb1; c0 += kRcCells) {
+    const bool more = c0 + kRcCells < cb1;
+    if (more) load_rows(c0 + kRcCells);  // in flight during this block's products
+    const bf16* Rz = rm[buf][0];
+    const bf16* Rg = rm[buf][1];
+    const bf16* Z = tr[buf][0];
+    const bf16* Gt = tr[buf][1];
+    f32x16 pre[2], gh[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      pre[hb] = f32x16{};
+      gh[hb] = f32x16{};
+    }
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const int r = (32 * hb + l32) * kRcRow + 16 * t + 8 * h;
+        const bf16x8 za = *reinterpret_cast<const bf16x8*>(Rz + r);
+        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(Rg + r);
+        pre[hb] = wg_mfma(za, wf1[t], pre[hb]);
+        gh[hb] = wg_mfma(ga, wf2[t], gh[hb]);
+      }
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      bf16x8 hk[2], gk[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = pre[hb][8 * s + e];
+          hk[s][e] = (bf16)(pv > 0.f ? pv : 0.f);
+          gk[s][e] = (bf16)(pv > 0.f ? gh[hb][8 * s + e] : 0.f);
+        }
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int f = 0; f < FB; ++f) {
+          const int row = (32 * f + l32) * kRcPitch + 32 * hb + 16 * s + 4 * h;
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          const bf16x4 z0 = *reinterpret_cast<const bf16x4*>(Z + row);
+          const bf16x4 z1 = *reinterpret_cast<const bf16x4*>(Z + row + 8);
+          const bf16x4 g0 = *reinterpret_cast<const bf16x4*>(Gt + row);
+          const bf16x4 g1 = *reinterpret_cast<const bf16x4*>(Gt + row + 8);
+          bf16x8 zf, gf;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            zf[e] = z0[e];
+            zf[4 + e] = z1[e];
+            gf[e] = g0[e];
+            gf[4 + e] = g1[e];
+          }
+          acc1[f] = wg_mfma(gk[s], zf, acc1[f]);  // dW1[j] (units x features)
+          acc2[f] = wg_mfma(gf, hk[s], acc2[f]);  // dW2[:, j] (features x units)
+        }
+    }
+    // the other buffer was last read two blocks ago, before the previous barrier
+    if (more) write_rows(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+  // partials: acc1[f] element r is unit 8 (r / 4) + 4 h + r % 4, feature 32 f + l32;
+  // acc2[f] element r is feature 32 f + 8 (r / 4) + 4 h + r % 4, unit l32
+  float* o1 = part1 + slice * HID * CZ;
+  float* o2 = part2 + slice * CZ * HID;
+#pragma unroll
+  for (int f = 0; f < FB; ++f)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 8 * (r / 4) + 4 * h + r % 4;
+      o1[(int64_t)(32 * j + i) * CZ + 32 * f + l32] = acc1[f][r];
+      o2[(int64_t)(32 * f + i) * HID + 32 * j + l32] = acc2[f][r];
+    }
+}
+
 }  // namespace
+
+bool wgrad_rc_supported(int c_z, int hidden, nt_dtype dtype) {
+  return dtype == NT_BF16 && c_z == 128 && hidden == 512;
+}
+
+// Slices of the cells: one workgroup per (slice, group of four chunks), about
+// one workgroup per CU of a 256-CU part, at least 256 cells a slice.
+int wgrad_rc_slices(int64_t cells) {
+  int64_t S = 256 / 4;
+  const int64_t smax = (cells + 255) / 256;
+  if (S > smax) S = smax;
+  return (int)(S < 1 ? 1 : S);
+}
+
+hipError_t launch_wgrad_rc(const void* z, const void* Gb, const void* W1, const void* W2T,
+                           float* dW1, float* dW2, float* part, int64_t cells, int slices,
+                           hipStream_t stream) {
+  constexpr int CZ = 128, HID = 512;
+  const int64_t MN = (int64_t)CZ * HID;
+  if (cells == 0) {
+    hipError_t e = launch_sum_splits(part, dW1, 0, MN, stream);
+    return e != hipSuccess ? e : launch_sum_splits(part, dW2, 0, MN, stream);
+  }
+  int64_t slice_cells = (cells + slices - 1) / slices;
+  slice_cells = (slice_cells + kRcCells - 1) / kRcCells * kRcCells;
+  const int64_t S = (cells + slice_cells - 1) / slice_cells;
+  float* part1 = part;
+  float* part2 = part + S * MN;
+  hipLaunchKernelGGL((k_wgrad_rc<CZ, HID>), dim3((unsigned)(S * (HID / 128))), dim3(256), 0,
+                     stream, static_cast<const bf16*>(z), static_cast<const bf16*>(Gb),
+                     static_cast<const bf16*>(W1), static_cast<const bf16*>(W2T), part1, part2,
+                     cells, slice_cells);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_sum_splits(part1, dW1, (int)S, MN, stream);
+  return e != hipSuccess ? e : launch_sum_splits(part2, dW2, (int)S, MN, stream);
+}
 
 int wgrad_splits(int64_t K, int M, int N) {
   const int64_t tiles = (int64_t)(M / kWgTile) * (N / kWgTile);
