@@ -15,8 +15,8 @@
 //   gh^T  (32 x cells) = W2T[j]  . bf16(G)^T  (k = features)
 //   g_z^T (c_z x cells) += W1T[:, j] . g_H^T  (k = the chunk's units)
 // The chunk's 24 KiB of weight fragments are double-buffered through LDS:
-// the loads of chunk j + 1 are issued at the start of chunk j and written
-// after its products. Result rows of the first two products are permuted
+// the loads of chunk j + 2 are issued at the start of chunk j, and chunk
+// j + 1 is written after chunk j's products. Result rows of the first two products are permuted
 // (bits 2 and 3 of the row swapped) so that lane group h holds units
 // 16 s + 8 h + 0..7 in elements 8 s .. 8 s + 7: the mask, the bf16 pack of
 // g_H and the third product's operand are lane-local, and the third
@@ -28,9 +28,10 @@
 namespace nt {
 namespace {
 
-constexpr int kBwWaves = 4;
+constexpr int kBwCB = 1;                          // 32-cell blocks per wave
+constexpr int kBwWaves = 8;
 constexpr int kBwThreads = kBwWaves * 64;
-constexpr int kBwTileCells = kBwWaves * 64;
+constexpr int kBwTileCells = kBwWaves * 32 * kBwCB;
 
 __device__ __forceinline__ f32x16 bw_mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -58,7 +59,7 @@ struct MeanAdjoint {
 // without it the weight gradients are recomputed from z and bf16(G).
 // FROM_MEAN: G is formed from `ma` instead of read.
 template <int CZ, int HID, bool WRITE_H, bool FROM_MEAN>
-__global__ __launch_bounds__(kBwThreads, 1) void k_transition_bwd(
+__global__ __launch_bounds__(kBwThreads, 2) void k_transition_bwd(
     const bf16* __restrict__ z, const float* G, MeanAdjoint ma, const bf16* __restrict__ W1,
     const bf16* __restrict__ W2T, const bf16* __restrict__ W1T, float* g_z,
     bf16* __restrict__ H, bf16* __restrict__ GH, bf16* __restrict__ Gb, int64_t cells,
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(kBwThreads, 1) void k_transition_bwd(
   constexpr int KT = CZ / 16;    // k-steps of the first two products
   constexpr int FB = CZ / 32;    // feature blocks of the third
   constexpr int NCH = HID / 32;  // hidden chunks
-  constexpr int CB = 2;          // 32-cell blocks per wave
+  constexpr int CB = kBwCB;
   // one chunk's fragments: W1 (KT x 64 lanes), W2T (KT x 64), W1T (FB x 2 x 64)
   constexpr int F1 = KT * 64, F2 = KT * 64, F3 = FB * 2 * 64;
   constexpr int FRAGS = F1 + F2 + F3;                 // 16-byte pieces
@@ -80,51 +81,47 @@ __global__ __launch_bounds__(kBwThreads, 1) void k_transition_bwd(
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
 
-  // Piece p of a chunk (natural, coalesced global order) and its fragment
-  // slot. W1 / W2T chunk: 32 rows x CZ features, 16-byte piece q of row r
-  // goes to fragment t = q / 2, lane 32 (q % 2) + p32(r). W1T chunk: CZ rows
-  // x 32 units, piece q (0..3) of row f to fragment (2 (f / 32) + q / 2),
-  // lane 32 (q % 2) + p32(f % 32).
+  // Slot p of a chunk's fragment area and the 16 bytes of the weights it
+  // holds; thread tid fills slots tid, tid + threads, ... (consecutive lanes
+  // write consecutive LDS slots). W1 / W2T fragment t, lane L: row
+  // 32 j + p32(L % 32), features 16 t + 8 (L / 32) ..; W1T fragment
+  // 2 fb + s, lane L: row 32 fb + p32(L % 32), units 32 j + 16 s + 8 (L / 32) ..
   auto piece_src = [&](int j, int p) -> const bf16* {
+    const int L = p & 63, r = bw_p32(L & 31), hh = L >> 5;
     if (p < F1 + F2) {
-      const int pp = p < F1 ? p : p - F1;
-      const int r = pp / (CZ / 8), q = pp % (CZ / 8);
       const bf16* M = p < F1 ? W1 : W2T;
-      return M + (int64_t)(32 * j + r) * CZ + 8 * q;
+      const int t = (p < F1 ? p : p - F1) >> 6;
+      return M + (int64_t)(32 * j + r) * CZ + 16 * t + 8 * hh;
     }
-    const int pp = p - F1 - F2;
-    const int f = pp / 4, q = pp % 4;
-    return W1T + (int64_t)f * HID + 32 * j + 8 * q;
+    const int i = (p - F1 - F2) >> 6, fb = i >> 1, sh = i & 1;
+    return W1T + (int64_t)(32 * fb + r) * HID + 32 * j + 16 * sh + 8 * hh;
   };
-  auto piece_slot = [&](int p) -> int {
-    if (p < F1 + F2) {
-      const int base = p < F1 ? 0 : F1;
-      const int pp = p - base;
-      const int r = pp / (CZ / 8), q = pp % (CZ / 8);
-      return base + 64 * (q / 2) + 32 * (q % 2) + bw_p32(r);
-    }
-    const int pp = p - F1 - F2;
-    const int f = pp / 4, q = pp % 4;
-    return F1 + F2 + 64 * (2 * (f / 32) + q / 2) + 32 * (q % 2) + bw_p32(f % 32);
-  };
+  auto piece_slot = [&](int p) -> int { return p; };
 
-  bf16x8 stage[PER];
-  auto load_chunk = [&](int j) {
+  // Two register sets of staged pieces: the loads of chunk j + 2 are issued
+  // at the start of chunk j, and chunk j + 1 (loaded a chunk earlier) is
+  // written to LDS at its end, so each write waits only for loads that had a
+  // whole chunk of products to land. The chunk loop is unrolled by two so
+  // that the sets are fixed registers.
+  bf16x8 stA[PER], stB[PER];
+  auto load_chunk = [&](int j, bf16x8 (&st)[PER]) {
 #pragma unroll
     for (int k = 0; k < PER; ++k)
-      stage[k] = *reinterpret_cast<const bf16x8*>(piece_src(j, tid + k * kBwThreads));
+      st[k] = *reinterpret_cast<const bf16x8*>(piece_src(j % NCH, tid + k * kBwThreads));
   };
-  auto store_chunk = [&](int buf) {
+  auto store_chunk = [&](int buf, const bf16x8 (&st)[PER]) {
 #pragma unroll
-    for (int k = 0; k < PER; ++k) wbuf[buf][piece_slot(tid + k * kBwThreads)] = stage[k];
+    for (int k = 0; k < PER; ++k) wbuf[buf][piece_slot(tid + k * kBwThreads)] = st[k];
   };
+  static_assert(NCH % 2 == 0, "the chunk loop is unrolled by two");
 
-  load_chunk(0);
-  store_chunk(0);
+  load_chunk(0, stA);
+  store_chunk(0, stA);
+  load_chunk(1, stB);
   __syncthreads();
 
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int64_t cell0 = tile * kBwTileCells + wave * 64;
+    const int64_t cell0 = tile * kBwTileCells + wave * 32 * CB;
     // z and G of this wave's cells: lane (l32, h) of block cb holds features
     // 16 t + 8 h + 0..7 of cell cell0 + 32 cb + l32
     bf16x8 zb[CB][KT], gb[CB][KT];
@@ -179,9 +176,11 @@ __global__ __launch_bounds__(kBwThreads, 1) void k_transition_bwd(
       }
     }
 
-    for (int j = 0; j < NCH; ++j) {
+    // chunk j reads buffer j % 2; `nxt` holds chunk j + 1, `fill` receives
+    // chunk j + 2 (chunks wrap into the next tile's: the weights repeat)
+    auto chunk = [&](int j, bf16x8 (&nxt)[PER], bf16x8 (&fill)[PER]) {
       const int buf = j & 1;
-      load_chunk(j + 1 < NCH ? j + 1 : 0);  // the next chunk (or the next tile's first)
+      load_chunk(j + 2, fill);
       const bf16x8* wb = wbuf[buf];
       f32x16 pre[CB], gh[CB];
 #pragma unroll
@@ -229,8 +228,12 @@ __global__ __launch_bounds__(kBwThreads, 1) void k_transition_bwd(
           for (int cb = 0; cb < CB; ++cb) y[cb][fb] = bw_mfma(a3, hf[cb][s], y[cb][fb]);
         }
       // the other buffer was last read in chunk j - 1, before the previous barrier
-      store_chunk(buf ^ 1);
+      store_chunk(buf ^ 1, nxt);
       __syncthreads();
+    };
+    for (int j = 0; j < NCH; j += 2) {
+      chunk(j, stB, stA);
+      chunk(j + 1, stA, stB);
     }
 
     // g_z (fp32) and bf16(G) of this wave's cells
