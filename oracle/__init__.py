@@ -58,5 +58,5 @@ from .pair_block import (  # noqa: F401
 )
 from .backward import (  # noqa: F401
     loss_weights, loss_eq5, reduce_mean_backward, broadcast_backward, transition_backward,
-    block_backward, chain_loss, chain_backward,
+    block_backward, chain_loss, chain_backward, block_nl, block_backward_nl,
 )

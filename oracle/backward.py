@@ -49,8 +49,11 @@ def loss_weights(B):
 
 
 def loss_eq5(rows, cols, x, pz, S=1):
-    """Equation 5 over the singles x [sum N_i, C] and the pair state
-    pz [sum N_i M_i, C_p]. Returns (L, g_x, g_pz) with the exact gradients
+    """Equation 5 over the singles x [sum N_i, S*C] and the pair state
+    pz [sum N_i M_i, S*C_p]; S is the static leading axis of the non-leading
+    layout, packed inside each row (Eq. 2 moves the ragged axes to the
+    front), so ||X_i||_F^2 sums S*N_i*C values and S = 1 is the leading
+    layout. Returns (L, g_x, g_pz) with the exact gradients
     g_x = 2 alpha_i x / (S C sum N) and g_pz = 2 beta_i pz / (S C_p sum N M)."""
     x = np.asarray(x, dtype=np.float64)
     pz = np.asarray(pz, dtype=np.float64)
@@ -58,7 +61,9 @@ def loss_eq5(rows, cols, x, pz, S=1):
     M = [int(m) for m in cols]
     B = len(N)
     alpha, beta = loss_weights(B)
-    C, Cp = x.shape[1], pz.shape[1]
+    if x.shape[1] % S or pz.shape[1] % S:
+        raise ValueError("row widths must be multiples of S")
+    C, Cp = x.shape[1] // S, pz.shape[1] // S
     d1 = S * C * sum(N)
     d2 = S * Cp * sum(n * m for n, m in zip(N, M))
     L = 0.0
@@ -196,3 +201,56 @@ def chain_backward(lengths, s, ws, S=1):
         g = r.pop("s")
         grads[k] = r
     return L, g, grads
+
+
+# --------------------------------------------- non-leading layout (S, N_i, C)
+def block_nl(lengths, s, w, S):
+    """The block on the non-leading layout: each sample's singles are
+    (S, N_i, C), packed as rows of S*C values (Eq. 2), its pair state
+    (S, N_i, N_i, C_p) as rows of S*C_p. Projections, the transition and the
+    output projection act on the last axis, the broadcast adds along the pair
+    axes, the mean runs over columns: nothing mixes the S slices. Written
+    with an explicit S axis. Returns (s_out [T, S*c_s], z_out [cells, S*c_z])."""
+    s = np.asarray(s, dtype=np.float64)
+    T = s.shape[0]
+    x = s.reshape(T, S, -1)
+    W = {k: np.asarray(v, dtype=np.float64) for k, v in w.items()}
+    a = x @ W["Wa"].T                      # [T, S, c_z]
+    b = x @ W["Wb"].T
+    c_z = a.shape[2]
+    zs, ms = [], []
+    eta = 0
+    for n in (int(v) for v in lengths):
+        A, Bm = a[eta:eta + n], b[eta:eta + n]              # [n, S, c_z]
+        Z = A[:, None, :, :] + Bm[None, :, :, :]            # [n, n, S, c_z]
+        Z = Z + np.maximum(Z @ W["W1"].T, 0.0) @ W["W2"].T
+        zs.append(Z.reshape(n * n, S * c_z))
+        if n:
+            ms.append(Z.mean(axis=1))                       # [n, S, c_z]
+        eta += n
+    z = np.concatenate(zs, axis=0) if zs else np.zeros((0, S * c_z))
+    m = np.concatenate(ms, axis=0) if ms else np.zeros((0, S, c_z))
+    out = x + m @ W["Wo"].T
+    return out.reshape(T, -1), z
+
+
+def block_backward_nl(lengths, s, w, S, g_s_out, g_z_out=None, round_z=None):
+    """Gradients of block_nl: the S slices are independent blocks sharing the
+    weights, so the single and pair gradients are per slice and the weight
+    gradients are sums over slices (the chain rule through the shared
+    weights). Returns a dict like block_backward."""
+    s = np.asarray(s, dtype=np.float64)
+    T = s.shape[0]
+    x = s.reshape(T, S, -1)
+    gs = np.asarray(g_s_out, dtype=np.float64).reshape(T, S, -1)
+    gz = None if g_z_out is None else np.asarray(g_z_out, dtype=np.float64)
+    c_z = np.asarray(w["Wa"]).shape[0]
+    out = {"s": np.zeros_like(x)}
+    for k in range(S):
+        gzk = None if gz is None else gz.reshape(gz.shape[0], S, c_z)[:, k, :]
+        r = block_backward(lengths, x[:, k, :], w, gs[:, k, :], gzk, round_z=round_z)
+        out["s"][:, k, :] = r.pop("s")
+        for name, v in r.items():
+            out[name] = out.get(name, 0.0) + v
+    out["s"] = out["s"].reshape(T, -1)
+    return out

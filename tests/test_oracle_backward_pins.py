@@ -34,10 +34,14 @@ def test_eq5_hand_computed():
     assert L == pytest.approx(20.5 / 3 + 1.3, rel=1e-15)
     np.testing.assert_allclose(gx[:, 0], [2 / 3, 2.0, 3.0], rtol=1e-15)
     np.testing.assert_allclose(gp[:, 0], [0.6, 0.5, 0.5, 0.5, 0.5], rtol=1e-15)
-    # S = 3 (the non-leading layout's divisor) divides both terms by three
-    L3, gx3, _ = oracle.loss_eq5([1, 2], [1, 2], x, pz, S=3)
-    assert L3 == pytest.approx(L / 3, rel=1e-15)
-    np.testing.assert_allclose(gx3, gx / 3, rtol=1e-15)
+    # S = 3 (the non-leading layout: each row holds S slices of C values):
+    # the same values in every slice give the same loss, and each of the
+    # three copies of a value gets a third of its gradient
+    L3, gx3, gp3 = oracle.loss_eq5([1, 2], [1, 2], np.repeat(x, 3, axis=1),
+                                   np.repeat(pz, 3, axis=1), S=3)
+    assert L3 == pytest.approx(L, rel=1e-15)
+    np.testing.assert_allclose(gx3, np.repeat(gx / 3, 3, axis=1), rtol=1e-15)
+    np.testing.assert_allclose(gp3, np.repeat(gp / 3, 3, axis=1), rtol=1e-15)
 
 
 def test_eq5_rectangular_divides_by_n_times_m():
@@ -147,3 +151,36 @@ def test_chain_gradients_match_torch_autograd_dense():
     for w, g in zip(tw, grads):
         for k in w:
             np.testing.assert_allclose(w[k].grad.numpy(), g[k], rtol=1e-10, atol=1e-13)
+
+
+def test_non_leading_block_is_per_slice_leading_block():
+    """Nothing in the block mixes the static axis: slice k of the non-leading
+    block equals the leading block on slice k of the singles."""
+    rng = np.random.default_rng(8)
+    lengths, S, c_s, c_z, hidden = [3, 0, 5, 2], 3, 4, 6, 5
+    s = rng.normal(size=(sum(lengths), S * c_s))
+    w = _weights(rng, c_s, c_z, hidden)
+    s_out, z_out = oracle.block_nl(lengths, s, w, S)
+    cells = int(np.square(lengths).sum())
+    for k in range(S):
+        rs, rz = oracle.block(lengths, s[:, k * c_s:(k + 1) * c_s], w)
+        np.testing.assert_allclose(s_out[:, k * c_s:(k + 1) * c_s], rs, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(z_out.reshape(cells, S, c_z)[:, k, :], rz, rtol=1e-12,
+                                   atol=1e-12)
+
+
+def test_non_leading_gradients_match_finite_differences():
+    rng = np.random.default_rng(9)
+    lengths, S, c_s, c_z, hidden = [2, 3], 3, 4, 3, 5
+    s = rng.normal(size=(sum(lengths), S * c_s))
+    w = _weights(rng, c_s, c_z, hidden)
+
+    def loss():
+        so, zo = oracle.block_nl(lengths, s, w, S)
+        return oracle.loss_eq5(lengths, lengths, so, zo, S=S)[0]
+
+    so, zo = oracle.block_nl(lengths, s, w, S)
+    _, gx, gz = oracle.loss_eq5(lengths, lengths, so, zo, S=S)
+    g = oracle.block_backward_nl(lengths, s, w, S, gx, gz)
+    params = {"s": s, **w}
+    _fd_check(loss, params, g)
