@@ -300,14 +300,15 @@ nt_status nt_loss_workspace_bytes(const nt_partition* p, size_t* bytes);
 
 /*
  * The sample-weighted squared loss of Appendix A.1, Equation 5, over a
- * block's returned singles x [T, c_s] and pair state pz [cells, c_z]:
+ * block's returned singles x [T, S, c_s] and pair state pz [cells, S, c_z]:
  *   L = sum_i alpha_i |x_i|^2 / (S c_s sum_i N_i)
  *     + sum_i beta_i |pz_i|^2 / (S c_z sum_i N_i M_i),
  *   alpha_i = 1 + i / B, beta_i = 1.5 - i / (2 B), i = 0 .. B - 1,
- * with S = 1 for the leading layouts (S >= 1 is accepted for others). The
+ * S is the static leading axis of the non-leading (S, N_i, C) layout, packed
+ * inside each row (Eq. 2), 1 <= S <= 64; S = 1 is the leading layout. The
  * squares accumulate in fp32 per row and the rows' terms in fp64 into
- * *loss (device, one double). g_x [T, c_s] and g_pz [cells, c_z] (fp32,
- * either may be NULL) receive 2 alpha_i x / (S c_s sum N) and
+ * *loss (device, one double). g_x [T, S, c_s] and g_pz [cells, S, c_z]
+ * (fp32, either may be NULL) receive 2 alpha_i x / (S c_s sum N) and
  * 2 beta_i pz / (S c_z sum N M). Deterministic. workspace: device, at least
  * nt_loss_workspace_bytes, 16-byte aligned.
  */
@@ -386,6 +387,51 @@ nt_status nt_pair_block_backward(const nt_partition* p, const void* s_in, const 
                                  const float* g_z_out, float* g_s_in, const nt_block_grads* grads,
                                  int32_t c_s, int32_t c_z, int32_t hidden, nt_dtype dtype,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The non-leading layout (Appendix A.1's non-leading variant; Section 3.1,
+ * Eq. 2: a sample with a static leading axis, singles (S, N_i, C) and pairs
+ * (S, N_i, N_i, C_p), packs its ragged axes first, so every single row holds
+ * S slices of c_s values and every pair cell S slices of c_z). Projections,
+ * the transition and the output projection act per slice on the last axis,
+ * the broadcast adds along the pair axes and the mean runs over columns, so
+ * no step mixes the slices; the weights are shared by all of them. Square
+ * partitions; 1 <= S <= 64 and S * c_z <= 512. With S > 1 the broadcast and
+ * the transition run as two kernels (z rounded to the storage type between
+ * them), the residual adding that rounded z.
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes nt_pair_block_nl needs. */
+nt_status nt_block_nl_workspace_bytes(const nt_partition* p, int32_t S, int32_t c_s, int32_t c_z,
+                                      int32_t hidden, nt_dtype dtype, size_t* bytes);
+
+/*
+ * One block on the non-leading layout: s_in, s_out [T, S, c_s]; z_out
+ * [cells, S, c_z]; weights as for nt_pair_block. s_out may equal s_in.
+ * Errors as nt_pair_block, plus NT_ERR_INVALID for S out of range or a
+ * rectangular partition.
+ */
+nt_status nt_pair_block_nl(const nt_partition* p, const void* s_in, void* s_out, void* z_out,
+                           const nt_block_weights* w, int32_t S, int32_t c_s, int32_t c_z,
+                           int32_t hidden, nt_dtype dtype, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Workspace bytes nt_pair_block_backward_nl needs. */
+nt_status nt_block_backward_nl_workspace_bytes(const nt_partition* p, int32_t S, int32_t c_s,
+                                               int32_t c_z, int32_t hidden, nt_dtype dtype,
+                                               size_t* bytes);
+
+/*
+ * Backward of nt_pair_block_nl, as nt_pair_block_backward with every single
+ * array [T, S, ...] and pair array [cells, S, ...]; the weight gradients sum
+ * over the slices.
+ */
+nt_status nt_pair_block_backward_nl(const nt_partition* p, const void* s_in, const void* z_out,
+                                    const nt_block_weights* w, const float* g_s_out,
+                                    const float* g_z_out, float* g_s_in,
+                                    const nt_block_grads* grads, int32_t S, int32_t c_s,
+                                    int32_t c_z, int32_t hidden, nt_dtype dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /* Thread-local description of the last failure in this thread ("" if none). */
 const char* nt_last_error(void);

@@ -371,7 +371,8 @@ def nt_loss_workspace_bytes(p: Partition) -> int:
 
 def nt_pair_loss_eq5(p: Partition, x, pz, S: int = 1, grads: bool = True, workspace=None,
                      stream=None):
-    """Equation 5 over singles x [T, c_s] and pair state pz [cells, c_z].
+    """Equation 5 over singles x [T, S*c_s] and pair state pz [cells, S*c_z]
+    (S: the static axis of the non-leading layout, 1 for the leading one).
     Returns (loss, g_x, g_pz): loss a float64 device tensor of one element,
     the gradients fp32 (None when grads is False)."""
     torch = _torch()
@@ -383,8 +384,11 @@ def nt_pair_loss_eq5(p: Partition, x, pz, S: int = 1, grads: bool = True, worksp
     g_pz = torch.empty(pz.shape, dtype=torch.float32, device=dev) if grads else None
     if workspace is None:
         workspace = torch.empty(nt_loss_workspace_bytes(p), dtype=torch.uint8, device=dev)
-    _check(_native.lib().nt_pair_loss_eq5(ctypes.byref(p.struct), _ptr(x), x.shape[-1], _ptr(pz),
-                                          pz.shape[-1], S, _dtype_code(x), _ptr(loss), _ptr(g_x),
+    if x.shape[-1] % S or pz.shape[-1] % S:
+        raise ValueError("row widths must be multiples of S")
+    _check(_native.lib().nt_pair_loss_eq5(ctypes.byref(p.struct), _ptr(x), x.shape[-1] // S,
+                                          _ptr(pz), pz.shape[-1] // S, S, _dtype_code(x),
+                                          _ptr(loss), _ptr(g_x),
                                           _ptr(g_pz), _ptr(workspace), workspace.numel(),
                                           _stream(stream, dev)))
     return loss[:1], g_x, g_pz
@@ -482,5 +486,62 @@ def nt_pair_block_backward(p: Partition, s_in, z_out, weights, g_s_out, g_z_out=
     _check(_native.lib().nt_pair_block_backward(
         ctypes.byref(p.struct), _ptr(s_in), _ptr(z_out), ctypes.byref(wst), _ptr(g_s_out),
         _ptr(g_z_out), _ptr(g_s_in), ctypes.byref(gst), c_s, c_z, hidden, _dtype_code(s_in),
+        _ptr(workspace), workspace.numel(), _stream(stream, dev)))
+    return g_s_in, grads
+
+
+# ------------------------------------------------------ non-leading layout
+def nt_pair_block_nl(p: Partition, s_in, weights, S: int, s_out=None, z_out=None,
+                     workspace=None, stream=None):
+    """The block on the non-leading layout: s_in [T, S*c_s]; returns
+    (s_out [T, S*c_s], z_out [cells, S*c_z])."""
+    torch = _torch()
+    if isinstance(weights, dict):
+        weights = [weights[k] for k in _WEIGHT_NAMES]
+    Wa, Wb, W1, W2, Wo = weights
+    c_s, c_z, hidden = Wa.shape[1], Wa.shape[0], W1.shape[0]
+    if s_in.shape[-1] != S * c_s:
+        raise ValueError("s_in rows must hold S * c_s values")
+    if s_out is None:
+        s_out = torch.empty_like(s_in)
+    if z_out is None:
+        z_out = torch.empty((p.cells, S * c_z), dtype=s_in.dtype, device=s_in.device)
+    n = ctypes.c_size_t()
+    _check(_native.lib().nt_block_nl_workspace_bytes(ctypes.byref(p.struct), S, c_s, c_z, hidden,
+                                                     _dtype_code(s_in), ctypes.byref(n)))
+    if workspace is None:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=s_in.device)
+    wst = NtBlockWeights(*[_ptr(w) for w in weights])
+    _check(_native.lib().nt_pair_block_nl(ctypes.byref(p.struct), _ptr(s_in), _ptr(s_out),
+                                          _ptr(z_out), ctypes.byref(wst), S, c_s, c_z, hidden,
+                                          _dtype_code(s_in), _ptr(workspace), workspace.numel(),
+                                          _stream(stream, s_in.device)))
+    return s_out, z_out
+
+
+def nt_pair_block_backward_nl(p: Partition, s_in, z_out, weights, S: int, g_s_out, g_z_out=None,
+                              g_s_in=None, grads=None, workspace=None, stream=None):
+    """Backward of nt_pair_block_nl; returns (g_s_in, grads)."""
+    torch = _torch()
+    dev = s_in.device
+    if isinstance(weights, dict):
+        weights = [weights[k] for k in _WEIGHT_NAMES]
+    Wa, Wb, W1, W2, Wo = weights
+    c_s, c_z, hidden = Wa.shape[1], Wa.shape[0], W1.shape[0]
+    if g_s_in is None:
+        g_s_in = torch.empty((p.T, S * c_s), dtype=torch.float32, device=dev)
+    if grads is None:
+        grads = {k: torch.empty(w.shape, dtype=torch.float32, device=dev)
+                 for k, w in zip(_WEIGHT_NAMES, weights)}
+    n = ctypes.c_size_t()
+    _check(_native.lib().nt_block_backward_nl_workspace_bytes(
+        ctypes.byref(p.struct), S, c_s, c_z, hidden, _dtype_code(s_in), ctypes.byref(n)))
+    if workspace is None:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+    wst = NtBlockWeights(*[_ptr(w) for w in weights])
+    gst = _native.NtBlockGrads(*[_ptr(grads[k]) for k in _WEIGHT_NAMES])
+    _check(_native.lib().nt_pair_block_backward_nl(
+        ctypes.byref(p.struct), _ptr(s_in), _ptr(z_out), ctypes.byref(wst), _ptr(g_s_out),
+        _ptr(g_z_out), _ptr(g_s_in), ctypes.byref(gst), S, c_s, c_z, hidden, _dtype_code(s_in),
         _ptr(workspace), workspace.numel(), _stream(stream, dev)))
     return g_s_in, grads

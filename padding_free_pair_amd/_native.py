@@ -21,7 +21,9 @@ EXPORTS = ("nt_partition_sizes", "nt_make_partition", "nt_partition_sizes_rect",
            "nt_loss_workspace_bytes", "nt_pair_loss_eq5", "nt_pair_reduce_backward",
            "nt_pair_broadcast_backward", "nt_transition_backward_workspace_bytes",
            "nt_pair_transition_backward", "nt_block_backward_workspace_bytes",
-           "nt_pair_block_backward", "nt_last_error", "nt_version")
+           "nt_pair_block_backward", "nt_block_nl_workspace_bytes", "nt_pair_block_nl",
+           "nt_block_backward_nl_workspace_bytes", "nt_pair_block_backward_nl", "nt_last_error",
+           "nt_version")
 
 
 class NtPartition(ctypes.Structure):
@@ -94,6 +96,12 @@ def lib() -> ctypes.CDLL:
         "nt_block_backward_workspace_bytes": [part, i32, i32, i32, ctypes.c_int, P(sz)],
         "nt_pair_block_backward": [part, vp, vp, P(NtBlockWeights), vp, vp, vp, P(NtBlockGrads),
                                    i32, i32, i32, ctypes.c_int, vp, sz, vp],
+        "nt_block_nl_workspace_bytes": [part, i32, i32, i32, i32, ctypes.c_int, P(sz)],
+        "nt_pair_block_nl": [part, vp, vp, vp, P(NtBlockWeights), i32, i32, i32, i32, ctypes.c_int,
+                             vp, sz, vp],
+        "nt_block_backward_nl_workspace_bytes": [part, i32, i32, i32, i32, ctypes.c_int, P(sz)],
+        "nt_pair_block_backward_nl": [part, vp, vp, P(NtBlockWeights), vp, vp, vp, P(NtBlockGrads),
+                                      i32, i32, i32, i32, ctypes.c_int, vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)

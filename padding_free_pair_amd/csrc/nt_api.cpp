@@ -95,11 +95,12 @@ struct BlockWorkspace {
 };
 
 // a and b are kept in fp32 (the projections' accumulators, unrounded), m too;
-// b has one row per column single (T_cols, which is T for square pairs).
-BlockWorkspace block_workspace(int64_t T, int64_t T_cols, int c_z, nt_dtype) {
+// b has one row per column single (T_cols, which is T for square pairs). In
+// the non-leading layout every single row holds S slices.
+BlockWorkspace block_workspace(int64_t T, int64_t T_cols, int c_z, nt_dtype, int S = 1) {
   BlockWorkspace w;
-  const uint64_t a = nt::align256((size_t)T * c_z * sizeof(float));
-  const uint64_t b = nt::align256((size_t)T_cols * c_z * sizeof(float));
+  const uint64_t a = nt::align256((size_t)T * S * c_z * sizeof(float));
+  const uint64_t b = nt::align256((size_t)T_cols * S * c_z * sizeof(float));
   w.a = 0;
   w.b = a;
   w.m = a + b;
@@ -200,21 +201,41 @@ nt_status make_partition(const int32_t* rows, const int32_t* cols, int32_t B, bo
   return ok();
 }
 
-// One block; s_cols is s_rows for square partitions.
+// The partition seen by a cell-local kernel over rows of width c_z when each
+// cell holds S of them (the non-leading layout): cells * S rows, no sample
+// index (cell-local kernels without the fused broadcast do not decode).
+nt_partition rows_view(const nt_partition& p, int S) {
+  nt_partition v = p;
+  v.cells = p.cells * S;
+  v.tile_sample = nullptr;
+  return v;
+}
+
+nt_status check_static_axis(int32_t S, int32_t c_z) {
+  if (S < 1 || S > 64)
+    return fail(NT_ERR_INVALID, "S = %d must be in [1, 64]", (int)S);
+  if ((int64_t)S * c_z > nt::kMaxCz)
+    return fail(NT_ERR_INVALID, "S * c_z = %d exceeds %d", (int)(S * c_z), nt::kMaxCz);
+  return NT_OK;
+}
+
+// One block; s_cols is s_rows for square partitions. S > 1: the non-leading
+// layout (square partitions), rows of S slices.
 nt_status pair_block(const nt_partition* p, const void* s_rows, const void* s_cols, void* s_out,
                      void* z_out, const nt_block_weights* w, int32_t c_s, int32_t c_z,
                      int32_t hidden, nt_dtype dtype, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+                     void* stream, int32_t S = 1) {
   NT_TRY(check_partition(p));
   NT_TRY(check_dtype(dtype));
   NT_TRY(check_width("c_s", c_s, nt::kMaxCs));
   NT_TRY(check_width("c_z", c_z, nt::kMaxCz));
   NT_TRY(check_width("hidden", hidden, nt::kMaxHidden));
+  NT_TRY(check_static_axis(S, c_z));
   if (!w) return fail(NT_ERR_NULL, "weights is NULL");
   const size_t es = esize(dtype);
-  const uint64_t sbytes = (uint64_t)p->T * c_s * es;
-  const uint64_t cbytes = (uint64_t)p->T_cols * c_s * es;
-  const uint64_t pair = (uint64_t)p->cells * c_z * es;
+  const uint64_t sbytes = (uint64_t)p->T * S * c_s * es;
+  const uint64_t cbytes = (uint64_t)p->T_cols * S * c_s * es;
+  const uint64_t pair = (uint64_t)p->cells * S * c_z * es;
   const uint64_t proj = (uint64_t)c_z * c_s * es;
   const uint64_t mlp = (uint64_t)c_z * hidden * es;
   NT_TRY(check_array("s_rows", s_rows, sbytes));
@@ -226,7 +247,7 @@ nt_status pair_block(const nt_partition* p, const void* s_rows, const void* s_co
   NT_TRY(check_array("W1", w->W1, mlp));
   NT_TRY(check_array("W2", w->W2, mlp));
   NT_TRY(check_array("Wo", w->Wo, proj));
-  const BlockWorkspace ws = block_workspace(p->T, p->T_cols, c_z, dtype);
+  const BlockWorkspace ws = block_workspace(p->T, p->T_cols, c_z, dtype, S);
   if (ws.total > 0) {
     NT_TRY(check_array("workspace", workspace, ws.total));
     if (workspace_bytes < ws.total)
@@ -253,8 +274,9 @@ nt_status pair_block(const nt_partition* p, const void* s_rows, const void* s_co
   void* a = base + ws.a;
   void* b = base + ws.b;
   float* m = reinterpret_cast<float*>(base + ws.m);
+  const int64_t TS = p->T * S;  // single rows of c_s values
   if (s_cols == s_rows && p->T_cols == p->T) {
-    NT_TRY(hip_status(nt::launch_linear2(s_rows, dtype, w->Wa, w->Wb, a, b, p->T, c_z, c_s, s),
+    NT_TRY(hip_status(nt::launch_linear2(s_rows, dtype, w->Wa, w->Wb, a, b, TS, c_z, c_s, s),
                       "projections a, b"));
   } else {
     NT_TRY(hip_status(nt::launch_linear(s_rows, dtype, w->Wa, dtype, nullptr, a, NT_F32, p->T,
@@ -264,11 +286,22 @@ nt_status pair_block(const nt_partition* p, const void* s_rows, const void* s_co
                                         p->T_cols, c_z, c_s, s),
                       "projection b"));
   }
-  NT_TRY(hip_status(nt::launch_transition(*p, nullptr, a, b, z_out, w->W1, w->W2, c_z, hidden,
-                                          dtype, s),
-                    "fused broadcast + transition"));
-  NT_TRY(hip_status(nt::launch_reduce(*p, z_out, m, c_z, dtype, s), "column mean"));
-  return hip_status(nt::launch_linear(m, NT_F32, w->Wo, dtype, s_rows, s_out, dtype, p->T, c_s,
+  if (S == 1) {
+    NT_TRY(hip_status(nt::launch_transition(*p, nullptr, a, b, z_out, w->W1, w->W2, c_z, hidden,
+                                            dtype, s),
+                      "fused broadcast + transition"));
+  } else {
+    // the broadcast over rows of S slices, then the cell-local transition in
+    // place over cells * S rows of c_z
+    NT_TRY(hip_status(nt::launch_broadcast(*p, a, b, z_out, S * c_z, dtype, s, true),
+                      "broadcast"));
+    const nt_partition v = rows_view(*p, S);
+    NT_TRY(hip_status(nt::launch_transition(v, z_out, nullptr, nullptr, z_out, w->W1, w->W2, c_z,
+                                            hidden, dtype, s),
+                      "transition"));
+  }
+  NT_TRY(hip_status(nt::launch_reduce(*p, z_out, m, S * c_z, dtype, s), "column mean"));
+  return hip_status(nt::launch_linear(m, NT_F32, w->Wo, dtype, s_rows, s_out, dtype, TS, c_s,
                                       c_z, s),
                     "output projection");
 }
@@ -402,26 +435,27 @@ struct BlockBwdWs {
 };
 
 BlockBwdWs block_backward_ws(const nt_partition* p, int c_s, int c_z, int hidden,
-                             nt_dtype dtype) {
+                             nt_dtype dtype, int S = 1) {
   BlockBwdWs w;
   const uint64_t es = esize(dtype);
-  const uint64_t single = nt::align256((size_t)p->T * c_z * sizeof(float));
+  const int64_t TS = p->T * S, CS = p->cells * S;  // rows of c_s / c_z values
+  const uint64_t single = nt::align256((size_t)TS * c_z * sizeof(float));
   const uint64_t proj = nt::align256((size_t)c_s * c_z * es);
   uint64_t off = 0;
   w.a = off;     off += single;
   w.b = off;     off += single;
-  w.z = off;     off += nt::align256((size_t)p->cells * c_z * es);
+  w.z = off;     off += nt::align256((size_t)CS * c_z * es);
   w.m = off;     off += single;
   w.g_m = off;   off += single;
-  w.G = off;     off += nt::align256((size_t)p->cells * c_z * sizeof(float));
+  w.G = off;     off += nt::align256((size_t)CS * c_z * sizeof(float));
   w.g_a = off;   off += single;
   w.g_b = off;   off += single;
   w.WoT = off;   off += proj;
   w.WaT = off;   off += proj;
   w.WbT = off;   off += proj;
-  w.psplits = nt::gemm_tn_splits(p->T, c_z, c_s);
+  w.psplits = nt::gemm_tn_splits(TS, c_z, c_s);
   w.ppart = off; off += nt::align256((size_t)w.psplits * c_s * c_z * sizeof(float));
-  w.trans = off; off += transition_backward_ws(p->cells, c_z, hidden, dtype).total;
+  w.trans = off; off += transition_backward_ws(CS, c_z, hidden, dtype).total;
   w.total = off;
   return w;
 }
@@ -650,9 +684,11 @@ nt_status nt_pair_loss_eq5(const nt_partition* p, const void* x, int32_t c_s, co
   NT_TRY(check_width("c_s", c_s, nt::kMaxCs));
   NT_TRY(check_width("c_z", c_z, nt::kMaxCz));
   if (S < 1) return fail(NT_ERR_INVALID, "S = %d must be at least 1", (int)S);
+  if (S > 64) return fail(NT_ERR_INVALID, "S = %d must be at most 64", (int)S);
   const uint64_t es = esize(dtype);
-  const uint64_t xb = (uint64_t)p->T * c_s * es, pb = (uint64_t)p->cells * c_z * es;
-  const uint64_t gxb = (uint64_t)p->T * c_s * 4, gpb = (uint64_t)p->cells * c_z * 4;
+  const uint64_t xw = (uint64_t)S * c_s, pw = (uint64_t)S * c_z;  // values per row
+  const uint64_t xb = (uint64_t)p->T * xw * es, pb = (uint64_t)p->cells * pw * es;
+  const uint64_t gxb = (uint64_t)p->T * xw * 4, gpb = (uint64_t)p->cells * pw * 4;
   const uint64_t need = nt::align256((size_t)(p->T > 0 ? p->T : 1) * sizeof(double));
   NT_TRY(check_array("x", x, xb));
   NT_TRY(check_array("pz", pz, pb));
@@ -754,24 +790,28 @@ nt_status nt_block_backward_workspace_bytes(const nt_partition* p, int32_t c_s, 
   return ok();
 }
 
-nt_status nt_pair_block_backward(const nt_partition* p, const void* s_in, const void* z_out,
-                                 const nt_block_weights* w, const float* g_s_out,
-                                 const float* g_z_out, float* g_s_in, const nt_block_grads* grads,
-                                 int32_t c_s, int32_t c_z, int32_t hidden, nt_dtype dtype,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+// The block backward; S > 1 is the non-leading layout (rows of S slices).
+static nt_status block_backward_s(const nt_partition* p, const void* s_in, const void* z_out,
+                                  const nt_block_weights* w, const float* g_s_out,
+                                  const float* g_z_out, float* g_s_in,
+                                  const nt_block_grads* grads, int32_t c_s, int32_t c_z,
+                                  int32_t hidden, nt_dtype dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream, int32_t S) {
   NT_TRY(check_partition(p));
   if (p->col_offsets != p->single_offsets)
     return fail(NT_ERR_INVALID, "the block backward takes square partitions");
   NT_TRY(check_dtype(dtype));
   NT_TRY(check_widths(c_s, c_z, hidden));
+  NT_TRY(check_static_axis(S, c_z));
   if (!w) return fail(NT_ERR_NULL, "weights is NULL");
   if (!grads) return fail(NT_ERR_NULL, "grads is NULL");
   const uint64_t es = esize(dtype);
-  const uint64_t sb = (uint64_t)p->T * c_s * es, zb = (uint64_t)p->cells * c_z * es;
-  const uint64_t gsb = (uint64_t)p->T * c_s * 4, gzb = (uint64_t)p->cells * c_z * 4;
+  const uint64_t TS = (uint64_t)p->T * S, CS = (uint64_t)p->cells * S;
+  const uint64_t sb = TS * c_s * es, zb = CS * c_z * es;
+  const uint64_t gsb = TS * c_s * 4, gzb = CS * c_z * 4;
   const uint64_t proj = (uint64_t)c_z * c_s * es, mlp = (uint64_t)c_z * hidden * es;
   const uint64_t dproj = (uint64_t)c_z * c_s * 4, dmlp = (uint64_t)c_z * hidden * 4;
-  const BlockBwdWs L = block_backward_ws(p, c_s, c_z, hidden, dtype);
+  const BlockBwdWs L = block_backward_ws(p, c_s, c_z, hidden, dtype, S);
   NT_TRY(check_array("s_in", s_in, sb));
   NT_TRY(check_array("z_out", z_out, zb));
   NT_TRY(check_array("Wa", w->Wa, proj));
@@ -815,13 +855,14 @@ nt_status nt_pair_block_backward(const nt_partition* p, const void* s_in, const 
   void* WaT = base + L.WaT;
   void* WbT = base + L.WbT;
   float* ppart = reinterpret_cast<float*>(base + L.ppart);
-  const int64_t T = p->T;
+  const int64_t T = p->T * S;  // single rows of c_s values
+  const int W = S * c_z;       // pair and single row width of the pair-side arrays
 
   // recompute the forward's a, b, z and m
   NT_TRY(hip_status(nt::launch_linear2(s_in, dtype, w->Wa, w->Wb, a, b, T, c_z, c_s, s),
                     "projections a, b"));
-  NT_TRY(hip_status(nt::launch_broadcast(*p, a, b, z, c_z, dtype, s, true), "broadcast"));
-  NT_TRY(hip_status(nt::launch_reduce(*p, z_out, m, c_z, dtype, s), "column mean"));
+  NT_TRY(hip_status(nt::launch_broadcast(*p, a, b, z, W, dtype, s, true), "broadcast"));
+  NT_TRY(hip_status(nt::launch_reduce(*p, z_out, m, W, dtype, s), "column mean"));
   NT_TRY(hip_status(nt::launch_transpose(w->Wo, WoT, c_s, c_z, dtype, s), "transpose Wo"));
   NT_TRY(hip_status(nt::launch_transpose(w->Wa, WaT, c_z, c_s, dtype, s), "transpose Wa"));
   NT_TRY(hip_status(nt::launch_transpose(w->Wb, WbT, c_z, c_s, dtype, s), "transpose Wb"));
@@ -833,10 +874,19 @@ nt_status nt_pair_block_backward(const nt_partition* p, const void* s_in, const 
                                        L.psplits, s),
                     "dWo"));
   // mean (formed inside the transition's gradient), transition, broadcast
-  NT_TRY(transition_backward(p, z, nullptr, w->W1, w->W2, G, grads->W1, grads->W2, c_z, hidden,
-                             dtype, base + L.trans, s, g_m, g_z_out));
-  NT_TRY(hip_status(nt::launch_reduce(*p, G, g_a, c_z, NT_F32, s, false), "row sums"));
-  NT_TRY(hip_status(nt::launch_col_sums(*p, G, g_b, c_z, s), "column sums"));
+  if (S == 1) {
+    NT_TRY(transition_backward(p, z, nullptr, w->W1, w->W2, G, grads->W1, grads->W2, c_z, hidden,
+                               dtype, base + L.trans, s, g_m, g_z_out));
+  } else {
+    // the mean's adjoint over rows of S slices, then the cell-local gradient
+    // over cells * S rows of c_z
+    NT_TRY(hip_status(nt::launch_mean_backward(*p, g_m, g_z_out, G, W, s), "mean backward"));
+    const nt_partition v = rows_view(*p, S);
+    NT_TRY(transition_backward(&v, z, G, w->W1, w->W2, G, grads->W1, grads->W2, c_z, hidden,
+                               dtype, base + L.trans, s));
+  }
+  NT_TRY(hip_status(nt::launch_reduce(*p, G, g_a, W, NT_F32, s, false), "row sums"));
+  NT_TRY(hip_status(nt::launch_col_sums(*p, G, g_b, W, s), "column sums"));
   // a = s Wa^T, b = s Wb^T
   NT_TRY(hip_status(nt::launch_linear(g_a, NT_F32, WaT, dtype, g_s_out, g_s_in, NT_F32, T, c_s,
                                       c_z, s),
@@ -850,6 +900,59 @@ nt_status nt_pair_block_backward(const nt_partition* p, const void* s_in, const 
   return hip_status(nt::launch_gemm_tn(g_b, NT_F32, s_in, dtype, grads->Wb, ppart, T, c_z, c_s,
                                        L.psplits, s),
                     "dWb");
+}
+
+nt_status nt_pair_block_backward(const nt_partition* p, const void* s_in, const void* z_out,
+                                 const nt_block_weights* w, const float* g_s_out,
+                                 const float* g_z_out, float* g_s_in, const nt_block_grads* grads,
+                                 int32_t c_s, int32_t c_z, int32_t hidden, nt_dtype dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return block_backward_s(p, s_in, z_out, w, g_s_out, g_z_out, g_s_in, grads, c_s, c_z, hidden,
+                          dtype, workspace, workspace_bytes, stream, 1);
+}
+
+nt_status nt_block_nl_workspace_bytes(const nt_partition* p, int32_t S, int32_t c_s, int32_t c_z,
+                                      int32_t hidden, nt_dtype dtype, size_t* bytes) {
+  NT_TRY(check_partition(p));
+  NT_TRY(check_dtype(dtype));
+  NT_TRY(check_widths(c_s, c_z, hidden));
+  NT_TRY(check_static_axis(S, c_z));
+  if (!bytes) return fail(NT_ERR_NULL, "bytes is NULL");
+  *bytes = block_workspace(p->T, p->T_cols, c_z, dtype, S).total;
+  return ok();
+}
+
+nt_status nt_pair_block_nl(const nt_partition* p, const void* s_in, void* s_out, void* z_out,
+                           const nt_block_weights* w, int32_t S, int32_t c_s, int32_t c_z,
+                           int32_t hidden, nt_dtype dtype, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  NT_TRY(check_partition(p));
+  if (p->col_offsets != p->single_offsets)
+    return fail(NT_ERR_INVALID, "the non-leading block takes square partitions");
+  return pair_block(p, s_in, s_in, s_out, z_out, w, c_s, c_z, hidden, dtype, workspace,
+                    workspace_bytes, stream, S);
+}
+
+nt_status nt_block_backward_nl_workspace_bytes(const nt_partition* p, int32_t S, int32_t c_s,
+                                               int32_t c_z, int32_t hidden, nt_dtype dtype,
+                                               size_t* bytes) {
+  NT_TRY(check_partition(p));
+  NT_TRY(check_dtype(dtype));
+  NT_TRY(check_widths(c_s, c_z, hidden));
+  NT_TRY(check_static_axis(S, c_z));
+  if (!bytes) return fail(NT_ERR_NULL, "bytes is NULL");
+  *bytes = block_backward_ws(p, c_s, c_z, hidden, dtype, S).total;
+  return ok();
+}
+
+nt_status nt_pair_block_backward_nl(const nt_partition* p, const void* s_in, const void* z_out,
+                                    const nt_block_weights* w, const float* g_s_out,
+                                    const float* g_z_out, float* g_s_in,
+                                    const nt_block_grads* grads, int32_t S, int32_t c_s,
+                                    int32_t c_z, int32_t hidden, nt_dtype dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return block_backward_s(p, s_in, z_out, w, g_s_out, g_z_out, g_s_in, grads, c_s, c_z, hidden,
+                          dtype, workspace, workspace_bytes, stream, S);
 }
 
 }  // extern "C"

@@ -348,15 +348,16 @@ hipError_t launch_col_sums(const nt_partition& p, const float* g_z, float* g_b, 
 hipError_t launch_loss_eq5(const nt_partition& p, const void* x, int c_s, const void* pz, int c_z,
                            int S, nt_dtype dtype, double* partial, double* loss, float* g_x,
                            float* g_pz, hipStream_t s) {
+  // rows hold S slices of c_s (c_z) values: the divisors count every value
   const double d1 = (double)S * c_s * (double)p.T;
   const double d2 = (double)S * c_z * (double)p.cells;
   const double inv_d1 = d1 > 0 ? 1.0 / d1 : 0.0, inv_d2 = d2 > 0 ? 1.0 / d2 : 0.0;
   if (p.T > 0) {
     hipError_t e = dtype == NT_BF16
-                       ? launch_loss_t<bf16>(p, x, c_s, pz, c_z, inv_d1, inv_d2, partial, g_x,
-                                             g_pz, s)
-                       : launch_loss_t<float>(p, x, c_s, pz, c_z, inv_d1, inv_d2, partial, g_x,
-                                              g_pz, s);
+                       ? launch_loss_t<bf16>(p, x, S * c_s, pz, S * c_z, inv_d1, inv_d2, partial,
+                                             g_x, g_pz, s)
+                       : launch_loss_t<float>(p, x, S * c_s, pz, S * c_z, inv_d1, inv_d2, partial,
+                                              g_x, g_pz, s);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_loss_final, dim3(1), dim3(kThreads), 0, s, partial, p.T, loss);

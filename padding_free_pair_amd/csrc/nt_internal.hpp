@@ -138,7 +138,8 @@ hipError_t launch_mean_backward(const nt_partition& p, const float* g_m, const f
 // g_b[mu_i + c] = sum_r g_z[o_i + r M_i + c] (fp32).
 hipError_t launch_col_sums(const nt_partition& p, const float* g_z, float* g_b, int c_z,
                            hipStream_t stream);
-// Equation 5: partial [max(T, 1)] fp64 scratch, loss one fp64; g_x, g_pz may be null.
+// Equation 5: rows of x hold S * c_s values, rows of pz S * c_z; partial
+// [max(T, 1)] fp64 scratch, loss one fp64; g_x, g_pz may be null.
 hipError_t launch_loss_eq5(const nt_partition& p, const void* x, int c_s, const void* pz, int c_z,
                            int S, nt_dtype dtype, double* partial, double* loss, float* g_x,
                            float* g_pz, hipStream_t stream);

@@ -299,3 +299,35 @@ def test_backward_calls_validate(lib):
     g.W1 = None
     assert bb(P, s, zo, W, gso, None, gsi, Gr, 16, 16, 32, 1, bw, need.value, None) == \
         E.NT_ERR_NULL
+
+
+def test_non_leading_calls_validate(lib):
+    p = fake_partition()
+    P = ctypes.byref(p)
+    E = _native
+    w = _native.NtBlockWeights(*(FAKE + 0x4000000 + 0x10000 * k for k in range(5)))
+    W = ctypes.byref(w)
+    s, so, z, ws = (FAKE + 0x6000000 + 0x100000 * k for k in range(4))
+    need = ctypes.c_size_t()
+    assert lib.nt_block_nl_workspace_bytes(P, 3, 16, 16, 32, 1, ctypes.byref(need)) == 0
+    assert need.value >= 3 * 5 * 16 * 4 * 3   # a, b, m over T * S rows
+    one = ctypes.c_size_t()
+    assert lib.nt_block_workspace_bytes(P, 16, 16, 32, 1, ctypes.byref(one)) == 0
+    assert need.value > one.value
+    bl = lib.nt_pair_block_nl
+    assert bl(P, s, so, z, W, 0, 16, 16, 32, 1, ws, need.value, None) == E.NT_ERR_INVALID
+    assert bl(P, s, so, z, W, 65, 16, 16, 32, 1, ws, need.value, None) == E.NT_ERR_INVALID
+    assert bl(P, s, so, z, W, 5, 16, 128, 32, 1, ws, need.value, None) == E.NT_ERR_INVALID
+    assert bl(P, s, so, z, W, 3, 16, 16, 32, 1, ws, need.value - 1, None) == E.NT_ERR_WORKSPACE
+    rect = fake_partition()
+    rect.col_offsets = FAKE + 0x9000
+    assert bl(ctypes.byref(rect), s, so, z, W, 3, 16, 16, 32, 1, ws, need.value, None) == \
+        E.NT_ERR_INVALID
+    g = _native.NtBlockGrads(*(FAKE + 0x5000000 + 0x10000 * k for k in range(5)))
+    assert lib.nt_block_backward_nl_workspace_bytes(P, 3, 16, 16, 32, 1, ctypes.byref(need)) == 0
+    bb = lib.nt_pair_block_backward_nl
+    gso, gsi = FAKE + 0x7000000, FAKE + 0x7100000
+    assert bb(P, s, z, W, gso, None, gsi, ctypes.byref(g), 3, 16, 16, 32, 1, ws,
+              need.value - 1, None) == E.NT_ERR_WORKSPACE
+    assert bb(P, s, z, W, gso, None, gsi, ctypes.byref(g), 9, 16, 64, 32, 1, ws,
+              need.value, None) == E.NT_ERR_INVALID

@@ -63,9 +63,12 @@ def test_loss_eq5(nt, name, rows, cols, c_s, c_z, dtype):
     pz = pin.random_rows(cells, c_z, dtype, seed=2)
     p = nt.nt_make_partition(rows) if cols is None else nt.nt_make_partition_rect(rows, cols)
     for S in (1, 3):
-        loss, gx, gp = nt.nt_pair_loss_eq5(p, to_dev(x, torch), to_dev(pz, torch), S=S)
+        # S > 1: rows of S slices (the non-leading layout); slices differ
+        xs = pin.random_rows(sum(rows), S * c_s, dtype, seed=1) if S > 1 else x
+        ps = pin.random_rows(cells, S * c_z, dtype, seed=2) if S > 1 else pz
+        loss, gx, gp = nt.nt_pair_loss_eq5(p, to_dev(xs, torch), to_dev(ps, torch), S=S)
         torch.cuda.synchronize()
-        L, rgx, rgp = oracle.loss_eq5(rows, cols_, x.f64, pz.f64, S=S)
+        L, rgx, rgp = oracle.loss_eq5(rows, cols_, xs.f64, ps.f64, S=S)
         assert float(loss.cpu()[0]) == pytest.approx(L, rel=1e-5)
         assert scaled_max_err(gx.cpu().numpy(), rgx) <= 1e-6
         assert scaled_max_err(gp.cpu().numpy(), rgp) <= 1e-6
