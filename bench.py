@@ -218,6 +218,60 @@ def rectangular(x: pin.Inputs, args, torch, nt) -> dict:
             "unit": "pair cells/s per block"}
 
 
+def non_leading(x: pin.Inputs, args, torch, nt, S: int = 3) -> dict:
+    """The non-leading variant (Appendix A.1, S = 3): the workload's lengths
+    and widths with a static axis of S slices in every single row and pair
+    cell, the same four blocks; forward and the training step (forward,
+    Equation 5 with S, backward). Cells/s per block counts pair cells (each
+    holding S slices)."""
+    tdt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    lengths = torch.from_numpy(x.lengths.astype(np.int32)).pin_memory()
+    T, cells, _, nbytes = nt.nt_partition_sizes(x.lengths)
+    buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    p = nt.nt_make_partition(lengths, buffer=buf)
+    s0 = torch.randn(T, S * x.c_s, device="cuda", generator=g).to(tdt)
+    weights = [{k: dev(v, torch) for k, v in wk.items()} for wk in x.weights]
+    nb = len(weights)
+    s = [s0] + [torch.empty_like(s0) for _ in range(nb)]
+    z = [torch.empty((cells, S * x.c_z), dtype=tdt, device="cuda") for _ in range(nb)]
+    ws = torch.empty(max(nt.nt_block_nl_workspace_bytes(p, S, x.c_s, x.c_z, x.hidden, tdt), 1),
+                     dtype=torch.uint8, device="cuda")
+    bws = torch.empty(max(nt.nt_block_backward_nl_workspace_bytes(p, S, x.c_s, x.c_z, x.hidden,
+                                                                  tdt), 1),
+                      dtype=torch.uint8, device="cuda")
+    gbuf = [torch.empty((T, S * x.c_s), dtype=torch.float32, device="cuda") for _ in range(2)]
+    grads = [{k: torch.empty(v.shape, dtype=torch.float32, device="cuda") for k, v in w.items()}
+             for w in weights]
+
+    def forward():
+        q = nt.nt_make_partition(lengths, buffer=buf)
+        for k, w in enumerate(weights):
+            nt.nt_pair_block_nl(q, s[k], w, S, s_out=s[k + 1], z_out=z[k], workspace=ws)
+        return q
+
+    def train():
+        q = forward()
+        loss, gx, gp = nt.nt_pair_loss_eq5(q, s[-1], z[-1], S=S)
+        gcur = gx
+        for k in range(nb - 1, -1, -1):
+            out = gbuf[k % 2]
+            nt.nt_pair_block_backward_nl(q, s[k], z[k], weights[k], S, gcur,
+                                         gp if k == nb - 1 else None, g_s_in=out,
+                                         grads=grads[k], workspace=bws)
+            gcur = out
+
+    t_f = time_steps(forward, args.steps, args.warmup, torch)
+    t_t = time_steps(train, max(3, args.steps // 2), 2, torch)
+    log(f"non-leading S={S}: forward {t_f * 1e3:.3f} ms/step "
+        f"({cells * nb / t_f:.4g} cells/s per block), train step {t_t * 1e3:.3f} ms")
+    return {"S": S, "cells": cells, "blocks": nb, "forward_ms_per_step": t_f * 1e3,
+            "forward_value": cells * nb / t_f, "train_ms_per_step": t_t * 1e3,
+            "train_value": cells * nb / t_t, "unit": "pair cells/s per block (S slices per cell)",
+            "path": "broadcast, then the transition over cells * S rows (unfused)"}
+
+
 def granularity(x: pin.Inputs, r: PackedRunner, t_seg: float, args, torch, nt) -> dict:
     """Per-sample launches against the segmented launch on the same kernels:
     the granularity gain is per-sample time over segmented time."""
@@ -536,6 +590,7 @@ def main():
                             "impl": "PyTorch ops over B x N_max^2 (bf16 matmul, masked mean)"}
         result["granularity"] = granularity(x, r, t_step, args, torch, nt)
         result["rectangular"] = rectangular(x, args, torch, nt)
+        result["non_leading"] = non_leading(x, args, torch, nt)
         regimes = {}
         for other in pin.WORKLOADS[1:]:
             if other.name == w.name:

@@ -491,6 +491,22 @@ def nt_pair_block_backward(p: Partition, s_in, z_out, weights, g_s_out, g_z_out=
 
 
 # ------------------------------------------------------ non-leading layout
+def nt_block_nl_workspace_bytes(p: Partition, S: int, c_s: int, c_z: int, hidden: int,
+                                dtype) -> int:
+    n = ctypes.c_size_t()
+    _check(_native.lib().nt_block_nl_workspace_bytes(ctypes.byref(p.struct), S, c_s, c_z, hidden,
+                                                     _code(dtype), ctypes.byref(n)))
+    return n.value
+
+
+def nt_block_backward_nl_workspace_bytes(p: Partition, S: int, c_s: int, c_z: int, hidden: int,
+                                         dtype) -> int:
+    n = ctypes.c_size_t()
+    _check(_native.lib().nt_block_backward_nl_workspace_bytes(
+        ctypes.byref(p.struct), S, c_s, c_z, hidden, _code(dtype), ctypes.byref(n)))
+    return n.value
+
+
 def nt_pair_block_nl(p: Partition, s_in, weights, S: int, s_out=None, z_out=None,
                      workspace=None, stream=None):
     """The block on the non-leading layout: s_in [T, S*c_s]; returns
@@ -506,11 +522,9 @@ def nt_pair_block_nl(p: Partition, s_in, weights, S: int, s_out=None, z_out=None
         s_out = torch.empty_like(s_in)
     if z_out is None:
         z_out = torch.empty((p.cells, S * c_z), dtype=s_in.dtype, device=s_in.device)
-    n = ctypes.c_size_t()
-    _check(_native.lib().nt_block_nl_workspace_bytes(ctypes.byref(p.struct), S, c_s, c_z, hidden,
-                                                     _dtype_code(s_in), ctypes.byref(n)))
     if workspace is None:
-        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=s_in.device)
+        need = nt_block_nl_workspace_bytes(p, S, c_s, c_z, hidden, _dtype_code(s_in))
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=s_in.device)
     wst = NtBlockWeights(*[_ptr(w) for w in weights])
     _check(_native.lib().nt_pair_block_nl(ctypes.byref(p.struct), _ptr(s_in), _ptr(s_out),
                                           _ptr(z_out), ctypes.byref(wst), S, c_s, c_z, hidden,
@@ -533,11 +547,9 @@ def nt_pair_block_backward_nl(p: Partition, s_in, z_out, weights, S: int, g_s_ou
     if grads is None:
         grads = {k: torch.empty(w.shape, dtype=torch.float32, device=dev)
                  for k, w in zip(_WEIGHT_NAMES, weights)}
-    n = ctypes.c_size_t()
-    _check(_native.lib().nt_block_backward_nl_workspace_bytes(
-        ctypes.byref(p.struct), S, c_s, c_z, hidden, _dtype_code(s_in), ctypes.byref(n)))
     if workspace is None:
-        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+        need = nt_block_backward_nl_workspace_bytes(p, S, c_s, c_z, hidden, _dtype_code(s_in))
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     wst = NtBlockWeights(*[_ptr(w) for w in weights])
     gst = _native.NtBlockGrads(*[_ptr(grads[k]) for k in _WEIGHT_NAMES])
     _check(_native.lib().nt_pair_block_backward_nl(
