@@ -280,3 +280,59 @@ def test_chain_backward_under_eq5(nt):
     for k in range(2):
         for name in rgrads[k]:
             assert scaled_max_err(grads[k][name].cpu().numpy(), rgrads[k][name]) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("lengths", [[0, 0, 0], [0]])
+def test_block_backward_empty_batch(nt, lengths):
+    """No singles and no cells: every gradient is zero, nothing is read."""
+    announce(f"block backward empty {lengths}")
+    c_s, c_z, hidden = 64, 128, 512
+    x = pin.make_inputs([1], c_s, c_z, hidden, "bf16", seed=3)   # weights only
+    p = nt.nt_make_partition(lengths)
+    wd = weights_to_dev(x.weights[0], torch)
+    s = torch.empty((0, c_s), dtype=torch.bfloat16, device="cuda")
+    z = torch.empty((0, c_z), dtype=torch.bfloat16, device="cuda")
+    gs = torch.empty((0, c_s), dtype=torch.float32, device="cuda")
+    g, grads = nt.nt_pair_block_backward(p, s, z, wd, gs)
+    torch.cuda.synchronize()
+    assert g.numel() == 0
+    for k, v in grads.items():
+        assert torch.count_nonzero(v).item() == 0, k
+
+
+def test_block_backward_many_samples(nt):
+    """More samples than the one-launch partition takes (B = 300), with
+    empty samples among them, fp32 against the oracle."""
+    rng = np.random.default_rng(17)
+    lengths = rng.integers(0, 6, 300).tolist()
+    announce(f"block backward B={len(lengths)} T={sum(lengths)}")
+    x = pin.make_inputs(lengths, 16, 8, 16, "f32", seed=18)
+    w = x.weights[0]
+    cells = int(np.square(lengths).sum())
+    gs = rng.standard_normal((sum(lengths), 16)).astype(np.float32)
+    gz = rng.standard_normal((cells, 8)).astype(np.float32)
+    p = nt.nt_make_partition(lengths)
+    wd = weights_to_dev(w, torch)
+    sd = to_dev(x.s, torch)
+    _, z_out = nt.nt_pair_block(p, sd, wd)
+    g, grads = nt.nt_pair_block_backward(p, sd, z_out, wd, _f32(gs), _f32(gz))
+    torch.cuda.synchronize()
+    ref = oracle.block_backward(lengths, x.s.f64, {k: v.f64 for k, v in w.items()},
+                                gs.astype(np.float64), gz.astype(np.float64))
+    assert scaled_max_err(g.cpu().numpy(), ref["s"]) <= TOL["f32"]
+    for k in ("Wa", "Wb", "W1", "W2", "Wo"):
+        assert scaled_max_err(grads[k].cpu().numpy(), ref[k]) <= TOL["f32"], k
+
+
+def test_transition_backward_no_cells(nt):
+    announce("transition backward, no cells")
+    p = nt.nt_make_partition([0, 0])
+    z = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    G = torch.empty((0, 128), dtype=torch.float32, device="cuda")
+    W1 = torch.ones((512, 128), dtype=torch.bfloat16, device="cuda")
+    W2 = torch.ones((128, 512), dtype=torch.bfloat16, device="cuda")
+    dW1 = torch.full((512, 128), 7.0, device="cuda")
+    dW2 = torch.full((128, 512), 7.0, device="cuda")
+    nt.nt_pair_transition_backward(p, z, G, W1, W2, dW1=dW1, dW2=dW2)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dW1).item() == 0 and torch.count_nonzero(dW2).item() == 0

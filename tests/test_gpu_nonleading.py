@@ -98,3 +98,29 @@ def test_nl_with_one_slice_is_the_leading_block(nt):
     s_b, z_b = nt.nt_pair_block_nl(p, sd, w, 1)
     torch.cuda.synchronize()
     assert torch.equal(s_a, s_b) and torch.equal(z_a, z_b)
+
+
+def test_block_nl_many_samples(nt):
+    """B = 300 (two-launch partition), S = 3, fp32: forward and backward."""
+    rng = np.random.default_rng(21)
+    lengths = rng.integers(0, 6, 300).tolist()
+    S, c_s, c_z, hidden = 3, 8, 8, 16
+    announce(f"non-leading B={len(lengths)} S={S}")
+    s, w = _inputs(lengths, S, c_s, c_z, hidden, "f32", False, 22)
+    cells = int(np.square(lengths).sum())
+    gs = rng.standard_normal((sum(lengths), S * c_s)).astype(np.float32)
+    p = nt.nt_make_partition(lengths)
+    wd = weights_to_dev(w, torch)
+    sd = to_dev(s, torch)
+    so, zo = nt.nt_pair_block_nl(p, sd, wd, S)
+    g, grads = nt.nt_pair_block_backward_nl(p, sd, zo, wd, S, _f32(gs))
+    torch.cuda.synchronize()
+    W64 = {k: v.f64 for k, v in w.items()}
+    rs, rz = oracle.block_nl(lengths, s.f64, W64, S)
+    assert scaled_max_err(f64(zo, torch), rz) <= TOL["f32"]
+    assert scaled_max_err(f64(so, torch), rs) <= TOL["f32"]
+    ref = oracle.block_backward_nl(lengths, s.f64, W64, S, gs.astype(np.float64))
+    assert scaled_max_err(g.cpu().numpy(), ref["s"]) <= TOL["f32"]
+    for k in ("Wa", "Wb", "W1", "W2", "Wo"):
+        assert scaled_max_err(grads[k].cpu().numpy(), ref[k]) <= TOL["f32"], k
+    assert cells > 0
