@@ -185,43 +185,51 @@ __global__ __launch_bounds__(kThreads) void k_transpose(const T* __restrict__ sr
 
 // ---------------------------------------------------------------------------
 // Weight-gradient contraction over rows: C[m, n] = sum_k A[k, m] B[k, n],
-// A [K, M] and B [K, N] row-major, fp32 products and accumulation. Each
-// workgroup owns a 32 x 32 tile of C and one of `gridDim.z` slices of K and
-// writes its partial tile; k_sum_splits adds the slices in order.
+// A [K, M] and B [K, N] row-major (bf16 inputs widened), fp32 products and
+// accumulation on v_mfma_f32_32x32x2_f32, whose operands hold one k per
+// lane: lane (l % 32, l / 32) takes A[k + l / 32][m0 + l % 32], so the loads
+// of a K-major operand stay coalesced. Each workgroup owns a 32 x 32 tile of
+// C and one of `gridDim.z` slices of K (a multiple of 32 rows); its four
+// waves take interleaved pairs of rows and add their tiles through LDS; the
+// partial tile is written and k_sum_splits adds the slices in order.
 template <typename TA, typename TB>
 __global__ __launch_bounds__(kThreads) void k_gemm_tn(const TA* __restrict__ A,
                                                       const TB* __restrict__ Bm,
                                                       float* __restrict__ part, int64_t K, int M,
                                                       int N, int64_t kchunk) {
-  __shared__ float As[32][33], Bs[32][33];
-  const int tid = threadIdx.x;
+  __shared__ float red[kThreads / 64][32 * 33];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
   const int m0 = blockIdx.x * 32, n0 = blockIdx.y * 32;
   const int64_t kb = (int64_t)blockIdx.z * kchunk;
   const int64_t ke = kb + kchunk < K ? kb + kchunk : K;
-  const int tm = tid & 31, tn = (tid >> 5) * 4;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t k0 = kb; k0 < ke; k0 += 32) {
+  const int m = m0 + l32, n = n0 + l32;
+  const bool mok = m < M, nok = n < N;
+  f32x16 acc = f32x16{};
+  // wave w takes the row pairs kb + 2 w + 8 u (u = 0, 1, ...), lane half h row + h
+  for (int64_t k0 = kb + 2 * wave; k0 < ke; k0 += 32) {
+    float av[4], bv[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = tid + kThreads * q, kk = e >> 5, mm = e & 31;
-      const int64_t k = k0 + kk;
-      As[kk][mm] = (k < ke && m0 + mm < M) ? to_f32(A[k * M + m0 + mm]) : 0.f;
-      Bs[kk][mm] = (k < ke && n0 + mm < N) ? to_f32(Bm[k * N + n0 + mm]) : 0.f;
+    for (int u = 0; u < 4; ++u) {
+      const int64_t k = k0 + 8 * u + h;
+      const bool kin = k < ke;
+      av[u] = (kin && mok) ? to_f32(A[k * M + m]) : 0.f;
+      bv[u] = (kin && nok) ? to_f32(Bm[k * N + n]) : 0.f;
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < 32; ++kk) {
-      const float a = As[kk][tm];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += a * Bs[kk][tn + j];
-    }
-    __syncthreads();
+    for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u], bv[u], acc, 0, 0, 0);
   }
-  if (m0 + tm < M) {
+  // element r of the tile: row 8 (r / 4) + 4 h + r % 4, column l32
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (n0 + tn + j < N)
-        part[((int64_t)blockIdx.z * M + m0 + tm) * N + n0 + tn + j] = acc[j];
+  for (int r = 0; r < 16; ++r) red[wave][(8 * (r / 4) + 4 * h + r % 4) * 33 + l32] = acc[r];
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int idx = tid + kThreads * q, row = idx >> 5, col = idx & 31;
+    const float v = red[0][row * 33 + col] + red[1][row * 33 + col] + red[2][row * 33 + col] +
+                    red[3][row * 33 + col];
+    if (m0 + row < M && n0 + col < N)
+      part[((int64_t)blockIdx.z * M + m0 + row) * N + n0 + col] = v;
   }
 }
 
