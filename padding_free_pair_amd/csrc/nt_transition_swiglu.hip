@@ -24,8 +24,8 @@
 namespace nt {
 namespace {
 
-constexpr int kSgWaves = 4;
-constexpr int kSgCellsPerWave = 64;
+constexpr int kSgWaves = 8;            // two waves per SIMD
+constexpr int kSgCellsPerWave = 32;
 constexpr int kSgBlocks = kSgCellsPerWave / 16;
 constexpr int kSgTileCells = kSgWaves * kSgCellsPerWave;
 constexpr int kSgChunk = 32;
@@ -45,7 +45,7 @@ __device__ __forceinline__ int sg_feat_row(int fb, int q) {
 }
 
 template <int CZ>
-__global__ __launch_bounds__(kSgWaves * 64, 1) void k_transition_swiglu(
+__global__ __launch_bounds__(kSgWaves * 64, 2) void k_transition_swiglu(
     const bf16* __restrict__ z_in, const float* __restrict__ gamma,
     const float* __restrict__ beta, const bf16* __restrict__ Wg, const bf16* __restrict__ Wu,
     const bf16* __restrict__ Wd, bf16* z_out, int64_t cells, int hidden, float eps) {
@@ -55,8 +55,7 @@ __global__ __launch_bounds__(kSgWaves * 64, 1) void k_transition_swiglu(
   constexpr int NFRAG = 2 * GF + FB;   // fragments per chunk, 1 KiB each
   constexpr int PIECES = NFRAG * 64;
   constexpr int THREADS = kSgWaves * 64;
-  constexpr int PER_THREAD = PIECES / THREADS;
-  static_assert(PIECES % THREADS == 0, "chunk staging must divide evenly");
+  constexpr int PER_THREAD = (PIECES + THREADS - 1) / THREADS;  // the last may be partial
 
   __shared__ bf16x8 lds[2][PIECES];
 
@@ -138,9 +137,11 @@ __global__ __launch_bounds__(kSgWaves * 64, 1) void k_transition_swiglu(
   bf16x8 stage[PER_THREAD];
 #pragma unroll
   for (int k = 0; k < PER_THREAD; ++k)
-    stage[k] = *reinterpret_cast<const bf16x8*>(stage_src(0, tid + k * THREADS));
+    if (tid + k * THREADS < PIECES)
+      stage[k] = *reinterpret_cast<const bf16x8*>(stage_src(0, tid + k * THREADS));
 #pragma unroll
-  for (int k = 0; k < PER_THREAD; ++k) lds[0][tid + k * THREADS] = stage[k];
+  for (int k = 0; k < PER_THREAD; ++k)
+    if (tid + k * THREADS < PIECES) lds[0][tid + k * THREADS] = stage[k];
   __syncthreads();
 
   f32x4 y[kSgBlocks][FB];
@@ -155,7 +156,8 @@ __global__ __launch_bounds__(kSgWaves * 64, 1) void k_transition_swiglu(
     if (more) {
 #pragma unroll
       for (int k = 0; k < PER_THREAD; ++k)
-        stage[k] = *reinterpret_cast<const bf16x8*>(stage_src(ch + 1, tid + k * THREADS));
+        if (tid + k * THREADS < PIECES)
+          stage[k] = *reinterpret_cast<const bf16x8*>(stage_src(ch + 1, tid + k * THREADS));
     }
     // gate and value products, one 16-cell block at a time
     bf16x8 af[kSgBlocks];
@@ -186,7 +188,8 @@ __global__ __launch_bounds__(kSgWaves * 64, 1) void k_transition_swiglu(
     }
     if (more) {
 #pragma unroll
-      for (int k = 0; k < PER_THREAD; ++k) lds[cur ^ 1][tid + k * THREADS] = stage[k];
+      for (int k = 0; k < PER_THREAD; ++k)
+        if (tid + k * THREADS < PIECES) lds[cur ^ 1][tid + k * THREADS] = stage[k];
     }
     __syncthreads();
   }
