@@ -313,9 +313,11 @@ def time_kernel(fn, reps: int, torch) -> float:
 
 def transition_kernel_label(c_z: int, hidden: int, dtype: str) -> str:
     """The kernel the library launches for the fused broadcast + transition."""
-    if dtype == "bf16" and c_z == 128 and hidden == 512 and \
-            os.environ.get("NT_TRANSITION_KERNEL") != "p32":
+    choice = os.environ.get("NT_TRANSITION_KERNEL")
+    if dtype == "bf16" and c_z == 128 and hidden == 512 and choice == "pf":
         return "k_transition_pf (fused broadcast, next tile's b rows prefetched)"
+    if dtype == "bf16" and c_z == 128 and hidden == 512 and choice != "p32":
+        return "k_transition_ws (fused broadcast, weights resident in registers)"
     if dtype == "bf16" and (c_z, hidden) in ((128, 512), (64, 128)):
         return "k_transition_p32 (fused broadcast prologue)"
     return "fused broadcast + transition"

@@ -35,6 +35,14 @@ COMMON = [
 ]
 
 
+# Per-file flags. The weight-stationary transition keeps both weights in the
+# accumulation registers (AGPRs) as product operands, so its accumulators go
+# to ordinary VGPRs.
+FILE_FLAGS = {
+    "nt_transition_ws.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith(".hip") or f.endswith(".cpp"))
@@ -43,7 +51,8 @@ def sources():
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [_hipcc(), *COMMON, *lang, "-c", src, "-o", obj]
+    extra = FILE_FLAGS.get(os.path.basename(src), [])
+    cmd = [_hipcc(), *COMMON, *extra, *lang, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)

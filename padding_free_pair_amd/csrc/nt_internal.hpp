@@ -113,6 +113,11 @@ hipError_t launch_transition_swiglu(const nt_partition& p, const void* z_in, voi
 hipError_t launch_transition_prefetch(const nt_partition& p, const void* a, const void* b,
                                       void* z_out, const void* W1, const void* W2, int cus,
                                       hipStream_t stream);
+// Fused broadcast + transition for c_z = 128, hidden = 512 with both weights
+// held in registers (one hidden quarter per wave) over 32-cell blocks; needs
+// the tile_sample index and T < 2^22.
+hipError_t launch_transition_ws(const nt_partition& p, const void* a, const void* b, void* z_out,
+                                const void* W1, const void* W2, int cus, hipStream_t stream);
 hipError_t launch_transition(const nt_partition& p, const void* z_in, const void* a, const void* b,
                              void* z_out, const void* W1, const void* W2, int c_z, int hidden,
                              nt_dtype dtype, hipStream_t stream);

@@ -1,0 +1,434 @@
+// Weight-stationary fused broadcast + residual pair transition (DanLing
+// NestedTensor, Equation 1 second line with a ReLU MLP update over the packed
+// cells of Section 3.3; z = a[row] + b[col] follows Equation 3's addressing).
+//
+// Arithmetic: the 32x32x16 bf16 products H^T = W1 . z^T and
+// Y^T += W2 . relu(H)^T with fp32 accumulators, one bf16 rounding of z as the
+// first product's operand and one of the output; the residual is the fp32
+// z = a + b.
+//
+// Organisation (c_z = 128, hidden = 512, four waves per workgroup, one
+// workgroup per CU):
+//  * Wave w keeps hidden units 128 w .. 128 w + 127 of both weights in
+//    registers for the whole launch: their W1 rows as the first product's
+//    A fragments (128 VGPRs) and the matching W2 columns as the second's
+//    (128 VGPRs). Nothing is streamed per cell.
+//  * Cells move in blocks of 32 (one MFMA column block). For each block every
+//    wave computes its hidden quarter and a partial Y over all 128 outputs;
+//    the four partials meet in LDS, where the wave that owns out block j
+//    (the 32 outputs j + w of wave w's rotation) adds the other three to its
+//    own, which was seeded with the fp32 residual, and stores the result.
+//  * A workgroup walks blocks blockIdx.x, + gridDim.x, ... One phase per
+//    block, closed by one barrier. During the MFMAs of block k a wave also
+//    reduces and stores block k - 1 and stages block k + 1: its threads
+//    gather a[row] and b[col] (eight threads per cell, 64 contiguous bytes
+//    each), form z in fp32 and write both the bf16 operand fragments and the
+//    fp32 residual in the owners' accumulator layout.
+//  * LDS (double-buffered so that one barrier per block suffices): operand
+//    fragments 2 x 8 KiB, residuals 2 x 16 KiB, partials 2 x 48 KiB.
+#include "nt_device.hpp"
+#include "nt_internal.hpp"
+
+namespace nt {
+namespace {
+
+constexpr int kWsWaves = 4;
+constexpr int kWsCells = 32;     // cells per block
+constexpr int kWsSamples = 256;  // partitions up to this many samples decode from LDS
+constexpr int kWsBufFlags = 0x00020000;  // raw buffer, 32-bit data format
+
+__device__ __forceinline__ f32x16 ws_mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Result row rho of a 32x32 product -> row of the 32-row block it computes
+// (bits 2 and 3 swapped). With the weight rows loaded in this order, lane
+// group h of an accumulator holds rows 16 s + 8 h + (0..7) in elements
+// 8 s .. 8 s + 7: the operand layout of the next product's k-step s, and
+// eight consecutive outputs of one cell. The map is its own inverse.
+__device__ __forceinline__ int ws_perm(int rho) {
+  return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
+}
+
+__device__ __forceinline__ float ws_relu(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
+// This wave's LDS operations have completed, then s_barrier. Global stores
+// and loads in flight are not waited for (nothing in LDS depends on them);
+// the asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void ws_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// Row and column single of packed cell `cell` (Equation 3 inverted),
+// searching upwards from sample i0, which is at most the cell's sample.
+template <typename OFF, typename IDX, typename CIDX>
+__device__ __forceinline__ void ws_decode(const OFF* po, const IDX* eta, const CIDX* mu,
+                                          const int32_t* m, int i0, int64_t cell, int& row,
+                                          int& col) {
+  int i = i0;
+  while (po[i + 1] <= cell) ++i;
+  const int64_t len = m[i], local = cell - (int64_t)po[i];
+  int64_t r, c;
+  if (len <= 65535 && local <= 0xffffffffLL) {
+    const uint32_t q = (uint32_t)local / (uint32_t)len;
+    r = q;
+    c = (uint32_t)local - q * (uint32_t)len;
+  } else {
+    r = local / len;
+    c = local - r * len;
+  }
+  row = (int)((int64_t)eta[i] + r);
+  col = (int)((int64_t)mu[i] + c);
+}
+
+// LDS_PART: a square partition of at most kWsSamples samples with N_i <=
+// 65535, decoded from an LDS copy with 32-bit arithmetic; otherwise the
+// partition is read from global memory.
+template <bool LDS_PART>
+__global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
+    const float* __restrict__ a, const float* __restrict__ b,
+    const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
+    const int64_t* __restrict__ col_offsets, const int32_t* __restrict__ col_lengths,
+    const int32_t* __restrict__ tile_sample, int B,
+    const bf16* __restrict__ W1, const bf16* __restrict__ W2, bf16* __restrict__ z_out,
+    int64_t cells, int64_t nblocks, int64_t T_rows, int64_t T_cols) {
+  constexpr int CZ = 128, HID = 512;
+  constexpr int KT = CZ / 16;  // first-product k-steps
+  constexpr int ROW = CZ * 4;  // bytes of one fp32 single row
+  // LDS: operand fragments [buf][k-step][64 lanes] x 16 B (lane index XOR 2 t);
+  // residuals [buf][out block][q][64 lanes] x 16 B (lane index XOR 4 j + 2 (q / 2));
+  // partials [buf][writer wave][rotation slot][q][64 lanes] x 16 B.
+  __shared__ __attribute__((aligned(16))) unsigned char zs[2][KT * 1024];
+  __shared__ __attribute__((aligned(16))) unsigned char rs[2][4 * 4096];
+  __shared__ __attribute__((aligned(16))) unsigned char ps[2][kWsWaves][3][4096];
+  __shared__ int64_t po_s[kWsSamples + 1];
+  __shared__ int32_t eta_s[kWsSamples];
+  __shared__ int32_t n_s[kWsSamples];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+
+  if (LDS_PART) {
+    for (int i = tid; i <= B; i += kWsWaves * 64) {
+      po_s[i] = pair_offsets[i];
+      if (i < B) {
+        eta_s[i] = (int32_t)single_offsets[i];
+        n_s[i] = col_lengths[i];
+      }
+    }
+  }
+
+  // ---- stationary weights. Out block j of this wave is (wave + j) mod 4.
+  bf16x8 w1f[4][KT];    // [hidden block][k-step]
+  bf16x8 w2f[4][4][2];  // [rotation j][hidden block][k-step within the block]
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+      w1f[hb][t] = load16(W1 + (int64_t)(128 * wave + 32 * hb + ws_perm(n)) * CZ + 16 * t + 8 * h).v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ob = (wave + j) & 3;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        w2f[j][hb][s] = load16(W2 + (int64_t)(32 * ob + ws_perm(n)) * HID + 128 * wave + 32 * hb +
+                               16 * s + 8 * h).v;
+  }
+  // The products read the weights straight from accumulation registers
+  // (AGPRs), which leaves the VGPRs to accumulators, operands and staging.
+  // An empty asm with a tied AGPR operand places each fragment there once.
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+    for (int t = 0; t < KT; ++t) asm volatile("" : "=a"(w1f[hb][t]) : "0"(w1f[hb][t]));
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) asm volatile("" : "=a"(w2f[j][hb][s]) : "0"(w2f[j][hb][s]));
+  __syncthreads();
+
+  // ---- staging: thread (cell sc of the block, features 16 k8 .. 16 k8 + 15)
+  const int sc = tid >> 3, k8 = tid & 7;
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a, 0, (int)(T_rows * ROW), kWsBufFlags);
+  const __amdgpu_buffer_rsrc_t b_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)b, 0, (int)(T_cols * ROW), kWsBufFlags);
+  f32x4 va[4], vb[4];
+  // Decode of cell `cell` of the next block, in steps spread over a phase so
+  // that every memory read has several products' time to land. Step 1: the
+  // first sample of the cell's 256-cell tile (a vector load, so that it does
+  // not share a counter with the LDS traffic).
+  const __amdgpu_buffer_rsrc_t ts_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)tile_sample, 0, (int)(4 * ((cells + kSampleIndexSpan - 1) / kSampleIndexSpan)),
+      kWsBufFlags);
+  // It is issued a phase ahead, for the block after next.
+  int64_t d_cell = 0, d_p1 = 0, d_p2 = 0, d_base = 0;
+  int d_i0 = 0, d_i = 0, d_len = 1, d_eta = 0, d_mu = 0, d_row = 0, d_col = 0;
+  auto dec1 = [&](int64_t blk) {
+    d_i0 = __builtin_amdgcn_raw_buffer_load_b32(
+        ts_rsrc, (int)((blk * kWsCells / kSampleIndexSpan) * 4), 0, 0);
+  };
+  // step 2: offsets of the next two samples
+  auto dec2 = [&](int64_t blk) {
+    const int64_t c = blk * kWsCells + sc;
+    d_cell = c < cells ? c : cells - 1;  // a cell past the end repeats the last one
+    d_i = d_i0;
+    const int i2 = d_i + 2 < B ? d_i + 2 : B;
+    if constexpr (LDS_PART) {
+      d_p1 = po_s[d_i + 1];
+      d_p2 = po_s[i2];
+    } else {
+      d_p1 = pair_offsets[d_i + 1];
+      d_p2 = pair_offsets[i2];
+    }
+  };
+  // step 3: the sample (at most two steps here, a walk beyond that), then its
+  // length, single offsets and first cell
+  auto dec3 = [&]() {
+    d_i += (d_p1 <= d_cell) + (d_p2 <= d_cell);
+    if (d_p2 <= d_cell) {
+      if constexpr (LDS_PART) {
+        while (po_s[d_i + 1] <= d_cell) ++d_i;
+      } else {
+        while (pair_offsets[d_i + 1] <= d_cell) ++d_i;
+      }
+    }
+    if constexpr (LDS_PART) {
+      d_len = n_s[d_i];
+      d_eta = eta_s[d_i];
+      d_mu = d_eta;
+      d_base = po_s[d_i];
+    } else {
+      d_len = col_lengths[d_i];
+      d_eta = (int)single_offsets[d_i];
+      d_mu = (int)col_offsets[d_i];
+      d_base = pair_offsets[d_i];
+    }
+  };
+  // step 4: row and column (Equation 3 inverted)
+  auto dec4 = [&]() {
+    const int64_t local = d_cell - d_base;
+    int64_t r, c;
+    if (LDS_PART || (d_len <= 65535 && local <= 0xffffffffLL)) {
+      const uint32_t q = (uint32_t)local / (uint32_t)d_len;
+      r = q;
+      c = (uint32_t)local - q * (uint32_t)d_len;
+    } else {
+      r = local / d_len;
+      c = local - r * d_len;
+    }
+    d_row = (int)(d_eta + r);
+    d_col = (int)(d_mu + c);
+  };
+  // step 5: the gathers (eight threads per cell, 64 contiguous bytes each)
+  auto gather_a = [&]() {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      va[q] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, d_row * ROW + 64 * k8 + 16 * q, 0, 0);
+  };
+  auto gather_b = [&]() {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      vb[q] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, d_col * ROW + 64 * k8 + 16 * q, 0, 0);
+  };
+  // z = a + b in fp32: bf16 operand fragment k8 (lanes sc and sc + 32) and
+  // the fp32 residual of out block k8 / 2, rows 16 (k8 % 2) .. + 15.
+  // half hh of the staging store: features 16 k8 + 8 hh .. + 7
+  auto stage_half = [&](int buf, int hh) {
+    float z[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = va[2 * hh + e / 4][e % 4] + vb[2 * hh + e / 4][e % 4];
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16)z[e];
+    *reinterpret_cast<bf16x8*>(zs[buf] + 1024 * k8 + 16 * ((sc + 32 * hh) ^ (2 * k8))) = o;
+    const int ob = k8 >> 1, s = k8 & 1;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = z[4 * qq + e];
+      *reinterpret_cast<f32x4*>(rs[buf] + 4096 * ob + 1024 * (2 * s + qq) +
+                                16 * ((sc + 32 * hh) ^ (2 * k8))) = v;
+    }
+  };
+
+  // ---- per-block state
+  f32x16 y[4];     // partial outputs, rotation order; y[0] is this wave's own block
+  f32x16 own;      // own block of the previous block (residual + this wave's partial)
+  f32x16 seed;     // fp32 residual of this block's own outputs
+  f32x16 hacc[4];  // first-product accumulators, one per hidden block
+  bf16x8 hf[2][2];
+  bf16x8 zf[KT];
+  f32x4 pr[2][3];
+  int64_t prev = -1;
+
+  // relu of k-step s of a first-product accumulator, packed to bf16. The
+  // rounding comes first: bf16 preserves signs, so relu(bf16(x)) is
+  // bf16(relu(x)) bit for bit, and the max is one packed integer op.
+  auto relu_pack = [&](const f32x16& acc, int s) -> bf16x8 {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16)acc[8 * s + e];
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = __builtin_elementwise_max(__builtin_bit_cast(s16x8, o), (s16x8){});
+    return __builtin_bit_cast(bf16x8, v);
+  };
+  // part q (elements 4 q .. 4 q + 3) of the sum of the four partials of out
+  // block `wave`: own first, then waves wave + 1, + 2, + 3 in turn
+  auto read_part = [&](int pbuf, int q, int j) {
+    pr[q & 1][j - 1] =
+        *reinterpret_cast<const f32x4*>(&ps[pbuf][(wave + j) & 3][3 - j][1024 * q + 16 * lane]);
+  };
+  auto add_part = [&](int q, int j) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) own[4 * q + e] += pr[q & 1][j - 1][e];
+  };
+  auto store_out = [&](int64_t blk, int s) {
+    const int64_t cell = blk * kWsCells + n;
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16)own[8 * s + e];
+    if (blk >= 0 && cell < cells)
+      *reinterpret_cast<bf16x8*>(z_out + cell * CZ + 32 * wave + 16 * s + 8 * h) = o;
+  };
+  auto write_part = [&](int pbuf, int j, int q) {
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = y[j][4 * q + e];
+    *reinterpret_cast<f32x4*>(&ps[pbuf][wave][j - 1][1024 * q + 16 * lane]) = v;
+  };
+
+  int64_t blk = blockIdx.x;
+  dec1(blk);
+  dec2(blk);
+  dec3();
+  dec4();
+  gather_a();
+  gather_b();
+  stage_half(0, 0);
+  stage_half(0, 1);
+  dec1(blk + gridDim.x < nblocks ? blk + gridDim.x : nblocks - 1);
+  ws_barrier();
+
+  // One phase per block: 64 product slots. Slots 0..31 run the first
+  // product (k-step i / 4 of hidden block i % 4, four independent chains),
+  // slots 32..63 the second (hidden block (i - 32) / 8; out blocks in the
+  // order 1, 2, 3, 0 so that the partials the other waves need finish
+  // first). Each slot carries a small share of the other work:
+  //   0        this block's residual (own out block)
+  //   5..16    next block: offsets, sample, row and column, gathers
+  //   20       the block after next: its tile's first sample
+  //   2..26    previous block: the other waves' partials, read four slots
+  //            before they are added
+  //   27, 28   previous block: rounding and store
+  //   30..50   relu of hidden blocks 0..3, two slots each
+  //   44..47   next block: z = a + b into the operand and residual buffers
+  //   62, 63   this block: partials of out block 1
+  int buf = 0;
+  for (int it = 0;; ++it) {
+    buf = it & 1;
+    const int64_t next = blk + gridDim.x;
+    const bool has_next = next < nblocks;
+    // after the last block the staging repeats it into the idle buffer, and
+    // the first phase sums stale partials without storing them, so that the
+    // phase body has no branches
+    const int64_t stg = has_next ? next : blk;
+    const int64_t stg2 = stg + gridDim.x < nblocks ? stg + gridDim.x : nblocks - 1;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+      zf[t] = *reinterpret_cast<const bf16x8*>(zs[buf] + 1024 * t + 16 * (lane ^ (2 * t)));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      if (i < 32) {
+        const int t = i >> 2, hb = i & 3;
+        hacc[hb] = ws_mfma(w1f[hb][t], zf[t], t == 0 ? f32x16{} : hacc[hb]);
+      } else {
+        const int hb = (i - 32) >> 3, k = (i - 32) & 7, s = k >> 2, j = (k + 1) & 3;
+        const f32x16 c = hb > 0 || s > 0 ? y[j] : (j == 0 ? seed : f32x16{});
+        y[j] = ws_mfma(w2f[j][hb][s], hf[hb & 1][s], c);
+      }
+      if (i == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(
+              rs[buf] + 4096 * wave + 1024 * q + 16 * (lane ^ (4 * wave + 2 * (q >> 1))));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) seed[4 * q + e] = v[e];
+        }
+      }
+      if (i == 5) dec2(stg);
+      if (i == 9) dec3();
+      if (i == 13) dec4();
+      if (i == 15) gather_a();
+      if (i == 16) gather_b();
+      if (i == 20) dec1(stg2);
+      if (i == 44 || i == 46) stage_half(buf ^ 1, (i - 44) / 2);
+      if (i >= 2 && i <= 22 && (i - 2) % 6 < 3) read_part(buf ^ 1, (i - 2) / 6, (i - 2) % 6 + 1);
+      if (i >= 6 && i <= 26 && (i - 6) % 6 < 3) add_part((i - 6) / 6, (i - 6) % 6 + 1);
+      if (i == 27 || i == 28) store_out(prev, i - 27);
+      if (i == 30 || i == 31) hf[0][i - 30] = relu_pack(hacc[0], i - 30);
+      if (i == 33 || i == 34) hf[1][i - 33] = relu_pack(hacc[1], i - 33);
+      if (i == 41 || i == 42) hf[0][i - 41] = relu_pack(hacc[2], i - 41);
+      if (i == 49 || i == 50) hf[1][i - 49] = relu_pack(hacc[3], i - 49);
+      if (i == 62 || i == 63) {
+        write_part(buf, 1, 2 * (i - 62));
+        write_part(buf, 1, 2 * (i - 62) + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 2; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) write_part(buf, j, q);
+    own = y[0];
+    ws_barrier();
+    prev = blk;
+    if (!has_next) break;
+    blk = next;
+  }
+  // the last block's sum
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int j = 1; j < 4; ++j) {
+      read_part(buf, q, j);
+      add_part(q, j);
+    }
+  store_out(prev, 0);
+  store_out(prev, 1);
+}
+
+}  // namespace
+
+hipError_t launch_transition_ws(const nt_partition& p, const void* a, const void* b, void* z_out,
+                                const void* W1, const void* W2, int cus, hipStream_t stream) {
+  const int64_t nblocks = (p.cells + kWsCells - 1) / kWsCells;
+  const int64_t grid = nblocks < cus ? nblocks : cus;
+  // the LDS copy of the partition holds square partitions (mu = eta, M = N)
+  const bool lds_part =
+      p.B <= kWsSamples && p.col_offsets == p.single_offsets && p.n_max <= 65535;
+  auto kern = lds_part ? k_transition_ws<true> : k_transition_ws<false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kWsWaves * 64), 0, stream,
+                     static_cast<const float*>(a), static_cast<const float*>(b), p.pair_offsets,
+                     p.single_offsets, p.col_offsets, p.col_lengths, p.tile_sample, p.B,
+                     static_cast<const bf16*>(W1), static_cast<const bf16*>(W2),
+                     static_cast<bf16*>(z_out), p.cells, nblocks, p.T, p.T_cols);
+  return hipGetLastError();
+}
+
+}  // namespace nt

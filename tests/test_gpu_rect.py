@@ -98,19 +98,19 @@ def test_rect_reduce_exact(nt, dtype, c_z):
                                   ref[keep].astype(np.float32).view(np.uint32))
 
 
-@pytest.mark.parametrize("kernel", ["default", "p32"])
+@pytest.mark.parametrize("kernel", ["default", "pf", "p32"])
 @pytest.mark.parametrize("rows,cols,c_s,c_z,hidden,dtype", [
-    ([7, 12, 5, 16], [3, 20, 5, 1], 32, 128, 512, "bf16"),  # prefetching fused kernel
+    ([7, 12, 5, 16], [3, 20, 5, 1], 32, 128, 512, "bf16"),  # weight-stationary fused kernel
     ([9, 40, 2], [33, 6, 64], 32, 64, 128, "bf16"),          # persistent fused kernel
     ([7, 12, 5], [3, 20, 6], 16, 48, 40, "bf16"),            # generic kernel
     ([7, 12, 5], [3, 20, 6], 16, 8, 16, "f32"),
 ])
 def test_rect_block_matches_oracle(nt, rows, cols, c_s, c_z, hidden, dtype, kernel,
                                    monkeypatch):
-    if kernel == "p32":
+    if kernel != "default":
         if (c_z, hidden) != (128, 512):
             pytest.skip("the override only matters for the 128/512 fused kernel")
-        monkeypatch.setenv("NT_TRANSITION_KERNEL", "p32")
+        monkeypatch.setenv("NT_TRANSITION_KERNEL", kernel)
     announce(f"rect block {dtype} c_z={c_z} hidden={hidden} kernel={kernel}")
     x_r = pin.random_rows(sum(rows), c_s, dtype, seed=31)
     x_c = pin.random_rows(sum(cols), c_s, dtype, seed=32)

@@ -204,13 +204,14 @@ def test_broadcast_transition_parity(nt, lengths, c_z, hidden, dtype):
     assert scaled_max_err(f64(out, torch), ref) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("kernel", ["default", "p32"])
+@pytest.mark.parametrize("kernel", ["default", "pf", "p32"])
 def test_broadcast_transition_kernels_agree(nt, kernel, monkeypatch):
-    """The fused c_z = 128, hidden = 512 form has two kernels (the prefetching
-    one by default, the persistent one on request); both match the oracle on a
-    multi-tile ragged batch whose tiles mix short and long rows."""
-    if kernel == "p32":
-        monkeypatch.setenv("NT_TRANSITION_KERNEL", "p32")
+    """The fused c_z = 128, hidden = 512 form has three kernels (the
+    weight-stationary one by default, the prefetching and the persistent ones
+    on request); each matches the oracle on a multi-block ragged batch whose
+    blocks mix short and long rows."""
+    if kernel != "default":
+        monkeypatch.setenv("NT_TRANSITION_KERNEL", kernel)
     lengths = [3, 40, 1, 17, 64, 5, 33, 2, 29, 8]
     announce(f"broadcast+transition kernel={kernel} B={len(lengths)}")
     T = sum(lengths)
@@ -227,15 +228,15 @@ def test_broadcast_transition_kernels_agree(nt, kernel, monkeypatch):
     assert scaled_max_err(f64(out, torch), ref) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("kernel", ["default", "p32"])
+@pytest.mark.parametrize("kernel", ["default", "pf", "p32"])
 @pytest.mark.parametrize("idx", [3, 4])
 def test_broadcast_transition_full_size_sampled(nt, kernel, idx, monkeypatch):
-    """Both fused kernels at a full workload size, where every workgroup runs
-    several tiles (and the prefetching kernel prefetches across tiles),
-    checked on sampled cells: tile starts and ends, sample boundaries and
+    """The fused kernels at a full workload size, where every workgroup runs
+    many blocks (and stages each next block during the current one), checked
+    on sampled cells: tile and block starts and ends, sample boundaries and
     random cells."""
-    if kernel == "p32":
-        monkeypatch.setenv("NT_TRANSITION_KERNEL", "p32")
+    if kernel != "default":
+        monkeypatch.setenv("NT_TRANSITION_KERNEL", kernel)
     x = pin.workload_inputs(idx)
     lengths = x.lengths.tolist()
     announce(f"broadcast+transition full size {x.name} kernel={kernel}")
