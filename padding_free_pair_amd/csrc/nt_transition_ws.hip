@@ -37,6 +37,11 @@ constexpr int kWsCells = 32;     // cells per block
 constexpr int kWsSamples = 256;  // partitions up to this many samples decode from LDS
 constexpr int kWsBufFlags = 0x00020000;  // raw buffer, 32-bit data format
 
+template <int V>
+struct ws_int {
+  static constexpr int value = V;
+};
+
 __device__ __forceinline__ f32x16 ws_mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -54,13 +59,29 @@ __device__ __forceinline__ float ws_relu(float x) {
   return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
 }
 
-// This wave's LDS operations have completed, then s_barrier. Global stores
-// and loads in flight are not waited for (nothing in LDS depends on them);
-// the asm statements keep the compiler from moving memory accesses across.
+// Eight floats rounded to bf16 (nearest-even) two at a time: one
+// v_cvt_pk_bf16_f32 per pair instead of a conversion and a permute per value.
+typedef float ws_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 ws_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8 ws_pack8(float v0, float v1, float v2, float v3, float v4,
+                                          float v5, float v6, float v7) {
+  const ws_bf16x2 p0 = __builtin_convertvector((ws_f32x2){v0, v1}, ws_bf16x2);
+  const ws_bf16x2 p1 = __builtin_convertvector((ws_f32x2){v2, v3}, ws_bf16x2);
+  const ws_bf16x2 p2 = __builtin_convertvector((ws_f32x2){v4, v5}, ws_bf16x2);
+  const ws_bf16x2 p3 = __builtin_convertvector((ws_f32x2){v6, v7}, ws_bf16x2);
+  return (bf16x8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// This wave's LDS operations except the N most recent have completed, then
+// s_barrier. Global stores and loads in flight are not waited for (nothing in
+// LDS depends on them); the asm statements keep the compiler from moving
+// memory accesses across.
+template <int N>
 __device__ __forceinline__ void ws_barrier() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
@@ -166,7 +187,7 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
       __builtin_amdgcn_make_buffer_rsrc((void*)a, 0, (int)(T_rows * ROW), kWsBufFlags);
   const __amdgpu_buffer_rsrc_t b_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)b, 0, (int)(T_cols * ROW), kWsBufFlags);
-  f32x4 va[4], vb[4];
+  f32x4 va[2][4], vb[2][4];  // two gather sets: a block is gathered two phases ahead
   // Decode of cell `cell` of the next block, in steps spread over a phase so
   // that every memory read has several products' time to land. Step 1: the
   // first sample of the cell's 256-cell tile (a vector load, so that it does
@@ -234,26 +255,25 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
     d_col = (int)(d_mu + c);
   };
   // step 5: the gathers (eight threads per cell, 64 contiguous bytes each)
-  auto gather_a = [&]() {
+  auto gather_a = [&](int set) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      va[q] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, d_row * ROW + 64 * k8 + 16 * q, 0, 0);
+      va[set][q] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, d_row * ROW + 64 * k8 + 16 * q, 0, 0);
   };
-  auto gather_b = [&]() {
+  auto gather_b = [&](int set) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      vb[q] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, d_col * ROW + 64 * k8 + 16 * q, 0, 0);
+      vb[set][q] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, d_col * ROW + 64 * k8 + 16 * q, 0, 0);
   };
   // z = a + b in fp32: bf16 operand fragment k8 (lanes sc and sc + 32) and
   // the fp32 residual of out block k8 / 2, rows 16 (k8 % 2) .. + 15.
   // half hh of the staging store: features 16 k8 + 8 hh .. + 7
-  auto stage_half = [&](int buf, int hh) {
+  auto stage_half = [&](int buf, int hh, int set) {
     float z[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) z[e] = va[2 * hh + e / 4][e % 4] + vb[2 * hh + e / 4][e % 4];
-    bf16x8 o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (bf16)z[e];
+    for (int e = 0; e < 8; ++e)
+      z[e] = va[set][2 * hh + e / 4][e % 4] + vb[set][2 * hh + e / 4][e % 4];
+    const bf16x8 o = ws_pack8(z[0], z[1], z[2], z[3], z[4], z[5], z[6], z[7]);
     *reinterpret_cast<bf16x8*>(zs[buf] + 1024 * k8 + 16 * ((sc + 32 * hh) ^ (2 * k8))) = o;
     const int ob = k8 >> 1, s = k8 & 1;
 #pragma unroll
@@ -269,20 +289,19 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
   // ---- per-block state
   f32x16 y[4];     // partial outputs, rotation order; y[0] is this wave's own block
   f32x16 own;      // own block of the previous block (residual + this wave's partial)
-  f32x16 seed;     // fp32 residual of this block's own outputs
   f32x16 hacc[4];  // first-product accumulators, one per hidden block
   bf16x8 hf[2][2];
   bf16x8 zf[KT];
-  f32x4 pr[2][3];
+  f32x4 pr[3];
   int64_t prev = -1;
 
   // relu of k-step s of a first-product accumulator, packed to bf16. The
   // rounding comes first: bf16 preserves signs, so relu(bf16(x)) is
   // bf16(relu(x)) bit for bit, and the max is one packed integer op.
   auto relu_pack = [&](const f32x16& acc, int s) -> bf16x8 {
-    bf16x8 o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (bf16)acc[8 * s + e];
+    const int b = 8 * s;
+    const bf16x8 o = ws_pack8(acc[b], acc[b + 1], acc[b + 2], acc[b + 3], acc[b + 4], acc[b + 5],
+                              acc[b + 6], acc[b + 7]);
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     const s16x8 v = __builtin_elementwise_max(__builtin_bit_cast(s16x8, o), (s16x8){});
     return __builtin_bit_cast(bf16x8, v);
@@ -290,18 +309,18 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
   // part q (elements 4 q .. 4 q + 3) of the sum of the four partials of out
   // block `wave`: own first, then waves wave + 1, + 2, + 3 in turn
   auto read_part = [&](int pbuf, int q, int j) {
-    pr[q & 1][j - 1] =
+    pr[j - 1] =
         *reinterpret_cast<const f32x4*>(&ps[pbuf][(wave + j) & 3][3 - j][1024 * q + 16 * lane]);
   };
   auto add_part = [&](int q, int j) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) own[4 * q + e] += pr[q & 1][j - 1][e];
+    for (int e = 0; e < 4; ++e) own[4 * q + e] += pr[j - 1][e];
   };
   auto store_out = [&](int64_t blk, int s) {
     const int64_t cell = blk * kWsCells + n;
-    bf16x8 o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (bf16)own[8 * s + e];
+    const int b = 8 * s;
+    const bf16x8 o = ws_pack8(own[b], own[b + 1], own[b + 2], own[b + 3], own[b + 4], own[b + 5],
+                              own[b + 6], own[b + 7]);
     if (blk >= 0 && cell < cells)
       *reinterpret_cast<bf16x8*>(z_out + cell * CZ + 32 * wave + 16 * s + 8 * h) = o;
   };
@@ -312,45 +331,59 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
     *reinterpret_cast<f32x4*>(&ps[pbuf][wave][j - 1][1024 * q + 16 * lane]) = v;
   };
 
+  // blocks past the end are replaced by the last block: staged into a buffer
+  // nobody reads, so that the phase body has no branches
+  auto clampb = [&](int64_t x) -> int64_t { return x < nblocks ? x : nblocks - 1; };
+  const int64_t G = gridDim.x;
   int64_t blk = blockIdx.x;
   dec1(blk);
   dec2(blk);
   dec3();
   dec4();
-  gather_a();
-  gather_b();
-  stage_half(0, 0);
-  stage_half(0, 1);
-  dec1(blk + gridDim.x < nblocks ? blk + gridDim.x : nblocks - 1);
-  ws_barrier();
+  gather_a(0);
+  gather_b(0);
+  stage_half(0, 0, 0);
+  stage_half(0, 1, 0);
+  dec1(clampb(blk + G));
+  dec2(clampb(blk + G));
+  dec3();
+  dec4();
+  gather_a(1);
+  gather_b(1);
+  dec1(clampb(blk + 2 * G));
+  ws_barrier<0>();
 
   // One phase per block: 64 product slots. Slots 0..31 run the first
   // product (k-step i / 4 of hidden block i % 4, four independent chains),
-  // slots 32..63 the second (hidden block (i - 32) / 8; out blocks in the
-  // order 1, 2, 3, 0 so that the partials the other waves need finish
-  // first). Each slot carries a small share of the other work:
-  //   0        this block's residual (own out block)
+  // slots 32..63 the second (hidden block (i - 32) / 8, four out-block
+  // chains; in the last hidden block out blocks 1, 2, 3 finish first, since
+  // the other waves need them). Each slot carries a small share of the other
+  // work:
+  //   0..22    this block's operand fragments, read four slots ahead of use
+  //   1        barrier: every wave's partials of the previous block are in LDS
+  //   3..25    previous block: the other waves' partials, each read four
+  //            slots before it is added (and six before its buffer is reused)
   //   5..16    next block: offsets, sample, row and column, gathers
   //   20       the block after next: its tile's first sample
-  //   2..26    previous block: the other waves' partials, read four slots
-  //            before they are added
+  //   24..27   this block's residual (own out block)
   //   27, 28   previous block: rounding and store
   //   30..50   relu of hidden blocks 0..3, two slots each
   //   44..47   next block: z = a + b into the operand and residual buffers
-  //   62, 63   this block: partials of out block 1
-  int buf = 0;
-  for (int it = 0;; ++it) {
-    buf = it & 1;
-    const int64_t next = blk + gridDim.x;
+  //   61..63   this block: partials of out blocks 1 and 2 (the rest follow)
+  // The barrier closing a phase waits for the staging writes but not for the
+  // twelve partial writes; the barrier in slot 1 of the next phase does.
+  // Phase P of a pair of phases (P = block parity: LDS buffer P holds this
+  // block's operands, gather set P receives the block two ahead, set P ^ 1
+  // holds the next block's rows). Returns whether another block follows.
+  auto phase = [&](auto par) -> bool {
+    constexpr int buf = decltype(par)::value;
+    const int64_t next = blk + G;
     const bool has_next = next < nblocks;
-    // after the last block the staging repeats it into the idle buffer, and
-    // the first phase sums stale partials without storing them, so that the
-    // phase body has no branches
-    const int64_t stg = has_next ? next : blk;
-    const int64_t stg2 = stg + gridDim.x < nblocks ? stg + gridDim.x : nblocks - 1;
-#pragma unroll
-    for (int t = 0; t < KT; ++t)
+    auto read_zf = [&](int t) {
       zf[t] = *reinterpret_cast<const bf16x8*>(zs[buf] + 1024 * t + 16 * (lane ^ (2 * t)));
+    };
+    read_zf(0);
+    read_zf(1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
@@ -358,26 +391,31 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
         const int t = i >> 2, hb = i & 3;
         hacc[hb] = ws_mfma(w1f[hb][t], zf[t], t == 0 ? f32x16{} : hacc[hb]);
       } else {
-        const int hb = (i - 32) >> 3, k = (i - 32) & 7, s = k >> 2, j = (k + 1) & 3;
-        const f32x16 c = hb > 0 || s > 0 ? y[j] : (j == 0 ? seed : f32x16{});
+        const int hb = (i - 32) >> 3, k = (i - 32) & 7;
+        // (s, out block) of product k: s-major, out blocks 1, 2, 3, 0; in the
+        // last hidden block interleaved so that blocks 1, 2, 3 finish first
+        constexpr int kS[8] = {0, 0, 1, 0, 1, 0, 1, 1}, kJ[8] = {1, 2, 1, 3, 2, 0, 3, 0};
+        const int s = hb == 3 ? kS[k] : k >> 2, j = hb == 3 ? kJ[k] : (k + 1) & 3;
+        // y[0] starts from the residual read into it in slots 24..27
+        const f32x16 c = hb > 0 || s > 0 || j == 0 ? y[j] : f32x16{};
         y[j] = ws_mfma(w2f[j][hb][s], hf[hb & 1][s], c);
       }
-      if (i == 0) {
+      if (i >= 2 && i <= 22 && (i + 2) % 4 == 0) read_zf((i + 6) / 4);
+      if (i == 1) ws_barrier<2>();
+      if (i >= 24 && i <= 27) {
+        const int q = i - 24;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(
+            rs[buf] + 4096 * wave + 1024 * q + 16 * (lane ^ (4 * wave + 2 * (q >> 1))));
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(
-              rs[buf] + 4096 * wave + 1024 * q + 16 * (lane ^ (4 * wave + 2 * (q >> 1))));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) seed[4 * q + e] = v[e];
-        }
+        for (int e = 0; e < 4; ++e) y[0][4 * q + e] = v[e];
       }
-      if (i == 5) dec2(stg);
+      if (i == 5) dec2(clampb(blk + 2 * G));
       if (i == 9) dec3();
       if (i == 13) dec4();
-      if (i == 15) gather_a();
-      if (i == 16) gather_b();
-      if (i == 20) dec1(stg2);
-      if (i == 44 || i == 46) stage_half(buf ^ 1, (i - 44) / 2);
+      if (i == 15) gather_a(buf);
+      if (i == 16) gather_b(buf);
+      if (i == 20) dec1(clampb(blk + 3 * G));
+      if (i == 44 || i == 46) stage_half(buf ^ 1, (i - 44) / 2, buf ^ 1);
       if (i >= 2 && i <= 22 && (i - 2) % 6 < 3) read_part(buf ^ 1, (i - 2) / 6, (i - 2) % 6 + 1);
       if (i >= 6 && i <= 26 && (i - 6) % 6 < 3) add_part((i - 6) / 6, (i - 6) % 6 + 1);
       if (i == 27 || i == 28) store_out(prev, i - 27);
@@ -385,22 +423,38 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
       if (i == 33 || i == 34) hf[1][i - 33] = relu_pack(hacc[1], i - 33);
       if (i == 41 || i == 42) hf[0][i - 41] = relu_pack(hacc[2], i - 41);
       if (i == 49 || i == 50) hf[1][i - 49] = relu_pack(hacc[3], i - 49);
-      if (i == 62 || i == 63) {
-        write_part(buf, 1, 2 * (i - 62));
-        write_part(buf, 1, 2 * (i - 62) + 1);
+      if (i == 61 || i == 62) {
+        write_part(buf, 1, 2 * (i - 61));
+        write_part(buf, 1, 2 * (i - 61) + 1);
+      }
+      if (i == 63) {
+        write_part(buf, 2, 0);
+        write_part(buf, 2, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    write_part(buf, 2, 2);
+    write_part(buf, 2, 3);
 #pragma unroll
-    for (int j = 2; j < 4; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) write_part(buf, j, q);
+    for (int q = 0; q < 4; ++q) write_part(buf, 3, q);
     own = y[0];
-    ws_barrier();
+    ws_barrier<12>();
     prev = blk;
-    if (!has_next) break;
     blk = next;
+    return has_next;
+  };
+  int buf;
+  for (;;) {
+    if (!phase(ws_int<0>{})) {
+      buf = 0;
+      break;
+    }
+    if (!phase(ws_int<1>{})) {
+      buf = 1;
+      break;
+    }
   }
+  ws_barrier<0>();
   // the last block's sum
 #pragma unroll
   for (int q = 0; q < 4; ++q)
