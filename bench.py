@@ -311,12 +311,22 @@ def time_kernel(fn, reps: int, torch) -> float:
     return start.elapsed_time(end) / 1e3 / reps
 
 
-def transition_kernel_label(c_z: int, hidden: int, dtype: str) -> str:
+def transition_kernel_id(c_z: int, hidden: int, dtype: str) -> str:
     """The kernel the library launches for the fused broadcast + transition."""
     choice = os.environ.get("NT_TRANSITION_KERNEL")
-    if dtype == "bf16" and c_z == 128 and hidden == 512 and choice == "pf":
+    if dtype == "bf16" and c_z == 128 and hidden == 512:
+        return {"pf": "k_transition_pf", "p32": "k_transition_p32"}.get(choice, "k_transition_ws")
+    if dtype == "bf16" and (c_z, hidden) == (64, 128):
+        return "k_transition_p32"
+    return "fused"
+
+
+def transition_kernel_label(c_z: int, hidden: int, dtype: str) -> str:
+    """The kernel the library launches for the fused broadcast + transition."""
+    kid = transition_kernel_id(c_z, hidden, dtype)
+    if kid == "k_transition_pf":
         return "k_transition_pf (fused broadcast, next tile's b rows prefetched)"
-    if dtype == "bf16" and c_z == 128 and hidden == 512 and choice != "p32":
+    if kid == "k_transition_ws":
         return "k_transition_ws (fused broadcast, weights resident in registers)"
     if dtype == "bf16" and (c_z, hidden) in ((128, 512), (64, 128)):
         return "k_transition_p32 (fused broadcast prologue)"
@@ -404,7 +414,7 @@ def traffic_for(kernel_key: str):
     with open(path) as f:
         data = json.load(f)
     entry = data.get(kernel_key)
-    if not entry:
+    if not entry or entry.get("kernel") != kernel_key.split(":")[0]:
         return None
     src = os.path.join(ROOT, "padding_free_pair_amd", "csrc", entry["source"])
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
@@ -564,7 +574,7 @@ def main():
     dom = kern["transition"]
     roofline = {"bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
                 "unit": dom["unit"], "frac": dom["frac"],
-                "traffic": traffic_for(f"transition_fused:{w.name}"),
+                "traffic": traffic_for(f"{transition_kernel_id(w.c_z, w.hidden, w.dtype)}:{w.name}"),
                 "kernel": dom["kernel"], "avg_launch_ms": dom["ms"]}
 
     result = {
