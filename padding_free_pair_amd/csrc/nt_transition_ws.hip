@@ -59,6 +59,13 @@ __device__ __forceinline__ float ws_relu(float x) {
   return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
 }
 
+// Lane-index swizzle of the staging buffers. A staging store is issued by
+// eight threads of one cell (k = 0..7) and its two neighbours' cells; with
+// this key the eight stores of one cell land in eight different 16-byte bank
+// groups and those of a cell pair in sixteen, while a fragment read (lane
+// index XOR a constant below 16) stays a permutation of 16-lane groups.
+__device__ __forceinline__ int ws_key(int k) { return k + 8 * (k & 1); }
+
 // Eight floats rounded to bf16 (nearest-even) two at a time: one
 // v_cvt_pk_bf16_f32 per pair instead of a conversion and a permute per value.
 typedef float ws_f32x2 __attribute__((ext_vector_type(2)));
@@ -123,8 +130,9 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
   constexpr int CZ = 128, HID = 512;
   constexpr int KT = CZ / 16;  // first-product k-steps
   constexpr int ROW = CZ * 4;  // bytes of one fp32 single row
-  // LDS: operand fragments [buf][k-step][64 lanes] x 16 B (lane index XOR 2 t);
-  // residuals [buf][out block][q][64 lanes] x 16 B (lane index XOR 4 j + 2 (q / 2));
+  // LDS: operand fragments [buf][k-step t][64 lanes] x 16 B, lane index XOR
+  // ws_key(t); residuals [buf][out block j][q][64 lanes] x 16 B, lane index
+  // XOR ws_key(2 j + q / 2);
   // partials [buf][writer wave][rotation slot][q][64 lanes] x 16 B.
   __shared__ __attribute__((aligned(16))) unsigned char zs[2][KT * 1024];
   __shared__ __attribute__((aligned(16))) unsigned char rs[2][4 * 4096];
@@ -274,7 +282,7 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
     for (int e = 0; e < 8; ++e)
       z[e] = va[set][2 * hh + e / 4][e % 4] + vb[set][2 * hh + e / 4][e % 4];
     const bf16x8 o = ws_pack8(z[0], z[1], z[2], z[3], z[4], z[5], z[6], z[7]);
-    *reinterpret_cast<bf16x8*>(zs[buf] + 1024 * k8 + 16 * ((sc + 32 * hh) ^ (2 * k8))) = o;
+    *reinterpret_cast<bf16x8*>(zs[buf] + 1024 * k8 + 16 * ((sc + 32 * hh) ^ ws_key(k8))) = o;
     const int ob = k8 >> 1, s = k8 & 1;
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
@@ -282,7 +290,7 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = z[4 * qq + e];
       *reinterpret_cast<f32x4*>(rs[buf] + 4096 * ob + 1024 * (2 * s + qq) +
-                                16 * ((sc + 32 * hh) ^ (2 * k8))) = v;
+                                16 * ((sc + 32 * hh) ^ ws_key(k8))) = v;
     }
   };
 
@@ -290,7 +298,7 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
   f32x16 y[4];     // partial outputs, rotation order; y[0] is this wave's own block
   f32x16 own;      // own block of the previous block (residual + this wave's partial)
   f32x16 hacc[4];  // first-product accumulators, one per hidden block
-  bf16x8 hf[2][2];
+  bf16x8 hf[4][2];  // relu(H) of the four hidden blocks, two k-steps each
   bf16x8 zf[KT];
   f32x4 pr[3];
   int64_t prev = -1;
@@ -355,21 +363,21 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
 
   // One phase per block: 64 product slots. Slots 0..31 run the first
   // product (k-step i / 4 of hidden block i % 4, four independent chains),
-  // slots 32..63 the second (hidden block (i - 32) / 8, four out-block
-  // chains; in the last hidden block out blocks 1, 2, 3 finish first, since
-  // the other waves need them). Each slot carries a small share of the other
-  // work:
+  // slots 32..63 the second, two out-block chains at a time (1 and 2, then 3
+  // and 0), so that the partials the other waves need are ready early. Each
+  // slot carries a small share of the other work:
   //   0..22    this block's operand fragments, read four slots ahead of use
   //   1        barrier: every wave's partials of the previous block are in LDS
   //   3..25    previous block: the other waves' partials, each read four
   //            slots before it is added (and six before its buffer is reused)
   //   5..16    next block: offsets, sample, row and column, gathers
   //   20       the block after next: its tile's first sample
-  //   24..27   this block's residual (own out block)
+  //   29..32   this block's residual (own out block)
   //   27, 28   previous block: rounding and store
-  //   30..50   relu of hidden blocks 0..3, two slots each
+  //   30..42   relu of hidden blocks 0..3, two slots each
   //   44..47   next block: z = a + b into the operand and residual buffers
-  //   61..63   this block: partials of out blocks 1 and 2 (the rest follow)
+  //   49..56   this block: partials of out blocks 1 and 2 (block 3 follows
+  //            the last product)
   // The barrier closing a phase waits for the staging writes but not for the
   // twelve partial writes; the barrier in slot 1 of the next phase does.
   // Phase P of a pair of phases (P = block parity: LDS buffer P holds this
@@ -380,7 +388,7 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
     const int64_t next = blk + G;
     const bool has_next = next < nblocks;
     auto read_zf = [&](int t) {
-      zf[t] = *reinterpret_cast<const bf16x8*>(zs[buf] + 1024 * t + 16 * (lane ^ (2 * t)));
+      zf[t] = *reinterpret_cast<const bf16x8*>(zs[buf] + 1024 * t + 16 * (lane ^ ws_key(t)));
     };
     read_zf(0);
     read_zf(1);
@@ -391,21 +399,21 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
         const int t = i >> 2, hb = i & 3;
         hacc[hb] = ws_mfma(w1f[hb][t], zf[t], t == 0 ? f32x16{} : hacc[hb]);
       } else {
-        const int hb = (i - 32) >> 3, k = (i - 32) & 7;
-        // (s, out block) of product k: s-major, out blocks 1, 2, 3, 0; in the
-        // last hidden block interleaved so that blocks 1, 2, 3 finish first
-        constexpr int kS[8] = {0, 0, 1, 0, 1, 0, 1, 1}, kJ[8] = {1, 2, 1, 3, 2, 0, 3, 0};
-        const int s = hb == 3 ? kS[k] : k >> 2, j = hb == 3 ? kJ[k] : (k + 1) & 3;
-        // y[0] starts from the residual read into it in slots 24..27
+        // out blocks two at a time (1 with 2, then 3 with 0), each over
+        // hidden block hb and k-step s in turn, so that the blocks the
+        // other waves need finish first
+        const int m = (i - 32) >> 1, hb = (m & 7) >> 1, s = m & 1;
+        const int j = (i < 48 ? 1 : 3) + (i & 1) - (i >= 48 && (i & 1) ? 4 : 0);
+        // y[0] starts from the residual read into it in slots 29..32
         const f32x16 c = hb > 0 || s > 0 || j == 0 ? y[j] : f32x16{};
-        y[j] = ws_mfma(w2f[j][hb][s], hf[hb & 1][s], c);
+        y[j] = ws_mfma(w2f[j][hb][s], hf[hb][s], c);
       }
       if (i >= 2 && i <= 22 && (i + 2) % 4 == 0) read_zf((i + 6) / 4);
       if (i == 1) ws_barrier<2>();
-      if (i >= 24 && i <= 27) {
-        const int q = i - 24;
+      if (i >= 29 && i <= 32) {
+        const int q = i - 29;
         const f32x4 v = *reinterpret_cast<const f32x4*>(
-            rs[buf] + 4096 * wave + 1024 * q + 16 * (lane ^ (4 * wave + 2 * (q >> 1))));
+            rs[buf] + 4096 * wave + 1024 * q + 16 * (lane ^ ws_key(2 * wave + (q >> 1))));
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[0][4 * q + e] = v[e];
       }
@@ -421,20 +429,11 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
       if (i == 27 || i == 28) store_out(prev, i - 27);
       if (i == 30 || i == 31) hf[0][i - 30] = relu_pack(hacc[0], i - 30);
       if (i == 33 || i == 34) hf[1][i - 33] = relu_pack(hacc[1], i - 33);
-      if (i == 41 || i == 42) hf[0][i - 41] = relu_pack(hacc[2], i - 41);
-      if (i == 49 || i == 50) hf[1][i - 49] = relu_pack(hacc[3], i - 49);
-      if (i == 61 || i == 62) {
-        write_part(buf, 1, 2 * (i - 61));
-        write_part(buf, 1, 2 * (i - 61) + 1);
-      }
-      if (i == 63) {
-        write_part(buf, 2, 0);
-        write_part(buf, 2, 1);
-      }
+      if (i == 37 || i == 38) hf[2][i - 37] = relu_pack(hacc[2], i - 37);
+      if (i == 41 || i == 42) hf[3][i - 41] = relu_pack(hacc[3], i - 41);
+      if (i >= 49 && i <= 56) write_part(buf, 1 + (i - 49) / 4, (i - 49) % 4);
       __builtin_amdgcn_sched_barrier(0);
     }
-    write_part(buf, 2, 2);
-    write_part(buf, 2, 3);
 #pragma unroll
     for (int q = 0; q < 4; ++q) write_part(buf, 3, q);
     own = y[0];
