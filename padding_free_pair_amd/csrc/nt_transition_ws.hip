@@ -18,8 +18,8 @@
 //    the four partials meet in LDS, where the wave that owns out block j
 //    (the 32 outputs j + w of wave w's rotation) adds the other three to its
 //    own, which was seeded with the fp32 residual, and stores the result.
-//  * A workgroup walks blocks blockIdx.x, + gridDim.x, ... One phase per
-//    block, closed by one barrier. During the MFMAs of block k a wave also
+//  * A workgroup walks a contiguous range of blocks, one phase per block.
+//    During the MFMAs of block k a wave also
 //    reduces and stores block k - 1 and stages block k + 1: its threads
 //    gather a[row] and b[col] (eight threads per cell, 64 contiguous bytes
 //    each), form z in fp32 and write both the bf16 operand fragments and the
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
     const int64_t* __restrict__ col_offsets, const int32_t* __restrict__ col_lengths,
     const int32_t* __restrict__ tile_sample, int B,
     const bf16* __restrict__ W1, const bf16* __restrict__ W2, bf16* __restrict__ z_out,
-    int64_t cells, int64_t nblocks, int64_t T_rows, int64_t T_cols) {
+    int64_t cells, int64_t nblocks, int64_t per, int64_t T_rows, int64_t T_cols) {
   constexpr int CZ = 128, HID = 512;
   constexpr int KT = CZ / 16;  // first-product k-steps
   constexpr int ROW = CZ * 4;  // bytes of one fp32 single row
@@ -341,9 +341,13 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
 
   // blocks past the end are replaced by the last block: staged into a buffer
   // nobody reads, so that the phase body has no branches
-  auto clampb = [&](int64_t x) -> int64_t { return x < nblocks ? x : nblocks - 1; };
-  const int64_t G = gridDim.x;
-  int64_t blk = blockIdx.x;
+  // Workgroup g takes the contiguous blocks [first, last): consecutive phases
+  // then gather neighbouring single rows, which the caches still hold.
+  const int64_t first = (int64_t)blockIdx.x * per;
+  const int64_t last = first + per < nblocks ? first + per : nblocks;
+  auto clampb = [&](int64_t x) -> int64_t { return x < last ? x : last - 1; };
+  const int64_t G = 1;
+  int64_t blk = first;
   dec1(blk);
   dec2(blk);
   dec3();
@@ -386,7 +390,7 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
   auto phase = [&](auto par) -> bool {
     constexpr int buf = decltype(par)::value;
     const int64_t next = blk + G;
-    const bool has_next = next < nblocks;
+    const bool has_next = next < last;
     auto read_zf = [&](int t) {
       zf[t] = *reinterpret_cast<const bf16x8*>(zs[buf] + 1024 * t + 16 * (lane ^ ws_key(t)));
     };
@@ -471,7 +475,10 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
 hipError_t launch_transition_ws(const nt_partition& p, const void* a, const void* b, void* z_out,
                                 const void* W1, const void* W2, int cus, hipStream_t stream) {
   const int64_t nblocks = (p.cells + kWsCells - 1) / kWsCells;
-  const int64_t grid = nblocks < cus ? nblocks : cus;
+  // `per` blocks to a workgroup, and only as many workgroups as that needs,
+  // so that (grid - 1) * per < nblocks: every workgroup has a block
+  const int64_t per = (nblocks + cus - 1) / cus;
+  const int64_t grid = (nblocks + per - 1) / per;
   // the LDS copy of the partition holds square partitions (mu = eta, M = N)
   const bool lds_part =
       p.B <= kWsSamples && p.col_offsets == p.single_offsets && p.n_max <= 65535;
@@ -480,7 +487,7 @@ hipError_t launch_transition_ws(const nt_partition& p, const void* a, const void
                      static_cast<const float*>(a), static_cast<const float*>(b), p.pair_offsets,
                      p.single_offsets, p.col_offsets, p.col_lengths, p.tile_sample, p.B,
                      static_cast<const bf16*>(W1), static_cast<const bf16*>(W2),
-                     static_cast<bf16*>(z_out), p.cells, nblocks, p.T, p.T_cols);
+                     static_cast<bf16*>(z_out), p.cells, nblocks, per, p.T, p.T_cols);
   return hipGetLastError();
 }
 
