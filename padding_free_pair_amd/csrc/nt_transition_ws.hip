@@ -59,6 +59,14 @@ __device__ __forceinline__ float ws_relu(float x) {
   return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
 }
 
+// Index of workgroup g among the workgroups of its XCD, counted XCD by XCD:
+// XCD x = g mod 8 holds q or q + 1 of the grid's G = 8 q + rem workgroups.
+// A bijection of [0, G).
+__device__ __forceinline__ int64_t ws_xcd_order(int64_t g, int64_t G) {
+  const int64_t q = G / 8, rem = G % 8, x = g % 8, pos = g / 8;
+  return x * q + (x < rem ? x : rem) + pos;
+}
+
 // Lane-index swizzle of the staging buffers. A staging store is issued by
 // eight threads of one cell (k = 0..7) and its two neighbours' cells; with
 // this key the eight stores of one cell land in eight different 16-byte bank
@@ -343,7 +351,11 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
   // nobody reads, so that the phase body has no branches
   // Workgroup g takes the contiguous blocks [first, last): consecutive phases
   // then gather neighbouring single rows, which the caches still hold.
-  const int64_t first = (int64_t)blockIdx.x * per;
+  // Workgroups are dispatched to the eight XCDs in turn (g mod 8); ranges are
+  // numbered so that each XCD's workgroups take neighbouring ranges, and its
+  // L2 serves a contiguous eighth of the pair state.
+  const int64_t range = ws_xcd_order(blockIdx.x, gridDim.x);
+  const int64_t first = range * per;
   const int64_t last = first + per < nblocks ? first + per : nblocks;
   auto clampb = [&](int64_t x) -> int64_t { return x < last ? x : last - 1; };
   const int64_t G = 1;
