@@ -262,6 +262,52 @@ def test_broadcast_transition_full_size_sampled(nt, kernel, idx, monkeypatch):
     assert scaled_max_err(got, ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("lengths", [
+    [90],          # 8,100 cells: 254 blocks of 32, fewer than one per CU
+    [91],          # 8,281 cells: 259 blocks, two to a workgroup
+    [128, 3],      # 16,393 cells: 513 blocks, a one-cell tail
+    [181, 1, 0],   # 32,762 cells: 1,024 blocks minus a ragged tail
+])
+def test_broadcast_transition_block_ranges(nt, lengths):
+    """The fused 128/512 kernel hands each workgroup a contiguous range of
+    32-cell blocks and numbers the ranges by XCD: grids of fewer blocks than
+    CUs, just over one per CU and several per CU, checked on every cell."""
+    announce(f"broadcast+transition block ranges {lengths}")
+    T = sum(lengths)
+    a = pin.random_rows(T, 128, "f32", seed=51)
+    b = pin.random_rows(T, 128, "f32", seed=52)
+    W1, W2 = _mlp(128, 512, "bf16", seed=53)
+    p = nt.nt_make_partition(lengths)
+    full, out = _guarded(p.cells, 128, TD["bf16"])
+    nt.nt_pair_broadcast_transition(p, to_dev(a, torch), to_dev(b, torch), to_dev(W1, torch),
+                                    to_dev(W2, torch), z_out=out)
+    torch.cuda.synchronize()
+    _check_guard(full, 64, p.cells)
+    ref = oracle.transition(oracle.broadcast(lengths, a.f64, b.f64), W1.f64, W2.f64)
+    assert scaled_max_err(f64(out, torch), ref) <= TOL["bf16"]
+
+
+def test_broadcast_transition_many_samples(nt):
+    """More than 256 samples (the partition is decoded from global memory
+    rather than an LDS copy) with empty and one-cell samples, at the fused
+    128/512 shape; every cell against the oracle."""
+    rng = np.random.default_rng(61)
+    lengths = rng.integers(0, 13, 300).tolist() + [40, 1, 0, 33]
+    announce(f"broadcast+transition B={len(lengths)}")
+    T = sum(lengths)
+    a = pin.random_rows(T, 128, "f32", seed=62)
+    b = pin.random_rows(T, 128, "f32", seed=63)
+    W1, W2 = _mlp(128, 512, "bf16", seed=64)
+    p = nt.nt_make_partition(lengths)
+    full, out = _guarded(p.cells, 128, TD["bf16"])
+    nt.nt_pair_broadcast_transition(p, to_dev(a, torch), to_dev(b, torch), to_dev(W1, torch),
+                                    to_dev(W2, torch), z_out=out)
+    torch.cuda.synchronize()
+    _check_guard(full, 64, p.cells)
+    ref = oracle.transition(oracle.broadcast(lengths, a.f64, b.f64), W1.f64, W2.f64)
+    assert scaled_max_err(f64(out, torch), ref) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("c_z,hidden", [(128, 512), (64, 128), (16, 24)])
 def test_broadcast_transition_exact(nt, dtype, c_z, hidden):
