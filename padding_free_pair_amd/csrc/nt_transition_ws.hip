@@ -376,15 +376,13 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
   gather_b(1);
   dec1(clampb(blk + 2 * G));
   ws_barrier<0>();
-#pragma unroll
-  for (int t = 0; t < KT; ++t)
-    zf[t] = *reinterpret_cast<const bf16x8*>(zs[0] + 1024 * t + 16 * (lane ^ ws_key(t)));
 
   // One phase per block: 64 product slots. Slots 0..31 run the first
   // product (k-step i / 4 of hidden block i % 4, four independent chains),
   // slots 32..63 the second, two out-block chains at a time (1 and 2, then 3
   // and 0), so that the partials the other waves need are ready early. Each
   // slot carries a small share of the other work:
+  //   0..22    this block's operand fragments, read four slots ahead of use
   //   1        barrier: every wave's partials of the previous block are in LDS
   //   3..25    previous block: the other waves' partials, each read four
   //            slots before it is added (and six before its buffer is reused)
@@ -394,12 +392,10 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
   //   27, 28   previous block: rounding and store
   //   30..42   relu of hidden blocks 0..3, two slots each
   //   44..47   next block: z = a + b into the operand and residual buffers
-  //   48       barrier: every wave's staging writes are in LDS
   //   49..56   this block: partials of out blocks 1 and 2 (block 3 follows
-  //            the last product); the next block's operand fragments, into
-  //            the registers the first product finished with at slot 31
-  // No barrier closes a phase: the tail's partial writes are covered by the
-  // barrier in slot 1 of the next phase.
+  //            the last product)
+  // The barrier closing a phase waits for the staging writes but not for the
+  // twelve partial writes; the barrier in slot 1 of the next phase does.
   // Phase P of a pair of phases (P = block parity: LDS buffer P holds this
   // block's operands, gather set P receives the block two ahead, set P ^ 1
   // holds the next block's rows). Returns whether another block follows.
@@ -407,9 +403,11 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
     constexpr int buf = decltype(par)::value;
     const int64_t next = blk + G;
     const bool has_next = next < last;
-    auto read_zf = [&](int t) {  // the next block's fragments
-      zf[t] = *reinterpret_cast<const bf16x8*>(zs[buf ^ 1] + 1024 * t + 16 * (lane ^ ws_key(t)));
+    auto read_zf = [&](int t) {
+      zf[t] = *reinterpret_cast<const bf16x8*>(zs[buf] + 1024 * t + 16 * (lane ^ ws_key(t)));
     };
+    read_zf(0);
+    read_zf(1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
@@ -426,9 +424,8 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
         const f32x16 c = hb > 0 || s > 0 || j == 0 ? y[j] : f32x16{};
         y[j] = ws_mfma(w2f[j][hb][s], hf[hb][s], c);
       }
-      if (i == 1) ws_barrier<0>();
-      if (i == 48) ws_barrier<0>();
-      if (i >= 49 && i <= 56) read_zf(i - 49);
+      if (i >= 2 && i <= 22 && (i + 2) % 4 == 0) read_zf((i + 6) / 4);
+      if (i == 1) ws_barrier<2>();
       if (i >= 29 && i <= 32) {
         const int q = i - 29;
         const f32x4 v = *reinterpret_cast<const f32x4*>(
@@ -456,6 +453,7 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
 #pragma unroll
     for (int q = 0; q < 4; ++q) write_part(buf, 3, q);
     own = y[0];
+    ws_barrier<12>();
     prev = blk;
     blk = next;
     return has_next;
