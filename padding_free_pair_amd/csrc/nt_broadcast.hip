@@ -25,11 +25,9 @@ __device__ __forceinline__ void load_vec(const TI* p, float (&v)[VEC]) {
 }
 
 // Thread (f, cl) owns 16-byte output vector f of every CL-th cell of the
-// workgroup's chunk of CL * kSteps consecutive cells. The thread first
-// decodes its kSteps cells (one search, then incremental steps), then issues
-// all of their a and b loads, then adds and stores: the loads of one thread
-// are all in flight together instead of one cell's at a time. TI is the type
-// of a and b (T, or fp32 projections for a bf16 pair state: the sum is formed
+// workgroup's chunk of CL * kSteps consecutive cells. The cell decode is done
+// once per thread and then advanced by CL cells at a time. TI is the type of
+// a and b (T, or fp32 projections for a bf16 pair state: the sum is formed
 // in fp32 and rounded once, as in the fused transition).
 template <typename TI, typename T>
 __global__ __launch_bounds__(kThreads) void k_broadcast(
@@ -42,49 +40,31 @@ __global__ __launch_bounds__(kThreads) void k_broadcast(
   const int f = tid % G;
   const int cl = tid / G;
   if (cl >= CL) return;
-  const int64_t t0 = (int64_t)blockIdx.x * CL * kSteps + cl;
-  if (t0 >= cells) return;
-  // rows of a and b for the thread's cells (a cell past the end repeats the
-  // last valid one; its store is skipped)
-  int64_t arow[kSteps], brow[kSteps];
-  {
-    Cell x = decode_cell(pair_offsets, single_offsets, col_offsets, col_lengths, B, t0);
-    int64_t end = pair_offsets[x.i + 1];  // first cell past the sample
-    int64_t t = t0;
-#pragma unroll
-    for (int k = 0; k < kSteps; ++k) {
-      arow[k] = x.eta + x.r;
-      brow[k] = x.mu + x.c;
-      if (k + 1 < kSteps && t + CL < cells) {
-        t += CL;
-        x.c += CL;
-        if (x.c >= x.m) {
-          if (x.m > CL && t < end) {  // at most one wrap into the next row
-            x.c -= x.m;
-            x.r += 1;
-          } else {
-            x = decode_cell(pair_offsets, single_offsets, col_offsets, col_lengths, B, t);
-            end = pair_offsets[x.i + 1];
-          }
-        }
-      }
-    }
-  }
+  int64_t t = (int64_t)blockIdx.x * CL * kSteps + cl;
+  if (t >= cells) return;
+  Cell x = decode_cell(pair_offsets, single_offsets, col_offsets, col_lengths, B, t);
+  int64_t end = pair_offsets[x.i + 1];  // first cell past the sample
   const int64_t fo = (int64_t)f * VEC;
-  float va[kSteps][VEC], vb[kSteps][VEC];
 #pragma unroll
   for (int k = 0; k < kSteps; ++k) {
-    load_vec<TI, VEC>(a + arow[k] * c_z + fo, va[k]);
-    load_vec<TI, VEC>(b + brow[k] * c_z + fo, vb[k]);
-  }
+    float va[VEC], vb[VEC];
+    load_vec<TI, VEC>(a + (x.eta + x.r) * c_z + fo, va);
+    load_vec<TI, VEC>(b + (x.mu + x.c) * c_z + fo, vb);
+    Vec16<T> out;
 #pragma unroll
-  for (int k = 0; k < kSteps; ++k) {
-    const int64_t t = t0 + (int64_t)k * CL;
-    if (t < cells) {
-      Vec16<T> out;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) out.set(e, va[k][e] + vb[k][e]);
-      store16(z + t * c_z + fo, out);
+    for (int e = 0; e < VEC; ++e) out.set(e, va[e] + vb[e]);
+    store16(z + t * c_z + fo, out);
+    t += CL;
+    if (k + 1 == kSteps || t >= cells) break;
+    x.c += CL;
+    if (x.c >= x.m) {
+      if (x.m > CL && t < end) {  // at most one wrap into the next row
+        x.c -= x.m;
+        x.r += 1;
+      } else {
+        x = decode_cell(pair_offsets, single_offsets, col_offsets, col_lengths, B, t);
+        end = pair_offsets[x.i + 1];
+      }
     }
   }
 }
