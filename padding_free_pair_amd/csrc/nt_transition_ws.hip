@@ -9,23 +9,24 @@
 //
 // Organisation (c_z = 128, hidden = 512, four waves per workgroup, one
 // workgroup per CU):
-//  * Wave w keeps hidden units 128 w .. 128 w + 127 of both weights in
-//    registers for the whole launch: their W1 rows as the first product's
-//    A fragments (128 VGPRs) and the matching W2 columns as the second's
-//    (128 VGPRs). Nothing is streamed per cell.
+//  * Wave w keeps hidden units 128 w .. 128 w + 127 of both weights in its
+//    accumulation registers (AGPRs) for the whole launch: their W1 rows as
+//    the first product's A fragments (128 registers) and the matching W2
+//    columns as the second's (128 registers). Nothing is streamed per cell.
 //  * Cells move in blocks of 32 (one MFMA column block). For each block every
-//    wave computes its hidden quarter and a partial Y over all 128 outputs;
-//    the four partials meet in LDS, where the wave that owns out block j
-//    (the 32 outputs j + w of wave w's rotation) adds the other three to its
-//    own, which was seeded with the fp32 residual, and stores the result.
+//    wave computes its hidden quarter and a partial Y over all 128 outputs.
+//    Out block j (outputs 32 j .. 32 j + 31) belongs to wave j: the owner's
+//    partial starts from the fp32 residual, the other three waves' partials
+//    reach it through LDS, and the owner adds them, rounds and stores.
 //  * A workgroup walks a contiguous range of blocks, one phase per block.
-//    During the MFMAs of block k a wave also
-//    reduces and stores block k - 1 and stages block k + 1: its threads
-//    gather a[row] and b[col] (eight threads per cell, 64 contiguous bytes
-//    each), form z in fp32 and write both the bf16 operand fragments and the
-//    fp32 residual in the owners' accumulator layout.
-//  * LDS (double-buffered so that one barrier per block suffices): operand
-//    fragments 2 x 8 KiB, residuals 2 x 16 KiB, partials 2 x 48 KiB.
+//    During the MFMAs of block k a wave also sums and stores block k - 1,
+//    stages block k + 1 and gathers the rows of block k + 2: eight threads
+//    per cell load a[row] and b[col] (64 contiguous bytes each), form z in
+//    fp32 and write the bf16 operand fragments and the fp32 residual in the
+//    owners' accumulator layout.
+//  * LDS, double-buffered: operand fragments 2 x 8 KiB, residuals
+//    2 x 16 KiB, partials 2 x 48 KiB. Two barriers per phase (the staging
+//    writes at its end, the partial writes in slot 1 of the next).
 #include "nt_device.hpp"
 #include "nt_internal.hpp"
 
@@ -358,7 +359,6 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
   const int64_t first = range * per;
   const int64_t last = first + per < nblocks ? first + per : nblocks;
   auto clampb = [&](int64_t x) -> int64_t { return x < last ? x : last - 1; };
-  const int64_t G = 1;
   int64_t blk = first;
   dec1(blk);
   dec2(blk);
@@ -368,13 +368,13 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
   gather_b(0);
   stage_half(0, 0, 0);
   stage_half(0, 1, 0);
-  dec1(clampb(blk + G));
-  dec2(clampb(blk + G));
+  dec1(clampb(blk + 1));
+  dec2(clampb(blk + 1));
   dec3();
   dec4();
   gather_a(1);
   gather_b(1);
-  dec1(clampb(blk + 2 * G));
+  dec1(clampb(blk + 2));
   ws_barrier<0>();
 
   // One phase per block: 64 product slots. Slots 0..31 run the first
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
   // holds the next block's rows). Returns whether another block follows.
   auto phase = [&](auto par) -> bool {
     constexpr int buf = decltype(par)::value;
-    const int64_t next = blk + G;
+    const int64_t next = blk + 1;
     const bool has_next = next < last;
     auto read_zf = [&](int t) {
       zf[t] = *reinterpret_cast<const bf16x8*>(zs[buf] + 1024 * t + 16 * (lane ^ ws_key(t)));
@@ -433,12 +433,12 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[0][4 * q + e] = v[e];
       }
-      if (i == 5) dec2(clampb(blk + 2 * G));
+      if (i == 5) dec2(clampb(blk + 2));
       if (i == 9) dec3();
       if (i == 13) dec4();
       if (i == 15) gather_a(buf);
       if (i == 16) gather_b(buf);
-      if (i == 20) dec1(clampb(blk + 3 * G));
+      if (i == 20) dec1(clampb(blk + 3));
       if (i == 44 || i == 46) stage_half(buf ^ 1, (i - 44) / 2, buf ^ 1);
       if (i >= 2 && i <= 22 && (i - 2) % 6 < 3) read_part(buf ^ 1, (i - 2) / 6, (i - 2) % 6 + 1);
       if (i >= 6 && i <= 26 && (i - 6) % 6 < 3) add_part((i - 6) / 6, (i - 6) % 6 + 1);
