@@ -284,6 +284,20 @@ def granularity(x: pin.Inputs, r: PackedRunner, t_seg: float, args, torch, nt) -
             "samples": len(x.lengths)}
 
 
+def step_spread(fn, steps: int, torch) -> dict:
+    """Median and minimum of single steps, from HIP events recorded between
+    `steps` further back-to-back steps (after the timed region, which stays
+    bracketed by synchronisations only)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for k in range(steps):
+        fn()
+        ev[k + 1].record()
+    ev[-1].synchronize()
+    d = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(steps))
+    return {"median": d[len(d) // 2], "min": d[0], "max": d[-1], "steps": steps}
+
+
 def time_steps(fn, steps: int, warmup: int, torch) -> float:
     for _ in range(warmup):
         fn()
@@ -405,22 +419,29 @@ def swiglu_roofline(r: PackedRunner, reps: int) -> dict:
             "frac": flops / t / 1e12 / PEAK_BF16_TFLOPS}
 
 
-def traffic_for(kernel_key: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; otherwise None."""
+def counters_for(kernel_key: str) -> dict:
+    """The committed rocprofv3 counter results of a kernel (HBM bytes per
+    launch, matrix-pipe busy fraction), if they were taken on the current
+    kernel source; otherwise an empty dict."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
-        return None
+        return {}
     with open(path) as f:
         data = json.load(f)
     entry = data.get(kernel_key)
     if not entry or entry.get("kernel") != kernel_key.split(":")[0]:
-        return None
+        return {}
     src = os.path.join(ROOT, "padding_free_pair_amd", "csrc", entry["source"])
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
     if digest != entry.get("source_sha256"):
-        return None
-    return entry.get("bytes_per_launch")
+        return {}
+    return entry
+
+
+def traffic_for(kernel_key: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; otherwise None."""
+    return counters_for(kernel_key).get("bytes_per_launch")
 
 
 def padded_baseline(x: pin.Inputs, steps: int, warmup: int, torch):
@@ -548,6 +569,7 @@ def main():
         t.numel() * t.element_size() for t in (r.z, r.ws, r.part_buf, r.s[0], r.s[1], r.s0))
     value = r.cells * w.blocks / t_step
     log(f"step {t_step * 1e3:.3f} ms -> {value:.4g} cells/s per block")
+    spread = step_spread(r.step, args.steps, torch)
 
     kern = kernel_rooflines(r, args.kernel_reps)
     for k, v in kern.items():
@@ -575,11 +597,14 @@ def main():
     roofline = {"bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
                 "unit": dom["unit"], "frac": dom["frac"],
                 "traffic": traffic_for(f"{transition_kernel_id(w.c_z, w.hidden, w.dtype)}:{w.name}"),
+                "mfma_busy_frac": counters_for(
+                    f"{transition_kernel_id(w.c_z, w.hidden, w.dtype)}:{w.name}").get("mfma_busy_frac"),
                 "kernel": dom["kernel"], "avg_launch_ms": dom["ms"]}
 
     result = {
         "metric": METRIC, "value": value, "unit": "pair cells/s per block", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": t_step * 1e3,
+        "step_ms": spread,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded lengths, N(0,1) singles, "
                                   "N(0,1/fan_in) weights)",
