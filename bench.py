@@ -284,6 +284,25 @@ def granularity(x: pin.Inputs, r: PackedRunner, t_seg: float, args, torch, nt) -
             "samples": len(x.lengths)}
 
 
+def hbm_ceiling(torch) -> dict:
+    """Practical HBM rates on this device, as a reference beside the spec
+    peak (the kernels are graded against the spec): a torch device copy of
+    1 GiB each way and a torch fill of 512 MiB, HIP-event timed."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = time_kernel(lambda: dst.copy_(src), 20, torch)
+    half = dst[: n // 2]
+    t_fill = time_kernel(lambda: half.fill_(2.0), 20, torch)
+    del src, dst, half
+    torch.cuda.empty_cache()
+    copy_gbs = 2 * n * 4 / t_copy / 1e9
+    fill_gbs = n // 2 * 4 / t_fill / 1e9
+    return {"copy_GBps": copy_gbs, "copy_frac": copy_gbs / PEAK_HBM_GBS,
+            "fill_GBps": fill_gbs, "fill_frac": fill_gbs / PEAK_HBM_GBS,
+            "impl": "torch copy_ (1 GiB read + 1 GiB written) and fill_ (512 MiB written)"}
+
+
 def step_spread(fn, steps: int, torch) -> dict:
     """Median and minimum of single steps, from HIP events recorded between
     `steps` further back-to-back steps (after the timed region, which stays
@@ -613,6 +632,7 @@ def main():
                    "T": r.T, "parallelism": "single GPU"},
         "roofline": roofline,
         "kernels": kern,
+        "hbm_ceiling": hbm_ceiling(torch),
         "train": train,
     }
 
