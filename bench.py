@@ -13,6 +13,7 @@ Prints one JSON line; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -463,6 +464,27 @@ def traffic_for(kernel_key: str):
     return counters_for(kernel_key).get("bytes_per_launch")
 
 
+def padded_same_kernels(x: pin.Inputs, steps: int, warmup: int, torch, nt) -> float:
+    """Step time of this library's own kernels over the B x N_max^2 envelope:
+    every sample padded to N_max with zero singles, the same weights. It
+    separates the cost of padding from the choice of kernels. It is a timing
+    baseline only: the kernels have no validity mask, so the padded columns
+    enter the mean."""
+    L = x.lengths.astype(np.int64)
+    B, nmax = len(L), int(L.max())
+    eta = np.concatenate([[0], np.cumsum(L)])
+    s64 = np.zeros((B * nmax, x.c_s))
+    for i in range(B):
+        s64[i * nmax: i * nmax + L[i]] = x.s.f64[eta[i]: eta[i + 1]]
+    env = dataclasses.replace(x, lengths=np.full(B, nmax, dtype=np.int32),
+                              s=pin.store(s64, x.dtype))
+    r = PackedRunner(env, torch, nt)
+    t = time_steps(r.step, steps, warmup, torch)
+    del r
+    torch.cuda.empty_cache()
+    return t
+
+
 def padded_baseline(x: pin.Inputs, steps: int, warmup: int, torch):
     """The same blocks over the B x N_max^2 envelope with PyTorch-native ops
     (zero-padded singles, validity mask, mean over valid columns): the
@@ -645,6 +667,13 @@ def main():
                             "peak_bytes_padded": pad_peak, "peak_bytes_packed": packed_peak,
                             "memory_efficiency": pad_peak / max(packed_peak, 1),
                             "impl": "PyTorch ops over B x N_max^2 (bf16 matmul, masked mean)"}
+        t_env = padded_same_kernels(x, args.steps, args.warmup, torch, nt)
+        log(f"this library's kernels over the envelope: {t_env * 1e3:.3f} ms/step "
+            f"({t_env / t_step:.2f}x the packed step)")
+        result["padded_same_kernels"] = {
+            "ms_per_step": t_env * 1e3, "speedup": t_env / t_step, "envelope_cells": env,
+            "impl": "this library's block over every sample padded to N_max "
+                    "(timing only: no validity mask)"}
         result["granularity"] = granularity(x, r, t_step, args, torch, nt)
         result["rectangular"] = rectangular(x, args, torch, nt)
         result["non_leading"] = non_leading(x, args, torch, nt)
