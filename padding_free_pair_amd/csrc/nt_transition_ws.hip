@@ -166,22 +166,55 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
   }
 
   // ---- stationary weights. Out block j of this wave is (wave + j) mod 4.
+  // A wave's W1 rows are one contiguous 32 KiB run and its W2 columns 128
+  // rows of 256 contiguous bytes, but a fragment takes 16 bytes from each of
+  // 32 rows. So each part is fetched with whole-row loads (a wave load covers
+  // four 256-byte rows), written to a wave-private LDS region with the 16-byte
+  // piece index XORed by the row's low four bits, and read back in fragment
+  // order; both the writes and the fragment reads are then conflict-free.
+  // The region lies in the partial and residual buffers, which are not yet
+  // in use; the barrier below separates it from the first staging.
   bf16x8 w1f[4][KT];    // [hidden block][k-step]
   bf16x8 w2f[4][4][2];  // [rotation j][hidden block][k-step within the block]
+  {
+    unsigned char* const wscr = wave < 3 ? &ps[0][0][0][0] + 32768 * wave : &rs[0][0];
+    const int prow = lane >> 4, piece = lane & 15;
+    auto scr = [&](int row, int pc) -> bf16x8* {
+      return reinterpret_cast<bf16x8*>(wscr + 256 * row + 16 * (pc ^ (row & 15)));
+    };
+    const bf16* w1src = W1 + (int64_t)128 * wave * CZ;
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb)
+    for (int i0 = 0; i0 < 32; i0 += 16) {
+      bf16x8 tmp[16];
 #pragma unroll
-    for (int t = 0; t < KT; ++t)
-      w1f[hb][t] = load16(W1 + (int64_t)(128 * wave + 32 * hb + ws_perm(n)) * CZ + 16 * t + 8 * h).v;
+      for (int k = 0; k < 16; ++k)
+        tmp[k] = load16(w1src + (int64_t)(4 * (i0 + k) + prow) * CZ + 8 * piece).v;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ob = (wave + j) & 3;
+      for (int k = 0; k < 16; ++k) *scr(4 * (i0 + k) + prow, piece) = tmp[k];
+    }
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-        w2f[j][hb][s] = load16(W2 + (int64_t)(32 * ob + ws_perm(n)) * HID + 128 * wave + 32 * hb +
-                               16 * s + 8 * h).v;
+      for (int t = 0; t < KT; ++t) w1f[hb][t] = *scr(32 * hb + ws_perm(n), 2 * t + h);
+    const bf16* w2src = W2 + 128 * wave;
+#pragma unroll
+    for (int i0 = 0; i0 < 32; i0 += 16) {
+      bf16x8 tmp[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        tmp[k] = load16(w2src + (int64_t)(4 * (i0 + k) + prow) * HID + 8 * piece).v;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) *scr(4 * (i0 + k) + prow, piece) = tmp[k];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ob = (wave + j) & 3;
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          w2f[j][hb][s] = *scr(32 * ob + ws_perm(n), 4 * hb + 2 * s + h);
+    }
   }
   // The products read the weights straight from accumulation registers
   // (AGPRs), which leaves the VGPRs to accumulators, operands and staging.
