@@ -318,6 +318,21 @@ def step_spread(fn, steps: int, torch) -> dict:
     return {"median": d[len(d) // 2], "min": d[0], "max": d[-1], "steps": steps}
 
 
+def settle(fn, ms: float, torch) -> int:
+    """Repeat fn for `ms` milliseconds of wall time (untimed), so that the
+    timed steps and kernel timings see the clocks a GPU holds under sustained
+    load: over the first few hundred milliseconds of work they are still
+    rising, and a kernel runs up to 20% slower. Returns the number of calls."""
+    n = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(10):
+            fn()
+        n += 10
+        torch.cuda.synchronize()
+    return n
+
+
 def time_steps(fn, steps: int, warmup: int, torch) -> float:
     for _ in range(warmup):
         fn()
@@ -343,6 +358,26 @@ def time_kernel(fn, reps: int, torch) -> float:
     end.record()
     end.synchronize()
     return start.elapsed_time(end) / 1e3 / reps
+
+
+def time_kernel_in_steps(fn, step, reps: int, torch) -> float:
+    """Average duration (s) of fn's launches when each is followed by a whole
+    step, as the kernel runs inside the hot path, from HIP events recorded on
+    the current stream right before and after it. Back to back, an MFMA-bound
+    kernel draws power without pause and the clocks sag after a few launches;
+    in steps the memory-bound kernels between its launches leave headroom."""
+    for _ in range(5):
+        fn()
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+    for k in range(reps):
+        ev[2 * k].record()
+        fn()
+        ev[2 * k + 1].record()
+        step()
+    ev[-1].synchronize()
+    return sum(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(reps)) / 1e3 / reps
 
 
 def transition_kernel_id(c_z: int, hidden: int, dtype: str) -> str:
@@ -384,8 +419,10 @@ def kernel_rooflines(r: PackedRunner, reps: int):
     zt = torch.empty_like(r.z)
     out = {}
 
-    t = time_kernel(lambda: nt.nt_pair_broadcast_transition(r.p, a32, b32, w["W1"], w["W2"],
-                                                            z_out=r.z), reps, torch)
+    def fused():
+        nt.nt_pair_broadcast_transition(r.p, a32, b32, w["W1"], w["W2"], z_out=r.z)
+    t_b2b = time_kernel(fused, reps, torch)
+    t = time_kernel_in_steps(fused, r.step, reps, torch)
     flops = 4.0 * cz * hd * cells
     nbytes = cells * cz * es + 2 * T * cz * 4 + 2 * hd * cz * es
     peak_f = PEAK_BF16_TFLOPS if x.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -395,12 +432,14 @@ def kernel_rooflines(r: PackedRunner, reps: int):
         out["transition"] = {"kernel": label,
                              "bound": "mfma", "ms": t * 1e3, "achieved": flops / t / 1e12,
                              "peak": peak_f, "unit": "TFLOP/s", "flop_per_launch": flops,
-                             "bytes_per_launch": nbytes}
+                             "bytes_per_launch": nbytes, "timing": "in steps",
+                             "back_to_back_ms": t_b2b * 1e3}
     else:
         out["transition"] = {"kernel": label,
                              "bound": "hbm", "ms": t * 1e3, "achieved": nbytes / t / 1e9,
                              "peak": PEAK_HBM_GBS, "unit": "GB/s", "flop_per_launch": flops,
-                             "bytes_per_launch": nbytes}
+                             "bytes_per_launch": nbytes, "timing": "in steps",
+                             "back_to_back_ms": t_b2b * 1e3}
     t = time_kernel(lambda: nt.nt_pair_broadcast(r.p, a, b, z=zt), reps, torch)
     nbytes = cells * cz * es + 2 * T * cz * es
     out["broadcast"] = {"kernel": "k_broadcast", "bound": "hbm", "ms": t * 1e3,
@@ -562,6 +601,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--kernel-reps", type=int, default=100)
+    ap.add_argument("--settle-ms", type=float, default=1000.0,
+                    help="untimed steps for this long before the warm-up steps, until the "
+                         "GPU clocks have settled under load")
     ap.add_argument("--quick", action="store_true",
                     help="timed steps and kernel timings only (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -605,6 +647,7 @@ def main():
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     base_mem = torch.cuda.memory_allocated()
+    settle_calls = settle(r.step, args.settle_ms, torch)
     t_step = time_steps(r.step, args.steps, args.warmup, torch)
     packed_peak = torch.cuda.max_memory_allocated() - base_mem + sum(
         t.numel() * t.element_size() for t in (r.z, r.ws, r.part_buf, r.s[0], r.s[1], r.s0))
@@ -614,6 +657,8 @@ def main():
 
     kern = kernel_rooflines(r, args.kernel_reps)
     for k, v in kern.items():
+        if "back_to_back_ms" in v:
+            log(f"kernel {k} back to back: {v['back_to_back_ms'] * 1e3:.1f} us")
         log(f"kernel {k}: {v['ms'] * 1e3:.1f} us, {v['achieved']:.1f} {v['unit']} "
             f"({100 * v['frac']:.1f}% of peak)")
     if x.dtype == "bf16" and x.c_z in (64, 128) and x.hidden % 32 == 0:
@@ -640,11 +685,15 @@ def main():
                 "traffic": traffic_for(f"{transition_kernel_id(w.c_z, w.hidden, w.dtype)}:{w.name}"),
                 "mfma_busy_frac": counters_for(
                     f"{transition_kernel_id(w.c_z, w.hidden, w.dtype)}:{w.name}").get("mfma_busy_frac"),
-                "kernel": dom["kernel"], "avg_launch_ms": dom["ms"]}
+                "kernel": dom["kernel"], "avg_launch_ms": dom["ms"],
+                "timing": "HIP events around each launch, every launch followed by a whole step",
+                "back_to_back_ms": dom.get("back_to_back_ms")}
 
     result = {
         "metric": METRIC, "value": value, "unit": "pair cells/s per block", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": t_step * 1e3,
+        "settle": {"ms": args.settle_ms, "steps": settle_calls,
+                   "why": "untimed steps before the warm-up steps, until the clocks settle"},
         "step_ms": spread,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded lengths, N(0,1) singles, "
@@ -684,6 +733,7 @@ def main():
             log(f"regime {other.name}")
             xo = pin.workload_inputs(other.index)
             ro = PackedRunner(xo, torch, nt)
+            settle(ro.step, args.settle_ms / 2, torch)  # the GPU idled while inputs were drawn
             to = time_steps(ro.step, args.steps, args.warmup, torch)
             ko = kernel_rooflines(ro, args.kernel_reps)
             regimes[other.name] = {
