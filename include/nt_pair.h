@@ -262,6 +262,38 @@ nt_status nt_pair_block(const nt_partition* p, const void* s_in, void* s_out, vo
                         nt_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Workspace bytes nt_pair_chain needs: the block's, plus one [T, c_s] buffer
+ * of singles (in `dtype`) when nblocks >= 2.
+ */
+nt_status nt_chain_workspace_bytes(const nt_partition* p, int32_t nblocks, int32_t c_s,
+                                   int32_t c_z, int32_t hidden, nt_dtype dtype, size_t* bytes);
+
+/*
+ * nblocks blocks in sequence (Section 4.3, "A larger pair application": the
+ * singles of each block feed the next, whose pair state is rebuilt from
+ * them). w points to nblocks weight sets in host memory; the weights
+ * themselves are on the device. s_out [T, c_s] receives the last block's
+ * singles, z_out [cells, c_z] the last block's pair state (every block
+ * writes it in turn). s_out may equal s_in. Square partitions only.
+ * By default the blocks run nt_pair_block's launches in turn, and the
+ * results are those of chained nt_pair_block calls. With the environment
+ * variable NT_CHAIN_BOUNDARY=fused, one launch between two blocks forms
+ * s~ = s + m Wo^T (rounded once to `dtype`) and the next block's a and b
+ * from the same rows (bf16, c_s = 384 with c_z = 128, or c_s = c_z = 64;
+ * other shapes keep the separate launches). Each row is still computed from
+ * itself alone, so results do not depend on the rest of the batch; they may
+ * differ from chained nt_pair_block calls in the last bits of a and b
+ * (another summation order).
+ * workspace: device, at least nt_chain_workspace_bytes, 16-byte aligned,
+ * disjoint from every other array. Errors as nt_pair_block; nothing is
+ * launched when a check fails.
+ */
+nt_status nt_pair_chain(const nt_partition* p, const void* s_in, void* s_out, void* z_out,
+                        const nt_block_weights* w, int32_t nblocks, int32_t c_s, int32_t c_z,
+                        int32_t hidden, nt_dtype dtype, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
  * The rectangular block (Appendix A.1's rectangular variant of Equation 1):
  * pair rows are built from s_rows [T, c_s], pair columns from s_cols
  * [T_cols, c_s]: a = s_rows Wa^T, b = s_cols Wb^T, z~ = transition(a[row] +

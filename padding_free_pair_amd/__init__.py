@@ -22,7 +22,8 @@ __all__ = ["NtError", "Partition", "nt_partition_sizes", "nt_make_partition",
            "nt_decode_cells",
            "nt_pair_broadcast", "nt_pair_transition", "nt_pair_broadcast_transition",
            "nt_pair_transition_swiglu", "nt_pair_reduce",
-           "nt_block_workspace_bytes", "nt_pair_block", "nt_last_error", "nt_version",
+           "nt_block_workspace_bytes", "nt_pair_block", "nt_chain_workspace_bytes",
+           "nt_pair_chain", "nt_last_error", "nt_version",
            "NT_F32", "NT_BF16"]
 
 
@@ -323,6 +324,48 @@ def nt_pair_block(p: Partition, s_in, weights, s_out=None, z_out=None, workspace
                                        _ptr(z_out), ctypes.byref(wst), c_s, c_z, hidden,
                                        _dtype_code(s_in), _ptr(workspace),
                                        workspace.numel(), _stream(stream, s_in.device)))
+    return s_out, z_out
+
+
+def nt_chain_workspace_bytes(p: Partition, nblocks: int, c_s: int, c_z: int, hidden: int,
+                             dtype) -> int:
+    n = ctypes.c_size_t()
+    code = dtype if isinstance(dtype, int) else (NT_BF16 if "bfloat16" in str(dtype) else NT_F32)
+    _check(_native.lib().nt_chain_workspace_bytes(ctypes.byref(p.struct), nblocks, c_s, c_z,
+                                                  hidden, code, ctypes.byref(n)))
+    return n.value
+
+
+def nt_pair_chain(p: Partition, s_in, weights, s_out=None, z_out=None, workspace=None,
+                  stream=None):
+    """Blocks in sequence in one call; returns (s_out, z_out) of the last block.
+
+    weights: a list with one entry per block, each as nt_pair_block takes it.
+    """
+    torch = _torch()
+    sets = []
+    for wk in weights:
+        if isinstance(wk, dict):
+            wk = [wk[k] for k in ("Wa", "Wb", "W1", "W2", "Wo")]
+        for w in wk:
+            if w.dtype != s_in.dtype:
+                raise TypeError("weights must share s_in's dtype")
+        sets.append(list(wk))
+    if not sets:
+        raise ValueError("at least one block")
+    c_s, c_z, hidden = s_in.shape[-1], sets[0][0].shape[0], sets[0][2].shape[0]
+    if s_out is None:
+        s_out = torch.empty_like(s_in)
+    if z_out is None:
+        z_out = torch.empty((p.cells, c_z), dtype=s_in.dtype, device=s_in.device)
+    need = nt_chain_workspace_bytes(p, len(sets), c_s, c_z, hidden, _dtype_code(s_in))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=s_in.device)
+    arr = (NtBlockWeights * len(sets))(*[NtBlockWeights(*[_ptr(w) for w in wk]) for wk in sets])
+    _check(_native.lib().nt_pair_chain(ctypes.byref(p.struct), _ptr(s_in), _ptr(s_out),
+                                       _ptr(z_out), arr, len(sets), c_s, c_z, hidden,
+                                       _dtype_code(s_in), _ptr(workspace), workspace.numel(),
+                                       _stream(stream, s_in.device)))
     return s_out, z_out
 
 

@@ -5,6 +5,7 @@
 
 #include <climits>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -656,6 +657,126 @@ nt_status nt_pair_block(const nt_partition* p, const void* s_in, void* s_out, vo
     return fail(NT_ERR_INVALID, "rectangular partition: use nt_pair_block_rect");
   return pair_block(p, s_in, s_in, s_out, z_out, w, c_s, c_z, hidden, dtype, workspace,
                     workspace_bytes, stream);
+}
+
+// Chain workspace: the block's, then (for two or more blocks) one bf16/fp32
+// buffer of T x c_s singles that the chain alternates with s_out.
+static uint64_t chain_workspace(const nt_partition* p, int32_t nblocks, int32_t c_s, int32_t c_z,
+                         nt_dtype dtype) {
+  const uint64_t blk = block_workspace(p->T, p->T_cols, c_z, dtype).total;
+  return blk + (nblocks > 1 ? nt::align256((size_t)p->T * c_s * esize(dtype)) : 0);
+}
+
+nt_status nt_chain_workspace_bytes(const nt_partition* p, int32_t nblocks, int32_t c_s,
+                                   int32_t c_z, int32_t hidden, nt_dtype dtype, size_t* bytes) {
+  NT_TRY(check_partition(p));
+  NT_TRY(check_dtype(dtype));
+  NT_TRY(check_width("c_s", c_s, nt::kMaxCs));
+  NT_TRY(check_width("c_z", c_z, nt::kMaxCz));
+  NT_TRY(check_width("hidden", hidden, nt::kMaxHidden));
+  if (nblocks < 1) return fail(NT_ERR_INVALID, "nblocks = %d must be at least 1", (int)nblocks);
+  if (!bytes) return fail(NT_ERR_NULL, "bytes is NULL");
+  *bytes = chain_workspace(p, nblocks, c_s, c_z, dtype);
+  return ok();
+}
+
+nt_status nt_pair_chain(const nt_partition* p, const void* s_in, void* s_out, void* z_out,
+                        const nt_block_weights* w, int32_t nblocks, int32_t c_s, int32_t c_z,
+                        int32_t hidden, nt_dtype dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  NT_TRY(check_partition(p));
+  NT_TRY(check_dtype(dtype));
+  NT_TRY(check_width("c_s", c_s, nt::kMaxCs));
+  NT_TRY(check_width("c_z", c_z, nt::kMaxCz));
+  NT_TRY(check_width("hidden", hidden, nt::kMaxHidden));
+  if (p->col_offsets != p->single_offsets)
+    return fail(NT_ERR_INVALID, "rectangular partition: chain nt_pair_block_rect calls");
+  if (nblocks < 1) return fail(NT_ERR_INVALID, "nblocks = %d must be at least 1", (int)nblocks);
+  if (!w) return fail(NT_ERR_NULL, "weights is NULL");
+  const size_t es = esize(dtype);
+  const uint64_t sbytes = (uint64_t)p->T * c_s * es;
+  const uint64_t pair = (uint64_t)p->cells * c_z * es;
+  const uint64_t proj = (uint64_t)c_z * c_s * es;
+  const uint64_t mlp = (uint64_t)c_z * hidden * es;
+  const uint64_t blk = block_workspace(p->T, p->T_cols, c_z, dtype).total;
+  const uint64_t need = chain_workspace(p, nblocks, c_s, c_z, dtype);
+  NT_TRY(check_array("s_in", s_in, sbytes));
+  NT_TRY(check_array("s_out", s_out, sbytes));
+  NT_TRY(check_array("z_out", z_out, pair));
+  if (need > 0) {
+    NT_TRY(check_array("workspace", workspace, need));
+    if (workspace_bytes < need)
+      return fail(NT_ERR_WORKSPACE, "workspace has %zu bytes, needs %llu", workspace_bytes,
+                  (unsigned long long)need);
+  }
+  if (s_in != s_out && overlaps(s_in, sbytes, s_out, sbytes))
+    return fail(NT_ERR_INVALID, "s_out partially overlaps s_in");
+  const void* outs[] = {s_out, z_out, workspace};
+  const uint64_t outsz[] = {sbytes, pair, need};
+  for (int k = 0; k < nblocks; ++k) {
+    const nt_block_weights& wk = w[k];
+    const void* wp[] = {wk.Wa, wk.Wb, wk.W1, wk.W2, wk.Wo};
+    const uint64_t wsz[] = {proj, proj, mlp, mlp, proj};
+    static const char* const names[] = {"Wa", "Wb", "W1", "W2", "Wo"};
+    for (int q = 0; q < 5; ++q) {
+      NT_TRY(check_array(names[q], wp[q], wsz[q]));
+      for (int o = 0; o < 3; ++o)
+        if (overlaps(outs[o], outsz[o], wp[q], wsz[q]))
+          return fail(NT_ERR_INVALID, "block %d's %s overlaps an output or the workspace", k,
+                      names[q]);
+    }
+  }
+  if (overlaps(z_out, pair, s_in, sbytes) || overlaps(z_out, pair, s_out, sbytes) ||
+      overlaps(workspace, need, s_in, sbytes) || overlaps(workspace, need, s_out, sbytes) ||
+      overlaps(workspace, need, z_out, pair))
+    return fail(NT_ERR_INVALID, "z_out, the singles and the workspace must not overlap");
+  if (p->T == 0) return ok();
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
+  void* sbuf = base + blk;
+  // block k writes s_out when nblocks - 1 - k is even, else the workspace
+  // buffer, so that the last block writes s_out
+  auto dest = [&](int k) -> void* { return (nblocks - 1 - k) % 2 == 0 ? s_out : sbuf; };
+  // The fused boundary (one launch for block k's output projection and block
+  // k + 1's projections) is taken on request only: it measured slower than
+  // the two launches it replaces (0.540 against 0.524 ms per four-block step
+  // on the high-variation batch).
+  const char* boundary = getenv("NT_CHAIN_BOUNDARY");
+  const bool fused = boundary && strcmp(boundary, "fused") == 0;
+  if (nblocks == 1 || !fused || !nt::out_then_ab_supported(c_s, c_z, dtype)) {
+    const void* cur = s_in;
+    for (int k = 0; k < nblocks; ++k) {
+      NT_TRY(pair_block(p, cur, cur, dest(k), z_out, &w[k], c_s, c_z, hidden, dtype, workspace,
+                        blk, stream));
+      cur = dest(k);
+    }
+    return ok();
+  }
+  const BlockWorkspace ws = block_workspace(p->T, p->T_cols, c_z, dtype);
+  float* a = reinterpret_cast<float*>(base + ws.a);
+  float* b = reinterpret_cast<float*>(base + ws.b);
+  float* m = reinterpret_cast<float*>(base + ws.m);
+  NT_TRY(hip_status(nt::launch_linear2(s_in, dtype, w[0].Wa, w[0].Wb, a, b, p->T, c_z, c_s, s),
+                    "projections a, b"));
+  const void* cur = s_in;
+  for (int k = 0; k < nblocks; ++k) {
+    NT_TRY(hip_status(nt::launch_transition(*p, nullptr, a, b, z_out, w[k].W1, w[k].W2, c_z,
+                                            hidden, dtype, s),
+                      "fused broadcast + transition"));
+    NT_TRY(hip_status(nt::launch_reduce(*p, z_out, m, c_z, dtype, s), "column mean"));
+    if (k + 1 < nblocks) {
+      NT_TRY(hip_status(nt::launch_out_then_ab(m, w[k].Wo, cur, dest(k), w[k + 1].Wa,
+                                               w[k + 1].Wb, a, b, p->T, c_s, c_z, s),
+                        "output projection + next projections"));
+    } else {
+      NT_TRY(hip_status(nt::launch_linear(m, NT_F32, w[k].Wo, dtype, cur, dest(k), dtype, p->T,
+                                          c_s, c_z, s),
+                        "output projection"));
+    }
+    cur = dest(k);
+  }
+  return ok();
 }
 
 nt_status nt_pair_block_rect(const nt_partition* p, const void* s_rows, const void* s_cols,

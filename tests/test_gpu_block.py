@@ -169,3 +169,127 @@ def test_per_sample_launches_match_segmented(nt, idx):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bits(s_ps, torch), bits(s_seg, torch))
     np.testing.assert_array_equal(bits(z_ps, torch), bits(z_seg, torch))
+
+
+# ---------------------------------------------------------------- nt_pair_chain
+@pytest.mark.parametrize("lengths,c_s,c_z,hidden,dtype,blocks", [
+    ([3, 0, 17, 40, 1, 33], 384, 128, 512, "bf16", 3),  # fused block boundaries
+    ([5, 20, 0, 9], 64, 64, 128, "bf16", 2),              # fused, the other shape
+    ([6, 2, 11], 48, 24, 40, "bf16", 2),                  # blocks launched in turn
+    ([7, 12, 5], 16, 8, 16, "f32", 3),                    # fp32: blocks in turn
+    ([4], 384, 128, 512, "bf16", 1),                      # one block
+])
+@pytest.mark.parametrize("boundary", ["default", "fused"])
+def test_chain_matches_oracle(nt, monkeypatch, boundary, lengths, c_s, c_z, hidden, dtype,
+                              blocks):
+    _boundary(monkeypatch, boundary)
+    announce(f"chain {boundary} {dtype} {lengths} c_s={c_s} c_z={c_z} h={hidden} "
+             f"blocks={blocks}")
+    x = pin.make_inputs(lengths, c_s, c_z, hidden, dtype, blocks=blocks, seed=23)
+    p = nt.nt_make_partition(lengths)
+    s_out, z_out = nt.nt_pair_chain(p, to_dev(x.s, torch),
+                                    [weights_to_dev(wk, torch) for wk in x.weights])
+    torch.cuda.synchronize()
+    ref_s, ref_z = oracle.chain(lengths, x.s.f64, [_w64(wk) for wk in x.weights])
+    ez = scaled_max_err(f64(z_out, torch), ref_z)
+    es = scaled_max_err(f64(s_out, torch), ref_s)
+    announce(f"errors z={ez:.3e} s={es:.3e}")
+    assert ez <= TOL[dtype] and es <= TOL[dtype]
+
+
+def _boundary(monkeypatch, boundary):
+    if boundary == "fused":
+        monkeypatch.setenv("NT_CHAIN_BOUNDARY", "fused")
+    else:
+        monkeypatch.delenv("NT_CHAIN_BOUNDARY", raising=False)
+
+
+def _block_loop(nt, p, s, ws, z):
+    for w in ws:
+        s_next = torch.empty_like(s)
+        nt.nt_pair_block(p, s, w, s_out=s_next, z_out=z)
+        s = s_next
+    return s
+
+
+@pytest.mark.parametrize("boundary", ["default", "fused"])
+@pytest.mark.parametrize("idx", [3, 4])
+def test_chain_full_size_matches_block_loop(nt, monkeypatch, boundary, idx):
+    """The chain at full size against the same blocks called one by one (each
+    of which the per-block test holds to the oracle): bit for bit by default;
+    the fused boundary sums the projections in another order, so there the
+    two agree to the bf16 tolerance."""
+    _boundary(monkeypatch, boundary)
+    x = pin.workload_inputs(idx)
+    L = x.lengths.tolist()
+    announce(f"chain vs block loop {x.name}")
+    p = nt.nt_make_partition(L)
+    ws = [weights_to_dev(wk, torch) for wk in x.weights]
+    s0 = to_dev(x.s, torch)
+    z_loop = torch.empty((p.cells, x.c_z), dtype=torch.bfloat16, device="cuda")
+    s_loop = _block_loop(nt, p, s0, ws, z_loop)
+    s_ch, z_ch = nt.nt_pair_chain(p, s0, ws)
+    torch.cuda.synchronize()
+    es = scaled_max_err(f64(s_ch, torch), f64(s_loop, torch))
+    ez = scaled_max_err(f64(z_ch, torch), f64(z_loop, torch))
+    announce(f"chain vs loop: s {es:.3e} z {ez:.3e}")
+    assert es <= TOL["bf16"] and ez <= TOL["bf16"]
+    if boundary == "default":
+        np.testing.assert_array_equal(bits(s_ch, torch), bits(s_loop, torch))
+        np.testing.assert_array_equal(bits(z_ch, torch), bits(z_loop, torch))
+
+
+def test_chain_one_block_is_the_block(nt):
+    x = pin.make_inputs([9, 30, 2], 384, 128, 512, "bf16", seed=5)
+    p = nt.nt_make_partition([9, 30, 2])
+    s0, w = to_dev(x.s, torch), weights_to_dev(x.weights[0], torch)
+    s_b, z_b = nt.nt_pair_block(p, s0, w)
+    s_c, z_c = nt.nt_pair_chain(p, s0, [w])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(s_c, torch), bits(s_b, torch))
+    np.testing.assert_array_equal(bits(z_c, torch), bits(z_b, torch))
+
+
+@pytest.mark.parametrize("boundary", ["default", "fused"])
+def test_chain_in_place(nt, monkeypatch, boundary):
+    """s_out may be s_in: every row is read before it is written."""
+    _boundary(monkeypatch, boundary)
+    L = [13, 1, 64, 0, 27]
+    x = pin.make_inputs(L, 384, 128, 512, "bf16", blocks=4, seed=8)
+    p = nt.nt_make_partition(L)
+    ws = [weights_to_dev(wk, torch) for wk in x.weights]
+    s0 = to_dev(x.s, torch)
+    s_ref, z_ref = nt.nt_pair_chain(p, s0, ws)
+    s_io = s0.clone()
+    _, z_io = nt.nt_pair_chain(p, s_io, ws, s_out=s_io)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(s_io, torch), bits(s_ref, torch))
+    np.testing.assert_array_equal(bits(z_io, torch), bits(z_ref, torch))
+
+
+@pytest.mark.parametrize("boundary", ["default", "fused"])
+@pytest.mark.parametrize("idx", [3])
+def test_chain_per_sample_matches_segmented(nt, monkeypatch, boundary, idx):
+    """The chain run on each sample alone gives the bits of the batched chain:
+    either boundary computes every row from that row only."""
+    _boundary(monkeypatch, boundary)
+    x = pin.workload_inputs(idx)
+    L = [int(n) for n in x.lengths]
+    announce(f"chain per-sample vs segmented {x.name}")
+    ws = [weights_to_dev(wk, torch) for wk in x.weights]
+    p = nt.nt_make_partition(L)
+    s0 = to_dev(x.s, torch)
+    s_seg, z_seg = nt.nt_pair_chain(p, s0, ws)
+    eta = np.concatenate([[0], np.cumsum(L)])
+    o = np.concatenate([[0], np.cumsum(np.square(np.asarray(L, dtype=np.int64)))])
+    s_ps = torch.empty_like(s_seg)
+    z_ps = torch.empty_like(z_seg)
+    for i, n in enumerate(L):
+        if n == 0:
+            continue
+        e0, e1, o0, o1 = int(eta[i]), int(eta[i + 1]), int(o[i]), int(o[i + 1])
+        nt.nt_pair_chain(nt.nt_make_partition([n]), s0[e0:e1], ws, s_out=s_ps[e0:e1],
+                         z_out=z_ps[o0:o1])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(s_ps, torch), bits(s_seg, torch))
+    np.testing.assert_array_equal(bits(z_ps, torch), bits(z_seg, torch))
