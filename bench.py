@@ -63,10 +63,25 @@ class PackedRunner:
         self.ws = torch.empty(max(nt.nt_block_workspace_bytes(self.p, x.c_s, x.c_z, x.hidden, tdt),
                                   1), dtype=torch.uint8, device="cuda")
         self.w = [{k: dev(v, torch) for k, v in wk.items()} for wk in x.weights]
+        # the blocks through one nt_pair_chain call instead of one call each
+        self.chain = False
+        self.chain_ws = None
+
+    def use_chain(self):
+        x, torch, nt = self.x, self.torch, self.nt
+        tdt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+        self.chain_ws = self.torch.empty(max(nt.nt_chain_workspace_bytes(
+            self.p, len(self.w), x.c_s, x.c_z, x.hidden, tdt), 1), dtype=torch.uint8,
+            device="cuda")
+        self.chain = True
 
     def step(self):
         nt = self.nt
         p = nt.nt_make_partition(self.lengths, buffer=self.part_buf)
+        if self.chain:
+            nt.nt_pair_chain(p, self.s0, self.w, s_out=self.s[1], z_out=self.z,
+                             workspace=self.chain_ws)
+            return self.s[1], self.z
         s_in = self.s0
         for k, w in enumerate(self.w):
             s_out = self.s[k % 2]
@@ -607,6 +622,9 @@ def main():
     ap.add_argument("--quick", action="store_true",
                     help="timed steps and kernel timings only (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chain", action="store_true",
+                    help="run each step's blocks through one nt_pair_chain call (with "
+                         "NT_CHAIN_BOUNDARY=fused: the fused block boundary)")
     ap.add_argument("--copy-reference", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -644,6 +662,8 @@ def main():
     log(f"workload {w.name}: B={w.B} cells={int((x.lengths.astype(np.int64) ** 2).sum())} "
         f"blocks={w.blocks}")
     r = PackedRunner(x, torch, nt)
+    if args.chain:
+        r.use_chain()
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     base_mem = torch.cuda.memory_allocated()
@@ -700,7 +720,8 @@ def main():
                                   "N(0,1/fan_in) weights)",
         "config": {"workload": w.name, "B": w.B, "lengths": x.lengths.tolist(), "c_s": w.c_s,
                    "c_z": w.c_z, "hidden": w.hidden, "blocks": w.blocks, "cells": r.cells,
-                   "T": r.T, "parallelism": "single GPU"},
+                   "T": r.T, "parallelism": "single GPU",
+                   "blocks_via": "nt_pair_chain" if args.chain else "nt_pair_block"},
         "roofline": roofline,
         "kernels": kern,
         "hbm_ceiling": hbm_ceiling(torch),
