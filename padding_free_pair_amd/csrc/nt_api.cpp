@@ -740,7 +740,7 @@ nt_status nt_pair_chain(const nt_partition* p, const void* s_in, void* s_out, vo
   auto dest = [&](int k) -> void* { return (nblocks - 1 - k) % 2 == 0 ? s_out : sbuf; };
   // The fused boundary (one launch for block k's output projection and block
   // k + 1's projections) is taken on request only: it measured slower than
-  // the two launches it replaces (0.540 against 0.524 ms per four-block step
+  // the two launches it replaces (0.537 against 0.522 ms per four-block step
   // on the high-variation batch).
   const char* boundary = getenv("NT_CHAIN_BOUNDARY");
   const bool fused = boundary && strcmp(boundary, "fused") == 0;

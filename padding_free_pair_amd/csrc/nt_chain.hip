@@ -9,9 +9,9 @@
 // Every row is computed from that row alone, so results do not depend on the
 // other samples of the batch. One launch replaces the output projection and
 // the next block's a/b projection; s~ goes from registers to LDS and feeds
-// the second product without a round trip through HBM. Workgroup (x, y) takes
-// row tile x and column group y of [a | b]; the first product is repeated by
-// the groups of a row tile (it is the smaller one).
+// the second product without a round trip through HBM. One workgroup of
+// sixteen waves per row tile: the waves split the first product's column
+// tiles, then each takes one 16-column tile of [a | b].
 #include "nt_device.hpp"
 #include "nt_internal.hpp"
 
@@ -24,19 +24,22 @@ __device__ __forceinline__ f32x4 mma16(const bf16x8& a, const bf16x8& b, const f
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Four waves. Lane (l16, g): l16 is a row of the A operand / a column of the
+// Sixteen waves. Lane (l16, g): l16 is a row of the A operand / a column of the
 // B operand, g picks 8 of the 32 k of a step; accumulator element e is row
 // 4 g + e, column l16 of the 16 x 16 result.
+constexpr int kWaves = 16;
+
 template <int CS, int CZ>
-__global__ __launch_bounds__(256) void k_out_then_ab(
+__global__ __launch_bounds__(64 * kWaves) void k_out_then_ab(
     const float* __restrict__ m, const bf16* __restrict__ Wo, const bf16* s_res, bf16* s_new,
     const bf16* __restrict__ Wa, const bf16* __restrict__ Wb, float* __restrict__ a,
     float* __restrict__ b, int64_t M) {
   constexpr int KS1 = CZ / 32;         // k-steps of s~ = s + m Wo^T
-  constexpr int NJ1 = CS / 64;         // 16-column tiles of s~ per wave
+  constexpr int NT1 = CS / 16;         // 16-column tiles of s~
+  constexpr int NJ1 = (NT1 + kWaves - 1) / kWaves;  // per wave, the last ones partly idle
   constexpr int KS2 = CS / 32;         // k-steps of a, b
   constexpr int LD = CS + 8;           // LDS row stride of s~ (bf16): 16 B of padding
-  static_assert(CS % 64 == 0 && CZ % 32 == 0, "every wave takes whole 16-column tiles");
+  static_assert(CS % 32 == 0 && CZ % 32 == 0 && 2 * CZ / 16 <= kWaves, "tile counts");
   __shared__ __align__(16) bf16 st[kRows * LD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -44,7 +47,7 @@ __global__ __launch_bounds__(256) void k_out_then_ab(
   const int64_t r0 = (int64_t)blockIdx.x * kRows;
   const bool row_ok = r0 + l16 < M;
 
-  // ---- s~ = s + m Wo^T for columns 16 j .. 16 j + 15, j = wave + 4 i
+  // ---- s~ = s + m Wo^T for columns 16 j .. 16 j + 15, j = wave + 16 i
   bf16x8 mh[KS1], ml[KS1];
   {
     const float* mrow = m + (row_ok ? r0 + l16 : 0) * CZ + 8 * g;
@@ -69,7 +72,8 @@ __global__ __launch_bounds__(256) void k_out_then_ab(
   float res[NJ1][4];
 #pragma unroll
   for (int i = 0; i < NJ1; ++i) {
-    const int col = 16 * (wave + 4 * i) + l16;
+    const int j = wave + kWaves * i;
+    const int col = 16 * (j < NT1 ? j : 0) + l16;
 #pragma unroll
     for (int ks = 0; ks < KS1; ++ks)
       wo[i][ks] = *reinterpret_cast<const bf16x8*>(Wo + (int64_t)col * CZ + 32 * ks + 8 * g);
@@ -81,36 +85,37 @@ __global__ __launch_bounds__(256) void k_out_then_ab(
   }
 #pragma unroll
   for (int i = 0; i < NJ1; ++i) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int j = wave + kWaves * i;
+    if (j < NT1) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS1; ++ks) {
-      acc = mma16(mh[ks], wo[i][ks], acc);
-      acc = mma16(ml[ks], wo[i][ks], acc);
+      for (int ks = 0; ks < KS1; ++ks) {
+        acc = mma16(mh[ks], wo[i][ks], acc);
+        acc = mma16(ml[ks], wo[i][ks], acc);
+      }
+      const int col = 16 * j + l16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st[(4 * g + e) * LD + col] = (bf16)(acc[e] + res[i][e]);
     }
-    const int col = 16 * (wave + 4 * i) + l16;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) st[(4 * g + e) * LD + col] = (bf16)(acc[e] + res[i][e]);
   }
   __syncthreads();
 
   // ---- s~ rows out (16-byte stores), by the first column group only
   constexpr int VPR = CS / 8;  // 16-byte vectors per row
-  for (int v = blockIdx.y == 0 ? tid : kRows * VPR; v < kRows * VPR; v += 256) {
+  for (int v = tid; v < kRows * VPR; v += 64 * kWaves) {
     const int r = v / VPR, c = 8 * (v % VPR);
     if (r0 + r < M)
       *reinterpret_cast<bf16x8*>(s_new + (r0 + r) * CS + c) =
           *reinterpret_cast<const bf16x8*>(&st[r * LD + c]);
   }
 
-  // ---- [a | b] = s~ [Wa | Wb]^T for tile t = wave + 4 y of 2 CZ / 16, where
-  // y = blockIdx.y is the workgroup's column group: the 2 c_z / 64 workgroups of a
-  // row tile share the (small) first product and split the second
+  // ---- [a | b] = s~ [Wa | Wb]^T, wave t takes 16-column tile t of 2 CZ / 16
   bf16x8 sf[KS2];
 #pragma unroll
   for (int ks = 0; ks < KS2; ++ks)
     sf[ks] = *reinterpret_cast<const bf16x8*>(&st[l16 * LD + 32 * ks + 8 * g]);
-  {
-    const int t = wave + 4 * (int)blockIdx.y;
+  if (wave < 2 * CZ / 16) {
+    const int t = wave;
     const bool is_b = t >= CZ / 16;
     const int col = 16 * (is_b ? t - CZ / 16 : t) + l16;
     const bf16* wrow = (is_b ? Wb : Wa) + (int64_t)col * CS + 8 * g;
@@ -134,8 +139,7 @@ hipError_t launch_t(const float* m, const void* Wo, const void* s_res, void* s_n
                     const void* Wa, const void* Wb, float* a, float* b, int64_t M,
                     hipStream_t stream) {
   const int64_t tiles = (M + kRows - 1) / kRows;
-  constexpr int groups = 2 * CZ / 64;  // column groups of [a | b], one tile per wave
-  hipLaunchKernelGGL((k_out_then_ab<CS, CZ>), dim3((unsigned)tiles, groups), dim3(256), 0, stream, m,
+  hipLaunchKernelGGL((k_out_then_ab<CS, CZ>), dim3((unsigned)tiles), dim3(64 * kWaves), 0, stream, m,
                      static_cast<const bf16*>(Wo), static_cast<const bf16*>(s_res),
                      static_cast<bf16*>(s_new), static_cast<const bf16*>(Wa),
                      static_cast<const bf16*>(Wb), a, b, M);
