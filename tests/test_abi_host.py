@@ -331,3 +331,45 @@ def test_non_leading_calls_validate(lib):
               need.value - 1, None) == E.NT_ERR_WORKSPACE
     assert bb(P, s, z, W, gso, None, gsi, ctypes.byref(g), 9, 16, 64, 32, 1, ws,
               need.value, None) == E.NT_ERR_INVALID
+
+
+def test_chain_validates(lib):
+    """nt_pair_chain rejects bad arguments before anything is launched."""
+    p = fake_partition()
+    P = ctypes.byref(p)
+    s, so, z = FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000
+    w = (_native.NtBlockWeights * 2)(
+        _native.NtBlockWeights(*(FAKE + 0x400000 + 0x1000 * k for k in range(5))),
+        _native.NtBlockWeights(*(FAKE + 0x500000 + 0x1000 * k for k in range(5))))
+    ws = FAKE + 0x800000
+    E = _native
+    one, two = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.nt_chain_workspace_bytes(P, 1, 16, 16, 32, 1, ctypes.byref(one)) == 0
+    assert lib.nt_chain_workspace_bytes(P, 2, 16, 16, 32, 1, ctypes.byref(two)) == 0
+    blk = ctypes.c_size_t()
+    assert lib.nt_block_workspace_bytes(P, 16, 16, 32, 1, ctypes.byref(blk)) == 0
+    assert one.value == blk.value                    # one block: the block's workspace
+    assert two.value >= blk.value + 5 * 16 * 2       # plus a [T, c_s] bf16 buffer
+    assert lib.nt_chain_workspace_bytes(P, 0, 16, 16, 32, 1, ctypes.byref(one)) == \
+        E.NT_ERR_INVALID
+    need = two.value
+    ch = lib.nt_pair_chain
+    assert ch(P, s, so, z, w, 0, 16, 16, 32, 1, ws, need, None) == E.NT_ERR_INVALID
+    assert ch(P, s, so, z, None, 2, 16, 16, 32, 1, ws, need, None) == E.NT_ERR_NULL
+    assert ch(P, s, so, z, w, 2, 16, 16, 32, 7, ws, need, None) == E.NT_ERR_DTYPE
+    assert ch(P, s, so, z, w, 2, 16, 16, 32, 1, ws, need - 1, None) == E.NT_ERR_WORKSPACE
+    assert ch(P, s, so, z, w, 2, 16, 16, 32, 1, None, need, None) == E.NT_ERR_NULL
+    assert ch(P, None, so, z, w, 2, 16, 16, 32, 1, ws, need, None) == E.NT_ERR_NULL
+    assert ch(P, s, s + 32, z, w, 2, 16, 16, 32, 1, ws, need, None) == E.NT_ERR_INVALID
+    assert ch(P, s, so, so + 32, w, 2, 16, 16, 32, 1, ws, need, None) == E.NT_ERR_INVALID
+    assert ch(P, s, so, z, w, 2, 16, 16, 32, 1, z + 64, need, None) == E.NT_ERR_INVALID
+    bad = (_native.NtBlockWeights * 2)(w[0], _native.NtBlockWeights(
+        FAKE + 0x500000, None, FAKE + 0x502000, FAKE + 0x503000, FAKE + 0x504000))
+    assert ch(P, s, so, z, bad, 2, 16, 16, 32, 1, ws, need, None) == E.NT_ERR_NULL
+    wz = (_native.NtBlockWeights * 2)(w[0], _native.NtBlockWeights(
+        z, FAKE + 0x501000, FAKE + 0x502000, FAKE + 0x503000, FAKE + 0x504000))
+    assert ch(P, s, so, z, wz, 2, 16, 16, 32, 1, ws, need, None) == E.NT_ERR_INVALID
+    rect = fake_partition()
+    rect.col_offsets = FAKE + 0x9000
+    assert ch(ctypes.byref(rect), s, so, z, w, 2, 16, 16, 32, 1, ws, need, None) == \
+        E.NT_ERR_INVALID
