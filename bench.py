@@ -396,10 +396,10 @@ def time_kernel_in_steps(fn, step, reps: int, torch) -> float:
 
 
 def transition_kernel_id(c_z: int, hidden: int, dtype: str) -> str:
-    """The kernel the library launches for the fused broadcast + transition."""
-    choice = os.environ.get("NT_TRANSITION_KERNEL")
+    """The kernel the library launches for the fused broadcast + transition
+    (batches of fewer than 2^22 single rows)."""
     if dtype == "bf16" and c_z == 128 and hidden == 512:
-        return {"pf": "k_transition_pf", "p32": "k_transition_p32"}.get(choice, "k_transition_ws")
+        return "k_transition_ws"
     if dtype == "bf16" and (c_z, hidden) == (64, 128):
         return "k_transition_p32"
     return "fused"
@@ -408,11 +408,9 @@ def transition_kernel_id(c_z: int, hidden: int, dtype: str) -> str:
 def transition_kernel_label(c_z: int, hidden: int, dtype: str) -> str:
     """The kernel the library launches for the fused broadcast + transition."""
     kid = transition_kernel_id(c_z, hidden, dtype)
-    if kid == "k_transition_pf":
-        return "k_transition_pf (fused broadcast, next tile's b rows prefetched)"
     if kid == "k_transition_ws":
         return "k_transition_ws (fused broadcast, weights resident in registers)"
-    if dtype == "bf16" and (c_z, hidden) in ((128, 512), (64, 128)):
+    if kid == "k_transition_p32":
         return "k_transition_p32 (fused broadcast prologue)"
     return "fused broadcast + transition"
 
@@ -623,8 +621,7 @@ def main():
                     help="timed steps and kernel timings only (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chain", action="store_true",
-                    help="run each step's blocks through one nt_pair_chain call (with "
-                         "NT_CHAIN_BOUNDARY=fused: the fused block boundary)")
+                    help="run each step's blocks through one nt_pair_chain call")
     ap.add_argument("--copy-reference", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()

@@ -237,8 +237,9 @@ nt_status nt_pair_transition_swiglu(const nt_partition* p, const void* z_in, voi
  * Column mean (Equation 1, third line; Equation 4 divided by M_i, which is
  * N_i for square pairs):
  *   m[eta_i + r, :] = (1/M_i) sum_{c < M_i} z[o_i + r M_i + c, :].
- * z: [cells, c_z] of `dtype`; m: fp32 [T, c_z]. Deterministic: every row is
- * summed by one workgroup in a fixed order, no atomics.
+ * z: [cells, c_z] of `dtype`; m: fp32 [T, c_z]. Deterministic: a row of at
+ * least 256 cells is summed by one workgroup, a shorter row by one wave,
+ * each in a fixed order, with no atomics.
  */
 nt_status nt_pair_reduce(const nt_partition* p, const void* z, float* m, int32_t c_z,
                          nt_dtype dtype, void* stream);
@@ -275,15 +276,8 @@ nt_status nt_chain_workspace_bytes(const nt_partition* p, int32_t nblocks, int32
  * themselves are on the device. s_out [T, c_s] receives the last block's
  * singles, z_out [cells, c_z] the last block's pair state (every block
  * writes it in turn). s_out may equal s_in. Square partitions only.
- * By default the blocks run nt_pair_block's launches in turn, and the
- * results are those of chained nt_pair_block calls. With the environment
- * variable NT_CHAIN_BOUNDARY=fused, one launch between two blocks forms
- * s~ = s + m Wo^T (rounded once to `dtype`) and the next block's a and b
- * from the same rows (bf16, c_s = 384 with c_z = 128, or c_s = c_z = 64;
- * other shapes keep the separate launches). Each row is still computed from
- * itself alone, so results do not depend on the rest of the batch; they may
- * differ from chained nt_pair_block calls in the last bits of a and b
- * (another summation order).
+ * The blocks run nt_pair_block's launches in turn, and the results are
+ * those of chained nt_pair_block calls, bit for bit.
  * workspace: device, at least nt_chain_workspace_bytes, 16-byte aligned,
  * disjoint from every other array. Errors as nt_pair_block; nothing is
  * launched when a check fails.

@@ -143,15 +143,10 @@ def transition_backward(z, W1, W2, G):
 
 
 # ------------------------------------------------------------- the block
-def block_backward(lengths, s, w, g_s_out, g_z_out=None, round_z=None):
+def block_backward(lengths, s, w, g_s_out, g_z_out=None):
     """Gradients of one square block (pair_block.block) for incoming g_s_out
     = dL/ds~ and, optionally, g_z_out = dL/dz' (the returned pair state).
-    Returns a dict with "s" (dL/ds) and "Wa", "Wb", "W1", "W2", "Wo".
-
-    round_z, when given, maps the pair state z to the values the transition's
-    products read (e.g. round_bf16 for a bf16 matrix-core path), so that the
-    relu decision z W1^T > 0 is taken on the same z as there; every other
-    step stays exact."""
+    Returns a dict with "s" (dL/ds) and "Wa", "Wb", "W1", "W2", "Wo"."""
     s = np.asarray(s, dtype=np.float64)
     g_s_out = np.asarray(g_s_out, dtype=np.float64)
     W = {k: np.asarray(v, dtype=np.float64) for k, v in w.items()}
@@ -167,8 +162,7 @@ def block_backward(lengths, s, w, g_s_out, g_z_out=None, round_z=None):
     G = reduce_mean_backward(lengths, lengths, g_m)
     if g_z_out is not None:
         G = G + np.asarray(g_z_out, dtype=np.float64)
-    zq = round_z(z) if round_z is not None else z
-    g_z, dW1, dW2 = transition_backward(zq, W["W1"], W["W2"], G)
+    g_z, dW1, dW2 = transition_backward(z, W["W1"], W["W2"], G)
     g_a, g_b = broadcast_backward(lengths, lengths, g_z)
     g_s = g_s_out + g_a @ W["Wa"] + g_b @ W["Wb"]
     return {"s": g_s, "Wa": g_a.T @ s, "Wb": g_b.T @ s, "W1": dW1, "W2": dW2, "Wo": dWo}
@@ -234,7 +228,7 @@ def block_nl(lengths, s, w, S):
     return out.reshape(T, -1), z
 
 
-def block_backward_nl(lengths, s, w, S, g_s_out, g_z_out=None, round_z=None):
+def block_backward_nl(lengths, s, w, S, g_s_out, g_z_out=None):
     """Gradients of block_nl: the S slices are independent blocks sharing the
     weights, so the single and pair gradients are per slice and the weight
     gradients are sums over slices (the chain rule through the shared
@@ -248,7 +242,7 @@ def block_backward_nl(lengths, s, w, S, g_s_out, g_z_out=None, round_z=None):
     out = {"s": np.zeros_like(x)}
     for k in range(S):
         gzk = None if gz is None else gz.reshape(gz.shape[0], S, c_z)[:, k, :]
-        r = block_backward(lengths, x[:, k, :], w, gs[:, k, :], gzk, round_z=round_z)
+        r = block_backward(lengths, x[:, k, :], w, gs[:, k, :], gzk)
         out["s"][:, k, :] = r.pop("s")
         for name, v in r.items():
             out[name] = out.get(name, 0.0) + v

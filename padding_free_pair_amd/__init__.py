@@ -69,6 +69,38 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr() if t.numel() else None
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _expect(p, name, t, shape, dtype=None):
+    """Host-side extent check before a native call: the C ABI sees only
+    pointers, so a tensor of the wrong shape or on another device would be
+    read or written out of bounds by the kernels."""
+    if t is None:
+        return
+    if t.device != p.device:
+        raise ValueError(f"{name} is on {t.device}, the partition on {p.device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _expect_workspace(p, workspace, need: int) -> None:
+    if workspace.device != p.device:
+        raise ValueError(f"workspace is on {workspace.device}, the partition on {p.device}")
+    if _nbytes(workspace) < need:
+        raise ValueError(f"workspace has {_nbytes(workspace)} bytes, needs {need}")
+
+
+def _expect_weights(p, weights, c_s, c_z, hidden, dtype, label="") -> None:
+    shapes = {"Wa": (c_z, c_s), "Wb": (c_z, c_s), "W1": (hidden, c_z), "W2": (c_z, hidden),
+              "Wo": (c_s, c_z)}
+    for name, w in zip(("Wa", "Wb", "W1", "W2", "Wo"), weights):
+        _expect(p, label + name, w, shapes[name], dtype)
+
+
 def _stream(stream, device) -> int:
     torch = _torch()
     if stream is None:
@@ -218,6 +250,9 @@ def nt_pair_broadcast(p: Partition, a, b, z=None, stream=None):
         z = torch.empty((p.cells, c_z), dtype=a.dtype, device=a.device)
     if a.dtype != b.dtype or z.dtype != a.dtype:
         raise TypeError("a, b and z must share a dtype")
+    _expect(p, "a", a, (p.T, c_z))
+    _expect(p, "b", b, (p.T_cols, c_z))
+    _expect(p, "z", z, (p.cells, c_z))
     _check(_native.lib().nt_pair_broadcast(ctypes.byref(p.struct), _ptr(a), _ptr(b), _ptr(z),
                                            c_z, _dtype_code(a), _stream(stream, a.device)))
     return z
@@ -231,6 +266,10 @@ def nt_pair_transition(p: Partition, z_in, W1, W2, z_out=None, stream=None):
         z_out = torch.empty_like(z_in)
     if not (z_in.dtype == W1.dtype == W2.dtype == z_out.dtype):
         raise TypeError("z and weights must share a dtype")
+    _expect(p, "z_in", z_in, (p.cells, c_z))
+    _expect(p, "z_out", z_out, (p.cells, c_z))
+    _expect(p, "W1", W1, (hidden, c_z))
+    _expect(p, "W2", W2, (c_z, hidden))
     _check(_native.lib().nt_pair_transition(ctypes.byref(p.struct), _ptr(z_in), _ptr(z_out),
                                             _ptr(W1), _ptr(W2), c_z, hidden,
                                             _dtype_code(z_in), _stream(stream, z_in.device)))
@@ -250,6 +289,11 @@ def nt_pair_broadcast_transition(p: Partition, a, b, W1, W2, z_out=None, stream=
         z_out = torch.empty((p.cells, c_z), dtype=W1.dtype, device=a.device)
     if not (W1.dtype == W2.dtype == z_out.dtype):
         raise TypeError("weights and z_out must share a dtype")
+    _expect(p, "a", a, (p.T, c_z))
+    _expect(p, "b", b, (p.T_cols, c_z))
+    _expect(p, "z_out", z_out, (p.cells, c_z))
+    _expect(p, "W1", W1, (hidden, c_z))
+    _expect(p, "W2", W2, (c_z, hidden))
     _check(_native.lib().nt_pair_broadcast_transition(
         ctypes.byref(p.struct), _ptr(a), _ptr(b), _ptr(z_out), _ptr(W1), _ptr(W2), c_z, hidden,
         _dtype_code(W1), _stream(stream, a.device)))
@@ -271,6 +315,13 @@ def nt_pair_transition_swiglu(p: Partition, z_in, ln_gamma, ln_beta, W_gate, W_u
         raise TypeError("ln_gamma and ln_beta must be float32")
     if not (z_in.dtype == W_gate.dtype == W_up.dtype == W_down.dtype == z_out.dtype):
         raise TypeError("z and weights must share a dtype")
+    _expect(p, "z_in", z_in, (p.cells, c_z))
+    _expect(p, "z_out", z_out, (p.cells, c_z))
+    _expect(p, "ln_gamma", ln_gamma, (c_z,))
+    _expect(p, "ln_beta", ln_beta, (c_z,))
+    _expect(p, "W_gate", W_gate, (hidden, c_z))
+    _expect(p, "W_up", W_up, (hidden, c_z))
+    _expect(p, "W_down", W_down, (c_z, hidden))
     _check(_native.lib().nt_pair_transition_swiglu(
         ctypes.byref(p.struct), _ptr(z_in), _ptr(z_out), _ptr(ln_gamma), _ptr(ln_beta),
         _ptr(W_gate), _ptr(W_up), _ptr(W_down), c_z, hidden, ln_eps, _dtype_code(z_in),
@@ -284,6 +335,8 @@ def nt_pair_reduce(p: Partition, z, m=None, stream=None):
     c_z = z.shape[-1]
     if m is None:
         m = torch.empty((p.T, c_z), dtype=torch.float32, device=z.device)
+    _expect(p, "z", z, (p.cells, c_z))
+    _expect(p, "m", m, (p.T, c_z), torch.float32)
     _check(_native.lib().nt_pair_reduce(ctypes.byref(p.struct), _ptr(z), _ptr(m), c_z,
                                         _dtype_code(z), _stream(stream, z.device)))
     return m
@@ -319,11 +372,16 @@ def nt_pair_block(p: Partition, s_in, weights, s_out=None, z_out=None, workspace
     need = nt_block_workspace_bytes(p, c_s, c_z, hidden, _dtype_code(s_in))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=s_in.device)
+    _expect(p, "s_in", s_in, (p.T, c_s))
+    _expect(p, "s_out", s_out, (p.T, c_s), s_in.dtype)
+    _expect(p, "z_out", z_out, (p.cells, c_z), s_in.dtype)
+    _expect_weights(p, weights, c_s, c_z, hidden, s_in.dtype)
+    _expect_workspace(p, workspace, need)
     wst = NtBlockWeights(*[_ptr(w) for w in weights])
     _check(_native.lib().nt_pair_block(ctypes.byref(p.struct), _ptr(s_in), _ptr(s_out),
                                        _ptr(z_out), ctypes.byref(wst), c_s, c_z, hidden,
                                        _dtype_code(s_in), _ptr(workspace),
-                                       workspace.numel(), _stream(stream, s_in.device)))
+                                       _nbytes(workspace), _stream(stream, s_in.device)))
     return s_out, z_out
 
 
@@ -361,10 +419,16 @@ def nt_pair_chain(p: Partition, s_in, weights, s_out=None, z_out=None, workspace
     need = nt_chain_workspace_bytes(p, len(sets), c_s, c_z, hidden, _dtype_code(s_in))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=s_in.device)
+    _expect(p, "s_in", s_in, (p.T, c_s))
+    _expect(p, "s_out", s_out, (p.T, c_s), s_in.dtype)
+    _expect(p, "z_out", z_out, (p.cells, c_z), s_in.dtype)
+    for k, wk in enumerate(sets):
+        _expect_weights(p, wk, c_s, c_z, hidden, s_in.dtype, label=f"block {k} ")
+    _expect_workspace(p, workspace, need)
     arr = (NtBlockWeights * len(sets))(*[NtBlockWeights(*[_ptr(w) for w in wk]) for wk in sets])
     _check(_native.lib().nt_pair_chain(ctypes.byref(p.struct), _ptr(s_in), _ptr(s_out),
                                        _ptr(z_out), arr, len(sets), c_s, c_z, hidden,
-                                       _dtype_code(s_in), _ptr(workspace), workspace.numel(),
+                                       _dtype_code(s_in), _ptr(workspace), _nbytes(workspace),
                                        _stream(stream, s_in.device)))
     return s_out, z_out
 
@@ -390,11 +454,17 @@ def nt_pair_block_rect(p: Partition, s_rows, s_cols, weights, s_out=None, z_out=
     need = nt_block_workspace_bytes(p, c_s, c_z, hidden, _dtype_code(s_rows))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=s_rows.device)
+    _expect(p, "s_rows", s_rows, (p.T, c_s))
+    _expect(p, "s_cols", s_cols, (p.T_cols, c_s))
+    _expect(p, "s_out", s_out, (p.T, c_s), s_rows.dtype)
+    _expect(p, "z_out", z_out, (p.cells, c_z), s_rows.dtype)
+    _expect_weights(p, weights, c_s, c_z, hidden, s_rows.dtype)
+    _expect_workspace(p, workspace, need)
     wst = NtBlockWeights(*[_ptr(w) for w in weights])
     _check(_native.lib().nt_pair_block_rect(ctypes.byref(p.struct), _ptr(s_rows), _ptr(s_cols),
                                             _ptr(s_out), _ptr(z_out), ctypes.byref(wst), c_s, c_z,
                                             hidden, _dtype_code(s_rows), _ptr(workspace),
-                                            workspace.numel(), _stream(stream, s_rows.device)))
+                                            _nbytes(workspace), _stream(stream, s_rows.device)))
     return s_out, z_out
 
 
@@ -427,12 +497,15 @@ def nt_pair_loss_eq5(p: Partition, x, pz, S: int = 1, grads: bool = True, worksp
     g_pz = torch.empty(pz.shape, dtype=torch.float32, device=dev) if grads else None
     if workspace is None:
         workspace = torch.empty(nt_loss_workspace_bytes(p), dtype=torch.uint8, device=dev)
-    if x.shape[-1] % S or pz.shape[-1] % S:
-        raise ValueError("row widths must be multiples of S")
+    if x.dim() != 2 or pz.dim() != 2 or x.shape[-1] % S or pz.shape[-1] % S:
+        raise ValueError("x and pz must be 2-D with row widths that are multiples of S")
+    _expect(p, "x", x, (p.T, x.shape[-1]))
+    _expect(p, "pz", pz, (p.cells, pz.shape[-1]))
+    _expect_workspace(p, workspace, nt_loss_workspace_bytes(p))
     _check(_native.lib().nt_pair_loss_eq5(ctypes.byref(p.struct), _ptr(x), x.shape[-1] // S,
                                           _ptr(pz), pz.shape[-1] // S, S, _dtype_code(x),
                                           _ptr(loss), _ptr(g_x),
-                                          _ptr(g_pz), _ptr(workspace), workspace.numel(),
+                                          _ptr(g_pz), _ptr(workspace), _nbytes(workspace),
                                           _stream(stream, dev)))
     return loss[:1], g_x, g_pz
 
@@ -443,6 +516,9 @@ def nt_pair_reduce_backward(p: Partition, g_m, g_z_in=None, G=None, stream=None)
     c_z = g_m.shape[-1]
     if G is None:
         G = torch.empty((p.cells, c_z), dtype=torch.float32, device=g_m.device)
+    _expect(p, "g_m", g_m, (p.T, c_z), torch.float32)
+    _expect(p, "g_z_in", g_z_in, (p.cells, c_z), torch.float32)
+    _expect(p, "G", G, (p.cells, c_z), torch.float32)
     _check(_native.lib().nt_pair_reduce_backward(ctypes.byref(p.struct), _ptr(g_m), _ptr(g_z_in),
                                                  _ptr(G), c_z, _stream(stream, g_m.device)))
     return G
@@ -456,6 +532,9 @@ def nt_pair_broadcast_backward(p: Partition, g_z, g_a=None, g_b=None, stream=Non
         g_a = torch.empty((p.T, c_z), dtype=torch.float32, device=g_z.device)
     if g_b is None:
         g_b = torch.empty((p.T_cols, c_z), dtype=torch.float32, device=g_z.device)
+    _expect(p, "g_z", g_z, (p.cells, c_z), torch.float32)
+    _expect(p, "g_a", g_a, (p.T, c_z), torch.float32)
+    _expect(p, "g_b", g_b, (p.T_cols, c_z), torch.float32)
     _check(_native.lib().nt_pair_broadcast_backward(ctypes.byref(p.struct), _ptr(g_z), _ptr(g_a),
                                                     _ptr(g_b), c_z, _stream(stream, g_z.device)))
     return g_a, g_b
@@ -482,12 +561,20 @@ def nt_pair_transition_backward(p: Partition, z, G, W1, W2, g_z=None, dW1=None, 
         dW1 = torch.empty((hidden, c_z), dtype=f32, device=dev)
     if dW2 is None:
         dW2 = torch.empty((c_z, hidden), dtype=f32, device=dev)
+    need = nt_transition_backward_workspace_bytes(p, c_z, hidden, _dtype_code(z))
     if workspace is None:
-        need = nt_transition_backward_workspace_bytes(p, c_z, hidden, _dtype_code(z))
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _expect(p, "z", z, (p.cells, c_z))
+    _expect(p, "G", G, (p.cells, c_z), f32)
+    _expect(p, "W1", W1, (hidden, c_z), z.dtype)
+    _expect(p, "W2", W2, (c_z, hidden), z.dtype)
+    _expect(p, "g_z", g_z, (p.cells, c_z), f32)
+    _expect(p, "dW1", dW1, (hidden, c_z), f32)
+    _expect(p, "dW2", dW2, (c_z, hidden), f32)
+    _expect_workspace(p, workspace, need)
     _check(_native.lib().nt_pair_transition_backward(
         ctypes.byref(p.struct), _ptr(z), _ptr(G), _ptr(W1), _ptr(W2), _ptr(g_z), _ptr(dW1),
-        _ptr(dW2), c_z, hidden, _dtype_code(z), _ptr(workspace), workspace.numel(),
+        _ptr(dW2), c_z, hidden, _dtype_code(z), _ptr(workspace), _nbytes(workspace),
         _stream(stream, dev)))
     return g_z, dW1, dW2
 
@@ -521,15 +608,24 @@ def nt_pair_block_backward(p: Partition, s_in, z_out, weights, g_s_out, g_z_out=
     if grads is None:
         grads = {k: torch.empty(w.shape, dtype=torch.float32, device=dev)
                  for k, w in zip(_WEIGHT_NAMES, weights)}
+    need = nt_block_backward_workspace_bytes(p, c_s, c_z, hidden, _dtype_code(s_in))
     if workspace is None:
-        need = nt_block_backward_workspace_bytes(p, c_s, c_z, hidden, _dtype_code(s_in))
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    f32 = torch.float32
+    _expect(p, "s_in", s_in, (p.T, c_s))
+    _expect(p, "z_out", z_out, (p.cells, c_z), s_in.dtype)
+    _expect_weights(p, weights, c_s, c_z, hidden, s_in.dtype)
+    _expect(p, "g_s_out", g_s_out, (p.T, c_s), f32)
+    _expect(p, "g_z_out", g_z_out, (p.cells, c_z), f32)
+    _expect(p, "g_s_in", g_s_in, (p.T, c_s), f32)
+    _expect_weights(p, [grads[k] for k in _WEIGHT_NAMES], c_s, c_z, hidden, f32, label="d")
+    _expect_workspace(p, workspace, need)
     wst = NtBlockWeights(*[_ptr(w) for w in weights])
     gst = _native.NtBlockGrads(*[_ptr(grads[k]) for k in _WEIGHT_NAMES])
     _check(_native.lib().nt_pair_block_backward(
         ctypes.byref(p.struct), _ptr(s_in), _ptr(z_out), ctypes.byref(wst), _ptr(g_s_out),
         _ptr(g_z_out), _ptr(g_s_in), ctypes.byref(gst), c_s, c_z, hidden, _dtype_code(s_in),
-        _ptr(workspace), workspace.numel(), _stream(stream, dev)))
+        _ptr(workspace), _nbytes(workspace), _stream(stream, dev)))
     return g_s_in, grads
 
 
@@ -565,13 +661,18 @@ def nt_pair_block_nl(p: Partition, s_in, weights, S: int, s_out=None, z_out=None
         s_out = torch.empty_like(s_in)
     if z_out is None:
         z_out = torch.empty((p.cells, S * c_z), dtype=s_in.dtype, device=s_in.device)
+    need = nt_block_nl_workspace_bytes(p, S, c_s, c_z, hidden, _dtype_code(s_in))
     if workspace is None:
-        need = nt_block_nl_workspace_bytes(p, S, c_s, c_z, hidden, _dtype_code(s_in))
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=s_in.device)
+    _expect(p, "s_in", s_in, (p.T, S * c_s))
+    _expect(p, "s_out", s_out, (p.T, S * c_s), s_in.dtype)
+    _expect(p, "z_out", z_out, (p.cells, S * c_z), s_in.dtype)
+    _expect_weights(p, weights, c_s, c_z, hidden, s_in.dtype)
+    _expect_workspace(p, workspace, need)
     wst = NtBlockWeights(*[_ptr(w) for w in weights])
     _check(_native.lib().nt_pair_block_nl(ctypes.byref(p.struct), _ptr(s_in), _ptr(s_out),
                                           _ptr(z_out), ctypes.byref(wst), S, c_s, c_z, hidden,
-                                          _dtype_code(s_in), _ptr(workspace), workspace.numel(),
+                                          _dtype_code(s_in), _ptr(workspace), _nbytes(workspace),
                                           _stream(stream, s_in.device)))
     return s_out, z_out
 
@@ -590,13 +691,22 @@ def nt_pair_block_backward_nl(p: Partition, s_in, z_out, weights, S: int, g_s_ou
     if grads is None:
         grads = {k: torch.empty(w.shape, dtype=torch.float32, device=dev)
                  for k, w in zip(_WEIGHT_NAMES, weights)}
+    need = nt_block_backward_nl_workspace_bytes(p, S, c_s, c_z, hidden, _dtype_code(s_in))
     if workspace is None:
-        need = nt_block_backward_nl_workspace_bytes(p, S, c_s, c_z, hidden, _dtype_code(s_in))
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    f32 = torch.float32
+    _expect(p, "s_in", s_in, (p.T, S * c_s))
+    _expect(p, "z_out", z_out, (p.cells, S * c_z), s_in.dtype)
+    _expect_weights(p, weights, c_s, c_z, hidden, s_in.dtype)
+    _expect(p, "g_s_out", g_s_out, (p.T, S * c_s), f32)
+    _expect(p, "g_z_out", g_z_out, (p.cells, S * c_z), f32)
+    _expect(p, "g_s_in", g_s_in, (p.T, S * c_s), f32)
+    _expect_weights(p, [grads[k] for k in _WEIGHT_NAMES], c_s, c_z, hidden, f32, label="d")
+    _expect_workspace(p, workspace, need)
     wst = NtBlockWeights(*[_ptr(w) for w in weights])
     gst = _native.NtBlockGrads(*[_ptr(grads[k]) for k in _WEIGHT_NAMES])
     _check(_native.lib().nt_pair_block_backward_nl(
         ctypes.byref(p.struct), _ptr(s_in), _ptr(z_out), ctypes.byref(wst), _ptr(g_s_out),
         _ptr(g_z_out), _ptr(g_s_in), ctypes.byref(gst), S, c_s, c_z, hidden, _dtype_code(s_in),
-        _ptr(workspace), workspace.numel(), _stream(stream, dev)))
+        _ptr(workspace), _nbytes(workspace), _stream(stream, dev)))
     return g_s_in, grads

@@ -5,7 +5,6 @@
 
 #include <climits>
 #include <cstdarg>
-#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -732,48 +731,15 @@ nt_status nt_pair_chain(const nt_partition* p, const void* s_in, void* s_out, vo
     return fail(NT_ERR_INVALID, "z_out, the singles and the workspace must not overlap");
   if (p->T == 0) return ok();
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
   void* sbuf = base + blk;
   // block k writes s_out when nblocks - 1 - k is even, else the workspace
   // buffer, so that the last block writes s_out
   auto dest = [&](int k) -> void* { return (nblocks - 1 - k) % 2 == 0 ? s_out : sbuf; };
-  // The fused boundary (one launch for block k's output projection and block
-  // k + 1's projections) is taken on request only: it measured slower than
-  // the two launches it replaces (0.537 against 0.522 ms per four-block step
-  // on the high-variation batch).
-  const char* boundary = getenv("NT_CHAIN_BOUNDARY");
-  const bool fused = boundary && strcmp(boundary, "fused") == 0;
-  if (nblocks == 1 || !fused || !nt::out_then_ab_supported(c_s, c_z, dtype)) {
-    const void* cur = s_in;
-    for (int k = 0; k < nblocks; ++k) {
-      NT_TRY(pair_block(p, cur, cur, dest(k), z_out, &w[k], c_s, c_z, hidden, dtype, workspace,
-                        blk, stream));
-      cur = dest(k);
-    }
-    return ok();
-  }
-  const BlockWorkspace ws = block_workspace(p->T, p->T_cols, c_z, dtype);
-  float* a = reinterpret_cast<float*>(base + ws.a);
-  float* b = reinterpret_cast<float*>(base + ws.b);
-  float* m = reinterpret_cast<float*>(base + ws.m);
-  NT_TRY(hip_status(nt::launch_linear2(s_in, dtype, w[0].Wa, w[0].Wb, a, b, p->T, c_z, c_s, s),
-                    "projections a, b"));
   const void* cur = s_in;
   for (int k = 0; k < nblocks; ++k) {
-    NT_TRY(hip_status(nt::launch_transition(*p, nullptr, a, b, z_out, w[k].W1, w[k].W2, c_z,
-                                            hidden, dtype, s),
-                      "fused broadcast + transition"));
-    NT_TRY(hip_status(nt::launch_reduce(*p, z_out, m, c_z, dtype, s), "column mean"));
-    if (k + 1 < nblocks) {
-      NT_TRY(hip_status(nt::launch_out_then_ab(m, w[k].Wo, cur, dest(k), w[k + 1].Wa,
-                                               w[k + 1].Wb, a, b, p->T, c_s, c_z, s),
-                        "output projection + next projections"));
-    } else {
-      NT_TRY(hip_status(nt::launch_linear(m, NT_F32, w[k].Wo, dtype, cur, dest(k), dtype, p->T,
-                                          c_s, c_z, s),
-                        "output projection"));
-    }
+    NT_TRY(pair_block(p, cur, cur, dest(k), z_out, &w[k], c_s, c_z, hidden, dtype, workspace,
+                      blk, stream));
     cur = dest(k);
   }
   return ok();

@@ -108,11 +108,6 @@ hipError_t launch_transition_swiglu(const nt_partition& p, const void* z_in, voi
                                     const float* gamma, const float* beta, const void* Wg,
                                     const void* Wu, const void* Wd, int c_z, int hidden,
                                     float eps, hipStream_t stream);
-// Fused broadcast + transition for c_z = 128, hidden = 512 with the next
-// tile's inputs prefetched into LDS; needs the tile_sample index and T < 2^31.
-hipError_t launch_transition_prefetch(const nt_partition& p, const void* a, const void* b,
-                                      void* z_out, const void* W1, const void* W2, int cus,
-                                      hipStream_t stream);
 // Fused broadcast + transition for c_z = 128, hidden = 512 with both weights
 // held in registers (one hidden quarter per wave) over 32-cell blocks; needs
 // the tile_sample index and T < 2^22.
@@ -135,16 +130,6 @@ hipError_t launch_linear(const void* A, nt_dtype a_dtype, const void* W, nt_dtyp
 // (fp32 results; A and the weights are `a_dtype`).
 hipError_t launch_linear2(const void* A, nt_dtype a_dtype, const void* W0, const void* W1,
                           void* C0, void* C1, int64_t M, int N, int K, hipStream_t stream);
-
-// Boundary of a chain (nt_chain.hip): s_new = bf16(s_res + m Wo^T), then
-// a = s_new Wa^T, b = s_new Wb^T in fp32, all from one launch over 16-row
-// tiles. bf16 only, for the (c_s, c_z) that out_then_ab_supported accepts.
-// s_new may equal s_res (each row is read before it is written, by one
-// workgroup).
-bool out_then_ab_supported(int c_s, int c_z, nt_dtype dtype);
-hipError_t launch_out_then_ab(const float* m, const void* Wo, const void* s_res, void* s_new,
-                              const void* Wa, const void* Wb, float* a, float* b, int64_t M,
-                              int c_s, int c_z, hipStream_t stream);
 
 // ---- backward (nt_backward.hip, nt_transition_bwd.hip)
 // G = g_in (or 0) + g_m[row] / M_i on every cell; G may equal g_in.

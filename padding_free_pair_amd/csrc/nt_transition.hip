@@ -18,9 +18,6 @@
 // residual, so the pair state is rounded once, on output.
 //
 // Generic path (any width, fp32 or bf16): plain fp32 arithmetic through LDS.
-#include <cstdlib>
-#include <cstring>
-
 #include "nt_device.hpp"
 #include "nt_internal.hpp"
 
@@ -846,17 +843,11 @@ hipError_t launch_transition(const nt_partition& p, const void* z_in, const void
   if (transition_has_mfma(c_z, hidden, dtype)) {
     // the persistent kernel keeps single indices in 32 bits
     const bool small_t = p.T <= INT32_MAX && p.T_cols <= INT32_MAX;
-    // NT_TRANSITION_KERNEL=p32 or =pf selects the persistent or the
-    // prefetching kernel for the fused form instead of the weight-stationary
-    // one (read on every call, for comparisons and tests)
-    const char* choice = getenv("NT_TRANSITION_KERNEL");
-    const bool want_p32 = choice && strcmp(choice, "p32") == 0;
-    const bool want_pf = choice && strcmp(choice, "pf") == 0;
-    // the fused kernels below address a and b through 32-bit buffer ranges
+    // the weight-stationary kernel addresses a and b through 32-bit buffer
+    // ranges: T * 512 bytes must fit; larger batches take the persistent kernel
     const bool fits = (p.T > p.T_cols ? p.T : p.T_cols) <= (int64_t)(INT32_MAX / (128 * 4));
-    if (!want_p32 && fits && !z_in && c_z == 128 && hidden == 512 && p.tile_sample)
-      return want_pf ? launch_transition_prefetch(p, a, b, z_out, W1, W2, device_cus(), stream)
-                     : launch_transition_ws(p, a, b, z_out, W1, W2, device_cus(), stream);
+    if (fits && !z_in && c_z == 128 && hidden == 512 && p.tile_sample)
+      return launch_transition_ws(p, a, b, z_out, W1, W2, device_cus(), stream);
     if (small_t && c_z == 128 && hidden == 512)
       return launch_persistent<128, 512>(p, z_in, a, b, z_out, W1, W2, stream);
     if (small_t && c_z == 64 && hidden == 128)

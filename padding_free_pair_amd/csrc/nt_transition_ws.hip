@@ -56,10 +56,6 @@ __device__ __forceinline__ int ws_perm(int rho) {
   return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
 }
 
-__device__ __forceinline__ float ws_relu(float x) {
-  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
-}
-
 // Index of workgroup g among the workgroups of its XCD, counted XCD by XCD:
 // XCD x = g mod 8 holds q or q + 1 of the grid's G = 8 q + rem workgroups.
 // A bijection of [0, G).

@@ -373,3 +373,78 @@ def test_chain_validates(lib):
     rect.col_offsets = FAKE + 0x9000
     assert ch(ctypes.byref(rect), s, so, z, w, 2, 16, 16, 32, 1, ws, need, None) == \
         E.NT_ERR_INVALID
+
+
+# ------------------------------------------------ binding extent checks (host)
+def _binding_partition(B=2, T=5, cells=13):
+    """A Partition whose buffer lives on the CPU: every tensor below is a CPU
+    tensor too, and each call is rejected by the binding's shape, dtype,
+    device or workspace checks before any native launch."""
+    torch = pytest.importorskip("torch")
+    import padding_free_pair_amd as nt
+    return nt, torch, nt.Partition(fake_partition(B, T, cells), torch.empty(256, dtype=torch.uint8),
+                                   np.array([2, 3], dtype=np.int32))
+
+
+def _block_args(torch, T=5, cells=13, c_s=16, c_z=8, hidden=16, dt=None):
+    dt = dt or torch.float32
+    s = torch.zeros((T, c_s), dtype=dt)
+    w = {"Wa": torch.zeros((c_z, c_s), dtype=dt), "Wb": torch.zeros((c_z, c_s), dtype=dt),
+         "W1": torch.zeros((hidden, c_z), dtype=dt), "W2": torch.zeros((c_z, hidden), dtype=dt),
+         "Wo": torch.zeros((c_s, c_z), dtype=dt)}
+    return s, w
+
+
+@pytest.mark.parametrize("case", ["s_rows", "s_out", "z_out", "W1", "Wo", "workspace",
+                                  "chain_block1", "device"])
+def test_binding_rejects_bad_extents(lib, case):
+    nt, torch, p = _binding_partition()
+    s, w = _block_args(torch)
+    kw = {}
+    if case == "s_rows":
+        s = torch.zeros((4, 16))
+    elif case == "s_out":
+        kw["s_out"] = torch.zeros((5, 8))
+    elif case == "z_out":
+        kw["z_out"] = torch.zeros((12, 8))
+    elif case == "W1":
+        w["W1"] = torch.zeros((16, 16))
+    elif case == "Wo":
+        w["Wo"] = torch.zeros((8, 16))
+    elif case == "workspace":
+        kw["workspace"] = torch.zeros(8, dtype=torch.uint8)
+    elif case == "device":
+        kw["workspace"] = torch.zeros(1 << 16, dtype=torch.uint8, device="meta")
+    if case == "chain_block1":
+        w2 = dict(w)
+        w2["W2"] = torch.zeros((8, 24))
+        with pytest.raises(ValueError, match="block 1 W2"):
+            nt.nt_pair_chain(p, s, [w, w2])
+        return
+    with pytest.raises(ValueError):
+        nt.nt_pair_block(p, s, w, **kw)
+
+
+def test_binding_rejects_bad_stage_extents(lib):
+    nt, torch, p = _binding_partition()
+    a = torch.zeros((5, 8))
+    with pytest.raises(ValueError, match="b has shape"):
+        nt.nt_pair_broadcast(p, a, torch.zeros((4, 8)))
+    with pytest.raises(ValueError, match="z_in has shape"):
+        nt.nt_pair_transition(p, torch.zeros((14, 8)), torch.zeros((16, 8)), torch.zeros((8, 16)))
+    with pytest.raises(ValueError, match="W2 has shape"):
+        nt.nt_pair_broadcast_transition(p, a, a, torch.zeros((16, 8)), torch.zeros((16, 8)))
+    with pytest.raises(ValueError, match="m has shape"):
+        nt.nt_pair_reduce(p, torch.zeros((13, 8)), m=torch.zeros((13, 8)))
+    with pytest.raises(ValueError, match="g_z has shape"):
+        nt.nt_pair_broadcast_backward(p, torch.zeros((12, 8)))
+    with pytest.raises(ValueError, match="dW1 has shape"):
+        nt.nt_pair_transition_backward(p, torch.zeros((13, 8)), torch.zeros((13, 8)),
+                                       torch.zeros((16, 8)), torch.zeros((8, 16)),
+                                       dW1=torch.zeros((8, 16)))
+    s, w = _block_args(torch)
+    with pytest.raises(ValueError, match="dWa has shape"):
+        grads = {k: torch.zeros(v.shape) for k, v in w.items()}
+        grads["Wa"] = torch.zeros((16, 8))
+        nt.nt_pair_block_backward(p, s, torch.zeros((13, 8)), w, torch.zeros((5, 16)),
+                                  grads=grads)

@@ -43,7 +43,7 @@ def test_counters_dropped_when_source_changed(tmp_path, monkeypatch):
 
 def test_counters_dropped_for_another_kernel(tmp_path, monkeypatch):
     # an entry recorded for one kernel is never reported under another's key
-    _fake_tree(tmp_path, b"kernel v1", b"kernel v1", kernel="k_transition_pf")
+    _fake_tree(tmp_path, b"kernel v1", b"kernel v1", kernel="k_transition_p32")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.traffic_for("k_transition_ws:wl") is None
     assert bench.traffic_for("k_transition_ws:other") is None
@@ -54,18 +54,12 @@ def test_no_counter_file(tmp_path, monkeypatch):
     assert bench.traffic_for("k_transition_ws:wl") is None
 
 
-@pytest.mark.parametrize("env,c_z,hidden,dtype,want", [
-    (None, 128, 512, "bf16", "k_transition_ws"),
-    ("pf", 128, 512, "bf16", "k_transition_pf"),
-    ("p32", 128, 512, "bf16", "k_transition_p32"),
-    (None, 64, 128, "bf16", "k_transition_p32"),
-    (None, 128, 512, "f32", "fused"),
+@pytest.mark.parametrize("c_z,hidden,dtype,want", [
+    (128, 512, "bf16", "k_transition_ws"),
+    (64, 128, "bf16", "k_transition_p32"),
+    (128, 512, "f32", "fused"),
 ])
-def test_transition_kernel_id(monkeypatch, env, c_z, hidden, dtype, want):
-    if env is None:
-        monkeypatch.delenv("NT_TRANSITION_KERNEL", raising=False)
-    else:
-        monkeypatch.setenv("NT_TRANSITION_KERNEL", env)
+def test_transition_kernel_id(c_z, hidden, dtype, want):
     assert bench.transition_kernel_id(c_z, hidden, dtype) == want
 
 

@@ -95,28 +95,14 @@ def test_block_fused_matches_stages(nt):
     np.testing.assert_array_equal(bits(z_block, torch), bits(z_stage, torch))
 
 
-def _sampled_block_check(lengths, s_in64, w64, s_out, z_out, rng, n_cells=6000, n_rows=48):
-    o = oracle.partition(lengths)["pair_offsets"]
-    cells = int(o[-1])
-    ids = np.unique(np.concatenate([rng.integers(0, cells, n_cells), o[:-1], o[1:] - 1]))
-    got_z = f64(z_out[torch.from_numpy(ids).cuda()], torch)
-    ref_z = oracle.block_cells(lengths, s_in64, w64, ids)
-    T = sum(lengths)
-    eta = np.concatenate([[0], np.cumsum(lengths)])
-    rows = np.unique(np.concatenate([rng.integers(0, T, n_rows), eta[:-1], eta[1:] - 1]))
-    _, ref_s = oracle.block_rows(lengths, s_in64, w64, rows)
-    got_s = f64(s_out[torch.from_numpy(rows).cuda()], torch)
-    return scaled_max_err(got_z, ref_z), scaled_max_err(got_s, ref_s)
-
-
 @pytest.mark.parametrize("idx", [2, 3, 4])
 def test_chain_full_size_per_block(nt, idx):
     """Each block of the four-block chain at full size, launched as the
-    benchmark launches it, against the oracle on that block's GPU inputs."""
+    benchmark launches it, against the oracle on that block's GPU inputs:
+    every cell of the pair state and every single row."""
     x = pin.workload_inputs(idx)
     L = x.lengths.tolist()
     p = nt.nt_make_partition(L)
-    rng = np.random.default_rng(idx)
     s = to_dev(x.s, torch)
     z_out = torch.empty((p.cells, x.c_z), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(nt.nt_block_workspace_bytes(p, x.c_s, x.c_z, x.hidden, torch.bfloat16),
@@ -128,7 +114,9 @@ def test_chain_full_size_per_block(nt, idx):
         nt.nt_pair_block(p, s, weights_to_dev(wk, torch), s_out=s_next, z_out=z_out,
                          workspace=ws)
         torch.cuda.synchronize()
-        ez, es = _sampled_block_check(L, s_in64, _w64(wk), s_next, z_out, rng)
+        ref_s, ref_z = oracle.block(L, s_in64, _w64(wk))
+        ez = scaled_max_err(f64(z_out, torch), ref_z)
+        es = scaled_max_err(f64(s_next, torch), ref_s)
         announce(f"errors z={ez:.3e} s={es:.3e}")
         assert ez <= TOL["bf16"], (k, ez)
         assert es <= TOL["bf16"], (k, es)
@@ -173,17 +161,14 @@ def test_per_sample_launches_match_segmented(nt, idx):
 
 # ---------------------------------------------------------------- nt_pair_chain
 @pytest.mark.parametrize("lengths,c_s,c_z,hidden,dtype,blocks", [
-    ([3, 0, 17, 40, 1, 33], 384, 128, 512, "bf16", 3),  # fused block boundaries
-    ([5, 20, 0, 9], 64, 64, 128, "bf16", 2),              # fused, the other shape
-    ([6, 2, 11], 48, 24, 40, "bf16", 2),                  # blocks launched in turn
-    ([7, 12, 5], 16, 8, 16, "f32", 3),                    # fp32: blocks in turn
+    ([3, 0, 17, 40, 1, 33], 384, 128, 512, "bf16", 3),  # weight-stationary transition
+    ([5, 20, 0, 9], 64, 64, 128, "bf16", 2),              # persistent transition
+    ([6, 2, 11], 48, 24, 40, "bf16", 2),                  # generic transition
+    ([7, 12, 5], 16, 8, 16, "f32", 3),                    # fp32
     ([4], 384, 128, 512, "bf16", 1),                      # one block
 ])
-@pytest.mark.parametrize("boundary", ["default", "fused"])
-def test_chain_matches_oracle(nt, monkeypatch, boundary, lengths, c_s, c_z, hidden, dtype,
-                              blocks):
-    _boundary(monkeypatch, boundary)
-    announce(f"chain {boundary} {dtype} {lengths} c_s={c_s} c_z={c_z} h={hidden} "
+def test_chain_matches_oracle(nt, lengths, c_s, c_z, hidden, dtype, blocks):
+    announce(f"chain {dtype} {lengths} c_s={c_s} c_z={c_z} h={hidden} "
              f"blocks={blocks}")
     x = pin.make_inputs(lengths, c_s, c_z, hidden, dtype, blocks=blocks, seed=23)
     p = nt.nt_make_partition(lengths)
@@ -197,13 +182,6 @@ def test_chain_matches_oracle(nt, monkeypatch, boundary, lengths, c_s, c_z, hidd
     assert ez <= TOL[dtype] and es <= TOL[dtype]
 
 
-def _boundary(monkeypatch, boundary):
-    if boundary == "fused":
-        monkeypatch.setenv("NT_CHAIN_BOUNDARY", "fused")
-    else:
-        monkeypatch.delenv("NT_CHAIN_BOUNDARY", raising=False)
-
-
 def _block_loop(nt, p, s, ws, z):
     for w in ws:
         s_next = torch.empty_like(s)
@@ -212,14 +190,10 @@ def _block_loop(nt, p, s, ws, z):
     return s
 
 
-@pytest.mark.parametrize("boundary", ["default", "fused"])
 @pytest.mark.parametrize("idx", [3, 4])
-def test_chain_full_size_matches_block_loop(nt, monkeypatch, boundary, idx):
+def test_chain_full_size_matches_block_loop(nt, idx):
     """The chain at full size against the same blocks called one by one (each
-    of which the per-block test holds to the oracle): bit for bit by default;
-    the fused boundary sums the projections in another order, so there the
-    two agree to the bf16 tolerance."""
-    _boundary(monkeypatch, boundary)
+    of which the per-block test holds to the oracle): bit for bit."""
     x = pin.workload_inputs(idx)
     L = x.lengths.tolist()
     announce(f"chain vs block loop {x.name}")
@@ -230,13 +204,8 @@ def test_chain_full_size_matches_block_loop(nt, monkeypatch, boundary, idx):
     s_loop = _block_loop(nt, p, s0, ws, z_loop)
     s_ch, z_ch = nt.nt_pair_chain(p, s0, ws)
     torch.cuda.synchronize()
-    es = scaled_max_err(f64(s_ch, torch), f64(s_loop, torch))
-    ez = scaled_max_err(f64(z_ch, torch), f64(z_loop, torch))
-    announce(f"chain vs loop: s {es:.3e} z {ez:.3e}")
-    assert es <= TOL["bf16"] and ez <= TOL["bf16"]
-    if boundary == "default":
-        np.testing.assert_array_equal(bits(s_ch, torch), bits(s_loop, torch))
-        np.testing.assert_array_equal(bits(z_ch, torch), bits(z_loop, torch))
+    np.testing.assert_array_equal(bits(s_ch, torch), bits(s_loop, torch))
+    np.testing.assert_array_equal(bits(z_ch, torch), bits(z_loop, torch))
 
 
 def test_chain_one_block_is_the_block(nt):
@@ -250,10 +219,8 @@ def test_chain_one_block_is_the_block(nt):
     np.testing.assert_array_equal(bits(z_c, torch), bits(z_b, torch))
 
 
-@pytest.mark.parametrize("boundary", ["default", "fused"])
-def test_chain_in_place(nt, monkeypatch, boundary):
+def test_chain_in_place(nt):
     """s_out may be s_in: every row is read before it is written."""
-    _boundary(monkeypatch, boundary)
     L = [13, 1, 64, 0, 27]
     x = pin.make_inputs(L, 384, 128, 512, "bf16", blocks=4, seed=8)
     p = nt.nt_make_partition(L)
@@ -267,12 +234,10 @@ def test_chain_in_place(nt, monkeypatch, boundary):
     np.testing.assert_array_equal(bits(z_io, torch), bits(z_ref, torch))
 
 
-@pytest.mark.parametrize("boundary", ["default", "fused"])
 @pytest.mark.parametrize("idx", [3])
-def test_chain_per_sample_matches_segmented(nt, monkeypatch, boundary, idx):
+def test_chain_per_sample_matches_segmented(nt, idx):
     """The chain run on each sample alone gives the bits of the batched chain:
-    either boundary computes every row from that row only."""
-    _boundary(monkeypatch, boundary)
+    every kernel computes a row or a cell from that row or cell only."""
     x = pin.workload_inputs(idx)
     L = [int(n) for n in x.lengths]
     announce(f"chain per-sample vs segmented {x.name}")

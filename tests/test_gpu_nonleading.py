@@ -1,8 +1,9 @@
 """GPU parity of the non-leading (S, N_i, C) layout (Appendix A.1's
 non-leading variant, S = 3): the block and its gradients through the C ABI
-against the oracle (fp32: 1e-5; bf16: 2e-2). bf16 gradients use exact
-inputs, on which every relu decision and bf16 operand is exact on both
-sides (see test_gpu_backward.py)."""
+against the oracle (fp32: 1e-5; bf16: 2e-2). bf16 gradients on random
+inputs carry the relu flips fitted within the operand's error window
+(relu_kinks, as in test_gpu_backward.py); exact inputs make every decision
+and operand exact on both sides."""
 import numpy as np
 import pytest
 
@@ -10,6 +11,7 @@ import oracle
 import pair_inputs as pin
 from gpu_util import announce, f64, to_dev, weights_to_dev
 from helpers import TOL, scaled_max_err
+import relu_kinks
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -59,6 +61,7 @@ def test_block_nl_forward(nt, lengths, S, c_s, c_z, hidden, dtype):
     ([7, 12, 5, 16], 3, 16, 8, 16, "f32", False),
     ([8, 16, 4], 3, 64, 128, 512, "bf16", True),
     ([8, 4, 0, 2], 2, 32, 64, 128, "bf16", True),
+    ([9, 20, 0, 13], 3, 64, 128, 512, "bf16", False),   # the pages' widths, random inputs
 ])
 def test_block_nl_backward(nt, lengths, S, c_s, c_z, hidden, dtype, exact):
     announce(f"non-leading backward S={S} c_z={c_z} hidden={hidden} {dtype}")
@@ -77,13 +80,15 @@ def test_block_nl_backward(nt, lengths, S, c_s, c_z, hidden, dtype, exact):
     so, zo = nt.nt_pair_block_nl(p, sd, wd, S)
     g, grads = nt.nt_pair_block_backward_nl(p, sd, zo, wd, S, _f32(gs), _f32(gz))
     torch.cuda.synchronize()
-    ref = oracle.block_backward_nl(lengths, s.f64, {k: v.f64 for k, v in w.items()}, S,
-                                   gs.astype(np.float64), gz.astype(np.float64),
-                                   round_z=oracle.round_bf16 if dtype == "bf16" else None)
+    got = {k: v.cpu().numpy() for k, v in grads.items()}
+    ref, nf, nc = relu_kinks.block_reference(lengths, s.f64, {k: v.f64 for k, v in w.items()},
+                                             gs.astype(np.float64), gz.astype(np.float64),
+                                             got["W1"], dtype == "bf16", S=S)
+    announce(f"relu flips fitted {nf} of {nc} candidates")
     tol = TOL[dtype]
     assert scaled_max_err(g.cpu().numpy(), ref["s"]) <= tol
     for k in ("Wa", "Wb", "W1", "W2", "Wo"):
-        assert scaled_max_err(grads[k].cpu().numpy(), ref[k]) <= tol, k
+        assert scaled_max_err(got[k], ref[k]) <= tol, k
 
 
 def test_nl_with_one_slice_is_the_leading_block(nt):

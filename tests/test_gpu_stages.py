@@ -59,7 +59,9 @@ def test_broadcast_bit_exact(nt, lengths, c_z, dtype):
     np.testing.assert_array_equal(bits(z, torch), want)
 
 
-def test_broadcast_full_size_sampled(nt):
+def test_broadcast_full_size(nt):
+    """The broadcast over the long-square lengths (1,795,072 cells), every
+    cell bit for bit."""
     lengths, c_z = LONG, 128
     announce("broadcast full size, long square lengths")
     T = sum(lengths)
@@ -68,13 +70,8 @@ def test_broadcast_full_size_sampled(nt):
     p = nt.nt_make_partition(lengths)
     z = nt.nt_pair_broadcast(p, to_dev(a, torch), to_dev(b, torch))
     torch.cuda.synchronize()
-    rng = np.random.default_rng(0)
-    o = oracle.partition(lengths)["pair_offsets"]
-    ids = np.unique(np.concatenate([rng.integers(0, p.cells, 20000), o[:-1], o[1:] - 1,
-                                    o[:-1] + lengths]))
-    got = bits(z[torch.from_numpy(ids).cuda()], torch)
-    want = oracle.bf16_bits(oracle.broadcast_cells(lengths, a.f64, b.f64, ids))
-    np.testing.assert_array_equal(got, want)
+    want = oracle.bf16_bits(oracle.broadcast(lengths, a.f64, b.f64))
+    np.testing.assert_array_equal(bits(z, torch), want)
 
 
 # ----------------------------------------------------------------- transition
@@ -113,7 +110,8 @@ def test_transition_parity(nt, lengths, c_z, hidden, dtype):
     assert err <= TOL[dtype], err
 
 
-def test_transition_full_size_sampled(nt):
+def test_transition_full_size(nt):
+    """The unfused transition over the long-square lengths, every cell."""
     lengths, c_z, hidden = LONG, 128, 512
     announce("transition full size, long square lengths")
     z = pin.random_pair_rows(lengths, c_z, "bf16", seed=7)
@@ -121,11 +119,8 @@ def test_transition_full_size_sampled(nt):
     p = nt.nt_make_partition(lengths)
     out = nt.nt_pair_transition(p, to_dev(z, torch), to_dev(W1, torch), to_dev(W2, torch))
     torch.cuda.synchronize()
-    ids = np.unique(np.concatenate([np.random.default_rng(1).integers(0, p.cells, 30000),
-                                    np.arange(256), np.arange(p.cells - 300, p.cells)]))
-    got = f64(out[torch.from_numpy(ids).cuda()], torch)
-    ref = oracle.transition(z.f64[ids], W1.f64, W2.f64)
-    assert scaled_max_err(got, ref) <= TOL["bf16"]
+    ref = oracle.transition(z.f64, W1.f64, W2.f64)
+    assert scaled_max_err(f64(out, torch), ref) <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -204,16 +199,11 @@ def test_broadcast_transition_parity(nt, lengths, c_z, hidden, dtype):
     assert scaled_max_err(f64(out, torch), ref) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("kernel", ["default", "pf", "p32"])
-def test_broadcast_transition_kernels_agree(nt, kernel, monkeypatch):
-    """The fused c_z = 128, hidden = 512 form has three kernels (the
-    weight-stationary one by default, the prefetching and the persistent ones
-    on request); each matches the oracle on a multi-block ragged batch whose
-    blocks mix short and long rows."""
-    if kernel != "default":
-        monkeypatch.setenv("NT_TRANSITION_KERNEL", kernel)
+def test_broadcast_transition_ragged_blocks(nt):
+    """The fused c_z = 128, hidden = 512 form (the weight-stationary kernel)
+    on a multi-block ragged batch whose blocks mix short and long rows."""
     lengths = [3, 40, 1, 17, 64, 5, 33, 2, 29, 8]
-    announce(f"broadcast+transition kernel={kernel} B={len(lengths)}")
+    announce(f"broadcast+transition ragged blocks B={len(lengths)}")
     T = sum(lengths)
     a = pin.random_rows(T, 128, "f32", seed=21)
     b = pin.random_rows(T, 128, "f32", seed=22)
@@ -228,18 +218,14 @@ def test_broadcast_transition_kernels_agree(nt, kernel, monkeypatch):
     assert scaled_max_err(f64(out, torch), ref) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("kernel", ["default", "pf", "p32"])
 @pytest.mark.parametrize("idx", [3, 4])
-def test_broadcast_transition_full_size_sampled(nt, kernel, idx, monkeypatch):
-    """The fused kernels at a full workload size, where every workgroup runs
+def test_broadcast_transition_full_size(nt, idx):
+    """The fused kernel at a full workload size, where every workgroup runs
     many blocks (and stages each next block during the current one), checked
-    on sampled cells: tile and block starts and ends, sample boundaries and
-    random cells."""
-    if kernel != "default":
-        monkeypatch.setenv("NT_TRANSITION_KERNEL", kernel)
+    on every cell against the oracle."""
     x = pin.workload_inputs(idx)
     lengths = x.lengths.tolist()
-    announce(f"broadcast+transition full size {x.name} kernel={kernel}")
+    announce(f"broadcast+transition full size {x.name}")
     T = sum(lengths)
     a = pin.random_rows(T, 128, "f32", seed=31)
     b = pin.random_rows(T, 128, "f32", seed=32)
@@ -250,15 +236,8 @@ def test_broadcast_transition_full_size_sampled(nt, kernel, idx, monkeypatch):
                                     to_dev(W2, torch), z_out=out)
     torch.cuda.synchronize()
     _check_guard(full, 64, p.cells)
-    o = np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64) ** 2)])
-    tiles = np.arange(0, p.cells, 256)
-    ids = np.unique(np.concatenate([np.random.default_rng(idx).integers(0, p.cells, 20000),
-                                    tiles, np.minimum(tiles + 255, p.cells - 1),
-                                    o[:-1], o[1:] - 1, np.arange(p.cells - 300, p.cells)]))
-    ids = ids[(ids >= 0) & (ids < p.cells)]
-    got = f64(out[torch.from_numpy(ids).cuda()], torch)
-    z = oracle.broadcast_cells(lengths, a.f64, b.f64, ids)
-    ref = oracle.transition(z, W1.f64, W2.f64)
+    got = f64(out, torch)
+    ref = oracle.transition(oracle.broadcast(lengths, a.f64, b.f64), W1.f64, W2.f64)
     assert scaled_max_err(got, ref) <= TOL["bf16"]
 
 
@@ -405,7 +384,7 @@ def test_swiglu_transition_in_place_and_eps(nt):
     assert scaled_max_err(f64(zd, torch), _swiglu_ref(z.f64, params, 1e-3)) <= TOL["bf16"]
 
 
-def test_swiglu_transition_full_size_sampled(nt):
+def test_swiglu_transition_full_size(nt):
     x = pin.workload_inputs(3)
     lengths = x.lengths.tolist()
     announce(f"swiglu transition full size {x.name}")
@@ -414,8 +393,4 @@ def test_swiglu_transition_full_size_sampled(nt):
     p = nt.nt_make_partition(lengths)
     out = nt.nt_pair_transition_swiglu(p, to_dev(z, torch), *_swiglu_dev(params))
     torch.cuda.synchronize()
-    o = np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64) ** 2)])
-    ids = np.unique(np.concatenate([np.random.default_rng(3).integers(0, p.cells, 20000),
-                                    o[:-1], o[1:] - 1, np.arange(p.cells - 300, p.cells)]))
-    got = f64(out[torch.from_numpy(ids).cuda()], torch)
-    assert scaled_max_err(got, _swiglu_ref(z.f64[ids], params)) <= TOL["bf16"]
+    assert scaled_max_err(f64(out, torch), _swiglu_ref(z.f64, params)) <= TOL["bf16"]
