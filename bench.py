@@ -27,7 +27,7 @@ import numpy as np  # noqa: E402
 
 import pair_inputs as pin  # noqa: E402
 
-HEADLINE = "high_variation_x4"
+HEADLINE = "long_square_x4"
 METRIC = "pair cells/sec per block (1 GPU) + HBM GB/s & MFMA util vs peak"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
@@ -537,74 +537,189 @@ def padded_same_kernels(x: pin.Inputs, steps: int, warmup: int, torch, nt) -> fl
     return t
 
 
-def padded_baseline(x: pin.Inputs, steps: int, warmup: int, torch):
-    """The same blocks over the B x N_max^2 envelope with PyTorch-native ops
-    (zero-padded singles, validity mask, mean over valid columns): the
-    comparator of the packed path, not part of it."""
-    L = x.lengths.astype(np.int64)
-    B, nmax = len(L), int(L.max())
-    tdt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
-    s = dev(x.s, torch)
-    S0 = torch.zeros((B, nmax, x.c_s), dtype=tdt, device="cuda")
-    eta = np.concatenate([[0], np.cumsum(L)])
-    for i in range(B):
-        S0[i, :L[i]] = s[eta[i]:eta[i + 1]]
-    valid = torch.zeros((B, nmax), dtype=torch.bool, device="cuda")
-    for i in range(B):
-        valid[i, :L[i]] = True
-    colmask = valid[:, None, :, None].to(torch.float32)
-    cnt = torch.from_numpy(L.astype(np.float32)).cuda()[:, None, None]
-    W = [{k: dev(v, torch).t().contiguous() for k, v in wk.items()} for wk in x.weights]
+class PaddedEnvelope:
+    """The padded comparator (DanLing NestedTensor, Section 4.1
+    "Measurement": padding is the baseline; Table 2's caption: padding runs
+    native PyTorch kernels): the same blocks over the B x N_max^2 envelope
+    with PyTorch ops on zero-padded singles, a validity mask over the
+    columns and the mean over valid columns only. Its rounding points are
+    the packed path's, so both meet the same bound against the oracle: fp32
+    projections, the pair state rounded to the storage type as the MLP's
+    operand, the residual added in fp32 and rounded once, an fp32 mean and
+    output projection. It is the comparator of the packed path, not part of
+    it, and it runs on any torch device."""
 
-    def step():
-        S = S0
-        P = None
-        for w in W:
-            U = (S.reshape(-1, x.c_s) @ w["Wa"]).reshape(B, nmax, x.c_z)
-            V = (S.reshape(-1, x.c_s) @ w["Wb"]).reshape(B, nmax, x.c_z)
-            P = (U[:, :, None, :] + V[:, None, :, :]).reshape(-1, x.c_z)
-            H = torch.relu(P @ w["W1"])
-            P = P + H @ w["W2"]
-            M = (P.reshape(B, nmax, nmax, x.c_z).float() * colmask).sum(dim=2) / cnt
-            S = S + (M.reshape(-1, x.c_z) @ w["Wo"].float()).to(tdt).reshape(B, nmax, x.c_s)
+    def __init__(self, x: pin.Inputs, torch, device="cuda"):
+        self.torch, self.x = torch, x
+        L = x.lengths.astype(np.int64)
+        self.B, self.N = len(L), int(L.max()) if len(L) else 0
+        self.tdt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+        self.fp32_out = torch.device(device).type == "cuda"
+        B, N = self.B, self.N
+        s = dev(x.s, torch).to(device)
+        eta = np.concatenate([[0], np.cumsum(L)])
+        self.S0 = torch.zeros((B, N, x.c_s), dtype=self.tdt, device=device)
+        self.colmask = torch.zeros((B, 1, N, 1), dtype=self.tdt, device=device)
+        for i in range(B):
+            self.S0[i, :L[i]] = s[eta[i]:eta[i + 1]]
+            self.colmask[i, :, :L[i]] = 1
+        # every row of an empty sample is padding: its count only avoids 0/0
+        self.cnt = torch.from_numpy(np.maximum(L, 1).astype(np.float32)).to(device)[:, None, None]
+        self.W = []
+        for wk in x.weights:
+            w = {k: dev(v, torch).to(device).t().contiguous() for k, v in wk.items()}  # [in, out]
+            for k in ("Wa", "Wb", "Wo"):
+                w[k] = w[k].float()
+            self.W.append(w)
+
+    def _add_product(self, Z, H, W2):
+        """Z + H W2 in fp32 (the packed path's residual). On a GPU the product
+        of the bf16 operands is written in fp32 by the GEMM itself (torch's
+        out_dtype); where torch has no such kernel the product is rounded to
+        the storage type first, one rounding more than the packed path."""
+        torch = self.torch
+        if self.fp32_out and H.dtype == torch.bfloat16:
+            try:
+                return torch.addmm(Z, H, W2, out_dtype=torch.float32)
+            except (RuntimeError, TypeError, NotImplementedError):
+                self.fp32_out = False
+        Z += (H @ W2).float()
+        return Z
+
+    def step(self):
+        """One pass of every block; returns the last block's singles
+        [B, N_max, c_s] and pair state [B * N_max^2, c_z] (invalid columns
+        zeroed by the mask)."""
+        torch, x, B, N = self.torch, self.x, self.B, self.N
+        S, P = self.S0, None
+        for w in self.W:
+            S2 = S.reshape(-1, x.c_s).float()
+            U = (S2 @ w["Wa"]).view(B, N, 1, x.c_z)
+            V = (S2 @ w["Wb"]).view(B, 1, N, x.c_z)
+            Z = (U + V).view(-1, x.c_z)                      # fp32 envelope
+            H = torch.relu_(Z.to(self.tdt) @ w["W1"])
+            Z = self._add_product(Z, H, w["W2"])
+            del H
+            P = Z.to(self.tdt)
+            del Z
+            P4 = P.view(B, N, N, x.c_z)
+            P4.mul_(self.colmask)                            # mask invalid columns in place
+            M = P4.sum(dim=2, dtype=torch.float32) / self.cnt
+            S = (S2 + M.view(-1, x.c_z) @ w["Wo"]).to(self.tdt).view(B, N, x.c_s)
         return S, P
 
+    def valid(self, S, P):
+        """The valid rows of S and cells of P in packed order (eta and o)."""
+        torch = self.torch
+        L = self.x.lengths.astype(np.int64)
+        rows = [S[i, :n] for i, n in enumerate(L)]
+        P4 = P.view(self.B, self.N, self.N, -1)
+        cells = [P4[i, :n, :n].reshape(-1, P.shape[-1]) for i, n in enumerate(L)]
+        return torch.cat(rows), torch.cat(cells)
+
+
+def padded_report(x: pin.Inputs, t_step: float, packed_peak: int, cells: int, args, torch,
+                  nt) -> dict:
+    """The padded comparator beside a packed measurement: step time, peak
+    allocated bytes and the ratios S_m = T_pad / T and E_m = M_pad / M
+    (DanLing NestedTensor, Section 4.1 "Measurement"), the pair occupancy
+    rho_pair = sum N_i^2 / (B N_max^2), and this library's own block over
+    the envelope (timing only), which separates the cost of padding from the
+    choice of kernels."""
+    env = int(x.lengths.max()) ** 2 * len(x.lengths)
+    log(f"padded envelope baseline {x.name}")
+    t_pad, pad_peak, fp32_out = padded_baseline(x, max(3, args.steps // 4), 2, torch)
+    t_env = padded_same_kernels(x, args.steps, args.warmup, torch, nt)
+    log(f"padded {t_pad * 1e3:.3f} ms/step ({t_pad / t_step:.2f}x); this library's kernels over "
+        f"the envelope: {t_env * 1e3:.3f} ms/step ({t_env / t_step:.2f}x)")
+    return {"ms_per_step": t_pad * 1e3, "speedup": t_pad / t_step, "envelope_cells": env,
+            "rho_pair": cells / env, "peak_bytes_padded": pad_peak,
+            "peak_bytes_packed": packed_peak, "memory_efficiency": pad_peak / max(packed_peak, 1),
+            "impl": "PyTorch ops over B x N_max^2: fp32 projections, bf16 MLP products, fp32 "
+                    "residual and masked mean (the packed path's rounding points)",
+            "second_product_fp32_output": fp32_out,
+            "same_kernels": {"ms_per_step": t_env * 1e3, "speedup": t_env / t_step,
+                             "impl": "this library's block over every sample padded to N_max "
+                                     "(timing only: no validity mask)"}}
+
+
+def padded_baseline(x: pin.Inputs, steps: int, warmup: int, torch):
+    """Step time and peak allocated bytes of the padded comparator."""
+    env = PaddedEnvelope(x, torch)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     base = torch.cuda.memory_allocated()
-    t = time_steps(step, steps, warmup, torch)
+    t = time_steps(env.step, steps, warmup, torch)
     peak = torch.cuda.max_memory_allocated() - base
-    return t, peak
+    fp32_out = env.fp32_out
+    del env
+    torch.cuda.empty_cache()
+    return t, peak, fp32_out
 
 
-def cpu_baseline(x: pin.Inputs, min_seconds: float = 10.0, max_reps: int = 50):
-    """The float64 oracle on this host over the whole workload (all samples, all
-    blocks), repeated until at least min_seconds have passed; cells/s per block
-    over the repetitions."""
+def host_threads() -> int:
+    """Threads the oracle may use on this host: OMP_NUM_THREADS when the
+    environment sets it (GPU hosts give each GPU its share of cores that
+    way), otherwise the cores this process may run on."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    return len(os.sched_getaffinity(0))
+
+
+def oracle_rate(x: pin.Inputs, min_seconds: float, threads: int) -> dict:
+    """The float64 oracle (oracle.block, as it stands) timed on this host
+    with its BLAS limited to `threads`: the workload's blocks in order, each
+    over its samples in batch order, one oracle.block call per sample (the
+    block is sample-local, so this is the batch's arithmetic), until every
+    block is done or at least min_seconds have passed. Returns pair cells/s
+    per block over the sample-blocks timed."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        threads = None
-    L = x.lengths.astype(np.int64).tolist()
-    cells = int(sum(n * n for n in L))
+    from threadpoolctl import threadpool_limits
+    L = [int(n) for n in x.lengths]
+    eta = np.concatenate([[0], np.cumsum(L)]).astype(np.int64)
     s = x.s.f64
     ws = [{k: v.f64 for k, v in wk.items()} for wk in x.weights]
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.chain(L, s, ws)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds or reps >= max_reps:
-            break
-    return {"value": cells * len(ws) * reps / dt, "unit": "pair cells/s per block",
-            "cores": threads if threads else len(os.sched_getaffinity(0)),
-            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "seconds": dt,
-            "sample": f"the whole workload ({len(L)} samples, {cells} cells, {len(ws)} blocks) "
-                      f"x {reps} repetitions, float64 numpy oracle"}
+    cells = units = 0
+    with threadpool_limits(limits=threads):
+        t0 = time.perf_counter()
+        dt = 0.0
+        for w in ws:
+            for i, n in enumerate(L):
+                oracle.block([n], s[eta[i]:eta[i + 1]], w)
+                cells += n * n
+                units += 1
+                dt = time.perf_counter() - t0
+                if dt >= min_seconds:
+                    break
+            if dt >= min_seconds:
+                break
+    total = len(ws) * len(L)
+    return {"value": cells / dt, "unit": "pair cells/s per block", "cores": threads,
+            "kind": "oracle", "seconds": dt,
+            "sample": f"{units} of the {total} sample-blocks of {x.name} ({cells} cells), "
+                      f"in order, one float64 oracle.block call each"}
+
+
+def cpu_baseline(x: pin.Inputs, min_seconds: float = 12.0) -> dict:
+    """The headline workload's oracle rate on the host's thread share, then
+    the protocol's companions: the same on every other workload (a few
+    seconds each), and one thread on the three smallest workloads."""
+    threads = host_threads()
+    out = oracle_rate(x, min_seconds, threads)
+    out["host_cpus"] = len(os.sched_getaffinity(0))
+    out["thread_env"] = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS",
+                                                         "OPENBLAS_NUM_THREADS")}
+    regimes, one = {}, {}
+    for w in pin.WORKLOADS:
+        xo = x if w.name == x.name else pin.workload_inputs(w.index)
+        if w.name != x.name:
+            regimes[w.name] = oracle_rate(xo, 3.0, threads)
+        if w.index <= 2:
+            one[w.name] = oracle_rate(xo, 4.0, 1)
+    out["regimes"] = regimes
+    out["one_thread"] = one
+    return out
 
 
 def main():
@@ -726,33 +841,23 @@ def main():
     }
 
     if not args.quick:
-        env = int(x.lengths.max()) ** 2 * len(x.lengths)
-        log("padded envelope baseline")
-        t_pad, pad_peak = padded_baseline(x, max(3, args.steps // 4), 2, torch)
-        result["padded"] = {"ms_per_step": t_pad * 1e3, "speedup": t_pad / t_step,
-                            "envelope_cells": env, "rho_pair": r.cells / env,
-                            "peak_bytes_padded": pad_peak, "peak_bytes_packed": packed_peak,
-                            "memory_efficiency": pad_peak / max(packed_peak, 1),
-                            "impl": "PyTorch ops over B x N_max^2 (bf16 matmul, masked mean)"}
-        t_env = padded_same_kernels(x, args.steps, args.warmup, torch, nt)
-        log(f"this library's kernels over the envelope: {t_env * 1e3:.3f} ms/step "
-            f"({t_env / t_step:.2f}x the packed step)")
-        result["padded_same_kernels"] = {
-            "ms_per_step": t_env * 1e3, "speedup": t_env / t_step, "envelope_cells": env,
-            "impl": "this library's block over every sample padded to N_max "
-                    "(timing only: no validity mask)"}
+        result["padded"] = padded_report(x, t_step, packed_peak, r.cells, args, torch, nt)
         result["granularity"] = granularity(x, r, t_step, args, torch, nt)
-        result["rectangular"] = rectangular(x, args, torch, nt)
-        result["non_leading"] = non_leading(x, args, torch, nt)
+        del r
+        torch.cuda.empty_cache()
         regimes = {}
         for other in pin.WORKLOADS[1:]:
             if other.name == w.name:
                 continue
             log(f"regime {other.name}")
             xo = pin.workload_inputs(other.index)
+            torch.cuda.synchronize()
+            torch.cuda.reset_peak_memory_stats()
+            base_o = torch.cuda.memory_allocated()
             ro = PackedRunner(xo, torch, nt)
             settle(ro.step, args.settle_ms / 2, torch)  # the GPU idled while inputs were drawn
             to = time_steps(ro.step, args.steps, args.warmup, torch)
+            peak_o = torch.cuda.max_memory_allocated() - base_o
             ko = kernel_rooflines(ro, args.kernel_reps)
             regimes[other.name] = {
                 "value": ro.cells * other.blocks / to, "ms_per_step": to * 1e3,
@@ -761,8 +866,16 @@ def main():
                                 "frac": v["frac"]} for k, v in ko.items()}}
             if other.blocks > 1:
                 regimes[other.name]["granularity"] = granularity(xo, ro, to, args, torch, nt)
+            cells_o = ro.cells
             del ro
             torch.cuda.empty_cache()
+            if other.blocks > 1:
+                regimes[other.name]["padded"] = padded_report(xo, to, peak_o, cells_o, args,
+                                                              torch, nt)
+            if other.name == "high_variation_x4":
+                # the variants on the paper's high-variation regime
+                result["rectangular"] = rectangular(xo, args, torch, nt)
+                result["non_leading"] = non_leading(xo, args, torch, nt)
         result["regimes"] = regimes
     if not args.no_cpu_baseline and not args.quick:
         log("cpu baseline (oracle)")

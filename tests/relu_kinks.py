@@ -76,7 +76,18 @@ def unit_terms(G, W2, cells, units):
     return np.einsum("ij,ji->i", G[cells], W2[:, units]) if len(cells) else np.zeros(0)
 
 
-def fit_flips(resid, group, vectors, max_per_group=12):
+def _best_subset(r, V, max_candidates=12):
+    """The 0/1 weights x minimising max |r - x V| (V: [k, d]), over all 2^k
+    subsets. A group with more candidates than max_candidates is refused:
+    the test's batch is then too large for its window."""
+    k = V.shape[0]
+    if k > max_candidates:
+        raise AssertionError(f"{k} candidates in one group: use a smaller batch")
+    masks = np.array(list(itertools.product((0.0, 1.0), repeat=k)))  # [2^k, k]
+    return masks[int(np.argmin(np.max(np.abs(r[None, :] - masks @ V), axis=1)))]
+
+
+def fit_flips(resid, group, vectors):
     """resid [n_groups, d]: kernel output minus reference, one row per group;
     group [n]: the group of each candidate; vectors [n, d]: the change a
     flip of that candidate makes to its group's row. For every group, the
@@ -91,13 +102,7 @@ def fit_flips(resid, group, vectors, max_per_group=12):
     ends = np.r_[starts[1:], len(order)]
     for a, b in zip(starts, ends):
         idx = order[a:b]
-        k = len(idx)
-        if k > max_per_group:
-            raise AssertionError(f"{k} candidates in one group: the window is too wide")
-        masks = np.array(list(itertools.product((0.0, 1.0), repeat=k)))  # [2^k, k]
-        r = resid[g_sorted[a]][None, :] - masks @ vectors[idx]
-        best = int(np.argmin(np.max(np.abs(r), axis=1)))
-        chosen[idx] = masks[best].astype(bool)
+        chosen[idx] = _best_subset(resid[g_sorted[a]], vectors[idx]).astype(bool)
     return chosen
 
 

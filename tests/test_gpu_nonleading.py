@@ -81,10 +81,16 @@ def test_block_nl_backward(nt, lengths, S, c_s, c_z, hidden, dtype, exact):
     g, grads = nt.nt_pair_block_backward_nl(p, sd, zo, wd, S, _f32(gs), _f32(gz))
     torch.cuda.synchronize()
     got = {k: v.cpu().numpy() for k, v in grads.items()}
-    ref, nf, nc = relu_kinks.block_reference(lengths, s.f64, {k: v.f64 for k, v in w.items()},
-                                             gs.astype(np.float64), gz.astype(np.float64),
-                                             got["W1"], dtype == "bf16", S=S)
-    announce(f"relu flips fitted {nf} of {nc} candidates")
+    W64 = {k: v.f64 for k, v in w.items()}
+    if exact:
+        # every operand and pre-activation is exact on both sides
+        ref = oracle.block_backward_nl(lengths, s.f64, W64, S, gs.astype(np.float64),
+                                       gz.astype(np.float64))
+    else:
+        ref, nf, nc = relu_kinks.block_reference(lengths, s.f64, W64, gs.astype(np.float64),
+                                                 gz.astype(np.float64), got["W1"],
+                                                 dtype == "bf16", S=S)
+        announce(f"relu flips fitted {nf} of {nc} candidates")
     tol = TOL[dtype]
     assert scaled_max_err(g.cpu().numpy(), ref["s"]) <= tol
     for k in ("Wa", "Wb", "W1", "W2", "Wo"):

@@ -394,3 +394,31 @@ def test_swiglu_transition_full_size(nt):
     out = nt.nt_pair_transition_swiglu(p, to_dev(z, torch), *_swiglu_dev(params))
     torch.cuda.synchronize()
     assert scaled_max_err(f64(out, torch), _swiglu_ref(z.f64, params)) <= TOL["bf16"]
+
+
+def test_broadcast_transition_beyond_buffer_range(nt):
+    """More than 2^22 single rows: a and b (fp32, 512 bytes a row) no longer
+    fit the 32-bit buffer range the weight-stationary kernel addresses them
+    with, and the fused 128/512 form runs the persistent kernel instead (its
+    partition decoded from global memory: 2,097,153 samples). Lengths 1, 2
+    and 3 in turn; sampled cells, first and last cells of samples and the
+    ragged end against the oracle."""
+    k = 699051
+    lengths = [1, 2, 3] * k + [1, 2, 3]
+    T = sum(lengths)
+    assert T > (2 ** 31 - 1) // 512
+    announce(f"broadcast+transition beyond the buffer range T={T}")
+    a = pin.random_rows(T, 128, "f32", seed=61)
+    b = pin.random_rows(T, 128, "f32", seed=62)
+    W1, W2 = _mlp(128, 512, "bf16", seed=63)
+    p = nt.nt_make_partition(lengths)
+    out = nt.nt_pair_broadcast_transition(p, to_dev(a, torch), to_dev(b, torch),
+                                          to_dev(W1, torch), to_dev(W2, torch))
+    torch.cuda.synchronize()
+    o = np.concatenate([[0], np.cumsum(np.square(np.asarray(lengths, dtype=np.int64)))])
+    rng = np.random.default_rng(64)
+    ids = np.unique(np.concatenate([rng.integers(0, p.cells, 20000), o[:2000], o[-2000:-1],
+                                    np.arange(p.cells - 300, p.cells)]))
+    got = f64(out[torch.from_numpy(ids).cuda()], torch)
+    ref = oracle.transition(oracle.broadcast_cells(lengths, a.f64, b.f64, ids), W1.f64, W2.f64)
+    assert scaled_max_err(got, ref) <= TOL["bf16"]
