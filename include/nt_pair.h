@@ -263,6 +263,25 @@ nt_status nt_pair_block(const nt_partition* p, const void* s_in, void* s_out, vo
                         nt_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nt_pair_block without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). The workspace nt_pair_block
+ * takes (fp32 a, b and m, nt_block_workspace_bytes) lives in a static device
+ * array of 16 MiB that every GPU the library runs on holds until the process
+ * ends: 3 x (T * c_z * 4 bytes, rounded up to 256) <= 16 MiB, so T <= 10,922
+ * single rows at c_z = 128. The call itself allocates nothing and clears nothing (every
+ * launch writes the scratch before reading it); the first call on a device
+ * looks up the array's address there. Calls on one GPU share the array, so
+ * calls that overlap in time on one GPU (other streams, other threads) race;
+ * serialise them. Square partitions. Inputs, outputs and errors as
+ * nt_pair_block, plus NT_ERR_WORKSPACE when the partition needs more scratch
+ * than the array holds (checked before anything is enqueued).
+ */
+nt_status nt_pair_block_noalloc(const nt_partition* p, const void* s_in, void* s_out,
+                                void* z_out, const nt_block_weights* w, int32_t c_s, int32_t c_z,
+                                int32_t hidden, nt_dtype dtype, void* stream);
+
+/*
  * Workspace bytes nt_pair_chain needs: the block's, plus one [T, c_s] buffer
  * of singles (in `dtype`) when nblocks >= 2.
  */

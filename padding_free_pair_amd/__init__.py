@@ -22,7 +22,8 @@ __all__ = ["NtError", "Partition", "nt_partition_sizes", "nt_make_partition",
            "nt_decode_cells",
            "nt_pair_broadcast", "nt_pair_transition", "nt_pair_broadcast_transition",
            "nt_pair_transition_swiglu", "nt_pair_reduce",
-           "nt_block_workspace_bytes", "nt_pair_block", "nt_chain_workspace_bytes",
+           "nt_block_workspace_bytes", "nt_pair_block", "nt_pair_block_noalloc",
+           "nt_chain_workspace_bytes",
            "nt_pair_chain", "nt_last_error", "nt_version",
            "NT_F32", "NT_BF16"]
 
@@ -382,6 +383,30 @@ def nt_pair_block(p: Partition, s_in, weights, s_out=None, z_out=None, workspace
                                        _ptr(z_out), ctypes.byref(wst), c_s, c_z, hidden,
                                        _dtype_code(s_in), _ptr(workspace),
                                        _nbytes(workspace), _stream(stream, s_in.device)))
+    return s_out, z_out
+
+
+def nt_pair_block_noalloc(p: Partition, s_in, weights, s_out=None, z_out=None, stream=None):
+    """nt_pair_block with its workspace in the library's static device
+    scratch (nt_pair_block_noalloc): the native call allocates nothing.
+    Pass s_out and z_out to keep this wrapper from allocating them."""
+    torch = _torch()
+    if isinstance(weights, dict):
+        weights = [weights[k] for k in ("Wa", "Wb", "W1", "W2", "Wo")]
+    Wa, Wb, W1, W2, Wo = weights
+    c_s, c_z, hidden = s_in.shape[-1], Wa.shape[0], W1.shape[0]
+    if s_out is None:
+        s_out = torch.empty_like(s_in)
+    if z_out is None:
+        z_out = torch.empty((p.cells, c_z), dtype=s_in.dtype, device=s_in.device)
+    _expect(p, "s_in", s_in, (p.T, c_s))
+    _expect(p, "s_out", s_out, (p.T, c_s), s_in.dtype)
+    _expect(p, "z_out", z_out, (p.cells, c_z), s_in.dtype)
+    _expect_weights(p, weights, c_s, c_z, hidden, s_in.dtype)
+    wst = NtBlockWeights(*[_ptr(w) for w in weights])
+    _check(_native.lib().nt_pair_block_noalloc(ctypes.byref(p.struct), _ptr(s_in), _ptr(s_out),
+                                               _ptr(z_out), ctypes.byref(wst), c_s, c_z, hidden,
+                                               _dtype_code(s_in), _stream(stream, s_in.device)))
     return s_out, z_out
 
 

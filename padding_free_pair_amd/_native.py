@@ -17,7 +17,8 @@ EXPORTS = ("nt_partition_sizes", "nt_make_partition", "nt_partition_sizes_rect",
            "nt_make_partition_rect", "nt_decode_cells", "nt_pair_broadcast",
            "nt_pair_transition", "nt_pair_broadcast_transition", "nt_pair_transition_swiglu",
            "nt_pair_reduce",
-           "nt_block_workspace_bytes", "nt_pair_block", "nt_pair_block_rect",
+           "nt_block_workspace_bytes", "nt_pair_block", "nt_pair_block_noalloc",
+           "nt_pair_block_rect",
            "nt_chain_workspace_bytes", "nt_pair_chain",
            "nt_loss_workspace_bytes", "nt_pair_loss_eq5", "nt_pair_reduce_backward",
            "nt_pair_broadcast_backward", "nt_transition_backward_workspace_bytes",
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
         "nt_block_workspace_bytes": [part, i32, i32, i32, ctypes.c_int, P(sz)],
         "nt_pair_block": [part, vp, vp, vp, P(NtBlockWeights), i32, i32, i32, ctypes.c_int, vp,
                           sz, vp],
+        "nt_pair_block_noalloc": [part, vp, vp, vp, P(NtBlockWeights), i32, i32, i32,
+                                  ctypes.c_int, vp],
         "nt_chain_workspace_bytes": [part, i32, i32, i32, i32, ctypes.c_int, P(sz)],
         "nt_pair_chain": [part, vp, vp, vp, P(NtBlockWeights), i32, i32, i32, i32, ctypes.c_int,
                           vp, sz, vp],

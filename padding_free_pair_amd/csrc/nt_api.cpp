@@ -658,6 +658,26 @@ nt_status nt_pair_block(const nt_partition* p, const void* s_in, void* s_out, vo
                     workspace_bytes, stream);
 }
 
+nt_status nt_pair_block_noalloc(const nt_partition* p, const void* s_in, void* s_out,
+                                void* z_out, const nt_block_weights* w, int32_t c_s, int32_t c_z,
+                                int32_t hidden, nt_dtype dtype, void* stream) {
+  NT_TRY(check_partition(p));
+  if (p->col_offsets != p->single_offsets)
+    return fail(NT_ERR_INVALID, "rectangular partition: use nt_pair_block_rect");
+  NT_TRY(check_dtype(dtype));
+  NT_TRY(check_widths(c_s, c_z, hidden));
+  const uint64_t need = block_workspace(p->T, p->T_cols, c_z, dtype).total;
+  if (need > nt::kStaticScratchBytes)
+    return fail(NT_ERR_WORKSPACE,
+                "the block needs %llu bytes of scratch (T = %lld rows of 3 x c_z fp32 values); "
+                "the static scratch holds %zu: use nt_pair_block with a workspace",
+                (unsigned long long)need, (long long)p->T, nt::kStaticScratchBytes);
+  void* ws = nullptr;
+  NT_TRY(hip_status(nt::static_scratch(&ws), "static scratch address"));
+  return pair_block(p, s_in, s_in, s_out, z_out, w, c_s, c_z, hidden, dtype, ws,
+                    nt::kStaticScratchBytes, stream);
+}
+
 // Chain workspace: the block's, then (for two or more blocks) one bf16/fp32
 // buffer of T x c_s singles that the chain alternates with s_out.
 static uint64_t chain_workspace(const nt_partition* p, int32_t nblocks, int32_t c_s, int32_t c_z,

@@ -165,6 +165,10 @@ int wgrad_rc_slices(int64_t cells);
 hipError_t launch_wgrad_rc(const void* z, const void* Gb, const void* W1, const void* W2T,
                            float* dW1, float* dW2, float* part, int64_t cells, int slices,
                            hipStream_t stream);
+// Static scratch of nt_pair_block_noalloc (nt_static.hip): bytes per
+// device, and its device address on the current device.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+hipError_t static_scratch(void** ptr);
 // Compute units of the current device (cached per device).
 int device_cu_count();
 // Matrix-core transition gradient (bf16, c_z = 128, hidden = 512): W2T =

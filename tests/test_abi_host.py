@@ -448,3 +448,16 @@ def test_binding_rejects_bad_stage_extents(lib):
         grads["Wa"] = torch.zeros((16, 8))
         nt.nt_pair_block_backward(p, s, torch.zeros((13, 8)), w, torch.zeros((5, 16)),
                                   grads=grads)
+
+
+def test_noalloc_rejects_oversized_partition(lib):
+    """The static scratch holds 16 MiB: a partition needing more is refused
+    with NT_ERR_WORKSPACE before any device work (T = 10,923 at c_z = 128)."""
+    p = fake_partition(B=1, T=10923, cells=10923 * 10923)
+    w = _native.NtBlockWeights(FAKE + 0x400000, FAKE + 0x410000, FAKE + 0x420000,
+                               FAKE + 0x430000, FAKE + 0x440000)
+    st = lib.nt_pair_block_noalloc(ctypes.byref(p), FAKE + 0x100000, FAKE + 0x200000,
+                                   FAKE + 0x300000, ctypes.byref(w), 384, 128, 512,
+                                   _native.NT_BF16, None)
+    assert st == _native.NT_ERR_WORKSPACE
+    assert "static scratch" in lib.nt_last_error().decode()
