@@ -53,10 +53,12 @@ from .pair_block import (  # noqa: F401
     partition, decode_cells, broadcast, transition, reduce_mean, project,
     block, chain, block_padded_masked, block_gather, block_bruteforce,
     round_bf16, bf16_bits, block_cells, block_rows, dense_block, broadcast_cells,
-    layer_norm, transition_swiglu,
+    layer_norm, transition_swiglu, block_swiglu, chain_swiglu,
     partition_rect, decode_cells_rect, broadcast_rect, reduce_mean_rect, block_rect,
 )
 from .backward import (  # noqa: F401
     loss_weights, loss_eq5, reduce_mean_backward, broadcast_backward, transition_backward,
     block_backward, chain_loss, chain_backward, block_nl, block_backward_nl,
+    layer_norm_backward, transition_swiglu_backward, block_swiglu_backward, chain_swiglu_loss,
+    chain_swiglu_backward,
 )

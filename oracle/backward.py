@@ -28,17 +28,23 @@ step by step in reverse order, written from the forward's definitions:
   m[r] = (1/M_i) sum_c z'[..]      G[o_i + r M_i + c] += g_m[r] / M_i
   s~ = s + m Wo^T                  g_m = g_s~ Wo; dWo = g_s~^T m; g_s = g_s~ + ...
 
-Pins (tests/test_oracle_pins.py): central finite differences of the whole
-loss through a two-block chain, a hand-evaluated Equation 5, adjoint
-(dot-product) identities of the broadcast and the mean, and the
-reduction of the transition's gradient to the closed form of a linear map
-when every hidden unit is active.
+The block with the paper's own transition (pre-normalised SwiGLU,
+pair_block.block_swiglu) has its gradients here too: the chain rule through
+the SwiGLU gate, its three products and the LayerNorm over the c_z features.
+
+Pins (tests/test_oracle_backward_pins.py): central finite differences of the
+whole loss through two-block chains (ReLU and SwiGLU), a hand-evaluated
+Equation 5, adjoint (dot-product) identities of the broadcast and the mean,
+LayerNorm's adjoint identities, the closed forms of an all-active ReLU
+transition and of a SwiGLU transition with zero output weights, and
+PyTorch's autograd on dense per-sample formulations.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .pair_block import _CHUNK_ROWS, block, broadcast, project, reduce_mean, transition
+from .pair_block import (_CHUNK_ROWS, block, block_swiglu, broadcast, layer_norm, project,
+                         reduce_mean, transition)
 
 
 # ------------------------------------------------------------------ Eq. 5
@@ -142,6 +148,61 @@ def transition_backward(z, W1, W2, G):
     return g_z, dW1, dW2
 
 
+def layer_norm_backward(z, gamma, g_x, eps):
+    """Adjoint of x = xhat * gamma + beta, xhat = (z - mean) / sqrt(var + eps)
+    over the features of each row (biased variance), for an incoming g_x.
+    With g_xhat = g_x * gamma, the mean's and the variance's dependence on
+    every feature give g_z = (g_xhat - mean(g_xhat) - xhat mean(g_xhat xhat))
+    / sqrt(var + eps); dgamma = sum over rows of g_x xhat, dbeta = sum of
+    g_x. Returns (g_z, dgamma, dbeta)."""
+    z = np.asarray(z, dtype=np.float64)
+    g_x = np.asarray(g_x, dtype=np.float64)
+    gamma = np.asarray(gamma, dtype=np.float64)
+    mu = z.mean(axis=-1, keepdims=True)
+    rstd = 1.0 / np.sqrt(np.square(z - mu).mean(axis=-1, keepdims=True) + eps)
+    xhat = (z - mu) * rstd
+    gh = g_x * gamma
+    g_z = rstd * (gh - gh.mean(axis=-1, keepdims=True)
+                  - xhat * (gh * xhat).mean(axis=-1, keepdims=True))
+    return g_z, (g_x * xhat).sum(axis=0), g_x.sum(axis=0)
+
+
+def transition_swiglu_backward(z, gamma, beta, Wg, Wu, Wd, G, eps=1e-5):
+    """Gradients of z' = z + (silu(x Wg^T) * (x Wu^T)) Wd^T, x = LN(z), for an
+    incoming G = dL/dz'. With g = x Wg^T, u = x Wu^T, s = sigmoid(g) and the
+    gated activation A = g s u:
+      dWd = G^T A,  g_A = G Wd,
+      g_u = g_A g s,  g_g = g_A u s (1 + g (1 - s))   (silu' = s (1 + g (1 - s))),
+      dWu = g_u^T x,  dWg = g_g^T x,  g_x = g_u Wu + g_g Wg,
+      g_z = G + LN's adjoint of g_x (layer_norm_backward).
+    Returns (g_z, dgamma, dbeta, dWg, dWu, dWd)."""
+    z = np.asarray(z, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    Wg, Wu, Wd = (np.asarray(w, dtype=np.float64) for w in (Wg, Wu, Wd))
+    g_z = np.empty_like(z)
+    dWg, dWu, dWd = np.zeros_like(Wg), np.zeros_like(Wu), np.zeros_like(Wd)
+    dgamma = np.zeros(z.shape[1])
+    dbeta = np.zeros(z.shape[1])
+    for c in range(0, z.shape[0], _CHUNK_ROWS):
+        zc, Gc = z[c:c + _CHUNK_ROWS], G[c:c + _CHUNK_ROWS]
+        x = layer_norm(zc, gamma, beta, eps)
+        g = x @ Wg.T
+        u = x @ Wu.T
+        sg = 1.0 / (1.0 + np.exp(-g))
+        A = g * sg * u
+        dWd += Gc.T @ A
+        gA = Gc @ Wd
+        gu = gA * g * sg
+        gg = gA * u * sg * (1.0 + g * (1.0 - sg))
+        dWu += gu.T @ x
+        dWg += gg.T @ x
+        gzl, dga, dbe = layer_norm_backward(zc, gamma, gu @ Wu + gg @ Wg, eps)
+        g_z[c:c + _CHUNK_ROWS] = Gc + gzl
+        dgamma += dga
+        dbeta += dbe
+    return g_z, dgamma, dbeta, dWg, dWu, dWd
+
+
 # ------------------------------------------------------------- the block
 def block_backward(lengths, s, w, g_s_out, g_z_out=None):
     """Gradients of one square block (pair_block.block) for incoming g_s_out
@@ -166,6 +227,60 @@ def block_backward(lengths, s, w, g_s_out, g_z_out=None):
     g_a, g_b = broadcast_backward(lengths, lengths, g_z)
     g_s = g_s_out + g_a @ W["Wa"] + g_b @ W["Wb"]
     return {"s": g_s, "Wa": g_a.T @ s, "Wb": g_b.T @ s, "W1": dW1, "W2": dW2, "Wo": dWo}
+
+
+def block_swiglu_backward(lengths, s, w, g_s_out, g_z_out=None, eps=1e-5):
+    """Gradients of pair_block.block_swiglu for incoming g_s_out and,
+    optionally, g_z_out: the steps of block_backward with the SwiGLU
+    transition's adjoint. Returns a dict with "s" and the gradient of every
+    weight (Wa, Wb, Wo, ln_gamma, ln_beta, Wg, Wu, Wd)."""
+    s = np.asarray(s, dtype=np.float64)
+    g_s_out = np.asarray(g_s_out, dtype=np.float64)
+    W = {k: np.asarray(v, dtype=np.float64) for k, v in w.items()}
+    a = project(s, W["Wa"])
+    b = project(s, W["Wb"])
+    z = broadcast(lengths, a, b)
+    zt = block_swiglu(lengths, s, W, eps)[1]
+    m = reduce_mean(lengths, zt)
+    g_m = g_s_out @ W["Wo"]
+    dWo = g_s_out.T @ m
+    G = reduce_mean_backward(lengths, lengths, g_m)
+    if g_z_out is not None:
+        G = G + np.asarray(g_z_out, dtype=np.float64)
+    g_z, dga, dbe, dWg, dWu, dWd = transition_swiglu_backward(
+        z, W["ln_gamma"], W["ln_beta"], W["Wg"], W["Wu"], W["Wd"], G, eps)
+    g_a, g_b = broadcast_backward(lengths, lengths, g_z)
+    g_s = g_s_out + g_a @ W["Wa"] + g_b @ W["Wb"]
+    return {"s": g_s, "Wa": g_a.T @ s, "Wb": g_b.T @ s, "Wo": dWo, "ln_gamma": dga,
+            "ln_beta": dbe, "Wg": dWg, "Wu": dWu, "Wd": dWd}
+
+
+def chain_swiglu_loss(lengths, s, ws, eps=1e-5):
+    """Equation 5 of a chain of SwiGLU blocks."""
+    z = None
+    x = np.asarray(s, dtype=np.float64)
+    for w in ws:
+        x, z = block_swiglu(lengths, x, w, eps)
+    return loss_eq5(lengths, lengths, x, z)[0]
+
+
+def chain_swiglu_backward(lengths, s, ws, eps=1e-5):
+    """Loss and gradients of a chain of SwiGLU blocks under Equation 5.
+    Returns (L, g_s, [per-block weight gradients])."""
+    xs = [np.asarray(s, dtype=np.float64)]
+    z = None
+    for w in ws:
+        x, z = block_swiglu(lengths, xs[-1], w, eps)
+        xs.append(x)
+    L, g_x, g_z = loss_eq5(lengths, lengths, xs[-1], z)
+    grads = [None] * len(ws)
+    g = g_x
+    for k in range(len(ws) - 1, -1, -1):
+        r = block_swiglu_backward(lengths, xs[k], ws[k], g, g_z if k == len(ws) - 1 else None,
+                                  eps)
+        g = r.pop("s")
+        grads[k] = r
+    return L, g, grads
 
 
 def chain_loss(lengths, s, ws, S=1):

@@ -266,6 +266,29 @@ def chain(lengths, s, ws):
     return s, z
 
 
+def block_swiglu(lengths, s, w, eps=1e-5):
+    """The block with the paper's own transition (Eq. 1 with h o LN_{C_p};
+    Appendix A.1: a residual, pre-normalised SwiGLU of expansion four) in
+    place of the ReLU MLP; every other step as in block(). w holds Wa, Wb,
+    Wo and the transition's ln_gamma, ln_beta, Wg, Wu, Wd. Returns
+    (s_out, z_out)."""
+    s = np.asarray(s, dtype=np.float64)
+    a = project(s, w["Wa"])
+    b = project(s, w["Wb"])
+    z = broadcast(lengths, a, b)
+    zt = transition_swiglu(z, w["ln_gamma"], w["ln_beta"], w["Wg"], w["Wu"], w["Wd"], eps)
+    m = reduce_mean(lengths, zt)
+    return s + project(m, w["Wo"]), zt
+
+
+def chain_swiglu(lengths, s, ws, eps=1e-5):
+    """SwiGLU blocks in sequence, as chain() chains ReLU blocks."""
+    z = None
+    for w in ws:
+        s, z = block_swiglu(lengths, s, w, eps)
+    return s, z
+
+
 # ------------------------------------------------- independent forms (pins)
 def dense_block(X, w):
     """The dense per-sample computation of one sample X [N, c_s] (Appendix A's

@@ -184,3 +184,104 @@ def test_non_leading_gradients_match_finite_differences():
     g = oracle.block_backward_nl(lengths, s, w, S, gx, gz)
     params = {"s": s, **w}
     _fd_check(loss, params, g)
+
+
+# ------------------------------------------------ the SwiGLU block (Eq. 1)
+def _swiglu_weights(rng, c_s, c_z, hidden):
+    return {"Wa": rng.normal(0.0, 1.0 / np.sqrt(c_s), (c_z, c_s)),
+            "Wb": rng.normal(0.0, 1.0 / np.sqrt(c_s), (c_z, c_s)),
+            "Wo": rng.normal(0.0, 1.0 / np.sqrt(c_z), (c_s, c_z)),
+            "ln_gamma": 1.0 + 0.3 * rng.normal(size=c_z),
+            "ln_beta": 0.2 * rng.normal(size=c_z),
+            "Wg": rng.normal(0.0, 1.0 / np.sqrt(c_z), (hidden, c_z)),
+            "Wu": rng.normal(0.0, 1.0 / np.sqrt(c_z), (hidden, c_z)),
+            "Wd": rng.normal(0.0, 1.0 / np.sqrt(hidden), (c_z, hidden))}
+
+
+@pytest.mark.parametrize("lengths,seed", [([2, 3, 1], 10), ([3, 0, 2], 11)])
+def test_swiglu_chain_gradients_match_finite_differences(lengths, seed):
+    rng = np.random.default_rng(seed)
+    c_s, c_z, hidden = 4, 3, 5
+    s = rng.normal(size=(sum(lengths), c_s))
+    ws = [_swiglu_weights(rng, c_s, c_z, hidden) for _ in range(2)]
+    L, g_s, grads = oracle.chain_swiglu_backward(lengths, s, ws)
+    assert L == pytest.approx(oracle.chain_swiglu_loss(lengths, s, ws), rel=1e-14)
+    params = {"s": s}
+    flat = {"s": g_s}
+    for k, (w, g) in enumerate(zip(ws, grads)):
+        for name in w:
+            params[f"{name}{k}"] = w[name]
+            flat[f"{name}{k}"] = g[name]
+    _fd_check(lambda: oracle.chain_swiglu_loss(lengths, s, ws), params, flat)
+
+
+def test_layer_norm_adjoint_identities():
+    # LN(z + c 1) = LN(z) and LN(k z) = LN(z) (eps = 0): the adjoint of every
+    # row is orthogonal to the ones vector and to the row itself; with the
+    # plain mean removed, <g_z, dz> equals <g_x, d LN> for any direction dz
+    rng = np.random.default_rng(12)
+    z = rng.normal(size=(7, 9))
+    gamma, gx = 1 + rng.normal(size=9), rng.normal(size=(7, 9))
+    g_z, dgamma, dbeta = oracle.layer_norm_backward(z, gamma, gx, 0.0)
+    np.testing.assert_allclose(g_z.sum(axis=1), 0.0, atol=1e-12)
+    np.testing.assert_allclose((g_z * z).sum(axis=1), 0.0, atol=1e-11)
+    dz = rng.normal(size=z.shape)
+    h = 1e-6
+    dx = (oracle.layer_norm(z + h * dz, gamma, 0 * gamma, 0.0)
+          - oracle.layer_norm(z - h * dz, gamma, 0 * gamma, 0.0)) / (2 * h)
+    assert float((g_z * dz).sum()) == pytest.approx(float((gx * dx).sum()), rel=1e-7)
+    xhat = oracle.layer_norm(z, np.ones(9), np.zeros(9), 0.0)
+    np.testing.assert_allclose(dgamma, (gx * xhat).sum(axis=0), rtol=1e-12)
+    np.testing.assert_allclose(dbeta, gx.sum(axis=0), rtol=1e-12)
+
+
+def test_swiglu_transition_zero_down_weights():
+    # Wd = 0: the transition is the identity, so g_z = G and every weight of
+    # the gate and the LN gets no gradient; dWd is G^T (silu(g) * u)
+    rng = np.random.default_rng(13)
+    z, G = rng.normal(size=(11, 6)), rng.normal(size=(11, 6))
+    gamma, beta = 1 + rng.normal(size=6), rng.normal(size=6)
+    Wg, Wu = rng.normal(size=(8, 6)), rng.normal(size=(8, 6))
+    g_z, dga, dbe, dWg, dWu, dWd = oracle.transition_swiglu_backward(
+        z, gamma, beta, Wg, Wu, np.zeros((6, 8)), G)
+    np.testing.assert_array_equal(g_z, G)
+    for v in (dga, dbe, dWg, dWu):
+        np.testing.assert_array_equal(v, 0.0)
+    x = oracle.layer_norm(z, gamma, beta, 1e-5)
+    g = x @ Wg.T
+    np.testing.assert_allclose(dWd, G.T @ (g / (1 + np.exp(-g)) * (x @ Wu.T)), rtol=1e-12)
+
+
+def test_swiglu_chain_gradients_match_torch_autograd_dense():
+    """Dense per-sample SwiGLU blocks (LN and silu from torch.nn.functional)
+    differentiated by PyTorch's autograd in float64."""
+    F = torch.nn.functional
+    rng = np.random.default_rng(14)
+    lengths, c_s, c_z, hidden = [5, 9, 3], 8, 6, 12
+    s = rng.normal(size=(sum(lengths), c_s))
+    ws = [_swiglu_weights(rng, c_s, c_z, hidden) for _ in range(2)]
+    L, g_s, grads = oracle.chain_swiglu_backward(lengths, s, ws)
+    ts = torch.tensor(s, requires_grad=True)
+    tw = [{k: torch.tensor(v, requires_grad=True) for k, v in w.items()} for w in ws]
+    B = len(lengths)
+    xs = list(torch.split(ts, lengths))
+    for w in tw:
+        new_x, pairs = [], []
+        for X in xs:
+            P = (X @ w["Wa"].T)[:, None, :] + (X @ w["Wb"].T)[None, :, :]
+            x = F.layer_norm(P, (c_z,), w["ln_gamma"], w["ln_beta"], eps=1e-5)
+            P = P + (F.silu(x @ w["Wg"].T) * (x @ w["Wu"].T)) @ w["Wd"].T
+            new_x.append(X + P.mean(dim=1) @ w["Wo"].T)
+            pairs.append(P)
+        xs = new_x
+    n = torch.tensor(lengths, dtype=torch.float64)
+    alpha = 1 + torch.arange(B, dtype=torch.float64) / B
+    beta = 1.5 - torch.arange(B, dtype=torch.float64) / (2 * B)
+    loss = sum(alpha[i] * (xs[i] ** 2).sum() for i in range(B)) / (c_s * n.sum()) \
+        + sum(beta[i] * (pairs[i] ** 2).sum() for i in range(B)) / (c_z * (n * n).sum())
+    loss.backward()
+    assert float(loss.detach()) == pytest.approx(L, rel=1e-12)
+    np.testing.assert_allclose(ts.grad.numpy(), g_s, rtol=1e-10, atol=1e-13)
+    for w, g in zip(tw, grads):
+        for k in w:
+            np.testing.assert_allclose(w[k].grad.numpy(), g[k], rtol=1e-10, atol=1e-13)

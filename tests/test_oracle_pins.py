@@ -487,3 +487,36 @@ def test_rect_block_equals_dense_per_sample():
         if rows[i] and cols[i]:
             want = X + Pt.mean(axis=1) @ w["Wo"].T
             assert np.allclose(s_new[eta[i]:eta[i + 1]], want, rtol=1e-12, atol=1e-12)
+
+
+def test_swiglu_block_closed_form_and_dense():
+    """The SwiGLU block: with Wd = 0 the transition is the identity and the
+    column mean is a + mean_c b (as for the ReLU block with W2 = 0); for any
+    weights each sample equals the dense per-sample formula (the transition
+    applied to the outer sum, a mean over axis 1)."""
+    rng = np.random.default_rng(31)
+    lengths, c_s, c_z, hidden = [3, 0, 5, 2], 6, 4, 8
+    s = rng.normal(size=(sum(lengths), c_s))
+    w = {"Wa": rng.normal(size=(c_z, c_s)), "Wb": rng.normal(size=(c_z, c_s)),
+         "Wo": rng.normal(size=(c_s, c_z)), "ln_gamma": 1 + rng.normal(size=c_z),
+         "ln_beta": rng.normal(size=c_z), "Wg": rng.normal(size=(hidden, c_z)),
+         "Wu": rng.normal(size=(hidden, c_z)), "Wd": np.zeros((c_z, hidden))}
+    s_out, z_out = oracle.block_swiglu(lengths, s, w)
+    a, b = s @ w["Wa"].T, s @ w["Wb"].T
+    eta = np.concatenate([[0], np.cumsum(lengths)])
+    m = np.concatenate([a[eta[i]:eta[i + 1]] + b[eta[i]:eta[i + 1]].mean(axis=0)
+                        for i in range(len(lengths)) if lengths[i]])
+    np.testing.assert_allclose(s_out, s + m @ w["Wo"].T, rtol=1e-12, atol=1e-12)
+    w["Wd"] = rng.normal(size=(c_z, hidden))
+    s_out, z_out = oracle.block_swiglu(lengths, s, w)
+    o = 0
+    for i, n in enumerate(lengths):
+        X = s[eta[i]:eta[i + 1]]
+        P = (X @ w["Wa"].T)[:, None, :] + (X @ w["Wb"].T)[None, :, :]
+        Pt = oracle.transition_swiglu(P.reshape(-1, c_z), w["ln_gamma"], w["ln_beta"], w["Wg"],
+                                      w["Wu"], w["Wd"]).reshape(n, n, c_z)
+        np.testing.assert_allclose(z_out[o:o + n * n], Pt.reshape(-1, c_z), rtol=1e-12)
+        if n:
+            np.testing.assert_allclose(s_out[eta[i]:eta[i + 1]],
+                                       X + Pt.mean(axis=1) @ w["Wo"].T, rtol=1e-12)
+        o += n * n
