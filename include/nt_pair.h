@@ -321,6 +321,86 @@ nt_status nt_pair_block_rect(const nt_partition* p, const void* s_rows, const vo
                              size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Blocks with the transition named explicitly (Equation 1, second line:
+ * P~ = P + h(LN_{C_p}(P))). NT_TRANSITION_RELU_MLP is the two-layer ReLU
+ * MLP without normalisation that nt_pair_block runs (the measured
+ * workloads' update); NT_TRANSITION_LN_SWIGLU is the paper's own update, a
+ * residual pre-normalised SwiGLU (Appendix A.1, expansion four):
+ *   x = (z - mean) / sqrt(var + ln_eps) * ln_gamma + ln_beta
+ *       (mean and biased var over the c_z features of a cell),
+ *   z~ = z + (silu(x W_gate^T) * (x W_up^T)) W_down^T,  silu(g) = g / (1 + e^-g).
+ * In the block z = a[row] + b[col] is formed in fp32 and never stored: LN
+ * takes its statistics on it, x and the gated activations are rounded to
+ * bf16 before the products that read them, and the residual adds z in fp32
+ * (the pair state is rounded once, on output). NT_TRANSITION_LN_SWIGLU
+ * needs dtype NT_BF16, c_z 64 or 128, hidden a multiple of 32 and a
+ * finite ln_eps >= 0 (else NT_ERR_DTYPE / NT_ERR_INVALID).
+ * ------------------------------------------------------------------------ */
+typedef enum nt_transition_kind {
+  NT_TRANSITION_RELU_MLP = 0,
+  NT_TRANSITION_LN_SWIGLU = 1
+} nt_transition_kind;
+
+/*
+ * One block's parameters. Wa, Wb, Wo as in nt_block_weights. RELU_MLP reads
+ * W1 [hidden, c_z] and W2 [c_z, hidden]; LN_SWIGLU reads ln_gamma, ln_beta
+ * (fp32 [c_z]), W_gate, W_up ([hidden, c_z]) and W_down ([c_z, hidden]), all
+ * other weights in the block's dtype. Pointers the kind does not read may be
+ * NULL.
+ */
+typedef struct nt_block_params {
+  int32_t kind; /* nt_transition_kind */
+  float ln_eps;
+  const void* Wa;
+  const void* Wb;
+  const void* Wo;
+  const void* W1;
+  const void* W2;
+  const float* ln_gamma;
+  const float* ln_beta;
+  const void* W_gate;
+  const void* W_up;
+  const void* W_down;
+} nt_block_params;
+
+/* fp32 gradients, shaped like the parameters; those the kind has no
+ * parameter for are not written and may be NULL. */
+typedef struct nt_block_param_grads {
+  float* Wa;
+  float* Wb;
+  float* Wo;
+  float* W1;
+  float* W2;
+  float* ln_gamma;
+  float* ln_beta;
+  float* W_gate;
+  float* W_up;
+  float* W_down;
+} nt_block_param_grads;
+
+/*
+ * nt_pair_block with the transition of w->kind: projections, the broadcast
+ * fused into the transition, the column mean, the output projection.
+ * Workspace as nt_pair_block (nt_block_workspace_bytes); square or
+ * rectangular partitions (rectangular: s_cols [T_cols, c_s] gives the
+ * columns, s_cols = NULL means s_in). Other arguments and errors as
+ * nt_pair_block.
+ */
+nt_status nt_pair_block_ex(const nt_partition* p, const void* s_in, const void* s_cols,
+                           void* s_out, void* z_out, const nt_block_params* w, int32_t c_s,
+                           int32_t c_z, int32_t hidden, nt_dtype dtype, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * nt_pair_chain with nblocks parameter sets (each block's kind may differ).
+ * Workspace as nt_pair_chain (nt_chain_workspace_bytes). Square partitions.
+ */
+nt_status nt_pair_chain_ex(const nt_partition* p, const void* s_in, void* s_out, void* z_out,
+                           const nt_block_params* w, int32_t nblocks, int32_t c_s, int32_t c_z,
+                           int32_t hidden, nt_dtype dtype, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Backward pass and loss (Section 4: the measured step is forward, loss and
  * backward; Section 3.4: gradients reach the projections, the pair update
  * and the reduction of Equation 1 through the packed storage). Gradients
@@ -432,6 +512,35 @@ nt_status nt_pair_block_backward(const nt_partition* p, const void* s_in, const 
                                  const float* g_z_out, float* g_s_in, const nt_block_grads* grads,
                                  int32_t c_s, int32_t c_z, int32_t hidden, nt_dtype dtype,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes nt_pair_block_backward_ex needs for a transition kind.
+ */
+nt_status nt_block_backward_ex_workspace_bytes(const nt_partition* p, int32_t kind, int32_t c_s,
+                                               int32_t c_z, int32_t hidden, nt_dtype dtype,
+                                               size_t* bytes);
+
+/*
+ * Backward of nt_pair_block_ex on a square partition, as
+ * nt_pair_block_backward with the transition of w->kind. For
+ * NT_TRANSITION_LN_SWIGLU the transition's adjoint, for G = dL/dz~, is
+ * (g = x W_gate^T, u = x W_up^T, s = sigmoid(g), A = g s u):
+ *   dW_down = G^T A,  g_A = G W_down,  g_u = g_A g s,  g_g = g_A u s (1 + g (1 - s)),
+ *   dW_up = g_u^T x,  dW_gate = g_g^T x,  g_x = g_u W_up + g_g W_gate,
+ *   dln_gamma = sum g_x xhat,  dln_beta = sum g_x,
+ *   g_z = G + (g_xhat - mean(g_xhat) - xhat mean(g_xhat xhat)) / sqrt(var + ln_eps),
+ *   g_xhat = g_x ln_gamma,  xhat = (z - mean) / sqrt(var + ln_eps),
+ * with z re-formed in fp32 from the recomputed projections; the products
+ * read x, A, g_u, g_g and G rounded to bf16 and accumulate in fp32. The
+ * weight gradients are sums over all cells in a fixed order. grads: the
+ * kind's gradients, fp32, overwritten.
+ */
+nt_status nt_pair_block_backward_ex(const nt_partition* p, const void* s_in, const void* z_out,
+                                    const nt_block_params* w, const float* g_s_out,
+                                    const float* g_z_out, float* g_s_in,
+                                    const nt_block_param_grads* grads, int32_t c_s, int32_t c_z,
+                                    int32_t hidden, nt_dtype dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * The non-leading layout (Appendix A.1's non-leading variant; Section 3.1,

@@ -14,8 +14,9 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 from . import _native
-from ._native import (NT_BF16, NT_F32, NativeLibraryMissing, NtBlockWeights,  # noqa: F401
-                      NtPartition)
+from ._native import (NT_BF16, NT_F32, NT_TRANSITION_LN_SWIGLU,  # noqa: F401
+                      NT_TRANSITION_RELU_MLP, NativeLibraryMissing, NtBlockParamGrads,
+                      NtBlockParams, NtBlockWeights, NtPartition)
 
 __all__ = ["NtError", "Partition", "nt_partition_sizes", "nt_make_partition",
            "nt_partition_sizes_rect", "nt_make_partition_rect", "nt_pair_block_rect",
@@ -24,7 +25,8 @@ __all__ = ["NtError", "Partition", "nt_partition_sizes", "nt_make_partition",
            "nt_pair_transition_swiglu", "nt_pair_reduce",
            "nt_block_workspace_bytes", "nt_pair_block", "nt_pair_block_noalloc",
            "nt_chain_workspace_bytes",
-           "nt_pair_chain", "nt_last_error", "nt_version",
+           "nt_pair_chain", "nt_pair_block_ex", "nt_pair_chain_ex", "nt_pair_block_backward_ex",
+           "nt_block_backward_ex_workspace_bytes", "nt_last_error", "nt_version",
            "NT_F32", "NT_BF16"]
 
 
@@ -733,5 +735,148 @@ def nt_pair_block_backward_nl(p: Partition, s_in, z_out, weights, S: int, g_s_ou
     _check(_native.lib().nt_pair_block_backward_nl(
         ctypes.byref(p.struct), _ptr(s_in), _ptr(z_out), ctypes.byref(wst), _ptr(g_s_out),
         _ptr(g_z_out), _ptr(g_s_in), ctypes.byref(gst), S, c_s, c_z, hidden, _dtype_code(s_in),
+        _ptr(workspace), _nbytes(workspace), _stream(stream, dev)))
+    return g_s_in, grads
+
+
+# ------------------------------------------- blocks with a named transition
+_KIND_KEYS = {NT_TRANSITION_RELU_MLP: ("Wa", "Wb", "Wo", "W1", "W2"),
+              NT_TRANSITION_LN_SWIGLU: ("Wa", "Wb", "Wo", "ln_gamma", "ln_beta", "W_gate", "W_up",
+                                        "W_down")}
+
+
+def _kind_of(params: dict) -> int:
+    """NT_TRANSITION_LN_SWIGLU when the parameters hold W_gate, else the ReLU MLP."""
+    return NT_TRANSITION_LN_SWIGLU if "W_gate" in params else NT_TRANSITION_RELU_MLP
+
+
+def _expect_params(p, params: dict, c_s, c_z, hidden, dtype, label="") -> int:
+    torch = _torch()
+    kind = _kind_of(params)
+    shapes = {"Wa": (c_z, c_s), "Wb": (c_z, c_s), "Wo": (c_s, c_z), "W1": (hidden, c_z),
+              "W2": (c_z, hidden), "ln_gamma": (c_z,), "ln_beta": (c_z,),
+              "W_gate": (hidden, c_z), "W_up": (hidden, c_z), "W_down": (c_z, hidden)}
+    for k in _KIND_KEYS[kind]:
+        if k not in params:
+            raise KeyError(f"{label}{k} missing")
+        dt = torch.float32 if k.startswith("ln_") else dtype
+        _expect(p, label + k, params[k], shapes[k], dt)
+    return kind
+
+
+def _params_struct(params: dict, ln_eps: float) -> NtBlockParams:
+    st = NtBlockParams()
+    st.kind = _kind_of(params)
+    st.ln_eps = ln_eps
+    for k in _KIND_KEYS[st.kind]:
+        setattr(st, k, _ptr(params[k]))
+    return st
+
+
+def _widths(params: dict):
+    kind = _kind_of(params)
+    c_z, c_s = params["Wa"].shape
+    hidden = params["W1" if kind == NT_TRANSITION_RELU_MLP else "W_gate"].shape[0]
+    return c_s, c_z, hidden
+
+
+def nt_pair_block_ex(p: Partition, s_in, params: dict, s_cols=None, s_out=None, z_out=None,
+                     workspace=None, ln_eps: float = 1e-5, stream=None):
+    """One block with its transition named by its parameters: Wa, Wb, Wo
+    and either W1, W2 (the ReLU MLP) or ln_gamma, ln_beta (fp32), W_gate,
+    W_up, W_down (the pre-normalised SwiGLU). Returns (s_out, z_out)."""
+    torch = _torch()
+    c_s, c_z, hidden = _widths(params)
+    if s_out is None:
+        s_out = torch.empty_like(s_in)
+    if z_out is None:
+        z_out = torch.empty((p.cells, c_z), dtype=s_in.dtype, device=s_in.device)
+    need = nt_block_workspace_bytes(p, c_s, c_z, hidden, _dtype_code(s_in))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=s_in.device)
+    _expect(p, "s_in", s_in, (p.T, c_s))
+    _expect(p, "s_cols", s_cols, (p.T_cols, c_s), s_in.dtype)
+    _expect(p, "s_out", s_out, (p.T, c_s), s_in.dtype)
+    _expect(p, "z_out", z_out, (p.cells, c_z), s_in.dtype)
+    _expect_params(p, params, c_s, c_z, hidden, s_in.dtype)
+    _expect_workspace(p, workspace, need)
+    st = _params_struct(params, ln_eps)
+    _check(_native.lib().nt_pair_block_ex(ctypes.byref(p.struct), _ptr(s_in), _ptr(s_cols),
+                                          _ptr(s_out), _ptr(z_out), ctypes.byref(st), c_s, c_z,
+                                          hidden, _dtype_code(s_in), _ptr(workspace),
+                                          _nbytes(workspace), _stream(stream, s_in.device)))
+    return s_out, z_out
+
+
+def nt_pair_chain_ex(p: Partition, s_in, params: list, s_out=None, z_out=None, workspace=None,
+                     ln_eps: float = 1e-5, stream=None):
+    """Blocks in sequence, each with the parameters nt_pair_block_ex takes;
+    returns (s_out, z_out) of the last block."""
+    torch = _torch()
+    if not params:
+        raise ValueError("at least one block")
+    c_s, c_z, hidden = _widths(params[0])
+    if s_out is None:
+        s_out = torch.empty_like(s_in)
+    if z_out is None:
+        z_out = torch.empty((p.cells, c_z), dtype=s_in.dtype, device=s_in.device)
+    need = nt_chain_workspace_bytes(p, len(params), c_s, c_z, hidden, _dtype_code(s_in))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=s_in.device)
+    _expect(p, "s_in", s_in, (p.T, c_s))
+    _expect(p, "s_out", s_out, (p.T, c_s), s_in.dtype)
+    _expect(p, "z_out", z_out, (p.cells, c_z), s_in.dtype)
+    for k, pk in enumerate(params):
+        _expect_params(p, pk, c_s, c_z, hidden, s_in.dtype, label=f"block {k} ")
+    _expect_workspace(p, workspace, need)
+    arr = (NtBlockParams * len(params))(*[_params_struct(pk, ln_eps) for pk in params])
+    _check(_native.lib().nt_pair_chain_ex(ctypes.byref(p.struct), _ptr(s_in), _ptr(s_out),
+                                          _ptr(z_out), arr, len(params), c_s, c_z, hidden,
+                                          _dtype_code(s_in), _ptr(workspace), _nbytes(workspace),
+                                          _stream(stream, s_in.device)))
+    return s_out, z_out
+
+
+def nt_block_backward_ex_workspace_bytes(p: Partition, kind: int, c_s: int, c_z: int,
+                                         hidden: int, dtype) -> int:
+    n = ctypes.c_size_t()
+    _check(_native.lib().nt_block_backward_ex_workspace_bytes(
+        ctypes.byref(p.struct), kind, c_s, c_z, hidden, _code(dtype), ctypes.byref(n)))
+    return n.value
+
+
+def nt_pair_block_backward_ex(p: Partition, s_in, z_out, params: dict, g_s_out, g_z_out=None,
+                              g_s_in=None, grads=None, workspace=None, ln_eps: float = 1e-5,
+                              stream=None):
+    """Backward of nt_pair_block_ex; returns (g_s_in, grads), grads a dict of
+    fp32 gradients keyed like the kind's parameters."""
+    torch = _torch()
+    dev = s_in.device
+    kind = _kind_of(params)
+    c_s, c_z, hidden = _widths(params)
+    f32 = torch.float32
+    if g_s_in is None:
+        g_s_in = torch.empty((p.T, c_s), dtype=f32, device=dev)
+    if grads is None:
+        grads = {k: torch.empty(params[k].shape, dtype=f32, device=dev) for k in _KIND_KEYS[kind]}
+    need = nt_block_backward_ex_workspace_bytes(p, kind, c_s, c_z, hidden, _dtype_code(s_in))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _expect(p, "s_in", s_in, (p.T, c_s))
+    _expect(p, "z_out", z_out, (p.cells, c_z), s_in.dtype)
+    _expect_params(p, params, c_s, c_z, hidden, s_in.dtype)
+    _expect(p, "g_s_out", g_s_out, (p.T, c_s), f32)
+    _expect(p, "g_z_out", g_z_out, (p.cells, c_z), f32)
+    _expect(p, "g_s_in", g_s_in, (p.T, c_s), f32)
+    for k in _KIND_KEYS[kind]:
+        _expect(p, "d" + k, grads[k], tuple(params[k].shape), f32)
+    _expect_workspace(p, workspace, need)
+    st = _params_struct(params, ln_eps)
+    gst = NtBlockParamGrads()
+    for k in _KIND_KEYS[kind]:
+        setattr(gst, k, _ptr(grads[k]))
+    _check(_native.lib().nt_pair_block_backward_ex(
+        ctypes.byref(p.struct), _ptr(s_in), _ptr(z_out), ctypes.byref(st), _ptr(g_s_out),
+        _ptr(g_z_out), _ptr(g_s_in), ctypes.byref(gst), c_s, c_z, hidden, _dtype_code(s_in),
         _ptr(workspace), _nbytes(workspace), _stream(stream, dev)))
     return g_s_in, grads

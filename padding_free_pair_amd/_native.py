@@ -11,6 +11,7 @@ NT_OK, NT_ERR_NULL, NT_ERR_INVALID, NT_ERR_OVERFLOW, NT_ERR_ALIGN, NT_ERR_WORKSP
 STATUS_NAMES = {0: "NT_OK", 1: "NT_ERR_NULL", 2: "NT_ERR_INVALID", 3: "NT_ERR_OVERFLOW",
                 4: "NT_ERR_ALIGN", 5: "NT_ERR_WORKSPACE", 6: "NT_ERR_DTYPE", 7: "NT_ERR_HIP"}
 NT_F32, NT_BF16 = 0, 1
+NT_TRANSITION_RELU_MLP, NT_TRANSITION_LN_SWIGLU = 0, 1
 
 # Every symbol the header declares, for the export check.
 EXPORTS = ("nt_partition_sizes", "nt_make_partition", "nt_partition_sizes_rect",
@@ -19,7 +20,8 @@ EXPORTS = ("nt_partition_sizes", "nt_make_partition", "nt_partition_sizes_rect",
            "nt_pair_reduce",
            "nt_block_workspace_bytes", "nt_pair_block", "nt_pair_block_noalloc",
            "nt_pair_block_rect",
-           "nt_chain_workspace_bytes", "nt_pair_chain",
+           "nt_chain_workspace_bytes", "nt_pair_chain", "nt_pair_block_ex", "nt_pair_chain_ex",
+           "nt_block_backward_ex_workspace_bytes", "nt_pair_block_backward_ex",
            "nt_loss_workspace_bytes", "nt_pair_loss_eq5", "nt_pair_reduce_backward",
            "nt_pair_broadcast_backward", "nt_transition_backward_workspace_bytes",
            "nt_pair_transition_backward", "nt_block_backward_workspace_bytes",
@@ -49,6 +51,19 @@ class NtBlockWeights(ctypes.Structure):
 class NtBlockGrads(ctypes.Structure):
     _fields_ = [("Wa", ctypes.c_void_p), ("Wb", ctypes.c_void_p), ("W1", ctypes.c_void_p),
                 ("W2", ctypes.c_void_p), ("Wo", ctypes.c_void_p)]
+
+
+# nt_block_params / nt_block_param_grads: field names as in the header
+PARAM_NAMES = ("Wa", "Wb", "Wo", "W1", "W2", "ln_gamma", "ln_beta", "W_gate", "W_up", "W_down")
+
+
+class NtBlockParams(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("ln_eps", ctypes.c_float)] + \
+        [(k, ctypes.c_void_p) for k in PARAM_NAMES]
+
+
+class NtBlockParamGrads(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in PARAM_NAMES]
 
 
 _lib = None
@@ -93,6 +108,14 @@ def lib() -> ctypes.CDLL:
                           vp, sz, vp],
         "nt_pair_block_rect": [part, vp, vp, vp, vp, P(NtBlockWeights), i32, i32, i32,
                                ctypes.c_int, vp, sz, vp],
+        "nt_pair_block_ex": [part, vp, vp, vp, vp, P(NtBlockParams), i32, i32, i32, ctypes.c_int,
+                             vp, sz, vp],
+        "nt_pair_chain_ex": [part, vp, vp, vp, P(NtBlockParams), i32, i32, i32, i32, ctypes.c_int,
+                             vp, sz, vp],
+        "nt_block_backward_ex_workspace_bytes": [part, i32, i32, i32, i32, ctypes.c_int, P(sz)],
+        "nt_pair_block_backward_ex": [part, vp, vp, P(NtBlockParams), vp, vp, vp,
+                                      P(NtBlockParamGrads), i32, i32, i32, ctypes.c_int, vp, sz,
+                                      vp],
         "nt_loss_workspace_bytes": [part, P(sz)],
         "nt_pair_loss_eq5": [part, vp, i32, vp, i32, i32, ctypes.c_int, vp, vp, vp, vp, sz, vp],
         "nt_pair_reduce_backward": [part, vp, vp, vp, i32, vp],

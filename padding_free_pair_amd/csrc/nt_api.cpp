@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "nt_internal.hpp"
 
@@ -219,10 +220,99 @@ nt_status check_static_axis(int32_t S, int32_t c_z) {
   return NT_OK;
 }
 
+// The ReLU-MLP weights of nt_block_weights as block parameters.
+nt_block_params relu_params(const nt_block_weights& w) {
+  nt_block_params q;
+  std::memset(&q, 0, sizeof(q));
+  q.kind = NT_TRANSITION_RELU_MLP;
+  q.Wa = w.Wa;
+  q.Wb = w.Wb;
+  q.Wo = w.Wo;
+  q.W1 = w.W1;
+  q.W2 = w.W2;
+  return q;
+}
+
+// The arrays a block's parameters consist of, by kind; checked for NULL and
+// alignment, and returned for the overlap checks (at most 8).
+struct ParamArrays {
+  const char* name[8];
+  const void* ptr[8];
+  uint64_t bytes[8];
+  int n = 0;
+  void add(const char* nm, const void* p, uint64_t b) {
+    name[n] = nm;
+    ptr[n] = p;
+    bytes[n] = b;
+    ++n;
+  }
+};
+
+nt_status check_params(const nt_block_params* w, int32_t c_s, int32_t c_z, int32_t hidden,
+                       nt_dtype dtype, ParamArrays* out) {
+  if (!w) return fail(NT_ERR_NULL, "weights is NULL");
+  const size_t es = esize(dtype);
+  const uint64_t proj = (uint64_t)c_z * c_s * es, mlp = (uint64_t)c_z * hidden * es;
+  ParamArrays a;
+  a.add("Wa", w->Wa, proj);
+  a.add("Wb", w->Wb, proj);
+  a.add("Wo", w->Wo, proj);
+  if (w->kind == NT_TRANSITION_RELU_MLP) {
+    a.add("W1", w->W1, mlp);
+    a.add("W2", w->W2, mlp);
+  } else if (w->kind == NT_TRANSITION_LN_SWIGLU) {
+    if (dtype != NT_BF16) return fail(NT_ERR_DTYPE, "the SwiGLU transition runs in bf16 only");
+    if (!nt::transition_swiglu_supported(c_z, hidden, dtype))
+      return fail(NT_ERR_INVALID, "SwiGLU transition needs c_z 64 or 128 and hidden a positive "
+                                  "multiple of 32 (got c_z %d, hidden %d)", (int)c_z, (int)hidden);
+    if (!(w->ln_eps >= 0.f) || w->ln_eps > 3.0e38f)
+      return fail(NT_ERR_INVALID, "ln_eps must be finite and >= 0");
+    a.add("ln_gamma", w->ln_gamma, (uint64_t)c_z * sizeof(float));
+    a.add("ln_beta", w->ln_beta, (uint64_t)c_z * sizeof(float));
+    a.add("W_gate", w->W_gate, mlp);
+    a.add("W_up", w->W_up, mlp);
+    a.add("W_down", w->W_down, mlp);
+  } else {
+    return fail(NT_ERR_INVALID, "unknown transition kind %d", (int)w->kind);
+  }
+  for (int k = 0; k < a.n; ++k) NT_TRY(check_array(a.name[k], a.ptr[k], a.bytes[k]));
+  if (out) *out = a;
+  return NT_OK;
+}
+
+// The transition of a block over its pair state: fused (z = a[row] + b[col]
+// formed on chip) for S = 1, else the broadcast over rows of S slices
+// followed by the cell-local transition in place over cells * S rows.
+nt_status block_transition(const nt_partition& p, const nt_block_params& w, const void* a,
+                           const void* b, void* z_out, int32_t c_z, int32_t hidden,
+                           nt_dtype dtype, int32_t S, hipStream_t s) {
+  const bool swiglu = w.kind == NT_TRANSITION_LN_SWIGLU;
+  if (S == 1) {
+    if (swiglu)
+      return hip_status(nt::launch_transition_swiglu(p, nullptr, a, b, z_out, w.ln_gamma,
+                                                     w.ln_beta, w.W_gate, w.W_up, w.W_down, c_z,
+                                                     hidden, w.ln_eps, s),
+                        "fused broadcast + SwiGLU transition");
+    return hip_status(nt::launch_transition(p, nullptr, a, b, z_out, w.W1, w.W2, c_z, hidden,
+                                            dtype, s),
+                      "fused broadcast + transition");
+  }
+  NT_TRY(hip_status(nt::launch_broadcast(p, a, b, z_out, S * c_z, dtype, s, true), "broadcast"));
+  const nt_partition v = rows_view(p, S);
+  if (swiglu)
+    return hip_status(nt::launch_transition_swiglu(v, z_out, nullptr, nullptr, z_out, w.ln_gamma,
+                                                   w.ln_beta, w.W_gate, w.W_up, w.W_down, c_z,
+                                                   hidden, w.ln_eps, s),
+                      "SwiGLU transition");
+  return hip_status(nt::launch_transition(v, z_out, nullptr, nullptr, z_out, w.W1, w.W2, c_z,
+                                          hidden, dtype, s),
+                    "transition");
+}
+
 // One block; s_cols is s_rows for square partitions. S > 1: the non-leading
 // layout (square partitions), rows of S slices.
 nt_status pair_block(const nt_partition* p, const void* s_rows, const void* s_cols, void* s_out,
-                     void* z_out, const nt_block_weights* w, int32_t c_s, int32_t c_z,
+                     void* z_out, const nt_block_params* w, int32_t c_s, int32_t c_z,
                      int32_t hidden, nt_dtype dtype, void* workspace, size_t workspace_bytes,
                      void* stream, int32_t S = 1) {
   NT_TRY(check_partition(p));
@@ -231,22 +321,16 @@ nt_status pair_block(const nt_partition* p, const void* s_rows, const void* s_co
   NT_TRY(check_width("c_z", c_z, nt::kMaxCz));
   NT_TRY(check_width("hidden", hidden, nt::kMaxHidden));
   NT_TRY(check_static_axis(S, c_z));
-  if (!w) return fail(NT_ERR_NULL, "weights is NULL");
+  ParamArrays pa;
+  NT_TRY(check_params(w, c_s, c_z, hidden, dtype, &pa));
   const size_t es = esize(dtype);
   const uint64_t sbytes = (uint64_t)p->T * S * c_s * es;
   const uint64_t cbytes = (uint64_t)p->T_cols * S * c_s * es;
   const uint64_t pair = (uint64_t)p->cells * S * c_z * es;
-  const uint64_t proj = (uint64_t)c_z * c_s * es;
-  const uint64_t mlp = (uint64_t)c_z * hidden * es;
   NT_TRY(check_array("s_rows", s_rows, sbytes));
   NT_TRY(check_array("s_cols", s_cols, cbytes));
   NT_TRY(check_array("s_out", s_out, sbytes));
   NT_TRY(check_array("z_out", z_out, pair));
-  NT_TRY(check_array("Wa", w->Wa, proj));
-  NT_TRY(check_array("Wb", w->Wb, proj));
-  NT_TRY(check_array("W1", w->W1, mlp));
-  NT_TRY(check_array("W2", w->W2, mlp));
-  NT_TRY(check_array("Wo", w->Wo, proj));
   const BlockWorkspace ws = block_workspace(p->T, p->T_cols, c_z, dtype, S);
   if (ws.total > 0) {
     NT_TRY(check_array("workspace", workspace, ws.total));
@@ -258,13 +342,14 @@ nt_status pair_block(const nt_partition* p, const void* s_rows, const void* s_co
     return fail(NT_ERR_INVALID, "s_out partially overlaps s_in");
   if (s_cols != s_rows && overlaps(s_out, sbytes, s_cols, cbytes))
     return fail(NT_ERR_INVALID, "s_out overlaps s_cols");
-  const void* ins[] = {s_rows, w->Wa, w->Wb, w->W1, w->W2, w->Wo, workspace, s_cols};
-  const uint64_t insz[] = {sbytes, proj, proj, mlp, mlp, proj, ws.total, cbytes};
-  for (int k = 0; k < 8; ++k) {
-    if (overlaps(z_out, pair, ins[k], insz[k]) ||
-        (k > 0 && k < 7 && overlaps(s_out, sbytes, ins[k], insz[k])))
-      return fail(NT_ERR_INVALID, "an output overlaps an input or the workspace");
-  }
+  if (overlaps(z_out, pair, s_rows, sbytes) || overlaps(z_out, pair, s_cols, cbytes) ||
+      overlaps(z_out, pair, workspace, ws.total) || overlaps(s_out, sbytes, workspace, ws.total))
+    return fail(NT_ERR_INVALID, "an output overlaps an input or the workspace");
+  for (int k = 0; k < pa.n; ++k)
+    if (overlaps(z_out, pair, pa.ptr[k], pa.bytes[k]) ||
+        overlaps(s_out, sbytes, pa.ptr[k], pa.bytes[k]) ||
+        overlaps(workspace, ws.total, pa.ptr[k], pa.bytes[k]))
+      return fail(NT_ERR_INVALID, "an output or the workspace overlaps %s", pa.name[k]);
   if (overlaps(z_out, pair, s_out, sbytes))
     return fail(NT_ERR_INVALID, "z_out overlaps s_out");
   if (p->T == 0) return ok();
@@ -286,20 +371,7 @@ nt_status pair_block(const nt_partition* p, const void* s_rows, const void* s_co
                                         p->T_cols, c_z, c_s, s),
                       "projection b"));
   }
-  if (S == 1) {
-    NT_TRY(hip_status(nt::launch_transition(*p, nullptr, a, b, z_out, w->W1, w->W2, c_z, hidden,
-                                            dtype, s),
-                      "fused broadcast + transition"));
-  } else {
-    // the broadcast over rows of S slices, then the cell-local transition in
-    // place over cells * S rows of c_z
-    NT_TRY(hip_status(nt::launch_broadcast(*p, a, b, z_out, S * c_z, dtype, s, true),
-                      "broadcast"));
-    const nt_partition v = rows_view(*p, S);
-    NT_TRY(hip_status(nt::launch_transition(v, z_out, nullptr, nullptr, z_out, w->W1, w->W2, c_z,
-                                            hidden, dtype, s),
-                      "transition"));
-  }
+  if (p->cells > 0) NT_TRY(block_transition(*p, *w, a, b, z_out, c_z, hidden, dtype, S, s));
   NT_TRY(hip_status(nt::launch_reduce(*p, z_out, m, S * c_z, dtype, s), "column mean"));
   return hip_status(nt::launch_linear(m, NT_F32, w->Wo, dtype, s_rows, s_out, dtype, TS, c_s,
                                       c_z, s),
@@ -425,6 +497,105 @@ nt_status transition_backward(const nt_partition* p, const void* z, const float*
                     "dW2 contraction");
 }
 
+// SwiGLU transition gradient workspace (c_z 64 or 128, bf16): x = LN(z)
+// (fp32), the gate and value pre-activations and the activation adjoint
+// (fp32 [cells, hidden] each), their bf16 successors A, g_u, g_g, g_x
+// (fp32), the transposed weights, and the partial sums of the weight
+// gradients and of LN's parameter gradients.
+struct SwigluBwdWs {
+  uint64_t x, gp, up, ga, A, gu, gg, gx, WuT, WgT, WdT, wpart, lnpart, total;
+  int wsplits, lnblocks;
+};
+
+SwigluBwdWs swiglu_backward_ws(int64_t cells, int c_z, int hidden) {
+  SwigluBwdWs w;
+  const uint64_t ch = (uint64_t)cells * hidden, cz = (uint64_t)cells * c_z;
+  const uint64_t wbytes = nt::align256((size_t)hidden * c_z * 2);
+  uint64_t off = 0;
+  w.x = off;   off += nt::align256(cz * 4);
+  w.gp = off;  off += nt::align256(ch * 4);
+  w.up = off;  off += nt::align256(ch * 4);
+  w.ga = off;  off += nt::align256(ch * 4);
+  w.A = off;   off += nt::align256(ch * 2);
+  w.gu = off;  off += nt::align256(ch * 2);
+  w.gg = off;  off += nt::align256(ch * 2);
+  w.gx = off;  off += nt::align256(cz * 4);
+  w.WuT = off; off += wbytes;
+  w.WgT = off; off += wbytes;
+  w.WdT = off; off += wbytes;
+  w.wsplits = nt::gemm_tn_splits(cells, c_z, hidden);
+  w.wpart = off; off += nt::align256((size_t)w.wsplits * hidden * c_z * sizeof(float));
+  w.lnblocks = nt::ln_backward_blocks(cells, c_z);
+  w.lnpart = off; off += nt::align256((size_t)2 * w.lnblocks * c_z * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+// Gradient of z~ = z + (silu(x Wg^T) * (x Wu^T)) Wd^T, x = LN(z), for G =
+// dL/dz~ (fp32 [cells, c_z], replaced by g_z): z32 is the fp32 pair state.
+// x and G enter the products unrounded (fp32 operands split into bf16 hi
+// and lo parts on the matrix cores, fp32 contractions over the cells); the
+// gate's outputs A, g_u, g_g are rounded to bf16.
+nt_status swiglu_transition_backward(int64_t cells, const float* z32, float* G,
+                                     const nt_block_params& w, const nt_block_param_grads& g,
+                                     int c_z, int hidden, char* ws, hipStream_t s) {
+  const SwigluBwdWs L = swiglu_backward_ws(cells, c_z, hidden);
+  float* x = reinterpret_cast<float*>(ws + L.x);
+  float* gp = reinterpret_cast<float*>(ws + L.gp);
+  float* up = reinterpret_cast<float*>(ws + L.up);
+  float* ga = reinterpret_cast<float*>(ws + L.ga);
+  void *A = ws + L.A, *gu = ws + L.gu, *gg = ws + L.gg;
+  float* gx = reinterpret_cast<float*>(ws + L.gx);
+  void *WuT = ws + L.WuT, *WgT = ws + L.WgT, *WdT = ws + L.WdT;
+  float* wpart = reinterpret_cast<float*>(ws + L.wpart);
+  float* lnpart = reinterpret_cast<float*>(ws + L.lnpart);
+  const float* gamma = w.ln_gamma;
+  const int splits = L.wsplits;
+  // forward pieces: x, then the gate and value pre-activations
+  NT_TRY(hip_status(nt::launch_ln_rows(z32, gamma, w.ln_beta, x, cells, c_z, w.ln_eps, s),
+                    "LN of the pair state"));
+  NT_TRY(hip_status(nt::launch_linear(x, NT_F32, w.W_gate, NT_BF16, nullptr, gp, NT_F32, cells,
+                                      hidden, c_z, s),
+                    "gate product"));
+  NT_TRY(hip_status(nt::launch_linear(x, NT_F32, w.W_up, NT_BF16, nullptr, up, NT_F32, cells,
+                                      hidden, c_z, s),
+                    "value product"));
+  // g_A = G Wd, then the gate's adjoints
+  NT_TRY(hip_status(nt::launch_transpose(w.W_down, WdT, c_z, hidden, NT_BF16, s),
+                    "transpose W_down"));
+  NT_TRY(hip_status(nt::launch_linear(G, NT_F32, WdT, NT_BF16, nullptr, ga, NT_F32, cells,
+                                      hidden, c_z, s),
+                    "g_A = G W_down"));
+  NT_TRY(hip_status(nt::launch_swiglu_gate_bwd(gp, up, ga, A, gu, gg, cells * hidden, s),
+                    "gate adjoints"));
+  // the three weight gradients, contractions over the cells
+  NT_TRY(hip_status(nt::launch_gemm_tn(G, NT_F32, A, NT_BF16, g.W_down, wpart, cells, c_z,
+                                       hidden, splits, s),
+                    "dW_down"));
+  NT_TRY(hip_status(nt::launch_gemm_tn(gu, NT_BF16, x, NT_F32, g.W_up, wpart, cells, hidden, c_z,
+                                       splits, s),
+                    "dW_up"));
+  NT_TRY(hip_status(nt::launch_gemm_tn(gg, NT_BF16, x, NT_F32, g.W_gate, wpart, cells, hidden,
+                                       c_z, splits, s),
+                    "dW_gate"));
+  // g_x = g_u W_up + g_g W_gate
+  NT_TRY(hip_status(nt::launch_transpose(w.W_up, WuT, hidden, c_z, NT_BF16, s),
+                    "transpose W_up"));
+  NT_TRY(hip_status(nt::launch_transpose(w.W_gate, WgT, hidden, c_z, NT_BF16, s),
+                    "transpose W_gate"));
+  NT_TRY(hip_status(nt::launch_linear(gu, NT_BF16, WuT, NT_BF16, nullptr, gx, NT_F32, cells, c_z,
+                                      hidden, s),
+                    "g_x = g_u W_up"));
+  NT_TRY(hip_status(nt::launch_linear(gg, NT_BF16, WgT, NT_BF16, gx, gx, NT_F32, cells, c_z,
+                                      hidden, s),
+                    "g_x += g_g W_gate"));
+  // LN's adjoint into G, and its parameters' gradients
+  return hip_status(nt::launch_ln_backward(z32, gamma, gx, G, lnpart,
+                                           lnpart + (size_t)L.lnblocks * c_z, g.ln_gamma,
+                                           g.ln_beta, cells, c_z, w.ln_eps, s),
+                    "LN backward");
+}
+
 // Block backward workspace (square partitions): a, b (fp32), z (storage
 // type), m, g_m, G (fp32; G becomes g_z in place), g_a, g_b (fp32), the
 // transposed projection weights, the projections' split partials, then the
@@ -435,7 +606,8 @@ struct BlockBwdWs {
 };
 
 BlockBwdWs block_backward_ws(const nt_partition* p, int c_s, int c_z, int hidden,
-                             nt_dtype dtype, int S = 1) {
+                             nt_dtype dtype, int S = 1, int kind = NT_TRANSITION_RELU_MLP) {
+  const bool swiglu = kind == NT_TRANSITION_LN_SWIGLU;
   BlockBwdWs w;
   const uint64_t es = esize(dtype);
   const int64_t TS = p->T * S, CS = p->cells * S;  // rows of c_s / c_z values
@@ -444,7 +616,8 @@ BlockBwdWs block_backward_ws(const nt_partition* p, int c_s, int c_z, int hidden
   uint64_t off = 0;
   w.a = off;     off += single;
   w.b = off;     off += single;
-  w.z = off;     off += nt::align256((size_t)CS * c_z * es);
+  // the SwiGLU gradient reads the pair state in fp32 (LN's statistics)
+  w.z = off;     off += nt::align256((size_t)CS * c_z * (swiglu ? 4 : es));
   w.m = off;     off += single;
   w.g_m = off;   off += single;
   w.G = off;     off += nt::align256((size_t)CS * c_z * sizeof(float));
@@ -455,7 +628,9 @@ BlockBwdWs block_backward_ws(const nt_partition* p, int c_s, int c_z, int hidden
   w.WbT = off;   off += proj;
   w.psplits = nt::gemm_tn_splits(TS, c_z, c_s);
   w.ppart = off; off += nt::align256((size_t)w.psplits * c_s * c_z * sizeof(float));
-  w.trans = off; off += transition_backward_ws(CS, c_z, hidden, dtype).total;
+  w.trans = off;
+  off += swiglu ? swiglu_backward_ws(CS, c_z, hidden).total
+                : transition_backward_ws(CS, c_z, hidden, dtype).total;
   w.total = off;
   return w;
 }
@@ -591,8 +766,9 @@ nt_status nt_pair_transition_swiglu(const nt_partition* p, const void* z_in, voi
       overlaps(z_out, pair, ln_beta, lnbytes))
     return fail(NT_ERR_INVALID, "z_out overlaps a parameter");
   if (p->cells == 0) return ok();
-  return hip_status(nt::launch_transition_swiglu(*p, z_in, z_out, ln_gamma, ln_beta, W_gate, W_up,
-                                                 W_down, c_z, hidden, ln_eps,
+  return hip_status(nt::launch_transition_swiglu(*p, z_in, nullptr, nullptr, z_out, ln_gamma,
+                                                 ln_beta, W_gate, W_up, W_down, c_z, hidden,
+                                                 ln_eps,
                                                  static_cast<hipStream_t>(stream)),
                     "SwiGLU transition kernel");
 }
@@ -654,7 +830,22 @@ nt_status nt_pair_block(const nt_partition* p, const void* s_in, void* s_out, vo
   NT_TRY(check_partition(p));
   if (p->col_offsets != p->single_offsets)
     return fail(NT_ERR_INVALID, "rectangular partition: use nt_pair_block_rect");
-  return pair_block(p, s_in, s_in, s_out, z_out, w, c_s, c_z, hidden, dtype, workspace,
+  if (!w) return fail(NT_ERR_NULL, "weights is NULL");
+  const nt_block_params q = relu_params(*w);
+  return pair_block(p, s_in, s_in, s_out, z_out, &q, c_s, c_z, hidden, dtype, workspace,
+                    workspace_bytes, stream);
+}
+
+nt_status nt_pair_block_ex(const nt_partition* p, const void* s_in, const void* s_cols,
+                           void* s_out, void* z_out, const nt_block_params* w, int32_t c_s,
+                           int32_t c_z, int32_t hidden, nt_dtype dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  NT_TRY(check_partition(p));
+  const bool rect = p->col_offsets != p->single_offsets;
+  if (!s_cols) s_cols = s_in;
+  if (!rect && s_cols != s_in)
+    return fail(NT_ERR_INVALID, "s_cols must be NULL or s_in for a square partition");
+  return pair_block(p, s_in, s_cols, s_out, z_out, w, c_s, c_z, hidden, dtype, workspace,
                     workspace_bytes, stream);
 }
 
@@ -672,9 +863,11 @@ nt_status nt_pair_block_noalloc(const nt_partition* p, const void* s_in, void* s
                 "the block needs %llu bytes of scratch (T = %lld rows of 3 x c_z fp32 values); "
                 "the static scratch holds %zu: use nt_pair_block with a workspace",
                 (unsigned long long)need, (long long)p->T, nt::kStaticScratchBytes);
+  if (!w) return fail(NT_ERR_NULL, "weights is NULL");
+  const nt_block_params q = relu_params(*w);
   void* ws = nullptr;
   NT_TRY(hip_status(nt::static_scratch(&ws), "static scratch address"));
-  return pair_block(p, s_in, s_in, s_out, z_out, w, c_s, c_z, hidden, dtype, ws,
+  return pair_block(p, s_in, s_in, s_out, z_out, &q, c_s, c_z, hidden, dtype, ws,
                     nt::kStaticScratchBytes, stream);
 }
 
@@ -699,10 +892,12 @@ nt_status nt_chain_workspace_bytes(const nt_partition* p, int32_t nblocks, int32
   return ok();
 }
 
-nt_status nt_pair_chain(const nt_partition* p, const void* s_in, void* s_out, void* z_out,
-                        const nt_block_weights* w, int32_t nblocks, int32_t c_s, int32_t c_z,
-                        int32_t hidden, nt_dtype dtype, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+// nblocks blocks in sequence; params(k) gives block k's parameters.
+}  // extern "C"
+template <typename Params>
+nt_status pair_chain(const nt_partition* p, const void* s_in, void* s_out, void* z_out,
+                     Params params, int32_t nblocks, int32_t c_s, int32_t c_z, int32_t hidden,
+                     nt_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
   NT_TRY(check_partition(p));
   NT_TRY(check_dtype(dtype));
   NT_TRY(check_width("c_s", c_s, nt::kMaxCs));
@@ -711,12 +906,9 @@ nt_status nt_pair_chain(const nt_partition* p, const void* s_in, void* s_out, vo
   if (p->col_offsets != p->single_offsets)
     return fail(NT_ERR_INVALID, "rectangular partition: chain nt_pair_block_rect calls");
   if (nblocks < 1) return fail(NT_ERR_INVALID, "nblocks = %d must be at least 1", (int)nblocks);
-  if (!w) return fail(NT_ERR_NULL, "weights is NULL");
   const size_t es = esize(dtype);
   const uint64_t sbytes = (uint64_t)p->T * c_s * es;
   const uint64_t pair = (uint64_t)p->cells * c_z * es;
-  const uint64_t proj = (uint64_t)c_z * c_s * es;
-  const uint64_t mlp = (uint64_t)c_z * hidden * es;
   const uint64_t blk = block_workspace(p->T, p->T_cols, c_z, dtype).total;
   const uint64_t need = chain_workspace(p, nblocks, c_s, c_z, dtype);
   NT_TRY(check_array("s_in", s_in, sbytes));
@@ -733,17 +925,15 @@ nt_status nt_pair_chain(const nt_partition* p, const void* s_in, void* s_out, vo
   const void* outs[] = {s_out, z_out, workspace};
   const uint64_t outsz[] = {sbytes, pair, need};
   for (int k = 0; k < nblocks; ++k) {
-    const nt_block_weights& wk = w[k];
-    const void* wp[] = {wk.Wa, wk.Wb, wk.W1, wk.W2, wk.Wo};
-    const uint64_t wsz[] = {proj, proj, mlp, mlp, proj};
-    static const char* const names[] = {"Wa", "Wb", "W1", "W2", "Wo"};
-    for (int q = 0; q < 5; ++q) {
-      NT_TRY(check_array(names[q], wp[q], wsz[q]));
+    ParamArrays pa;
+    const nt_block_params* q = params(k);
+    if (!q) return fail(NT_ERR_NULL, "weights is NULL");
+    NT_TRY(check_params(q, c_s, c_z, hidden, dtype, &pa));
+    for (int j = 0; j < pa.n; ++j)
       for (int o = 0; o < 3; ++o)
-        if (overlaps(outs[o], outsz[o], wp[q], wsz[q]))
+        if (overlaps(outs[o], outsz[o], pa.ptr[j], pa.bytes[j]))
           return fail(NT_ERR_INVALID, "block %d's %s overlaps an output or the workspace", k,
-                      names[q]);
-    }
+                      pa.name[j]);
   }
   if (overlaps(z_out, pair, s_in, sbytes) || overlaps(z_out, pair, s_out, sbytes) ||
       overlaps(workspace, need, s_in, sbytes) || overlaps(workspace, need, s_out, sbytes) ||
@@ -758,18 +948,42 @@ nt_status nt_pair_chain(const nt_partition* p, const void* s_in, void* s_out, vo
   auto dest = [&](int k) -> void* { return (nblocks - 1 - k) % 2 == 0 ? s_out : sbuf; };
   const void* cur = s_in;
   for (int k = 0; k < nblocks; ++k) {
-    NT_TRY(pair_block(p, cur, cur, dest(k), z_out, &w[k], c_s, c_z, hidden, dtype, workspace,
-                      blk, stream));
+    NT_TRY(pair_block(p, cur, cur, dest(k), z_out, params(k), c_s, c_z, hidden, dtype,
+                      workspace, blk, stream));
     cur = dest(k);
   }
   return ok();
+}
+extern "C" {
+
+nt_status nt_pair_chain(const nt_partition* p, const void* s_in, void* s_out, void* z_out,
+                        const nt_block_weights* w, int32_t nblocks, int32_t c_s, int32_t c_z,
+                        int32_t hidden, nt_dtype dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!w) return fail(NT_ERR_NULL, "weights is NULL");
+  if (nblocks < 1) return fail(NT_ERR_INVALID, "nblocks = %d must be at least 1", (int)nblocks);
+  std::vector<nt_block_params> q(nblocks);
+  for (int k = 0; k < nblocks; ++k) q[k] = relu_params(w[k]);
+  return pair_chain(p, s_in, s_out, z_out, [&](int k) { return &q[k]; }, nblocks, c_s, c_z,
+                    hidden, dtype, workspace, workspace_bytes, stream);
+}
+
+nt_status nt_pair_chain_ex(const nt_partition* p, const void* s_in, void* s_out, void* z_out,
+                           const nt_block_params* w, int32_t nblocks, int32_t c_s, int32_t c_z,
+                           int32_t hidden, nt_dtype dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!w) return fail(NT_ERR_NULL, "weights is NULL");
+  return pair_chain(p, s_in, s_out, z_out, [&](int k) { return &w[k]; }, nblocks, c_s, c_z,
+                    hidden, dtype, workspace, workspace_bytes, stream);
 }
 
 nt_status nt_pair_block_rect(const nt_partition* p, const void* s_rows, const void* s_cols,
                              void* s_out, void* z_out, const nt_block_weights* w, int32_t c_s,
                              int32_t c_z, int32_t hidden, nt_dtype dtype, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  return pair_block(p, s_rows, s_cols, s_out, z_out, w, c_s, c_z, hidden, dtype, workspace,
+  if (!w) return fail(NT_ERR_NULL, "weights is NULL");
+  const nt_block_params q = relu_params(*w);
+  return pair_block(p, s_rows, s_cols, s_out, z_out, &q, c_s, c_z, hidden, dtype, workspace,
                     workspace_bytes, stream);
 }
 
@@ -898,10 +1112,22 @@ nt_status nt_block_backward_workspace_bytes(const nt_partition* p, int32_t c_s, 
 }
 
 // The block backward; S > 1 is the non-leading layout (rows of S slices).
+// The ReLU-MLP gradients of nt_block_grads as block parameter gradients.
+static nt_block_param_grads relu_grads(const nt_block_grads& g) {
+  nt_block_param_grads q;
+  std::memset(&q, 0, sizeof(q));
+  q.Wa = g.Wa;
+  q.Wb = g.Wb;
+  q.Wo = g.Wo;
+  q.W1 = g.W1;
+  q.W2 = g.W2;
+  return q;
+}
+
 static nt_status block_backward_s(const nt_partition* p, const void* s_in, const void* z_out,
-                                  const nt_block_weights* w, const float* g_s_out,
+                                  const nt_block_params* w, const float* g_s_out,
                                   const float* g_z_out, float* g_s_in,
-                                  const nt_block_grads* grads, int32_t c_s, int32_t c_z,
+                                  const nt_block_param_grads* grads, int32_t c_s, int32_t c_z,
                                   int32_t hidden, nt_dtype dtype, void* workspace,
                                   size_t workspace_bytes, void* stream, int32_t S) {
   NT_TRY(check_partition(p));
@@ -910,43 +1136,50 @@ static nt_status block_backward_s(const nt_partition* p, const void* s_in, const
   NT_TRY(check_dtype(dtype));
   NT_TRY(check_widths(c_s, c_z, hidden));
   NT_TRY(check_static_axis(S, c_z));
-  if (!w) return fail(NT_ERR_NULL, "weights is NULL");
+  ParamArrays pa;
+  NT_TRY(check_params(w, c_s, c_z, hidden, dtype, &pa));
+  const bool swiglu = w->kind == NT_TRANSITION_LN_SWIGLU;
+  if (swiglu && S != 1)
+    return fail(NT_ERR_INVALID, "the SwiGLU block gradient takes the leading layout (S = 1)");
   if (!grads) return fail(NT_ERR_NULL, "grads is NULL");
   const uint64_t es = esize(dtype);
   const uint64_t TS = (uint64_t)p->T * S, CS = (uint64_t)p->cells * S;
   const uint64_t sb = TS * c_s * es, zb = CS * c_z * es;
   const uint64_t gsb = TS * c_s * 4, gzb = CS * c_z * 4;
-  const uint64_t proj = (uint64_t)c_z * c_s * es, mlp = (uint64_t)c_z * hidden * es;
   const uint64_t dproj = (uint64_t)c_z * c_s * 4, dmlp = (uint64_t)c_z * hidden * 4;
-  const BlockBwdWs L = block_backward_ws(p, c_s, c_z, hidden, dtype, S);
+  const uint64_t dln = (uint64_t)c_z * 4;
+  const BlockBwdWs L = block_backward_ws(p, c_s, c_z, hidden, dtype, S, w->kind);
   NT_TRY(check_array("s_in", s_in, sb));
   NT_TRY(check_array("z_out", z_out, zb));
-  NT_TRY(check_array("Wa", w->Wa, proj));
-  NT_TRY(check_array("Wb", w->Wb, proj));
-  NT_TRY(check_array("W1", w->W1, mlp));
-  NT_TRY(check_array("W2", w->W2, mlp));
-  NT_TRY(check_array("Wo", w->Wo, proj));
   NT_TRY(check_array("g_s_out", g_s_out, gsb));
   if (g_z_out) NT_TRY(check_array("g_z_out", g_z_out, gzb));
   NT_TRY(check_array("g_s_in", g_s_in, gsb));
-  NT_TRY(check_array("dWa", grads->Wa, dproj));
-  NT_TRY(check_array("dWb", grads->Wb, dproj));
-  NT_TRY(check_array("dW1", grads->W1, dmlp));
-  NT_TRY(check_array("dW2", grads->W2, dmlp));
-  NT_TRY(check_array("dWo", grads->Wo, dproj));
+  Arr arrs[24];
+  int n = 0;
+  arrs[n++] = {"s_in", s_in, sb, false};
+  arrs[n++] = {"z_out", z_out, zb, false};
+  arrs[n++] = {"g_s_out", g_s_out, gsb, false};
+  arrs[n++] = {"g_z_out", g_z_out, g_z_out ? gzb : 0, false};
+  arrs[n++] = {"g_s_in", g_s_in, gsb, true};
+  arrs[n++] = {"workspace", workspace, L.total, true};
+  for (int k = 0; k < pa.n; ++k) arrs[n++] = {pa.name[k], pa.ptr[k], pa.bytes[k], false};
+  struct { const char* name; float* ptr; uint64_t bytes; } outs[] = {
+      {"dWa", grads->Wa, dproj}, {"dWb", grads->Wb, dproj}, {"dWo", grads->Wo, dproj},
+      {"dW1", grads->W1, dmlp}, {"dW2", grads->W2, dmlp}, {"dln_gamma", grads->ln_gamma, dln},
+      {"dln_beta", grads->ln_beta, dln}, {"dW_gate", grads->W_gate, dmlp},
+      {"dW_up", grads->W_up, dmlp}, {"dW_down", grads->W_down, dmlp}};
+  const int first = swiglu ? 5 : 3, count = swiglu ? 5 : 2;
+  for (int k = 0; k < 3; ++k) {
+    NT_TRY(check_array(outs[k].name, outs[k].ptr, outs[k].bytes));
+    arrs[n++] = {outs[k].name, outs[k].ptr, outs[k].bytes, true};
+  }
+  for (int k = first; k < first + count; ++k) {
+    NT_TRY(check_array(outs[k].name, outs[k].ptr, outs[k].bytes));
+    arrs[n++] = {outs[k].name, outs[k].ptr, outs[k].bytes, true};
+  }
   NT_TRY(check_workspace(workspace, workspace_bytes, L.total));
-  const Arr arrs[] = {
-      {"s_in", s_in, sb, false},          {"z_out", z_out, zb, false},
-      {"Wa", w->Wa, proj, false},         {"Wb", w->Wb, proj, false},
-      {"W1", w->W1, mlp, false},          {"W2", w->W2, mlp, false},
-      {"Wo", w->Wo, proj, false},         {"g_s_out", g_s_out, gsb, false},
-      {"g_z_out", g_z_out, g_z_out ? gzb : 0, false},
-      {"g_s_in", g_s_in, gsb, true},      {"dWa", grads->Wa, dproj, true},
-      {"dWb", grads->Wb, dproj, true},    {"dW1", grads->W1, dmlp, true},
-      {"dW2", grads->W2, dmlp, true},     {"dWo", grads->Wo, dproj, true},
-      {"workspace", workspace, L.total, true}};
-  const int same[][2] = {{7, 9}};
-  NT_TRY(check_disjoint(arrs, 16, same, 1));
+  const int same[][2] = {{2, 4}};
+  NT_TRY(check_disjoint(arrs, n, same, 1));
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
@@ -968,7 +1201,8 @@ static nt_status block_backward_s(const nt_partition* p, const void* s_in, const
   // recompute the forward's a, b, z and m
   NT_TRY(hip_status(nt::launch_linear2(s_in, dtype, w->Wa, w->Wb, a, b, T, c_z, c_s, s),
                     "projections a, b"));
-  NT_TRY(hip_status(nt::launch_broadcast(*p, a, b, z, W, dtype, s, true), "broadcast"));
+  NT_TRY(hip_status(nt::launch_broadcast(*p, a, b, z, W, swiglu ? NT_F32 : dtype, s, true),
+                    "broadcast"));
   NT_TRY(hip_status(nt::launch_reduce(*p, z_out, m, W, dtype, s), "column mean"));
   NT_TRY(hip_status(nt::launch_transpose(w->Wo, WoT, c_s, c_z, dtype, s), "transpose Wo"));
   NT_TRY(hip_status(nt::launch_transpose(w->Wa, WaT, c_z, c_s, dtype, s), "transpose Wa"));
@@ -981,7 +1215,11 @@ static nt_status block_backward_s(const nt_partition* p, const void* s_in, const
                                        L.psplits, s),
                     "dWo"));
   // mean (formed inside the transition's gradient), transition, broadcast
-  if (S == 1) {
+  if (swiglu) {
+    NT_TRY(hip_status(nt::launch_mean_backward(*p, g_m, g_z_out, G, W, s), "mean backward"));
+    NT_TRY(swiglu_transition_backward(p->cells, static_cast<const float*>(z), G, *w, *grads, c_z,
+                                      hidden, base + L.trans, s));
+  } else if (S == 1) {
     NT_TRY(transition_backward(p, z, nullptr, w->W1, w->W2, G, grads->W1, grads->W2, c_z, hidden,
                                dtype, base + L.trans, s, g_m, g_z_out));
   } else {
@@ -1014,6 +1252,33 @@ nt_status nt_pair_block_backward(const nt_partition* p, const void* s_in, const 
                                  const float* g_z_out, float* g_s_in, const nt_block_grads* grads,
                                  int32_t c_s, int32_t c_z, int32_t hidden, nt_dtype dtype,
                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (!w) return fail(NT_ERR_NULL, "weights is NULL");
+  if (!grads) return fail(NT_ERR_NULL, "grads is NULL");
+  const nt_block_params q = relu_params(*w);
+  const nt_block_param_grads g = relu_grads(*grads);
+  return block_backward_s(p, s_in, z_out, &q, g_s_out, g_z_out, g_s_in, &g, c_s, c_z, hidden,
+                          dtype, workspace, workspace_bytes, stream, 1);
+}
+
+nt_status nt_block_backward_ex_workspace_bytes(const nt_partition* p, int32_t kind, int32_t c_s,
+                                               int32_t c_z, int32_t hidden, nt_dtype dtype,
+                                               size_t* bytes) {
+  NT_TRY(check_partition(p));
+  NT_TRY(check_dtype(dtype));
+  NT_TRY(check_widths(c_s, c_z, hidden));
+  if (kind != NT_TRANSITION_RELU_MLP && kind != NT_TRANSITION_LN_SWIGLU)
+    return fail(NT_ERR_INVALID, "unknown transition kind %d", (int)kind);
+  if (!bytes) return fail(NT_ERR_NULL, "bytes is NULL");
+  *bytes = block_backward_ws(p, c_s, c_z, hidden, dtype, 1, kind).total;
+  return ok();
+}
+
+nt_status nt_pair_block_backward_ex(const nt_partition* p, const void* s_in, const void* z_out,
+                                    const nt_block_params* w, const float* g_s_out,
+                                    const float* g_z_out, float* g_s_in,
+                                    const nt_block_param_grads* grads, int32_t c_s, int32_t c_z,
+                                    int32_t hidden, nt_dtype dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
   return block_backward_s(p, s_in, z_out, w, g_s_out, g_z_out, g_s_in, grads, c_s, c_z, hidden,
                           dtype, workspace, workspace_bytes, stream, 1);
 }
@@ -1036,7 +1301,9 @@ nt_status nt_pair_block_nl(const nt_partition* p, const void* s_in, void* s_out,
   NT_TRY(check_partition(p));
   if (p->col_offsets != p->single_offsets)
     return fail(NT_ERR_INVALID, "the non-leading block takes square partitions");
-  return pair_block(p, s_in, s_in, s_out, z_out, w, c_s, c_z, hidden, dtype, workspace,
+  if (!w) return fail(NT_ERR_NULL, "weights is NULL");
+  const nt_block_params q = relu_params(*w);
+  return pair_block(p, s_in, s_in, s_out, z_out, &q, c_s, c_z, hidden, dtype, workspace,
                     workspace_bytes, stream, S);
 }
 
@@ -1058,7 +1325,11 @@ nt_status nt_pair_block_backward_nl(const nt_partition* p, const void* s_in, con
                                     const nt_block_grads* grads, int32_t S, int32_t c_s,
                                     int32_t c_z, int32_t hidden, nt_dtype dtype, void* workspace,
                                     size_t workspace_bytes, void* stream) {
-  return block_backward_s(p, s_in, z_out, w, g_s_out, g_z_out, g_s_in, grads, c_s, c_z, hidden,
+  if (!w) return fail(NT_ERR_NULL, "weights is NULL");
+  if (!grads) return fail(NT_ERR_NULL, "grads is NULL");
+  const nt_block_params q = relu_params(*w);
+  const nt_block_param_grads g = relu_grads(*grads);
+  return block_backward_s(p, s_in, z_out, &q, g_s_out, g_z_out, g_s_in, &g, c_s, c_z, hidden,
                           dtype, workspace, workspace_bytes, stream, S);
 }
 

@@ -103,11 +103,14 @@ hipError_t launch_broadcast(const nt_partition& p, const void* a, const void* b,
 // the prologue (a, b are fp32 [T, c_z] whatever the storage dtype).
 bool transition_has_mfma(int c_z, int hidden, nt_dtype dtype);
 // Pre-normalised SwiGLU transition (bf16, c_z in {64, 128}, hidden % 32 == 0).
+// z_in == nullptr selects the fused form: z = a[row] + b[col] from the fp32
+// projections (needs the tile_sample index).
 bool transition_swiglu_supported(int c_z, int hidden, nt_dtype dtype);
-hipError_t launch_transition_swiglu(const nt_partition& p, const void* z_in, void* z_out,
-                                    const float* gamma, const float* beta, const void* Wg,
-                                    const void* Wu, const void* Wd, int c_z, int hidden,
-                                    float eps, hipStream_t stream);
+hipError_t launch_transition_swiglu(const nt_partition& p, const void* z_in, const void* a,
+                                    const void* b, void* z_out, const float* gamma,
+                                    const float* beta, const void* Wg, const void* Wu,
+                                    const void* Wd, int c_z, int hidden, float eps,
+                                    hipStream_t stream);
 // Fused broadcast + transition for c_z = 128, hidden = 512 with both weights
 // held in registers (one hidden quarter per wave) over 32-cell blocks; needs
 // the tile_sample index and T < 2^22.
@@ -169,6 +172,19 @@ hipError_t launch_wgrad_rc(const void* z, const void* Gb, const void* W1, const 
 // device, and its device address on the current device.
 constexpr size_t kStaticScratchBytes = size_t(16) << 20;
 hipError_t static_scratch(void** ptr);
+// ---- SwiGLU transition gradient pieces (nt_swiglu_bwd.hip), c_z 64 or 128
+// x = LN(z) row by row, fp32 (z fp32 [rows, c_z]).
+hipError_t launch_ln_rows(const float* z, const float* gamma, const float* beta, float* x,
+                          int64_t rows, int c_z, float eps, hipStream_t s);
+// A = silu(g) u, g_u = g_A silu(g), g_g = g_A u silu'(g), all bf16; n elements.
+hipError_t launch_swiglu_gate_bwd(const float* g, const float* u, const float* gA, void* A,
+                                  void* gu, void* gg, int64_t n, hipStream_t s);
+// G += LN's adjoint of gx (in place); dgamma, dbeta [c_z] from per-workgroup
+// partials (part_gamma, part_beta: ln_backward_blocks(rows, c_z) x c_z floats).
+int ln_backward_blocks(int64_t rows, int c_z);
+hipError_t launch_ln_backward(const float* z, const float* gamma, const float* gx, float* G,
+                              float* part_gamma, float* part_beta, float* dgamma, float* dbeta,
+                              int64_t rows, int c_z, float eps, hipStream_t s);
 // Compute units of the current device (cached per device).
 int device_cu_count();
 // Matrix-core transition gradient (bf16, c_z = 128, hidden = 512): W2T =

@@ -18,6 +18,13 @@
 //    into the second product's operand, Y^T += Wd . A^T;
 //  * the residual adds the bf16 input in fp32 and rounds once.
 // The three weight chunks stream through two LDS buffers.
+//
+// Fused form (the block's, Equation 1's first two lines in one kernel): z is
+// not read but formed, z = a[row] + b[col] from the fp32 projections, each
+// lane decoding its cell (Equation 3 inverted, from the first sample of the
+// 256-cell tile); LN takes its statistics on that fp32 z, and the epilogue
+// forms z again in fp32 for the residual, so the pair state is rounded once,
+// on output.
 #include "nt_device.hpp"
 #include "nt_internal.hpp"
 
@@ -44,9 +51,14 @@ __device__ __forceinline__ int sg_feat_row(int fb, int q) {
   return 32 * (fb >> 1) + 8 * (q >> 2) + 4 * (fb & 1) + (q & 3);
 }
 
-template <int CZ>
+static_assert(kSgTileCells == kSampleIndexSpan, "a tile is one entry of the sample index");
+
+template <int CZ, bool FUSED>
 __global__ __launch_bounds__(kSgWaves * 64, 2) void k_transition_swiglu(
-    const bf16* __restrict__ z_in, const float* __restrict__ gamma,
+    const bf16* __restrict__ z_in, const float* __restrict__ a, const float* __restrict__ b,
+    const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
+    const int64_t* __restrict__ col_offsets, const int32_t* __restrict__ col_lengths,
+    const int32_t* __restrict__ tile_sample, const float* __restrict__ gamma,
     const float* __restrict__ beta, const bf16* __restrict__ Wg, const bf16* __restrict__ Wu,
     const bf16* __restrict__ Wd, bf16* z_out, int64_t cells, int hidden, float eps) {
   constexpr int KB = CZ / 32;          // k-blocks of GEMM1 (K = c_z)
@@ -64,20 +76,50 @@ __global__ __launch_bounds__(kSgWaves * 64, 2) void k_transition_swiglu(
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t cell0 = (int64_t)blockIdx.x * kSgTileCells + wave * kSgCellsPerWave;
 
-  // ---- prologue: z slices and their LN
+  // ---- prologue: z slices and their LN. Fused: the single rows of each
+  // lane's cell (a cell past the end decodes as the last one; it is not
+  // stored).
+  int64_t arow[kSgBlocks], bcol[kSgBlocks];
+  if constexpr (FUSED) {
+    const int i0 = tile_sample[blockIdx.x];
+#pragma unroll
+    for (int cb = 0; cb < kSgBlocks; ++cb) {
+      const int64_t c0 = cell0 + cb * 16 + l16;
+      const int64_t cell = c0 < cells ? c0 : cells - 1;
+      int i = i0;
+      while (pair_offsets[i + 1] <= cell) ++i;
+      const int64_t m = col_lengths[i], local = cell - pair_offsets[i];
+      const int64_t r = local / m;
+      arow[cb] = (single_offsets[i] + r) * CZ + 8 * g;
+      bcol[cb] = (col_offsets[i] + (local - r * m)) * CZ + 8 * g;
+    }
+  }
+  // z of one lane's cell: 8 features of each k-block, fp32
+  auto fused_z = [&](int cb, int kb, float* z8) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 va = *reinterpret_cast<const f32x4*>(a + arow[cb] + 32 * kb + 4 * h);
+      const f32x4 vb = *reinterpret_cast<const f32x4*>(b + bcol[cb] + 32 * kb + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z8[4 * h + e] = va[e] + vb[e];
+    }
+  };
   bf16x8 zb[kSgBlocks][KB], xb[kSgBlocks][KB];
+  if constexpr (!FUSED) {
 #pragma unroll
-  for (int cb = 0; cb < kSgBlocks; ++cb) {
-    const int64_t cell = cell0 + cb * 16 + l16;
-    if (cell < cells) {
-      const bf16* zr = z_in + cell * CZ + 8 * g;
+    for (int cb = 0; cb < kSgBlocks; ++cb) {
+      const int64_t cell = cell0 + cb * 16 + l16;
+      if (cell < cells) {
+        const bf16* zr = z_in + cell * CZ + 8 * g;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) zb[cb][kb] = *reinterpret_cast<const bf16x8*>(zr + 32 * kb);
-    } else {
+        for (int kb = 0; kb < KB; ++kb)
+          zb[cb][kb] = *reinterpret_cast<const bf16x8*>(zr + 32 * kb);
+      } else {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) zb[cb][kb][e] = (bf16)0.f;
+          for (int e = 0; e < 8; ++e) zb[cb][kb][e] = (bf16)0.f;
+      }
     }
   }
   float gam[KB][8], bet[KB][8];
@@ -95,11 +137,21 @@ __global__ __launch_bounds__(kSgWaves * 64, 2) void k_transition_swiglu(
     }
 #pragma unroll
   for (int cb = 0; cb < kSgBlocks; ++cb) {
+    float zf[KB][8];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if constexpr (FUSED) {
+        fused_z(cb, kb, zf[kb]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zf[kb][e] = (float)zb[cb][kb][e];
+      }
+    }
     float s = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += (float)zb[cb][kb][e];
+      for (int e = 0; e < 8; ++e) s += zf[kb][e];
     s += __shfl_xor(s, 16);
     s += __shfl_xor(s, 32);
     const float mu = s * (1.f / CZ);
@@ -108,7 +160,7 @@ __global__ __launch_bounds__(kSgWaves * 64, 2) void k_transition_swiglu(
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float d = (float)zb[cb][kb][e] - mu;
+        const float d = zf[kb][e] - mu;
         q += d * d;
       }
     q += __shfl_xor(q, 16);
@@ -118,7 +170,7 @@ __global__ __launch_bounds__(kSgWaves * 64, 2) void k_transition_swiglu(
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        xb[cb][kb][e] = (bf16)(((float)zb[cb][kb][e] - mu) * rstd * gam[kb][e] + bet[kb][e]);
+        xb[cb][kb][e] = (bf16)((zf[kb][e] - mu) * rstd * gam[kb][e] + bet[kb][e]);
   }
 
   // ---- weight staging: piece p of a chunk -> fragment p / 64, lane p % 64
@@ -202,10 +254,16 @@ __global__ __launch_bounds__(kSgWaves * 64, 2) void k_transition_swiglu(
     bf16* dst = z_out + cell * CZ + 8 * g;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      float zf[8];
+      if constexpr (FUSED) {
+        fused_z(cb, kb, zf);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zf[e] = (float)zb[cb][kb][e];
+      }
       bf16x8 o;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        o[e] = (bf16)((float)zb[cb][kb][e] + y[cb][2 * kb + (e >> 2)][e & 3]);
+      for (int e = 0; e < 8; ++e) o[e] = (bf16)(zf[e] + y[cb][2 * kb + (e >> 2)][e & 3]);
       *reinterpret_cast<bf16x8*>(dst + 32 * kb) = o;
     }
   }
@@ -217,21 +275,22 @@ bool transition_swiglu_supported(int c_z, int hidden, nt_dtype dtype) {
   return dtype == NT_BF16 && (c_z == 64 || c_z == 128) && hidden > 0 && hidden % kSgChunk == 0;
 }
 
-hipError_t launch_transition_swiglu(const nt_partition& p, const void* z_in, void* z_out,
-                                    const float* gamma, const float* beta, const void* Wg,
-                                    const void* Wu, const void* Wd, int c_z, int hidden,
-                                    float eps, hipStream_t stream) {
+hipError_t launch_transition_swiglu(const nt_partition& p, const void* z_in, const void* a,
+                                    const void* b, void* z_out, const float* gamma,
+                                    const float* beta, const void* Wg, const void* Wu,
+                                    const void* Wd, int c_z, int hidden, float eps,
+                                    hipStream_t stream) {
   if (p.cells == 0) return hipSuccess;
   const int64_t blocks = (p.cells + kSgTileCells - 1) / kSgTileCells;
   const bf16 *zi = static_cast<const bf16*>(z_in), *wg = static_cast<const bf16*>(Wg),
              *wu = static_cast<const bf16*>(Wu), *wd = static_cast<const bf16*>(Wd);
+  const float *af = static_cast<const float*>(a), *bf = static_cast<const float*>(b);
   bf16* zo = static_cast<bf16*>(z_out);
-  if (c_z == 128)
-    hipLaunchKernelGGL(k_transition_swiglu<128>, dim3((unsigned)blocks), dim3(kSgWaves * 64), 0,
-                       stream, zi, gamma, beta, wg, wu, wd, zo, p.cells, hidden, eps);
-  else
-    hipLaunchKernelGGL(k_transition_swiglu<64>, dim3((unsigned)blocks), dim3(kSgWaves * 64), 0,
-                       stream, zi, gamma, beta, wg, wu, wd, zo, p.cells, hidden, eps);
+  auto kern = z_in ? (c_z == 128 ? k_transition_swiglu<128, false> : k_transition_swiglu<64, false>)
+                   : (c_z == 128 ? k_transition_swiglu<128, true> : k_transition_swiglu<64, true>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kSgWaves * 64), 0, stream, zi, af, bf,
+                     p.pair_offsets, p.single_offsets, p.col_offsets, p.col_lengths,
+                     p.tile_sample, gamma, beta, wg, wu, wd, zo, p.cells, hidden, eps);
   return hipGetLastError();
 }
 

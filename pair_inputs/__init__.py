@@ -154,6 +154,42 @@ def make_inputs(lengths: Sequence[int], c_s: int, c_z: int, hidden: int,
     return Inputs(lengths, s, weights, c_s, c_z, hidden, dtype, name)
 
 
+SWIGLU_NAMES = ("Wa", "Wb", "Wo", "ln_gamma", "ln_beta", "W_gate", "W_up", "W_down")
+
+
+def draw_swiglu_weights(rng: np.random.Generator, c_s: int, c_z: int, hidden: int,
+                        dtype: str) -> dict:
+    """One block's parameters for the pre-normalised SwiGLU transition: the
+    projections and the three products N(0, 1/fan_in), drawn [in, out] then
+    stored [out, in] in `dtype`; the LayerNorm affine pair stored fp32,
+    gamma ~ 1 + 0.2 N(0, 1) and beta ~ 0.1 N(0, 1) (away from the identity
+    initialisation, so that both reach the results)."""
+    shapes = {"Wa": (c_s, c_z), "Wb": (c_s, c_z), "Wo": (c_z, c_s), "W_gate": (c_z, hidden),
+              "W_up": (c_z, hidden), "W_down": (hidden, c_z)}
+    out = {}
+    for name in SWIGLU_NAMES:
+        if name == "ln_gamma":
+            out[name] = store(1.0 + 0.2 * rng.standard_normal(c_z), "f32")
+        elif name == "ln_beta":
+            out[name] = store(0.1 * rng.standard_normal(c_z), "f32")
+        else:
+            fan_in, fan_out = shapes[name]
+            w = rng.standard_normal((fan_in, fan_out)) / math.sqrt(fan_in)
+            out[name] = store(np.ascontiguousarray(w.T), dtype)
+    return out
+
+
+def make_swiglu_inputs(lengths: Sequence[int], c_s: int, c_z: int, hidden: int, dtype: str,
+                       blocks: int = 1, seed: int = 0) -> Inputs:
+    """Singles ~ N(0, 1) and per-block SwiGLU-block parameters, seeded."""
+    rng = np.random.default_rng(seed)
+    lengths = np.asarray(lengths, dtype=np.int32)
+    T = int(lengths.astype(np.int64).sum())
+    s = store(rng.standard_normal((T, c_s)), dtype)
+    weights = [draw_swiglu_weights(rng, c_s, c_z, hidden, dtype) for _ in range(blocks)]
+    return Inputs(lengths, s, weights, c_s, c_z, hidden, dtype, "swiglu")
+
+
 def workload_inputs(index_or_name, blocks: Optional[int] = None) -> Inputs:
     """The seeded inputs of a workload: lengths, then singles, then weights."""
     w = workload(index_or_name)

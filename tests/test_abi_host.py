@@ -461,3 +461,38 @@ def test_noalloc_rejects_oversized_partition(lib):
                                    _native.NT_BF16, None)
     assert st == _native.NT_ERR_WORKSPACE
     assert "static scratch" in lib.nt_last_error().decode()
+
+
+def test_block_params_layout_and_validation(lib):
+    """nt_block_params: int32 kind, float ln_eps, ten pointers. The transition
+    kind is checked before anything is enqueued: an unknown kind, the SwiGLU
+    kind in fp32, widths it does not take, a negative epsilon."""
+    assert ctypes.sizeof(_native.NtBlockParams) == 8 + 10 * 8
+    assert _native.NtBlockParams.Wa.offset == 8
+    assert ctypes.sizeof(_native.NtBlockParamGrads) == 10 * 8
+    p = fake_partition()
+    s, so, z = FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000
+    ws = FAKE + 0x800000
+
+    def call(kind, dtype=_native.NT_BF16, c_z=128, hidden=512, eps=1e-5):
+        w = _native.NtBlockParams()
+        w.kind, w.ln_eps = kind, eps
+        for k, name in enumerate(_native.PARAM_NAMES):
+            setattr(w, name, FAKE + 0x400000 + 0x40000 * k)
+        return lib.nt_pair_block_ex(ctypes.byref(p), s, None, so, z, ctypes.byref(w), 64, c_z,
+                                    hidden, dtype, ws, 1 << 30, None)
+
+    assert call(7) == _native.NT_ERR_INVALID
+    assert "transition kind" in lib.nt_last_error().decode()
+    assert call(_native.NT_TRANSITION_LN_SWIGLU, dtype=_native.NT_F32) == _native.NT_ERR_DTYPE
+    assert call(_native.NT_TRANSITION_LN_SWIGLU, c_z=96) == _native.NT_ERR_INVALID
+    assert call(_native.NT_TRANSITION_LN_SWIGLU, hidden=520) == _native.NT_ERR_INVALID
+    assert call(_native.NT_TRANSITION_LN_SWIGLU, eps=-1.0) == _native.NT_ERR_INVALID
+    need = ctypes.c_size_t()
+    assert lib.nt_block_backward_ex_workspace_bytes(ctypes.byref(p), 9, 64, 128, 512,
+                                                    _native.NT_BF16,
+                                                    ctypes.byref(need)) == _native.NT_ERR_INVALID
+    assert lib.nt_block_backward_ex_workspace_bytes(ctypes.byref(p),
+                                                    _native.NT_TRANSITION_LN_SWIGLU, 64, 128, 512,
+                                                    _native.NT_BF16, ctypes.byref(need)) == 0
+    assert need.value > 0
