@@ -281,8 +281,10 @@ nt_status check_params(const nt_block_params* w, int32_t c_s, int32_t c_z, int32
 }
 
 // The transition of a block over its pair state: fused (z = a[row] + b[col]
-// formed on chip) for S = 1, else the broadcast over rows of S slices
-// followed by the cell-local transition in place over cells * S rows.
+// formed on chip) for S = 1, and for S slices per cell where the
+// weight-stationary kernel takes the shape; else the broadcast over rows of
+// S slices followed by the cell-local transition in place over cells * S
+// rows.
 nt_status block_transition(const nt_partition& p, const nt_block_params& w, const void* a,
                            const void* b, void* z_out, int32_t c_z, int32_t hidden,
                            nt_dtype dtype, int32_t S, hipStream_t s) {
@@ -297,6 +299,10 @@ nt_status block_transition(const nt_partition& p, const nt_block_params& w, cons
                                             dtype, s),
                       "fused broadcast + transition");
   }
+  if (!swiglu && nt::transition_ws_slices_supported(p, c_z, hidden, dtype, S))
+    return hip_status(nt::launch_transition_ws(p, a, b, z_out, w.W1, w.W2, nt::device_cu_count(),
+                                               s, S),
+                      "fused broadcast + transition over slices");
   NT_TRY(hip_status(nt::launch_broadcast(p, a, b, z_out, S * c_z, dtype, s, true), "broadcast"));
   const nt_partition v = rows_view(p, S);
   if (swiglu)

@@ -112,10 +112,17 @@ hipError_t launch_transition_swiglu(const nt_partition& p, const void* z_in, con
                                     const void* Wd, int c_z, int hidden, float eps,
                                     hipStream_t stream);
 // Fused broadcast + transition for c_z = 128, hidden = 512 with both weights
-// held in registers (one hidden quarter per wave) over 32-cell blocks; needs
-// the tile_sample index and T < 2^22.
+// held in registers (one hidden quarter per wave) over 32-row blocks; needs
+// the tile_sample index and T S < 2^22. S > 1: the non-leading layout, S
+// slices of c_z per pair cell and per single row (a, b: [T S, c_z]).
 hipError_t launch_transition_ws(const nt_partition& p, const void* a, const void* b, void* z_out,
-                                const void* W1, const void* W2, int cus, hipStream_t stream);
+                                const void* W1, const void* W2, int cus, hipStream_t stream,
+                                int S = 1);
+// The fused non-leading form: the weight-stationary kernel over S slices
+// per cell (bf16, c_z 128, hidden 512, T S < 2^22); false when the shape or
+// size does not allow it.
+bool transition_ws_slices_supported(const nt_partition& p, int c_z, int hidden, nt_dtype dtype,
+                                    int S);
 hipError_t launch_transition(const nt_partition& p, const void* z_in, const void* a, const void* b,
                              void* z_out, const void* W1, const void* W2, int c_z, int hidden,
                              nt_dtype dtype, hipStream_t stream);

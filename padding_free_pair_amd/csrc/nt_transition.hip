@@ -832,6 +832,13 @@ hipError_t launch_generic(const nt_partition& p, const void* z_in, const void* a
 
 int device_cu_count() { return device_cus(); }
 
+bool transition_ws_slices_supported(const nt_partition& p, int c_z, int hidden, nt_dtype dtype,
+                                    int S) {
+  const int64_t t = (p.T > p.T_cols ? p.T : p.T_cols) * S;
+  return dtype == NT_BF16 && c_z == 128 && hidden == 512 && p.tile_sample &&
+         t <= (int64_t)(INT32_MAX / (128 * 4));
+}
+
 bool transition_has_mfma(int c_z, int hidden, nt_dtype dtype) {
   return dtype == NT_BF16 && (c_z == 64 || c_z == 128) && hidden % kChunk == 0;
 }

@@ -24,6 +24,9 @@
 //    per cell load a[row] and b[col] (64 contiguous bytes each), form z in
 //    fp32 and write the bf16 operand fragments and the fp32 residual in the
 //    owners' accumulator layout.
+//  * With S > 1 (the non-leading layout) the rows are S slices per pair
+//    cell: row R is slice R mod S of cell R / S, and its operands are
+//    a[(eta_i + r) S + s] and b[(mu_i + c) S + s].
 //  * LDS, double-buffered: operand fragments 2 x 8 KiB, residuals
 //    2 x 16 KiB, partials 2 x 48 KiB. Two barriers per phase (the staging
 //    writes at its end, the partial writes in slot 1 of the next).
@@ -131,7 +134,7 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
     const int64_t* __restrict__ col_offsets, const int32_t* __restrict__ col_lengths,
     const int32_t* __restrict__ tile_sample, int B,
     const bf16* __restrict__ W1, const bf16* __restrict__ W2, bf16* __restrict__ z_out,
-    int64_t cells, int64_t nblocks, int64_t per, int64_t T_rows, int64_t T_cols) {
+    int64_t cells, int64_t nblocks, int64_t per, int64_t T_rows, int64_t T_cols, int S) {
   constexpr int CZ = 128, HID = 512;
   constexpr int KT = CZ / 16;  // first-product k-steps
   constexpr int ROW = CZ * 4;  // bytes of one fp32 single row
@@ -239,19 +242,24 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
   // first sample of the cell's 256-cell tile (a vector load, so that it does
   // not share a counter with the LDS traffic).
   const __amdgpu_buffer_rsrc_t ts_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)tile_sample, 0, (int)(4 * ((cells + kSampleIndexSpan - 1) / kSampleIndexSpan)),
+      (void*)tile_sample, 0, (int)(4 * ((cells / S + kSampleIndexSpan - 1) / kSampleIndexSpan)),
       kWsBufFlags);
   // It is issued a phase ahead, for the block after next.
   int64_t d_cell = 0, d_p1 = 0, d_p2 = 0, d_base = 0;
-  int d_i0 = 0, d_i = 0, d_len = 1, d_eta = 0, d_mu = 0, d_row = 0, d_col = 0;
+  int d_i0 = 0, d_i = 0, d_len = 1, d_eta = 0, d_mu = 0, d_row = 0, d_col = 0, d_slice = 0;
   auto dec1 = [&](int64_t blk) {
     d_i0 = __builtin_amdgcn_raw_buffer_load_b32(
-        ts_rsrc, (int)((blk * kWsCells / kSampleIndexSpan) * 4), 0, 0);
+        ts_rsrc, (int)((blk * kWsCells / S / kSampleIndexSpan) * 4), 0, 0);
   };
   // step 2: offsets of the next two samples
   auto dec2 = [&](int64_t blk) {
     const int64_t c = blk * kWsCells + sc;
-    d_cell = c < cells ? c : cells - 1;  // a cell past the end repeats the last one
+    d_cell = c < cells ? c : cells - 1;  // a row past the end repeats the last one
+    if (S > 1) {  // row d_cell = slice d_slice of pair cell d_cell / S
+      const int64_t pc = d_cell / S;
+      d_slice = (int)(d_cell - pc * S);
+      d_cell = pc;
+    }
     d_i = d_i0;
     const int i2 = d_i + 2 < B ? d_i + 2 : B;
     if constexpr (LDS_PART) {
@@ -297,8 +305,8 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
       r = local / d_len;
       c = local - r * d_len;
     }
-    d_row = (int)(d_eta + r);
-    d_col = (int)(d_mu + c);
+    d_row = (int)((d_eta + r) * S + d_slice);
+    d_col = (int)((d_mu + c) * S + d_slice);
   };
   // step 5: the gathers (eight threads per cell, 64 contiguous bytes each)
   auto gather_a = [&](int set) {
@@ -514,8 +522,10 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
 }  // namespace
 
 hipError_t launch_transition_ws(const nt_partition& p, const void* a, const void* b, void* z_out,
-                                const void* W1, const void* W2, int cus, hipStream_t stream) {
-  const int64_t nblocks = (p.cells + kWsCells - 1) / kWsCells;
+                                const void* W1, const void* W2, int cus, hipStream_t stream,
+                                int S) {
+  const int64_t rows = p.cells * S;  // rows of c_z: S slices per pair cell
+  const int64_t nblocks = (rows + kWsCells - 1) / kWsCells;
   // `per` blocks to a workgroup, and only as many workgroups as that needs,
   // so that (grid - 1) * per < nblocks: every workgroup has a block
   const int64_t per = (nblocks + cus - 1) / cus;
@@ -528,7 +538,7 @@ hipError_t launch_transition_ws(const nt_partition& p, const void* a, const void
                      static_cast<const float*>(a), static_cast<const float*>(b), p.pair_offsets,
                      p.single_offsets, p.col_offsets, p.col_lengths, p.tile_sample, p.B,
                      static_cast<const bf16*>(W1), static_cast<const bf16*>(W2),
-                     static_cast<bf16*>(z_out), p.cells, nblocks, per, p.T, p.T_cols);
+                     static_cast<bf16*>(z_out), rows, nblocks, per, p.T * S, p.T_cols * S, S);
   return hipGetLastError();
 }
 

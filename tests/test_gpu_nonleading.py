@@ -135,3 +135,20 @@ def test_block_nl_many_samples(nt):
     for k in ("Wa", "Wb", "W1", "W2", "Wo"):
         assert scaled_max_err(grads[k].cpu().numpy(), ref[k]) <= TOL["f32"], k
     assert cells > 0
+
+
+def test_block_nl_full_size(nt):
+    """S = 3 slices on the high-variation lengths at the four-block widths,
+    the broadcast fused into the weight-stationary transition: every cell
+    and single row against the oracle."""
+    x = pin.workload_inputs(3, blocks=1)
+    lengths = x.lengths.tolist()
+    S = 3
+    announce(f"non-leading block full size S={S}")
+    s = pin.random_rows(sum(lengths), S * x.c_s, "bf16", seed=31)
+    p = nt.nt_make_partition(lengths)
+    so, zo = nt.nt_pair_block_nl(p, to_dev(s, torch), weights_to_dev(x.weights[0], torch), S)
+    torch.cuda.synchronize()
+    rs, rz = oracle.block_nl(lengths, s.f64, {k: v.f64 for k, v in x.weights[0].items()}, S)
+    assert scaled_max_err(f64(zo, torch), rz) <= TOL["bf16"]
+    assert scaled_max_err(f64(so, torch), rs) <= TOL["bf16"]
