@@ -117,7 +117,11 @@ __global__ __launch_bounds__(kWgThreads) void k_wgrad(const bf16* __restrict__ A
 //   g_H = gh * [pre > 0], H = relu(pre)            (lane-local)
 //   dW1[j] += g_H^T z,  dW2[:, j] += bf16(G)^T H    (k = cells)
 // Workgroup (slice, group): four waves own chunks 4 group .. 4 group + 3 and
-// walk the same 64-cell blocks of the slice. In the first two products the
+// walk the same 64-cell blocks of the slice. Workgroups are handed to the
+// XCDs round robin (workgroup b to XCD b mod 8), so the index is split as
+// b = 8 (GROUPS q + group) + x with slice 8 q + x: the GROUPS workgroups of a
+// slice run on one XCD at the same time and read its cells through one L2
+// (one HBM fetch instead of GROUPS). In the first two products the
 // lane holds a unit and 16 cells, so the packed g_H and H are already the
 // MFMA operands of the contractions over cells (k-step s takes result
 // elements 8 s .. 8 s + 7, cells 16 s + 8 (e / 4) + 4 h + e % 4); the other
@@ -136,7 +140,7 @@ template <int CZ, int HID>
 __global__ __launch_bounds__(256, 1) void k_wgrad_rc(
     const bf16* __restrict__ z, const bf16* __restrict__ Gb, const bf16* __restrict__ W1,
     const bf16* __restrict__ W2T, float* __restrict__ part1, float* __restrict__ part2,
-    int64_t cells, int64_t slice_cells) {
+    int64_t cells, int64_t slice_cells, int64_t slices) {
   constexpr int KT = CZ / 16, FB = CZ / 32, GROUPS = HID / 128;
   static_assert(CZ == 128, "row staging assumes 128 features");
   // [buffer][operand: 0 z, 1 G]
@@ -144,8 +148,10 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_rc(
   __shared__ bf16 rm[2][2][kRcCells * kRcRow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int group = blockIdx.x % GROUPS;
-  const int64_t slice = blockIdx.x / GROUPS;
+  const int64_t q = blockIdx.x / 8;
+  const int group = (int)(q % GROUPS);
+  const int64_t slice = 8 * (q / GROUPS) + blockIdx.x % 8;
+  if (slice >= slices) return;  // the grid is rounded up to whole XCD rounds
   const int j = 4 * group + wave;
   const int64_t cb0 = slice * slice_cells;
   const int64_t cb1 = cb0 + slice_cells < cells ? cb0 + slice_cells : cells;
@@ -310,10 +316,11 @@ hipError_t launch_wgrad_rc(const void* z, const void* Gb, const void* W1, const 
   const int64_t S = (cells + slice_cells - 1) / slice_cells;
   float* part1 = part;
   float* part2 = part + S * MN;
-  hipLaunchKernelGGL((k_wgrad_rc<CZ, HID>), dim3((unsigned)(S * (HID / 128))), dim3(256), 0,
+  const int64_t S8 = (S + 7) / 8 * 8;
+  hipLaunchKernelGGL((k_wgrad_rc<CZ, HID>), dim3((unsigned)(S8 * (HID / 128))), dim3(256), 0,
                      stream, static_cast<const bf16*>(z), static_cast<const bf16*>(Gb),
                      static_cast<const bf16*>(W1), static_cast<const bf16*>(W2T), part1, part2,
-                     cells, slice_cells);
+                     cells, slice_cells, S);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_sum_splits(part1, dW1, (int)S, MN, stream);
