@@ -189,7 +189,7 @@ def backward_rooflines(r: PackedRunner, reps: int) -> dict:
                                                            g_z=g_z, dW1=dW1, dW2=dW2,
                                                            workspace=ws), reps, torch)
     flops = 10.0 * x.c_z * x.hidden * r.cells
-    return {"kernel": "k_transition_bwd + k_wgrad x2 (transition gradient, one call)",
+    return {"kernel": "k_transition_bwd + k_wgrad_rc (transition gradient, one call)",
             "bound": "mfma", "ms": t * 1e3, "achieved": flops / t / 1e12,
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "flop_per_launch": flops,
             "frac": flops / t / 1e12 / PEAK_BF16_TFLOPS}
@@ -285,7 +285,9 @@ def non_leading(x: pin.Inputs, args, torch, nt, S: int = 3) -> dict:
     return {"S": S, "cells": cells, "blocks": nb, "forward_ms_per_step": t_f * 1e3,
             "forward_value": cells * nb / t_f, "train_ms_per_step": t_t * 1e3,
             "train_value": cells * nb / t_t, "unit": "pair cells/s per block (S slices per cell)",
-            "path": "broadcast, then the transition over cells * S rows (unfused)"}
+            "path": "the broadcast fused into the weight-stationary transition over the S "
+                    "slices of every cell (k_transition_ws), then the column mean over rows of "
+                    "S c_z values"}
 
 
 def granularity(x: pin.Inputs, r: PackedRunner, t_seg: float, args, torch, nt) -> dict:
@@ -485,7 +487,7 @@ def swiglu_roofline(r: PackedRunner, reps: int) -> dict:
     t = time_kernel(lambda: nt.nt_pair_transition_swiglu(r.p, r.z, gamma, beta, Wg, Wu, Wd,
                                                          z_out=out), reps, torch)
     flops = 6.0 * cz * hd * r.cells
-    return {"kernel": "k_transition_swiglu (LN + SwiGLU, expansion four)", "bound": "mfma",
+    return {"kernel": "k_swiglu32 (LN + SwiGLU, expansion four; unfused stage)", "bound": "mfma",
             "ms": t * 1e3, "achieved": flops / t / 1e12, "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "flop_per_launch": flops,
             "frac": flops / t / 1e12 / PEAK_BF16_TFLOPS}
