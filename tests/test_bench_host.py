@@ -67,7 +67,7 @@ def test_committed_counters_are_current():
     """The committed counters of the roofline kernel match its source, so the
     bench line carries them. After a change to the kernel they are stale
     until retaken on a GPU: the test then skips and says so."""
-    key = "k_transition_ws:high_variation_x4"
+    key = f"k_transition_ws:{bench.HEADLINE}"
     c = bench.counters_for(key)
     if not c:
         pytest.skip("counters in profiles/traffic.json were taken on another kernel source")
