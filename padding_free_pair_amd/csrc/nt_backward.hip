@@ -52,7 +52,12 @@ __global__ __launch_bounds__(kThreads) void k_mean_backward(
 // Column adjoint of the broadcast: g_b[mu_i + c] = sum_r g_z[o_i + r M_i + c].
 // A pair row of sample i is M_i c_z contiguous floats, and float4 q of it is
 // float4 q of g_b's block for the sample, so each thread sums one float4
-// position down the sample's N_i rows, in row order.
+// position down the sample's N_i rows, in row order. A column is a long
+// dependent walk and there are few of them, so each thread keeps
+// kColUnroll rows' loads in flight (with four, the whole grid held about
+// 4 MB in flight and read at about 3 TB/s).
+constexpr int kColUnroll = 16;
+
 __global__ __launch_bounds__(kThreads) void k_col_sums(
     const float* __restrict__ g_z, float* __restrict__ g_b,
     const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ col_offsets,
@@ -69,12 +74,13 @@ __global__ __launch_bounds__(kThreads) void k_col_sums(
     const float* src = base + 4 * q;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     int64_t r = 0;
-    for (; r + 4 <= N; r += 4) {
-      f32x4 v[4];
+    for (; r + kColUnroll <= N; r += kColUnroll) {
+      f32x4 v[kColUnroll];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4*>(src + (r + u) * step);
+      for (int u = 0; u < kColUnroll; ++u)
+        v[u] = *reinterpret_cast<const f32x4*>(src + (r + u) * step);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < kColUnroll; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] += v[u][e];
     }
@@ -344,10 +350,10 @@ hipError_t launch_mean_backward(const nt_partition& p, const float* g_m, const f
 hipError_t launch_col_sums(const nt_partition& p, const float* g_z, float* g_b, int c_z,
                            hipStream_t s) {
   if (p.T_cols == 0 || p.B == 0) return hipSuccess;
-  // a workgroup covers 256 float4s of a row; samples take at most 64 of them
+  // a workgroup covers 256 float4s of a row; samples take at most 128 of them
   const int64_t widest = (p.col_offsets == p.single_offsets ? (int64_t)p.n_max : p.T_cols);
   int64_t per = (widest * c_z / 4 + kThreads - 1) / kThreads;
-  per = per < 1 ? 1 : (per > 64 ? 64 : per);
+  per = per < 1 ? 1 : (per > 128 ? 128 : per);
   hipLaunchKernelGGL(k_col_sums, dim3((unsigned)(p.B * per)), dim3(kThreads), 0, s, g_z, g_b,
                      p.pair_offsets, p.col_offsets, p.lengths, p.col_lengths, (int)per, c_z);
   return hipGetLastError();

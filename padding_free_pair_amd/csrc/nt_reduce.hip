@@ -15,15 +15,27 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 4;
 
-template <typename T>
-__device__ __forceinline__ void accumulate(float (&acc)[Vec16<T>::N], const T* p) {
-  const Vec16<T> v = load16(p);
-#pragma unroll
-  for (int e = 0; e < Vec16<T>::N; ++e) acc[e] += v.get(e);
+// The last-level cache (MALL) of one MI355X. A pair state larger than this
+// cannot still be cached from the kernel that wrote it, so it is read with
+// nontemporal loads, which do not allocate in the caches: on long_square_x4
+// (459.5 MB) the column mean then takes 68.5 us instead of 80.6 us; on a
+// pair state that fits (near_uniform_x4, 242 MB) cached loads are 5% faster.
+constexpr int64_t kStreamBytes = int64_t(256) << 20;
+
+// 16 bytes at p; STREAM: a nontemporal load
+template <typename T, bool STREAM>
+__device__ __forceinline__ Vec16<T> load_row16(const T* p) {
+  if constexpr (STREAM) {
+    Vec16<T> r;
+    r.v = __builtin_nontemporal_load(reinterpret_cast<const decltype(r.v)*>(p));
+    return r;
+  } else {
+    return load16(p);
+  }
 }
 
 // Sum of the 16-byte vectors at cells c0, c0 + step, ... < n of one pair row.
-template <typename T>
+template <typename T, bool STREAM>
 __device__ __forceinline__ void row_partial(float (&acc)[Vec16<T>::N], const T* row_base,
                                             int64_t c0, int64_t n, int64_t step, int c_z) {
   constexpr int VEC = Vec16<T>::N;
@@ -33,19 +45,23 @@ __device__ __forceinline__ void row_partial(float (&acc)[Vec16<T>::N], const T* 
   for (; c + (kUnroll - 1) * step < n; c += kUnroll * step) {
     Vec16<T> v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = load16(row_base + (c + u * step) * c_z);
+    for (int u = 0; u < kUnroll; ++u) v[u] = load_row16<T, STREAM>(row_base + (c + u * step) * c_z);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
       for (int e = 0; e < VEC; ++e) acc[e] += v[u].get(e);
   }
-  for (; c < n; c += step) accumulate<T>(acc, row_base + c * c_z);
+  for (; c < n; c += step) {
+    const Vec16<T> v = load_row16<T, STREAM>(row_base + c * c_z);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] += v.get(e);
+  }
 }
 
 // G = c_z / VEC feature vectors per cell, a power of two <= 64: lane (f, cl)
 // of a wave holds vector f of every (64/G)-th cell; a butterfly over the
 // cell-lane bits sums the lanes that share f.
-template <typename T, int G>
+template <typename T, int G, bool STREAM>
 __global__ __launch_bounds__(kThreads) void k_reduce_pow2(
     const T* __restrict__ z, float* __restrict__ m, const int64_t* __restrict__ item_offsets,
     const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
@@ -70,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_pow2(
     // one row, every wave takes a share of its cells
     const int64_t r = j;
     const T* base = z + (o + r * n) * c_z + f * VEC;
-    row_partial<T>(acc, base, wave * CLW + cl, n, kWaves * CLW, c_z);
+    row_partial<T, STREAM>(acc, base, wave * CLW + cl, n, kWaves * CLW, c_z);
 #pragma unroll
     for (int off = G; off < 64; off <<= 1)
 #pragma unroll
@@ -100,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_pow2(
     const int64_t r1 = r0 + R < rows ? r0 + R : rows;
     for (int64_t r = r0 + wave; r < r1; r += kWaves) {
       const T* base = z + (o + r * n) * c_z + f * VEC;
-      row_partial<T>(acc, base, cl, n, CLW, c_z);
+      row_partial<T, STREAM>(acc, base, cl, n, CLW, c_z);
 #pragma unroll
       for (int off = G; off < 64; off <<= 1)
 #pragma unroll
@@ -134,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_generic(
   const int64_t n = col_lengths[row_sample[g]];
   const float nf = mean ? (float)n : 1.f;
   float acc[VEC];
-  row_partial<T>(acc, z + row_splits[g] * c_z + f * VEC, 0, n, 1, c_z);
+  row_partial<T, false>(acc, z + row_splits[g] * c_z + f * VEC, 0, n, 1, c_z);
   float* dst = m + g * c_z + f * VEC;
 #pragma unroll
   for (int q = 0; q < VEC / 4; ++q) {
@@ -148,7 +164,9 @@ __global__ __launch_bounds__(kThreads) void k_reduce_generic(
 template <typename T, int G>
 hipError_t launch_pow2(const nt_partition& p, const void* z, float* m, int c_z, bool mean,
                        hipStream_t stream) {
-  hipLaunchKernelGGL((k_reduce_pow2<T, G>), dim3((unsigned)p.n_items), dim3(kThreads), 0, stream,
+  const bool stream_z = p.cells * c_z * (int64_t)sizeof(T) > kStreamBytes;
+  auto kern = stream_z ? k_reduce_pow2<T, G, true> : k_reduce_pow2<T, G, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.n_items), dim3(kThreads), 0, stream,
                      static_cast<const T*>(z), m, p.item_offsets, p.pair_offsets,
                      p.single_offsets, p.lengths, p.col_lengths, p.B, c_z, mean);
   return hipGetLastError();
