@@ -55,9 +55,18 @@ __global__ __launch_bounds__(kThreads) void k_mean_backward(
 // position down the sample's N_i rows, in row order. A column is a long
 // dependent walk and there are few of them, so each thread keeps
 // kColUnroll rows' loads in flight (with four, the whole grid held about
-// 4 MB in flight and read at about 3 TB/s).
+// 4 MB in flight and read at about 3 TB/s). STREAM: nontemporal loads, for
+// a g_z above the last-level cache (long_square_x4: row and column sums
+// 301 -> 287 us; on high_variation_x4's 208 MB, which fits, 10% slower).
 constexpr int kColUnroll = 16;
 
+template <bool STREAM>
+__device__ __forceinline__ f32x4 load_col4(const float* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return *reinterpret_cast<const f32x4*>(p);
+}
+
+template <bool STREAM>
 __global__ __launch_bounds__(kThreads) void k_col_sums(
     const float* __restrict__ g_z, float* __restrict__ g_b,
     const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ col_offsets,
@@ -78,14 +87,14 @@ __global__ __launch_bounds__(kThreads) void k_col_sums(
       f32x4 v[kColUnroll];
 #pragma unroll
       for (int u = 0; u < kColUnroll; ++u)
-        v[u] = *reinterpret_cast<const f32x4*>(src + (r + u) * step);
+        v[u] = load_col4<STREAM>(src + (r + u) * step);
 #pragma unroll
       for (int u = 0; u < kColUnroll; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] += v[u][e];
     }
     for (; r < N; ++r) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src + r * step);
+      const f32x4 v = load_col4<STREAM>(src + r * step);
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] += v[e];
     }
@@ -111,6 +120,8 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
+constexpr int kLossUnroll = 4;
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_loss_rows(
     const T* __restrict__ x, int c_s, const T* __restrict__ pz, int c_z,
@@ -133,9 +144,11 @@ __global__ __launch_bounds__(kThreads) void k_loss_rows(
         if (g_x) g_x[r * c_s + f + e] = gxs * xv;
       }
     }
+    // the pair row's vectors, kLossUnroll loads in flight per thread; each
+    // thread still adds its squares in element order
     const int64_t e0 = row_splits[r] * c_z, e1 = row_splits[r + 1] * c_z;
-    for (int64_t e = e0 + (int64_t)threadIdx.x * VEC; e < e1; e += kThreads * VEC) {
-      const Vec16<T> v = load16(pz + e);
+    constexpr int64_t step = (int64_t)kThreads * VEC;
+    auto use = [&](const Vec16<T>& v, int64_t e) {
       float g[VEC];
 #pragma unroll
       for (int k = 0; k < VEC; ++k) {
@@ -148,7 +161,16 @@ __global__ __launch_bounds__(kThreads) void k_loss_rows(
         for (int k = 0; k < VEC; k += 4)
           *reinterpret_cast<f32x4*>(g_pz + e + k) = f32x4{g[k], g[k + 1], g[k + 2], g[k + 3]};
       }
+    };
+    int64_t e = e0 + (int64_t)threadIdx.x * VEC;
+    for (; e + (kLossUnroll - 1) * step < e1; e += kLossUnroll * step) {
+      Vec16<T> v[kLossUnroll];
+#pragma unroll
+      for (int u = 0; u < kLossUnroll; ++u) v[u] = load16(pz + e + u * step);
+#pragma unroll
+      for (int u = 0; u < kLossUnroll; ++u) use(v[u], e + u * step);
     }
+    for (; e < e1; e += step) use(load16(pz + e), e);
     sx = block_sum(sx, red);
     sp = block_sum(sp, red);
     if (threadIdx.x == 0) partial[r] = alpha * (double)sx * inv_d1 + beta * (double)sp * inv_d2;
@@ -354,7 +376,9 @@ hipError_t launch_col_sums(const nt_partition& p, const float* g_z, float* g_b, 
   const int64_t widest = (p.col_offsets == p.single_offsets ? (int64_t)p.n_max : p.T_cols);
   int64_t per = (widest * c_z / 4 + kThreads - 1) / kThreads;
   per = per < 1 ? 1 : (per > 128 ? 128 : per);
-  hipLaunchKernelGGL(k_col_sums, dim3((unsigned)(p.B * per)), dim3(kThreads), 0, s, g_z, g_b,
+  const bool stream_g = p.cells * c_z * (int64_t)sizeof(float) > kStreamBytes;
+  hipLaunchKernelGGL(stream_g ? k_col_sums<true> : k_col_sums<false>, dim3((unsigned)(p.B * per)),
+                     dim3(kThreads), 0, s, g_z, g_b,
                      p.pair_offsets, p.col_offsets, p.lengths, p.col_lengths, (int)per, c_z);
   return hipGetLastError();
 }

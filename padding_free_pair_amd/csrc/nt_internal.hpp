@@ -40,6 +40,11 @@ __host__ __device__ inline int64_t items_of(int64_t n, int64_t m) {
   return (n + r - 1) / r;
 }
 
+// The last-level cache (MALL) of one MI355X. An array larger than this that
+// one kernel writes and the next reads once cannot still be cached, so the
+// reading kernel streams it with nontemporal loads, which do not allocate.
+constexpr int64_t kStreamBytes = int64_t(256) << 20;
+
 // Cells per entry of the tile_sample execution index.
 constexpr int64_t kSampleIndexSpan = 256;
 inline int64_t sample_index_entries(int64_t cells) {

@@ -15,12 +15,10 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 4;
 
-// The last-level cache (MALL) of one MI355X. A pair state larger than this
-// cannot still be cached from the kernel that wrote it, so it is read with
-// nontemporal loads, which do not allocate in the caches: on long_square_x4
-// (459.5 MB) the column mean then takes 68.5 us instead of 80.6 us; on a
-// pair state that fits (near_uniform_x4, 242 MB) cached loads are 5% faster.
-constexpr int64_t kStreamBytes = int64_t(256) << 20;
+// A pair state above kStreamBytes is read with nontemporal loads: on
+// long_square_x4 (459.5 MB) the column mean then takes 68.5 us instead of
+// 80.6 us; on a pair state that fits the cache (near_uniform_x4, 242 MB)
+// cached loads are 5% faster.
 
 // 16 bytes at p; STREAM: a nontemporal load
 template <typename T, bool STREAM>
