@@ -493,6 +493,31 @@ def swiglu_roofline(r: PackedRunner, reps: int) -> dict:
             "frac": flops / t / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def swiglu_block(r: PackedRunner, reps: int) -> dict:
+    """The paper's own block end to end (Equation 1 with h o LN; App. A.1):
+    nt_pair_block_ex with the pre-normalised SwiGLU transition on the
+    workload's singles, seeded SwiGLU-block weights of its widths. One
+    block: projections, the fused broadcast + LN + SwiGLU + residual
+    (k_swiglu32), the column mean and the output projection. `frac` counts
+    only the transition's 6 c_z h flop per cell against the whole block's
+    time, a lower bound of the fused kernel's own fraction."""
+    torch, nt, x = r.torch, r.nt, r.x
+    w = pin.draw_swiglu_weights(np.random.default_rng(77), x.c_s, x.c_z, x.hidden, x.dtype)
+    params = {k: dev(v, torch) for k, v in w.items()}
+    s_out = torch.empty_like(r.s0)
+    z_out = torch.empty_like(r.z)
+    ws = torch.empty(max(nt.nt_block_workspace_bytes(r.p, x.c_s, x.c_z, x.hidden, torch.bfloat16),
+                         1), dtype=torch.uint8, device="cuda")
+    t = time_kernel(lambda: nt.nt_pair_block_ex(r.p, r.s0, params, s_out=s_out, z_out=z_out,
+                                                workspace=ws), reps, torch)
+    flops = 6.0 * x.c_z * x.hidden * r.cells
+    return {"kernel": "nt_pair_block_ex, SwiGLU kind (k_swiglu32 fused, with the block's "
+                      "projections and column mean)", "bound": "mfma",
+            "ms": t * 1e3, "cells_per_s": r.cells / t, "achieved": flops / t / 1e12,
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "flop_per_launch": flops,
+            "frac": flops / t / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def counters_for(kernel_key: str) -> dict:
     """The committed rocprofv3 counter results of a kernel (HBM bytes per
     launch, matrix-pipe busy fraction), if they were taken on the current
@@ -800,6 +825,11 @@ def main():
         v = kern["swiglu_transition"]
         log(f"kernel swiglu_transition: {v['ms'] * 1e3:.1f} us, {v['achieved']:.1f} TFLOP/s "
             f"({100 * v['frac']:.1f}% of peak)")
+        if x.c_z == 128 and x.hidden % 64 == 0:
+            kern["swiglu_block"] = swiglu_block(r, args.kernel_reps)
+            v = kern["swiglu_block"]
+            log(f"swiglu block (paper's transition, fused): {v['ms'] * 1e3:.1f} us per block, "
+                f"{v['cells_per_s']:.4g} cells/s; transition flop {100 * v['frac']:.1f}% of peak")
     if x.dtype == "bf16":
         kern["transition_backward"] = backward_rooflines(r, max(10, args.kernel_reps // 5))
         v = kern["transition_backward"]
