@@ -8,7 +8,8 @@
 // nt_wgrad.hip (k_wgrad_rc recomputes H and g_H from z and bf16(G)).
 //
 // Persistent kernel, bf16, c_z = 128, hidden a multiple of 32. A workgroup
-// of four waves takes 256 cells at a time (64 per wave, two 32-cell blocks).
+// of eight waves (two per SIMD) takes 256 cells at a time, 32 per wave (one
+// 32-cell column block, kBwCB).
 // Per 32-unit hidden chunk j, three products run on v_mfma_f32_32x32x16_bf16
 // with the cells as the N dimension:
 //   pre^T (32 x cells) = W1[j]   . z^T        (k = features)
