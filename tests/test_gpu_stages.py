@@ -371,6 +371,26 @@ def test_swiglu_transition_parity(nt, lengths, c_z, hidden):
     assert err <= TOL["bf16"], err
 
 
+@pytest.mark.parametrize("hidden", [128, 192, 1024])
+def test_swiglu_transition_ring_phases(nt, hidden):
+    """The persistent 32x32 kernel at 4, 6 and 32 hidden chunks: its
+    three-buffer weight ring meets a tile boundary at every phase (the chunk
+    count mod 3), and 301 tiles of 256 cells give some workgroups a second
+    tile, others one."""
+    lengths, c_z = [256, 100, 37], 128
+    announce(f"swiglu transition ring phases hidden={hidden} cells={sum(n * n for n in lengths)}")
+    z = pin.random_pair_rows(lengths, c_z, "bf16", seed=61)
+    params = _swiglu_params(c_z, hidden, seed=62)
+    p = nt.nt_make_partition(lengths)
+    full, out = _guarded(p.cells, c_z, torch.bfloat16)
+    nt.nt_pair_transition_swiglu(p, to_dev(z, torch), *_swiglu_dev(params), z_out=out)
+    torch.cuda.synchronize()
+    _check_guard(full, 64, p.cells)
+    err = scaled_max_err(f64(out, torch), _swiglu_ref(z.f64, params))
+    announce(f"error {err:.3e}")
+    assert err <= TOL["bf16"], err
+
+
 def test_swiglu_transition_in_place_and_eps(nt):
     lengths, c_z, hidden = [21, 9, 30], 128, 512
     announce("swiglu transition in place, eps 1e-3")

@@ -52,6 +52,22 @@ def test_swiglu_block_matches_oracle(nt, lengths, c_s, c_z, hidden):
     assert scaled_max_err(f64(s_out, torch), rs) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("hidden", [192, 1024])
+def test_swiglu_block_ring_phases(nt, hidden):
+    """The fused kernel at 6 and 32 hidden chunks over 301 tiles of 256
+    cells: the weight ring meets tile boundaries at other phases than at 16
+    chunks, and some workgroups take a second tile."""
+    lengths, c_s, c_z = [256, 100, 37], 64, 128
+    announce(f"swiglu block ring phases hidden={hidden}")
+    x = pin.make_swiglu_inputs(lengths, c_s, c_z, hidden, "bf16", seed=12)
+    p = nt.nt_make_partition(lengths)
+    s_out, z_out = nt.nt_pair_block_ex(p, to_dev(x.s, torch), weights_to_dev(x.weights[0], torch))
+    torch.cuda.synchronize()
+    rs, rz = oracle.block_swiglu(lengths, x.s.f64, _w64(x.weights[0]))
+    assert scaled_max_err(f64(z_out, torch), rz) <= TOL["bf16"]
+    assert scaled_max_err(f64(s_out, torch), rs) <= TOL["bf16"]
+
+
 def test_swiglu_block_eps_and_many_samples(nt):
     """300 samples (two-launch partition, cells decoded over many samples per
     tile) and a larger LN epsilon."""
