@@ -281,10 +281,10 @@ nt_status check_params(const nt_block_params* w, int32_t c_s, int32_t c_z, int32
 }
 
 // The transition of a block over its pair state: fused (z = a[row] + b[col]
-// formed on chip) for S = 1, and for S slices per cell where the
-// weight-stationary kernel takes the shape; else the broadcast over rows of
-// S slices followed by the cell-local transition in place over cells * S
-// rows.
+// formed on chip) for S = 1, either kind, and for S slices per cell (ReLU)
+// where the weight-stationary kernel takes the shape; else the broadcast
+// over rows of S slices followed by the cell-local transition in place over
+// cells * S rows.
 nt_status block_transition(const nt_partition& p, const nt_block_params& w, const void* a,
                            const void* b, void* z_out, int32_t c_z, int32_t hidden,
                            nt_dtype dtype, int32_t S, hipStream_t s) {
@@ -299,17 +299,13 @@ nt_status block_transition(const nt_partition& p, const nt_block_params& w, cons
                                             dtype, s),
                       "fused broadcast + transition");
   }
-  if (!swiglu && nt::transition_ws_slices_supported(p, c_z, hidden, dtype, S))
+  // S > 1: the non-leading layout, ReLU MLP only (checked by pair_block)
+  if (nt::transition_ws_slices_supported(p, c_z, hidden, dtype, S))
     return hip_status(nt::launch_transition_ws(p, a, b, z_out, w.W1, w.W2, nt::device_cu_count(),
                                                s, S),
                       "fused broadcast + transition over slices");
   NT_TRY(hip_status(nt::launch_broadcast(p, a, b, z_out, S * c_z, dtype, s, true), "broadcast"));
   const nt_partition v = rows_view(p, S);
-  if (swiglu)
-    return hip_status(nt::launch_transition_swiglu(v, z_out, nullptr, nullptr, z_out, w.ln_gamma,
-                                                   w.ln_beta, w.W_gate, w.W_up, w.W_down, c_z,
-                                                   hidden, w.ln_eps, s),
-                      "SwiGLU transition");
   return hip_status(nt::launch_transition(v, z_out, nullptr, nullptr, z_out, w.W1, w.W2, c_z,
                                           hidden, dtype, s),
                     "transition");
@@ -329,6 +325,8 @@ nt_status pair_block(const nt_partition* p, const void* s_rows, const void* s_co
   NT_TRY(check_static_axis(S, c_z));
   ParamArrays pa;
   NT_TRY(check_params(w, c_s, c_z, hidden, dtype, &pa));
+  if (w->kind == NT_TRANSITION_LN_SWIGLU && S != 1)
+    return fail(NT_ERR_INVALID, "the SwiGLU block takes the leading layout (S = 1)");
   const size_t es = esize(dtype);
   const uint64_t sbytes = (uint64_t)p->T * S * c_s * es;
   const uint64_t cbytes = (uint64_t)p->T_cols * S * c_s * es;
