@@ -158,6 +158,24 @@ def test_swiglu_chain_full_size_per_block(nt):
         s = s_next
 
 
+def test_swiglu_block_full_size_long_square(nt):
+    """One SwiGLU block at the long-square workload's lengths and widths
+    (1,795,072 cells; 7,012 tiles over the persistent grid): every cell and
+    single row against the oracle."""
+    w = pin.workload("long_square_x4")
+    L = pin.workload_inputs(w.index).lengths.tolist()
+    announce(f"swiglu block full size {w.name}")
+    x = pin.make_swiglu_inputs(L, w.c_s, w.c_z, w.hidden, "bf16", blocks=1, seed=13)
+    p = nt.nt_make_partition(L)
+    s_out, z_out = nt.nt_pair_block_ex(p, to_dev(x.s, torch), weights_to_dev(x.weights[0], torch))
+    torch.cuda.synchronize()
+    rs, rz = oracle.block_swiglu(L, x.s.f64, _w64(x.weights[0]))
+    ez = scaled_max_err(f64(z_out, torch), rz)
+    es = scaled_max_err(f64(s_out, torch), rs)
+    announce(f"errors z={ez:.3e} s={es:.3e}")
+    assert ez <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("lengths,c_s,c_z,hidden,with_gz", [
     ([7, 0, 12, 1, 5], 64, 128, 512, True),
     ([9, 20, 13], 384, 128, 512, False),     # the pages' widths
