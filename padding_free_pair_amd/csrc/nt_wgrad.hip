@@ -125,16 +125,26 @@ __global__ __launch_bounds__(kWgThreads) void k_wgrad(const bf16* __restrict__ A
 // lane holds a unit and 16 cells, so the packed g_H and H are already the
 // MFMA operands of the contractions over cells (k-step s takes result
 // elements 8 s .. 8 s + 7, cells 16 s + 8 (e / 4) + 4 h + e % 4); the other
-// operand, z or bf16(G) with a feature per lane, is read from an LDS copy in
-// [feature][cell] layout as two 8-byte runs per fragment. Each block is
-// staged in LDS twice (row-major for the first two products, transposed for
-// the contractions); the next block's rows are loaded into registers while
-// the current block's products run and are written after them. Each wave
+// operand, z or bf16(G) with a feature per lane, is read from the same
+// row-major LDS copy with gfx950's transposing read (ds_read_b64_tr_b16:
+// within each 16 lanes, lane j's element e is element j mod 4 of the 8 bytes
+// at the address of lane 4 e + j / 4), two reads per fragment. The next
+// block's rows are loaded into registers while the current block's products
+// run and are written after them. Each wave
 // writes its chunk's partial dW1 rows and dW2 columns for the slice; the
 // slices are added in order afterwards.
 constexpr int kRcCells = 64;              // cells per block (two 32-cell halves)
-constexpr int kRcPitch = kRcCells + 4;   // [feature][cell] pitch in elements (136 bytes)
 constexpr int kRcRow = 128 + 8;          // [cell][feature] pitch in elements (272 bytes)
+
+typedef short rc_i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 rc_bf16x4 __attribute__((ext_vector_type(4)));
+
+// Four bf16 by the transposing LDS read; p is this lane's 8-byte address.
+__device__ __forceinline__ rc_bf16x4 rc_read_tr(const bf16* p) {
+  const rc_i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) rc_i16x4*)(p));
+  return __builtin_bit_cast(rc_bf16x4, v);
+}
 
 template <int CZ, int HID>
 __global__ __launch_bounds__(256, 1) void k_wgrad_rc(
@@ -144,7 +154,6 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_rc(
   constexpr int KT = CZ / 16, FB = CZ / 32, GROUPS = HID / 128;
   static_assert(CZ == 128, "row staging assumes 128 features");
   // [buffer][operand: 0 z, 1 G]
-  __shared__ bf16 tr[2][2][CZ * kRcPitch];
   __shared__ bf16 rm[2][2][kRcCells * kRcRow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
@@ -171,8 +180,7 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_rc(
   }
 
   // staging: thread -> operand (tid < 128: z, else G), cells 2 cp and 2 cp + 1,
-  // 16-byte pieces sp0 .. sp0 + 3 of each; the transposed copy is written a
-  // 4-byte word (two adjacent cells of one feature) at a time
+  // 16-byte pieces sp0 .. sp0 + 3 of each
   const int op = tid >> 7, st = tid & 127, cp = st >> 2, sp0 = 4 * (st & 3);
   const bf16* ssrc = op == 0 ? z : Gb;
   bf16x8 nxt[2][4];  // [cell of the pair][piece]
@@ -187,24 +195,18 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_rc(
     }
   };
   auto write_rows = [&](int buf) {
-    bf16* T = tr[buf][op];
     bf16* R = rm[buf][op];
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int f0 = 8 * (sp0 + q);
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        *reinterpret_cast<bf16x8*>(R + (2 * cp + u) * kRcRow + f0) = nxt[u][q];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16x2 w;
-        w[0] = nxt[0][q][e];
-        w[1] = nxt[1][q][e];
-        *reinterpret_cast<bf16x2*>(T + (f0 + e) * kRcPitch + 2 * cp) = w;
-      }
-    }
+        *reinterpret_cast<bf16x8*>(R + (2 * cp + u) * kRcRow + 8 * (sp0 + q)) = nxt[u][q];
   };
+  // this lane's transposing-read address in a 32-cell half: within its
+  // 16-lane group (features 32 f + 16 (g mod 2) .., cells 4 h ..), lane l'
+  // points at cell 4 h + l' / 4, features + 4 (l' mod 4)
+  const int lq = lane & 15, lg = lane >> 4;
+  const int tr_off = (4 * h + (lq >> 2)) * kRcRow + 16 * (lg & 1) + 4 * (lq & 3);
 
   int buf = 0;
   if (cb0 < cb1) {
@@ -217,8 +219,6 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_rc(
     if (more) load_rows(c0 + kRcCells);  // in flight during this block's products
     const bf16* Rz = rm[buf][0];
     const bf16* Rg = rm[buf][1];
-    const bf16* Z = tr[buf][0];
-    const bf16* Gt = tr[buf][1];
     f32x16 pre[2], gh[2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -250,12 +250,12 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_rc(
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int f = 0; f < FB; ++f) {
-          const int row = (32 * f + l32) * kRcPitch + 32 * hb + 16 * s + 4 * h;
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          const bf16x4 z0 = *reinterpret_cast<const bf16x4*>(Z + row);
-          const bf16x4 z1 = *reinterpret_cast<const bf16x4*>(Z + row + 8);
-          const bf16x4 g0 = *reinterpret_cast<const bf16x4*>(Gt + row);
-          const bf16x4 g1 = *reinterpret_cast<const bf16x4*>(Gt + row + 8);
+          // cells 32 hb + 16 s + 4 h + (0..3) and + 8, feature 32 f + l32
+          const int off = tr_off + (32 * hb + 16 * s) * kRcRow + 32 * f;
+          const rc_bf16x4 z0 = rc_read_tr(Rz + off);
+          const rc_bf16x4 z1 = rc_read_tr(Rz + off + 8 * kRcRow);
+          const rc_bf16x4 g0 = rc_read_tr(Rg + off);
+          const rc_bf16x4 g1 = rc_read_tr(Rg + off + 8 * kRcRow);
           bf16x8 zf, gf;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
