@@ -33,6 +33,8 @@ constexpr int kBwCB = 1;                          // 32-cell blocks per wave
 constexpr int kBwWaves = 8;
 constexpr int kBwThreads = kBwWaves * 64;
 constexpr int kBwTileCells = kBwWaves * 32 * kBwCB;
+// s_waitcnt immediate (gfx9 encoding): every vector-memory load has completed
+constexpr int kBwWaitVm0 = 0x0F70;
 
 __device__ __forceinline__ f32x16 bw_mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -176,6 +178,13 @@ __global__ __launch_bounds__(kBwThreads, 2) void k_transition_bwd(
         }
       }
     }
+
+    // The tile's z and G have landed before the chunk loop. Without this wait
+    // the compiler's count at the loop header merges the prologue's pending
+    // loads with the loop's own, and it waits on vmcnt before the products
+    // of every chunk, which then also waits for the weight loads issued at
+    // the chunk's start for two chunks ahead.
+    __builtin_amdgcn_s_waitcnt(kBwWaitVm0);
 
     // chunk j reads buffer j % 2; `nxt` holds chunk j + 1, `fill` receives
     // chunk j + 2 (chunks wrap into the next tile's: the weights repeat)
