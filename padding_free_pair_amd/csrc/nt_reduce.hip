@@ -56,15 +56,17 @@ __device__ __forceinline__ void row_partial(float (&acc)[Vec16<T>::N], const T* 
   }
 }
 
-// G = c_z / VEC feature vectors per cell, a power of two <= 64: lane (f, cl)
-// of a wave holds vector f of every (64/G)-th cell; a butterfly over the
-// cell-lane bits sums the lanes that share f.
+// A cell's c_z values are sl slices of G feature vectors (G a power of two
+// <= 64; sl = 1 unless c_z / VEC is not one, as for the S slices of the
+// non-leading layout). Lane (f, cl) of a wave holds vector f of a slice of
+// every (64/G)-th cell; a butterfly over the cell-lane bits sums the lanes
+// that share f. The slices of a row are summed one after another.
 template <typename T, int G, bool STREAM>
 __global__ __launch_bounds__(kThreads) void k_reduce_pow2(
     const T* __restrict__ z, float* __restrict__ m, const int64_t* __restrict__ item_offsets,
     const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
     const int32_t* __restrict__ lengths, const int32_t* __restrict__ col_lengths, int B,
-    int c_z, bool mean) {
+    int c_z, int sl, bool mean) {
   constexpr int VEC = Vec16<T>::N;
   constexpr int CLW = 64 / G;
   __shared__ float part[kWaves][G * VEC];
@@ -83,29 +85,33 @@ __global__ __launch_bounds__(kThreads) void k_reduce_pow2(
   if (n >= kLongRow) {
     // one row, every wave takes a share of its cells
     const int64_t r = j;
-    const T* base = z + (o + r * n) * c_z + f * VEC;
-    row_partial<T, STREAM>(acc, base, wave * CLW + cl, n, kWaves * CLW, c_z);
+    for (int sc = 0; sc < sl; ++sc) {
+      const int fo = (sc * G + f) * VEC;  // the lane's first value in the cell
+      row_partial<T, STREAM>(acc, z + (o + r * n) * c_z + fo, wave * CLW + cl, n, kWaves * CLW,
+                             c_z);
 #pragma unroll
-    for (int off = G; off < 64; off <<= 1)
+      for (int off = G; off < 64; off <<= 1)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
-    if (cl == 0) {
+        for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
+      if (cl == 0) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) part[wave][f * VEC + e] = acc[e];
-    }
-    __syncthreads();
-    if (wave == 0 && cl == 0) {
-      Vec16<float> out[VEC / 4];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        float s = part[0][f * VEC + e];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) s += part[w][f * VEC + e];
-        out[e / 4].set(e % 4, s / nf);
+        for (int e = 0; e < VEC; ++e) part[wave][f * VEC + e] = acc[e];
       }
-      float* dst = m + (eta + r) * c_z + f * VEC;
+      __syncthreads();
+      if (wave == 0 && cl == 0) {
+        Vec16<float> out[VEC / 4];
 #pragma unroll
-      for (int q = 0; q < VEC / 4; ++q) store16(dst + 4 * q, out[q]);
+        for (int e = 0; e < VEC; ++e) {
+          float s = part[0][f * VEC + e];
+#pragma unroll
+          for (int w = 1; w < kWaves; ++w) s += part[w][f * VEC + e];
+          out[e / 4].set(e % 4, s / nf);
+        }
+        float* dst = m + (eta + r) * c_z + fo;
+#pragma unroll
+        for (int q = 0; q < VEC / 4; ++q) store16(dst + 4 * q, out[q]);
+      }
+      __syncthreads();  // part is written again for the next slice
     }
   } else {
     // a group of whole rows; each wave reduces its own rows
@@ -113,20 +119,22 @@ __global__ __launch_bounds__(kThreads) void k_reduce_pow2(
     const int64_t r0 = j * R;
     const int64_t r1 = r0 + R < rows ? r0 + R : rows;
     for (int64_t r = r0 + wave; r < r1; r += kWaves) {
-      const T* base = z + (o + r * n) * c_z + f * VEC;
-      row_partial<T, STREAM>(acc, base, cl, n, CLW, c_z);
+      for (int sc = 0; sc < sl; ++sc) {
+        const int fo = (sc * G + f) * VEC;
+        row_partial<T, STREAM>(acc, z + (o + r * n) * c_z + fo, cl, n, CLW, c_z);
 #pragma unroll
-      for (int off = G; off < 64; off <<= 1)
+        for (int off = G; off < 64; off <<= 1)
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
-      if (cl == 0) {
-        float* dst = m + (eta + r) * c_z + f * VEC;
+          for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
+        if (cl == 0) {
+          float* dst = m + (eta + r) * c_z + fo;
 #pragma unroll
-        for (int q = 0; q < VEC / 4; ++q) {
-          Vec16<float> out;
+          for (int q = 0; q < VEC / 4; ++q) {
+            Vec16<float> out;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) out.set(e, acc[4 * q + e] / nf);
-          store16(dst + 4 * q, out);
+            for (int e = 0; e < 4; ++e) out.set(e, acc[4 * q + e] / nf);
+            store16(dst + 4 * q, out);
+          }
         }
       }
     }
@@ -160,34 +168,44 @@ __global__ __launch_bounds__(kThreads) void k_reduce_generic(
 }
 
 template <typename T, int G>
-hipError_t launch_pow2(const nt_partition& p, const void* z, float* m, int c_z, bool mean,
-                       hipStream_t stream) {
+hipError_t launch_pow2(const nt_partition& p, const void* z, float* m, int c_z, int sl,
+                       bool mean, hipStream_t stream) {
   const bool stream_z = p.cells * c_z * (int64_t)sizeof(T) > kStreamBytes;
   auto kern = stream_z ? k_reduce_pow2<T, G, true> : k_reduce_pow2<T, G, false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)p.n_items), dim3(kThreads), 0, stream,
                      static_cast<const T*>(z), m, p.item_offsets, p.pair_offsets,
-                     p.single_offsets, p.lengths, p.col_lengths, p.B, c_z, mean);
+                     p.single_offsets, p.lengths, p.col_lengths, p.B, c_z, sl, mean);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_t(const nt_partition& p, const void* z, float* m, int c_z, bool mean,
                     hipStream_t stream) {
-  const int G = c_z / Vec16<T>::N;
-  switch (G) {
-    case 1: return launch_pow2<T, 1>(p, z, m, c_z, mean, stream);
-    case 2: return launch_pow2<T, 2>(p, z, m, c_z, mean, stream);
-    case 4: return launch_pow2<T, 4>(p, z, m, c_z, mean, stream);
-    case 8: return launch_pow2<T, 8>(p, z, m, c_z, mean, stream);
-    case 16: return launch_pow2<T, 16>(p, z, m, c_z, mean, stream);
-    case 32: return launch_pow2<T, 32>(p, z, m, c_z, mean, stream);
-    case 64: return launch_pow2<T, 64>(p, z, m, c_z, mean, stream);
+  const int vecs = c_z / Vec16<T>::N;  // feature vectors per cell
+  // the slices: the largest power of two <= 64 that divides vecs, at least 4
+  int G = 64;
+  while (G > 4 && vecs % G != 0) G >>= 1;
+  if (vecs % G == 0) {
+    const int sl = vecs / G;
+    switch (G) {
+      case 4: return launch_pow2<T, 4>(p, z, m, c_z, sl, mean, stream);
+      case 8: return launch_pow2<T, 8>(p, z, m, c_z, sl, mean, stream);
+      case 16: return launch_pow2<T, 16>(p, z, m, c_z, sl, mean, stream);
+      case 32: return launch_pow2<T, 32>(p, z, m, c_z, sl, mean, stream);
+      case 64: return launch_pow2<T, 64>(p, z, m, c_z, sl, mean, stream);
+      default: break;
+    }
+  }
+  switch (vecs) {
+    case 1: return launch_pow2<T, 1>(p, z, m, c_z, 1, mean, stream);
+    case 2: return launch_pow2<T, 2>(p, z, m, c_z, 1, mean, stream);
     default: break;
   }
-  const int64_t total = p.T * G;
+  const int G1 = vecs;
+  const int64_t total = p.T * G1;
   hipLaunchKernelGGL(k_reduce_generic<T>, dim3((unsigned)((total + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, stream, static_cast<const T*>(z), m, p.row_splits,
-                     p.row_sample, p.col_lengths, p.T, c_z, G, mean);
+                     p.row_sample, p.col_lengths, p.T, c_z, G1, mean);
   return hipGetLastError();
 }
 
