@@ -35,11 +35,16 @@ COMMON = [
 ]
 
 
-# Per-file flags. The weight-stationary transition keeps both weights in the
-# accumulation registers (AGPRs) as product operands, so its accumulators go
-# to ordinary VGPRs.
+# Per-file flags: matrix-core accumulators in ordinary VGPRs.
+# - The weight-stationary transition keeps both weights in the accumulation
+#   registers (AGPRs) as product operands.
+# - The recomputing weight gradient masks its recomputed products with VALU
+#   work; in the AGPR form the compiler also moved its long-lived
+#   accumulators between AGPRs and VGPRs every 64-cell block (192 moves per
+#   64 products).
 FILE_FLAGS = {
     "nt_transition_ws.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "nt_wgrad.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

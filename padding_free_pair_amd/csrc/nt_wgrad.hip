@@ -130,7 +130,11 @@ __global__ __launch_bounds__(kWgThreads) void k_wgrad(const bf16* __restrict__ A
 // within each 16 lanes, lane j's element e is element j mod 4 of the 8 bytes
 // at the address of lane 4 e + j / 4), two reads per fragment. The next
 // block's rows are loaded into registers while the current block's products
-// run and are written after them. Each wave
+// run and are written after them. Each wave's chunk weights (the B operands
+// of the first two products) are read from LDS, not held in registers: the
+// accumulators then fit the VGPRs (the file is built with the VGPR form of
+// the products), with no moves between AGPRs and VGPRs around them. The two
+// 32-cell halves of a block run one after the other. Each wave
 // writes its chunk's partial dW1 rows and dW2 columns for the slice; the
 // slices are added in order afterwards.
 constexpr int kRcCells = 64;              // cells per block (two 32-cell halves)
@@ -155,6 +159,8 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_rc(
   static_assert(CZ == 128, "row staging assumes 128 features");
   // [buffer][operand: 0 z, 1 G]
   __shared__ bf16 rm[2][2][kRcCells * kRcRow];
+  // each wave's chunk weights as B fragments: [wave][matrix][t][lane]
+  __shared__ bf16x8 wl[4][2][KT][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int64_t q = blockIdx.x / 8;
@@ -166,11 +172,13 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_rc(
   const int64_t cb1 = cb0 + slice_cells < cells ? cb0 + slice_cells : cells;
 
   // chunk j's weights as the B operand: unit 32 j + l32, features 16 t + 8 h ..
-  bf16x8 wf1[KT], wf2[KT];
+  // (kept in LDS, read by this wave only)
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
-    wf1[t] = *reinterpret_cast<const bf16x8*>(W1 + (int64_t)(32 * j + l32) * CZ + 16 * t + 8 * h);
-    wf2[t] = *reinterpret_cast<const bf16x8*>(W2T + (int64_t)(32 * j + l32) * CZ + 16 * t + 8 * h);
+    wl[wave][0][t][lane] =
+        *reinterpret_cast<const bf16x8*>(W1 + (int64_t)(32 * j + l32) * CZ + 16 * t + 8 * h);
+    wl[wave][1][t][lane] =
+        *reinterpret_cast<const bf16x8*>(W2T + (int64_t)(32 * j + l32) * CZ + 16 * t + 8 * h);
   }
   f32x16 acc1[FB], acc2[FB];
 #pragma unroll
@@ -219,32 +227,27 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_rc(
     if (more) load_rows(c0 + kRcCells);  // in flight during this block's products
     const bf16* Rz = rm[buf][0];
     const bf16* Rg = rm[buf][1];
-    f32x16 pre[2], gh[2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      pre[hb] = f32x16{};
-      gh[hb] = f32x16{};
-    }
+      f32x16 pre = f32x16{}, gh = f32x16{};
 #pragma unroll
-    for (int t = 0; t < KT; ++t)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
+      for (int t = 0; t < KT; ++t) {
         const int r = (32 * hb + l32) * kRcRow + 16 * t + 8 * h;
         const bf16x8 za = *reinterpret_cast<const bf16x8*>(Rz + r);
         const bf16x8 ga = *reinterpret_cast<const bf16x8*>(Rg + r);
-        pre[hb] = wg_mfma(za, wf1[t], pre[hb]);
-        gh[hb] = wg_mfma(ga, wf2[t], gh[hb]);
+        pre = wg_mfma(za, wl[wave][0][t][lane], pre);
+        gh = wg_mfma(ga, wl[wave][1][t][lane], gh);
       }
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+      // relu and the mask on the bits: a float is > 0 exactly when its bits
+      // are a positive integer (finite inputs), and max(bits, 0) is relu
       bf16x8 hk[2], gk[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pv = pre[hb][8 * s + e];
-          hk[s][e] = (bf16)(pv > 0.f ? pv : 0.f);
-          gk[s][e] = (bf16)(pv > 0.f ? gh[hb][8 * s + e] : 0.f);
+          const int pi = __float_as_int(pre[8 * s + e]);
+          hk[s][e] = (bf16)__int_as_float(pi > 0 ? pi : 0);
+          gk[s][e] = (bf16)(pi > 0 ? gh[8 * s + e] : 0.f);
         }
 #pragma unroll
       for (int s = 0; s < 2; ++s)
