@@ -116,8 +116,10 @@ __global__ __launch_bounds__(kWgThreads) void k_wgrad(const bf16* __restrict__ A
 //   pre^T = z W1[j]^T, gh^T = bf16(G) W2T[j]^T     (cells x units, k = features)
 //   g_H = gh * [pre > 0], H = relu(pre)            (lane-local)
 //   dW1[j] += g_H^T z,  dW2[:, j] += bf16(G)^T H    (k = cells)
-// Workgroup (slice, group): four waves own chunks 4 group .. 4 group + 3 and
-// walk the same 64-cell blocks of the slice. Workgroups are handed to the
+// Workgroup (slice, group): eight waves, two per SIMD, walk the same 64-cell
+// blocks of the slice; waves w and w + 4 own chunk 4 group + w % 4, the
+// first for the block's first 32 cells, the second for the other 32, and
+// their sums are added (first + second) at the end. Workgroups are handed to the
 // XCDs round robin (workgroup b to XCD b mod 8), so the index is split as
 // b = 8 (GROUPS q + group) + x with slice 8 q + x: the GROUPS workgroups of a
 // slice run on one XCD at the same time and read its cells through one L2
@@ -130,13 +132,13 @@ __global__ __launch_bounds__(kWgThreads) void k_wgrad(const bf16* __restrict__ A
 // within each 16 lanes, lane j's element e is element j mod 4 of the 8 bytes
 // at the address of lane 4 e + j / 4), two reads per fragment. The next
 // block's rows are loaded into registers while the current block's products
-// run and are written after them. Each wave's chunk weights (the B operands
-// of the first two products) are read from LDS, not held in registers: the
-// accumulators then fit the VGPRs (the file is built with the VGPR form of
-// the products), with no moves between AGPRs and VGPRs around them. The two
-// 32-cell halves of a block run one after the other. Each wave
-// writes its chunk's partial dW1 rows and dW2 columns for the slice; the
-// slices are added in order afterwards.
+// run and are written after them. The chunk weights (the B operands of the
+// first two products) are read from LDS, not held in registers: a wave's
+// accumulators then fit its 256 VGPRs (the file is built with the VGPR form
+// of the products), with no moves between AGPRs and VGPRs around them, and
+// two waves share each SIMD. Each chunk's first wave writes its partial dW1
+// rows and dW2 columns for the slice; the slices are added in order
+// afterwards.
 constexpr int kRcCells = 64;              // cells per block (two 32-cell halves)
 constexpr int kRcRow = 128 + 8;          // [cell][feature] pitch in elements (272 bytes)
 
@@ -151,7 +153,7 @@ __device__ __forceinline__ rc_bf16x4 rc_read_tr(const bf16* p) {
 }
 
 template <int CZ, int HID>
-__global__ __launch_bounds__(256, 1) void k_wgrad_rc(
+__global__ __launch_bounds__(512, 2) void k_wgrad_rc(
     const bf16* __restrict__ z, const bf16* __restrict__ Gb, const bf16* __restrict__ W1,
     const bf16* __restrict__ W2T, float* __restrict__ part1, float* __restrict__ part2,
     int64_t cells, int64_t slice_cells, int64_t slices) {
@@ -159,26 +161,29 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_rc(
   static_assert(CZ == 128, "row staging assumes 128 features");
   // [buffer][operand: 0 z, 1 G]
   __shared__ bf16 rm[2][2][kRcCells * kRcRow];
-  // each wave's chunk weights as B fragments: [wave][matrix][t][lane]
+  // each chunk's weights as B fragments: [chunk of the group][matrix][t][lane]
   __shared__ bf16x8 wl[4][2][KT][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
+  const int cw = wave & 3, hb = wave >> 2;  // chunk of the group, half of each block
   const int64_t q = blockIdx.x / 8;
   const int group = (int)(q % GROUPS);
   const int64_t slice = 8 * (q / GROUPS) + blockIdx.x % 8;
   if (slice >= slices) return;  // the grid is rounded up to whole XCD rounds
-  const int j = 4 * group + wave;
+  const int j = 4 * group + cw;
   const int64_t cb0 = slice * slice_cells;
   const int64_t cb1 = cb0 + slice_cells < cells ? cb0 + slice_cells : cells;
 
   // chunk j's weights as the B operand: unit 32 j + l32, features 16 t + 8 h ..
-  // (kept in LDS, read by this wave only)
+  // (in LDS, read by the chunk's two waves)
+  if (hb == 0) {
 #pragma unroll
-  for (int t = 0; t < KT; ++t) {
-    wl[wave][0][t][lane] =
-        *reinterpret_cast<const bf16x8*>(W1 + (int64_t)(32 * j + l32) * CZ + 16 * t + 8 * h);
-    wl[wave][1][t][lane] =
-        *reinterpret_cast<const bf16x8*>(W2T + (int64_t)(32 * j + l32) * CZ + 16 * t + 8 * h);
+    for (int t = 0; t < KT; ++t) {
+      wl[cw][0][t][lane] =
+          *reinterpret_cast<const bf16x8*>(W1 + (int64_t)(32 * j + l32) * CZ + 16 * t + 8 * h);
+      wl[cw][1][t][lane] =
+          *reinterpret_cast<const bf16x8*>(W2T + (int64_t)(32 * j + l32) * CZ + 16 * t + 8 * h);
+    }
   }
   f32x16 acc1[FB], acc2[FB];
 #pragma unroll
@@ -187,28 +192,23 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_rc(
     acc2[f] = f32x16{};
   }
 
-  // staging: thread -> operand (tid < 128: z, else G), cells 2 cp and 2 cp + 1,
-  // 16-byte pieces sp0 .. sp0 + 3 of each
-  const int op = tid >> 7, st = tid & 127, cp = st >> 2, sp0 = 4 * (st & 3);
+  // staging: thread -> operand (tid < 256: z, else G), cell cp, 16-byte
+  // pieces sp0 .. sp0 + 3 of it
+  const int op = tid >> 8, st = tid & 255, cp = st >> 2, sp0 = 4 * (st & 3);
   const bf16* ssrc = op == 0 ? z : Gb;
-  bf16x8 nxt[2][4];  // [cell of the pair][piece]
+  bf16x8 nxt[4];
   auto load_rows = [&](int64_t c0) {
+    const int64_t c = c0 + cp;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int64_t c = c0 + 2 * cp + u;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        nxt[u][q] = c < cb1 ? *reinterpret_cast<const bf16x8*>(ssrc + c * CZ + 8 * (sp0 + q))
-                            : bf16x8{};
-    }
+    for (int k = 0; k < 4; ++k)
+      nxt[k] = c < cb1 ? *reinterpret_cast<const bf16x8*>(ssrc + c * CZ + 8 * (sp0 + k))
+                       : bf16x8{};
   };
   auto write_rows = [&](int buf) {
     bf16* R = rm[buf][op];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        *reinterpret_cast<bf16x8*>(R + (2 * cp + u) * kRcRow + 8 * (sp0 + q)) = nxt[u][q];
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<bf16x8*>(R + cp * kRcRow + 8 * (sp0 + k)) = nxt[k];
   };
   // this lane's transposing-read address in a 32-cell half: within its
   // 16-lane group (features 32 f + 16 (g mod 2) .., cells 4 h ..), lane l'
@@ -227,55 +227,75 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_rc(
     if (more) load_rows(c0 + kRcCells);  // in flight during this block's products
     const bf16* Rz = rm[buf][0];
     const bf16* Rg = rm[buf][1];
+    f32x16 pre = f32x16{}, gh = f32x16{};
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      f32x16 pre = f32x16{}, gh = f32x16{};
-#pragma unroll
-      for (int t = 0; t < KT; ++t) {
-        const int r = (32 * hb + l32) * kRcRow + 16 * t + 8 * h;
-        const bf16x8 za = *reinterpret_cast<const bf16x8*>(Rz + r);
-        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(Rg + r);
-        pre = wg_mfma(za, wl[wave][0][t][lane], pre);
-        gh = wg_mfma(ga, wl[wave][1][t][lane], gh);
-      }
-      // relu and the mask on the bits: a float is > 0 exactly when its bits
-      // are a positive integer (finite inputs), and max(bits, 0) is relu
-      bf16x8 hk[2], gk[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int pi = __float_as_int(pre[8 * s + e]);
-          hk[s][e] = (bf16)__int_as_float(pi > 0 ? pi : 0);
-          gk[s][e] = (bf16)(pi > 0 ? gh[8 * s + e] : 0.f);
-        }
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int f = 0; f < FB; ++f) {
-          // cells 32 hb + 16 s + 4 h + (0..3) and + 8, feature 32 f + l32
-          const int off = tr_off + (32 * hb + 16 * s) * kRcRow + 32 * f;
-          const rc_bf16x4 z0 = rc_read_tr(Rz + off);
-          const rc_bf16x4 z1 = rc_read_tr(Rz + off + 8 * kRcRow);
-          const rc_bf16x4 g0 = rc_read_tr(Rg + off);
-          const rc_bf16x4 g1 = rc_read_tr(Rg + off + 8 * kRcRow);
-          bf16x8 zf, gf;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            zf[e] = z0[e];
-            zf[4 + e] = z1[e];
-            gf[e] = g0[e];
-            gf[4 + e] = g1[e];
-          }
-          acc1[f] = wg_mfma(gk[s], zf, acc1[f]);  // dW1[j] (units x features)
-          acc2[f] = wg_mfma(gf, hk[s], acc2[f]);  // dW2[:, j] (features x units)
-        }
+    for (int t = 0; t < KT; ++t) {
+      const int r = (32 * hb + l32) * kRcRow + 16 * t + 8 * h;
+      const bf16x8 za = *reinterpret_cast<const bf16x8*>(Rz + r);
+      const bf16x8 ga = *reinterpret_cast<const bf16x8*>(Rg + r);
+      pre = wg_mfma(za, wl[cw][0][t][lane], pre);
+      gh = wg_mfma(ga, wl[cw][1][t][lane], gh);
     }
+    // relu and the mask on the bits: a float is > 0 exactly when its bits
+    // are a positive integer (finite inputs), and max(bits, 0) is relu
+    bf16x8 hk[2], gk[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int pi = __float_as_int(pre[8 * s + e]);
+        hk[s][e] = (bf16)__int_as_float(pi > 0 ? pi : 0);
+        gk[s][e] = (bf16)(pi > 0 ? gh[8 * s + e] : 0.f);
+      }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int f = 0; f < FB; ++f) {
+        // cells 32 hb + 16 s + 4 h + (0..3) and + 8, feature 32 f + l32
+        const int off = tr_off + (32 * hb + 16 * s) * kRcRow + 32 * f;
+        const rc_bf16x4 z0 = rc_read_tr(Rz + off);
+        const rc_bf16x4 z1 = rc_read_tr(Rz + off + 8 * kRcRow);
+        const rc_bf16x4 g0 = rc_read_tr(Rg + off);
+        const rc_bf16x4 g1 = rc_read_tr(Rg + off + 8 * kRcRow);
+        bf16x8 zf, gf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          zf[e] = z0[e];
+          zf[4 + e] = z1[e];
+          gf[e] = g0[e];
+          gf[4 + e] = g1[e];
+        }
+        acc1[f] = wg_mfma(gk[s], zf, acc1[f]);  // dW1[j] (units x features)
+        acc2[f] = wg_mfma(gf, hk[s], acc2[f]);  // dW2[:, j] (features x units)
+      }
     // the other buffer was last read two blocks ago, before the previous barrier
     if (more) write_rows(buf ^ 1);
     __syncthreads();
     buf ^= 1;
   }
+  // the second half's sums join the first's through LDS (over the row
+  // buffers, free after the last barrier), dW1's then dW2's, in that order
+  float* xch = reinterpret_cast<float*>(&rm[0][0][0]);  // [chunk][f][r][lane]
+  static_assert(sizeof(rm) >= sizeof(float) * 4 * FB * 16 * 64, "exchange fits");
+#pragma unroll
+  for (int mat = 0; mat < 2; ++mat) {
+    f32x16 (&acc)[FB] = mat == 0 ? acc1 : acc2;
+    if (hb == 1) {
+#pragma unroll
+      for (int f = 0; f < FB; ++f)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[((cw * FB + f) * 16 + r) * 64 + lane] = acc[f][r];
+    }
+    __syncthreads();
+    if (hb == 0) {
+#pragma unroll
+      for (int f = 0; f < FB; ++f)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[f][r] += xch[((cw * FB + f) * 16 + r) * 64 + lane];
+    }
+    __syncthreads();
+  }
+  if (hb == 1) return;
   // partials: acc1[f] element r is unit 8 (r / 4) + 4 h + r % 4, feature 32 f + l32;
   // acc2[f] element r is feature 32 f + 8 (r / 4) + 4 h + r % 4, unit l32
   float* o1 = part1 + slice * HID * CZ;
@@ -320,7 +340,7 @@ hipError_t launch_wgrad_rc(const void* z, const void* Gb, const void* W1, const 
   float* part1 = part;
   float* part2 = part + S * MN;
   const int64_t S8 = (S + 7) / 8 * 8;
-  hipLaunchKernelGGL((k_wgrad_rc<CZ, HID>), dim3((unsigned)(S8 * (HID / 128))), dim3(256), 0,
+  hipLaunchKernelGGL((k_wgrad_rc<CZ, HID>), dim3((unsigned)(S8 * (HID / 128))), dim3(512), 0,
                      stream, static_cast<const bf16*>(z), static_cast<const bf16*>(Gb),
                      static_cast<const bf16*>(W1), static_cast<const bf16*>(W2T), part1, part2,
                      cells, slice_cells, S);
