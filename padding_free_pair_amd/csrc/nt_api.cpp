@@ -424,13 +424,16 @@ nt_status check_workspace(const void* ws, size_t have, uint64_t need) {
 // transposed weights, and the split partials of the weight gradients (both
 // are hidden x c_z contractions over the cells).
 struct TransBwdWs {
-  uint64_t H, GH, Gb, W1T, W2T, part, total;
+  uint64_t H, GH, Gb, W1T, W2T, part, gm_rows, total;
   int splits;
   bool mfma;  // the weight gradients run on the matrix cores
   bool rc;    // ... recomputing H and g_H from z and bf16(G) (no H, GH buffers)
 };
 
-TransBwdWs transition_backward_ws(int64_t cells, int c_z, int hidden, nt_dtype dtype) {
+// mean_rows: the pair rows whose mean adjoint the matrix-core kernel forms
+// (T when called with g_m, else 0); their quotients g_m / M_i come last.
+TransBwdWs transition_backward_ws(int64_t cells, int c_z, int hidden, nt_dtype dtype,
+                                  int64_t mean_rows = 0) {
   TransBwdWs w;
   const uint64_t es = esize(dtype);
   w.rc = nt::wgrad_rc_supported(c_z, hidden, dtype);
@@ -450,6 +453,9 @@ TransBwdWs transition_backward_ws(int64_t cells, int c_z, int hidden, nt_dtype d
                       : nt::gemm_tn_splits(cells, hidden, c_z);
     w.part = off; off += nt::align256((size_t)w.splits * hidden * c_z * sizeof(float));
   }
+  w.gm_rows = off;
+  if (nt::transition_backward_has_mfma(c_z, hidden, dtype))
+    off += nt::align256((size_t)mean_rows * c_z * sizeof(float));
   w.total = off;
   return w;
 }
@@ -460,7 +466,7 @@ nt_status transition_backward(const nt_partition* p, const void* z, const float*
                               const void* W1, const void* W2, float* g_z, float* dW1, float* dW2,
                               int c_z, int hidden, nt_dtype dtype, char* ws, hipStream_t s,
                               const float* g_m = nullptr, const float* g_in = nullptr) {
-  const TransBwdWs w = transition_backward_ws(p->cells, c_z, hidden, dtype);
+  const TransBwdWs w = transition_backward_ws(p->cells, c_z, hidden, dtype, g_m ? p->T : 0);
   void* H = w.rc ? nullptr : ws + w.H;
   void* GH = w.rc ? nullptr : ws + w.GH;
   void* Gb = ws + w.Gb;
@@ -470,8 +476,9 @@ nt_status transition_backward(const nt_partition* p, const void* z, const float*
     void* W2T = ws + w.W2T;
     NT_TRY(hip_status(nt::launch_transpose(W2, W2T, c_z, hidden, dtype, s), "transpose W2"));
     NT_TRY(hip_status(nt::launch_transpose(W1, W1T, hidden, c_z, dtype, s), "transpose W1"));
-    NT_TRY(hip_status(nt::launch_transition_backward_mfma(*p, z, G, g_m, g_in, W1, W2T, W1T, g_z,
-                                                          H, GH, Gb, nt::device_cu_count(), s),
+    NT_TRY(hip_status(nt::launch_transition_backward_mfma(
+                          *p, z, G, g_m, g_in, W1, W2T, W1T, g_z, H, GH, Gb,
+                          reinterpret_cast<float*>(ws + w.gm_rows), nt::device_cu_count(), s),
                       "transition backward"));
     if (w.rc)
       return hip_status(nt::launch_wgrad_rc(z, Gb, W1, W2T, dW1, dW2, part, p->cells, w.splits,
@@ -634,7 +641,8 @@ BlockBwdWs block_backward_ws(const nt_partition* p, int c_s, int c_z, int hidden
   w.ppart = off; off += nt::align256((size_t)w.psplits * c_s * c_z * sizeof(float));
   w.trans = off;
   off += swiglu ? swiglu_backward_ws(CS, c_z, hidden).total
-                : transition_backward_ws(CS, c_z, hidden, dtype).total;
+                : transition_backward_ws(CS, c_z, hidden, dtype,
+                                         S == 1 ? p->T : 0).total;
   w.total = off;
   return w;
 }

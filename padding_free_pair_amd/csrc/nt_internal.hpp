@@ -203,13 +203,14 @@ int device_cu_count();
 // W2^T [hidden, c_z] and W1T = W1^T [c_z, hidden] are prepared by the caller.
 // H and GH may be null (then they are not written). With g_m non-null, G is
 // not read: it is formed per cell as g_m[row] / M_i (+ g_in[cell] when
-// g_in is non-null), exactly as launch_mean_backward forms it.
+// g_in is non-null), exactly as launch_mean_backward forms it; the quotients
+// go to gm_rows [T, c_z] first.
 bool transition_backward_has_mfma(int c_z, int hidden, nt_dtype dtype);
 hipError_t launch_transition_backward_mfma(const nt_partition& p, const void* z, const float* G,
                                            const float* g_m, const float* g_in, const void* W1,
                                            const void* W2T, const void* W1T, float* g_z,
-                                           void* H, void* GH, void* Gb, int cus,
-                                           hipStream_t stream);
+                                           void* H, void* GH, void* Gb, float* gm_rows,
+                                           int cus, hipStream_t stream);
 // Transition gradient without weight gradients: g_z, and H, GH and Gb (G in
 // the storage type) for them. g_z may equal G.
 hipError_t launch_transition_backward_generic(const nt_partition& p, const void* z,

@@ -48,9 +48,11 @@ __device__ __forceinline__ int bw_p32(int rho) {
 
 // Where G comes from: read from memory, or formed from the column mean's
 // adjoint, G[cell] = g_m[row] / M_i (+ g_in[cell]), with the cell decoded on
-// the fly (Eq. 3 inverted from the tile's first sample).
+// the fly (Eq. 3 inverted from the tile's first sample). The division is
+// done once per row beforehand (k_mean_rows), so `g_m` here holds the
+// quotients.
 struct MeanAdjoint {
-  const float* g_m;             // [T, c_z]
+  const float* g_m;             // [T, c_z], g_m[row] / M_i
   const float* g_in;            // [cells, c_z] or null
   const int64_t* pair_offsets;
   const int64_t* single_offsets;
@@ -133,14 +135,12 @@ __global__ __launch_bounds__(kBwThreads, 2) void k_transition_bwd(
     for (int cb = 0; cb < CB; ++cb) {
       int64_t c = cell0 + 32 * cb + l32;
       c = c < cells ? c : cells - 1;
-      const float* grow = nullptr;  // g_m row of the cell (FROM_MEAN)
-      float mf = 0.f;  // M_i as a float (the divisor)
+      const float* grow = nullptr;  // g_m[row] / M_i for the cell's row (FROM_MEAN)
       if constexpr (FROM_MEAN) {
         int i = ma.tile_sample[tile];  // tiles are 256 cells, the index's span
         while (ma.pair_offsets[i + 1] <= c) ++i;
         const int64_t m = ma.col_lengths[i];
         grow = ma.g_m + (ma.single_offsets[i] + (c - ma.pair_offsets[i]) / m) * CZ;
-        mf = (float)m;
       }
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
@@ -148,13 +148,8 @@ __global__ __launch_bounds__(kBwThreads, 2) void k_transition_bwd(
         f32x4 g0, g1;
         if constexpr (FROM_MEAN) {
           // as the mean's adjoint kernel: g_m / M_i, then + g_in
-          const f32x4 m0 = *reinterpret_cast<const f32x4*>(grow + 16 * t + 8 * h);
-          const f32x4 m1 = *reinterpret_cast<const f32x4*>(grow + 16 * t + 8 * h + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            g0[e] = m0[e] / mf;
-            g1[e] = m1[e] / mf;
-          }
+          g0 = *reinterpret_cast<const f32x4*>(grow + 16 * t + 8 * h);
+          g1 = *reinterpret_cast<const f32x4*>(grow + 16 * t + 8 * h + 4);
           if (ma.g_in) {
             const f32x4 i0 = *reinterpret_cast<const f32x4*>(ma.g_in + c * CZ + 16 * t + 8 * h);
             const f32x4 i1 =
@@ -267,6 +262,23 @@ __global__ __launch_bounds__(kBwThreads, 2) void k_transition_bwd(
   }
 }
 
+// g_m[row] / M_i for every pair row, each a float4 per thread (the same
+// division, in the same precision, as the mean's adjoint kernel).
+__global__ __launch_bounds__(256) void k_mean_rows(const float* __restrict__ g_m,
+                                                   float* __restrict__ out,
+                                                   const int64_t* __restrict__ row_splits,
+                                                   int64_t T, int c_z) {
+  const int q4 = c_z / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // float4 of the rows
+  if (idx >= T * q4) return;
+  const int64_t r = idx / q4;
+  const float nf = (float)(row_splits[r + 1] - row_splits[r]);
+  f32x4 v = *reinterpret_cast<const f32x4*>(g_m + 4 * idx);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = v[e] / nf;
+  *reinterpret_cast<f32x4*>(out + 4 * idx) = v;
+}
+
 }  // namespace
 
 bool transition_backward_has_mfma(int c_z, int hidden, nt_dtype dtype) {
@@ -276,9 +288,17 @@ bool transition_backward_has_mfma(int c_z, int hidden, nt_dtype dtype) {
 hipError_t launch_transition_backward_mfma(const nt_partition& p, const void* z, const float* G,
                                            const float* g_m, const float* g_in, const void* W1,
                                            const void* W2T, const void* W1T, float* g_z,
-                                           void* H, void* GH, void* Gb, int cus,
-                                           hipStream_t stream) {
+                                           void* H, void* GH, void* Gb, float* gm_rows,
+                                           int cus, hipStream_t stream) {
   if (p.cells == 0) return hipSuccess;
+  if (g_m) {
+    const int64_t n4 = p.T * (128 / 4);
+    hipLaunchKernelGGL(k_mean_rows, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                       g_m, gm_rows, p.row_splits, p.T, 128);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_m = gm_rows;
+  }
   static_assert(kBwTileCells == kSampleIndexSpan, "tiles use the partition's sample index");
   const int64_t ntiles = (p.cells + kBwTileCells - 1) / kBwTileCells;
   const int64_t grid = ntiles < cus ? ntiles : cus;
