@@ -898,6 +898,14 @@ def main():
                                 "frac": v["frac"]} for k, v in ko.items()}}
             if other.blocks > 1:
                 regimes[other.name]["granularity"] = granularity(xo, ro, to, args, torch, nt)
+            if xo.dtype == "bf16" and other.blocks > 1:
+                tro = TrainRunner(xo, torch, nt, ro)
+                t_tr = time_steps(tro.step, args.steps, args.warmup, torch)
+                regimes[other.name]["train"] = {
+                    "value": ro.cells * other.blocks / t_tr, "unit": "pair cells/s per block",
+                    "ms_per_step": t_tr * 1e3, "forward_ms": to * 1e3}
+                log(f"regime {other.name}: train step {t_tr * 1e3:.3f} ms")
+                del tro
             cells_o = ro.cells
             del ro
             torch.cuda.empty_cache()

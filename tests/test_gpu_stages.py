@@ -146,6 +146,10 @@ def test_transition_exact(nt, dtype, c_z, hidden):
     (LONG, 128, "bf16"), (HIGH_VAR, 128, "bf16"), (ONE_BLOCK, 64, "bf16"), (TINY, 8, "f32"),
     (TINY, 24, "bf16"), (TINY, 24, "f32"), ([300, 5], 512, "bf16"), ([300, 5], 512, "f32"),
     (EDGE, 128, "bf16"), ([255, 256, 257, 1], 64, "f32"), ([1], 8, "bf16"),
+    # widths of several power-of-two slices (three of 16, 32, 4 or 8 vectors),
+    # on long rows (one workgroup a row) and short ones
+    ([300, 5], 384, "bf16"), ([300, 5], 384, "f32"), (TINY, 96, "bf16"), ([257, 40], 192, "bf16"),
+    (EDGE, 384, "bf16"),
 ])
 def test_reduce_parity(nt, lengths, c_z, dtype):
     announce(f"reduce {dtype} c_z={c_z} B={len(lengths)}")
@@ -164,7 +168,7 @@ def test_reduce_parity(nt, lengths, c_z, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("c_z", [128, 24])
+@pytest.mark.parametrize("c_z", [128, 24, 384])
 def test_reduce_exact(nt, dtype, c_z):
     lengths = [2, 4, 8, 16, 1, 256, 512]
     announce(f"reduce exact {dtype} c_z={c_z}")
