@@ -126,15 +126,18 @@ __device__ __forceinline__ void ws_decode(const OFF* po, const IDX* eta, const C
 
 // LDS_PART: a square partition of at most kWsSamples samples with N_i <=
 // 65535, decoded from an LDS copy with 32-bit arithmetic; otherwise the
-// partition is read from global memory.
-template <bool LDS_PART>
+// partition is read from global memory. SLICES: S > 1 (the non-leading
+// layout); without it S is 1 at compile time and the row arithmetic has no
+// divisions by S.
+template <bool LDS_PART, bool SLICES>
 __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
     const float* __restrict__ a, const float* __restrict__ b,
     const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
     const int64_t* __restrict__ col_offsets, const int32_t* __restrict__ col_lengths,
     const int32_t* __restrict__ tile_sample, int B,
     const bf16* __restrict__ W1, const bf16* __restrict__ W2, bf16* __restrict__ z_out,
-    int64_t cells, int64_t nblocks, int64_t per, int64_t T_rows, int64_t T_cols, int S) {
+    int64_t cells, int64_t nblocks, int64_t per, int64_t T_rows, int64_t T_cols, int S_arg) {
+  const int S = SLICES ? S_arg : 1;
   constexpr int CZ = 128, HID = 512;
   constexpr int KT = CZ / 16;  // first-product k-steps
   constexpr int ROW = CZ * 4;  // bytes of one fp32 single row
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(kWsWaves * 64, 1) void k_transition_ws(
   auto dec2 = [&](int64_t blk) {
     const int64_t c = blk * kWsCells + sc;
     d_cell = c < cells ? c : cells - 1;  // a row past the end repeats the last one
-    if (S > 1) {  // row d_cell = slice d_slice of pair cell d_cell / S
+    if constexpr (SLICES) {  // row d_cell = slice d_slice of pair cell d_cell / S
       const int64_t pc = d_cell / S;
       d_slice = (int)(d_cell - pc * S);
       d_cell = pc;
@@ -533,7 +536,8 @@ hipError_t launch_transition_ws(const nt_partition& p, const void* a, const void
   // the LDS copy of the partition holds square partitions (mu = eta, M = N)
   const bool lds_part =
       p.B <= kWsSamples && p.col_offsets == p.single_offsets && p.n_max <= 65535;
-  auto kern = lds_part ? k_transition_ws<true> : k_transition_ws<false>;
+  auto kern = S > 1 ? (lds_part ? k_transition_ws<true, true> : k_transition_ws<false, true>)
+                    : (lds_part ? k_transition_ws<true, false> : k_transition_ws<false, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kWsWaves * 64), 0, stream,
                      static_cast<const float*>(a), static_cast<const float*>(b), p.pair_offsets,
                      p.single_offsets, p.col_offsets, p.col_lengths, p.tile_sample, p.B,
