@@ -612,7 +612,7 @@ nt_status swiglu_transition_backward(int64_t cells, const float* z32, float* G,
 // transposed projection weights, the projections' split partials, then the
 // transition backward's own workspace.
 struct BlockBwdWs {
-  uint64_t a, b, z, m, g_m, G, g_a, g_b, WoT, WaT, WbT, ppart, trans, total;
+  uint64_t a, b, z, m, g_m, G, g_a, g_b, WoT, WaT, WbT, ppart, adj, trans, total;
   int psplits;
 };
 
@@ -639,6 +639,7 @@ BlockBwdWs block_backward_ws(const nt_partition* p, int c_s, int c_z, int hidden
   w.WbT = off;   off += proj;
   w.psplits = nt::gemm_tn_splits(TS, c_z, c_s);
   w.ppart = off; off += nt::align256((size_t)w.psplits * c_s * c_z * sizeof(float));
+  w.adj = off;   off += nt::align256(nt::bcast_adj_ws_bytes(*p, S * c_z));
   w.trans = off;
   off += swiglu ? swiglu_backward_ws(CS, c_z, hidden).total
                 : transition_backward_ws(CS, c_z, hidden, dtype,
@@ -1242,8 +1243,9 @@ static nt_status block_backward_s(const nt_partition* p, const void* s_in, const
     NT_TRY(transition_backward(&v, z, G, w->W1, w->W2, G, grads->W1, grads->W2, c_z, hidden,
                                dtype, base + L.trans, s));
   }
-  NT_TRY(hip_status(nt::launch_reduce(*p, G, g_a, W, NT_F32, s, false), "row sums"));
-  NT_TRY(hip_status(nt::launch_col_sums(*p, G, g_b, W, s), "column sums"));
+  NT_TRY(hip_status(nt::launch_bcast_adj(*p, G, g_a, g_b, W,
+                                         reinterpret_cast<float*>(base + L.adj), s),
+                    "row and column sums"));
   // a = s Wa^T, b = s Wb^T
   NT_TRY(hip_status(nt::launch_linear(g_a, NT_F32, WaT, dtype, g_s_out, g_s_in, NT_F32, T, c_s,
                                       c_z, s),

@@ -358,6 +358,128 @@ hipError_t launch_loss_t(const nt_partition& p, const void* x, int c_s, const vo
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Both adjoints of the broadcast from one read of g_z (square partitions of
+// at most kAdjSamples samples): g_a[eta_i + r] = sum_c g_z[o_i + r N_i + c]
+// and g_b[eta_i + c] = sum_r g_z[o_i + r N_i + c]. A workgroup takes a tile
+// of kAdjR rows x C columns of one sample (C = kAdjKC columns per thread);
+// thread (f, cl) owns float4 f of columns c0 + cl + cpp u. Each tile writes
+// its row sums to prow[column tile][row] and its column sums to
+// pcol[row tile][column]; k_adj_sum then adds a row's (column's) tiles in
+// tile order, so results are deterministic.
+constexpr int kAdjSamples = 256;
+constexpr int kAdjR = 16;   // rows of a tile
+constexpr int kAdjKC = 16;  // columns of a tile per thread
+
+template <bool STREAM>
+__global__ __launch_bounds__(kThreads) void k_bcast_adj(
+    const float* __restrict__ g_z, float* __restrict__ prow, float* __restrict__ pcol,
+    const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
+    const int32_t* __restrict__ lengths, int B, int W, int64_t T) {
+  __shared__ int64_t tile_end[kAdjSamples];  // inclusive prefix of tiles per sample
+  __shared__ int64_t wave_sum[kThreads / 64];
+  __shared__ f32x4 rsum[kAdjR][kThreads];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q4 = W / 4, cpp = kThreads / q4, C = cpp * kAdjKC;
+  int64_t v = 0;
+  if (tid < B) {
+    const int64_t n = lengths[tid];
+    v = ((n + kAdjR - 1) / kAdjR) * ((n + C - 1) / C);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) wave_sum[wave] = v;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) v += wave_sum[w];
+  tile_end[tid] = v;
+  __syncthreads();
+  const int64_t g = blockIdx.x;
+  if (B == 0 || g >= tile_end[B - 1]) return;  // the grid is an upper bound
+  int lo = 0, hi = B - 1;  // first sample with tile_end > g
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (tile_end[mid] > g) hi = mid; else lo = mid + 1;
+  }
+  const int i = lo;
+  const int64_t local = g - (i > 0 ? tile_end[i - 1] : 0);
+  const int64_t n = lengths[i], nct = (n + C - 1) / C;
+  const int64_t rt = local / nct, ct = local - rt * nct;
+  const int64_t r0 = rt * kAdjR, c0 = ct * C;
+  const int f = tid % q4, cl = tid / q4;
+  const bool act = cl < cpp;
+  const int64_t eta = single_offsets[i], o = pair_offsets[i];
+  f32x4 colp[kAdjKC];
+#pragma unroll
+  for (int u = 0; u < kAdjKC; ++u) colp[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < kAdjR; ++k) {
+    const int64_t r = r0 + k;
+    f32x4 rs = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (r < n && act) {
+      const float* row = g_z + (o + r * n) * W + 4 * f;
+      f32x4 x[kAdjKC];
+#pragma unroll
+      for (int u = 0; u < kAdjKC; ++u) {
+        const int64_t c = c0 + cl + (int64_t)cpp * u;
+        x[u] = c < n ? load_col4<STREAM>(row + c * W) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < kAdjKC; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          colp[u][e] += x[u][e];
+          rs[e] += x[u][e];
+        }
+    }
+    rsum[k][tid] = rs;
+  }
+  __syncthreads();
+  // the tile's row sums: row k, float4 ff, over the cpp column lanes in order
+  for (int idx = tid; idx < kAdjR * q4; idx += kThreads) {
+    const int k = idx / q4, ff = idx - k * q4;
+    const int64_t r = r0 + k;
+    if (r >= n) continue;
+    f32x4 sum = rsum[k][ff];
+    for (int c2 = 1; c2 < cpp; ++c2) {
+      const f32x4 t = rsum[k][c2 * q4 + ff];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum[e] += t[e];
+    }
+    *reinterpret_cast<f32x4*>(prow + ((int64_t)ct * T + eta + r) * W + 4 * ff) = sum;
+  }
+  if (act) {
+#pragma unroll
+    for (int u = 0; u < kAdjKC; ++u) {
+      const int64_t c = c0 + cl + (int64_t)cpp * u;
+      if (c < n) *reinterpret_cast<f32x4*>(pcol + ((int64_t)rt * T + eta + c) * W + 4 * f) = colp[u];
+    }
+  }
+}
+
+// out[x] = sum over the ceil(n / span) tiles t of part[t][x] in tile order, for
+// every row (column) x of T; n is the length of x's sample.
+__global__ __launch_bounds__(kThreads) void k_adj_sum(const float* __restrict__ part,
+                                                      float* __restrict__ out,
+                                                      const int32_t* __restrict__ row_sample,
+                                                      const int32_t* __restrict__ lengths,
+                                                      int64_t T, int W, int span) {
+  const int q4 = W / 4;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= T * q4) return;
+  const int64_t x = idx / q4;
+  const int f = (int)(idx - x * q4);
+  const int64_t n = lengths[row_sample[x]], cnt = (n + span - 1) / span;
+  f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t t = 0; t < cnt; ++t) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(part + (t * T + x) * W + 4 * f);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sum[e] += v[e];
+  }
+  *reinterpret_cast<f32x4*>(out + x * W + 4 * f) = sum;
+}
+
 }  // namespace
 
 hipError_t launch_mean_backward(const nt_partition& p, const float* g_m, const float* g_in,
@@ -380,6 +502,49 @@ hipError_t launch_col_sums(const nt_partition& p, const float* g_z, float* g_b, 
   hipLaunchKernelGGL(stream_g ? k_col_sums<true> : k_col_sums<false>, dim3((unsigned)(p.B * per)),
                      dim3(kThreads), 0, s, g_z, g_b,
                      p.pair_offsets, p.col_offsets, p.lengths, p.col_lengths, (int)per, c_z);
+  return hipGetLastError();
+}
+
+bool bcast_adj_fused(const nt_partition& p, int W) {
+  return p.col_offsets == p.single_offsets && p.B <= kAdjSamples && W % 4 == 0 && W / 4 <= kThreads;
+}
+
+size_t bcast_adj_ws_bytes(const nt_partition& p, int W) {
+  if (!bcast_adj_fused(p, W)) return 0;
+  const int64_t C = (int64_t)(kThreads / (W / 4)) * kAdjKC;
+  const int64_t CT = (p.n_max + C - 1) / C, RT = ((int64_t)p.n_max + kAdjR - 1) / kAdjR;
+  return (size_t)(CT + RT) * p.T * W * sizeof(float);
+}
+
+hipError_t launch_bcast_adj(const nt_partition& p, const float* g_z, float* g_a, float* g_b,
+                            int W, float* ws, hipStream_t s) {
+  if (!bcast_adj_fused(p, W)) {
+    hipError_t e = launch_reduce(p, g_z, g_a, W, NT_F32, s, false);
+    return e != hipSuccess ? e : launch_col_sums(p, g_z, g_b, W, s);
+  }
+  if (p.T == 0) return hipSuccess;
+  const int64_t C = (int64_t)(kThreads / (W / 4)) * kAdjKC;
+  const int64_t CT = (p.n_max + C - 1) / C;
+  float* prow = ws;
+  float* pcol = ws + CT * p.T * W;
+  // an upper bound of the tiles, sum ceil(N_i / R) ceil(N_i / C) <=
+  // sum (N_i / R + 1)(N_i / C + 1); workgroups past the last tile return at once
+  const int64_t tiles = (p.cells + kAdjR * C - 1) / (kAdjR * C) + (p.T + kAdjR - 1) / kAdjR +
+                        (p.T + C - 1) / C + p.B;
+  const bool stream_g = p.cells * W * (int64_t)sizeof(float) > kStreamBytes;
+  hipLaunchKernelGGL(stream_g ? k_bcast_adj<true> : k_bcast_adj<false>, dim3((unsigned)tiles),
+                     dim3(kThreads), 0, s, g_z, prow, pcol, p.pair_offsets, p.single_offsets,
+                     p.lengths, p.B, W, p.T);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n4 = p.T * (W / 4);
+  const dim3 grid((unsigned)((n4 + kThreads - 1) / kThreads));
+  hipLaunchKernelGGL(k_adj_sum, grid, dim3(kThreads), 0, s, prow, g_a, p.row_sample, p.lengths,
+                     p.T, W, (int)C);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_adj_sum, grid, dim3(kThreads), 0, s, pcol, g_b, p.row_sample, p.lengths,
+                     p.T, W, kAdjR);
   return hipGetLastError();
 }
 

@@ -153,6 +153,15 @@ hipError_t launch_mean_backward(const nt_partition& p, const float* g_m, const f
 // g_b[mu_i + c] = sum_r g_z[o_i + r M_i + c] (fp32).
 hipError_t launch_col_sums(const nt_partition& p, const float* g_z, float* g_b, int c_z,
                            hipStream_t stream);
+// Both broadcast adjoints, g_a (row sums) and g_b (column sums) of g_z with
+// rows of W floats, from one read of g_z when bcast_adj_fused (square
+// partitions, B <= 256): tile partial sums go to ws (bcast_adj_ws_bytes)
+// and are added in tile order. Otherwise the row and column kernels run
+// (ws unused).
+bool bcast_adj_fused(const nt_partition& p, int W);
+size_t bcast_adj_ws_bytes(const nt_partition& p, int W);
+hipError_t launch_bcast_adj(const nt_partition& p, const float* g_z, float* g_a, float* g_b,
+                            int W, float* ws, hipStream_t stream);
 // Equation 5: rows of x hold S * c_s values, rows of pz S * c_z; partial
 // [max(T, 1)] fp64 scratch, loss one fp64; g_x, g_pz may be null.
 hipError_t launch_loss_eq5(const nt_partition& p, const void* x, int c_s, const void* pz, int c_z,
