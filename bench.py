@@ -457,7 +457,9 @@ def kernel_rooflines(r: PackedRunner, reps: int):
                              "back_to_back_ms": t_b2b * 1e3}
     t = time_kernel(lambda: nt.nt_pair_broadcast(r.p, a, b, z=zt), reps, torch)
     nbytes = cells * cz * es + 2 * T * cz * es
-    out["broadcast"] = {"kernel": "k_broadcast", "bound": "hbm", "ms": t * 1e3,
+    # the stage's kernel: tiles of one sample for at most 256 samples
+    bkern = "k_broadcast_tiled" if len(r.lengths) <= 256 else "k_broadcast"
+    out["broadcast"] = {"kernel": bkern, "bound": "hbm", "ms": t * 1e3,
                         "achieved": nbytes / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "bytes_per_launch": nbytes}
     t = time_kernel(lambda: nt.nt_pair_reduce(r.p, zt, m=m), reps, torch)
