@@ -607,6 +607,88 @@ nt_status swiglu_transition_backward(int64_t cells, const float* z32, float* G,
                     "LN backward");
 }
 
+// Workspace of the fused SwiGLU gradient (c_z 128, hidden a multiple of 128,
+// bf16): the kernel's outputs x and G as bf16 pairs, A, g_u, g_g, the
+// transposed weights, the LN parameters' workgroup sums, the weight
+// contractions' split partials and their 2 c_z x hidden result.
+struct SwigluBwd32Ws {
+  uint64_t X2, G2, A, GU, GG, WdT, WuT, WgT, lnpart, wpart, ctmp, ttmp, total;
+  int wsplits, grid;
+};
+
+SwigluBwd32Ws swiglu_backward32_ws(int64_t cells, int c_z, int hidden) {
+  SwigluBwd32Ws w;
+  const uint64_t ch = (uint64_t)cells * hidden, c2 = (uint64_t)cells * 2 * c_z;
+  const uint64_t wbytes = nt::align256((size_t)hidden * c_z * 2);
+  const uint64_t mn2 = (uint64_t)2 * c_z * hidden;  // the [hi | lo] contractions
+  uint64_t off = 0;
+  w.X2 = off;  off += nt::align256(c2 * 2);
+  w.G2 = off;  off += nt::align256(c2 * 2);
+  w.A = off;   off += nt::align256(ch * 2);
+  w.GU = off;  off += nt::align256(ch * 2);
+  w.GG = off;  off += nt::align256(ch * 2);
+  w.WdT = off; off += wbytes;
+  w.WuT = off; off += wbytes;
+  w.WgT = off; off += wbytes;
+  w.grid = nt::swiglu_bwd32_grid(cells);
+  w.lnpart = off; off += nt::align256((size_t)2 * (w.grid > 0 ? w.grid : 1) * c_z * 4);
+  w.wsplits = nt::wgrad_splits(cells, 2 * c_z, hidden);
+  w.wpart = off; off += nt::align256((size_t)w.wsplits * mn2 * 4);
+  w.ctmp = off;  off += nt::align256(mn2 * 4);
+  w.ttmp = off;  off += nt::align256((size_t)c_z * hidden * 4);
+  w.total = off;
+  return w;
+}
+
+// The fused SwiGLU gradient: G (fp32 [cells, c_z]) becomes g_z; a and b are
+// the block's fp32 projections (the kernel forms the pair state per cell).
+// The weight gradients are contractions over the cells on the matrix cores,
+// with x and G as bf16 pairs: C = [hi; lo]^T B (2 c_z rows), then the two
+// halves added (and transposed for dWu, dWg, whose rows are the units).
+nt_status swiglu_transition_backward32(const nt_partition* p, const float* a, const float* b,
+                                       float* G, const nt_block_params& w,
+                                       const nt_block_param_grads& g, int c_z, int hidden,
+                                       char* ws, hipStream_t s) {
+  const SwigluBwd32Ws L = swiglu_backward32_ws(p->cells, c_z, hidden);
+  void *X2 = ws + L.X2, *G2 = ws + L.G2, *A = ws + L.A, *GU = ws + L.GU, *GG = ws + L.GG;
+  void *WdT = ws + L.WdT, *WuT = ws + L.WuT, *WgT = ws + L.WgT;
+  float* lnpart = reinterpret_cast<float*>(ws + L.lnpart);
+  float* wpart = reinterpret_cast<float*>(ws + L.wpart);
+  float* ctmp = reinterpret_cast<float*>(ws + L.ctmp);
+  float* ttmp = reinterpret_cast<float*>(ws + L.ttmp);
+  const int64_t cz_h = (int64_t)c_z * hidden;
+  NT_TRY(hip_status(nt::launch_transpose(w.W_down, WdT, c_z, hidden, NT_BF16, s),
+                    "transpose W_down"));
+  NT_TRY(hip_status(nt::launch_transpose(w.W_up, WuT, hidden, c_z, NT_BF16, s),
+                    "transpose W_up"));
+  NT_TRY(hip_status(nt::launch_transpose(w.W_gate, WgT, hidden, c_z, NT_BF16, s),
+                    "transpose W_gate"));
+  NT_TRY(hip_status(nt::launch_swiglu_bwd32(*p, a, b, w.ln_gamma, w.ln_beta, w.W_gate, w.W_up,
+                                            WdT, WuT, WgT, G, X2, G2, A, GU, GG, lnpart, hidden,
+                                            w.ln_eps, s),
+                    "fused SwiGLU gradient"));
+  const int grid = L.grid;
+  NT_TRY(hip_status(nt::launch_sum_splits(lnpart, g.ln_gamma, grid, c_z, s), "dln_gamma"));
+  NT_TRY(hip_status(nt::launch_sum_splits(lnpart + (size_t)grid * c_z, g.ln_beta, grid, c_z, s),
+                    "dln_beta"));
+  // dWd [c_z, hidden] = G^T A
+  NT_TRY(hip_status(nt::launch_wgrad(G2, A, ctmp, wpart, p->cells, 2 * c_z, hidden, L.wsplits,
+                                     s),
+                    "dW_down contraction"));
+  NT_TRY(hip_status(nt::launch_sum_splits(ctmp, g.W_down, 2, cz_h, s), "dW_down halves"));
+  // dWu^T, dWg^T [c_z, hidden] = x^T g_u, x^T g_g
+  const struct { void* B; float* out; const char* what; } wg[2] = {
+      {GU, g.W_up, "dW_up"}, {GG, g.W_gate, "dW_gate"}};
+  for (const auto& q : wg) {
+    NT_TRY(hip_status(nt::launch_wgrad(X2, q.B, ctmp, wpart, p->cells, 2 * c_z, hidden,
+                                       L.wsplits, s),
+                      q.what));
+    NT_TRY(hip_status(nt::launch_sum_splits(ctmp, ttmp, 2, cz_h, s), q.what));
+    NT_TRY(hip_status(nt::launch_transpose(ttmp, q.out, c_z, hidden, NT_F32, s), q.what));
+  }
+  return ok();
+}
+
 // Block backward workspace (square partitions): a, b (fp32), z (storage
 // type), m, g_m, G (fp32; G becomes g_z in place), g_a, g_b (fp32), the
 // transposed projection weights, the projections' split partials, then the
@@ -627,8 +709,10 @@ BlockBwdWs block_backward_ws(const nt_partition* p, int c_s, int c_z, int hidden
   uint64_t off = 0;
   w.a = off;     off += single;
   w.b = off;     off += single;
-  // the SwiGLU gradient reads the pair state in fp32 (LN's statistics)
-  w.z = off;     off += nt::align256((size_t)CS * c_z * (swiglu ? 4 : es));
+  // the unfused SwiGLU gradient reads the pair state in fp32 (LN's
+  // statistics); the fused one forms it per cell and needs none
+  const bool fused = swiglu && S == 1 && nt::swiglu_bwd32_supported(c_z, hidden, dtype);
+  w.z = off;     off += fused ? 0 : nt::align256((size_t)CS * c_z * (swiglu ? 4 : es));
   w.m = off;     off += single;
   w.g_m = off;   off += single;
   w.G = off;     off += nt::align256((size_t)CS * c_z * sizeof(float));
@@ -641,9 +725,9 @@ BlockBwdWs block_backward_ws(const nt_partition* p, int c_s, int c_z, int hidden
   w.ppart = off; off += nt::align256((size_t)w.psplits * c_s * c_z * sizeof(float));
   w.adj = off;   off += nt::align256(nt::bcast_adj_ws_bytes(*p, S * c_z));
   w.trans = off;
-  off += swiglu ? swiglu_backward_ws(CS, c_z, hidden).total
-                : transition_backward_ws(CS, c_z, hidden, dtype,
-                                         S == 1 ? p->T : 0).total;
+  off += fused    ? swiglu_backward32_ws(CS, c_z, hidden).total
+         : swiglu ? swiglu_backward_ws(CS, c_z, hidden).total
+                  : transition_backward_ws(CS, c_z, hidden, dtype, S == 1 ? p->T : 0).total;
   w.total = off;
   return w;
 }
@@ -1214,8 +1298,10 @@ static nt_status block_backward_s(const nt_partition* p, const void* s_in, const
   // recompute the forward's a, b, z and m
   NT_TRY(hip_status(nt::launch_linear2(s_in, dtype, w->Wa, w->Wb, a, b, T, c_z, c_s, s),
                     "projections a, b"));
-  NT_TRY(hip_status(nt::launch_broadcast(*p, a, b, z, W, swiglu ? NT_F32 : dtype, s, true),
-                    "broadcast"));
+  const bool swiglu_fused = swiglu && nt::swiglu_bwd32_supported(c_z, hidden, dtype);
+  if (!swiglu_fused)
+    NT_TRY(hip_status(nt::launch_broadcast(*p, a, b, z, W, swiglu ? NT_F32 : dtype, s, true),
+                      "broadcast"));
   NT_TRY(hip_status(nt::launch_reduce(*p, z_out, m, W, dtype, s), "column mean"));
   NT_TRY(hip_status(nt::launch_transpose(w->Wo, WoT, c_s, c_z, dtype, s), "transpose Wo"));
   NT_TRY(hip_status(nt::launch_transpose(w->Wa, WaT, c_z, c_s, dtype, s), "transpose Wa"));
@@ -1230,8 +1316,12 @@ static nt_status block_backward_s(const nt_partition* p, const void* s_in, const
   // mean (formed inside the transition's gradient), transition, broadcast
   if (swiglu) {
     NT_TRY(hip_status(nt::launch_mean_backward(*p, g_m, g_z_out, G, W, s), "mean backward"));
-    NT_TRY(swiglu_transition_backward(p->cells, static_cast<const float*>(z), G, *w, *grads, c_z,
-                                      hidden, base + L.trans, s));
+    if (swiglu_fused)
+      NT_TRY(swiglu_transition_backward32(p, a, b, G, *w, *grads, c_z, hidden, base + L.trans,
+                                          s));
+    else
+      NT_TRY(swiglu_transition_backward(p->cells, static_cast<const float*>(z), G, *w, *grads,
+                                        c_z, hidden, base + L.trans, s));
   } else if (S == 1) {
     NT_TRY(transition_backward(p, z, nullptr, w->W1, w->W2, G, grads->W1, grads->W2, c_z, hidden,
                                dtype, base + L.trans, s, g_m, g_z_out));

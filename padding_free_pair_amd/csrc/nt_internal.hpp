@@ -193,6 +193,20 @@ hipError_t launch_wgrad_rc(const void* z, const void* Gb, const void* W1, const 
 // device, and its device address on the current device.
 constexpr size_t kStaticScratchBytes = size_t(16) << 20;
 hipError_t static_scratch(void** ptr);
+// ---- Fused SwiGLU transition gradient (nt_swiglu_bwd32.hip): c_z 128, hidden
+// a multiple of 128, bf16. From the fp32 projections a, b (the pair state is
+// formed per cell) and G (fp32 [cells, c_z], replaced by g_z): X2 and G2 get
+// x = LN(z) and G as bf16 pairs [cells, 2 c_z] (hi | lo), A, GU, GG get
+// A, g_u, g_g [cells, hidden] in bf16, lnpart the workgroups' dgamma and
+// dbeta sums [2][swiglu_bwd32_grid(cells)][c_z]. WdT is Wd transposed
+// [hidden, c_z]; WuT, WgT are Wu, Wg transposed [c_z, hidden].
+bool swiglu_bwd32_supported(int c_z, int hidden, nt_dtype dtype);
+int swiglu_bwd32_grid(int64_t cells);
+hipError_t launch_swiglu_bwd32(const nt_partition& p, const float* a, const float* b,
+                               const float* gamma, const float* beta, const void* Wg,
+                               const void* Wu, const void* WdT, const void* WuT, const void* WgT,
+                               float* G, void* X2, void* G2, void* A, void* GU, void* GG,
+                               float* lnpart, int hidden, float eps, hipStream_t stream);
 // ---- SwiGLU transition gradient pieces (nt_swiglu_bwd.hip), c_z 64 or 128
 // x = LN(z) row by row, fp32 (z fp32 [rows, c_z]).
 hipError_t launch_ln_rows(const float* z, const float* gamma, const float* beta, float* x,
