@@ -618,7 +618,9 @@ struct SwigluBwd32Ws {
 
 SwigluBwd32Ws swiglu_backward32_ws(int64_t cells, int c_z, int hidden) {
   SwigluBwd32Ws w;
-  const uint64_t ch = (uint64_t)cells * hidden, c2 = (uint64_t)cells * 2 * c_z;
+  // the kernel's outputs cover whole tiles
+  const uint64_t rows = (uint64_t)nt::swiglu_bwd32_rows(cells);
+  const uint64_t ch = rows * hidden, c2 = rows * 2 * c_z;
   const uint64_t wbytes = nt::align256((size_t)hidden * c_z * 2);
   const uint64_t mn2 = (uint64_t)2 * c_z * hidden;  // the [hi | lo] contractions
   uint64_t off = 0;
@@ -672,8 +674,9 @@ nt_status swiglu_transition_backward32(const nt_partition* p, const float* a, co
   NT_TRY(hip_status(nt::launch_sum_splits(lnpart + (size_t)grid * c_z, g.ln_beta, grid, c_z, s),
                     "dln_beta"));
   // dWd [c_z, hidden] = G^T A
+  const int64_t rows = nt::swiglu_bwd32_rows(p->cells);  // the chunk-major operands
   NT_TRY(hip_status(nt::launch_wgrad(G2, A, ctmp, wpart, p->cells, 2 * c_z, hidden, L.wsplits,
-                                     s),
+                                     s, rows),
                     "dW_down contraction"));
   NT_TRY(hip_status(nt::launch_sum_splits(ctmp, g.W_down, 2, cz_h, s), "dW_down halves"));
   // dWu^T, dWg^T [c_z, hidden] = x^T g_u, x^T g_g
@@ -681,7 +684,7 @@ nt_status swiglu_transition_backward32(const nt_partition* p, const float* a, co
       {GU, g.W_up, "dW_up"}, {GG, g.W_gate, "dW_gate"}};
   for (const auto& q : wg) {
     NT_TRY(hip_status(nt::launch_wgrad(X2, q.B, ctmp, wpart, p->cells, 2 * c_z, hidden,
-                                       L.wsplits, s),
+                                       L.wsplits, s, rows),
                       q.what));
     NT_TRY(hip_status(nt::launch_sum_splits(ctmp, ttmp, 2, cz_h, s), q.what));
     NT_TRY(hip_status(nt::launch_transpose(ttmp, q.out, c_z, hidden, NT_F32, s), q.what));

@@ -177,11 +177,13 @@ hipError_t launch_gemm_tn(const void* A, nt_dtype a_dtype, const void* B, nt_dty
 // C = sum of S partials [S][MN] in slice order (S = 0: C = 0).
 hipError_t launch_sum_splits(const float* part, float* C, int S, int64_t MN, hipStream_t stream);
 // Matrix-core form of launch_gemm_tn for bf16 A, B with M, N multiples of
-// 128; part holds wgrad_splits(K, M, N) * M * N floats.
+// 128; part holds wgrad_splits(K, M, N) * M * N floats. With chunked_rows
+// > 0 both operands are chunk-major: element (k, m) at
+// ((m / 32) chunked_rows + k) 32 + m % 32, chunked_rows >= K.
 bool wgrad_supported(int M, int N);
 int wgrad_splits(int64_t K, int M, int N);
 hipError_t launch_wgrad(const void* A, const void* B, float* C, float* part, int64_t K, int M,
-                        int N, int splits, hipStream_t stream);
+                        int N, int splits, hipStream_t stream, int64_t chunked_rows = 0);
 // Weight gradients recomputed from z and bf16(G) (bf16, c_z 128, hidden 512):
 // part holds 2 * wgrad_rc_slices(cells) * c_z * hidden floats.
 bool wgrad_rc_supported(int c_z, int hidden, nt_dtype dtype);
@@ -196,11 +198,17 @@ hipError_t static_scratch(void** ptr);
 // ---- Fused SwiGLU transition gradient (nt_swiglu_bwd32.hip): c_z 128, hidden
 // a multiple of 128, bf16. From the fp32 projections a, b (the pair state is
 // formed per cell) and G (fp32 [cells, c_z], replaced by g_z): X2 and G2 get
-// x = LN(z) and G as bf16 pairs [cells, 2 c_z] (hi | lo), A, GU, GG get
-// A, g_u, g_g [cells, hidden] in bf16, lnpart the workgroups' dgamma and
-// dbeta sums [2][swiglu_bwd32_grid(cells)][c_z]. WdT is Wd transposed
-// [hidden, c_z]; WuT, WgT are Wu, Wg transposed [c_z, hidden].
+// x = LN(z) and G as bf16 pairs (hi in columns 0 .. c_z - 1, lo in c_z ..
+// 2 c_z - 1), A, GU, GG get A, g_u, g_g (hidden columns) in bf16, all
+// chunk-major (column m of row k at ((m / 32) rows + k) 32 + m % 32, so a
+// wave's stores of a chunk are contiguous), with rows =
+// swiglu_bwd32_rows(cells) (whole tiles; the rows past the cells hold
+// garbage), lnpart the
+// workgroups' dgamma and dbeta sums [2][swiglu_bwd32_grid(cells)][c_z].
+// WdT is Wd transposed [hidden, c_z]; WuT, WgT are Wu, Wg transposed
+// [c_z, hidden].
 bool swiglu_bwd32_supported(int c_z, int hidden, nt_dtype dtype);
+int64_t swiglu_bwd32_rows(int64_t cells);
 int swiglu_bwd32_grid(int64_t cells);
 hipError_t launch_swiglu_bwd32(const nt_partition& p, const float* a, const float* b,
                                const float* gamma, const float* beta, const void* Wg,

@@ -20,19 +20,31 @@
 // as G's mean adjoint along a pair row, and their sums reach the percent
 // level of the weight gradients.)
 //
-// Layout (the forward kernel's): persistent workgroups of eight waves, two
-// per SIMD, 32 cells a wave; lane (l32, h) holds cell l32 of its wave and,
-// in an operand of k-step t, features 16 t + 8 h .. + 7. Per 32-unit chunk j:
+// Layout: persistent workgroups of four waves, one per SIMD (so a wave has
+// the whole register file: two sets of chunk results for the software
+// pipeline below), 32 cells a wave; lane (l32, h) holds cell l32 of its
+// wave and, in an operand of k-step t, features 16 t + 8 h .. + 7. Per
+// 32-unit chunk j:
 //   g^T, u^T = Wg[j], Wu[j] . x^T,  g_A^T = WdT[j] . bf16(G)^T  (k = features)
 //   g_x^T += WuT[:, j] . g_u^T + WgT[:, j] . g_g^T                (k = units)
 // with every fragment's weight rows in the bits-2-and-3-swapped order, so the
 // three results of a unit sit in the same lane (the adjoints are lane-local),
 // g_u and g_g pack lane-locally into the last products' operands, and g_x
 // lands in the layout of x (the LN adjoint is lane-local plus one exchange
-// with lane l32 + 32). The chunks' 40 weight fragments stream through a ring
-// of three LDS buffers, across tiles. The pair state is formed from the fp32
-// projections, z = a[row] + b[col] (Equation 3 inverted per lane), as in the
-// forward, and formed again for the LN adjoint at the tile's end.
+// with lane l32 + 32). Step j of a tile issues chunk j + 1's three products
+// beside chunk j's adjoints (independent work, so the vector instructions
+// issue under the matrix products), then chunk j's g_x products. The
+// chunks' 40 weight fragments stream through a ring of three LDS buffers,
+// across tiles. The pair state is formed from the fp32 projections,
+// z = a[row] + b[col] (Equation 3 inverted per lane), as in the forward,
+// and formed again for the LN adjoint at the tile's end. The bf16 outputs
+// are chunk-major (column m of row k at ((m / 32) rows + k) 32 + m % 32), so
+// the two stores of a wave's chunk cover 2 KiB of contiguous memory (in the
+// row-major layout each 16-byte store of a lane went to another row, and
+// the line writes came out 1.4 times the bytes), and padded to whole tiles,
+// so the stores need no guard (a guard inside the chunk loop splits it, and
+// the compiler then waits for every outstanding memory operation at the
+// join).
 //
 // dgamma and dbeta: each wave sums its 32 cells' terms with a
 // reduce-scatter over the lanes, the waves' sums are added in wave order and
@@ -45,14 +57,14 @@
 namespace nt {
 namespace {
 
-constexpr int kSbWaves = 8;  // two waves per SIMD
+constexpr int kSbWaves = 4;  // one wave per SIMD
 constexpr int kSbThreads = kSbWaves * 64;
 constexpr int kSbTile = kSbWaves * 32;  // cells per tile
 constexpr int kSbCz = 128, kSbKt = 8, kSbFb = 4;
 constexpr int kSbFrags = 5 * kSbKt * 64;  // 16-byte pieces per chunk (40 fragments)
 constexpr int kSbPer = kSbFrags / kSbThreads;
 constexpr int kSbGrid = 256;
-static_assert(kSbTile == kSampleIndexSpan, "a tile is one entry of the sample index");
+static_assert(kSampleIndexSpan % kSbTile == 0, "tiles nest in the sample index");
 static_assert(kSbFrags % kSbThreads == 0, "chunk staging splits evenly");
 
 __device__ __forceinline__ f32x16 sb_mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -77,7 +89,7 @@ __device__ __forceinline__ void sb_scatter_step(float (&v)[128], int l32) {
   }
 }
 
-__global__ __launch_bounds__(kSbThreads, 2) void k_swiglu_bwd32(
+__global__ __launch_bounds__(kSbThreads, 1) void k_swiglu_bwd32(
     const float* __restrict__ a, const float* __restrict__ b,
     const int64_t* __restrict__ pair_offsets, const int64_t* __restrict__ single_offsets,
     const int64_t* __restrict__ col_offsets, const int32_t* __restrict__ col_lengths,
@@ -93,6 +105,7 @@ __global__ __launch_bounds__(kSbThreads, 2) void k_swiglu_bwd32(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int nchunks = hidden / 32;
+  const int64_t rows = ntiles * kSbTile;  // rows of the chunk-major outputs
 
   // piece p of chunk j: fragment p / 64 (Wg, Wu, WdT by k-step; then WuT,
   // WgT by (feature block, k-step)), lane p % 64
@@ -138,7 +151,7 @@ __global__ __launch_bounds__(kSbThreads, 2) void k_swiglu_bwd32(
     const int64_t c0 = tile * kSbTile + wave * 32 + l32;
     const bool live = c0 < cells;
     const int64_t cell = live ? c0 : cells - 1;  // past the end: the last cell, not stored
-    int i = tile_sample[tile];
+    int i = tile_sample[tile * kSbTile / kSampleIndexSpan];
     while (pair_offsets[i + 1] <= cell) ++i;
     const int64_t m = col_lengths[i], local = cell - pair_offsets[i];
     const int64_t r = local / m;
@@ -194,10 +207,10 @@ __global__ __launch_bounds__(kSbThreads, 2) void k_swiglu_bwd32(
           xb[t][e] = (bf16)x;
           lo[e] = (bf16)(x - (float)xb[t][e]);
         }
-        if (live) {
-          *reinterpret_cast<bf16x8*>(X2 + cell * (2 * CZ) + 16 * t + 8 * h) = xb[t];
-          *reinterpret_cast<bf16x8*>(X2 + cell * (2 * CZ) + CZ + 16 * t + 8 * h) = lo;
-        }
+        *reinterpret_cast<bf16x8*>(X2 + ((t >> 1) * rows + c0) * 32 + 16 * (t & 1) + 8 * h) =
+            xb[t];
+        *reinterpret_cast<bf16x8*>(X2 + ((KT / 2 + (t >> 1)) * rows + c0) * 32 + 16 * (t & 1) +
+                                   8 * h) = lo;
       }
     }
     // ---- G as the bf16 operand of g_A, and hi + lo for dWd
@@ -213,57 +226,110 @@ __global__ __launch_bounds__(kSbThreads, 2) void k_swiglu_bwd32(
         gb[t][e] = (bf16)v;
         lo[e] = (bf16)(v - (float)gb[t][e]);
       }
-      if (live) {
-        *reinterpret_cast<bf16x8*>(G2 + cell * (2 * CZ) + 16 * t + 8 * h) = gb[t];
-        *reinterpret_cast<bf16x8*>(G2 + cell * (2 * CZ) + CZ + 16 * t + 8 * h) = lo;
-      }
+      *reinterpret_cast<bf16x8*>(G2 + ((t >> 1) * rows + c0) * 32 + 16 * (t & 1) + 8 * h) =
+          gb[t];
+      *reinterpret_cast<bf16x8*>(G2 + ((KT / 2 + (t >> 1)) * rows + c0) * 32 + 16 * (t & 1) +
+                                 8 * h) = lo;
     }
 
-    // ---- the chunks
+    // ---- the chunks, software-pipelined (see above)
     f32x16 gx[FB];
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb) gx[fb] = f32x16{};
-    for (int j = 0; j < nchunks; ++j) {
-      const bf16x8* wb = lane_frags((qb + j) % 3);
-      f32x16 gt = f32x16{}, up = f32x16{}, ga = f32x16{};
+    // chunk products: g^T, u^T (k = features of x) and g_A^T (of bf16 G)
+    auto prod = [&](const bf16x8* wb, f32x16& gt, f32x16& up, f32x16& ga) {
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
-        gt = sb_mfma(wb[64 * t], xb[t], gt);
-        up = sb_mfma(wb[64 * (KT + t)], xb[t], up);
-        ga = sb_mfma(wb[64 * (2 * KT + t)], gb[t], ga);
+        gt = sb_mfma(wb[64 * t], xb[t], t ? gt : f32x16{});
+        up = sb_mfma(wb[64 * (KT + t)], xb[t], t ? up : f32x16{});
+        ga = sb_mfma(wb[64 * (2 * KT + t)], gb[t], t ? ga : f32x16{});
       }
-      // element 8 s + e: unit 32 j + 16 s + 8 h + e of this lane's cell
-      bf16x8 gu[2], gg[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        bf16x8 av;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float g = gt[8 * s + e], u = up[8 * s + e], gA = ga[8 * s + e];
-          const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-g));
-          const float silu = g * sg;
-          av[e] = (bf16)(silu * u);
-          gu[s][e] = (bf16)(gA * silu);
-          gg[s][e] = (bf16)(gA * u * sg * (1.f + g * (1.f - sg)));
-        }
-        if (live) {
-          const int64_t o = cell * hidden + 32 * j + 16 * s + 8 * h;
-          *reinterpret_cast<bf16x8*>(Ab + o) = av;
-          *reinterpret_cast<bf16x8*>(GUb + o) = gu[s];
-          *reinterpret_cast<bf16x8*>(GGb + o) = gg[s];
-        }
+    };
+    // the adjoints of result element r (unit 32 j + 16 (r / 8) + 8 h + r % 8
+    // of the lane's cell)
+    auto adjoint = [&](int r, const f32x16& gt, const f32x16& up, const f32x16& ga,
+                       bf16x8 (&av)[2], bf16x8 (&gu)[2], bf16x8 (&gg)[2]) {
+      const float g = gt[r], u = up[r], gA = ga[r];
+      const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-g));
+      const float silu = g * sg;
+      av[r >> 3][r & 7] = (bf16)(silu * u);
+      gu[r >> 3][r & 7] = (bf16)(gA * silu);
+      gg[r >> 3][r & 7] = (bf16)(gA * u * sg * (1.f + g * (1.f - sg)));
+    };
+    // step j: chunk j + 1's products, each k-step followed by two elements'
+    // adjoints of chunk j (the issue order is pinned: left alone, the
+    // compiler puts all of the adjoints before the products), then chunk j's
+    // g_x products and its stores; then chunk j + 2 written into the buffer
+    // chunk j - 1 used and chunk j + 3 loaded. Fragments are read one group
+    // ahead of their products.
+    auto step = [&](int j, const f32x16& gc, const f32x16& uc, const f32x16& ac, f32x16& gn,
+                    f32x16& un, f32x16& an, bool next) {
+      const bf16x8* wn = lane_frags((qb + j + 1) % 3);
+      const bf16x8* wc = lane_frags((qb + j) % 3);
+      bf16x8 av[2], gu[2], gg[2];
+      bf16x8 f0{}, f1{}, f2{};
+      if (next) {
+        f0 = wn[0];
+        f1 = wn[64 * KT];
+        f2 = wn[64 * 2 * KT];
       }
 #pragma unroll
-      for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          gx[fb] = sb_mfma(wb[64 * (3 * KT + 2 * fb + s)], gu[s], gx[fb]);
-          gx[fb] = sb_mfma(wb[64 * (3 * KT + 2 * FB + 2 * fb + s)], gg[s], gx[fb]);
+      for (int t = 0; t < KT; ++t) {
+        bf16x8 n0{}, n1{}, n2{};
+        if (next && t + 1 < KT) {
+          n0 = wn[64 * (t + 1)];
+          n1 = wn[64 * (KT + t + 1)];
+          n2 = wn[64 * (2 * KT + t + 1)];
         }
+        if (next) {
+          gn = sb_mfma(f0, xb[t], t ? gn : f32x16{});
+          un = sb_mfma(f1, xb[t], t ? un : f32x16{});
+          an = sb_mfma(f2, gb[t], t ? an : f32x16{});
+        }
+        adjoint(2 * t, gc, uc, ac, av, gu, gg);
+        adjoint(2 * t + 1, gc, uc, ac, av, gu, gg);
+        __builtin_amdgcn_sched_barrier(0);
+        f0 = n0;
+        f1 = n1;
+        f2 = n2;
+      }
+      // g_x^T += WuT[:, j] g_u^T + WgT[:, j] g_g^T: fragment q = 2 fb + s of
+      // each, read one product ahead
+      bf16x8 pu = wc[64 * (3 * KT)], pg = wc[64 * (3 * KT + 2 * FB)];
+#pragma unroll
+      for (int q = 0; q < 2 * FB; ++q) {
+        bf16x8 nu{}, ng{};
+        if (q + 1 < 2 * FB) {
+          nu = wc[64 * (3 * KT + q + 1)];
+          ng = wc[64 * (3 * KT + 2 * FB + q + 1)];
+        }
+        gx[q >> 1] = sb_mfma(pu, gu[q & 1], gx[q >> 1]);
+        gx[q >> 1] = sb_mfma(pg, gg[q & 1], gx[q >> 1]);
+        if (q < 2) {
+          const int64_t o = ((int64_t)j * rows + c0) * 32 + 16 * q + 8 * h;
+          *reinterpret_cast<bf16x8*>(Ab + o) = av[q];
+          *reinterpret_cast<bf16x8*>(GUb + o) = gu[q];
+          *reinterpret_cast<bf16x8*>(GGb + o) = gg[q];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        pu = nu;
+        pg = ng;
+      }
       store_chunk((qb + j + 2) % 3, stg);
       load_chunk((j + 3) % nchunks, stg);
       __syncthreads();
+    };
+    f32x16 gA, uA, aA, gB, uB, aB;
+    prod(lane_frags(qb), gA, uA, aA);
+    int j = 0;
+    for (; j + 2 < nchunks; j += 2) {
+      step(j, gA, uA, aA, gB, uB, aB, true);
+      step(j + 1, gB, uB, aB, gA, uA, aA, true);
     }
+    step(j, gA, uA, aA, gB, uB, aB, true);  // j = nchunks - 2
+    // the last chunk: its adjoints and g_x products only; the ring moves on
+    // to the next tile's chunk 1 (its chunk 0 was written by the step above)
+    step(j + 1, gB, uB, aB, gA, uA, aA, false);
     qb = (qb + nchunks) % 3;
 
     // ---- LN's adjoint: element 8 (t % 2) + e of gx[t / 2] is feature 16 t + 8 h + e
@@ -354,6 +420,10 @@ __global__ __launch_bounds__(kSbThreads, 2) void k_swiglu_bwd32(
 bool swiglu_bwd32_supported(int c_z, int hidden, nt_dtype dtype) {
   // hidden a multiple of 128: the weight contractions take 128 x 128 tiles
   return dtype == NT_BF16 && c_z == kSbCz && hidden > 0 && hidden % 128 == 0;
+}
+
+int64_t swiglu_bwd32_rows(int64_t cells) {
+  return (cells + kSbTile - 1) / kSbTile * kSbTile;
 }
 
 int swiglu_bwd32_grid(int64_t cells) {

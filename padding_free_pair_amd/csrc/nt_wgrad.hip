@@ -33,10 +33,14 @@ __device__ __forceinline__ f32x16 wg_mfma(const bf16x8& a, const bf16x8& b, cons
 // kWgK. Threads 0..127 stage A, 128..255 stage B: thread (bk, bm) of its half
 // moves the 8 x 8 block at rows 8 bk.., columns 8 bm.. of the step's 64 x 128
 // operand tile. Waves own 64 x 64 quadrants of the C tile.
+// CHUNKED: both operands in the chunk-major layout, element (k, m) at
+// ((m / 32) rows + k) 32 + m % 32 (rows >= K: 32-column chunks of rows).
+template <bool CHUNKED>
 __global__ __launch_bounds__(kWgThreads) void k_wgrad(const bf16* __restrict__ A,
                                                       const bf16* __restrict__ B,
                                                       float* __restrict__ part, int64_t K,
-                                                      int M, int N, int64_t kchunk) {
+                                                      int M, int N, int64_t kchunk,
+                                                      int64_t rows) {
   __shared__ bf16x8 lds[2][kWgTile * kWgPitch / 8];  // [operand][m * pitch + k] in 8s
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
@@ -49,9 +53,10 @@ __global__ __launch_bounds__(kWgThreads) void k_wgrad(const bf16* __restrict__ A
   const int op = tid >> 7;              // 0: A, 1: B
   const int st = tid & 127;
   const int bm = st & 15, bk = st >> 4;  // 16 column blocks x 8 row blocks
-  const bf16* src = op == 0 ? A + (int64_t)tm * kWgTile + 8 * bm
-                            : B + (int64_t)tn * kWgTile + 8 * bm;
-  const int ld = op == 0 ? M : N;
+  const int col = (op == 0 ? tm : tn) * kWgTile + 8 * bm;  // first column of the block
+  const bf16* src = CHUNKED ? (op == 0 ? A : B) + ((int64_t)(col >> 5) * rows) * 32 + (col & 31)
+                            : (op == 0 ? A : B) + col;
+  const int ld = CHUNKED ? 32 : (op == 0 ? M : N);
   bf16* dst = reinterpret_cast<bf16*>(lds[op]);
 
   const int wm = wave & 1, wn = wave >> 1;  // quadrant of the C tile
@@ -361,14 +366,15 @@ int wgrad_splits(int64_t K, int M, int N) {
 bool wgrad_supported(int M, int N) { return M % kWgTile == 0 && N % kWgTile == 0; }
 
 hipError_t launch_wgrad(const void* A, const void* B, float* C, float* part, int64_t K, int M,
-                        int N, int splits, hipStream_t stream) {
+                        int N, int splits, hipStream_t stream, int64_t chunked_rows) {
   if (K == 0) return launch_sum_splits(part, C, 0, (int64_t)M * N, stream);
   int64_t kchunk = (K + splits - 1) / splits;
   kchunk = (kchunk + kWgK - 1) / kWgK * kWgK;
   const int64_t S = (K + kchunk - 1) / kchunk;
   const dim3 grid((unsigned)((M / kWgTile) * (N / kWgTile)), (unsigned)S);
-  hipLaunchKernelGGL(k_wgrad, grid, dim3(kWgThreads), 0, stream, static_cast<const bf16*>(A),
-                     static_cast<const bf16*>(B), part, K, M, N, kchunk);
+  auto kern = chunked_rows > 0 ? k_wgrad<true> : k_wgrad<false>;
+  hipLaunchKernelGGL(kern, grid, dim3(kWgThreads), 0, stream, static_cast<const bf16*>(A),
+                     static_cast<const bf16*>(B), part, K, M, N, kchunk, chunked_rows);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_sum_splits(part, C, (int)S, (int64_t)M * N, stream);
