@@ -168,6 +168,54 @@ class TrainRunner:
         return loss, g
 
 
+class SwigluTrainRunner:
+    """The same training step with the paper's own transition (the
+    pre-normalised SwiGLU of expansion four, Equation 1 with h o LN;
+    Appendix A.1; Table 1's program): every block is nt_pair_block_ex with
+    seeded SwiGLU-block weights of the workload's widths, then Equation 5
+    and nt_pair_block_backward_ex in reverse order."""
+
+    def __init__(self, x: pin.Inputs, torch, nt, packed: PackedRunner):
+        self.torch, self.nt, self.r = torch, nt, packed
+        rng = np.random.default_rng(78)
+        nb = len(x.weights)
+        self.w = [{k: dev(v, torch) for k, v in
+                   pin.draw_swiglu_weights(rng, x.c_s, x.c_z, x.hidden, x.dtype).items()}
+                  for _ in range(nb)]
+        tdt = torch.bfloat16
+        self.s = [packed.s0] + [torch.empty_like(packed.s0) for _ in range(nb)]
+        self.z = [torch.empty((packed.cells, x.c_z), dtype=tdt, device="cuda") for _ in range(nb)]
+        self.g = [torch.empty((packed.T, x.c_s), dtype=torch.float32, device="cuda")
+                  for _ in range(2)]
+        self.grads = [{k: torch.empty(v.shape, dtype=torch.float32, device="cuda")
+                       for k, v in w.items()} for w in self.w]
+        kind = nt.NT_TRANSITION_LN_SWIGLU
+        self.bws = torch.empty(max(nt.nt_block_backward_ex_workspace_bytes(
+            packed.p, kind, x.c_s, x.c_z, x.hidden, tdt), 1), dtype=torch.uint8, device="cuda")
+        self.lws = torch.empty(nt.nt_loss_workspace_bytes(packed.p), dtype=torch.uint8,
+                               device="cuda")
+
+    def forward(self):
+        nt, r = self.nt, self.r
+        p = nt.nt_make_partition(r.lengths, buffer=r.part_buf)
+        for k, w in enumerate(self.w):
+            nt.nt_pair_block_ex(p, self.s[k], w, s_out=self.s[k + 1], z_out=self.z[k],
+                                workspace=r.ws)
+        return p
+
+    def step(self):
+        nt = self.nt
+        p = self.forward()
+        loss, g, g_pz = nt.nt_pair_loss_eq5(p, self.s[-1], self.z[-1], workspace=self.lws)
+        for k in range(len(self.w) - 1, -1, -1):
+            out = self.g[k % 2]
+            nt.nt_pair_block_backward_ex(p, self.s[k], self.z[k], self.w[k], g,
+                                         g_pz if k == len(self.w) - 1 else None, g_s_in=out,
+                                         grads=self.grads[k], workspace=self.bws)
+            g = out
+        return loss, g
+
+
 def backward_rooflines(r: PackedRunner, reps: int) -> dict:
     """The transition's gradient on block 0's pair state (matrix-core act
     kernel plus the two weight-gradient contractions, one call), against
@@ -845,6 +893,19 @@ def main():
     log(f"train step {t_train * 1e3:.3f} ms -> {train['value']:.4g} cells/s per block")
     del tr
     torch.cuda.empty_cache()
+    swiglu_train = None
+    if x.dtype == "bf16" and x.c_z == 128 and x.hidden % 64 == 0:
+        sr = SwigluTrainRunner(x, torch, nt, r)
+        t_sf = time_steps(sr.forward, args.steps, args.warmup, torch)
+        t_st = time_steps(sr.step, max(2, args.steps // 4), 2, torch)
+        swiglu_train = {"value": r.cells * w.blocks / t_st, "unit": "pair cells/s per block",
+                        "ms_per_step": t_st * 1e3, "forward_ms": t_sf * 1e3,
+                        "step": "the paper's block (pre-normalised SwiGLU transition): forward "
+                                "of every block, Equation 5 loss, backward of every block"}
+        log(f"swiglu train step {t_st * 1e3:.3f} ms (forward {t_sf * 1e3:.3f} ms) -> "
+            f"{swiglu_train['value']:.4g} cells/s per block")
+        del sr
+        torch.cuda.empty_cache()
     dom = kern["transition"]
     roofline = {"bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
                 "unit": dom["unit"], "frac": dom["frac"],
@@ -872,6 +933,7 @@ def main():
         "kernels": kern,
         "hbm_ceiling": hbm_ceiling(torch),
         "train": train,
+        "swiglu_train": swiglu_train,
     }
 
     if not args.quick:

@@ -28,11 +28,17 @@ __device__ __forceinline__ f32x16 wg_mfma(const bf16x8& a, const bf16x8& b, cons
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// blockIdx.x: tile of C (tm, tn) = (x % tiles_m, x / tiles_m); blockIdx.y:
-// the K slice [y * kchunk, min(K, (y + 1) * kchunk)), kchunk a multiple of
-// kWgK. Threads 0..127 stage A, 128..255 stage B: thread (bk, bm) of its half
-// moves the 8 x 8 block at rows 8 bk.., columns 8 bm.. of the step's 64 x 128
-// operand tile. Waves own 64 x 64 quadrants of the C tile.
+// Workgroup b takes tile t and K slice y (the slice [y kchunk, min(K,
+// (y + 1) kchunk)), kchunk a multiple of kWgK), numbered so that the tiles
+// of one slice run on one XCD (workgroups go to the XCDs round robin, b to
+// XCD b mod 8): b = 8 (tiles q + t) + x with y = 8 q + x; they then read the
+// slice's rows through one L2 (numbered tile-fastest, the tiles of a slice
+// went to different XCDs and each fetched the slice from HBM: 2.7 times the
+// operand bytes). Workgroups with y >= S return. The tile of C is (tm, tn) =
+// (t % tiles_m, t / tiles_m). Threads 0..127 stage A, 128..255 stage B:
+// thread (bk, bm) of its half moves the 8 x 8 block at rows 8 bk..,
+// columns 8 bm.. of the step's 64 x 128 operand tile. Waves own 64 x 64
+// quadrants of the C tile.
 // CHUNKED: both operands in the chunk-major layout, element (k, m) at
 // ((m / 32) rows + k) 32 + m % 32 (rows >= K: 32-column chunks of rows).
 template <bool CHUNKED>
@@ -40,13 +46,16 @@ __global__ __launch_bounds__(kWgThreads) void k_wgrad(const bf16* __restrict__ A
                                                       const bf16* __restrict__ B,
                                                       float* __restrict__ part, int64_t K,
                                                       int M, int N, int64_t kchunk,
-                                                      int64_t rows) {
+                                                      int64_t rows, int S) {
   __shared__ bf16x8 lds[2][kWgTile * kWgPitch / 8];  // [operand][m * pitch + k] in 8s
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int tiles_m = M / kWgTile;
-  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
-  const int64_t kb = (int64_t)blockIdx.y * kchunk;
+  const int tiles_m = M / kWgTile, tiles = tiles_m * (N / kWgTile);
+  const int q = blockIdx.x / 8, t = q % tiles;
+  const int y = (q / tiles) * 8 + blockIdx.x % 8;
+  if (y >= S) return;
+  const int tm = t % tiles_m, tn = t / tiles_m;
+  const int64_t kb = (int64_t)y * kchunk;
   const int64_t ke = kb + kchunk < K ? kb + kchunk : K;
 
   // staging role
@@ -102,7 +111,7 @@ __global__ __launch_bounds__(kWgThreads) void k_wgrad(const bf16* __restrict__ A
   }
   // partial tile: element r of block (i, j) is row 8 (r / 4) + 4 h + r % 4,
   // column l32 of that 32 x 32 block
-  float* out = part + (int64_t)blockIdx.y * M * N;
+  float* out = part + (int64_t)y * M * N;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -371,10 +380,12 @@ hipError_t launch_wgrad(const void* A, const void* B, float* C, float* part, int
   int64_t kchunk = (K + splits - 1) / splits;
   kchunk = (kchunk + kWgK - 1) / kWgK * kWgK;
   const int64_t S = (K + kchunk - 1) / kchunk;
-  const dim3 grid((unsigned)((M / kWgTile) * (N / kWgTile)), (unsigned)S);
+  const int64_t tiles = (int64_t)(M / kWgTile) * (N / kWgTile);
+  const int64_t grid = 8 * tiles * ((S + 7) / 8);
   auto kern = chunked_rows > 0 ? k_wgrad<true> : k_wgrad<false>;
-  hipLaunchKernelGGL(kern, grid, dim3(kWgThreads), 0, stream, static_cast<const bf16*>(A),
-                     static_cast<const bf16*>(B), part, K, M, N, kchunk, chunked_rows);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kWgThreads), 0, stream,
+                     static_cast<const bf16*>(A), static_cast<const bf16*>(B), part, K, M, N,
+                     kchunk, chunked_rows, (int)S);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_sum_splits(part, C, (int)S, (int64_t)M * N, stream);
