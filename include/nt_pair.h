@@ -530,10 +530,14 @@ nt_status nt_block_backward_ex_workspace_bytes(const nt_partition* p, int32_t ki
  *   dln_gamma = sum g_x xhat,  dln_beta = sum g_x,
  *   g_z = G + (g_xhat - mean(g_xhat) - xhat mean(g_xhat xhat)) / sqrt(var + ln_eps),
  *   g_xhat = g_x ln_gamma,  xhat = (z - mean) / sqrt(var + ln_eps),
- * with z re-formed in fp32 from the recomputed projections; the products
- * read x, A, g_u, g_g and G rounded to bf16 and accumulate in fp32. The
- * weight gradients are sums over all cells in a fixed order. grads: the
- * kind's gradients, fp32, overwritten.
+ * with z re-formed in fp32 from the recomputed projections. At c_z 128,
+ * hidden a multiple of 128 and bf16, the gate, value and g_A products read
+ * x and G rounded to bf16 (the forward's operands) and the weight
+ * contractions read them as bf16 pairs hi + lo (unrounded to about 2^-17);
+ * other shapes read x and G unrounded in every product. A, g_u and g_g are
+ * rounded to bf16; every product accumulates in fp32. The weight
+ * gradients are sums over all cells in a fixed order. grads: the kind's
+ * gradients, fp32, overwritten.
  */
 nt_status nt_pair_block_backward_ex(const nt_partition* p, const void* s_in, const void* z_out,
                                     const nt_block_params* w, const float* g_s_out,
