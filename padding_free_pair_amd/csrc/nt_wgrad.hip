@@ -9,10 +9,12 @@
 // tile of C over one slice of K and writes an fp32 partial tile; the slices
 // are then added in order (k_sum_splits in nt_backward.hip), so the result is
 // deterministic. Both operands arrive cell-major (K outermost), while a
-// 32x32x16 MFMA operand wants 8 consecutive k per lane, so each thread loads
-// an 8 (k) x 8 (m) block with eight 16-byte row loads, transposes it in
-// registers and writes eight 16-byte k-runs into LDS ([m][k] layout); the
-// fragment reads are then plain 16-byte LDS reads.
+// 32x32x16 MFMA operand wants 8 values of k per lane: the step's 64 x 128
+// rows of each operand are copied as they are into LDS ([k][m]), and the
+// fragments are read with gfx950's transposing LDS read (ds_read_b64_tr_b16,
+// two reads a fragment; both operands take the same k order within a step,
+// so the contraction is unchanged). The next step's rows are loaded while
+// the current step's products run, into the other of two LDS buffers.
 #include "nt_device.hpp"
 #include "nt_internal.hpp"
 
@@ -22,7 +24,19 @@ namespace {
 constexpr int kWgThreads = 256;
 constexpr int kWgTile = 128;   // C tile edge
 constexpr int kWgK = 64;       // k per step
-constexpr int kWgPitch = kWgK + 8;  // LDS row pitch in elements (144 bytes)
+constexpr int kWgRow = kWgTile + 8;  // LDS row pitch in elements (272 bytes)
+
+typedef short wg_i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 wg_bf16x4 __attribute__((ext_vector_type(4)));
+
+// Four bf16 by the transposing LDS read (within each 16 lanes, lane j's
+// element e is element j mod 4 of the 8 bytes at the address of lane
+// 4 e + j / 4); p is this lane's 8-byte address.
+__device__ __forceinline__ wg_bf16x4 wg_read_tr(const bf16* p) {
+  const wg_i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) wg_i16x4*)(p));
+  return __builtin_bit_cast(wg_bf16x4, v);
+}
 
 __device__ __forceinline__ f32x16 wg_mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -35,19 +49,17 @@ __device__ __forceinline__ f32x16 wg_mfma(const bf16x8& a, const bf16x8& b, cons
 // slice's rows through one L2 (numbered tile-fastest, the tiles of a slice
 // went to different XCDs and each fetched the slice from HBM: 2.7 times the
 // operand bytes). Workgroups with y >= S return. The tile of C is (tm, tn) =
-// (t % tiles_m, t / tiles_m). Threads 0..127 stage A, 128..255 stage B:
-// thread (bk, bm) of its half moves the 8 x 8 block at rows 8 bk..,
-// columns 8 bm.. of the step's 64 x 128 operand tile. Waves own 64 x 64
-// quadrants of the C tile.
+// (t % tiles_m, t / tiles_m); waves own 64 x 64 quadrants of it. Each thread
+// stages four 16-byte pieces of each operand per step.
 // CHUNKED: both operands in the chunk-major layout, element (k, m) at
 // ((m / 32) rows + k) 32 + m % 32 (rows >= K: 32-column chunks of rows).
 template <bool CHUNKED>
-__global__ __launch_bounds__(kWgThreads) void k_wgrad(const bf16* __restrict__ A,
-                                                      const bf16* __restrict__ B,
-                                                      float* __restrict__ part, int64_t K,
-                                                      int M, int N, int64_t kchunk,
-                                                      int64_t rows, int S) {
-  __shared__ bf16x8 lds[2][kWgTile * kWgPitch / 8];  // [operand][m * pitch + k] in 8s
+__global__ __launch_bounds__(kWgThreads, 2) void k_wgrad(const bf16* __restrict__ A,
+                                                         const bf16* __restrict__ B,
+                                                         float* __restrict__ part, int64_t K,
+                                                         int M, int N, int64_t kchunk,
+                                                         int64_t rows, int S) {
+  __shared__ bf16 lds[2][2][kWgK * kWgRow];  // [buffer][operand][k * pitch + m]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int tiles_m = M / kWgTile, tiles = tiles_m * (N / kWgTile);
@@ -58,15 +70,49 @@ __global__ __launch_bounds__(kWgThreads) void k_wgrad(const bf16* __restrict__ A
   const int64_t kb = (int64_t)y * kchunk;
   const int64_t ke = kb + kchunk < K ? kb + kchunk : K;
 
-  // staging role
-  const int op = tid >> 7;              // 0: A, 1: B
-  const int st = tid & 127;
-  const int bm = st & 15, bk = st >> 4;  // 16 column blocks x 8 row blocks
-  const int col = (op == 0 ? tm : tn) * kWgTile + 8 * bm;  // first column of the block
-  const bf16* src = CHUNKED ? (op == 0 ? A : B) + ((int64_t)(col >> 5) * rows) * 32 + (col & 31)
-                            : (op == 0 ? A : B) + col;
-  const int ld = CHUNKED ? 32 : (op == 0 ? M : N);
-  bf16* dst = reinterpret_cast<bf16*>(lds[op]);
+  // staging: piece p = tid + 256 u of an operand's 64 x 128 step tile is row
+  // pk[u], columns pm[u] .. + 7 (chunk-major: 64 contiguous bytes a row and
+  // chunk, so four lanes cover a chunk's row; row-major: 16 lanes a row)
+  int pk[4], pm[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int p = tid + kWgThreads * u;
+    if (CHUNKED) {
+      pk[u] = (p & 255) >> 2;
+      pm[u] = 32 * (p >> 8) + 8 * (p & 3);
+    } else {
+      pk[u] = p >> 4;
+      pm[u] = 8 * (p & 15);
+    }
+  }
+  const bf16* base[2] = {A, B};
+  const int col0[2] = {tm * kWgTile, tn * kWgTile};
+  const int ld[2] = {M, N};
+  auto gaddr = [&](int op, int64_t k, int m) -> const bf16* {
+    const int c = col0[op] + m;
+    return CHUNKED ? base[op] + (((int64_t)(c >> 5) * rows + k) * 32 + (c & 31))
+                   : base[op] + (k * ld[op] + c);
+  };
+  bf16x8 nxt[2][4];
+  // the rows of the step at k0; rows past the slice read its last row (in
+  // bounds, no branch) and are zeroed
+  auto fetch = [&](int64_t k0) {
+#pragma unroll
+    for (int op = 0; op < 2; ++op)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t k = k0 + pk[u];
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(gaddr(op, k < ke ? k : ke - 1, pm[u]));
+        nxt[op][u] = k < ke ? v : bf16x8{};
+      }
+  };
+  auto put = [&](int bb) {
+#pragma unroll
+    for (int op = 0; op < 2; ++op)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        *reinterpret_cast<bf16x8*>(&lds[bb][op][pk[u] * kWgRow + pm[u]]) = nxt[op][u];
+  };
 
   const int wm = wave & 1, wn = wave >> 1;  // quadrant of the C tile
   f32x16 acc[2][2];
@@ -74,40 +120,50 @@ __global__ __launch_bounds__(kWgThreads) void k_wgrad(const bf16* __restrict__ A
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  // this lane's transposing-read address: within its 16-lane group (columns
+  // 16 (g mod 2) .., rows 4 h ..), lane l' points at row 4 h + l' / 4,
+  // column + 4 (l' mod 4); the fragment of a 32-column block then holds, for
+  // column l32, rows 4 h + (0..3) and 8 + 4 h + (0..3) of a 16-row k-step
+  const int lq = lane & 15, lg = lane >> 4;
+  const int tr_off = (4 * h + (lq >> 2)) * kWgRow + 16 * (lg & 1) + 4 * (lq & 3);
+  auto frag = [&](const bf16* T, int s, int m0) -> bf16x8 {
+    const int off = tr_off + 16 * s * kWgRow + m0;
+    const wg_bf16x4 v0 = wg_read_tr(T + off);
+    const wg_bf16x4 v1 = wg_read_tr(T + off + 8 * kWgRow);
+    bf16x8 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = v0[e];
+      f[4 + e] = v1[e];
+    }
+    return f;
+  };
 
+  fetch(kb);
+  put(0);
+  __syncthreads();
+  int bb = 0;
   for (int64_t k0 = kb; k0 < ke; k0 += kWgK) {
-    bf16x8 rows[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t k = k0 + 8 * bk + i;
-      rows[i] = k < ke ? *reinterpret_cast<const bf16x8*>(src + k * ld) : bf16x8{};
-    }
-    __syncthreads();  // the previous step's fragment reads are done
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bf16x8 col;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) col[i] = rows[i][e];
-      *reinterpret_cast<bf16x8*>(dst + (8 * bm + e) * kWgPitch + 8 * bk) = col;
-    }
-    __syncthreads();
+    fetch(k0 + kWgK);  // past the slice: clamped reads, not used
+    const bf16* TA = lds[bb][0];
+    const bf16* TB = lds[bb][1];
 #pragma unroll
     for (int s = 0; s < kWgK / 16; ++s) {
       bf16x8 af[2], bfr[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int m = 64 * wm + 32 * i + l32;
-        af[i] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(lds[0]) +
-                                                 m * kWgPitch + 16 * s + 8 * h);
-        const int n = 64 * wn + 32 * i + l32;
-        bfr[i] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(lds[1]) +
-                                                  n * kWgPitch + 16 * s + 8 * h);
+        af[i] = frag(TA, s, 64 * wm + 32 * i);
+        bfr[i] = frag(TB, s, 64 * wn + 32 * i);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = wg_mfma(af[i], bfr[j], acc[i][j]);
     }
+    // the other buffer was last read in the previous step, before its barrier
+    put(bb ^ 1);
+    __syncthreads();
+    bb ^= 1;
   }
   // partial tile: element r of block (i, j) is row 8 (r / 4) + 4 h + r % 4,
   // column l32 of that 32 x 32 block
