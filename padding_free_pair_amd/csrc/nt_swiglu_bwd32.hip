@@ -162,6 +162,14 @@ __global__ __launch_bounds__(kSbThreads, 1) void k_swiglu_bwd32(
     int ao = 8 * h;
     asm volatile("" : "+v"(ao));
 
+    // G's loads go out first, beside the gathers below: issued after LN
+    // and the x stores, their latency added to the gathers'
+    f32x4 gv[KT][2];
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        gv[t][q] = *reinterpret_cast<const f32x4*>(G + cell * CZ + 16 * t + 8 * h + 4 * q);
     // ---- x = LN(z) (bf16 operand, and hi + lo for the weight gradients)
     bf16x8 xb[KT];
     float mu, rstd;
@@ -217,12 +225,10 @@ __global__ __launch_bounds__(kSbThreads, 1) void k_swiglu_bwd32(
     bf16x8 gb[KT];
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-      const f32x4 v0 = *reinterpret_cast<const f32x4*>(G + cell * CZ + 16 * t + 8 * h);
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(G + cell * CZ + 16 * t + 8 * h + 4);
       bf16x8 lo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = e < 4 ? v0[e] : v1[e - 4];
+        const float v = gv[t][e >> 2][e & 3];
         gb[t][e] = (bf16)v;
         lo[e] = (bf16)(v - (float)gb[t][e]);
       }
@@ -332,7 +338,14 @@ __global__ __launch_bounds__(kSbThreads, 1) void k_swiglu_bwd32(
     step(j + 1, gB, uB, aB, gA, uA, aA, false);
     qb = (qb + nchunks) % 3;
 
-    // ---- LN's adjoint: element 8 (t % 2) + e of gx[t / 2] is feature 16 t + 8 h + e
+    // ---- LN's adjoint: element 8 (t % 2) + e of gx[t / 2] is feature 16 t + 8 h + e.
+    // G (the residual) and the pair state's singles are loaded again, all at
+    // once
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        gv[t][q] = *reinterpret_cast<const f32x4*>(G + cell * CZ + 16 * t + 8 * h + 4 * q);
     float xh[KT][8];
 #pragma unroll
     for (int t = 0; t < KT; ++t)
@@ -363,13 +376,11 @@ __global__ __launch_bounds__(kSbThreads, 1) void k_swiglu_bwd32(
       const f32x4 g0 = *reinterpret_cast<const f32x4*>(gamma + ao + 16 * t);
       const f32x4 g1 = *reinterpret_cast<const f32x4*>(gamma + ao + 16 * t + 4);
       float* gp = G + cell * CZ + 16 * t + 8 * h;
-      const f32x4 v0 = *reinterpret_cast<const f32x4*>(gp);
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(gp + 4);
       f32x4 o0, o1;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float gxh = gx[t >> 1][8 * (t & 1) + e] * (e < 4 ? g0[e] : g1[e - 4]);
-        const float gz = (e < 4 ? v0[e] : v1[e - 4]) + rstd * (gxh - m1 - xh[t][e] * m2);
+        const float gz = gv[t][e >> 2][e & 3] + rstd * (gxh - m1 - xh[t][e] * m2);
         if (e < 4) o0[e] = gz; else o1[e - 4] = gz;
       }
       if (live) {
