@@ -42,9 +42,12 @@ COMMON = [
 #   work; in the AGPR form the compiler also moved its long-lived
 #   accumulators between AGPRs and VGPRs every 64-cell block (192 moves per
 #   64 products).
+# - The fused SwiGLU gradient reads every chunk's three results in VALU
+#   work (its x and G operands are placed in AGPRs instead).
 FILE_FLAGS = {
     "nt_transition_ws.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "nt_wgrad.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "nt_swiglu_bwd32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

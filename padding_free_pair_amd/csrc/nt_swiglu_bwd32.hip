@@ -238,6 +238,15 @@ __global__ __launch_bounds__(kSbThreads, 1) void k_swiglu_bwd32(
                                  8 * h) = lo;
     }
 
+    // the x and G operands wait in AGPRs (the products read them there), so
+    // the chunk results stay in VGPRs for the adjoints (the file is built
+    // with the VGPR form of the products): 29 instead of 48 moves between
+    // the two register files a chunk, 1% faster
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      asm volatile("" : "+a"(xb[t]));
+      asm volatile("" : "+a"(gb[t]));
+    }
     // ---- the chunks, software-pipelined (see above)
     f32x16 gx[FB];
 #pragma unroll
