@@ -180,6 +180,9 @@ def test_swiglu_block_full_size_long_square(nt):
     ([7, 0, 12, 1, 5], 64, 128, 512, True),
     ([9, 20, 13], 384, 128, 512, False),     # the pages' widths
     ([9, 40, 2], 128, 64, 128, True),
+    ([5, 33, 17], 64, 128, 256, True),       # fused gradient, 8 chunks
+    ([3, 40, 11], 64, 128, 1024, False),     # fused gradient, 32 chunks
+    ([9, 20], 64, 128, 192, True),           # hidden not a multiple of 128: composed gradient
 ])
 def test_swiglu_block_backward(nt, lengths, c_s, c_z, hidden, with_gz):
     announce(f"swiglu block backward {lengths} c_s={c_s} c_z={c_z} gz={with_gz}")
@@ -264,6 +267,29 @@ def test_swiglu_block_backward_full_size(nt):
     for k in pin.SWIGLU_NAMES:
         e = scaled_max_err(grads[k].cpu().numpy(), ref[ORACLE_KEYS.get(k, k)])
         assert e <= TOL["bf16"], (k, e)
+
+
+def test_swiglu_block_backward_deterministic(nt):
+    """Two calls on the same inputs give the same bits: the LN parameters'
+    sums over the cells run in a fixed order (per-workgroup sums over a
+    fixed grid, then the workgroups in order), as do the weight
+    contractions' slices."""
+    L = [40, 3, 130, 0, 77]
+    announce(f"swiglu block backward deterministic {L}")
+    x = pin.make_swiglu_inputs(L, 64, 128, 512, "bf16", seed=21)
+    rng = np.random.default_rng(22)
+    gs = _f32(rng.standard_normal((sum(L), 64)))
+    gz = _f32(rng.standard_normal((int(np.square(L).sum()), 128)))
+    p = nt.nt_make_partition(L)
+    wd = weights_to_dev(x.weights[0], torch)
+    sd = to_dev(x.s, torch)
+    _, z_out = nt.nt_pair_block_ex(p, sd, wd)
+    g1, r1 = nt.nt_pair_block_backward_ex(p, sd, z_out, wd, gs, gz)
+    g2, r2 = nt.nt_pair_block_backward_ex(p, sd, z_out, wd, gs, gz)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(g1.cpu().numpy(), g2.cpu().numpy())
+    for k in r1:
+        np.testing.assert_array_equal(r1[k].cpu().numpy(), r2[k].cpu().numpy(), err_msg=k)
 
 
 def test_swiglu_block_backward_empty_batch(nt):
