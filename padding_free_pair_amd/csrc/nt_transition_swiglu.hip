@@ -290,12 +290,13 @@ __global__ __launch_bounds__(kSgWaves * 64, 2) void k_transition_swiglu(
 // pair state, so the residual costs nothing at the end.
 //
 // Persistent: a workgroup per CU walks tiles of TILE cells. The weights
-// stream through a ring of three LDS buffers, chunk after chunk and across
-// tiles (the chunks repeat), in a software pipeline: step j runs the gate
-// and value products of chunk j + 1 beside silu of chunk j (independent,
-// so the vector work issues under the matrix products; sg32_interleave
-// fixes that order), then chunk j's down product, writes chunk j + 2 into
-// the buffer chunk j - 1 used and loads chunk j + 3.
+// stream through a ring of LDS buffers, chunk after chunk and across tiles
+// (the chunks repeat), in a software pipeline: step j runs the gate and
+// value products of chunk j + 1 beside silu of chunk j (independent, so the
+// vector work issues under the matrix products), then chunk j's down
+// product, in fixed issue groups that read each weight fragment two
+// products before its use; it then writes the chunk staged in registers
+// into the ring and loads the next one from memory.
 template <int NB, int WAVES>
 struct Sg32 {
   static constexpr int CZ = 128, KT = 8, FB = 4;
@@ -306,26 +307,6 @@ struct Sg32 {
   static_assert(FRAGS % THREADS == 0, "chunk staging splits evenly");
   static_assert(kSampleIndexSpan % TILE == 0, "tiles nest in the sample index");
 };
-
-// Issue order of one pipeline step (the compiler would otherwise put all of
-// silu's vector work before the products): each matrix product of the gate
-// and value chunk is followed by one LDS fragment read and six vector
-// instructions of silu, then the down product's MFMAs each take one more.
-template <int NB>
-__device__ __forceinline__ void sg32_interleave() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
-#pragma unroll
-  for (int i = 0; i < 16 * NB; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-  }
-#pragma unroll
-  for (int i = 0; i < 8 * NB; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
-  }
-}
 
 __device__ __forceinline__ int ws32_perm(int rho) {
   return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
@@ -343,7 +324,14 @@ __global__ __launch_bounds__(WAVES * 64, NB == 1 ? 2 : 1) void k_swiglu32(
   using C = Sg32<NB, WAVES>;
   constexpr int CZ = C::CZ, KT = C::KT, FB = C::FB, PER = C::PER;
   constexpr int WCELLS = 32 * NB;  // cells of one wave
-  __shared__ bf16x8 wbuf[3][C::FRAGS];
+  // LDS ring of weight chunks. Fused form: five buffers, a chunk written
+  // three steps before its first use and a barrier every other step. The
+  // unfused form's z prologue has no registers to spare for the longer lead
+  // (it would spill): three buffers, a lead of two, a barrier every step.
+  // Either way a buffer is rewritten only after a barrier that follows its
+  // last read, and first read only after a barrier that follows its write.
+  constexpr int RING = FUSED ? 5 : 3, LEAD = FUSED ? 3 : 2;
+  __shared__ bf16x8 wbuf[RING][C::FRAGS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int nchunks = hidden / 32;  // even, >= 2
@@ -490,60 +478,104 @@ __global__ __launch_bounds__(WAVES * 64, NB == 1 ? 2 : 1) void k_swiglu32(
   };
   auto p3 = [&](const bf16x8* wb, const bf16x8 (&af)[NB][2]) {
 #pragma unroll
-    for (int fb = 0; fb < FB; ++fb)
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int fb = 0; fb < FB; ++fb) {
         const bf16x8 a3 = wb[64 * (2 * KT + 2 * fb + s)];
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) y[cb][fb] = sg32_mfma(a3, af[cb][s], y[cb][fb]);
       }
   };
 
-  // ring state at a tile's start: chunks 0 and 1 in buffers qb and qb + 1
-  // (mod 3), chunk 2 in stg
+  // ring state at a tile's start: chunks 0 .. LEAD - 1 in buffers qb, qb + 1,
+  // ... (mod RING), chunk LEAD in stg
   bf16x8 stg[PER];
-  load_chunk(0, stg);
-  store_chunk(0, stg);
-  load_chunk(1, stg);
-  store_chunk(1, stg);
-  load_chunk(2 % nchunks, stg);
+#pragma unroll
+  for (int c = 0; c < LEAD; ++c) {
+    load_chunk(c % nchunks, stg);
+    store_chunk(c, stg);
+  }
+  load_chunk(LEAD % nchunks, stg);
   int64_t tile = blockIdx.x;
   __syncthreads();
   int qb = 0;
   f32x16 gA[NB], uA[NB], gB[NB], uB[NB];
   // step j of the tile: chunk j + 1's gate and value products, silu and the
-  // down product of chunk j, then chunk j + 2 written and chunk j + 3 loaded
+  // down product of chunk j, then chunk j + LEAD written and chunk
+  // j + LEAD + 1 loaded; sync: this step ends at a barrier
   auto step = [&](int j, const f32x16 (&gc)[NB], const f32x16 (&uc)[NB], f32x16 (&gn)[NB],
-                  f32x16 (&un)[NB]) {
-    p12(lane_frags((qb + j + 1) % 3), gn, un);
+                  f32x16 (&un)[NB], bool sync) {
+    // 24 issue groups: 0..15 the gate and value products of chunk j + 1
+    // (k-step i / 2, gate for even i), 16..23 chunk j's down product (k-step
+    // (i - 16) / 4, feature block i % 4). Group i issues its product, the
+    // LDS read of group i + 2's fragment and, in groups 0..15, silu of one
+    // element of chunk j.
+    const bf16x8* wn = lane_frags((qb + j + 1) % RING);
+    const bf16x8* wc = lane_frags((qb + j) % RING);
+    auto frag = [&](int i) -> bf16x8 {
+      return i < 16 ? wn[64 * ((i & 1) * KT + (i >> 1))]
+                    : wc[64 * (2 * KT + 2 * ((i - 16) & 3) + ((i - 16) >> 2))];
+    };
+    bf16x8 f0 = frag(0), f1 = frag(1);
     bf16x8 af[NB][2];
-    silu(gc, uc, af);
-    p3(lane_frags((qb + j) % 3), af);
-    sg32_interleave<NB>();
-    store_chunk((qb + j + 2) % 3, stg);
-    load_chunk((j + 3) % nchunks, stg);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 24; ++i) {
+      bf16x8 f2{};
+      if (i + 2 < 24) f2 = frag(i + 2);
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        if (i < 16) {
+          const int t = i >> 1;
+          if (i & 1)
+            un[cb] = sg32_mfma(f0, xb[cb][t], t ? un[cb] : f32x16{});
+          else
+            gn[cb] = sg32_mfma(f0, xb[cb][t], t ? gn[cb] : f32x16{});
+        } else {
+          const int k = i - 16;
+          y[cb][k & 3] = sg32_mfma(f0, af[cb][k >> 2], y[cb][k & 3]);
+        }
+      }
+      if (i < 16) {
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+          const float g = gc[cb][i];
+          af[cb][i >> 3][i & 7] =
+              (bf16)(g * uc[cb][i] * __builtin_amdgcn_rcpf(1.f + __expf(-g)));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f0 = f1;
+      f1 = f2;
+    }
+    store_chunk((qb + j + LEAD) % RING, stg);
+    load_chunk((j + LEAD + 1) % nchunks, stg);
+    if (sync || RING == 3)
+      __syncthreads();
+    else
+      __builtin_amdgcn_sched_barrier(0);
   };
   for (; tile < ntiles; tile += gridDim.x) {
     prologue(tile);
     p12(lane_frags(qb), gA, uA);
     int j = 0;
     for (; j + 2 < nchunks; j += 2) {
-      step(j, gA, uA, gB, uB);
-      step(j + 1, gB, uB, gA, uA);
+      step(j, gA, uA, gB, uB, false);  // j is even
+      step(j + 1, gB, uB, gA, uA, true);
     }
-    step(j, gA, uA, gB, uB);  // j = nchunks - 2
+    step(j, gA, uA, gB, uB, false);  // j = nchunks - 2
     {
-      // the last chunk's silu and down product; the ring moves on to the
-      // next tile's chunk 1 (its chunk 0 was written by the step above)
+      // the last chunk's silu and down product (an odd step: a barrier);
+      // the ring moves on to the next tile's chunk LEAD - 1 (its earlier
+      // chunks were written by the steps above)
       bf16x8 af[NB][2];
       silu(gB, uB, af);
-      p3(lane_frags((qb + j + 1) % 3), af);
-      store_chunk((qb + j + 3) % 3, stg);
-      load_chunk((j + 4) % nchunks, stg);
+      p3(lane_frags((qb + j + 1) % RING), af);
+      store_chunk((qb + j + 1 + LEAD) % RING, stg);
+      load_chunk((j + 2 + LEAD) % nchunks, stg);
       __syncthreads();
     }
-    qb = (qb + nchunks) % 3;
+    qb = (qb + nchunks) % RING;
 
     // epilogue: y already holds the residual sum; one rounding, 16-byte stores
     const int64_t cell0 = tile * C::TILE + wave * WCELLS;
