@@ -324,13 +324,11 @@ __global__ __launch_bounds__(WAVES * 64, NB == 1 ? 2 : 1) void k_swiglu32(
   using C = Sg32<NB, WAVES>;
   constexpr int CZ = C::CZ, KT = C::KT, FB = C::FB, PER = C::PER;
   constexpr int WCELLS = 32 * NB;  // cells of one wave
-  // LDS ring of weight chunks. Fused form: five buffers, a chunk written
-  // three steps before its first use and a barrier every other step. The
-  // unfused form's z prologue has no registers to spare for the longer lead
-  // (it would spill): three buffers, a lead of two, a barrier every step.
-  // Either way a buffer is rewritten only after a barrier that follows its
-  // last read, and first read only after a barrier that follows its write.
-  constexpr int RING = FUSED ? 5 : 3, LEAD = FUSED ? 3 : 2;
+  // LDS ring of weight chunks: five buffers, a chunk written three steps
+  // before its first use, a barrier every other step. A buffer is rewritten
+  // only after a barrier that follows its last read, and first read only
+  // after a barrier that follows its write.
+  constexpr int RING = 5, LEAD = 3;
   __shared__ bf16x8 wbuf[RING][C::FRAGS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
@@ -430,6 +428,10 @@ __global__ __launch_bounds__(WAVES * 64, NB == 1 ? 2 : 1) void k_swiglu32(
         }
       q += __shfl_xor(q, 32);
       const float rstd = 1.f / sqrtf(q * (1.f / CZ) + eps);
+      // an opaque copy of the mean: z - mean is formed again below instead
+      // of keeping the variance pass's 64 differences beside y
+      float mu2 = mu;
+      asm volatile("" : "+v"(mu2));
       // the affine pair is read per tile: an opaque offset keeps the compiler
       // from hoisting these loads out of the tile loop into 128 registers
       int ao = 8 * h;
@@ -442,8 +444,8 @@ __global__ __launch_bounds__(WAVES * 64, NB == 1 ? 2 : 1) void k_swiglu32(
         const f32x4 b1 = *reinterpret_cast<const f32x4*>(beta + ao + 16 * t + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          xb[cb][t][e] = (bf16)((zf[t][e] - mu) * rstd * g0[e] + b0[e]);
-          xb[cb][t][4 + e] = (bf16)((zf[t][4 + e] - mu) * rstd * g1[e] + b1[e]);
+          xb[cb][t][e] = (bf16)((zf[t][e] - mu2) * rstd * g0[e] + b0[e]);
+          xb[cb][t][4 + e] = (bf16)((zf[t][4 + e] - mu2) * rstd * g1[e] + b1[e]);
         }
       }
     }
@@ -550,7 +552,7 @@ __global__ __launch_bounds__(WAVES * 64, NB == 1 ? 2 : 1) void k_swiglu32(
     }
     store_chunk((qb + j + LEAD) % RING, stg);
     load_chunk((j + LEAD + 1) % nchunks, stg);
-    if (sync || RING == 3)
+    if (sync)
       __syncthreads();
     else
       __builtin_amdgcn_sched_barrier(0);
