@@ -375,12 +375,13 @@ def test_swiglu_transition_parity(nt, lengths, c_z, hidden):
     assert err <= TOL["bf16"], err
 
 
-@pytest.mark.parametrize("hidden", [128, 192, 1024])
+@pytest.mark.parametrize("hidden", [64, 128, 192, 256, 320, 1024])
 def test_swiglu_transition_ring_phases(nt, hidden):
-    """The persistent 32x32 kernel at 4, 6 and 32 hidden chunks: its
-    three-buffer weight ring meets a tile boundary at every phase (the chunk
-    count mod 3), and 301 tiles of 256 cells give some workgroups a second
-    tile, others one."""
+    """The persistent 32x32 kernel at 2, 4, 6, 8, 10 and 32 hidden chunks:
+    its five-buffer weight ring meets a tile boundary at every phase (the
+    chunk count mod 5: 2, 4, 1, 3, 0, 2; at two chunks the ring holds the
+    same chunk twice), and 301 tiles of 256 cells give some workgroups a
+    second tile, others one."""
     lengths, c_z = [256, 100, 37], 128
     announce(f"swiglu transition ring phases hidden={hidden} cells={sum(n * n for n in lengths)}")
     z = pin.random_pair_rows(lengths, c_z, "bf16", seed=61)

@@ -52,11 +52,11 @@ def test_swiglu_block_matches_oracle(nt, lengths, c_s, c_z, hidden):
     assert scaled_max_err(f64(s_out, torch), rs) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("hidden", [192, 1024])
+@pytest.mark.parametrize("hidden", [64, 192, 256, 320, 1024])
 def test_swiglu_block_ring_phases(nt, hidden):
-    """The fused kernel at 6 and 32 hidden chunks over 301 tiles of 256
-    cells: the weight ring meets tile boundaries at other phases than at 16
-    chunks, and some workgroups take a second tile."""
+    """The fused kernel at 2, 6, 8, 10 and 32 hidden chunks over 301 tiles of
+    256 cells: its five-buffer weight ring meets tile boundaries at every
+    phase (the chunk count mod 5), and some workgroups take a second tile."""
     lengths, c_s, c_z = [256, 100, 37], 64, 128
     announce(f"swiglu block ring phases hidden={hidden}")
     x = pin.make_swiglu_inputs(lengths, c_s, c_z, hidden, "bf16", seed=12)
